@@ -1,0 +1,172 @@
+/*
+ * mamba2_ssd.h -- C ABI of the Mamba-2 chunked SSD forward pass on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (NVIDIA developer blog "Accelerating Mamba-2 with
+ * high-performance forward-pass kernels in NVIDIA CUDA Tile", section
+ * "Mamba-2 architecture", the core recurrence): for every batch row b and
+ * head h, with g = h / (nheads / ngroups) the head's group,
+ *
+ *     state_t[p, n] = exp(A[h] * dt[b,t,h]) * state_{t-1}[p, n]
+ *                     + dt[b,t,h] * x[b,t,h,p] * B[b,t,g,n]
+ *     y[b,t,h,p]    = sum_n C[b,t,g,n] * state_t[p, n] + D[h] * x[b,t,h,p]
+ *
+ * starting from state_{-1} = init_state[b,h] (zeros when NULL). The state is
+ * held headdim-major ([headdim][dstate]). The library evaluates it chunk by
+ * chunk through the log-space cumulative-decay "jump" formulas of the same
+ * section, in four kernels enqueued on the caller's stream:
+ *
+ *   ssd_chunk_cumsum  chunk-local inclusive cumsum of A*dt, times log2(e)
+ *                     (blog section "Kernel 1")
+ *   ssd_chunk_state   each chunk's own state contribution, an MFMA
+ *                     contraction over the chunk's tokens (the inner
+ *                     product of the "Kernel 2: fwd_pass_state" section)
+ *   ssd_state_pass    the sequential pass over chunk checkpoints
+ *                     (the chunk loop of the same section)
+ *   ssd_chunk_scan    the per-chunk outputs: decayed carried-state term,
+ *                     masked decayed C.B^T product with dt*x, and D*x
+ *                     (blog section "Kernel 3: compute_out")
+ *
+ * Conventions for every entry point:
+ *  - All arrays are dense, row-major, with the layouts given below; there
+ *    are no strides. Pointers passed to mamba2_ssd_fwd are device pointers
+ *    (hipMalloc'd or torch CUDA tensors); the caller owns them. The library
+ *    never allocates or frees memory and keeps no state between calls.
+ *  - dt must be >= 0 (already through softplus; no bias or softplus is
+ *    applied inside) and A must be < 0 (the blog's "every A is negative").
+ *    These are documented preconditions, not checked on the device.
+ *  - Status codes are the MAMBA2_SSD_* values below: 0 on success, negative
+ *    on failure. Validation runs on the host before anything is enqueued;
+ *    on a validation error nothing is launched and no output is touched.
+ *  - mamba2_ssd_fwd is asynchronous: it returns once the kernels are
+ *    enqueued. Faults inside a kernel surface at the caller's next
+ *    synchronisation, not as a return code.
+ */
+#ifndef MAMBA2_SSD_H_
+#define MAMBA2_SSD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MAMBA2_SSD_OK                0
+#define MAMBA2_SSD_ERR_NULL_POINTER (-1) /* a required pointer is NULL               */
+#define MAMBA2_SSD_ERR_BAD_DIM      (-2) /* a size is <= 0 (< 0 for batch, seqlen),
+                                            overflows, or exceeds a grid limit        */
+#define MAMBA2_SSD_ERR_GROUPS       (-3) /* nheads is not a multiple of ngroups       */
+#define MAMBA2_SSD_ERR_CHUNK        (-4) /* chunk is not one of 64, 128, 256          */
+#define MAMBA2_SSD_ERR_UNSUPPORTED  (-5) /* (headdim, dstate, io dtype) not built     */
+#define MAMBA2_SSD_ERR_WORKSPACE    (-6) /* workspace NULL or smaller than required   */
+#define MAMBA2_SSD_ERR_ALIAS        (-7) /* an output overlaps another array          */
+#define MAMBA2_SSD_ERR_HIP          (-8) /* a kernel launch failed; see
+                                            mamba2_ssd_last_hip_error()               */
+
+/* ---- io dtypes: the element type of x, B, C and y ---------------------- */
+#define MAMBA2_SSD_F32  0   /* IEEE binary32                                    */
+#define MAMBA2_SSD_BF16 1   /* bfloat16 (upper half of a binary32)              */
+
+/* Problem sizes. batch and seqlen may be 0 (nothing to compute: with
+ * seqlen == 0 final_state receives init_state, or zeros). seqlen need not be
+ * a multiple of chunk: the last chunk is then ragged and behaves as if
+ * padded with tokens whose x, dt, B and C are zero (the blog's kernel loads
+ * use zero padding), which neither decay nor feed the state. */
+typedef struct {
+  int64_t batch;    /* B  */
+  int64_t seqlen;   /* T  */
+  int64_t nheads;   /* H  */
+  int64_t headdim;  /* P: 64 or 128                         */
+  int64_t dstate;   /* N: 64, 128 or 256                    */
+  int64_t ngroups;  /* G: H % G == 0; heads h*H/G .. (h+1)*H/G-1 share group h */
+  int64_t chunk;    /* Q: 64, 128 or 256                    */
+} mamba2_ssd_dims;
+
+/* Where each intermediate lives inside the caller's workspace. nchunks =
+ * ceil(seqlen / chunk); Tp = nchunks * chunk. Offsets are in bytes from the
+ * workspace base and 256-byte aligned. The contents after a call are
+ * documented so tests can check each kernel's output:
+ *   gcum    float [batch][nheads][Tp]  chunk-local inclusive cumsum of
+ *                                      A*dt, times log2(e); padded tokens
+ *                                      repeat the last real value
+ *   dtt     float [batch][nheads][Tp]  dt transposed, padded tokens 0
+ *   states  float [batch][nheads][nchunks][headdim][dstate]
+ *                                      each chunk's own contribution S_k
+ *   hprev   float [batch][nheads][nchunks][headdim][dstate]
+ *                                      the state entering chunk k             */
+typedef struct {
+  size_t total_bytes;
+  size_t gcum_offset;
+  size_t dtt_offset;
+  size_t states_offset;
+  size_t hprev_offset;
+  int64_t nchunks;
+} mamba2_ssd_workspace_layout;
+
+/* 1 if (headdim, dstate, chunk, io_dtype) has compiled kernels, else 0.
+ * Host only; needs no GPU. */
+int mamba2_ssd_supported(int64_t headdim, int64_t dstate, int64_t chunk, int io_dtype);
+
+/* Fill *out with the workspace layout for these sizes. Host only.
+ * Returns a status code (the dimension checks of mamba2_ssd_check_args). */
+int mamba2_ssd_workspace_layout_query(const mamba2_ssd_dims* dims, int io_dtype,
+                                      mamba2_ssd_workspace_layout* out);
+
+/* Workspace bytes mamba2_ssd_fwd needs, or 0 if the sizes are invalid.
+ * Host only. */
+size_t mamba2_ssd_fwd_workspace_bytes(const mamba2_ssd_dims* dims, int io_dtype);
+
+/* Every host-side check of mamba2_ssd_fwd, without touching the GPU: sizes,
+ * support, required pointers, workspace size and aliasing. Pointers are only
+ * compared, never dereferenced, so any values may be passed.
+ * Aliasing rules: init_state may be the same pointer as final_state (an
+ * in-place state update); apart from that, y, final_state and the
+ * workspace must not overlap any other array. Inputs may overlap each
+ * other. Arrays that are empty (batch or seqlen 0) may be NULL. */
+int mamba2_ssd_check_args(const mamba2_ssd_dims* dims, int io_dtype,
+                          const void* x, const float* dt, const float* A,
+                          const void* B, const void* C, const float* D,
+                          const float* init_state, const void* y, const float* final_state,
+                          const void* workspace, size_t workspace_bytes);
+
+/* The forward pass.
+ *   x           io    [batch][seqlen][nheads][headdim]
+ *   dt          float [batch][seqlen][nheads]          (>= 0)
+ *   A           float [nheads]                         (< 0)
+ *   B, C        io    [batch][seqlen][ngroups][dstate]
+ *   D           float [nheads]
+ *   init_state  float [batch][nheads][headdim][dstate], or NULL for zeros
+ *   y           io    [batch][seqlen][nheads][headdim]  (written)
+ *   final_state float [batch][nheads][headdim][dstate], or NULL to skip
+ *   workspace   device memory of at least mamba2_ssd_fwd_workspace_bytes;
+ *               contents on entry are ignored; concurrent calls need
+ *               separate workspaces
+ *   stream      a hipStream_t, or NULL for the default stream
+ * Arithmetic: fp32 accumulation and an fp32 carried state everywhere. With
+ * io = BF16 the products run on bf16 MFMA: x, B and C enter exactly, and each
+ * operand that is not an input (w*x in the chunk-state contraction, the
+ * decayed masked C.B^T times dt, and the carried state) enters as a pair of
+ * bf16 numbers hi + lo, about 16 significant bits, in two MFMAs. y is
+ * rounded to bf16 nearest-even once at the end; final_state is fp32. With
+ * io = F32 every product is an fp32 MFMA.
+ * Returns a status code; see the conventions above. */
+int mamba2_ssd_fwd(const mamba2_ssd_dims* dims, int io_dtype,
+                   const void* x, const float* dt, const float* A,
+                   const void* B, const void* C, const float* D,
+                   const float* init_state, void* y, float* final_state,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static string naming a status code. Never NULL. */
+const char* mamba2_ssd_status_string(int status);
+
+/* Text of the last HIP error this thread saw inside mamba2_ssd_fwd
+ * (MAMBA2_SSD_ERR_HIP), or "" if none. Valid until the thread's next call. */
+const char* mamba2_ssd_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA2_SSD_H_ */

@@ -1,0 +1,123 @@
+"""Mamba-2 chunked SSD forward pass for AMD MI355X (gfx950).
+
+A thin binding of ``libmamba2_ssd.so`` (C ABI in ``include/mamba2_ssd.h``).
+Every step of the forward pass runs in the library's HIP kernels; this module
+only marshals arguments. PyTorch provides device memory and the current
+stream. Importing raises if the library has not been built
+(``python state_space_sequence_ssd_amd/build.py``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+from ._lib import (BF16, F32, STATUS, Dims, SsdError, WorkspaceLayout, lib, status_string)
+
+__all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_layout", "check_args",
+           "Dims", "WorkspaceLayout", "SsdError", "F32", "BF16", "STATUS", "status_string",
+           "mamba2_ssd_fwd", "mamba2_ssd_check_args", "mamba2_ssd_supported",
+           "mamba2_ssd_fwd_workspace_bytes", "mamba2_ssd_workspace_layout_query",
+           "mamba2_ssd_status_string", "mamba2_ssd_last_hip_error"]
+
+# The C entry points under their own names (ctypes functions with prototypes).
+mamba2_ssd_fwd = lib.mamba2_ssd_fwd
+mamba2_ssd_check_args = lib.mamba2_ssd_check_args
+mamba2_ssd_supported = lib.mamba2_ssd_supported
+mamba2_ssd_fwd_workspace_bytes = lib.mamba2_ssd_fwd_workspace_bytes
+mamba2_ssd_workspace_layout_query = lib.mamba2_ssd_workspace_layout_query
+mamba2_ssd_status_string = lib.mamba2_ssd_status_string
+mamba2_ssd_last_hip_error = lib.mamba2_ssd_last_hip_error
+
+
+def _dims(d) -> Dims:
+    if isinstance(d, Dims):
+        return d
+    if isinstance(d, dict):
+        return Dims(**d)
+    return Dims(*d)
+
+
+def supported(headdim: int, dstate: int, chunk: int, io: int) -> bool:
+    return bool(lib.mamba2_ssd_supported(headdim, dstate, chunk, io))
+
+
+def workspace_layout(dims, io: int) -> WorkspaceLayout:
+    out = WorkspaceLayout()
+    st = lib.mamba2_ssd_workspace_layout_query(ctypes.byref(_dims(dims)), io, ctypes.byref(out))
+    if st != 0:
+        raise SsdError(st)
+    return out
+
+
+def workspace_bytes(dims, io: int) -> int:
+    return int(lib.mamba2_ssd_fwd_workspace_bytes(ctypes.byref(_dims(dims)), io))
+
+
+def check_args(dims, io, x, dt, A, B, C, D, init_state, y, final_state, workspace, ws_bytes) -> int:
+    """Host-only validation on raw integer addresses (0 for NULL)."""
+    return int(lib.mamba2_ssd_check_args(ctypes.byref(_dims(dims)), io, x, dt, A, B, C, D,
+                                         init_state, y, final_state, workspace, ws_bytes))
+
+
+def ssd_fwd_ptr(dims, io, x, dt, A, B, C, D, init_state, y, final_state, workspace, ws_bytes,
+                stream: int = 0) -> None:
+    """mamba2_ssd_fwd on raw device addresses; raises SsdError on a nonzero status."""
+    st = lib.mamba2_ssd_fwd(ctypes.byref(_dims(dims)), io, x, dt, A, B, C, D, init_state, y,
+                            final_state, workspace, ws_bytes, stream)
+    if st != 0:
+        raise SsdError(st, lib.mamba2_ssd_last_hip_error().decode())
+
+
+def ssd_fwd(x, dt, A, B, C, D, chunk: int, init_state=None, *, return_final_state: bool = True,
+            y=None, final_state=None, workspace=None) -> Tuple[object, Optional[object]]:
+    """Forward pass on torch CUDA tensors (all contiguous, same device).
+
+    x [batch, seqlen, nheads, headdim] and B, C [batch, seqlen, ngroups,
+    dstate] share the io dtype (torch.bfloat16 or torch.float32); dt
+    [batch, seqlen, nheads], A and D [nheads] and init_state [batch, nheads,
+    headdim, dstate] are float32. Returns ``(y, final_state)``; final_state is
+    None when ``return_final_state`` is False. ``y``, ``final_state`` and
+    ``workspace`` (a uint8 tensor) may be passed to reuse memory; otherwise
+    they are allocated with torch. Runs on torch's current stream.
+    """
+    import torch
+
+    if x.dtype == torch.bfloat16:
+        io = BF16
+    elif x.dtype == torch.float32:
+        io = F32
+    else:
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    for name, t, want in (("B", B, x.dtype), ("C", C, x.dtype), ("dt", dt, torch.float32),
+                          ("A", A, torch.float32), ("D", D, torch.float32)):
+        if t.dtype != want:
+            raise TypeError(f"{name} must be {want}, got {t.dtype}")
+    if init_state is not None and init_state.dtype != torch.float32:
+        raise TypeError("init_state must be float32")
+    tensors = [x, dt, A, B, C, D] + ([init_state] if init_state is not None else [])
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (bt, T, H) or tuple(B.shape) != (bt, T, G, N) or tuple(C.shape) != (bt, T, G, N) \
+            or tuple(A.shape) != (H,) or tuple(D.shape) != (H,):
+        raise ValueError("inconsistent shapes")
+    if init_state is not None and tuple(init_state.shape) != (bt, H, P, N):
+        raise ValueError("init_state must be [batch, nheads, headdim, dstate]")
+    dims = Dims(bt, T, H, P, N, G, chunk)
+    if y is None:
+        y = torch.empty_like(x)
+    if return_final_state and final_state is None:
+        final_state = torch.empty((bt, H, P, N), dtype=torch.float32, device=x.device)
+    nbytes = workspace_layout(dims, io).total_bytes   # raises SsdError on invalid sizes
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    ptr = lambda t: 0 if t is None else t.data_ptr()
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        ssd_fwd_ptr(dims, io, ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), ptr(init_state), ptr(y),
+                    ptr(final_state) if return_final_state else 0, ptr(workspace), workspace.numel(), stream)
+    return y, (final_state if return_final_state else None)

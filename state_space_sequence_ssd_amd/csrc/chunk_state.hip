@@ -1,0 +1,172 @@
+// ssd_chunk_state: each chunk's own contribution to the state,
+//
+//   S_k[p, n] = sum_{t in chunk k} x[t, p] * w_t * B[t, n],
+//   w_t = dt_t * 2^(G'_last - G'_t)
+//
+// i.e. (exp(G_last - G) o dt o B)^T X of the CUDA Tile Mamba-2 blog's jump
+// formula (section "Mamba-2 architecture"; the MMA in "Kernel 2:
+// fwd_pass_state"), held headdim-major. Here it is computed for every chunk
+// in parallel, and the sequential part lives in ssd_state_pass.
+//
+// One wave computes one (batch, head, chunk) tile's rows of one headdim
+// column group against NGW dstate column groups with 32x32 MFMAs; the
+// contraction runs over the chunk's tokens in steps of 2*KPL. The scale w_t
+// is applied to x (w and x are both per head, while B is shared by the
+// heads of a group). With bf16 io the product w*x is not a bf16 number, so
+// it enters the MFMA as a bf16 (hi, lo) pair in two MFMAs against the exact
+// bf16 B (the blog instead rounds its scaled operand to bf16 once; that
+// rounding alone breaks a 1e-2 + 2e-2|y| elementwise bound where large terms
+// cancel). Accumulation is fp32 and S is stored fp32 into the workspace.
+//
+// Operand loads: the contraction index (token) is the slow index of both x
+// and B in memory, so each lane loads one dword per token row; a 32-lane
+// half reads a whole 128-byte row. Element e of a dword feeds the MFMA block
+// of parity e (see ssd_device.h), so both operands arrive without any
+// transpose through LDS.
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+namespace {
+
+template <typename T, int P, int N>
+struct StateCfg {
+  static constexpr int E = Io<T>::E;
+  static constexpr int CG = 32 * E;                 // columns per column group
+  static constexpr int NPG = P / CG;                // headdim column groups
+  static constexpr int NNG = N / CG;                // dstate column groups
+  static constexpr int NGW = (E == 2) ? (NNG < 2 ? NNG : 2) : NNG;   // dstate groups per wave
+  static constexpr int NGS = NNG / NGW;
+  static constexpr int WPT = NPG * NGS;             // waves per (b, h, chunk) tile
+  static constexpr int TPW = 4 / WPT;               // tiles per 256-thread workgroup
+  static_assert(WPT >= 1 && WPT <= 4 && 4 % WPT == 0, "tile does not fit a workgroup");
+};
+
+template <typename T, int P, int N, int Q>
+__global__ __launch_bounds__(256) void ssd_chunk_state(const T* __restrict__ x,
+                                                       const T* __restrict__ Bm,
+                                                       const float* __restrict__ gcum,
+                                                       const float* __restrict__ dtt,
+                                                       float* __restrict__ states,
+                                                       int64_t Tlen, int H, int G, int64_t nc, int64_t Tp) {
+  using I = Io<T>;
+  using Cfg = StateCfg<T, P, N>;
+  constexpr int E = I::E, KPL = I::KPL, CG = Cfg::CG, NGW = Cfg::NGW, NGS = Cfg::NGS;
+  constexpr int WPT = Cfg::WPT, TPW = Cfg::TPW;
+  constexpr int KSTEPS = Q / (2 * KPL);
+
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int m = lane % 32, g = lane / 32;
+  const int tile = wave / WPT, sub = wave % WPT;
+  const int pg = sub / NGS, ng0 = (sub % NGS) * NGW;
+  const int h = blockIdx.x * TPW + tile;
+  if (h >= H) return;
+  const int k = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int grp = h / (H / G);
+  const int64_t t0 = (int64_t)k * Q;
+
+  const float* gc = gcum + ((int64_t)b * H + h) * Tp + t0;
+  const float* dtc = dtt + ((int64_t)b * H + h) * Tp + t0;
+  const float glast = gc[Q - 1];
+
+  // dword views: x row stride H*P elements, B row stride G*N elements
+  const int64_t xstride = (int64_t)H * P / E, bstride = (int64_t)G * N / E;
+  const uint32_t* xb = reinterpret_cast<const uint32_t*>(x + ((b * Tlen + t0) * H + h) * P + pg * CG) + m;
+  const uint32_t* bb = reinterpret_cast<const uint32_t*>(Bm + ((b * Tlen + t0) * G + grp) * N + ng0 * CG) + m;
+  const int64_t nvalid = Tlen - t0;   // tokens of this chunk inside the sequence
+
+  f32x16 acc[E][NGW][E];
+#pragma unroll
+  for (int a = 0; a < E; ++a)
+#pragma unroll
+    for (int j = 0; j < NGW; ++j)
+#pragma unroll
+      for (int c = 0; c < E; ++c) acc[a][j][c] = f32x16{};
+
+#pragma unroll 2
+  for (int s = 0; s < KSTEPS; ++s) {
+    const int tb = s * 2 * KPL + KPL * g;   // first of this lane half's KPL tokens
+    float w[KPL];
+    uint32_t xd[KPL];
+    uint32_t bd[NGW][KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int t = tb + i;
+      const bool valid = t < nvalid;
+      w[i] = dtc[t] * exp2_hw(glast - gc[t]);
+      xd[i] = valid ? xb[t * xstride] : 0u;
+#pragma unroll
+      for (int j = 0; j < NGW; ++j) bd[j][i] = valid ? bb[t * bstride + j * (CG / E)] : 0u;
+    }
+    typename I::Frag ahi[E], alo[E];
+#pragma unroll
+    for (int pe = 0; pe < E; ++pe) {
+      float v[KPL];
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) v[i] = w[i] * I::elem(xd[i], pe);
+      I::split(v, ahi[pe], alo[pe]);
+    }
+#pragma unroll
+    for (int j = 0; j < NGW; ++j)
+#pragma unroll
+      for (int ne = 0; ne < E; ++ne) {
+        const typename I::Frag bf = I::from_dwords(bd[j], ne);   // B is exact in the io dtype
+#pragma unroll
+        for (int pe = 0; pe < E; ++pe) {
+          I::mma(acc[pe][j][ne], ahi[pe], bf);
+          if constexpr (I::SPLIT) I::mma(acc[pe][j][ne], alo[pe], bf);
+        }
+      }
+  }
+
+  // S[p][n]: D row r -> p = pg*CG + E*drow(r, g) + pe, col -> n = (ng0+j)*CG + E*m + ne
+  float* sb = states + (((int64_t)b * H + h) * nc + k) * (int64_t)(P * N);
+#pragma unroll
+  for (int pe = 0; pe < E; ++pe)
+#pragma unroll
+    for (int j = 0; j < NGW; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = pg * CG + E * drow(r, g) + pe;
+        float* dst = sb + p * N + (ng0 + j) * CG + E * m;
+        if constexpr (E == 2)
+          *reinterpret_cast<float2*>(dst) = make_float2(acc[pe][j][0][r], acc[pe][j][1][r]);
+        else
+          *dst = acc[pe][j][0][r];
+      }
+}
+
+template <typename T, int P, int N, int Q>
+hipError_t launch_one(const Problem& p, hipStream_t stream) {
+  constexpr int TPW = StateCfg<T, P, N>::TPW;
+  const dim3 grid((unsigned)((p.H + TPW - 1) / TPW), (unsigned)p.nc, (unsigned)p.bt);
+  hipLaunchKernelGGL((ssd_chunk_state<T, P, N, Q>), grid, dim3(256), 0, stream, (const T*)p.x, (const T*)p.B,
+                     p.gcum, p.dtt, p.states, p.T, (int)p.H, (int)p.G, p.nc, p.Tp);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch(const Problem& p, hipStream_t s) {
+#define SSD_CASE(PP, NN, QQ) \
+  if (p.P == PP && p.N == NN && p.Q == QQ) return launch_one<T, PP, NN, QQ>(p, s);
+#define SSD_Q(PP, NN) SSD_CASE(PP, NN, 64) SSD_CASE(PP, NN, 128) SSD_CASE(PP, NN, 256)
+  SSD_Q(64, 64) SSD_Q(64, 128) SSD_Q(64, 256) SSD_Q(128, 64) SSD_Q(128, 128) SSD_Q(128, 256)
+#undef SSD_Q
+#undef SSD_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool chunk_state_has(int io, int64_t P, int64_t N, int64_t Q) {
+  return (io == 0 || io == 1) && (P == 64 || P == 128) && (N == 64 || N == 128 || N == 256) &&
+         (Q == 64 || Q == 128 || Q == 256);
+}
+
+hipError_t launch_chunk_state(const Problem& p, hipStream_t stream) {
+  return p.io == 1 ? dispatch<bf16>(p, stream) : dispatch<float>(p, stream);
+}
+
+}  // namespace ssd

@@ -1,0 +1,217 @@
+// C ABI of the Mamba-2 chunked SSD forward pass (declared in
+// include/mamba2_ssd.h). Host code only: argument validation, workspace
+// layout, and the four launches in dependency order on the caller's stream
+// (the kernel order of the CUDA Tile Mamba-2 blog: cumulative sum, state
+// pass, then the outputs, with the state contraction split out of the pass).
+#include "../../include/mamba2_ssd.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <string>
+
+#include "ssd_launch.h"
+
+namespace {
+
+thread_local std::string g_last_hip_error;
+
+constexpr size_t kAlign = 256;
+constexpr int64_t kMaxDim = int64_t(1) << 40;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+bool valid_io(int io) { return io == MAMBA2_SSD_F32 || io == MAMBA2_SSD_BF16; }
+size_t io_size(int io) { return io == MAMBA2_SSD_BF16 ? 2 : 4; }
+
+struct Sizes {
+  int64_t nc = 0, Tp = 0;
+  int64_t n_x = 0, n_dt = 0, n_bc = 0, n_state = 0, n_chunkstates = 0;
+};
+
+// Dimension checks shared by every entry point.
+int check_dims(const mamba2_ssd_dims* d, int io, Sizes* s) {
+  if (!d) return MAMBA2_SSD_ERR_NULL_POINTER;
+  if (!valid_io(io)) return MAMBA2_SSD_ERR_UNSUPPORTED;
+  if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 ||
+      d->ngroups <= 0 || d->chunk <= 0)
+    return MAMBA2_SSD_ERR_BAD_DIM;
+  if (d->batch > kMaxDim || d->seqlen > kMaxDim || d->nheads > kMaxDim || d->ngroups > kMaxDim)
+    return MAMBA2_SSD_ERR_BAD_DIM;
+  if (d->nheads % d->ngroups) return MAMBA2_SSD_ERR_GROUPS;
+  if (d->chunk != 64 && d->chunk != 128 && d->chunk != 256) return MAMBA2_SSD_ERR_CHUNK;
+  if (!ssd::chunk_state_has(io, d->headdim, d->dstate, d->chunk) ||
+      !ssd::chunk_scan_has(io, d->headdim, d->dstate, d->chunk))
+    return MAMBA2_SSD_ERR_UNSUPPORTED;
+  Sizes r;
+  r.nc = (d->seqlen + d->chunk - 1) / d->chunk;
+  r.Tp = r.nc * d->chunk;
+  int64_t bt, bth, pn;
+  if (!mul_ok(d->batch, d->seqlen, &bt)) return MAMBA2_SSD_ERR_BAD_DIM;
+  if (!mul_ok(bt, d->nheads, &bth)) return MAMBA2_SSD_ERR_BAD_DIM;
+  if (!mul_ok(bth, d->headdim, &r.n_x)) return MAMBA2_SSD_ERR_BAD_DIM;
+  r.n_dt = bth;
+  int64_t btg;
+  if (!mul_ok(bt, d->ngroups, &btg) || !mul_ok(btg, d->dstate, &r.n_bc)) return MAMBA2_SSD_ERR_BAD_DIM;
+  pn = d->headdim * d->dstate;
+  int64_t bh;
+  if (!mul_ok(d->batch, d->nheads, &bh) || !mul_ok(bh, pn, &r.n_state)) return MAMBA2_SSD_ERR_BAD_DIM;
+  if (!mul_ok(r.n_state, r.nc, &r.n_chunkstates)) return MAMBA2_SSD_ERR_BAD_DIM;
+  int64_t bytes;
+  if (!mul_ok(r.n_chunkstates, 8, &bytes) || !mul_ok(r.n_x, 8, &bytes)) return MAMBA2_SSD_ERR_BAD_DIM;
+  // grid limits of the launchers: y = nchunks (chunk-parallel kernels), z = batch
+  if (r.nc > ssd::kMaxGridYZ || d->batch > ssd::kMaxGridYZ) return MAMBA2_SSD_ERR_BAD_DIM;
+  if (bh > INT32_MAX) return MAMBA2_SSD_ERR_BAD_DIM;
+  *s = r;
+  return MAMBA2_SSD_OK;
+}
+
+void layout_of(const mamba2_ssd_dims* d, const Sizes& s, mamba2_ssd_workspace_layout* L) {
+  const size_t bh = (size_t)d->batch * (size_t)d->nheads;
+  size_t off = 0;
+  L->gcum_offset = off;
+  off = align_up(off + bh * (size_t)s.Tp * 4);
+  L->dtt_offset = off;
+  off = align_up(off + bh * (size_t)s.Tp * 4);
+  L->states_offset = off;
+  off = align_up(off + (size_t)s.n_chunkstates * 4);
+  L->hprev_offset = off;
+  off = align_up(off + (size_t)s.n_chunkstates * 4);
+  L->total_bytes = off;
+  L->nchunks = s.nc;
+}
+
+struct Range {
+  uintptr_t lo, hi;   // [lo, hi); empty when lo == hi
+};
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, p ? a + bytes : a};
+}
+bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+}  // namespace
+
+extern "C" {
+
+int mamba2_ssd_supported(int64_t headdim, int64_t dstate, int64_t chunk, int io_dtype) {
+  return valid_io(io_dtype) && ssd::chunk_state_has(io_dtype, headdim, dstate, chunk) &&
+         ssd::chunk_scan_has(io_dtype, headdim, dstate, chunk);
+}
+
+int mamba2_ssd_workspace_layout_query(const mamba2_ssd_dims* dims, int io_dtype,
+                                      mamba2_ssd_workspace_layout* out) {
+  Sizes s;
+  const int st = check_dims(dims, io_dtype, &s);
+  if (st != MAMBA2_SSD_OK) return st;
+  if (!out) return MAMBA2_SSD_ERR_NULL_POINTER;
+  layout_of(dims, s, out);
+  return MAMBA2_SSD_OK;
+}
+
+size_t mamba2_ssd_fwd_workspace_bytes(const mamba2_ssd_dims* dims, int io_dtype) {
+  mamba2_ssd_workspace_layout L;
+  if (mamba2_ssd_workspace_layout_query(dims, io_dtype, &L) != MAMBA2_SSD_OK) return 0;
+  return L.total_bytes;
+}
+
+int mamba2_ssd_check_args(const mamba2_ssd_dims* d, int io, const void* x, const float* dt,
+                          const float* A, const void* B, const void* C, const float* D,
+                          const float* init_state, const void* y, const float* final_state,
+                          const void* workspace, size_t workspace_bytes) {
+  Sizes s;
+  int st = check_dims(d, io, &s);
+  if (st != MAMBA2_SSD_OK) return st;
+  const bool tokens = s.n_x > 0;
+  if (!A || !D) return MAMBA2_SSD_ERR_NULL_POINTER;
+  if (tokens && (!x || !dt || !B || !C || !y)) return MAMBA2_SSD_ERR_NULL_POINTER;
+  mamba2_ssd_workspace_layout L;
+  layout_of(d, s, &L);
+  if (d->batch > 0 && L.total_bytes > 0 && (!workspace || workspace_bytes < L.total_bytes))
+    return MAMBA2_SSD_ERR_WORKSPACE;
+
+  const size_t e = io_size(io);
+  const Range rx = range_of(x, (size_t)s.n_x * e), rdt = range_of(dt, (size_t)s.n_dt * 4);
+  const Range rA = range_of(A, (size_t)d->nheads * 4), rD = range_of(D, (size_t)d->nheads * 4);
+  const Range rB = range_of(B, (size_t)s.n_bc * e), rC = range_of(C, (size_t)s.n_bc * e);
+  const Range rinit = range_of(init_state, (size_t)s.n_state * 4);
+  const Range ry = range_of(y, (size_t)s.n_x * e), rfin = range_of(final_state, (size_t)s.n_state * 4);
+  const Range rws = range_of(workspace, d->batch > 0 ? L.total_bytes : 0);
+
+  const Range others[] = {rx, rdt, rA, rD, rB, rC};
+  for (const Range& r : others) {
+    if (overlap(ry, r) || overlap(rws, r) || overlap(rfin, r)) return MAMBA2_SSD_ERR_ALIAS;
+  }
+  if (overlap(ry, rinit) || overlap(rws, rinit)) return MAMBA2_SSD_ERR_ALIAS;
+  // final_state may be exactly init_state (an in-place update), never a partial overlap
+  if (overlap(rfin, rinit) && !(rfin.lo == rinit.lo && rfin.hi == rinit.hi)) return MAMBA2_SSD_ERR_ALIAS;
+  if (overlap(ry, rfin) || overlap(ry, rws) || overlap(rfin, rws)) return MAMBA2_SSD_ERR_ALIAS;
+  return MAMBA2_SSD_OK;
+}
+
+int mamba2_ssd_fwd(const mamba2_ssd_dims* d, int io, const void* x, const float* dt, const float* A,
+                   const void* B, const void* C, const float* D, const float* init_state, void* y,
+                   float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_hip_error.clear();
+  int st = mamba2_ssd_check_args(d, io, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                                 workspace_bytes);
+  if (st != MAMBA2_SSD_OK) return st;
+  if (d->batch == 0) return MAMBA2_SSD_OK;
+
+  Sizes s;
+  check_dims(d, io, &s);
+  mamba2_ssd_workspace_layout L;
+  layout_of(d, s, &L);
+  char* ws = static_cast<char*>(workspace);
+
+  ssd::Problem p;
+  p.bt = d->batch; p.T = d->seqlen; p.H = d->nheads; p.P = d->headdim; p.N = d->dstate;
+  p.G = d->ngroups; p.Q = d->chunk; p.nc = s.nc; p.Tp = s.Tp; p.io = io;
+  p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D;
+  p.init = init_state; p.y = y; p.final_state = final_state;
+  p.gcum = reinterpret_cast<float*>(ws + L.gcum_offset);
+  p.dtt = reinterpret_cast<float*>(ws + L.dtt_offset);
+  p.states = reinterpret_cast<float*>(ws + L.states_offset);
+  p.hprev = reinterpret_cast<float*>(ws + L.hprev_offset);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  hipError_t err = hipSuccess;
+  if (s.nc > 0) {
+    err = ssd::launch_chunk_cumsum(p, hs);
+    if (err == hipSuccess) err = ssd::launch_chunk_state(p, hs);
+  }
+  // with seqlen == 0 the pass runs zero chunks: final_state = init_state (or 0)
+  if (err == hipSuccess && (s.nc > 0 || final_state)) err = ssd::launch_state_pass(p, hs);
+  if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_scan(p, hs);
+  if (err != hipSuccess) {
+    g_last_hip_error = hipGetErrorString(err);
+    return MAMBA2_SSD_ERR_HIP;
+  }
+  return MAMBA2_SSD_OK;
+}
+
+const char* mamba2_ssd_status_string(int status) {
+  switch (status) {
+    case MAMBA2_SSD_OK: return "ok";
+    case MAMBA2_SSD_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case MAMBA2_SSD_ERR_BAD_DIM: return "invalid or too large dimension";
+    case MAMBA2_SSD_ERR_GROUPS: return "nheads is not a multiple of ngroups";
+    case MAMBA2_SSD_ERR_CHUNK: return "chunk must be 64, 128 or 256";
+    case MAMBA2_SSD_ERR_UNSUPPORTED: return "unsupported (headdim, dstate, chunk, io dtype)";
+    case MAMBA2_SSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case MAMBA2_SSD_ERR_ALIAS: return "an output overlaps another array";
+    case MAMBA2_SSD_ERR_HIP: return "HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+const char* mamba2_ssd_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+}  // extern "C"

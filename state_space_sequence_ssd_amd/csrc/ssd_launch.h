@@ -1,0 +1,42 @@
+// Host-side description of one forward call, shared by the C ABI and the
+// kernel launchers. All pointers are device pointers, validated by the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct Problem {
+  int64_t bt, T, H, P, N, G, Q;  // batch, seqlen, nheads, headdim, dstate, ngroups, chunk
+  int64_t nc, Tp;                // nchunks, nchunks * chunk
+  int io;                        // 0 = fp32, 1 = bf16 (x, B, C, y)
+  const void* x;
+  const float* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const float* init;             // may be null (zeros)
+  void* y;
+  float* final_state;            // may be null (not written)
+  float* gcum;                   // workspace: [bt][H][Tp]
+  float* dtt;                    // workspace: [bt][H][Tp]
+  float* states;                 // workspace: [bt][H][nc][P][N]
+  float* hprev;                  // workspace: [bt][H][nc][P][N]
+};
+
+// Each launcher enqueues one kernel on `stream` and returns the launch status.
+hipError_t launch_chunk_cumsum(const Problem& p, hipStream_t stream);
+hipError_t launch_chunk_state(const Problem& p, hipStream_t stream);
+hipError_t launch_state_pass(const Problem& p, hipStream_t stream);
+hipError_t launch_chunk_scan(const Problem& p, hipStream_t stream);
+
+// Compile-time instantiation tables (host queries, no GPU needed).
+bool chunk_state_has(int io, int64_t P, int64_t N, int64_t Q);
+bool chunk_scan_has(int io, int64_t P, int64_t N, int64_t Q);
+
+// Grid-dimension limits the launchers rely on (y and z <= 65535).
+constexpr int64_t kMaxGridYZ = 65535;
+
+}  // namespace ssd
