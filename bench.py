@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Throughput of the Mamba-2 chunked SSD forward pass on one MI355X.
+
+One step is one full forward call (all four kernels: chunk cumsum, chunk
+state, state pass, chunk scan) over one synthetic layer whose inputs are
+already resident in GPU memory. The default workload is the 2.7B-like layer
+(batch 4, seqlen 8192, 80 heads, headdim 64, dstate 128, 1 group, chunk 256,
+bf16 x/B/C, fp32 dt/A/D/state).
+
+Prints ONE JSON line with tokens/s, the roofline of the dominant kernel (its
+algorithmic HBM bytes over its average duration, timed with HIP events on the
+launch stream inside the timed region), per-kernel figures, and the CPU
+oracle's throughput on a bounded sample of the same layer (timed on this
+host's cores), whose outputs also check the benchmarked GPU output.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+F32_PEAK_TFLOPS = 157.3        # MI355X dense fp32 MFMA, published
+KERNELS = ["ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_pass", "ssd_chunk_scan"]
+
+
+def algorithmic_cost(cfg):
+    """Bytes each kernel must move (every input read once, every output written
+    once) and the flops of its contraction, for one launch over the layer."""
+    e = 2 if cfg.io == "bf16" else 4
+    Bt, T, H, P, N, G, Q = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk
+    nc = math.ceil(T / Q)
+    Tp = nc * Q
+    x = Bt * T * H * P * e            # x, and y of the same size
+    bc = Bt * T * G * N * e           # one of B, C
+    dt = Bt * T * H * 4
+    gq = Bt * H * Tp * 4              # one of the transposed dt / cumsum arrays
+    st = Bt * H * nc * P * N * 4      # all chunk states (fp32)
+    fin = Bt * H * P * N * 4
+    init = fin if cfg.init_sigma is not None else 0
+    cost = {
+        "ssd_chunk_cumsum": (dt + 2 * gq, 0.0),
+        "ssd_chunk_state": (x + bc + 2 * gq + st, 2.0 * Bt * H * Tp * P * N),
+        "ssd_state_pass": (2 * st + fin + init + Bt * H * nc * 4, 2.0 * Bt * H * nc * P * N),
+        "ssd_chunk_scan": (2 * x + 2 * bc + 2 * gq + st + H * 4,
+                           2.0 * Bt * H * Tp * P * N                       # C . Hprev^T
+                           + Bt * H * nc * Q * (Q + 1) * P                 # causal (CB) . X
+                           + Bt * G * nc * Q * (Q + 1) * N),               # causal C . B^T once per group
+    }
+    return cost
+
+
+def cpu_baseline(cfg, inp, y_gpu, budget_s=10.0):
+    """The chunked fp64 oracle, as it stands, on whole batch rows of the same
+    layer until `budget_s` has elapsed; its outputs are checked against the
+    GPU output for the same rows."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import ssd_chunked
+
+    cores = len(os.sched_getaffinity(0))
+    box_threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    threads = min(cores, box_threads)
+    worst = 0.0
+    with threadpool_limits(limits=threads, user_api="blas"):
+        used = max([i["num_threads"] for i in threadpool_info() if i["user_api"] == "blas"] or [1])
+        rows, t0 = 0, time.perf_counter()
+        while rows < cfg.batch and (rows == 0 or time.perf_counter() - t0 < budget_s):
+            b = rows
+            init = None if inp["init_state"] is None else inp["init_state"][b:b + 1]
+            yr, _ = ssd_chunked(inp["x"][b:b + 1], inp["dt"][b:b + 1], inp["A"], inp["B"][b:b + 1],
+                                inp["C"][b:b + 1], inp["D"], cfg.chunk, init)
+            rows += 1
+            elapsed = time.perf_counter() - t0
+            yg = y_gpu[b:b + 1].astype(np.float64)
+            if cfg.io == "bf16":
+                worst = max(worst, float(np.max(np.abs(yg - yr) / (1e-2 + 2e-2 * np.abs(yr)))))
+            else:
+                worst = max(worst, float(np.max(np.abs(yg - yr)) / max(np.max(np.abs(yr)), 1e-30) / 1e-5))
+    tokens = rows * cfg.seqlen
+    return {
+        "value": tokens / elapsed, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+        "sample": (f"chunked fp64 oracle on batch rows 0..{rows - 1} of {cfg.batch} "
+                   f"({rows * cfg.seqlen} tokens, all {cfg.nheads} heads), {elapsed:.1f} s"),
+        "seconds": elapsed,
+    }, {"rows_checked": rows, "worst_err_over_tolerance": worst, "ok": worst <= 1.0}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="mamba2-2.7b")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Sequence or head sharding across GPUs is a design note only.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import state_space_sequence_ssd_amd as ssd
+    from workloads import config_by_name, generate
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    cfg = config_by_name(args.config)
+    dev = torch.device("cuda:0")
+    inp = generate(cfg)
+    io = ssd.BF16 if cfg.io == "bf16" else ssd.F32
+
+    def to_dev(k):
+        if cfg.io == "bf16" and k in ("x", "B", "C"):
+            return torch.from_numpy(inp[k + "_bits"].view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(inp[k], dtype=np.float32)).to(dev)
+
+    x, B, C, dt, A, D = (to_dev(k) for k in ("x", "B", "C", "dt", "A", "D"))
+    init = None if inp["init_state"] is None else to_dev("init_state")
+    dims = ssd.Dims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk)
+    L = ssd.workspace_layout(dims, io)
+    ws = torch.empty(L.total_bytes, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    fin = torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ptrs = (x.data_ptr(), dt.data_ptr(), A.data_ptr(), B.data_ptr(), C.data_ptr(), D.data_ptr(),
+            0 if init is None else init.data_ptr(), y.data_ptr(), fin.data_ptr(), ws.data_ptr(), ws.numel())
+
+    def new_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+        for e in evs:
+            e.record(stream)   # creates the underlying hipEvent_t
+        return evs
+
+    def step(evs):
+        ssd.ssd_fwd_timed_ptr(dims, io, *ptrs, stream.cuda_stream, [e.cuda_event for e in evs])
+
+    warm = new_events()
+    for _ in range(args.warmup):
+        step(warm)
+    events = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_kernel_ms = {k: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in events]))
+                     for i, k in enumerate(KERNELS)}
+    gpu_ms = float(np.mean([ev[0].elapsed_time(ev[4]) for ev in events]))
+    tokens = cfg.batch * cfg.seqlen
+    cost = algorithmic_cost(cfg)
+    kern = {}
+    for k in KERNELS:
+        nbytes, flops = cost[k]
+        sec = per_kernel_ms[k] * 1e-3
+        peak_tf = BF16_PEAK_TFLOPS if cfg.io == "bf16" else F32_PEAK_TFLOPS
+        kern[k] = {"us": round(per_kernel_ms[k] * 1e3, 2), "alg_bytes": int(nbytes),
+                   "GB/s": round(nbytes / sec / 1e9, 1), "frac_hbm": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+                   "alg_TFLOP/s": round(flops / sec / 1e12, 2), "frac_mfma": round(flops / sec / 1e12 / peak_tf, 4)}
+    dom = max(KERNELS, key=lambda k: per_kernel_ms[k])
+    achieved = kern[dom]["GB/s"]
+
+    out = {
+        "metric": "SSD fwd tokens/sec at 2.7B-layer shape (1 GPU); % MFMA peak / % HBM BW",
+        "value": round(tokens * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.io == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "seqlen": cfg.seqlen, "nheads": cfg.nheads,
+                   "headdim": cfg.headdim, "dstate": cfg.dstate, "ngroups": cfg.ngroups, "chunk": cfg.chunk,
+                   "io": cfg.io, "seed": cfg.seed, "tokens_per_step": tokens},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "gpu_event_ms_per_step": round(gpu_ms, 4),
+        "kernels": kern,
+        "path_bytes_per_step": int(sum(c[0] for c in cost.values())),
+    }
+    if not args.no_cpu:
+        base, parity = cpu_baseline(cfg, inp, y.float().cpu().numpy())
+        out["cpu_baseline"] = base
+        out["parity_vs_oracle"] = parity
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -158,6 +158,20 @@ int mamba2_ssd_fwd(const mamba2_ssd_dims* dims, int io_dtype,
                    const float* init_state, void* y, float* final_state,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* mamba2_ssd_fwd that also records caller-created events on `stream`, so
+ * each kernel can be timed where it runs: events[0] before ssd_chunk_cumsum,
+ * events[1] before ssd_chunk_state, events[2] before ssd_state_pass,
+ * events[3] before ssd_chunk_scan and events[4] after it. `events` points to
+ * 5 hipEvent_t handles (passed as void*) owned by the caller; NULL makes the
+ * call identical to mamba2_ssd_fwd. The kernels and their order are the
+ * same; a failed event record returns MAMBA2_SSD_ERR_HIP. */
+int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* dims, int io_dtype,
+                         const void* x, const float* dt, const float* A,
+                         const void* B, const void* C, const float* D,
+                         const float* init_state, void* y, float* final_state,
+                         void* workspace, size_t workspace_bytes, void* stream,
+                         void* const* events);
+
 /* Static string naming a status code. Never NULL. */
 const char* mamba2_ssd_status_string(int status);
 

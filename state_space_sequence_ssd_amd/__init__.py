@@ -15,12 +15,14 @@ from ._lib import (BF16, F32, STATUS, Dims, SsdError, WorkspaceLayout, lib, stat
 
 __all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_layout", "check_args",
            "Dims", "WorkspaceLayout", "SsdError", "F32", "BF16", "STATUS", "status_string",
-           "mamba2_ssd_fwd", "mamba2_ssd_check_args", "mamba2_ssd_supported",
+           "ssd_fwd_timed_ptr", "mamba2_ssd_fwd", "mamba2_ssd_fwd_timed", "mamba2_ssd_check_args",
+           "mamba2_ssd_supported",
            "mamba2_ssd_fwd_workspace_bytes", "mamba2_ssd_workspace_layout_query",
            "mamba2_ssd_status_string", "mamba2_ssd_last_hip_error"]
 
 # The C entry points under their own names (ctypes functions with prototypes).
 mamba2_ssd_fwd = lib.mamba2_ssd_fwd
+mamba2_ssd_fwd_timed = lib.mamba2_ssd_fwd_timed
 mamba2_ssd_check_args = lib.mamba2_ssd_check_args
 mamba2_ssd_supported = lib.mamba2_ssd_supported
 mamba2_ssd_fwd_workspace_bytes = lib.mamba2_ssd_fwd_workspace_bytes
@@ -64,6 +66,16 @@ def ssd_fwd_ptr(dims, io, x, dt, A, B, C, D, init_state, y, final_state, workspa
     """mamba2_ssd_fwd on raw device addresses; raises SsdError on a nonzero status."""
     st = lib.mamba2_ssd_fwd(ctypes.byref(_dims(dims)), io, x, dt, A, B, C, D, init_state, y,
                             final_state, workspace, ws_bytes, stream)
+    if st != 0:
+        raise SsdError(st, lib.mamba2_ssd_last_hip_error().decode())
+
+
+def ssd_fwd_timed_ptr(dims, io, x, dt, A, B, C, D, init_state, y, final_state, workspace, ws_bytes,
+                      stream: int, events) -> None:
+    """mamba2_ssd_fwd_timed on raw addresses; ``events`` holds 5 hipEvent_t handles."""
+    arr = (ctypes.c_void_p * 5)(*events)
+    st = lib.mamba2_ssd_fwd_timed(ctypes.byref(_dims(dims)), io, x, dt, A, B, C, D, init_state, y,
+                                  final_state, workspace, ws_bytes, stream, arr)
     if st != 0:
         raise SsdError(st, lib.mamba2_ssd_last_hip_error().decode())
 

@@ -73,6 +73,9 @@ def _load():
     L.mamba2_ssd_check_args.restype = ctypes.c_int
     L.mamba2_ssd_fwd.argtypes = [dims_p, ctypes.c_int, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, sz, vp]
     L.mamba2_ssd_fwd.restype = ctypes.c_int
+    L.mamba2_ssd_fwd_timed.argtypes = [dims_p, ctypes.c_int, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, sz, vp,
+                                       ctypes.POINTER(ctypes.c_void_p)]
+    L.mamba2_ssd_fwd_timed.restype = ctypes.c_int
     L.mamba2_ssd_status_string.argtypes = [ctypes.c_int]
     L.mamba2_ssd_status_string.restype = ctypes.c_char_p
     L.mamba2_ssd_last_hip_error.argtypes = []

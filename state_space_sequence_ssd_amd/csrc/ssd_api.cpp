@@ -159,6 +159,14 @@ int mamba2_ssd_check_args(const mamba2_ssd_dims* d, int io, const void* x, const
 int mamba2_ssd_fwd(const mamba2_ssd_dims* d, int io, const void* x, const float* dt, const float* A,
                    const void* B, const void* C, const float* D, const float* init_state, void* y,
                    float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+  return mamba2_ssd_fwd_timed(d, io, x, dt, A, B, C, D, init_state, y, final_state, workspace,
+                              workspace_bytes, stream, nullptr);
+}
+
+int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* d, int io, const void* x, const float* dt,
+                         const float* A, const void* B, const void* C, const float* D,
+                         const float* init_state, void* y, float* final_state, void* workspace,
+                         size_t workspace_bytes, void* stream, void* const* events) {
   g_last_hip_error.clear();
   int st = mamba2_ssd_check_args(d, io, x, dt, A, B, C, D, init_state, y, final_state, workspace,
                                  workspace_bytes);
@@ -183,13 +191,19 @@ int mamba2_ssd_fwd(const mamba2_ssd_dims* d, int io, const void* x, const float*
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
   hipError_t err = hipSuccess;
-  if (s.nc > 0) {
-    err = ssd::launch_chunk_cumsum(p, hs);
-    if (err == hipSuccess) err = ssd::launch_chunk_state(p, hs);
-  }
+  auto mark = [&](int i) {
+    if (events && err == hipSuccess) err = hipEventRecord(static_cast<hipEvent_t>(events[i]), hs);
+  };
+  mark(0);
+  if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_cumsum(p, hs);
+  mark(1);
+  if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_state(p, hs);
+  mark(2);
   // with seqlen == 0 the pass runs zero chunks: final_state = init_state (or 0)
   if (err == hipSuccess && (s.nc > 0 || final_state)) err = ssd::launch_state_pass(p, hs);
+  mark(3);
   if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_scan(p, hs);
+  mark(4);
   if (err != hipSuccess) {
     g_last_hip_error = hipGetErrorString(err);
     return MAMBA2_SSD_ERR_HIP;

@@ -27,7 +27,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
-        "mamba2_ssd_check_args", "mamba2_ssd_fwd", "mamba2_ssd_fwd_workspace_bytes",
+        "mamba2_ssd_check_args", "mamba2_ssd_fwd", "mamba2_ssd_fwd_timed", "mamba2_ssd_fwd_workspace_bytes",
         "mamba2_ssd_last_hip_error", "mamba2_ssd_status_string", "mamba2_ssd_supported",
         "mamba2_ssd_workspace_layout_query"])
 
