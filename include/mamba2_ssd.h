@@ -92,14 +92,20 @@ typedef struct {
  *                                      A*dt, times log2(e); padded tokens
  *                                      repeat the last real value
  *   dtt     float [batch][nheads][Tp]  dt transposed, padded tokens 0
+ *   wst     float [batch][nheads][Tp]  dt_t * 2^(G'_last - G'_t), the weight
+ *                                      of token t in its chunk's state
  *   states  float [batch][nheads][nchunks][headdim][dstate]
  *                                      each chunk's own contribution S_k
- *   hprev   float [batch][nheads][nchunks][headdim][dstate]
- *                                      the state entering chunk k             */
+ *   hprev   [batch][nheads][nchunks][headdim][dstate] states h entering
+ *           each chunk; io = F32: float; io = BF16: bf16 pairs, 4 bytes per
+ *           element: for each row and each aligned group of 8 dstate
+ *           columns, the 8 values bf16(h) followed by the 8 values
+ *           bf16(h - bf16(h)), so hi + lo carries h to about 16 bits        */
 typedef struct {
   size_t total_bytes;
   size_t gcum_offset;
   size_t dtt_offset;
+  size_t wst_offset;
   size_t states_offset;
   size_t hprev_offset;
   int64_t nchunks;

@@ -31,7 +31,8 @@ class Dims(ctypes.Structure):
 class WorkspaceLayout(ctypes.Structure):
     """mamba2_ssd_workspace_layout"""
     _fields_ = [("total_bytes", ctypes.c_size_t), ("gcum_offset", ctypes.c_size_t),
-                ("dtt_offset", ctypes.c_size_t), ("states_offset", ctypes.c_size_t),
+                ("dtt_offset", ctypes.c_size_t), ("wst_offset", ctypes.c_size_t),
+                ("states_offset", ctypes.c_size_t),
                 ("hprev_offset", ctypes.c_size_t), ("nchunks", ctypes.c_int64)]
 
 

@@ -7,7 +7,10 @@
 // [chunk tokens][32 heads] is read with whole 128-byte rows, scanned per
 // head through LDS, and written transposed, [batch][head][token], so the
 // consumers read each head's decays contiguously (the blog's "GMEM layout"
-// point, done here once for both consumers). dt is also written transposed.
+// point, done here once for both consumers). Three arrays come out, all
+// head-major: dt itself, G' (the scaled cumsum) and the chunk-state weight
+// w_t = dt_t * 2^(G'_last - G'_t) <= dt_t that ssd_chunk_state multiplies into
+// x (G'_last is the chunk's last G', known here once the scan is done).
 //
 // Monotonicity. Each head's chunk is split into 8 segments of Q/8 tokens.
 // A thread sums its segment sequentially; segment prefixes are then chained
@@ -32,10 +35,13 @@ __global__ __launch_bounds__(256) void ssd_chunk_cumsum(const float* __restrict_
                                                         const float* __restrict__ A,
                                                         float* __restrict__ gcum,
                                                         float* __restrict__ dtt,
+                                                        float* __restrict__ wst,
                                                         int64_t T, int H, int64_t Tp) {
   constexpr int SL = Q / kSeg;
   __shared__ float s_t[Q][kHB + 1];   // dt tile, then the scaled cumsum in place
+  __shared__ float s_w[Q][kHB + 1];   // state weights
   __shared__ float s_pre[kSeg][kHB];
+  __shared__ float s_lastloc[kHB];
 
   const int k = blockIdx.x;
   const int h0 = blockIdx.y * kHB;
@@ -68,6 +74,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_cumsum(const float* __restrict_
     loc[i] = run;
   }
   s_pre[seg][hh] = run;
+  if (seg == kSeg - 1) s_lastloc[hh] = run;
   __syncthreads();   // also orders the dtt reads of s_t before it is overwritten
   if (seg == 0) {
     float p = 0.f;
@@ -80,13 +87,24 @@ __global__ __launch_bounds__(256) void ssd_chunk_cumsum(const float* __restrict_
   }
   __syncthreads();
   const float pre = s_pre[seg][hh];
+  // G'_last: the last segment's prefix plus its last local sum, times log2 e
+  const float glast = (s_pre[kSeg - 1][hh] + s_lastloc[hh]) * kLog2e;
 #pragma unroll
-  for (int i = 0; i < SL; ++i) s_t[seg * SL + i][hh] = (pre + loc[i]) * kLog2e;
+  for (int i = 0; i < SL; ++i) {
+    const int t = seg * SL + i;
+    const float gv = (pre + loc[i]) * kLog2e;
+    s_w[t][hh] = s_t[t][hh] * exp2_hw(glast - gv);
+    s_t[t][hh] = gv;
+  }
   __syncthreads();
 
   for (int idx = tid; idx < Q * kHB; idx += 256) {
     const int hl = idx / Q, t = idx % Q;
-    if (h0 + hl < H) gcum[(b * H + h0 + hl) * Tp + t0 + t] = s_t[t][hl];
+    if (h0 + hl < H) {
+      const int64_t o = (b * H + h0 + hl) * Tp + t0 + t;
+      gcum[o] = s_t[t][hl];
+      wst[o] = s_w[t][hl];
+    }
   }
 }
 
@@ -97,13 +115,13 @@ hipError_t launch_chunk_cumsum(const Problem& p, hipStream_t stream) {
   const dim3 block(256);
   switch (p.Q) {
     case 64:
-      hipLaunchKernelGGL(ssd_chunk_cumsum<64>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.T, (int)p.H, p.Tp);
+      hipLaunchKernelGGL(ssd_chunk_cumsum<64>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp);
       break;
     case 128:
-      hipLaunchKernelGGL(ssd_chunk_cumsum<128>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.T, (int)p.H, p.Tp);
+      hipLaunchKernelGGL(ssd_chunk_cumsum<128>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp);
       break;
     case 256:
-      hipLaunchKernelGGL(ssd_chunk_cumsum<256>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.T, (int)p.H, p.Tp);
+      hipLaunchKernelGGL(ssd_chunk_cumsum<256>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp);
       break;
     default:
       return hipErrorInvalidValue;

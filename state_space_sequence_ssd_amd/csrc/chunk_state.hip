@@ -1,7 +1,7 @@
 // ssd_chunk_state: each chunk's own contribution to the state,
 //
 //   S_k[p, n] = sum_{t in chunk k} x[t, p] * w_t * B[t, n],
-//   w_t = dt_t * 2^(G'_last - G'_t)
+//   w_t = dt_t * 2^(G'_last - G'_t)   (computed by ssd_chunk_cumsum)
 //
 // i.e. (exp(G_last - G) o dt o B)^T X of the CUDA Tile Mamba-2 blog's jump
 // formula (section "Mamba-2 architecture"; the MMA in "Kernel 2:
@@ -10,7 +10,8 @@
 //
 // One wave computes one (batch, head, chunk) tile's rows of one headdim
 // column group against NGW dstate column groups with 32x32 MFMAs; the
-// contraction runs over the chunk's tokens in steps of 2*KPL. The scale w_t
+// contraction runs over the chunk's tokens in steps of 2*KPL, with the next
+// step's loads issued before this step's MFMAs. The scale w_t
 // is applied to x (w and x are both per head, while B is shared by the
 // heads of a group). With bf16 io the product w*x is not a bf16 number, so
 // it enters the MFMA as a bf16 (hi, lo) pair in two MFMAs against the exact
@@ -36,20 +37,20 @@ struct StateCfg {
   static constexpr int CG = 32 * E;                 // columns per column group
   static constexpr int NPG = P / CG;                // headdim column groups
   static constexpr int NNG = N / CG;                // dstate column groups
-  static constexpr int NGW = (E == 2) ? (NNG < 2 ? NNG : 2) : NNG;   // dstate groups per wave
+  // dstate groups per wave: one 32x32 block pair set per wave (64 fp32
+  // accumulators) unless that needs more than 8 waves per tile
+  static constexpr int NGW = (NPG * NNG > 8) ? (NPG * NNG) / 8 : 1;
   static constexpr int NGS = NNG / NGW;
   static constexpr int WPT = NPG * NGS;             // waves per (b, h, chunk) tile
-  static constexpr int TPW = 4 / WPT;               // tiles per 256-thread workgroup
-  static_assert(WPT >= 1 && WPT <= 4 && 4 % WPT == 0, "tile does not fit a workgroup");
+  static constexpr int TPW = WPT >= 4 ? 1 : 4 / WPT;   // tiles per workgroup
+  static constexpr int THREADS = 64 * WPT * TPW;
+  static_assert(WPT >= 1 && WPT <= 8, "tile does not fit a workgroup");
 };
 
 template <typename T, int P, int N, int Q>
-__global__ __launch_bounds__(256) void ssd_chunk_state(const T* __restrict__ x,
-                                                       const T* __restrict__ Bm,
-                                                       const float* __restrict__ gcum,
-                                                       const float* __restrict__ dtt,
-                                                       float* __restrict__ states,
-                                                       int64_t Tlen, int H, int G, int64_t nc, int64_t Tp) {
+__global__ __launch_bounds__((StateCfg<T, P, N>::THREADS)) void ssd_chunk_state(
+    const T* __restrict__ x, const T* __restrict__ Bm, const float* __restrict__ wst,
+    float* __restrict__ states, int64_t Tlen, int H, int G, int64_t nc, int64_t Tp) {
   using I = Io<T>;
   using Cfg = StateCfg<T, P, N>;
   constexpr int E = I::E, KPL = I::KPL, CG = Cfg::CG, NGW = Cfg::NGW, NGS = Cfg::NGS;
@@ -67,15 +68,40 @@ __global__ __launch_bounds__(256) void ssd_chunk_state(const T* __restrict__ x,
   const int grp = h / (H / G);
   const int64_t t0 = (int64_t)k * Q;
 
-  const float* gc = gcum + ((int64_t)b * H + h) * Tp + t0;
-  const float* dtc = dtt + ((int64_t)b * H + h) * Tp + t0;
-  const float glast = gc[Q - 1];
-
+  const float* wc = wst + ((int64_t)b * H + h) * Tp + t0;
   // dword views: x row stride H*P elements, B row stride G*N elements
   const int64_t xstride = (int64_t)H * P / E, bstride = (int64_t)G * N / E;
   const uint32_t* xb = reinterpret_cast<const uint32_t*>(x + ((b * Tlen + t0) * H + h) * P + pg * CG) + m;
   const uint32_t* bb = reinterpret_cast<const uint32_t*>(Bm + ((b * Tlen + t0) * G + grp) * N + ng0 * CG) + m;
   const int64_t nvalid = Tlen - t0;   // tokens of this chunk inside the sequence
+
+  // one k-step's operands: KPL token rows of x and B (one dword each), KPL weights
+  struct Step {
+    uint32_t xd[KPL];
+    uint32_t bd[NGW][KPL];
+    float w[KPL];
+  };
+  auto load = [&](int s, Step& st) {
+    const int tb = s * 2 * KPL + KPL * g;   // first of this lane half's KPL tokens
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+      const int t = tb + i;
+      const bool valid = t < nvalid;
+      st.xd[i] = valid ? xb[t * xstride] : 0u;
+#pragma unroll
+      for (int j = 0; j < NGW; ++j) st.bd[j][i] = valid ? bb[t * bstride + j * (CG / E)] : 0u;
+    }
+    if constexpr (KPL % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < KPL; i += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(wc + tb + i);
+        st.w[i] = v.x; st.w[i + 1] = v.y; st.w[i + 2] = v.z; st.w[i + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) st.w[i] = wc[tb + i];
+    }
+  };
 
   f32x16 acc[E][NGW][E];
 #pragma unroll
@@ -85,40 +111,31 @@ __global__ __launch_bounds__(256) void ssd_chunk_state(const T* __restrict__ x,
 #pragma unroll
       for (int c = 0; c < E; ++c) acc[a][j][c] = f32x16{};
 
-#pragma unroll 2
+  Step cur, nxt;
+  load(0, cur);
+#pragma unroll (KPL == 1 ? 8 : KSTEPS)
   for (int s = 0; s < KSTEPS; ++s) {
-    const int tb = s * 2 * KPL + KPL * g;   // first of this lane half's KPL tokens
-    float w[KPL];
-    uint32_t xd[KPL];
-    uint32_t bd[NGW][KPL];
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      const int t = tb + i;
-      const bool valid = t < nvalid;
-      w[i] = dtc[t] * exp2_hw(glast - gc[t]);
-      xd[i] = valid ? xb[t * xstride] : 0u;
-#pragma unroll
-      for (int j = 0; j < NGW; ++j) bd[j][i] = valid ? bb[t * bstride + j * (CG / E)] : 0u;
-    }
+    if (s + 1 < KSTEPS) load(s + 1, nxt);   // in flight while this step's MFMAs run
     typename I::Frag ahi[E], alo[E];
 #pragma unroll
     for (int pe = 0; pe < E; ++pe) {
       float v[KPL];
 #pragma unroll
-      for (int i = 0; i < KPL; ++i) v[i] = w[i] * I::elem(xd[i], pe);
+      for (int i = 0; i < KPL; ++i) v[i] = cur.w[i] * I::elem(cur.xd[i], pe);
       I::split(v, ahi[pe], alo[pe]);
     }
 #pragma unroll
     for (int j = 0; j < NGW; ++j)
 #pragma unroll
       for (int ne = 0; ne < E; ++ne) {
-        const typename I::Frag bf = I::from_dwords(bd[j], ne);   // B is exact in the io dtype
+        const typename I::Frag bf = I::from_dwords(cur.bd[j], ne);   // B is exact in the io dtype
 #pragma unroll
         for (int pe = 0; pe < E; ++pe) {
           I::mma(acc[pe][j][ne], ahi[pe], bf);
           if constexpr (I::SPLIT) I::mma(acc[pe][j][ne], alo[pe], bf);
         }
       }
+    cur = nxt;
   }
 
   // S[p][n]: D row r -> p = pg*CG + E*drow(r, g) + pe, col -> n = (ng0+j)*CG + E*m + ne
@@ -140,10 +157,10 @@ __global__ __launch_bounds__(256) void ssd_chunk_state(const T* __restrict__ x,
 
 template <typename T, int P, int N, int Q>
 hipError_t launch_one(const Problem& p, hipStream_t stream) {
-  constexpr int TPW = StateCfg<T, P, N>::TPW;
-  const dim3 grid((unsigned)((p.H + TPW - 1) / TPW), (unsigned)p.nc, (unsigned)p.bt);
-  hipLaunchKernelGGL((ssd_chunk_state<T, P, N, Q>), grid, dim3(256), 0, stream, (const T*)p.x, (const T*)p.B,
-                     p.gcum, p.dtt, p.states, p.T, (int)p.H, (int)p.G, p.nc, p.Tp);
+  using Cfg = StateCfg<T, P, N>;
+  const dim3 grid((unsigned)((p.H + Cfg::TPW - 1) / Cfg::TPW), (unsigned)p.nc, (unsigned)p.bt);
+  hipLaunchKernelGGL((ssd_chunk_state<T, P, N, Q>), grid, dim3(Cfg::THREADS), 0, stream, (const T*)p.x,
+                     (const T*)p.B, p.wst, p.states, p.T, (int)p.H, (int)p.G, p.nc, p.Tp);
   return hipGetLastError();
 }
 

@@ -80,6 +80,8 @@ void layout_of(const mamba2_ssd_dims* d, const Sizes& s, mamba2_ssd_workspace_la
   off = align_up(off + bh * (size_t)s.Tp * 4);
   L->dtt_offset = off;
   off = align_up(off + bh * (size_t)s.Tp * 4);
+  L->wst_offset = off;
+  off = align_up(off + bh * (size_t)s.Tp * 4);
   L->states_offset = off;
   off = align_up(off + (size_t)s.n_chunkstates * 4);
   L->hprev_offset = off;
@@ -186,8 +188,9 @@ int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* d, int io, const void* x, const 
   p.init = init_state; p.y = y; p.final_state = final_state;
   p.gcum = reinterpret_cast<float*>(ws + L.gcum_offset);
   p.dtt = reinterpret_cast<float*>(ws + L.dtt_offset);
+  p.wst = reinterpret_cast<float*>(ws + L.wst_offset);
   p.states = reinterpret_cast<float*>(ws + L.states_offset);
-  p.hprev = reinterpret_cast<float*>(ws + L.hprev_offset);
+  p.hprev = ws + L.hprev_offset;
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
   hipError_t err = hipSuccess;

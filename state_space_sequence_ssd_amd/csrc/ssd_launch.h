@@ -22,8 +22,9 @@ struct Problem {
   float* final_state;            // may be null (not written)
   float* gcum;                   // workspace: [bt][H][Tp]
   float* dtt;                    // workspace: [bt][H][Tp]
+  float* wst;                    // workspace: [bt][H][Tp]
   float* states;                 // workspace: [bt][H][nc][P][N]
-  float* hprev;                  // workspace: [bt][H][nc][P][N]
+  void* hprev;                   // workspace: [bt][H][nc][P][N] fp32, or bf16 (hi, lo) pairs
 };
 
 // Each launcher enqueues one kernel on `stream` and returns the launch status.

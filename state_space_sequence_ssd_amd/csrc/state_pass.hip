@@ -11,10 +11,15 @@
 // independent chain, so the grid is (batch*head, state/1024) and each thread
 // carries 4 consecutive state elements through all chunks in fp32
 // registers. The kernel is pure streaming: S is read once and hprev written
-// once, both fp32 (the output kernel splits hprev into a bf16 pair for its
-// MFMA, so the carried state keeps fp32 accuracy); loads for later chunks are
-// issued ahead of the dependent FMAs so each thread keeps several 16-byte
-// reads in flight.
+// once; loads for later chunks are issued ahead of the dependent FMAs so each
+// thread keeps several 16-byte reads in flight.
+//
+// hprev format. With fp32 io, hprev is the fp32 state. With bf16 io it is
+// stored as ready-made MFMA operand pairs: the fp32 state h is split as
+// hi = bf16(h), lo = bf16(h - hi), and for every row p and every aligned
+// group of 8 dstate columns the 8 hi values are followed by the 8 lo values
+// (32 bytes, the same size as the fp32 values). The output kernel then loads
+// a lane's hi and lo fragments with two 16-byte reads and no conversion.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -24,10 +29,34 @@ namespace {
 
 constexpr int kDepth = 4;   // chunks whose S loads are in flight per thread
 
+template <typename T>
+__device__ __forceinline__ void store_hprev(void* hp, int64_t chunk_off, int e, const float4& h);
+
+template <>
+__device__ __forceinline__ void store_hprev<float>(void* hp, int64_t chunk_off, int e, const float4& h) {
+  *reinterpret_cast<float4*>(static_cast<float*>(hp) + chunk_off + e) = h;
+}
+
+template <>
+__device__ __forceinline__ void store_hprev<bf16>(void* hp, int64_t chunk_off, int e, const float4& h) {
+  // element e (a multiple of 4) sits in group e/8 at position e%8 (0 or 4)
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const uint32_t h01 = pack_bf16x2(h.x, h.y), h23 = pack_bf16x2(h.z, h.w);
+  u32x2 hi, lo;
+  hi[0] = h01;
+  hi[1] = h23;
+  lo[0] = pack_bf16x2(h.x - bf16lo(h01), h.y - bf16hi(h01));
+  lo[1] = pack_bf16x2(h.z - bf16lo(h23), h.w - bf16hi(h23));
+  bf16* base = static_cast<bf16*>(hp) + 2 * chunk_off + (e / 8) * 16 + (e % 8);
+  *reinterpret_cast<u32x2*>(base) = hi;
+  *reinterpret_cast<u32x2*>(base + 8) = lo;
+}
+
+template <typename T>
 __global__ __launch_bounds__(256) void ssd_state_pass(const float* __restrict__ states,
                                                       const float* __restrict__ gcum,
                                                       const float* init,            // may equal final_state
-                                                      float* __restrict__ hprev,
+                                                      void* __restrict__ hprev,
                                                       float* final_state,
                                                       int nc, int Q, int64_t Tp, int PN) {
   const int64_t bh = blockIdx.x;
@@ -37,7 +66,7 @@ __global__ __launch_bounds__(256) void ssd_state_pass(const float* __restrict__ 
   if (init) h = *reinterpret_cast<const float4*>(init + bh * PN + e);
 
   const float* sp = states + bh * (int64_t)nc * PN + e;
-  float* hp = hprev + bh * (int64_t)nc * PN + e;
+  const int64_t hbase = bh * (int64_t)nc * PN;
   const float* glast = gcum + bh * Tp + (Q - 1);
 
   float4 buf[kDepth];
@@ -52,7 +81,7 @@ __global__ __launch_bounds__(256) void ssd_state_pass(const float* __restrict__ 
       if (k < nc) {
         const float4 s = buf[i];
         if (k + kDepth < nc) buf[i] = *reinterpret_cast<const float4*>(sp + (int64_t)(k + kDepth) * PN);
-        *reinterpret_cast<float4*>(hp + (int64_t)k * PN) = h;
+        store_hprev<T>(hprev, hbase + (int64_t)k * PN, e, h);
         const float sc = exp2_hw(glast[(int64_t)k * Q]);
         h.x = fmaf(sc, h.x, s.x);
         h.y = fmaf(sc, h.y, s.y);
@@ -70,8 +99,12 @@ hipError_t launch_state_pass(const Problem& p, hipStream_t stream) {
   const int PN = (int)(p.P * p.N);
   const dim3 grid((unsigned)(p.bt * p.H), (unsigned)(PN / 1024));
   const dim3 block(256);
-  hipLaunchKernelGGL(ssd_state_pass, grid, block, 0, stream, p.states, p.gcum, p.init, p.hprev,
-                     p.final_state, (int)p.nc, (int)p.Q, p.Tp, PN);
+  if (p.io == 1)
+    hipLaunchKernelGGL(ssd_state_pass<bf16>, grid, block, 0, stream, p.states, p.gcum, p.init, p.hprev,
+                       p.final_state, (int)p.nc, (int)p.Q, p.Tp, PN);
+  else
+    hipLaunchKernelGGL(ssd_state_pass<float>, grid, block, 0, stream, p.states, p.gcum, p.init, p.hprev,
+                       p.final_state, (int)p.nc, (int)p.Q, p.Tp, PN);
   return hipGetLastError();
 }
 

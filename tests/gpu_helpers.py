@@ -71,11 +71,19 @@ def workspace_views(ws, L, dims, io):
         nbytes = count * torch.tensor([], dtype=dtype).element_size()
         return ws[off:off + nbytes].view(dtype)
 
+    if io == BF16:
+        # (hi, lo) bf16 pairs: per row, per aligned group of 8 columns, 8 hi then 8 lo
+        pairs = view(L.hprev_offset, bt * H * nc * P * N * 2, torch.bfloat16).float()
+        pairs = pairs.view(bt, H, nc, P, N // 8, 2, 8)
+        hprev = (pairs[..., 0, :] + pairs[..., 1, :]).reshape(bt, H, nc, P, N)
+    else:
+        hprev = view(L.hprev_offset, bt * H * nc * P * N, torch.float32).view(bt, H, nc, P, N)
     return {
         "gcum": view(L.gcum_offset, bt * H * Tp, torch.float32).view(bt, H, Tp),
         "dtt": view(L.dtt_offset, bt * H * Tp, torch.float32).view(bt, H, Tp),
+        "wst": view(L.wst_offset, bt * H * Tp, torch.float32).view(bt, H, Tp),
         "states": view(L.states_offset, bt * H * nc * P * N, torch.float32).view(bt, H, nc, P, N),
-        "hprev": view(L.hprev_offset, bt * H * nc * P * N, torch.float32).view(bt, H, nc, P, N),
+        "hprev": hprev,
     }
 
 

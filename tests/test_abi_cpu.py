@@ -56,11 +56,12 @@ def test_workspace_layout_headline():
     assert L.nchunks == nc
     assert L.gcum_offset == 0
     assert L.dtt_offset == 4 * 80 * 8192 * 4
-    assert L.states_offset == 2 * 4 * 80 * 8192 * 4
+    assert L.wst_offset == 2 * 4 * 80 * 8192 * 4
+    assert L.states_offset == 3 * 4 * 80 * 8192 * 4
     states = 4 * 80 * nc * 64 * 128 * 4
     assert L.hprev_offset == L.states_offset + states
     assert L.total_bytes == L.hprev_offset + states          # hprev is fp32 for every io dtype
-    for off in (L.gcum_offset, L.dtt_offset, L.states_offset, L.hprev_offset, L.total_bytes):
+    for off in (L.gcum_offset, L.dtt_offset, L.wst_offset, L.states_offset, L.hprev_offset, L.total_bytes):
         assert off % 256 == 0
     assert ssd.workspace_bytes(HEADLINE, BF16) == L.total_bytes
     assert ssd.workspace_bytes(HEADLINE, F32) == L.total_bytes

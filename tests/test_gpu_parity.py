@@ -53,6 +53,16 @@ def test_small_variant_parity(name):
     dtt = v["dtt"].cpu().numpy()
     assert np.array_equal(dtt[:, :, :T], np.transpose(inp["dt"], (0, 2, 1))), "dtt"
     assert np.all(dtt[:, :, T:] == 0)
+    # state weights: dt_t * exp(G_last - G_t) of the chunk. G' is fp32, so the
+    # exponent G'_last - G'_t carries an absolute error of a few ulp(|G'|):
+    # the bound on w is relative, growing with the magnitudes involved.
+    Gr = inter["G"].reshape(cfg.batch, cfg.nheads, L.nchunks, cfg.chunk)
+    dtp = np.zeros((cfg.batch, cfg.nheads, Tp))
+    dtp[:, :, :T] = np.transpose(inp["dt"], (0, 2, 1))
+    wref = (dtp.reshape(Gr.shape) * np.exp(Gr[..., -1:] - Gr)).reshape(dtp.shape)
+    gmag = (np.abs(Gr[..., -1:]) + np.abs(Gr)).reshape(dtp.shape) * LOG2E
+    wg = host(v["wst"])
+    assert np.all(np.abs(wg - wref) <= (1e-5 + 8 * 2.0 ** -24 * gmag) * np.abs(wref) + 1e-30), "wst"
     # monotone within each chunk: every kept exponent is <= 0 exactly
     gc = v["gcum"].cpu().numpy().reshape(cfg.batch, cfg.nheads, L.nchunks, cfg.chunk)
     assert np.all(np.diff(gc, axis=-1) <= 0) and np.all(gc <= 0)
