@@ -105,6 +105,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="mamba2-2.7b")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device-to-device copy, a dispatch of known size that "
+                         "HBM byte counters (FETCH_SIZE, WRITE_SIZE) can be scaled against")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
@@ -148,6 +151,13 @@ def main():
 
     def step(evs):
         ssd.ssd_fwd_timed_ptr(dims, io, *ptrs, stream.cuda_stream, [e.cuda_event for e in evs])
+
+    if args.copy_calibration:
+        src_buf = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)   # 256 MiB
+        dst_buf = torch.empty_like(src_buf)
+        dst_buf.copy_(src_buf)
+        torch.cuda.synchronize()
+        del src_buf, dst_buf
 
     warm = new_events()
     for _ in range(args.warmup):

@@ -64,41 +64,26 @@ struct ScanCfg {
   static constexpr int NPS = NPG / PGW;
   static constexpr int WAVES = NTG * NPS;
   static constexpr int THREADS = 64 * WAVES;
-  // j-block staging through LDS with direct global->LDS loads (16 bytes per
-  // lane, lane i of a wave-instruction lands at base + 16 i): a block is the
-  // 32 B rows followed by the 32 x rows, in 16-byte pieces.
+  // j-block staging: direct global->LDS loads, 16 bytes per lane, lane i of
+  // a wave-instruction landing at base + 16 i. A block holds its 32 B rows
+  // padded to RB+1 pieces (16 bytes each) and its 32 x rows padded to RX+2
+  // pieces; pad pieces receive a copy of a real piece and are never read.
+  // With those strides the 16 lanes of a 16-byte B fragment read (rows
+  // m..m+15) and the two half-waves of a dword x read (rows j and j+4) fall
+  // on distinct LDS banks, and every read address is a per-lane base plus a
+  // compile-time offset.
   static constexpr int RB = N * (int)sizeof(T) / 16;    // pieces per B row
   static constexpr int RX = P * (int)sizeof(T) / 16;    // pieces per x row
-  static constexpr int IB = 32 * RB / 64, IX = 32 * RX / 64;   // wave-instructions per block
-  static constexpr int LB = (IB + WAVES - 1) / WAVES, LX = (IX + WAVES - 1) / WAVES;
-  static constexpr int LOADS = LB + LX;                 // per wave per block
-  static constexpr int BBYTES = 32 * RB * 16, XBYTES = 32 * RX * 16;
+  static constexpr int BROWP = RB + 1, XROWP = RX + 2;  // padded row strides, in pieces
+  static constexpr int IB = (32 * BROWP + 63) / 64, IX = (32 * XROWP + 63) / 64;   // wave-instructions
+  static constexpr int ITOT = IB + IX;
+  static constexpr int LOADS = (ITOT + WAVES - 1) / WAVES;   // per wave per block (spares repeat)
+  static constexpr int BBYTES = IB * 1024, XBYTES = IX * 1024;
   static constexpr int BLOCK = BBYTES + XBYTES;
   static constexpr int NBUF = BLOCK <= 16384 ? 4 : 3;   // blocks in the LDS ring
   static_assert(NTB % TBW == 0 && NPG % PGW == 0, "tile split");
   static_assert(WAVES >= 1 && WAVES <= 8, "tile does not fit a workgroup");
-  static_assert(RB >= 8 && RX >= 8, "row narrower than the swizzle");
 };
-
-// LDS placement (in 16-byte pieces) of B row m, piece c: the piece index is
-// XORed with a row-dependent value so that the 16 lanes of one 16-byte
-// fragment read (rows m..m+15, same piece) hit 16 different bank groups.
-template <int RB>
-__device__ __forceinline__ int bslot(int m, int c) {
-  const int f = RB >= 16 ? (m & 15) : ((m >> 1) & (RB - 1));
-  return m * RB + (c ^ f);
-}
-// x rows: the two half-waves read rows j and j+4 of the same columns; rows
-// with bit 2 set are moved to the other half of the banks (for 8-piece rows
-// by swapping row parity, for wider rows by XORing the piece with 8).
-template <int RX>
-__device__ __forceinline__ int xslot(int j, int c) {
-  const int b2 = (j >> 2) & 1;
-  if constexpr (RX == 8)
-    return (j ^ b2) * 8 + c;
-  else
-    return j * RX + (c ^ (b2 << 3));
-}
 
 // Wait until at most VM vector-memory operations of this wave are in flight
 // and its LDS operations are done, then meet the workgroup at the barrier.
@@ -108,36 +93,37 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
-// Direct global->LDS loads of j-block jb (B rows, then x rows) into one ring
-// slot. Every wave issues LB + LX 16-byte-per-lane loads; instruction kk
-// fills LDS bytes [kk*1024, kk*1024 + 1024) of its part, lane i the 16 bytes
-// at kk*1024 + 16 i, so the global piece each lane fetches is chosen to
-// realise the swizzled placement of bslot / xslot. Rows past the sequence are
-// clamped to its last row (a valid address); their products are masked out by
-// the caller. `wave` must be wave-uniform (it feeds the LDS address in M0).
+// Direct global->LDS loads of j-block jb into one ring slot: LOADS
+// wave-instructions per wave; instruction kk (0 <= kk < ITOT) fills bytes
+// [kk*1024, kk*1024 + 1024) of the slot, lane i the 16 bytes at kk*1024 +
+// 16 i, so each lane fetches the global piece that belongs at its slot.
+// Rows past the sequence are clamped to its last row (a valid address): those
+// tokens have dt = 0 in the workspace, which zeroes their products. `wave`
+// must be wave-uniform (it feeds the LDS address in M0).
 template <typename Cfg, typename T>
 __device__ __forceinline__ void issue_block(unsigned char* slot_base, const T* bbase, const T* xbase,
                                             int64_t brow, int64_t xrow, int jb, int nvalid, int wave, int lane) {
-  constexpr int RB = Cfg::RB, RX = Cfg::RX, EPC = 16 / (int)sizeof(T);
+  constexpr int EPC = 16 / (int)sizeof(T);
 #pragma unroll
-  for (int i = 0; i < Cfg::LB; ++i) {
-    const int kk = (wave + i * Cfg::WAVES) % Cfg::IB;   // spare instructions repeat a piece
-    const int s = kk * 64 + lane;
-    const int mr = s / RB, pc = s % RB;
-    const int f = RB >= 16 ? (mr & 15) : ((mr >> 1) & (RB - 1));
-    const int row = min(jb * 32 + mr, nvalid - 1);
-    __builtin_amdgcn_global_load_lds(bbase + row * brow + (pc ^ f) * EPC, slot_base + kk * 1024, 16, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < Cfg::LX; ++i) {
-    const int kk = (wave + i * Cfg::WAVES) % Cfg::IX;
-    const int s = kk * 64 + lane;
-    const int pr = s / RX, pc = s % RX;
-    const int b2 = (pr >> 2) & 1;
-    const int jr = RX == 8 ? (pr ^ b2) : pr;
-    const int c = RX == 8 ? pc : (pc ^ (b2 << 3));
-    const int row = min(jb * 32 + jr, nvalid - 1);
-    __builtin_amdgcn_global_load_lds(xbase + row * xrow + c * EPC, slot_base + Cfg::BBYTES + kk * 1024, 16, 0, 0);
+  for (int i = 0; i < Cfg::LOADS; ++i) {
+    const int kk = (wave + i * Cfg::WAVES) % Cfg::ITOT;   // spare instructions repeat one
+    if (kk < Cfg::IB) {
+      const int s = kk * 64 + lane;
+      int r = s / Cfg::BROWP, c = s % Cfg::BROWP;
+      if (r >= 32) r = 31;            // tail of the last instruction
+      if (c >= Cfg::RB) c = 0;        // pad piece
+      const int row = min(jb * 32 + r, nvalid - 1);
+      __builtin_amdgcn_global_load_lds(bbase + row * brow + c * EPC, slot_base + kk * 1024, 16, 0, 0);
+    } else {
+      const int kx = kk - Cfg::IB;
+      const int s = kx * 64 + lane;
+      int r = s / Cfg::XROWP, c = s % Cfg::XROWP;
+      if (r >= 32) r = 31;
+      if (c >= Cfg::RX) c = 0;
+      const int row = min(jb * 32 + r, nvalid - 1);
+      __builtin_amdgcn_global_load_lds(xbase + row * xrow + c * EPC, slot_base + Cfg::BBYTES + kx * 1024, 16,
+                                       0, 0);
+    }
   }
 }
 
@@ -152,14 +138,15 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
   using Cfg = ScanCfg<T, P, N, Q>;
   constexpr int E = I::E, KPL = I::KPL, CG = Cfg::CG, NTB = Cfg::NTB, TBW = Cfg::TBW;
   constexpr int PGW = Cfg::PGW, NPS = Cfg::NPS, WAVES = Cfg::WAVES;
-  constexpr int RB = Cfg::RB, RX = Cfg::RX, NBUF = Cfg::NBUF, LOADS = Cfg::LOADS;
+  constexpr int NBUF = Cfg::NBUF, LOADS = Cfg::LOADS;
+  constexpr int BRB = Cfg::BROWP * 16, XRB = Cfg::XROWP * 16;   // padded row bytes
   constexpr int KS = N / (2 * KPL);    // MFMA steps over dstate
   constexpr int JS = 32 / (2 * KPL);   // MFMA steps over a 32-token j-block
-  constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte piece
 
   __shared__ __attribute__((aligned(16))) unsigned char ring[NBUF][Cfg::BLOCK];
   __shared__ __attribute__((aligned(16))) float sG[Q];
   __shared__ __attribute__((aligned(16))) float sDt[Q];
+  __shared__ __attribute__((aligned(16))) float sW[Q];   // dt_j * 2^(G'_end(block of j) - G'_j) <= dt_j
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
@@ -194,8 +181,10 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
     for (int s = 0; s < KS; ++s) cf[u][s] = I::load_row(cbase + t * brow + s * 2 * KPL + KPL * g, valid);
   }
   for (int i = tid; i < Q; i += 64 * WAVES) {
-    sG[i] = gc[i];
-    sDt[i] = dtc[i];
+    const float gi = gc[i], di = dtc[i];
+    sG[i] = gi;
+    sDt[i] = di;
+    sW[i] = di * exp2_hw(gc[(i | 31)] - gi);   // exponent <= 0: the block's last G' is its smallest
   }
 
   // 2. carried state: acc[u][q][pe] = C . Hprev^T, col -> p = (pg0+q)*CG + E*m + pe
@@ -236,7 +225,7 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
   for (int i = 0; i < NBUF - 1; ++i)
     if (i < NTB) issue_block<Cfg>(ring[i], bbase, xbase, brow, xrow, i, nvalid, wave, lane);
 
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // sG, sDt visible
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // sG, sDt, sW visible
 #pragma unroll
   for (int u = 0; u < TBW; ++u)
 #pragma unroll
@@ -255,6 +244,10 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
   const float Dh = Dp[h];
   int tmax = tbs[0];
   if constexpr (TBW == 2) tmax = tbs[1];
+  // per-lane LDS read bases: B fragment rows m (16-byte pieces 2s+g), x dword
+  // rows drow(., g) (column (pg0+q)*CG + E*m)
+  const int boff = m * BRB + g * 16 * (KPL == 8 ? 1 : 0) + (KPL == 8 ? 0 : g * 4);
+  const int xoff = 4 * g * XRB + (pg0 * CG + E * m) * (int)sizeof(T);
 
   for (int jb = 0; jb < NTB; ++jb) {
     // block jb has landed once at most (blocks issued after it) x LOADS remain
@@ -266,11 +259,32 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
       issue_block<Cfg>(ring[(jb + NBUF - 1) % NBUF], bbase, xbase, brow, xrow, jb + NBUF - 1, nvalid, wave, lane);
     if (jb > tmax) continue;
 
-    const unsigned char* sb = ring[jb % NBUF];
-    const unsigned char* sx = sb + Cfg::BBYTES;
+    const unsigned char* sb = ring[jb % NBUF] + boff;
+    const unsigned char* sx = ring[jb % NBUF] + Cfg::BBYTES + xoff;
     const int j0 = jb * 32;
-    const float* gjb = sG + j0;
-    const float* djb = sDt + j0;
+    // this lane half's 16 j rows are rows drow(q, g) of the block (D row order)
+    float wj[16];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float4 wv = *reinterpret_cast<const float4*>(&sW[j0 + 8 * c + 4 * g]);
+      wj[4 * c + 0] = wv.x; wj[4 * c + 1] = wv.y; wj[4 * c + 2] = wv.z; wj[4 * c + 3] = wv.w;
+    }
+    // x fragments (exact in the io dtype), contraction index in the same j order
+    Frag xf[PGW][E][JS];
+#pragma unroll
+    for (int q = 0; q < PGW; ++q)
+#pragma unroll
+      for (int js = 0; js < JS; ++js) {
+        uint32_t d[KPL];
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) {
+          const int q2 = js * KPL + i;   // drow(q2, g) = 8*(q2/4) + 4g + q2%4; the 4g is in xoff
+          d[i] = *reinterpret_cast<const uint32_t*>(sx + (8 * (q2 / 4) + q2 % 4) * XRB + q * CG * (int)sizeof(T));
+        }
+#pragma unroll
+        for (int pe = 0; pe < E; ++pe) xf[q][pe][js] = I::from_dwords(d, pe);
+      }
+    const float gend = sG[j0 + 31];
 #pragma unroll
     for (int u = 0; u < TBW; ++u) {
       const int tb = tbs[u];
@@ -279,53 +293,49 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
       f32x16 cb = f32x16{};
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        const int byte = (s * 2 * KPL + KPL * g) * (int)sizeof(T);
-        const Frag bfr = *reinterpret_cast<const Frag*>(sb + bslot<RB>(m, byte / 16) * 16 + byte % 16);
+        const Frag bfr = *reinterpret_cast<const Frag*>(sb + s * 2 * KPL * (int)sizeof(T));
         I::mma(cb, bfr, cf[u][s]);
       }
-      // decay, dt, causal mask (and rows past the sequence), as a select
       float v[16];
+      if (tb > jb) {
+        // every t is past the whole j-block: 2^(G'_t - G'_j) = 2^(G'_t - G'_end) 2^(G'_end - G'_j),
+        // both factors <= 1; the second (times dt_j) is the table sW
+        const float a = exp2_hw(gt[u] - gend);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int jr = drow(q, g);
-        const bool keep = ((tb > jb) || (m >= jr)) && (j0 + jr < nvalid);
-        const float val = cb[q] * exp2_hw(gt[u] - gjb[jr]) * djb[jr];
-        v[q] = keep ? val : 0.f;
+        for (int q = 0; q < 16; ++q) v[q] = cb[q] * (wj[q] * a);
+      } else {
+        // diagonal block: direct decay, causal mask as a select (entries above the
+        // diagonal can hold 2^(+large))
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int jr = drow(q, g);
+          const float val = cb[q] * exp2_hw(gt[u] - sG[j0 + jr]) * sDt[j0 + jr];
+          v[q] = (m >= jr) ? val : 0.f;
+        }
       }
 #pragma unroll
       for (int js = 0; js < JS; ++js) {
         Frag ahi, alo;
         I::split(&v[js * KPL], ahi, alo);
 #pragma unroll
-        for (int q = 0; q < PGW; ++q) {
-          // x rows of this step, exact in the io dtype, in the same permuted j order
-          const int byte = ((pg0 + q) * CG + E * m) * (int)sizeof(T);
-          uint32_t d[KPL];
-#pragma unroll
-          for (int i = 0; i < KPL; ++i)
-            d[i] = *reinterpret_cast<const uint32_t*>(sx + xslot<RX>(drow(js * KPL + i, g), byte / 16) * 16 +
-                                                      byte % 16);
+        for (int q = 0; q < PGW; ++q)
 #pragma unroll
           for (int pe = 0; pe < E; ++pe) {
-            const Frag xf = I::from_dwords(d, pe);
-            I::mma(acc[u][q][pe], ahi, xf);
-            if constexpr (I::SPLIT) I::mma(acc[u][q][pe], alo, xf);
+            I::mma(acc[u][q][pe], ahi, xf[q][pe][js]);
+            if constexpr (I::SPLIT) I::mma(acc[u][q][pe], alo, xf[q][pe][js]);
           }
-        }
       }
       if (tb == jb) {
         // D x for the block's own rows, from the staged x rows
 #pragma unroll
-        for (int q = 0; q < PGW; ++q) {
-          const int byte = ((pg0 + q) * CG + E * m) * (int)sizeof(T);
+        for (int q = 0; q < PGW; ++q)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const uint32_t xd =
-                *reinterpret_cast<const uint32_t*>(sx + xslot<RX>(drow(r, g), byte / 16) * 16 + byte % 16);
+            const uint32_t xd = *reinterpret_cast<const uint32_t*>(
+                sx + (8 * (r / 4) + r % 4) * XRB + q * CG * (int)sizeof(T));
 #pragma unroll
             for (int pe = 0; pe < E; ++pe) acc[u][q][pe][r] += Dh * I::elem(xd, pe);
           }
-        }
       }
     }
   }
