@@ -80,7 +80,18 @@ struct ScanCfg {
   static constexpr int LOADS = (ITOT + WAVES - 1) / WAVES;   // per wave per block (spares repeat)
   static constexpr int BBYTES = IB * 1024, XBYTES = IX * 1024;
   static constexpr int BLOCK = BBYTES + XBYTES;
-  static constexpr int NBUF = BLOCK <= 16384 ? 4 : 3;   // blocks in the LDS ring
+  // The carried state Hprev (P rows of 4N bytes: fp32, or the bf16 (hi, lo)
+  // pairs) is the B operand every wave needs in full. When it fits, it is
+  // brought into LDS once per workgroup by direct loads, its rows reordered
+  // so that the 16 lanes of a fragment read hit distinct banks; otherwise
+  // each wave loads it from global memory.
+  static constexpr int HROWP = N / 4 + 1;                // padded row, in 16-byte pieces
+  static constexpr int HBYTES = P * HROWP * 16;
+  static constexpr bool HLDS = HBYTES <= 36 * 1024;
+  static constexpr int IH = HLDS ? (HBYTES + 1023) / 1024 : 0;
+  static constexpr int HLOADS = (IH + WAVES - 1) / WAVES;   // per wave (spares repeat)
+  static constexpr int HALLOC = HLDS ? IH * 1024 : 16;
+  static constexpr int NBUF = HLDS ? 3 : (BLOCK <= 16384 ? 4 : 3);   // blocks in the LDS ring
   static_assert(NTB % TBW == 0 && NPG % PGW == 0, "tile split");
   static_assert(WAVES >= 1 && WAVES <= 8, "tile does not fit a workgroup");
 };
@@ -127,6 +138,27 @@ __device__ __forceinline__ void issue_block(unsigned char* slot_base, const T* b
   }
 }
 
+// Direct global->LDS loads of the chunk's Hprev (HLDS case). LDS row slot r
+// holds headdim row p: with two bf16 columns per dword (E = 2) slot
+// q*64 + pe*32 + m holds p = q*64 + 2m + pe, so the lanes of one fragment
+// read (consecutive m) read consecutive slots; with fp32, slot p holds p.
+template <typename Cfg, typename T>
+__device__ __forceinline__ void issue_hprev(unsigned char* dst, const unsigned char* hsrc, int wave, int lane) {
+  constexpr int HROWP = Cfg::HROWP, P = Cfg::NPG * Cfg::CG;
+  constexpr int ROWB = (HROWP - 1) * 16;   // 4N bytes of data per row
+#pragma unroll
+  for (int i = 0; i < Cfg::HLOADS; ++i) {
+    const int kk = (wave + i * Cfg::WAVES) % Cfg::IH;
+    const int s = kk * 64 + lane;
+    int r = s / HROWP, c = s % HROWP;
+    if (r >= P) r = P - 1;        // tail of the last instruction
+    if (c >= HROWP - 1) c = 0;    // pad piece
+    int p = r;
+    if constexpr (Cfg::E == 2) p = (r / 64) * 64 + 2 * (r % 32) + (r / 32) % 2;
+    __builtin_amdgcn_global_load_lds(hsrc + (int64_t)p * ROWB + c * 16, dst + kk * 1024, 16, 0, 0);
+  }
+}
+
 template <typename T, int P, int N, int Q>
 __global__ __launch_bounds__((ScanCfg<T, P, N, Q>::THREADS)) __attribute__((amdgpu_waves_per_eu(2)))
 void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
@@ -144,6 +176,7 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
   constexpr int JS = 32 / (2 * KPL);   // MFMA steps over a 32-token j-block
 
   __shared__ __attribute__((aligned(16))) unsigned char ring[NBUF][Cfg::BLOCK];
+  __shared__ __attribute__((aligned(16))) unsigned char sH[Cfg::HALLOC];
   __shared__ __attribute__((aligned(16))) float sG[Q];
   __shared__ __attribute__((aligned(16))) float sDt[Q];
   __shared__ __attribute__((aligned(16))) float sW[Q];   // dt_j * 2^(G'_end(block of j) - G'_j) <= dt_j
@@ -187,6 +220,14 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
     sW[i] = di * exp2_hw(gc[(i | 31)] - gi);   // exponent <= 0: the block's last G' is its smallest
   }
 
+  // Hprev bytes of this chunk: P rows of 4N bytes
+  const unsigned char* hsrc = static_cast<const unsigned char*>(hprev) + hoff * 4;
+  if constexpr (Cfg::HLDS) issue_hprev<Cfg, T>(sH, hsrc, wave, lane);
+  // the first NBUF-1 j-blocks go in flight behind it
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i)
+    if (i < NTB) issue_block<Cfg>(ring[i], bbase, xbase, brow, xrow, i, nvalid, wave, lane);
+
   // 2. carried state: acc[u][q][pe] = C . Hprev^T, col -> p = (pg0+q)*CG + E*m + pe
   f32x16 acc[TBW][PGW][E];
 #pragma unroll
@@ -195,6 +236,15 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
     for (int q = 0; q < PGW; ++q)
 #pragma unroll
       for (int pe = 0; pe < E; ++pe) acc[u][q][pe] = f32x16{};
+  if constexpr (Cfg::HLDS) {
+    // Hprev landed once only the j-block loads issued after it remain
+    if constexpr (NBUF - 1 <= NTB) {
+      if constexpr (NBUF == 3) wait_vm_barrier<2 * LOADS>();
+      else wait_vm_barrier<3 * LOADS>();
+    } else {
+      wait_vm_barrier<0>();
+    }
+  }
 #pragma unroll
   for (int q = 0; q < PGW; ++q)
 #pragma unroll
@@ -203,7 +253,16 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
         Frag hhi, hlo;
-        if constexpr (I::SPLIT) {
+        if constexpr (Cfg::HLDS) {
+          const int slot = E == 2 ? (pg0 + q) * 64 + pe * 32 + m : p;
+          const unsigned char* hp = sH + slot * (Cfg::HROWP * 16);
+          if constexpr (I::SPLIT) {
+            hhi = *reinterpret_cast<const Frag*>(hp + (2 * s + g) * 32);
+            hlo = *reinterpret_cast<const Frag*>(hp + (2 * s + g) * 32 + 16);
+          } else {
+            hhi = *reinterpret_cast<const Frag*>(hp + (s * 2 * KPL + KPL * g) * 4);
+          }
+        } else if constexpr (I::SPLIT) {
           // (hi, lo) pairs: 8 hi then 8 lo bf16 per aligned group of 8 columns
           const bf16* hp = static_cast<const bf16*>(hprev) + 2 * hoff + (int64_t)p * 2 * N + (2 * s + g) * 16;
           hhi = I::load_row(reinterpret_cast<const T*>(hp), true);
@@ -219,13 +278,7 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
       }
     }
 
-  // the first NBUF-1 j-blocks go in flight now (issued after the C and Hprev
-  // loads, so waiting for those does not wait for these)
-#pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i)
-    if (i < NTB) issue_block<Cfg>(ring[i], bbase, xbase, brow, xrow, i, nvalid, wave, lane);
-
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // sG, sDt, sW visible
+  if constexpr (!Cfg::HLDS) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // sG, sDt, sW visible
 #pragma unroll
   for (int u = 0; u < TBW; ++u)
 #pragma unroll

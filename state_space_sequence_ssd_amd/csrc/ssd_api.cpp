@@ -3,7 +3,7 @@
 // layout, and the four launches in dependency order on the caller's stream
 // (the kernel order of the CUDA Tile Mamba-2 blog: cumulative sum, state
 // pass, then the outputs, with the state contraction split out of the pass).
-#include "../../include/mamba2_ssd.h"
+#include "mamba2_ssd.h"
 
 #include <hip/hip_runtime.h>
 
