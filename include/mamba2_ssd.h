@@ -56,7 +56,8 @@ extern "C" {
 #define MAMBA2_SSD_OK                0
 #define MAMBA2_SSD_ERR_NULL_POINTER (-1) /* a required pointer is NULL               */
 #define MAMBA2_SSD_ERR_BAD_DIM      (-2) /* a size is <= 0 (< 0 for batch, seqlen),
-                                            overflows, or exceeds a grid limit        */
+                                            overflows, exceeds a grid limit, or one
+                                            chunk of x (or of B, C) spans >= 2 GiB   */
 #define MAMBA2_SSD_ERR_GROUPS       (-3) /* nheads is not a multiple of ngroups       */
 #define MAMBA2_SSD_ERR_CHUNK        (-4) /* chunk is not one of 64, 128, 256          */
 #define MAMBA2_SSD_ERR_UNSUPPORTED  (-5) /* (headdim, dstate, io dtype) not built     */

@@ -3,16 +3,16 @@
 // hardware's base-2 exponential (CUDA Tile Mamba-2 blog, section "Kernel 1":
 // the sum restarts at every chunk and is stored pre-multiplied by log2 e).
 //
-// One workgroup per (chunk, block of 32 heads, batch row). The dt tile
-// [chunk tokens][32 heads] is read with whole 128-byte rows, scanned per
-// head through LDS, and written transposed, [batch][head][token], so the
+// One workgroup per (block of 16 heads, chunk, batch row). The dt tile
+// [chunk tokens][16 heads] is read as whole 64-byte rows, scanned per head
+// through LDS, and written transposed, [batch][head][token], so the
 // consumers read each head's decays contiguously (the blog's "GMEM layout"
 // point, done here once for both consumers). Three arrays come out, all
 // head-major: dt itself, G' (the scaled cumsum) and the chunk-state weight
 // w_t = dt_t * 2^(G'_last - G'_t) <= dt_t that ssd_chunk_state multiplies into
 // x (G'_last is the chunk's last G', known here once the scan is done).
 //
-// Monotonicity. Each head's chunk is split into 8 segments of Q/8 tokens.
+// Monotonicity. Each head's chunk is split into 16 segments of Q/16 tokens.
 // A thread sums its segment sequentially; segment prefixes are then chained
 // sequentially, P_{s+1} = P_s + L_s, and element i of segment s becomes
 // P_s + local_i. Since local_i only decreases (a_t <= 0), rounding is
@@ -27,8 +27,8 @@ namespace ssd {
 
 namespace {
 
-constexpr int kHB = 32;    // heads per workgroup
-constexpr int kSeg = 8;    // segments per head (threads per head)
+constexpr int kHB = 16;    // heads per workgroup
+constexpr int kSeg = 16;   // segments per head (threads per head)
 
 template <int Q>
 __global__ __launch_bounds__(256) void ssd_chunk_cumsum(const float* __restrict__ dt,
@@ -43,29 +43,42 @@ __global__ __launch_bounds__(256) void ssd_chunk_cumsum(const float* __restrict_
   __shared__ float s_pre[kSeg][kHB];
   __shared__ float s_lastloc[kHB];
 
-  const int k = blockIdx.x;
-  const int h0 = blockIdx.y * kHB;
+  const int h0 = blockIdx.x * kHB;
+  const int k = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)k * Q;
+  const int nh = H - h0 < kHB ? H - h0 : kHB;          // heads of this block
+  const int nt = T - t0 < Q ? (int)(T - t0) : Q;       // tokens of this chunk
+  const float* src = dt + (b * T + t0) * H + h0;
 
-  // token-major tile, 32 heads per row: lanes 0..31 read one 128-byte row
-  for (int idx = tid; idx < Q * kHB; idx += 256) {
-    const int t = idx / kHB, hh = idx % kHB;
-    float v = 0.f;
-    if (t0 + t < T && h0 + hh < H) v = dt[(b * T + t0 + t) * H + h0 + hh];
-    s_t[t][hh] = v;
+  // token-major tile, kHB heads per row (64 bytes); whole rows as 16-byte
+  // pieces when every row of the block is full and 16-byte aligned
+  if (nh == kHB && H % 4 == 0 && (reinterpret_cast<uintptr_t>(dt) & 15) == 0) {
+    for (int idx = tid; idx < Q * (kHB / 4); idx += 256) {
+      const int t = idx / (kHB / 4), c = idx % (kHB / 4);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < nt) v = *reinterpret_cast<const float4*>(src + (int64_t)t * H + 4 * c);
+      s_t[t][4 * c] = v.x; s_t[t][4 * c + 1] = v.y; s_t[t][4 * c + 2] = v.z; s_t[t][4 * c + 3] = v.w;
+    }
+  } else {
+    for (int idx = tid; idx < Q * kHB; idx += 256) {
+      const int t = idx / kHB, hh = idx % kHB;
+      s_t[t][hh] = (t < nt && hh < nh) ? src[(int64_t)t * H + hh] : 0.f;
+    }
   }
   __syncthreads();
 
-  // dt, head-major: consecutive lanes write consecutive tokens
-  for (int idx = tid; idx < Q * kHB; idx += 256) {
-    const int hl = idx / Q, t = idx % Q;
-    if (h0 + hl < H) dtt[(b * H + h0 + hl) * Tp + t0 + t] = s_t[t][hl];
+  // dt, head-major: each thread writes 4 consecutive tokens of one head
+  for (int idx = tid; idx < (Q / 4) * kHB; idx += 256) {
+    const int hl = idx / (Q / 4), t = 4 * (idx % (Q / 4));
+    if (hl < nh)
+      *reinterpret_cast<float4*>(dtt + (b * H + h0 + hl) * Tp + t0 + t) =
+          make_float4(s_t[t][hl], s_t[t + 1][hl], s_t[t + 2][hl], s_t[t + 3][hl]);
   }
 
   const int hh = tid % kHB, seg = tid / kHB;
-  const float a = (h0 + hh < H) ? A[h0 + hh] : 0.f;
+  const float a = hh < nh ? A[h0 + hh] : 0.f;
   float loc[SL];
   float run = 0.f;
 #pragma unroll
@@ -98,12 +111,12 @@ __global__ __launch_bounds__(256) void ssd_chunk_cumsum(const float* __restrict_
   }
   __syncthreads();
 
-  for (int idx = tid; idx < Q * kHB; idx += 256) {
-    const int hl = idx / Q, t = idx % Q;
-    if (h0 + hl < H) {
+  for (int idx = tid; idx < (Q / 4) * kHB; idx += 256) {
+    const int hl = idx / (Q / 4), t = 4 * (idx % (Q / 4));
+    if (hl < nh) {
       const int64_t o = (b * H + h0 + hl) * Tp + t0 + t;
-      gcum[o] = s_t[t][hl];
-      wst[o] = s_w[t][hl];
+      *reinterpret_cast<float4*>(gcum + o) = make_float4(s_t[t][hl], s_t[t + 1][hl], s_t[t + 2][hl], s_t[t + 3][hl]);
+      *reinterpret_cast<float4*>(wst + o) = make_float4(s_w[t][hl], s_w[t + 1][hl], s_w[t + 2][hl], s_w[t + 3][hl]);
     }
   }
 }
@@ -111,7 +124,8 @@ __global__ __launch_bounds__(256) void ssd_chunk_cumsum(const float* __restrict_
 }  // namespace
 
 hipError_t launch_chunk_cumsum(const Problem& p, hipStream_t stream) {
-  const dim3 grid((unsigned)p.nc, (unsigned)((p.H + kHB - 1) / kHB), (unsigned)p.bt);
+  // head blocks fastest, so neighbouring workgroups read the same dt rows
+  const dim3 grid((unsigned)((p.H + kHB - 1) / kHB), (unsigned)p.nc, (unsigned)p.bt);
   const dim3 block(256);
   switch (p.Q) {
     case 64:

@@ -79,6 +79,9 @@ struct ScanCfg {
   static constexpr int ITOT = IB + IX;
   static constexpr int LOADS = (ITOT + WAVES - 1) / WAVES;   // per wave per block (spares repeat)
   static constexpr int BBYTES = IB * 1024, XBYTES = IX * 1024;
+  // per-lane load offsets kept in registers for whole-chunk blocks (see
+  // plan_block) only when they are few; otherwise each block recomputes them
+  static constexpr bool PLAN = LOADS <= 4;
   static constexpr int BLOCK = BBYTES + XBYTES;
   // The carried state Hprev (P rows of 4N bytes: fp32, or the bf16 (hi, lo)
   // pairs) is the B operand every wave needs in full. When it fits, it is
@@ -135,6 +138,39 @@ __device__ __forceinline__ void issue_block(unsigned char* slot_base, const T* b
       __builtin_amdgcn_global_load_lds(xbase + row * xrow + c * EPC, slot_base + Cfg::BBYTES + kx * 1024, 16,
                                        0, 0);
     }
+  }
+}
+
+// The same loads for a j-block whose 32 rows all lie inside the sequence:
+// `off` holds, per load instruction, this lane's byte offset from the
+// block's first row (fixed for the whole chunk, see plan_block), and the
+// block base is wave-uniform, so each load is a scalar base plus a vector
+// offset with no per-block address arithmetic.
+template <typename Cfg, typename T>
+__device__ __forceinline__ void plan_block(uint32_t* off, int64_t brow, int64_t xrow, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < Cfg::LOADS; ++i) {
+    const int kk = (wave + i * Cfg::WAVES) % Cfg::ITOT;
+    const bool isb = kk < Cfg::IB;
+    const int s = (isb ? kk : kk - Cfg::IB) * 64 + lane;
+    const int rowp = isb ? Cfg::BROWP : Cfg::XROWP, rdat = isb ? Cfg::RB : Cfg::RX;
+    int r = s / rowp, c = s % rowp;
+    if (r >= 32) r = 31;     // tail of the last instruction
+    if (c >= rdat) c = 0;    // pad piece
+    off[i] = (uint32_t)(r * (isb ? brow : xrow) * (int64_t)sizeof(T) + c * 16);
+  }
+}
+
+template <typename Cfg>
+__device__ __forceinline__ void issue_block_full(unsigned char* slot_base, const unsigned char* bblk,
+                                                 const unsigned char* xblk, const uint32_t* off, int wave) {
+#pragma unroll
+  for (int i = 0; i < Cfg::LOADS; ++i) {
+    const int kk = (wave + i * Cfg::WAVES) % Cfg::ITOT;
+    if (kk < Cfg::IB)
+      __builtin_amdgcn_global_load_lds(bblk + off[i], slot_base + kk * 1024, 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(xblk + off[i], slot_base + Cfg::BBYTES + (kk - Cfg::IB) * 1024, 16, 0, 0);
   }
 }
 
@@ -203,6 +239,10 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
   const T* bbase = Bm + ((b * Tlen + t0) * G + grp) * N;
   const T* cbase = Cm + ((b * Tlen + t0) * G + grp) * N;
   const int64_t hoff = (((int64_t)b * H + h) * nc + k) * (int64_t)(P * N);
+  const bool full = Cfg::PLAN && nvalid == Q;   // every j-block lies inside the sequence
+  uint32_t boffs[LOADS];
+  if constexpr (Cfg::PLAN) plan_block<Cfg, T>(boffs, brow, xrow, wave, lane);
+  const int64_t bblk_bytes = 32 * brow * (int64_t)sizeof(T), xblk_bytes = 32 * xrow * (int64_t)sizeof(T);
 
   // 1. C fragments of the wave's t-blocks: row t = 32*tb + m, dstate k-step s
   Frag cf[TBW][KS];
@@ -226,7 +266,13 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
   // the first NBUF-1 j-blocks go in flight behind it
 #pragma unroll
   for (int i = 0; i < NBUF - 1; ++i)
-    if (i < NTB) issue_block<Cfg>(ring[i], bbase, xbase, brow, xrow, i, nvalid, wave, lane);
+    if (i < NTB) {
+      if (full)
+        issue_block_full<Cfg>(ring[i], reinterpret_cast<const unsigned char*>(bbase) + i * bblk_bytes,
+                              reinterpret_cast<const unsigned char*>(xbase) + i * xblk_bytes, boffs, wave);
+      else
+        issue_block<Cfg>(ring[i], bbase, xbase, brow, xrow, i, nvalid, wave, lane);
+    }
 
   // 2. carried state: acc[u][q][pe] = C . Hprev^T, col -> p = (pg0+q)*CG + E*m + pe
   f32x16 acc[TBW][PGW][E];
@@ -308,8 +354,14 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
     if (after <= 0) wait_vm_barrier<0>();
     else if (after == 1) wait_vm_barrier<LOADS>();
     else wait_vm_barrier<2 * LOADS>();
-    if (jb + NBUF - 1 < NTB)
-      issue_block<Cfg>(ring[(jb + NBUF - 1) % NBUF], bbase, xbase, brow, xrow, jb + NBUF - 1, nvalid, wave, lane);
+    if (jb + NBUF - 1 < NTB) {
+      const int jn = jb + NBUF - 1, sn = jn % NBUF;
+      if (full)
+        issue_block_full<Cfg>(ring[sn], reinterpret_cast<const unsigned char*>(bbase) + jn * bblk_bytes,
+                              reinterpret_cast<const unsigned char*>(xbase) + jn * xblk_bytes, boffs, wave);
+      else
+        issue_block<Cfg>(ring[sn], bbase, xbase, brow, xrow, jn, nvalid, wave, lane);
+    }
     if (jb > tmax) continue;
 
     const unsigned char* sb = ring[jb % NBUF] + boff;

@@ -10,8 +10,11 @@
 //
 // One wave computes one (batch, head, chunk) tile's rows of one headdim
 // column group against NGW dstate column groups with 32x32 MFMAs; the
-// contraction runs over the chunk's tokens in steps of 2*KPL, with the next
-// step's loads issued before this step's MFMAs. The scale w_t
+// contraction runs over the chunk's tokens in steps of 2*KPL, with the loads
+// of the next few steps in flight (a small ring of registers) while this
+// step's MFMAs run. Loads go through buffer resources: the token-row part of
+// each address is a scalar offset, and in a ragged last chunk the rows past
+// the sequence load as zeros. The scale w_t
 // is applied to x (w and x are both per head, while B is shared by the
 // heads of a group). With bf16 io the product w*x is not a bf16 number, so
 // it enters the MFMA as a bf16 (hi, lo) pair in two MFMAs against the exact
@@ -47,61 +50,76 @@ struct StateCfg {
   static_assert(WPT >= 1 && WPT <= 8, "tile does not fit a workgroup");
 };
 
-template <typename T, int P, int N, int Q>
-__global__ __launch_bounds__((StateCfg<T, P, N>::THREADS)) void ssd_chunk_state(
-    const T* __restrict__ x, const T* __restrict__ Bm, const float* __restrict__ wst,
-    float* __restrict__ states, int64_t Tlen, int H, int G, int64_t nc, int64_t Tp) {
+// One k-step's operands for a lane: KPL token rows of x and of each of the
+// wave's NGW dstate column groups of B (one dword each), and KPL weights.
+template <typename T, int NGW>
+struct Step {
+  static constexpr int KPL = Io<T>::KPL;
+  uint32_t xd[KPL];
+  uint32_t bd[NGW][KPL];
+  float w[KPL];
+};
+
+// Loads of k-step s. The lane's tokens are t = s*2*KPL + KPL*g + i. With
+// FULL (every token of the chunk inside the sequence) the row term of each
+// address is wave-uniform and goes in the scalar offset; otherwise the
+// whole offset is in the vector operand, so rows past the sequence fall
+// outside the resource and load as zeros.
+template <typename T, int NGW, bool FULL>
+__device__ __forceinline__ void load_step(Step<T, NGW>& st, int s, __amdgpu_buffer_rsrc_t rx,
+                                          __amdgpu_buffer_rsrc_t rb, const float* wc, uint32_t xlane,
+                                          uint32_t blane, uint32_t xsb, uint32_t bsb, int g) {
+  constexpr int KPL = Io<T>::KPL, CGB = 32 * 4;   // bytes per column group
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const uint32_t trow = (uint32_t)(s * 2 * KPL + i);   // plus KPL*g, in the lane term
+    if constexpr (FULL) {
+      st.xd[i] = buf_load_dword(rx, xlane, trow * xsb);
+#pragma unroll
+      for (int j = 0; j < NGW; ++j) st.bd[j][i] = buf_load_dword(rb, blane + j * CGB, trow * bsb);
+    } else {
+      st.xd[i] = buf_load_dword(rx, xlane + trow * xsb, 0);
+#pragma unroll
+      for (int j = 0; j < NGW; ++j) st.bd[j][i] = buf_load_dword(rb, blane + j * CGB + trow * bsb, 0);
+    }
+  }
+  const float* wp = wc + s * 2 * KPL + KPL * g;   // the workspace covers the padded chunk
+  if constexpr (KPL % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < KPL; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(wp + i);
+      st.w[i] = v.x; st.w[i + 1] = v.y; st.w[i + 2] = v.z; st.w[i + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) st.w[i] = wp[i];
+  }
+}
+
+template <typename T, int P, int N, int Q, bool FULL>
+__device__ __forceinline__ void state_tile(const T* __restrict__ x, const T* __restrict__ Bm,
+                                           const float* __restrict__ wst, float* __restrict__ states,
+                                           int64_t Tlen, int H, int G, int64_t nc, int64_t Tp, int h, int k,
+                                           int64_t b, int pg, int ng0, int m, int g) {
   using I = Io<T>;
   using Cfg = StateCfg<T, P, N>;
-  constexpr int E = I::E, KPL = I::KPL, CG = Cfg::CG, NGW = Cfg::NGW, NGS = Cfg::NGS;
-  constexpr int WPT = Cfg::WPT, TPW = Cfg::TPW;
+  constexpr int E = I::E, KPL = I::KPL, CG = Cfg::CG, NGW = Cfg::NGW;
   constexpr int KSTEPS = Q / (2 * KPL);
+  constexpr int D = KPL == 1 ? 4 : 3;   // k-steps of loads in flight (ring of registers)
+  static_assert(KPL != 1 || 8 % D == 0, "ring index must stay static under the partial unroll");
 
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const int m = lane % 32, g = lane / 32;
-  const int tile = wave / WPT, sub = wave % WPT;
-  const int pg = sub / NGS, ng0 = (sub % NGS) * NGW;
-  const int h = blockIdx.x * TPW + tile;
-  if (h >= H) return;
-  const int k = blockIdx.y;
-  const int64_t b = blockIdx.z;
   const int grp = h / (H / G);
   const int64_t t0 = (int64_t)k * Q;
-
+  const int nvalid = (int)(Tlen - t0 < Q ? Tlen - t0 : Q);
   const float* wc = wst + ((int64_t)b * H + h) * Tp + t0;
-  // dword views: x row stride H*P elements, B row stride G*N elements
-  const int64_t xstride = (int64_t)H * P / E, bstride = (int64_t)G * N / E;
-  const uint32_t* xb = reinterpret_cast<const uint32_t*>(x + ((b * Tlen + t0) * H + h) * P + pg * CG) + m;
-  const uint32_t* bb = reinterpret_cast<const uint32_t*>(Bm + ((b * Tlen + t0) * G + grp) * N + ng0 * CG) + m;
-  const int64_t nvalid = Tlen - t0;   // tokens of this chunk inside the sequence
-
-  // one k-step's operands: KPL token rows of x and B (one dword each), KPL weights
-  struct Step {
-    uint32_t xd[KPL];
-    uint32_t bd[NGW][KPL];
-    float w[KPL];
-  };
-  auto load = [&](int s, Step& st) {
-    const int tb = s * 2 * KPL + KPL * g;   // first of this lane half's KPL tokens
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      const int t = tb + i;
-      const bool valid = t < nvalid;
-      st.xd[i] = valid ? xb[t * xstride] : 0u;
-#pragma unroll
-      for (int j = 0; j < NGW; ++j) st.bd[j][i] = valid ? bb[t * bstride + j * (CG / E)] : 0u;
-    }
-    if constexpr (KPL % 4 == 0) {
-#pragma unroll
-      for (int i = 0; i < KPL; i += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(wc + tb + i);
-        st.w[i] = v.x; st.w[i + 1] = v.y; st.w[i + 2] = v.z; st.w[i + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < KPL; ++i) st.w[i] = wc[tb + i];
-    }
-  };
+  const uint32_t xsb = (uint32_t)((int64_t)H * P * sizeof(T)), bsb = (uint32_t)((int64_t)G * N * sizeof(T));
+  const T* xt = x + ((b * Tlen + t0) * H + h) * P + pg * CG;
+  const T* bt = Bm + ((b * Tlen + t0) * G + grp) * N + ng0 * CG;
+  // bytes the tile may read: rows 0..nvalid-1, each CG (x) or NGW*CG (B) columns
+  const uint32_t xbytes = (uint32_t)(nvalid - 1) * xsb + CG * sizeof(T);
+  const uint32_t bbytes = (uint32_t)(nvalid - 1) * bsb + NGW * CG * sizeof(T);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(xt, xbytes), rb = make_rsrc(bt, bbytes);
+  const uint32_t xlane = m * 4 + KPL * g * xsb, blane = m * 4 + KPL * g * bsb;
 
   f32x16 acc[E][NGW][E];
 #pragma unroll
@@ -111,11 +129,15 @@ __global__ __launch_bounds__((StateCfg<T, P, N>::THREADS)) void ssd_chunk_state(
 #pragma unroll
       for (int c = 0; c < E; ++c) acc[a][j][c] = f32x16{};
 
-  Step cur, nxt;
-  load(0, cur);
+  Step<T, NGW> ring[D];
+#pragma unroll
+  for (int s = 0; s < D - 1; ++s)
+    if (s < KSTEPS) load_step<T, NGW, FULL>(ring[s], s, rx, rb, wc, xlane, blane, xsb, bsb, g);
 #pragma unroll (KPL == 1 ? 8 : KSTEPS)
   for (int s = 0; s < KSTEPS; ++s) {
-    if (s + 1 < KSTEPS) load(s + 1, nxt);   // in flight while this step's MFMAs run
+    if (s + D - 1 < KSTEPS)   // in flight while this step's MFMAs run
+      load_step<T, NGW, FULL>(ring[(s + D - 1) % D], s + D - 1, rx, rb, wc, xlane, blane, xsb, bsb, g);
+    const Step<T, NGW>& cur = ring[s % D];
     typename I::Frag ahi[E], alo[E];
 #pragma unroll
     for (int pe = 0; pe < E; ++pe) {
@@ -135,7 +157,6 @@ __global__ __launch_bounds__((StateCfg<T, P, N>::THREADS)) void ssd_chunk_state(
           if constexpr (I::SPLIT) I::mma(acc[pe][j][ne], alo[pe], bf);
         }
       }
-    cur = nxt;
   }
 
   // S[p][n]: D row r -> p = pg*CG + E*drow(r, g) + pe, col -> n = (ng0+j)*CG + E*m + ne
@@ -153,6 +174,27 @@ __global__ __launch_bounds__((StateCfg<T, P, N>::THREADS)) void ssd_chunk_state(
         else
           *dst = acc[pe][j][0][r];
       }
+}
+
+template <typename T, int P, int N, int Q>
+__global__ __launch_bounds__((StateCfg<T, P, N>::THREADS)) void ssd_chunk_state(
+    const T* __restrict__ x, const T* __restrict__ Bm, const float* __restrict__ wst,
+    float* __restrict__ states, int64_t Tlen, int H, int G, int64_t nc, int64_t Tp) {
+  using Cfg = StateCfg<T, P, N>;
+  // wave-uniform (scalar) wave index: the buffer resources built from it
+  // must be provably uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
+  const int m = lane % 32, g = lane / 32;
+  const int tile = wave / Cfg::WPT, sub = wave % Cfg::WPT;
+  const int pg = sub / Cfg::NGS, ng0 = (sub % Cfg::NGS) * Cfg::NGW;
+  const int h = blockIdx.x * Cfg::TPW + tile;
+  if (h >= H) return;
+  const int k = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  if ((int64_t)(k + 1) * Q <= Tlen)
+    state_tile<T, P, N, Q, true>(x, Bm, wst, states, Tlen, H, G, nc, Tp, h, k, b, pg, ng0, m, g);
+  else
+    state_tile<T, P, N, Q, false>(x, Bm, wst, states, Tlen, H, G, nc, Tp, h, k, b, pg, ng0, m, g);
 }
 
 template <typename T, int P, int N, int Q>

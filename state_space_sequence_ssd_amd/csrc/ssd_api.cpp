@@ -69,6 +69,11 @@ int check_dims(const mamba2_ssd_dims* d, int io, Sizes* s) {
   // grid limits of the launchers: y = nchunks (chunk-parallel kernels), z = batch
   if (r.nc > ssd::kMaxGridYZ || d->batch > ssd::kMaxGridYZ) return MAMBA2_SSD_ERR_BAD_DIM;
   if (bh > INT32_MAX) return MAMBA2_SSD_ERR_BAD_DIM;
+  // the kernels address one chunk of x (or of B, C) with 32-bit byte offsets
+  const int64_t esz = io == MAMBA2_SSD_BF16 ? 2 : 4;
+  if (d->chunk * d->nheads * d->headdim * esz >= (int64_t)1 << 31 ||
+      d->chunk * d->ngroups * d->dstate * esz >= (int64_t)1 << 31)
+    return MAMBA2_SSD_ERR_BAD_DIM;
   *s = r;
   return MAMBA2_SSD_OK;
 }

@@ -134,6 +134,18 @@ template <> struct Io<float> {
   }
 };
 
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 word 3). Loads
+// through it return 0 for any byte offset >= bytes instead of touching
+// memory, and their scalar offset operand carries wave-uniform address
+// terms with no vector arithmetic. Range checks here always put the whole
+// offset in the vector operand (scalar offset 0) where they matter.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t buf_load_dword(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 // Row of the 32x32 D block held in register r of a lane in half g = l/32.
 __device__ __forceinline__ constexpr int drow(int r, int g) { return 8 * (r / 4) + 4 * g + (r % 4); }
 

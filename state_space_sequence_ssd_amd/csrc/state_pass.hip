@@ -8,8 +8,8 @@
 //   final = h
 //
 // Every (batch, head, element of the headdim x dstate state) is an
-// independent chain, so the grid is (batch*head, state/1024) and each thread
-// carries 4 consecutive state elements through all chunks in fp32
+// independent chain, so the grid is (batch*head, state/(256*EPT)) and each
+// thread carries EPT consecutive state elements through all chunks in fp32
 // registers. The kernel is pure streaming: S is read once and hprev written
 // once; loads for later chunks are issued ahead of the dependent FMAs so each
 // thread keeps several 16-byte reads in flight.
@@ -27,85 +27,140 @@ namespace ssd {
 
 namespace {
 
-constexpr int kDepth = 4;   // chunks whose S loads are in flight per thread
-
-template <typename T>
-__device__ __forceinline__ void store_hprev(void* hp, int64_t chunk_off, int e, const float4& h);
+// Each thread carries EPT consecutive state elements (EPT = 4 or 8, so one or
+// two 16-byte pieces per chunk) and keeps the S loads of the next DEPTH
+// chunks in flight. The host picks EPT = 8 when that still leaves at least
+// 16 waves per CU, which halves the wave count so every wave of the grid is
+// resident at once (no partial second round of waves, each of which would
+// walk every chunk); smaller problems take EPT = 4 for more parallelism.
+template <typename T, int EPT>
+__device__ __forceinline__ void store_hprev(void* hp, int64_t chunk_off, int e, const float* h);
 
 template <>
-__device__ __forceinline__ void store_hprev<float>(void* hp, int64_t chunk_off, int e, const float4& h) {
-  *reinterpret_cast<float4*>(static_cast<float*>(hp) + chunk_off + e) = h;
+__device__ __forceinline__ void store_hprev<float, 4>(void* hp, int64_t chunk_off, int e, const float* h) {
+  *reinterpret_cast<float4*>(static_cast<float*>(hp) + chunk_off + e) = make_float4(h[0], h[1], h[2], h[3]);
 }
 
 template <>
-__device__ __forceinline__ void store_hprev<bf16>(void* hp, int64_t chunk_off, int e, const float4& h) {
-  // element e (a multiple of 4) sits in group e/8 at position e%8 (0 or 4)
+__device__ __forceinline__ void store_hprev<float, 8>(void* hp, int64_t chunk_off, int e, const float* h) {
+  float4* d = reinterpret_cast<float4*>(static_cast<float*>(hp) + chunk_off + e);
+  d[0] = make_float4(h[0], h[1], h[2], h[3]);
+  d[1] = make_float4(h[4], h[5], h[6], h[7]);
+}
+
+// bf16 pairs: element e sits in the aligned group of 8 columns e/8, at
+// position e%8; the group holds 8 hi values then 8 lo values.
+template <>
+__device__ __forceinline__ void store_hprev<bf16, 4>(void* hp, int64_t chunk_off, int e, const float* h) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  const uint32_t h01 = pack_bf16x2(h.x, h.y), h23 = pack_bf16x2(h.z, h.w);
   u32x2 hi, lo;
-  hi[0] = h01;
-  hi[1] = h23;
-  lo[0] = pack_bf16x2(h.x - bf16lo(h01), h.y - bf16hi(h01));
-  lo[1] = pack_bf16x2(h.z - bf16lo(h23), h.w - bf16hi(h23));
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t d = pack_bf16x2(h[2 * i], h[2 * i + 1]);
+    hi[i] = d;
+    lo[i] = pack_bf16x2(h[2 * i] - bf16lo(d), h[2 * i + 1] - bf16hi(d));
+  }
   bf16* base = static_cast<bf16*>(hp) + 2 * chunk_off + (e / 8) * 16 + (e % 8);
   *reinterpret_cast<u32x2*>(base) = hi;
   *reinterpret_cast<u32x2*>(base + 8) = lo;
 }
 
-template <typename T>
+template <>
+__device__ __forceinline__ void store_hprev<bf16, 8>(void* hp, int64_t chunk_off, int e, const float* h) {
+  u32x4 hi, lo;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t d = pack_bf16x2(h[2 * i], h[2 * i + 1]);
+    hi[i] = d;
+    lo[i] = pack_bf16x2(h[2 * i] - bf16lo(d), h[2 * i + 1] - bf16hi(d));
+  }
+  u32x4* base = reinterpret_cast<u32x4*>(static_cast<bf16*>(hp) + 2 * chunk_off + 2 * e);
+  base[0] = hi;
+  base[1] = lo;
+}
+
+template <int EPT>
+struct Piece {
+  float v[EPT];
+};
+
+template <int EPT>
+__device__ __forceinline__ Piece<EPT> load_piece(const float* p) {
+  Piece<EPT> r;
+#pragma unroll
+  for (int i = 0; i < EPT; i += 4) {
+    const float4 a = *reinterpret_cast<const float4*>(p + i);
+    r.v[i] = a.x; r.v[i + 1] = a.y; r.v[i + 2] = a.z; r.v[i + 3] = a.w;
+  }
+  return r;
+}
+
+template <typename T, int EPT>
 __global__ __launch_bounds__(256) void ssd_state_pass(const float* __restrict__ states,
                                                       const float* __restrict__ gcum,
                                                       const float* init,            // may equal final_state
                                                       void* __restrict__ hprev,
                                                       float* final_state,
                                                       int nc, int Q, int64_t Tp, int PN) {
+  constexpr int DEPTH = 32 / EPT;
   const int64_t bh = blockIdx.x;
-  const int e = (blockIdx.y * 256 + threadIdx.x) * 4;   // PN is a multiple of 1024
+  const int e = (blockIdx.y * 256 + threadIdx.x) * EPT;   // PN is a multiple of 256 * EPT
 
-  float4 h = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (init) h = *reinterpret_cast<const float4*>(init + bh * PN + e);
+  Piece<EPT> h;
+  if (init) {
+    h = load_piece<EPT>(init + bh * PN + e);
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) h.v[i] = 0.f;
+  }
 
   const float* sp = states + bh * (int64_t)nc * PN + e;
   const int64_t hbase = bh * (int64_t)nc * PN;
   const float* glast = gcum + bh * Tp + (Q - 1);
 
-  float4 buf[kDepth];
+  Piece<EPT> buf[DEPTH];
 #pragma unroll
-  for (int i = 0; i < kDepth; ++i)
-    if (i < nc) buf[i] = *reinterpret_cast<const float4*>(sp + (int64_t)i * PN);
+  for (int i = 0; i < DEPTH; ++i)
+    if (i < nc) buf[i] = load_piece<EPT>(sp + (int64_t)i * PN);
 
-  for (int k0 = 0; k0 < nc; k0 += kDepth) {
+  for (int k0 = 0; k0 < nc; k0 += DEPTH) {
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) {
+    for (int i = 0; i < DEPTH; ++i) {
       const int k = k0 + i;
       if (k < nc) {
-        const float4 s = buf[i];
-        if (k + kDepth < nc) buf[i] = *reinterpret_cast<const float4*>(sp + (int64_t)(k + kDepth) * PN);
-        store_hprev<T>(hprev, hbase + (int64_t)k * PN, e, h);
+        const Piece<EPT> s = buf[i];
+        if (k + DEPTH < nc) buf[i] = load_piece<EPT>(sp + (int64_t)(k + DEPTH) * PN);
+        store_hprev<T, EPT>(hprev, hbase + (int64_t)k * PN, e, h.v);
         const float sc = exp2_hw(glast[(int64_t)k * Q]);
-        h.x = fmaf(sc, h.x, s.x);
-        h.y = fmaf(sc, h.y, s.y);
-        h.z = fmaf(sc, h.z, s.z);
-        h.w = fmaf(sc, h.w, s.w);
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) h.v[j] = fmaf(sc, h.v[j], s.v[j]);
       }
     }
   }
-  if (final_state) *reinterpret_cast<float4*>(final_state + bh * PN + e) = h;
+  if (final_state) {
+    float* f = final_state + bh * PN + e;
+#pragma unroll
+    for (int i = 0; i < EPT; i += 4)
+      *reinterpret_cast<float4*>(f + i) = make_float4(h.v[i], h.v[i + 1], h.v[i + 2], h.v[i + 3]);
+  }
+}
+
+template <typename T, int EPT>
+hipError_t launch(const Problem& p, hipStream_t stream) {
+  const int PN = (int)(p.P * p.N);
+  const dim3 grid((unsigned)(p.bt * p.H), (unsigned)(PN / (256 * EPT)));
+  hipLaunchKernelGGL((ssd_state_pass<T, EPT>), grid, dim3(256), 0, stream, p.states, p.gcum, p.init, p.hprev,
+                     p.final_state, (int)p.nc, (int)p.Q, p.Tp, PN);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_state_pass(const Problem& p, hipStream_t stream) {
-  const int PN = (int)(p.P * p.N);
-  const dim3 grid((unsigned)(p.bt * p.H), (unsigned)(PN / 1024));
-  const dim3 block(256);
-  if (p.io == 1)
-    hipLaunchKernelGGL(ssd_state_pass<bf16>, grid, block, 0, stream, p.states, p.gcum, p.init, p.hprev,
-                       p.final_state, (int)p.nc, (int)p.Q, p.Tp, PN);
-  else
-    hipLaunchKernelGGL(ssd_state_pass<float>, grid, block, 0, stream, p.states, p.gcum, p.init, p.hprev,
-                       p.final_state, (int)p.nc, (int)p.Q, p.Tp, PN);
-  return hipGetLastError();
+  // waves with 8 elements per thread: bt*H*P*N / 512; 256 CUs x 16 waves
+  const bool wide = p.bt * p.H * p.P * p.N / 512 >= 256 * 16;
+  if (p.io == 1) return wide ? launch<bf16, 8>(p, stream) : launch<bf16, 4>(p, stream);
+  return wide ? launch<float, 8>(p, stream) : launch<float, 4>(p, stream);
 }
 
 }  // namespace ssd
