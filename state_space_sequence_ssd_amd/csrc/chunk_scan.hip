@@ -127,7 +127,7 @@ __device__ __forceinline__ void issue_block(unsigned char* slot_base, const T* b
       if (r >= 32) r = 31;            // tail of the last instruction
       if (c >= Cfg::RB) c = 0;        // pad piece
       const int row = min(jb * 32 + r, nvalid - 1);
-      __builtin_amdgcn_global_load_lds(bbase + row * brow + c * EPC, slot_base + kk * 1024, 16, 0, 0);
+      lds_dma16(bbase + row * brow + c * EPC, slot_base + kk * 1024);
     } else {
       const int kx = kk - Cfg::IB;
       const int s = kx * 64 + lane;
@@ -135,8 +135,7 @@ __device__ __forceinline__ void issue_block(unsigned char* slot_base, const T* b
       if (r >= 32) r = 31;
       if (c >= Cfg::RX) c = 0;
       const int row = min(jb * 32 + r, nvalid - 1);
-      __builtin_amdgcn_global_load_lds(xbase + row * xrow + c * EPC, slot_base + Cfg::BBYTES + kx * 1024, 16,
-                                       0, 0);
+      lds_dma16(xbase + row * xrow + c * EPC, slot_base + Cfg::BBYTES + kx * 1024);
     }
   }
 }
@@ -168,9 +167,46 @@ __device__ __forceinline__ void issue_block_full(unsigned char* slot_base, const
   for (int i = 0; i < Cfg::LOADS; ++i) {
     const int kk = (wave + i * Cfg::WAVES) % Cfg::ITOT;
     if (kk < Cfg::IB)
-      __builtin_amdgcn_global_load_lds(bblk + off[i], slot_base + kk * 1024, 16, 0, 0);
+      lds_dma16(bblk + off[i], slot_base + kk * 1024);
     else
-      __builtin_amdgcn_global_load_lds(xblk + off[i], slot_base + Cfg::BBYTES + (kk - Cfg::IB) * 1024, 16, 0, 0);
+      lds_dma16(xblk + off[i], slot_base + Cfg::BBYTES + (kk - Cfg::IB) * 1024);
+  }
+}
+
+// Per-lane (row, byte column) of each of the wave's LOADS load instructions
+// within a j-block, packed as row << 16 | column byte offset (see
+// issue_block for the slot layout).
+template <typename Cfg>
+__device__ __forceinline__ void plan_block_rc(uint32_t* rc, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < Cfg::LOADS; ++i) {
+    const int kk = (wave + i * Cfg::WAVES) % Cfg::ITOT;
+    const bool isb = kk < Cfg::IB;
+    const int s = (isb ? kk : kk - Cfg::IB) * 64 + lane;
+    const int rowp = isb ? Cfg::BROWP : Cfg::XROWP, rdat = isb ? Cfg::RB : Cfg::RX;
+    int r = s / rowp, c = s % rowp;
+    if (r >= 32) r = 31;     // tail of the last instruction
+    if (c >= rdat) c = 0;    // pad piece
+    rc[i] = (uint32_t)(r << 16) | (uint32_t)(c * 16);
+  }
+}
+
+// issue_block from a plan: bt and xt are the tile's first B and x rows (as
+// bytes), bsb and xsb their row strides in bytes; rows past the sequence are
+// clamped to its last row, as in issue_block. Offsets are 32-bit (one chunk
+// of x spans less than 2 GiB).
+template <typename Cfg>
+__device__ __forceinline__ void issue_block_rc(unsigned char* slot_base, const unsigned char* bt,
+                                               const unsigned char* xt, uint32_t bsb, uint32_t xsb,
+                                               const uint32_t* rc, int jb, int nvalid, int wave) {
+#pragma unroll
+  for (int i = 0; i < Cfg::LOADS; ++i) {
+    const int kk = (wave + i * Cfg::WAVES) % Cfg::ITOT;
+    const int row = min(jb * 32 + (int)(rc[i] >> 16), nvalid - 1);
+    if (kk < Cfg::IB)
+      lds_dma16(bt + ((uint32_t)row * bsb + (rc[i] & 0xffffu)), slot_base + kk * 1024);
+    else
+      lds_dma16(xt + ((uint32_t)row * xsb + (rc[i] & 0xffffu)), slot_base + Cfg::BBYTES + (kk - Cfg::IB) * 1024);
   }
 }
 
@@ -191,7 +227,7 @@ __device__ __forceinline__ void issue_hprev(unsigned char* dst, const unsigned c
     if (c >= HROWP - 1) c = 0;    // pad piece
     int p = r;
     if constexpr (Cfg::E == 2) p = (r / 64) * 64 + 2 * (r % 32) + (r / 32) % 2;
-    __builtin_amdgcn_global_load_lds(hsrc + (int64_t)p * ROWB + c * 16, dst + kk * 1024, 16, 0, 0);
+    lds_dma16(hsrc + (int64_t)p * ROWB + c * 16, dst + kk * 1024);
   }
 }
 
@@ -459,13 +495,392 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
     }
 }
 
+// Everything one (batch, head, chunk) tile needs to find its data; all of it
+// is wave-uniform and lives in scalar registers.
+template <typename T>
+struct Tile {
+  int h, nvalid;
+  float Dh;
+  int64_t ckey;   // identifies the C rows (batch, chunk, group)
+  const T* xbase;
+  const T* bbase;
+  const T* cbase;
+  T* ybase;
+  const float* gc;
+  const float* dtc;
+  const unsigned char* hsrc;
+};
+
+// Tile number gi of the persistent walk. Tiles are numbered (batch*chunk,
+// head) with heads fastest; with xcd set (the grid and batch*nchunks are
+// multiples of 8), the numbering first groups the chunks by index mod 8, and
+// workgroup w, dealt round-robin to XCD w mod 8, walks a contiguous range of
+// its XCD's group. So a workgroup visits consecutive heads of one chunk
+// (its C fragments stay in registers across them), and each chunk's B and C
+// rows are read into one XCD's L2 only.
+template <typename T, int P, int N, int Q>
+__device__ __forceinline__ Tile<T> make_tile(int64_t gi, bool xcd, int64_t ntiles, const T* x, const T* Bm,
+                                             const T* Cm, const float* gcum, const float* dtt, const float* Dp,
+                                             const void* hprev, T* y, int64_t Tlen, int H, int G, int64_t nc,
+                                             int64_t Tp) {
+  int64_t bk;
+  int h;
+  if (xcd) {
+    const int64_t n8 = ntiles / 8, xg = gi / n8, i = gi % n8;
+    bk = xg + 8 * (i / H);
+    h = (int)(i % H);
+  } else {
+    bk = gi / H;
+    h = (int)(gi % H);
+  }
+  const int64_t k = bk % nc, b = bk / nc;
+  const int grp = h / (H / G);
+  const int64_t t0 = k * Q;
+  Tile<T> t;
+  t.h = h;
+  t.ckey = bk * G + grp;
+  t.nvalid = (int)(Tlen - t0 < Q ? Tlen - t0 : Q);
+  t.Dh = Dp[h];
+  t.xbase = x + ((b * Tlen + t0) * H + h) * P;
+  t.ybase = y + ((b * Tlen + t0) * H + h) * P;
+  t.bbase = Bm + ((b * Tlen + t0) * G + grp) * N;
+  t.cbase = Cm + ((b * Tlen + t0) * G + grp) * N;
+  t.gc = gcum + (b * H + h) * Tp + t0;
+  t.dtc = dtt + (b * H + h) * Tp + t0;
+  t.hsrc = static_cast<const unsigned char*>(hprev) + (((b * H + h) * nc + k) * (int64_t)(P * N)) * 4;
+  return t;
+}
+
+// Persistent form of the kernel above, used when the carried state fits in
+// LDS. Each workgroup walks a contiguous range of tiles (see make_tile); one
+// stream of direct global->LDS loads runs across tile boundaries: while a
+// tile's j-blocks are consumed, the next tile's Hprev (into the LDS buffer
+// freed once this tile's carried-state product is done) and its first two
+// j-blocks (into the ring slots as they free) are already in flight, and
+// the next tile's G' and dt are loaded into registers behind this tile's y
+// stores. The arithmetic
+// is the kernel above's, step for step.
+//
+// Load accounting: every wave issues LOADS instructions per j-block and
+// HLOADS per Hprev, in program order; vector memory operations complete in
+// issue order, so "item X has landed" is "at most (operations issued after
+// X) remain". The counts used below include only this stream's own loads,
+// a lower bound whenever the compiler adds loads or stores of its own.
+template <typename T, int P, int N, int Q>
+__global__ __launch_bounds__((ScanCfg<T, P, N, Q>::THREADS)) __attribute__((amdgpu_waves_per_eu(2)))
+void ssd_chunk_scan_persistent(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
+                               const float* __restrict__ gcum, const float* __restrict__ dtt,
+                               const float* __restrict__ Dp, const void* __restrict__ hprev, T* __restrict__ y,
+                               int64_t Tlen, int H, int G, int64_t nc, int64_t Tp, int64_t ntiles, int xcd) {
+  using I = Io<T>;
+  using Frag = typename I::Frag;
+  using Cfg = ScanCfg<T, P, N, Q>;
+  constexpr int E = I::E, KPL = I::KPL, CG = Cfg::CG, NTB = Cfg::NTB, TBW = Cfg::TBW;
+  constexpr int PGW = Cfg::PGW, NPS = Cfg::NPS, WAVES = Cfg::WAVES;
+  constexpr int LOADS = Cfg::LOADS, HLOADS = Cfg::HLOADS;
+  constexpr int BRB = Cfg::BROWP * 16, XRB = Cfg::XROWP * 16;
+  constexpr int KS = N / (2 * KPL);
+  constexpr int JS = 32 / (2 * KPL);
+  static_assert(Cfg::HLDS && Cfg::NBUF == 3, "persistent form: Hprev in LDS, three ring slots");
+  static_assert(Q <= Cfg::THREADS, "one token of G' per thread");
+
+  __shared__ __attribute__((aligned(16))) unsigned char ring[3][Cfg::BLOCK];
+  __shared__ __attribute__((aligned(16))) unsigned char sH[Cfg::HALLOC];
+  __shared__ __attribute__((aligned(16))) float sG[Q];
+  __shared__ __attribute__((aligned(16))) float sDt[Q];
+  __shared__ __attribute__((aligned(16))) float sW[Q];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int tg = wave / NPS, pg0 = (wave % NPS) * PGW;
+  int tbs[TBW];
+  tbs[0] = tg;
+  if constexpr (TBW == 2) tbs[1] = NTB - 1 - tg;
+  int tmax = tbs[0];
+  if constexpr (TBW == 2) tmax = tbs[1];
+  const int64_t xrow = (int64_t)H * P, brow = (int64_t)G * N;
+  uint32_t brc[LOADS];
+  plan_block_rc<Cfg>(brc, wave, threadIdx.x % 64);
+  const uint32_t bsb = (uint32_t)(brow * (int64_t)sizeof(T)), xsb = (uint32_t)(xrow * (int64_t)sizeof(T));
+  const bool use_xcd = xcd != 0;
+
+  // this workgroup's contiguous range [pos, last) of the tile numbering
+  int64_t pos, last;
+  if (use_xcd) {
+    const int64_t n8 = ntiles / 8, g8 = gridDim.x / 8, xg = blockIdx.x % 8, idx = blockIdx.x / 8;
+    pos = xg * n8 + idx * n8 / g8;
+    last = xg * n8 + (idx + 1) * n8 / g8;
+  } else {
+    pos = blockIdx.x * ntiles / gridDim.x;
+    last = (blockIdx.x + 1) * ntiles / gridDim.x;
+  }
+  if (pos >= last) return;
+  Tile<T> cur = make_tile<T, P, N, Q>(pos, use_xcd, ntiles, x, Bm, Cm, gcum, dtt, Dp, hprev, y, Tlen, H, G, nc, Tp);
+
+  // j-block jb of tile t into ring slot `slot`
+#define SSD_ISSUE(slot, t, jb)                                                                              \
+  issue_block_rc<Cfg>(ring[slot], reinterpret_cast<const unsigned char*>((t).bbase),                        \
+                      reinterpret_cast<const unsigned char*>((t).xbase), bsb, xsb, brc, jb, (t).nvalid, wave)
+
+  // stream head: Hprev and j-blocks 0, 1 of the first tile; its G' and dt
+  int tid = threadIdx.x, lane = tid % 64;
+  issue_hprev<Cfg, T>(sH, cur.hsrc, wave, lane);
+  SSD_ISSUE(0, cur, 0);
+  SSD_ISSUE(1, cur, 1);
+  int slot0 = 0;   // ring slot of the current tile's j-block 0
+  float pre_g = 0.f, pre_d = 0.f, pre_l = 0.f;
+  if (tid < Q) {
+    pre_g = cur.gc[tid];
+    pre_d = cur.dtc[tid];
+    pre_l = cur.gc[tid | 31];
+  }
+
+  Frag cf[TBW][KS];
+  int64_t cf_key = -1;
+  while (true) {
+    // Lane-derived addresses are rebuilt for every tile: an opaque copy of
+    // the thread index keeps the compiler from hoisting them out of the tile
+    // loop, where they would all stay live across it.
+    asm volatile("" : "+v"(tid));
+    lane = tid % 64;
+    const int m = lane % 32, g = lane / 32;
+    const int boff = m * BRB + g * 16 * (KPL == 8 ? 1 : 0) + (KPL == 8 ? 0 : g * 4);
+    const int xoff = 4 * g * XRB + (pg0 * CG + E * m) * (int)sizeof(T);
+    const int64_t npos = pos + 1;
+    const bool has_next = npos < last;
+    // (the last tile describes itself as its successor; nothing is loaded for it)
+    const Tile<T> nxt = make_tile<T, P, N, Q>(has_next ? npos : pos, use_xcd, ntiles, x, Bm, Cm, gcum, dtt, Dp,
+                                              hprev, y, Tlen, H, G, nc, Tp);
+
+    // 1. C fragments of the wave's t-blocks, unless the previous tile had the same C rows
+    if (cur.ckey != cf_key) {
+      cf_key = cur.ckey;
+#pragma unroll
+      for (int u = 0; u < TBW; ++u) {
+        const int t = tbs[u] * 32 + m;
+        const bool valid = t < cur.nvalid;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) cf[u][s] = I::load_row(cur.cbase + t * brow + s * 2 * KPL + KPL * g, valid);
+      }
+    }
+    // every wave is past the previous tile's reads of sG, sDt and sW
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (tid < Q) {
+      sG[tid] = pre_g;
+      sDt[tid] = pre_d;
+      sW[tid] = pre_d * exp2_hw(pre_l - pre_g);   // exponent <= 0
+    }
+
+    // 2. carried state. Hprev has landed once at most the two j-blocks
+    // issued after it remain (the barrier also publishes sG, sDt, sW).
+    f32x16 acc[TBW][PGW][E];
+#pragma unroll
+    for (int u = 0; u < TBW; ++u)
+#pragma unroll
+      for (int q = 0; q < PGW; ++q)
+#pragma unroll
+        for (int pe = 0; pe < E; ++pe) acc[u][q][pe] = f32x16{};
+    wait_vm_barrier<2 * LOADS>();
+#pragma unroll
+    for (int q = 0; q < PGW; ++q)
+#pragma unroll
+      for (int pe = 0; pe < E; ++pe) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          Frag hhi, hlo;
+          const int slot = E == 2 ? (pg0 + q) * 64 + pe * 32 + m : (pg0 + q) * CG + E * m + pe;
+          const unsigned char* hp = sH + slot * (Cfg::HROWP * 16);
+          if constexpr (I::SPLIT) {
+            hhi = *reinterpret_cast<const Frag*>(hp + (2 * s + g) * 32);
+            hlo = *reinterpret_cast<const Frag*>(hp + (2 * s + g) * 32 + 16);
+          } else {
+            hhi = *reinterpret_cast<const Frag*>(hp + (s * 2 * KPL + KPL * g) * 4);
+          }
+#pragma unroll
+          for (int u = 0; u < TBW; ++u) {
+            I::mma(acc[u][q][pe], cf[u][s], hhi);
+            if constexpr (I::SPLIT) I::mma(acc[u][q][pe], cf[u][s], hlo);
+          }
+        }
+      }
+    // every wave is done with sH: the next tile's Hprev may land there
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (has_next) issue_hprev<Cfg, T>(sH, nxt.hsrc, wave, lane);
+#pragma unroll
+    for (int u = 0; u < TBW; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float sc = exp2_hw(sG[tbs[u] * 32 + drow(r, g)]);
+#pragma unroll
+        for (int q = 0; q < PGW; ++q)
+#pragma unroll
+          for (int pe = 0; pe < E; ++pe) acc[u][q][pe][r] *= sc;
+      }
+
+    // 3. intra-chunk, causal over 32-token j-blocks
+    float gt[TBW];
+#pragma unroll
+    for (int u = 0; u < TBW; ++u) gt[u] = sG[tbs[u] * 32 + m];
+    for (int jb = 0; jb < NTB; ++jb) {
+      // block jb has landed once only the stream items issued after it remain:
+      // the next j-block (issued one iteration earlier, or before this tile
+      // for jb = 0) and, for jb <= 1, the next tile's Hprev
+      const bool blk_after = jb == 0 || jb + 1 < NTB || has_next;
+      const bool h_after = jb <= 1 && has_next;
+      if (blk_after && h_after) wait_vm_barrier<LOADS + HLOADS>();
+      else if (blk_after) wait_vm_barrier<LOADS>();
+      else if (h_after) wait_vm_barrier<HLOADS>();
+      else wait_vm_barrier<0>();
+      {
+        const int jn = jb + 2, sn = (slot0 + jn) % 3;
+        if (jn < NTB) SSD_ISSUE(sn, cur, jn);
+        else if (has_next) SSD_ISSUE(sn, nxt, jn - NTB);
+      }
+      if (jb > tmax) continue;
+
+      const unsigned char* sb = ring[(slot0 + jb) % 3] + boff;
+      const unsigned char* sx = ring[(slot0 + jb) % 3] + Cfg::BBYTES + xoff;
+      const int j0 = jb * 32;
+      float wj[16];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 wv = *reinterpret_cast<const float4*>(&sW[j0 + 8 * c + 4 * g]);
+        wj[4 * c + 0] = wv.x; wj[4 * c + 1] = wv.y; wj[4 * c + 2] = wv.z; wj[4 * c + 3] = wv.w;
+      }
+      Frag xf[PGW][E][JS];
+#pragma unroll
+      for (int q = 0; q < PGW; ++q)
+#pragma unroll
+        for (int js = 0; js < JS; ++js) {
+          uint32_t d[KPL];
+#pragma unroll
+          for (int i = 0; i < KPL; ++i) {
+            const int q2 = js * KPL + i;
+            d[i] = *reinterpret_cast<const uint32_t*>(sx + (8 * (q2 / 4) + q2 % 4) * XRB + q * CG * (int)sizeof(T));
+          }
+#pragma unroll
+          for (int pe = 0; pe < E; ++pe) xf[q][pe][js] = I::from_dwords(d, pe);
+        }
+      const float gend = sG[j0 + 31];
+#pragma unroll
+      for (int u = 0; u < TBW; ++u) {
+        const int tb = tbs[u];
+        if (tb < jb) continue;
+        f32x16 cb = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const Frag bfr = *reinterpret_cast<const Frag*>(sb + s * 2 * KPL * (int)sizeof(T));
+          I::mma(cb, bfr, cf[u][s]);
+        }
+        float v[16];
+        if (tb > jb) {
+          const float a = exp2_hw(gt[u] - gend);
+#pragma unroll
+          for (int q = 0; q < 16; ++q) v[q] = cb[q] * (wj[q] * a);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int jr = drow(q, g);
+            const float val = cb[q] * exp2_hw(gt[u] - sG[j0 + jr]) * sDt[j0 + jr];
+            v[q] = (m >= jr) ? val : 0.f;
+          }
+        }
+#pragma unroll
+        for (int js = 0; js < JS; ++js) {
+          Frag ahi, alo;
+          I::split(&v[js * KPL], ahi, alo);
+#pragma unroll
+          for (int q = 0; q < PGW; ++q)
+#pragma unroll
+            for (int pe = 0; pe < E; ++pe) {
+              I::mma(acc[u][q][pe], ahi, xf[q][pe][js]);
+              if constexpr (I::SPLIT) I::mma(acc[u][q][pe], alo, xf[q][pe][js]);
+            }
+        }
+        if (tb == jb) {
+#pragma unroll
+          for (int q = 0; q < PGW; ++q)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const uint32_t xd = *reinterpret_cast<const uint32_t*>(
+                  sx + (8 * (r / 4) + r % 4) * XRB + q * CG * (int)sizeof(T));
+#pragma unroll
+              for (int pe = 0; pe < E; ++pe) acc[u][q][pe][r] += cur.Dh * I::elem(xd, pe);
+            }
+        }
+      }
+    }
+
+    // the next tile's G' and dt, in flight behind this tile's y stores
+    if (has_next && tid < Q) {
+      pre_g = nxt.gc[tid];
+      pre_d = nxt.dtc[tid];
+      pre_l = nxt.gc[tid | 31];
+    }
+
+    // 4. y
+#pragma unroll
+    for (int u = 0; u < TBW; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = tbs[u] * 32 + drow(r, g);
+        if (t < cur.nvalid) {
+#pragma unroll
+          for (int q = 0; q < PGW; ++q)
+            I::store_pair(cur.ybase + t * xrow + (pg0 + q) * CG + E * m, acc[u][q][0][r], acc[u][q][E - 1][r]);
+        }
+      }
+    if (!has_next) break;
+    slot0 = (slot0 + NTB) % 3;
+    pos = npos;
+    cur = nxt;
+  }
+#undef SSD_ISSUE
+}
+
+// Workgroups of the persistent form that fit on the current device at once
+// (cached per device; a failed query falls back to 256).
+template <typename T, int P, int N, int Q>
+int64_t persistent_grid(int64_t ntiles) {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    dev = 0;
+  }
+  if (!cached[dev]) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ssd_chunk_scan_persistent<T, P, N, Q>,
+                                                     ScanCfg<T, P, N, Q>::THREADS, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0) {
+      (void)hipGetLastError();
+      cus = 256;
+      per_cu = 1;
+    }
+    cached[dev] = cus * per_cu;
+  }
+  int64_t grid = cached[dev] < ntiles ? cached[dev] : ntiles;
+  if (grid >= 8) grid -= grid % 8;
+  return grid;
+}
+
 template <typename T, int P, int N, int Q>
 hipError_t launch_one(const Problem& p, hipStream_t stream) {
   using Cfg = ScanCfg<T, P, N, Q>;
-  const dim3 grid((unsigned)p.H, (unsigned)p.nc, (unsigned)p.bt);
-  hipLaunchKernelGGL((ssd_chunk_scan<T, P, N, Q>), grid, dim3(Cfg::THREADS), 0, stream, (const T*)p.x,
-                     (const T*)p.B, (const T*)p.C, p.gcum, p.dtt, p.D, (const void*)p.hprev, (T*)p.y, p.T,
-                     (int)p.H, (int)p.G, p.nc, p.Tp);
+  if constexpr (Cfg::HLDS && Cfg::NBUF == 3) {
+    const int64_t ntiles = p.bt * p.nc * p.H;
+    if (ntiles == 0) return hipSuccess;
+    const int64_t grid = persistent_grid<T, P, N, Q>(ntiles);
+    const int xcd = (grid % 8 == 0 && (p.bt * p.nc) % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((ssd_chunk_scan_persistent<T, P, N, Q>), dim3((unsigned)grid), dim3(Cfg::THREADS), 0,
+                       stream, (const T*)p.x, (const T*)p.B, (const T*)p.C, p.gcum, p.dtt, p.D,
+                       (const void*)p.hprev, (T*)p.y, p.T, (int)p.H, (int)p.G, p.nc, p.Tp, ntiles, xcd);
+  } else {
+    const dim3 grid((unsigned)p.H, (unsigned)p.nc, (unsigned)p.bt);
+    hipLaunchKernelGGL((ssd_chunk_scan<T, P, N, Q>), grid, dim3(Cfg::THREADS), 0, stream, (const T*)p.x,
+                       (const T*)p.B, (const T*)p.C, p.gcum, p.dtt, p.D, (const void*)p.hprev, (T*)p.y, p.T,
+                       (int)p.H, (int)p.G, p.nc, p.Tp);
+  }
   return hipGetLastError();
 }
 

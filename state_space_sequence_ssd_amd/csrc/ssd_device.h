@@ -146,6 +146,19 @@ __device__ __forceinline__ uint32_t buf_load_dword(__amdgpu_buffer_rsrc_t r, uin
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
+// Direct global->LDS load of 16 bytes per lane: lane i's 16 bytes at gptr
+// land at LDS address lds + 16 i (lds wave-uniform; it goes in M0). Written
+// as inline assembly so the compiler does not treat the asynchronous LDS
+// write as aliasing every later LDS read and wait for the whole vector
+// memory queue before each of them: the kernels order these loads
+// themselves, with explicit vmcnt waits and barriers. The compiler still
+// counts them nowhere, which keeps its own waits conservative (they can
+// only see more operations outstanding than they assume).
+__device__ __forceinline__ void lds_dma16(const void* gptr, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(gptr) : "memory", "m0");
+}
+
 // Row of the 32x32 D block held in register r of a lane in half g = l/32.
 __device__ __forceinline__ constexpr int drow(int r, int g) { return 8 * (r / 4) + 4 * g + (r % 4); }
 
