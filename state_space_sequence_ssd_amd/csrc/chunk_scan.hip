@@ -551,6 +551,9 @@ __device__ __forceinline__ Tile<T> make_tile(int64_t gi, bool xcd, int64_t ntile
   return t;
 }
 
+// vmcnt's largest count.
+__device__ __forceinline__ constexpr int cap63(int n) { return n < 63 ? n : 63; }
+
 // Persistent form of the kernel above, used when the carried state fits in
 // LDS. Each workgroup walks a contiguous range of tiles (see make_tile); one
 // stream of direct global->LDS loads runs across tile boundaries: while a
@@ -583,6 +586,7 @@ void ssd_chunk_scan_persistent(const T* __restrict__ x, const T* __restrict__ Bm
   constexpr int JS = 32 / (2 * KPL);
   static_assert(Cfg::HLDS && Cfg::NBUF == 3, "persistent form: Hprev in LDS, three ring slots");
   static_assert(Q <= Cfg::THREADS, "one token of G' per thread");
+  constexpr int NYS = TBW * 16 * PGW;   // y store instructions per wave of a full tile
 
   __shared__ __attribute__((aligned(16))) unsigned char ring[3][Cfg::BLOCK];
   __shared__ __attribute__((aligned(16))) unsigned char sH[Cfg::HALLOC];
@@ -636,6 +640,10 @@ void ssd_chunk_scan_persistent(const T* __restrict__ x, const T* __restrict__ Bm
 
   Frag cf[TBW][KS];
   int64_t cf_key = -1;
+  // 1 when the previous tile issued exactly NYS y stores per wave (a full
+  // tile): the waits below then count them, so they do not also wait for
+  // the stores' write acknowledgements (vmcnt covers loads and stores alike)
+  int ys = 0;
   while (true) {
     // Lane-derived addresses are rebuilt for every tile: an opaque copy of
     // the thread index keeps the compiler from hoisting them out of the tile
@@ -661,6 +669,14 @@ void ssd_chunk_scan_persistent(const T* __restrict__ x, const T* __restrict__ Bm
 #pragma unroll
         for (int s = 0; s < KS; ++s) cf[u][s] = I::load_row(cur.cbase + t * brow + s * 2 * KPL + KPL * g, valid);
       }
+      // consume the fragments here, so the compiler's wait for these loads
+      // stays on this (rare) path instead of draining the whole load queue
+      // before every tile's first product
+#pragma unroll
+      for (int u = 0; u < TBW; ++u)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) asm volatile("" ::"v"(cf[u][s]));
+      ys = 0;   // that wait also waited for the stores
     }
     // every wave is past the previous tile's reads of sG, sDt and sW
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
@@ -671,7 +687,9 @@ void ssd_chunk_scan_persistent(const T* __restrict__ x, const T* __restrict__ Bm
     }
 
     // 2. carried state. Hprev has landed once at most the two j-blocks
-    // issued after it remain (the barrier also publishes sG, sDt, sW).
+    // issued after it remain -- after the previous tile's C.Hprev came all
+    // NTB of its j-block issues and its y stores (the barrier also publishes
+    // sG, sDt, sW).
     f32x16 acc[TBW][PGW][E];
 #pragma unroll
     for (int u = 0; u < TBW; ++u)
@@ -679,7 +697,8 @@ void ssd_chunk_scan_persistent(const T* __restrict__ x, const T* __restrict__ Bm
       for (int q = 0; q < PGW; ++q)
 #pragma unroll
         for (int pe = 0; pe < E; ++pe) acc[u][q][pe] = f32x16{};
-    wait_vm_barrier<2 * LOADS>();
+    if (ys) wait_vm_barrier<cap63(NTB * LOADS + NYS)>();
+    else wait_vm_barrier<2 * LOADS>();
 #pragma unroll
     for (int q = 0; q < PGW; ++q)
 #pragma unroll
@@ -724,12 +743,20 @@ void ssd_chunk_scan_persistent(const T* __restrict__ x, const T* __restrict__ Bm
       // block jb has landed once only the stream items issued after it remain:
       // the next j-block (issued one iteration earlier, or before this tile
       // for jb = 0) and, for jb <= 1, the next tile's Hprev
+      // (and, for jb <= 1 after a full tile, that tile's NYS y stores)
       const bool blk_after = jb == 0 || jb + 1 < NTB || has_next;
       const bool h_after = jb <= 1 && has_next;
-      if (blk_after && h_after) wait_vm_barrier<LOADS + HLOADS>();
-      else if (blk_after) wait_vm_barrier<LOADS>();
-      else if (h_after) wait_vm_barrier<HLOADS>();
-      else wait_vm_barrier<0>();
+      if (jb <= 1 && ys) {
+        if (blk_after && h_after) wait_vm_barrier<cap63(LOADS + HLOADS + NYS)>();
+        else if (blk_after) wait_vm_barrier<cap63(LOADS + NYS)>();
+        else if (h_after) wait_vm_barrier<cap63(HLOADS + NYS)>();
+        else wait_vm_barrier<cap63(NYS)>();
+      } else {
+        if (blk_after && h_after) wait_vm_barrier<LOADS + HLOADS>();
+        else if (blk_after) wait_vm_barrier<LOADS>();
+        else if (h_after) wait_vm_barrier<HLOADS>();
+        else wait_vm_barrier<0>();
+      }
       {
         const int jn = jb + 2, sn = (slot0 + jn) % 3;
         if (jn < NTB) SSD_ISSUE(sn, cur, jn);
@@ -829,6 +856,7 @@ void ssd_chunk_scan_persistent(const T* __restrict__ x, const T* __restrict__ Bm
             I::store_pair(cur.ybase + t * xrow + (pg0 + q) * CG + E * m, acc[u][q][0][r], acc[u][q][E - 1][r]);
         }
       }
+    ys = cur.nvalid == Q ? 1 : 0;
     if (!has_next) break;
     slot0 = (slot0 + NTB) % 3;
     pos = npos;

@@ -104,6 +104,8 @@ template <> struct Io<bf16> {
   __device__ static __forceinline__ void store_pair(bf16* p, float a, float b) {
     *reinterpret_cast<uint32_t*>(p) = pack_bf16x2(a, b);
   }
+  // the dword store_pair writes
+  __device__ static __forceinline__ uint32_t pack_pair(float a, float b) { return pack_bf16x2(a, b); }
   __device__ static __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     u32x2 v;
@@ -129,6 +131,7 @@ template <> struct Io<float> {
   __device__ static __forceinline__ Frag from_dwords(const uint32_t* d, int) { return __uint_as_float(d[0]); }
   __device__ static __forceinline__ Frag load_row(const float* p, bool valid) { return valid ? *p : 0.f; }
   __device__ static __forceinline__ void store_pair(float* p, float a, float) { *p = a; }
+  __device__ static __forceinline__ uint32_t pack_pair(float a, float) { return __float_as_uint(a); }
   __device__ static __forceinline__ void store4(float* p, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
   }
@@ -144,6 +147,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 }
 __device__ __forceinline__ uint32_t buf_load_dword(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+// Store through a buffer resource; with the whole offset in the vector
+// operand, bytes at or past the resource's size are dropped.
+__device__ __forceinline__ void buf_store_dword(uint32_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, voff, 0, 0);
 }
 
 // Direct global->LDS load of 16 bytes per lane: lane i's 16 bytes at gptr
