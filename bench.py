@@ -34,6 +34,41 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 F32_PEAK_TFLOPS = 157.3        # MI355X dense fp32 MFMA, published
 KERNELS = ["ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_pass", "ssd_chunk_scan"]
+KERNEL_SOURCES = {"ssd_chunk_cumsum": "chunk_cumsum.hip", "ssd_chunk_state": "chunk_state.hip",
+                  "ssd_state_pass": "state_pass.hip", "ssd_chunk_scan": "chunk_scan.hip"}
+TRAFFIC_SUMMARY = {"mamba2-2.7b": "hbm_traffic_mamba2-2.7b.md"}
+
+
+def source_hash(kernel):
+    """sha256 (first 16 hex digits) of a kernel's .hip file followed by the two
+    shared device headers: the key under which measured traffic is recorded."""
+    import hashlib
+    csrc = os.path.join(ROOT, "state_space_sequence_ssd_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "ssd_device.h", "ssd_launch.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per dispatch of `kernel` from the committed FETCH_SIZE/WRITE_SIZE
+    summary (each counter scaled against a plain copy of known size), or None
+    when there is no summary for the workload or the kernel's sources changed
+    since the counters were taken."""
+    name = TRAFFIC_SUMMARY.get(workload)
+    if name is None:
+        return None
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    want = source_hash(kernel)
+    with open(path) as fh:
+        for line in fh:
+            f = line.split()
+            if len(f) == 4 and f[0] == "traffic" and f[1] == kernel:
+                return int(f[2]) if f[3] == want else None
+    return None
 
 
 def algorithmic_cost(cfg):
@@ -185,6 +220,7 @@ def main():
                    "alg_TFLOP/s": round(flops / sec / 1e12, 2), "frac_mfma": round(flops / sec / 1e12 / peak_tf, 4)}
     dom = max(KERNELS, key=lambda k: per_kernel_ms[k])
     achieved = kern[dom]["GB/s"]
+    traffic = measured_traffic(cfg.name, dom)
 
     out = {
         "metric": "SSD fwd tokens/sec at 2.7B-layer shape (1 GPU); % MFMA peak / % HBM BW",
@@ -203,7 +239,9 @@ def main():
                    "headdim": cfg.headdim, "dstate": cfg.dstate, "ngroups": cfg.ngroups, "chunk": cfg.chunk,
                    "io": cfg.io, "seed": cfg.seed, "tokens_per_step": tokens},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "bytes/launch",
+                     "traffic_GB/s": None if traffic is None else round(traffic / (per_kernel_ms[dom] * 1e6), 1)},
         "gpu_event_ms_per_step": round(gpu_ms, 4),
         "kernels": kern,
         "path_bytes_per_step": int(sum(c[0] for c in cost.values())),
