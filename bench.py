@@ -13,6 +13,10 @@ launch stream inside the timed region), per-kernel figures, and the CPU
 oracle's throughput on a bounded sample of the same layer (timed on this
 host's cores), whose outputs also check the benchmarked GPU output.
 
+With --config mamba2-2.7b-decode it times the one-token decode step instead
+(256 sequences of the same layer advanced by one token per step, the state
+updated in place), with the same JSON fields.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
 """
 from __future__ import annotations
@@ -35,17 +39,20 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 F32_PEAK_TFLOPS = 157.3        # MI355X dense fp32 MFMA, published
 KERNELS = ["ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_pass", "ssd_chunk_scan"]
 KERNEL_SOURCES = {"ssd_chunk_cumsum": "chunk_cumsum.hip", "ssd_chunk_state": "chunk_state.hip",
-                  "ssd_state_pass": "state_pass.hip", "ssd_chunk_scan": "chunk_scan.hip"}
-TRAFFIC_SUMMARY = {"mamba2-2.7b": "hbm_traffic_mamba2-2.7b.md"}
+                  "ssd_state_pass": "state_pass.hip", "ssd_chunk_scan": "chunk_scan.hip",
+                  "ssd_step": "ssd_step.hip"}
+TRAFFIC_SUMMARY = {"mamba2-2.7b": "hbm_traffic_mamba2-2.7b.md",
+                   "mamba2-2.7b-decode": "hbm_traffic_mamba2-2.7b-decode.md"}
 
 
 def source_hash(kernel):
-    """sha256 (first 16 hex digits) of a kernel's .hip file followed by the two
-    shared device headers: the key under which measured traffic is recorded."""
+    """sha256 (first 16 hex digits) of a kernel's .hip file followed by the
+    shared device header: the key under which measured traffic is recorded.
+    (ssd_launch.h holds only host-side declarations.)"""
     import hashlib
     csrc = os.path.join(ROOT, "state_space_sequence_ssd_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "ssd_device.h", "ssd_launch.h"):
+    for f in (KERNEL_SOURCES[kernel], "ssd_device.h"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -95,6 +102,121 @@ def algorithmic_cost(cfg):
                            + Bt * G * nc * Q * (Q + 1) * N),               # causal C . B^T once per group
     }
     return cost
+
+
+def copy_calibration(dev):
+    """One plain device-to-device copy of a 256 MiB buffer: a dispatch of known
+    size that FETCH_SIZE / WRITE_SIZE can be scaled against."""
+    import torch
+    src_buf = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+    dst_buf = torch.empty_like(src_buf)
+    dst_buf.copy_(src_buf)
+    torch.cuda.synchronize()
+    del src_buf, dst_buf
+
+
+def decode_bytes(cfg):
+    """Algorithmic bytes of one decode step: the fp32 state read and written,
+    x and y, B and C, dt, A and D, each once."""
+    e = 2 if cfg.io == "bf16" else 4
+    Bt, H, P, N, G = cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups
+    return 8 * Bt * H * P * N + 2 * Bt * H * P * e + 2 * Bt * G * N * e + 4 * Bt * H + 8 * H
+
+
+def run_decode(args, cfg):
+    import torch
+
+    import state_space_sequence_ssd_amd as ssd
+    from workloads import generate
+
+    dev = torch.device("cuda:0")
+    inp = generate(cfg)
+
+    def to_dev(k, a):
+        if cfg.io == "bf16" and k in ("x", "B", "C"):
+            return torch.from_numpy(np.ascontiguousarray(inp[k + "_bits"][:, 0]).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    x, dt, B, C = (to_dev(k, inp[k][:, 0]) for k in ("x", "dt", "B", "C"))
+    A, D = to_dev("A", inp["A"]), to_dev("D", inp["D"])
+    state = to_dev("state", inp["init_state"])
+    y = torch.empty_like(x)
+    io = ssd.BF16 if cfg.io == "bf16" else ssd.F32
+    dims = ssd.StepDims(cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups)
+    stream = torch.cuda.current_stream(dev)
+    ptrs = (x.data_ptr(), dt.data_ptr(), A.data_ptr(), B.data_ptr(), C.data_ptr(), D.data_ptr(),
+            state.data_ptr(), y.data_ptr())
+
+    if args.copy_calibration:
+        copy_calibration(dev)
+    # first step checked against the oracle before anything is timed
+    ssd.ssd_step_ptr(dims, io, *ptrs, stream.cuda_stream)
+    torch.cuda.synchronize()
+    y_first = y.float().cpu().numpy()
+    for _ in range(args.warmup):
+        ssd.ssd_step_ptr(dims, io, *ptrs, stream.cuda_stream)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        ssd.ssd_step_ptr(dims, io, *ptrs, stream.cuda_stream)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])) * 1e3
+    nbytes = decode_bytes(cfg)
+    achieved = nbytes / (us * 1e-6) / 1e9
+    out = {
+        "metric": "SSD decode step tokens/sec (one token per sequence per step, 1 GPU); % HBM BW",
+        "value": round(cfg.batch * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.io == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "nheads": cfg.nheads, "headdim": cfg.headdim,
+                   "dstate": cfg.dstate, "ngroups": cfg.ngroups, "io": cfg.io, "seed": cfg.seed,
+                   "tokens_per_step": cfg.batch},
+        "roofline": {"bound": "hbm", "kernel": "ssd_step", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(cfg.name, "ssd_step"), "traffic_unit": "bytes/launch"},
+        "kernels": {"ssd_step": {"us": round(us, 2), "alg_bytes": int(nbytes), "GB/s": round(achieved, 1),
+                                 "frac_hbm": round(achieved / HBM_PEAK_GBS, 4)}},
+    }
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import ssd_step
+
+        cores = len(os.sched_getaffinity(0))
+        threads = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+        with threadpool_limits(limits=threads, user_api="blas"):
+            rows, t0, worst = 0, time.perf_counter(), 0.0
+            while rows < cfg.batch and (rows == 0 or time.perf_counter() - t0 < 10.0):
+                b = slice(rows, rows + 1)
+                yr, _ = ssd_step(inp["x"][b, 0], inp["dt"][b, 0], inp["A"], inp["B"][b, 0], inp["C"][b, 0],
+                                 inp["D"], inp["init_state"][b])
+                yg = y_first[b].astype(np.float64)
+                if cfg.io == "bf16":
+                    worst = max(worst, float(np.max(np.abs(yg - yr) / (1e-2 + 2e-2 * np.abs(yr)))))
+                else:
+                    worst = max(worst, float(np.max(np.abs(yg - yr)) / max(np.max(np.abs(yr)), 1e-30) / 1e-5))
+                rows += 1
+            elapsed = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": rows / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"fp64 step oracle on sequences 0..{rows - 1} of {cfg.batch} "
+                                         f"(all {cfg.nheads} heads), {elapsed:.1f} s", "seconds": elapsed}
+        out["parity_vs_oracle"] = {"rows_checked": rows, "worst_err_over_tolerance": worst, "ok": worst <= 1.0}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(cfg, inp, y_gpu, budget_s=10.0):
@@ -158,6 +280,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     cfg = config_by_name(args.config)
+    if cfg.seqlen == 1 and cfg.name.endswith("-decode"):
+        return run_decode(args, cfg)
     dev = torch.device("cuda:0")
     inp = generate(cfg)
     io = ssd.BF16 if cfg.io == "bf16" else ssd.F32
@@ -188,11 +312,7 @@ def main():
         ssd.ssd_fwd_timed_ptr(dims, io, *ptrs, stream.cuda_stream, [e.cuda_event for e in evs])
 
     if args.copy_calibration:
-        src_buf = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)   # 256 MiB
-        dst_buf = torch.empty_like(src_buf)
-        dst_buf.copy_(src_buf)
-        torch.cuda.synchronize()
-        del src_buf, dst_buf
+        copy_calibration(dev)
 
     warm = new_events()
     for _ in range(args.warmup):

@@ -65,6 +65,8 @@ extern "C" {
 #define MAMBA2_SSD_ERR_ALIAS        (-7) /* an output overlaps another array          */
 #define MAMBA2_SSD_ERR_HIP          (-8) /* a kernel launch failed; see
                                             mamba2_ssd_last_hip_error()               */
+#define MAMBA2_SSD_ERR_ALIGN        (-9) /* a pointer lacks the alignment an entry
+                                            point documents                           */
 
 /* ---- io dtypes: the element type of x, B, C and y ---------------------- */
 #define MAMBA2_SSD_F32  0   /* IEEE binary32                                    */
@@ -178,6 +180,58 @@ int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* dims, int io_dtype,
                          const float* init_state, void* y, float* final_state,
                          void* workspace, size_t workspace_bytes, void* stream,
                          void* const* events);
+
+/* ---- one decode step ----------------------------------------------------
+ *
+ * The recurrent form of the same layer (blog section "Mamba-2 architecture":
+ * the core recurrence, which the blog notes suits token-by-token inference):
+ * each of `batch` sequences advances by one token, for every head h, with
+ * g = h / (nheads / ngroups),
+ *
+ *     state[b,h,p,n] <- exp(A[h] * dt[b,h]) * state[b,h,p,n]
+ *                       + dt[b,h] * x[b,h,p] * B[b,g,n]
+ *     y[b,h,p]        = sum_n C[b,g,n] * state[b,h,p,n] + D[h] * x[b,h,p]
+ *
+ * (y reads the updated state, as in the forward pass). The state is the
+ * final_state of mamba2_ssd_fwd (same layout), updated in place, so a
+ * prefill followed by steps continues the same sequence. One kernel reads
+ * and writes the state once: the step is bound by HBM bandwidth. */
+typedef struct {
+  int64_t batch;    /* sequences, each advanced by one token (0 = nothing to do) */
+  int64_t nheads;   /* H  */
+  int64_t headdim;  /* P: any >= 1                                           */
+  int64_t dstate;   /* N: 64, 128 or 256                                     */
+  int64_t ngroups;  /* G: H % G == 0, heads grouped as in mamba2_ssd_fwd     */
+} mamba2_ssd_step_dims;
+
+/* 1 if mamba2_ssd_step has kernels for (dstate, io_dtype), else 0. Host only. */
+int mamba2_ssd_step_supported(int64_t dstate, int io_dtype);
+
+/* Every host-side check of mamba2_ssd_step, without touching the GPU:
+ * sizes (batch * nheads * headdim rows and batch * ngroups * dstate must
+ * stay below 2^31), support, required pointers, alignment (state 16 bytes;
+ * B and C 16 bytes for F32, 8 for BF16) and aliasing (state and y must not
+ * overlap each other or any input). Pointers are only compared. */
+int mamba2_ssd_step_check_args(const mamba2_ssd_step_dims* dims, int io_dtype,
+                               const void* x, const float* dt, const float* A,
+                               const void* B, const void* C, const float* D,
+                               const float* state, const void* y);
+
+/* One decode step.
+ *   x      io    [batch][nheads][headdim]
+ *   dt     float [batch][nheads]              (>= 0)
+ *   A, D   float [nheads]                     (A < 0)
+ *   B, C   io    [batch][ngroups][dstate]
+ *   state  float [batch][nheads][headdim][dstate]  read and written in place
+ *   y      io    [batch][nheads][headdim]     (written)
+ *   stream a hipStream_t, or NULL for the default stream
+ * Arithmetic in fp32 (exp(A dt) on the hardware base-2 exponential); y is
+ * rounded to the io dtype (bf16 nearest-even) once at the end. Asynchronous,
+ * like mamba2_ssd_fwd; returns a status code. */
+int mamba2_ssd_step(const mamba2_ssd_step_dims* dims, int io_dtype,
+                    const void* x, const float* dt, const float* A,
+                    const void* B, const void* C, const float* D,
+                    float* state, void* y, void* stream);
 
 /* Static string naming a status code. Never NULL. */
 const char* mamba2_ssd_status_string(int status);

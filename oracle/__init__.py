@@ -11,6 +11,8 @@ kernels:
 * ``ssd_sequential`` -- the token-by-token recurrence, the plain definition.
 * ``ssd_chunked``    -- the chunk-wise "jump" evaluation through log-space
   cumulative decays, in natural ``exp`` (no base-2 rescaling).
+* ``ssd_step``       -- one token of the recurrence for every sequence and
+  head (the decode step), updating a given state.
 
 Both upcast every input to float64 and never round to a narrower type.
 
@@ -23,5 +25,6 @@ tie both functions to facts fixed outside this package live in
 """
 from .ssd_seq import ssd_sequential, heads_to_groups
 from .ssd_chunked import ssd_chunked
+from .ssd_step import ssd_step
 
-__all__ = ["ssd_sequential", "ssd_chunked", "heads_to_groups"]
+__all__ = ["ssd_sequential", "ssd_chunked", "ssd_step", "heads_to_groups"]

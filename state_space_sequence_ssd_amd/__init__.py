@@ -11,14 +11,16 @@ from __future__ import annotations
 import ctypes
 from typing import Optional, Tuple
 
-from ._lib import (BF16, F32, STATUS, Dims, SsdError, WorkspaceLayout, lib, status_string)
+from ._lib import (BF16, F32, STATUS, Dims, SsdError, StepDims, WorkspaceLayout, lib, status_string)
 
 __all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_layout", "check_args",
            "Dims", "WorkspaceLayout", "SsdError", "F32", "BF16", "STATUS", "status_string",
            "ssd_fwd_timed_ptr", "mamba2_ssd_fwd", "mamba2_ssd_fwd_timed", "mamba2_ssd_check_args",
            "mamba2_ssd_supported",
            "mamba2_ssd_fwd_workspace_bytes", "mamba2_ssd_workspace_layout_query",
-           "mamba2_ssd_status_string", "mamba2_ssd_last_hip_error"]
+           "mamba2_ssd_status_string", "mamba2_ssd_last_hip_error",
+           "ssd_step", "ssd_step_ptr", "step_supported", "step_check_args", "StepDims",
+           "mamba2_ssd_step", "mamba2_ssd_step_check_args", "mamba2_ssd_step_supported"]
 
 # The C entry points under their own names (ctypes functions with prototypes).
 mamba2_ssd_fwd = lib.mamba2_ssd_fwd
@@ -29,6 +31,9 @@ mamba2_ssd_fwd_workspace_bytes = lib.mamba2_ssd_fwd_workspace_bytes
 mamba2_ssd_workspace_layout_query = lib.mamba2_ssd_workspace_layout_query
 mamba2_ssd_status_string = lib.mamba2_ssd_status_string
 mamba2_ssd_last_hip_error = lib.mamba2_ssd_last_hip_error
+mamba2_ssd_step = lib.mamba2_ssd_step
+mamba2_ssd_step_check_args = lib.mamba2_ssd_step_check_args
+mamba2_ssd_step_supported = lib.mamba2_ssd_step_supported
 
 
 def _dims(d) -> Dims:
@@ -133,3 +138,67 @@ def ssd_fwd(x, dt, A, B, C, D, chunk: int, init_state=None, *, return_final_stat
         ssd_fwd_ptr(dims, io, ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), ptr(init_state), ptr(y),
                     ptr(final_state) if return_final_state else 0, ptr(workspace), workspace.numel(), stream)
     return y, (final_state if return_final_state else None)
+
+
+def _step_dims(d) -> StepDims:
+    if isinstance(d, StepDims):
+        return d
+    if isinstance(d, dict):
+        return StepDims(**d)
+    return StepDims(*d)
+
+
+def step_supported(dstate: int, io: int) -> bool:
+    return bool(lib.mamba2_ssd_step_supported(dstate, io))
+
+
+def step_check_args(dims, io, x, dt, A, B, C, D, state, y) -> int:
+    """Host-only validation of a decode step on raw integer addresses (0 for NULL)."""
+    return int(lib.mamba2_ssd_step_check_args(ctypes.byref(_step_dims(dims)), io, x, dt, A, B, C, D, state, y))
+
+
+def ssd_step_ptr(dims, io, x, dt, A, B, C, D, state, y, stream: int = 0) -> None:
+    """mamba2_ssd_step on raw device addresses; raises SsdError on a nonzero status."""
+    st = lib.mamba2_ssd_step(ctypes.byref(_step_dims(dims)), io, x, dt, A, B, C, D, state, y, stream)
+    if st != 0:
+        raise SsdError(st, lib.mamba2_ssd_last_hip_error().decode())
+
+
+def ssd_step(x, dt, A, B, C, D, state, *, y=None):
+    """One decode step on torch CUDA tensors (contiguous, same device).
+
+    x [batch, nheads, headdim] and B, C [batch, ngroups, dstate] share the io
+    dtype (torch.bfloat16 or torch.float32); dt [batch, nheads], A and D
+    [nheads] and state [batch, nheads, headdim, dstate] are float32. The
+    state is updated in place; returns y [batch, nheads, headdim] in the io
+    dtype (written into ``y`` when given). Runs on torch's current stream.
+    """
+    import torch
+
+    if x.dtype == torch.bfloat16:
+        io = BF16
+    elif x.dtype == torch.float32:
+        io = F32
+    else:
+        raise TypeError(f"x must be bfloat16 or float32, got {x.dtype}")
+    for name, t, want in (("B", B, x.dtype), ("C", C, x.dtype), ("dt", dt, torch.float32),
+                          ("A", A, torch.float32), ("D", D, torch.float32), ("state", state, torch.float32)):
+        if t.dtype != want:
+            raise TypeError(f"{name} must be {want}, got {t.dtype}")
+    for t in (x, dt, A, B, C, D, state):
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    bt, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    if tuple(dt.shape) != (bt, H) or tuple(B.shape) != (bt, G, N) or tuple(C.shape) != (bt, G, N) \
+            or tuple(A.shape) != (H,) or tuple(D.shape) != (H,) or tuple(state.shape) != (bt, H, P, N):
+        raise ValueError("inconsistent shapes")
+    if y is None:
+        y = torch.empty_like(x)
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        ssd_step_ptr(StepDims(bt, H, P, N, G), io, x.data_ptr(), dt.data_ptr(), A.data_ptr(), B.data_ptr(),
+                     C.data_ptr(), D.data_ptr(), state.data_ptr(), y.data_ptr(), stream)
+    return y

@@ -19,6 +19,7 @@ STATUS = {
     -6: "ERR_WORKSPACE",
     -7: "ERR_ALIAS",
     -8: "ERR_HIP",
+    -9: "ERR_ALIGN",
 }
 
 
@@ -26,6 +27,11 @@ class Dims(ctypes.Structure):
     """mamba2_ssd_dims"""
     _fields_ = [(n, ctypes.c_int64) for n in
                 ("batch", "seqlen", "nheads", "headdim", "dstate", "ngroups", "chunk")]
+
+
+class StepDims(ctypes.Structure):
+    """mamba2_ssd_step_dims"""
+    _fields_ = [(n, ctypes.c_int64) for n in ("batch", "nheads", "headdim", "dstate", "ngroups")]
 
 
 class WorkspaceLayout(ctypes.Structure):
@@ -77,6 +83,13 @@ def _load():
     L.mamba2_ssd_fwd_timed.argtypes = [dims_p, ctypes.c_int, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, sz, vp,
                                        ctypes.POINTER(ctypes.c_void_p)]
     L.mamba2_ssd_fwd_timed.restype = ctypes.c_int
+    step_p = ctypes.POINTER(StepDims)
+    L.mamba2_ssd_step_supported.argtypes = [i64, ctypes.c_int]
+    L.mamba2_ssd_step_supported.restype = ctypes.c_int
+    L.mamba2_ssd_step_check_args.argtypes = [step_p, ctypes.c_int, vp, fp, fp, vp, vp, fp, fp, vp]
+    L.mamba2_ssd_step_check_args.restype = ctypes.c_int
+    L.mamba2_ssd_step.argtypes = [step_p, ctypes.c_int, vp, fp, fp, vp, vp, fp, fp, vp, vp]
+    L.mamba2_ssd_step.restype = ctypes.c_int
     L.mamba2_ssd_status_string.argtypes = [ctypes.c_int]
     L.mamba2_ssd_status_string.restype = ctypes.c_char_p
     L.mamba2_ssd_last_hip_error.argtypes = []

@@ -1,8 +1,9 @@
-// C ABI of the Mamba-2 chunked SSD forward pass (declared in
-// include/mamba2_ssd.h). Host code only: argument validation, workspace
-// layout, and the four launches in dependency order on the caller's stream
-// (the kernel order of the CUDA Tile Mamba-2 blog: cumulative sum, state
-// pass, then the outputs, with the state contraction split out of the pass).
+// C ABI of the Mamba-2 chunked SSD forward pass and its one-token decode step
+// (declared in include/mamba2_ssd.h). Host code only: argument validation,
+// workspace layout, and the launches in dependency order on the caller's
+// stream (the kernel order of the CUDA Tile Mamba-2 blog: cumulative sum,
+// state pass, then the outputs, with the state contraction split out of the
+// pass).
 #include "mamba2_ssd.h"
 
 #include <hip/hip_runtime.h>
@@ -219,6 +220,64 @@ int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* d, int io, const void* x, const 
   return MAMBA2_SSD_OK;
 }
 
+int mamba2_ssd_step_supported(int64_t dstate, int io_dtype) {
+  return valid_io(io_dtype) && ssd::step_has(io_dtype, dstate);
+}
+
+int mamba2_ssd_step_check_args(const mamba2_ssd_step_dims* d, int io, const void* x, const float* dt,
+                               const float* A, const void* B, const void* C, const float* D,
+                               const float* state, const void* y) {
+  if (!d) return MAMBA2_SSD_ERR_NULL_POINTER;
+  if (!valid_io(io)) return MAMBA2_SSD_ERR_UNSUPPORTED;
+  if (d->batch < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0)
+    return MAMBA2_SSD_ERR_BAD_DIM;
+  if (d->batch > kMaxDim || d->nheads > kMaxDim || d->headdim > kMaxDim || d->ngroups > kMaxDim)
+    return MAMBA2_SSD_ERR_BAD_DIM;
+  if (d->nheads % d->ngroups) return MAMBA2_SSD_ERR_GROUPS;
+  if (!ssd::step_has(io, d->dstate)) return MAMBA2_SSD_ERR_UNSUPPORTED;
+  int64_t bh, rows, bg, nbc, nstate;
+  if (!mul_ok(d->batch, d->nheads, &bh) || !mul_ok(bh, d->headdim, &rows) ||
+      !mul_ok(d->batch, d->ngroups, &bg) || !mul_ok(bg, d->dstate, &nbc) || !mul_ok(rows, d->dstate, &nstate))
+    return MAMBA2_SSD_ERR_BAD_DIM;
+  // the kernel indexes rows and B/C elements with 32-bit integers
+  if (rows >= INT32_MAX || nbc >= INT32_MAX) return MAMBA2_SSD_ERR_BAD_DIM;
+  if (rows == 0) return MAMBA2_SSD_OK;
+  if (!x || !dt || !A || !B || !C || !D || !state || !y) return MAMBA2_SSD_ERR_NULL_POINTER;
+  const size_t e = io_size(io);
+  const uintptr_t bc_align = io == MAMBA2_SSD_BF16 ? 8 : 16;
+  if (reinterpret_cast<uintptr_t>(state) % 16 || reinterpret_cast<uintptr_t>(B) % bc_align ||
+      reinterpret_cast<uintptr_t>(C) % bc_align || reinterpret_cast<uintptr_t>(x) % e ||
+      reinterpret_cast<uintptr_t>(y) % e || reinterpret_cast<uintptr_t>(dt) % 4 ||
+      reinterpret_cast<uintptr_t>(A) % 4 || reinterpret_cast<uintptr_t>(D) % 4)
+    return MAMBA2_SSD_ERR_ALIGN;
+  const Range rx = range_of(x, (size_t)rows * e), rdt = range_of(dt, (size_t)bh * 4);
+  const Range rA = range_of(A, (size_t)d->nheads * 4), rD = range_of(D, (size_t)d->nheads * 4);
+  const Range rB = range_of(B, (size_t)nbc * e), rC = range_of(C, (size_t)nbc * e);
+  const Range rs = range_of(state, (size_t)nstate * 4), ry = range_of(y, (size_t)rows * e);
+  const Range inputs[] = {rx, rdt, rA, rD, rB, rC};
+  for (const Range& r : inputs)
+    if (overlap(rs, r) || overlap(ry, r)) return MAMBA2_SSD_ERR_ALIAS;
+  if (overlap(rs, ry)) return MAMBA2_SSD_ERR_ALIAS;
+  return MAMBA2_SSD_OK;
+}
+
+int mamba2_ssd_step(const mamba2_ssd_step_dims* d, int io, const void* x, const float* dt, const float* A,
+                    const void* B, const void* C, const float* D, float* state, void* y, void* stream) {
+  g_last_hip_error.clear();
+  const int st = mamba2_ssd_step_check_args(d, io, x, dt, A, B, C, D, state, y);
+  if (st != MAMBA2_SSD_OK) return st;
+  if (d->batch == 0) return MAMBA2_SSD_OK;
+  ssd::StepProblem p;
+  p.bt = d->batch; p.H = d->nheads; p.P = d->headdim; p.N = d->dstate; p.G = d->ngroups; p.io = io;
+  p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.state = state; p.y = y;
+  const hipError_t err = ssd::launch_ssd_step(p, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) {
+    g_last_hip_error = hipGetErrorString(err);
+    return MAMBA2_SSD_ERR_HIP;
+  }
+  return MAMBA2_SSD_OK;
+}
+
 const char* mamba2_ssd_status_string(int status) {
   switch (status) {
     case MAMBA2_SSD_OK: return "ok";
@@ -230,6 +289,7 @@ const char* mamba2_ssd_status_string(int status) {
     case MAMBA2_SSD_ERR_WORKSPACE: return "workspace missing or too small";
     case MAMBA2_SSD_ERR_ALIAS: return "an output overlaps another array";
     case MAMBA2_SSD_ERR_HIP: return "HIP launch failure";
+    case MAMBA2_SSD_ERR_ALIGN: return "a pointer is not aligned as required";
     default: return "unknown status";
   }
 }

@@ -27,15 +27,31 @@ struct Problem {
   void* hprev;                   // workspace: [bt][H][nc][P][N] fp32, or bf16 (hi, lo) pairs
 };
 
+// One decode step (see ssd_step.hip). Device pointers, validated by the ABI.
+struct StepProblem {
+  int64_t bt, H, P, N, G;        // batch, nheads, headdim, dstate, ngroups
+  int io;                        // 0 = fp32, 1 = bf16 (x, B, C, y)
+  const void* x;                 // [bt][H][P]
+  const float* dt;               // [bt][H]
+  const float* A;                // [H]
+  const void* B;                 // [bt][G][N]
+  const void* C;                 // [bt][G][N]
+  const float* D;                // [H]
+  float* state;                  // [bt][H][P][N], read and written
+  void* y;                       // [bt][H][P]
+};
+
 // Each launcher enqueues one kernel on `stream` and returns the launch status.
 hipError_t launch_chunk_cumsum(const Problem& p, hipStream_t stream);
 hipError_t launch_chunk_state(const Problem& p, hipStream_t stream);
 hipError_t launch_state_pass(const Problem& p, hipStream_t stream);
 hipError_t launch_chunk_scan(const Problem& p, hipStream_t stream);
+hipError_t launch_ssd_step(const StepProblem& p, hipStream_t stream);
 
 // Compile-time instantiation tables (host queries, no GPU needed).
 bool chunk_state_has(int io, int64_t P, int64_t N, int64_t Q);
 bool chunk_scan_has(int io, int64_t P, int64_t N, int64_t Q);
+bool step_has(int io, int64_t N);
 
 // Grid-dimension limits the launchers rely on (y and z <= 65535).
 constexpr int64_t kMaxGridYZ = 65535;

@@ -17,6 +17,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mamba2_ssd.h")
 
 OK, NULLP, BAD_DIM, GROUPS, CHUNK, UNSUP, WS, ALIAS = 0, -1, -2, -3, -4, -5, -6, -7
+ALIGN = -9
 
 
 def declared_functions():
@@ -29,7 +30,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted([
         "mamba2_ssd_check_args", "mamba2_ssd_fwd", "mamba2_ssd_fwd_timed", "mamba2_ssd_fwd_workspace_bytes",
         "mamba2_ssd_last_hip_error", "mamba2_ssd_status_string", "mamba2_ssd_supported",
-        "mamba2_ssd_workspace_layout_query"])
+        "mamba2_ssd_workspace_layout_query", "mamba2_ssd_step", "mamba2_ssd_step_check_args",
+        "mamba2_ssd_step_supported"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -189,7 +191,87 @@ def test_fwd_reports_validation_errors_without_launching():
 
 
 def test_status_strings():
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         s = ssd.status_string(code)
         assert s and s != "unknown status"
     assert ssd.status_string(-99) == "unknown status"
+
+
+# ---------------------------------------------------------------- decode step
+STEP = ssd.StepDims(3, 6, 64, 128, 2)
+
+
+def _step_ptrs(d, io):
+    """Disjoint, aligned fake addresses for every step argument."""
+    e = 2 if io == BF16 else 4
+    sizes = {"x": d.batch * d.nheads * d.headdim * e, "dt": d.batch * d.nheads * 4, "A": d.nheads * 4,
+             "D": d.nheads * 4, "B": d.batch * d.ngroups * d.dstate * e, "C": d.batch * d.ngroups * d.dstate * e,
+             "state": d.batch * d.nheads * d.headdim * d.dstate * 4, "y": d.batch * d.nheads * d.headdim * e}
+    p, base = {}, 1 << 20
+    for k, n in sizes.items():
+        p[k] = base
+        base += (n + 4095) // 4096 * 4096 + 4096
+    return p
+
+
+def _step_check(d, io, **over):
+    p = {**_step_ptrs(d, io), **over}
+    return ssd.step_check_args(d, io, p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"], p["state"], p["y"])
+
+
+def test_step_supported_table():
+    for io in (F32, BF16):
+        for n in (64, 128, 256):
+            assert ssd.step_supported(n, io)
+        for n in (32, 96, 512):
+            assert not ssd.step_supported(n, io)
+    assert not ssd.step_supported(128, 7)
+
+
+def test_step_valid_call_passes():
+    assert _step_check(STEP, BF16) == OK
+    assert _step_check(STEP, F32) == OK
+    assert _step_check(ssd.StepDims(5, 3, 3, 64, 3), F32) == OK      # any headdim
+
+
+@pytest.mark.parametrize("field,value,code", [("batch", -1, BAD_DIM), ("nheads", 0, BAD_DIM),
+                                              ("headdim", 0, BAD_DIM), ("dstate", 96, UNSUP),
+                                              ("ngroups", 4, GROUPS), ("ngroups", 0, BAD_DIM),
+                                              ("batch", 1 << 30, BAD_DIM)])
+def test_step_bad_dims(field, value, code):
+    d = ssd.StepDims(STEP.batch, STEP.nheads, STEP.headdim, STEP.dstate, STEP.ngroups)
+    setattr(d, field, value)
+    p = _step_ptrs(STEP, BF16)
+    assert ssd.step_check_args(d, BF16, p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"], p["state"], p["y"]) == code
+
+
+@pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "D", "state", "y"])
+def test_step_null_pointers(name):
+    assert _step_check(STEP, BF16, **{name: 0}) == NULLP
+
+
+def test_step_alignment():
+    p = _step_ptrs(STEP, BF16)
+    assert _step_check(STEP, BF16, state=p["state"] + 8) == ALIGN
+    assert _step_check(STEP, BF16, B=p["B"] + 4) == ALIGN
+    assert _step_check(STEP, BF16, B=p["B"] + 8) == OK                 # bf16 B/C need 8 bytes
+    q = _step_ptrs(STEP, F32)
+    assert _step_check(STEP, F32, C=q["C"] + 8) == ALIGN              # fp32 B/C need 16 bytes
+    assert _step_check(STEP, F32, x=q["x"] + 2) == ALIGN
+
+
+def test_step_alias_rules():
+    p = _step_ptrs(STEP, BF16)
+    assert _step_check(STEP, BF16, y=p["x"]) == ALIAS
+    assert _step_check(STEP, BF16, state=p["B"]) == ALIAS
+    assert _step_check(STEP, BF16, y=p["state"] + 64) == ALIAS
+    assert _step_check(STEP, BF16, state=p["dt"] - 16) == ALIAS
+
+
+def test_step_empty_and_errors_without_launching():
+    assert ssd.step_check_args(ssd.StepDims(0, 4, 64, 128, 1), BF16, 0, 0, 0, 0, 0, 0, 0, 0) == OK
+    ssd.ssd_step_ptr(ssd.StepDims(0, 4, 64, 128, 1), BF16, 0, 0, 0, 0, 0, 0, 0, 0)
+    with pytest.raises(ssd.SsdError) as e:
+        ssd.ssd_step_ptr(ssd.StepDims(1, 3, 64, 128, 2), BF16, 1, 1, 1, 1, 1, 1, 1, 1)
+    assert e.value.status == GROUPS
+    assert ssd._lib.lib.mamba2_ssd_step_check_args(None, BF16, 1, 1, 1, 1, 1, 1, 1, 1) == NULLP

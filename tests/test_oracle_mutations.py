@@ -48,6 +48,18 @@ CHUNK_MUTANTS = {
 }
 
 
+STEP_MUTANTS = {
+    "decay_sign": ("alpha = np.exp(A[h] * dt[b, h])", "alpha = np.exp(-A[h] * dt[b, h])"),
+    "no_dt_on_update": ("upd = np.outer(x[b, h], B[b, g]) * dt[b, h]", "upd = np.outer(x[b, h], B[b, g])"),
+    "update_transposed": ("upd = np.outer(x[b, h], B[b, g]) * dt[b, h]",
+                          "upd = np.outer(x[b, h], B[b, g]).T.reshape(x.shape[2], -1) * dt[b, h]"),
+    "group_modulo": ("g = h // per_group", "g = h % G"),
+    "y_reads_old_state": ("y[b, h] = s @ C[b, g]", "y[b, h] = state[b, h] @ C[b, g]"),
+    "skip_dropped": ("+ D[h] * x[b, h]", "+ 0.0 * x[b, h]"),
+    "y_contracts_B": ("y[b, h] = s @ C[b, g]", "y[b, h] = s @ B[b, g]"),
+}
+
+
 def _load_mutant(fname, modname, old, new, followup=None):
     with open(os.path.join(ORACLE_DIR, fname)) as f:
         src = f.read()
@@ -108,3 +120,27 @@ def test_chunked_mutant_caught(name, q):
 def test_unmutated_oracle_passes_every_pin():
     mod = _load_mutant("ssd_chunked.py", "identity", "Glast = Gk[:, -1]", "Glast = Gk[:, -1]")
     assert not _caught(lambda x, dt, A, B, C, D, h0: mod.ssd_chunked(x, dt, A, B, C, D, 4, h0))
+
+
+@pytest.mark.parametrize("name", sorted(STEP_MUTANTS))
+def test_step_mutant_caught(name):
+    import numpy as np
+    old, new = STEP_MUTANTS[name]
+    with open(os.path.join(ORACLE_DIR, "ssd_step.py")) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutation anchor not unique: {old!r}"
+    mod = types.ModuleType("mutant_step")
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), mod.__dict__)
+
+    def stepped(x, dt, A, B, C, D, h0):
+        x = np.asarray(x)
+        bt, T, H, P = x.shape
+        N = np.asarray(B).shape[-1]
+        st = np.zeros((bt, H, P, N)) if h0 is None else np.asarray(h0, dtype=np.float64)
+        y = np.empty((bt, T, H, P))
+        for t in range(T):
+            y[:, t], st = mod.ssd_step(x[:, t], np.asarray(dt)[:, t], A, np.asarray(B)[:, t],
+                                       np.asarray(C)[:, t], D, st)
+        return y, st
+
+    assert _caught(stepped), f"no pin rejects the step mutant {name}"

@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from oracle import ssd_chunked, ssd_sequential
+from oracle import ssd_chunked, ssd_sequential, ssd_step
 from tests.oracle_pins import ALL_PINS, assert_close, rand_layer
 
 
@@ -16,8 +16,21 @@ def chunked_fwd(q):
     return f
 
 
+def stepped_fwd(x, dt, A, B, C, D, h0):
+    """A whole sequence as repeated decode steps: every forward pin then pins
+    the step oracle too."""
+    x = np.asarray(x)
+    bt, T, H, P = x.shape
+    N = np.asarray(B).shape[-1]
+    s = np.zeros((bt, H, P, N)) if h0 is None else np.asarray(h0, dtype=np.float64)
+    y = np.empty((bt, T, H, P))
+    for t in range(T):
+        y[:, t], s = ssd_step(x[:, t], np.asarray(dt)[:, t], A, np.asarray(B)[:, t], np.asarray(C)[:, t], D, s)
+    return y, s
+
+
 FWDS = {"sequential": seq_fwd, "chunked_q1": chunked_fwd(1), "chunked_q4": chunked_fwd(4),
-        "chunked_q5": chunked_fwd(5), "chunked_q64": chunked_fwd(64)}
+        "chunked_q5": chunked_fwd(5), "chunked_q64": chunked_fwd(64), "stepped": stepped_fwd}
 
 
 @pytest.mark.parametrize("pin", sorted(ALL_PINS))
@@ -92,3 +105,35 @@ def test_empty_sequence():
         y, fin = f(e(x), e(dt), A, e(B), e(C), D, h0)
         assert y.shape == (2, 0, 4, 3)
         assert np.array_equal(fin, h0)
+
+
+# ---------------------------------------------------------------- decode step
+def test_steps_equal_both_forward_oracles():
+    """Chaining the step oracle over a sequence reproduces the sequential and
+    the chunked oracles (an independent route for each)."""
+    x, dt, A, B, C, D, h0 = rand_layer(70, T=11, H=6, G=3, dt_zero_frac=0.1)
+    ys, fs = stepped_fwd(x, dt, A, B, C, D, h0)
+    yq, fq = ssd_sequential(x, dt, A, B, C, D, h0)
+    yc, fc = ssd_chunked(x, dt, A, B, C, D, 4, h0)
+    assert_close(ys, yq, 1e-13, "y vs sequential")
+    assert_close(fs, fq, 1e-13, "state vs sequential")
+    assert_close(ys, yc, 1e-12, "y vs chunked")
+    assert_close(fs, fc, 1e-12, "state vs chunked")
+
+
+def test_step_continues_a_prefill():
+    """A step from a forward call's final state gives the next token's output
+    and state of a forward call one token longer."""
+    x, dt, A, B, C, D, h0 = rand_layer(71, T=9)
+    yp, fp = ssd_chunked(x[:, :8], dt[:, :8], A, B[:, :8], C[:, :8], D, 4, h0)
+    y1, f1 = ssd_step(x[:, 8], dt[:, 8], A, B[:, 8], C[:, 8], D, fp)
+    yf, ff = ssd_sequential(x, dt, A, B, C, D, h0)
+    assert_close(y1, yf[:, 8], 1e-12, "next y")
+    assert_close(f1, ff, 1e-12, "next state")
+
+
+def test_step_leaves_its_input_state_alone():
+    x, dt, A, B, C, D, h0 = rand_layer(72, T=1)
+    keep = h0.copy()
+    ssd_step(x[:, 0], dt[:, 0], A, B[:, 0], C[:, 0], D, h0)
+    assert np.array_equal(h0, keep)

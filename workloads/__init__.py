@@ -26,7 +26,7 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["LayerConfig", "CONFIGS", "HELD_OUT", "config_by_name", "generate",
+__all__ = ["LayerConfig", "CONFIGS", "HELD_OUT", "DECODE_CONFIGS", "config_by_name", "generate",
            "round_to_bf16", "bf16_bits_to_f32"]
 
 
@@ -93,8 +93,22 @@ HELD_OUT = LayerConfig("tilegym-example", batch=4, seqlen=16384, nheads=8,
                        seed=5, description="held-out shape")
 
 
+# Decode-step workloads: seqlen 1, a nonzero state standing in for the final
+# state of an earlier prefill. The serving shape advances 256 sequences of the
+# 2.7B-like layer by one token each; its state (671 MB fp32) dwarfs every
+# other operand, which is the regime a batched decode step runs in.
+DECODE_CONFIGS = [
+    LayerConfig("mamba2-2.7b-decode", batch=256, seqlen=1, nheads=80, headdim=64,
+                dstate=128, ngroups=1, chunk=256, io="bf16", seed=6, init_sigma=0.5,
+                description="one decode step of 256 sequences, 2.7B-like layer"),
+    LayerConfig("decode-small", batch=3, seqlen=1, nheads=6, headdim=64, dstate=64,
+                ngroups=2, chunk=64, io="f32", seed=7, init_sigma=0.5,
+                description="small decode step, fp32, 2 groups"),
+]
+
+
 def config_by_name(name: str) -> LayerConfig:
-    for c in CONFIGS + [HELD_OUT]:
+    for c in CONFIGS + [HELD_OUT] + DECODE_CONFIGS:
         if c.name == name:
             return c
     raise KeyError(name)
