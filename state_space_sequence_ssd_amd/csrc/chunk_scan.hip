@@ -931,6 +931,7 @@ bool chunk_scan_has(int io, int64_t P, int64_t N, int64_t Q) {
 }
 
 hipError_t launch_chunk_scan(const Problem& p, hipStream_t stream) {
+  if (chunk_scan_resident_fits(p)) return launch_chunk_scan_resident(p, stream);
   return p.io == 1 ? dispatch<bf16>(p, stream) : dispatch<float>(p, stream);
 }
 

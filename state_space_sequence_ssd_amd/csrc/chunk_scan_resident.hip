@@ -1,0 +1,549 @@
+// ssd_chunk_scan, C.B^T-resident form (bf16 io, headdim 64, chunk 256,
+// dstate 64 or 128): the same outputs as chunk_scan.hip,
+//
+//   y[t, p] = 2^(G'_t) sum_n C[t, n] Hprev[p, n]
+//           + sum_{j <= t} (C_t . B_j) 2^(G'_t - G'_j) dt_j x[j, p] + D x[t, p]
+//
+// (CUDA Tile Mamba-2 blog, section "Mamba-2 architecture", the decayed block
+// output; section "Kernel 3: compute_out").
+//
+// What changes. C_t . B_j depends on (batch, chunk, group) only, not on the
+// head; every head of a group reuses the same causal Q x Q block. A
+// persistent workgroup walks consecutive heads of one chunk, so it computes
+// the chunk's C.B^T once, keeps it in registers (each wave holds its 9
+// causal 32x32 blocks, 144 fp32 per lane), and per head only applies the
+// head's decay and dt, splits, and multiplies with x. That removes the per
+// head C.B^T products (a third of the MFMAs of the per-head form).
+//
+// Per head ("tile"), the operands that change are x (32 KB), the carried
+// state Hprev (32 KB of bf16 hi/lo pairs) and the head's G', dt rows (2 KB).
+// They are brought into one of two LDS buffers by direct global->LDS loads
+// while the previous tile computes; a tile needs two workgroup barriers, not
+// one per 32-token block.
+//
+// Waves. 4 waves; wave w owns the 32-row t-blocks w and 7 - w, i.e. the
+// causal (t-block, j-block) pairs k = 0..8: (w, k) for k <= w, then
+// (7 - w, k - w - 1); pair w and pair 8 are diagonal blocks. Every wave has
+// 9 pairs.
+//
+// LDS layouts (all reads conflict-free):
+//  - x tile: 256 rows of 128 bytes, unpadded; global row j sits at row slot
+//    j ^ ((j >> 2) & 1), so the two half-waves of a dword read (rows j and
+//    j + 4) land on opposite 128-byte halves of the 256-byte bank space. A
+//    wave-instruction of the direct load fills 8 whole slots, so its
+//    per-lane source offset is one constant and the row block is a scalar.
+//  - Hprev: slot rows of N*4 bytes plus one 16-byte pad piece, slot
+//    q*64 + pe*32 + m holding headdim row 2m + pe (fragment reads of 16
+//    consecutive lanes hit 16 distinct bank groups).
+//  - B tile (C.B^T phase only, in the other buffer): rows padded by one
+//    16-byte piece.
+#include "ssd_device.h"
+#include "ssd_launch.h"
+
+namespace ssd {
+
+namespace {
+
+template <int N>
+struct RCfg {
+  static constexpr int P = 64, Q = 256, NTB = 8, WAVES = 4, THREADS = 256;
+  static constexpr int KS = N / 16;            // bf16 MFMA k-steps over dstate
+  static constexpr int NPAIR = NTB + 1;        // causal block pairs per wave
+  static constexpr int XRB = P * 2;            // x row bytes in LDS (unpadded)
+  static constexpr int XBYTES = Q * XRB;       // 32 KB
+  static constexpr int HROWP = N / 4 + 1;      // Hprev pieces per padded slot row
+  static constexpr int HRB = HROWP * 16;
+  static constexpr int HBYTES = (P * HROWP * 16 + 1023) / 1024 * 1024;
+  static constexpr int GBYTES = 2 * Q * 4;     // G' row, then dt row
+  static constexpr int HOFF = XBYTES, GOFF = XBYTES + HBYTES;
+  static constexpr int IX = XBYTES / 1024;     // wave-instructions of one tile's loads
+  static constexpr int IH = HBYTES / 1024;
+  static constexpr int IG = GBYTES / 1024;
+  static constexpr int LX = IX / WAVES;        // per wave
+  static constexpr int LR = (IH + IG + WAVES - 1) / WAVES;
+  static constexpr int LT = LX + LR;           // tile loads per wave
+  static constexpr int RB = N * 2 / 16;        // pieces per B row
+  static constexpr int BROWP = RB + 1;
+  static constexpr int BRB = BROWP * 16;
+  static constexpr int BBYTES = (Q * BRB + 1023) / 1024 * 1024;
+  static constexpr int IB = BBYTES / 1024;
+  static constexpr int LB = (IB + WAVES - 1) / WAVES;
+  // one tile buffer; the C.B^T phase puts the B tile in one as well
+  static constexpr int BUF = GOFF + GBYTES > BBYTES ? GOFF + GBYTES : BBYTES;
+  static_assert(IX % WAVES == 0, "x loads split evenly");
+  static_assert(2 * BUF + Q * 4 <= 160 * 1024, "LDS");
+  static_assert(LT <= 40 && LB + LT + 2 * KS <= 63, "vmcnt accounting");
+};
+
+// Direct global->LDS load, 16 bytes per lane, from a wave-uniform base plus a
+// per-lane 32-bit offset (the scalar-base form of the instruction). Lane i's
+// bytes land at lds + 16 i; lds must be wave-uniform (it goes in M0).
+__device__ __forceinline__ void lds_dma16_s(const void* sbase, uint32_t voff, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+// Values pinned in the accumulation registers (AGPRs): the resident C.B^T
+// blocks live there between tiles, leaving the VGPRs to the per-pair
+// working set; they are read back one 32x32 block at a time.
+__device__ __forceinline__ float to_agpr(float v) {
+  float a;
+  asm("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
+  return a;
+}
+__device__ __forceinline__ float from_agpr(float a) {
+  float v;
+  asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+template <int VM>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
+}
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One (batch, chunk, head) tile's addresses; all wave-uniform.
+struct RTile {
+  int64_t b, k, bk;
+  int h, nvalid;
+  int64_t ckey;
+  const unsigned char* x;      // first x row of the tile
+  unsigned char* y;
+  const bf16* bt;              // first B row
+  const bf16* ct;              // first C row
+  const unsigned char* gc;     // G' row (Q floats)
+  const unsigned char* dtc;    // dt row
+  const unsigned char* hs;     // Hprev block (P rows of 4N bytes)
+  float Dh;
+};
+
+template <int N>
+__device__ __forceinline__ RTile make_rtile(int64_t b, int64_t k, int64_t bk, int h, const bf16* x, const bf16* Bm,
+                                            const bf16* Cm, const float* gcum, const float* dtt, const float* Dp,
+                                            const void* hprev, bf16* y, int64_t Tlen, int H, int G, int64_t nc,
+                                            int64_t Tp) {
+  constexpr int P = 64, Q = 256;
+  RTile t;
+  const int grp = h / (H / G);
+  const int64_t t0 = k * Q;
+  t.b = b;
+  t.k = k;
+  t.bk = bk;
+  t.h = h;
+  t.nvalid = (int)(Tlen - t0 < Q ? Tlen - t0 : Q);
+  t.ckey = bk * G + grp;
+  t.x = reinterpret_cast<const unsigned char*>(x + ((b * Tlen + t0) * H + h) * P);
+  t.y = reinterpret_cast<unsigned char*>(y + ((b * Tlen + t0) * H + h) * P);
+  t.bt = Bm + ((b * Tlen + t0) * G + grp) * N;
+  t.ct = Cm + ((b * Tlen + t0) * G + grp) * N;
+  t.gc = reinterpret_cast<const unsigned char*>(gcum + (b * H + h) * Tp + t0);
+  t.dtc = reinterpret_cast<const unsigned char*>(dtt + (b * H + h) * Tp + t0);
+  t.hs = static_cast<const unsigned char*>(hprev) + ((b * H + h) * nc + k) * (int64_t)(P * N) * 4;
+  t.Dh = Dp[h];
+  return t;
+}
+
+template <int N>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict__ Bm, const bf16* __restrict__ Cm,
+                             const float* __restrict__ gcum, const float* __restrict__ dtt,
+                             const float* __restrict__ Dp, const void* __restrict__ hprev, bf16* __restrict__ y,
+                             int64_t Tlen, int H, int G, int64_t nc, int64_t Tp, int64_t ntiles, int xcd) {
+  using Cf = RCfg<N>;
+  using I = Io<bf16>;
+  using Frag = bf16x8;
+  constexpr int P = 64, Q = 256, KS = Cf::KS, LX = Cf::LX, LR = Cf::LR, LB = Cf::LB;
+  constexpr int IH = Cf::IH, IG = Cf::IG;
+
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2][Cf::BUF];
+  __shared__ __attribute__((aligned(16))) float sW[Q];   // dt_j * 2^(G'_end(block of j) - G'_j) <= dt_j
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  __builtin_assume(wave >= 0 && wave < 4);
+  const int lane = tid % 64, m = lane % 32, g = lane / 32;
+  const int tb0 = wave, tb1 = 7 - wave;
+
+  // this workgroup's contiguous range of tiles, heads fastest; with xcd set,
+  // the tiles of XCD group x are the chunks (batch*nchunks index) = x mod 8,
+  // walked by the workgroups that the dispatcher deals to XCD x
+  int64_t lo, hi;
+  {
+    const int64_t grid = gridDim.x, w = blockIdx.x;
+    if (xcd) {
+      const int64_t n8 = ntiles / 8, xg = w % 8, lw = w / 8, per = grid / 8;
+      lo = xg * n8 + lw * n8 / per;
+      hi = xg * n8 + (lw + 1) * n8 / per;
+    } else {
+      lo = w * ntiles / grid;
+      hi = (w + 1) * ntiles / grid;
+    }
+  }
+  if (lo >= hi) return;   // whole workgroup
+
+  // first tile: walk position lo -> (bk, h) -> (b, k)
+  int64_t bk;
+  int h;
+  if (xcd) {
+    const int64_t n8 = ntiles / 8, xg = lo / n8, i = lo % n8;
+    bk = xg + 8 * (i / H);
+    h = (int)(i % H);
+  } else {
+    bk = lo / H;
+    h = (int)(lo % H);
+  }
+  const int64_t bkstep = xcd ? 8 : 1;
+  int64_t b = bk / nc, k = bk % nc;
+
+  // per-lane load offsets, fixed for the whole walk
+  const uint32_t xrb = (uint32_t)H * P * 2;                  // x / y row stride in bytes
+  const int jl = (lane >> 3) ^ ((lane >> 5) & 1);            // x row (within 8) this lane loads
+  const uint32_t xlane = (uint32_t)jl * xrb + (lane & 7) * 16;
+  uint32_t roff[LR];    // Hprev (or G', dt) load offsets of the rest list
+#pragma unroll
+  for (int i = 0; i < LR; ++i) {
+    int rho = wave + i * 4;
+    if (rho >= IH + IG) rho %= IH + IG;     // spare: repeats a load
+    if (rho < IH) {
+      const int s = rho * 64 + lane;
+      int r = s / Cf::HROWP, c = s % Cf::HROWP;
+      if (r >= P) r = P - 1;                // tail of the last instruction
+      if (c >= Cf::HROWP - 1) c = 0;        // pad piece
+      const int p = 2 * (r % 32) + (r / 32) % 2 + (r / 64) * 64;
+      roff[i] = (uint32_t)(p * N * 4 + c * 16);
+    } else {
+      roff[i] = (uint32_t)(lane * 16);
+    }
+  }
+  // LDS read bases of the x tile (see the row swizzle above): even and odd
+  // fragment rows differ by +-1 slot in the upper half-wave
+  const int xbe = 512 * g + 4 * m + 128 * g, xbo = 512 * g + 4 * m - 128 * g;
+
+  float cbc[9][16];   // resident C.B^T blocks, in AGPRs
+  Frag cf[2][KS];
+  int64_t ckey_cached = -1;
+  int ys = 0;     // y stores issued after the current tile's loads (0 or 32)
+  int buf = 0;
+
+  // Issue the loads of one tile into LDS buffer `dst`.
+  // (The per-lane and per-instruction offsets below are derived from values
+  // laundered per call, so they are not hoisted out of the walk and kept
+  // alive in registers across it.)
+  auto issue_tile = [&](const RTile& t, unsigned char* dst) {
+    const bool full = t.nvalid == Q;
+    uint32_t xl = xlane, xr = xrb;
+    int jll = jl;
+    asm volatile("" : "+v"(xl), "+v"(jll), "+s"(xr));
+#pragma unroll
+    for (int i = 0; i < LX; ++i) {
+      const int kk = wave + 4 * i;           // 8 x rows per instruction
+      if (full) {
+        lds_dma16_s(t.x + (uint32_t)(kk * 8) * xr, xl, dst + kk * 1024);
+      } else {
+        const int row = min(kk * 8 + jll, t.nvalid - 1);
+        lds_dma16_s(t.x, (uint32_t)row * xr + (lane & 7) * 16, dst + kk * 1024);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LR; ++i) {
+      int rho = wave + i * 4;
+      if (rho >= IH + IG) rho %= IH + IG;
+      if (rho < IH)
+        lds_dma16_s(t.hs, roff[i], dst + Cf::HOFF + rho * 1024);
+      else
+        lds_dma16_s(rho == IH ? t.gc : t.dtc, roff[i], dst + Cf::GOFF + (rho - IH) * 1024);
+    }
+  };
+
+  for (int64_t pos = lo; pos < hi; ++pos) {
+    const RTile t = make_rtile<N>(b, k, bk, h, x, Bm, Cm, gcum, dtt, Dp, hprev, y, Tlen, H, G, nc, Tp);
+    unsigned char* cur = lds[buf];
+    unsigned char* oth = lds[buf ^ 1];
+
+    if (t.ckey != ckey_cached) {
+      // C.B^T phase: every earlier load and store of this wave is done and
+      // every wave has left the previous tile
+      wait_vm_barrier<0>();
+      // C rows of the wave's t-blocks as MFMA fragments
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int tr = (u ? tb1 : tb0) * 32 + m;
+        const bool valid = tr < t.nvalid;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) cf[u][s] = I::load_row(t.ct + (int64_t)tr * G * N + s * 16 + 8 * g, valid);
+      }
+      // the chunk's B rows into the other buffer (padded rows), rows past
+      // the sequence clamped to its last row
+#pragma unroll
+      for (int i = 0; i < LB; ++i) {
+        int kk = wave + 4 * i;
+        if (kk >= Cf::IB) kk %= Cf::IB;
+        const int s = kk * 64 + lane;
+        int r = s / Cf::BROWP, c = s % Cf::BROWP;
+        if (r >= Q) r = Q - 1;
+        if (c >= Cf::RB) c = 0;
+        const int row = min(r, t.nvalid - 1);
+        lds_dma16_s(t.bt, (uint32_t)((int64_t)row * G * N * 2 + c * 16), oth + kk * 1024);
+      }
+      issue_tile(t, cur);
+      // B and C landed once only this tile's LT loads remain
+      wait_vm_barrier<Cf::LT>();
+      const unsigned char* bb = oth + m * Cf::BRB + g * 16;
+#pragma unroll
+      for (int kp = 0; kp < 9; ++kp) {
+        const bool first = kp <= wave;
+        const int jb = first ? kp : kp - wave - 1;
+        const unsigned char* bj = bb + jb * 32 * Cf::BRB;
+        f32x16 acc = f32x16{};
+        if (first) {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) I::mma(acc, *reinterpret_cast<const Frag*>(bj + s * 32), cf[0][s]);
+        } else {
+#pragma unroll
+          for (int s = 0; s < KS; ++s) I::mma(acc, *reinterpret_cast<const Frag*>(bj + s * 32), cf[1][s]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cbc[kp][r] = to_agpr(acc[r]);
+      }
+      lds_barrier();      // the B tile is read; its buffer may be refilled
+      ckey_cached = t.ckey;
+      ys = 0;
+    }
+
+    // this tile's loads have landed once only the previous tile's y stores remain
+    if (ys) wait_vm_barrier<32>();
+    else wait_vm_barrier<0>();
+    const float* sG = reinterpret_cast<const float*>(cur + Cf::GOFF);
+    const float* sDt = sG + Q;
+    {
+      const float gi = sG[tid];
+      sW[tid] = sDt[tid] * exp2_hw(sG[tid | 31] - gi);   // exponent <= 0
+    }
+    const float gt0 = sG[tb0 * 32 + m], gt1 = sG[tb1 * 32 + m];
+    lds_barrier();
+
+    // next tile: advance the walk; prefetch it when it shares this chunk's C.B^T
+    const bool has_next = pos + 1 < hi;
+    if (has_next) {
+      if (++h == H) {
+        h = 0;
+        bk += bkstep;
+        k += bkstep;
+        while (k >= nc) {
+          k -= nc;
+          ++b;
+        }
+      }
+    }
+    bool prefetch = false;
+    if (has_next) {
+      const RTile nt = make_rtile<N>(b, k, bk, h, x, Bm, Cm, gcum, dtt, Dp, hprev, y, Tlen, H, G, nc, Tp);
+      prefetch = nt.ckey == ckey_cached;
+      if (prefetch) issue_tile(nt, oth);
+    }
+
+    // carried state: acc[u][pe] = C . Hprev^T, column p = 2m + pe, then rows
+    // scaled by 2^(G'_t)
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int pe = 0; pe < 2; ++pe) acc[u][pe] = f32x16{};
+#pragma unroll
+    for (int pe = 0; pe < 2; ++pe) {
+      const unsigned char* hp = cur + Cf::HOFF + (pe * 32 + m) * Cf::HRB;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        const Frag hhi = *reinterpret_cast<const Frag*>(hp + (2 * s + g) * 32);
+        const Frag hlo = *reinterpret_cast<const Frag*>(hp + (2 * s + g) * 32 + 16);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          I::mma(acc[u][pe], cf[u][s], hhi);
+          I::mma(acc[u][pe], cf[u][s], hlo);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float sc = exp2_hw(sG[(u ? tb1 : tb0) * 32 + drow(r, g)]);
+        acc[u][0][r] *= sc;
+        acc[u][1][r] *= sc;
+      }
+
+    // intra-chunk pairs
+    const unsigned char* xt = cur;
+#pragma unroll
+    for (int kp = 0; kp < 9; ++kp) {
+      __builtin_amdgcn_sched_barrier(0);   // one pair at a time: bounds the live registers
+      const bool first = kp <= wave;
+      const int jb = first ? kp : kp - wave - 1;
+      const bool diag = first ? (kp == wave) : (kp == 8);
+      const float gtu = first ? gt0 : gt1;
+      const int j0 = jb * 32;
+      // x dwords of rows drow(q, g) of the block (columns 2m, 2m+1)
+      uint32_t d[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int off = j0 * 128 + 128 * (8 * (q / 4) + q % 4);
+        d[q] = *reinterpret_cast<const uint32_t*>(xt + off + ((q & 1) ? xbo : xbe));
+      }
+      Frag xf[2][2];   // [pe][js]
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        u32x4 e0, e1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t a = d[js * 8 + 2 * i], c = d[js * 8 + 2 * i + 1];
+          e0[i] = __builtin_amdgcn_perm(c, a, 0x05040100u);   // low halves: column 2m
+          e1[i] = __builtin_amdgcn_perm(c, a, 0x07060302u);   // high halves: column 2m + 1
+        }
+        xf[0][js] = __builtin_bit_cast(Frag, e0);
+        xf[1][js] = __builtin_bit_cast(Frag, e1);
+      }
+      float v[16], cb[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cb[r] = from_agpr(cbc[kp][r]);
+      if (!diag) {
+        // every t is past the whole j-block: 2^(G'_t - G'_j) = 2^(G'_t - G'_end) 2^(G'_end - G'_j)
+        const float a = exp2_hw(gtu - sG[j0 + 31]);
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) {
+          const float4 wv = *reinterpret_cast<const float4*>(&sW[j0 + 8 * c4 + 4 * g]);
+          v[4 * c4 + 0] = cb[4 * c4 + 0] * (wv.x * a);
+          v[4 * c4 + 1] = cb[4 * c4 + 1] * (wv.y * a);
+          v[4 * c4 + 2] = cb[4 * c4 + 2] * (wv.z * a);
+          v[4 * c4 + 3] = cb[4 * c4 + 3] * (wv.w * a);
+        }
+      } else {
+        // diagonal block: direct decay; the causal mask is a select
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int jr = drow(q, g);
+          const float val = cb[q] * exp2_hw(gtu - sG[j0 + jr]) * sDt[j0 + jr];
+          v[q] = (m >= jr) ? val : 0.f;
+        }
+      }
+      // (hi, lo) bf16 split of the decayed block, two MFMAs per x fragment
+      Frag ahi[2], alo[2];
+#pragma unroll
+      for (int js = 0; js < 2; ++js) {
+        u32x4 uh, ul;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t hh = pack_bf16x2(v[js * 8 + 2 * i], v[js * 8 + 2 * i + 1]);
+          asm volatile("" : "+v"(hh));    // keep the pair packed: the hi parts below are bit slices of it
+          uh[i] = hh;
+          ul[i] = pack_bf16x2(v[js * 8 + 2 * i] - __uint_as_float(hh << 16),
+                              v[js * 8 + 2 * i + 1] - __uint_as_float(hh & 0xffff0000u));
+        }
+        ahi[js] = __builtin_bit_cast(Frag, uh);
+        alo[js] = __builtin_bit_cast(Frag, ul);
+      }
+      if (first) {
+#pragma unroll
+        for (int js = 0; js < 2; ++js)
+#pragma unroll
+          for (int pe = 0; pe < 2; ++pe) {
+            I::mma(acc[0][pe], ahi[js], xf[pe][js]);
+            I::mma(acc[0][pe], alo[js], xf[pe][js]);
+          }
+      } else {
+#pragma unroll
+        for (int js = 0; js < 2; ++js)
+#pragma unroll
+          for (int pe = 0; pe < 2; ++pe) {
+            I::mma(acc[1][pe], ahi[js], xf[pe][js]);
+            I::mma(acc[1][pe], alo[js], xf[pe][js]);
+          }
+      }
+      if (diag) {
+        // D x for the block's own rows: the same x dwords
+        if (first) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            acc[0][0][r] += t.Dh * bf16lo(d[r]);
+            acc[0][1][r] += t.Dh * bf16hi(d[r]);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            acc[1][0][r] += t.Dh * bf16lo(d[r]);
+            acc[1][1][r] += t.Dh * bf16hi(d[r]);
+          }
+        }
+      }
+    }
+
+    // y: one dword (columns 2m, 2m+1) per lane per row. The row offset is
+    // wave-uniform; the lane offset is re-derived per tile (laundered), so
+    // the compiler does not keep 32 loop-invariant row addresses alive
+    // across the whole walk.
+    const bool full = t.nvalid == Q;
+    uint32_t ylane = (uint32_t)(4 * g) * xrb + 4 * m;
+    uint32_t xrbs = xrb;
+    asm volatile("" : "+v"(ylane), "+s"(xrbs));
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int trow = (u ? tb1 : tb0) * 32 + 8 * (r / 4) + r % 4;   // + 4g in ylane
+        if (full || trow + 4 * g < t.nvalid)
+          *reinterpret_cast<uint32_t*>(t.y + (uint32_t)trow * xrbs + ylane) =
+              pack_bf16x2(acc[u][0][r], acc[u][1][r]);
+      }
+    ys = (prefetch && full) ? 1 : 0;
+    buf ^= 1;
+  }
+}
+
+template <int N>
+int64_t resident_grid(int64_t ntiles) {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    dev = 0;
+  }
+  if (!cached[dev]) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ssd_chunk_scan_resident<N>, 256, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0) {
+      (void)hipGetLastError();
+      cus = 256;
+      per_cu = 1;
+    }
+    cached[dev] = cus * per_cu;
+  }
+  int64_t grid = cached[dev] < ntiles ? cached[dev] : ntiles;
+  if (grid >= 8) grid -= grid % 8;
+  return grid;
+}
+
+template <int N>
+hipError_t launch_resident(const Problem& p, hipStream_t stream) {
+  const int64_t ntiles = p.bt * p.nc * p.H;
+  if (ntiles == 0) return hipSuccess;
+  const int64_t grid = resident_grid<N>(ntiles);
+  const int xcd = (grid % 8 == 0 && (p.bt * p.nc) % 8 == 0) ? 1 : 0;
+  hipLaunchKernelGGL((ssd_chunk_scan_resident<N>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const bf16*)p.x, (const bf16*)p.B, (const bf16*)p.C, p.gcum, p.dtt, p.D,
+                     (const void*)p.hprev, (bf16*)p.y, p.T, (int)p.H, (int)p.G, p.nc, p.Tp, ntiles, xcd);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool chunk_scan_resident_fits(const Problem& p) {
+  return p.io == 1 && p.P == 64 && p.Q == 256 && (p.N == 64 || p.N == 128);
+}
+
+hipError_t launch_chunk_scan_resident(const Problem& p, hipStream_t stream) {
+  return p.N == 64 ? launch_resident<64>(p, stream) : launch_resident<128>(p, stream);
+}
+
+}  // namespace ssd

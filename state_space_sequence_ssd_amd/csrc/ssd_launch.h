@@ -47,6 +47,9 @@ hipError_t launch_chunk_state(const Problem& p, hipStream_t stream);
 hipError_t launch_state_pass(const Problem& p, hipStream_t stream);
 hipError_t launch_chunk_scan(const Problem& p, hipStream_t stream);
 hipError_t launch_ssd_step(const StepProblem& p, hipStream_t stream);
+// The C.B^T-resident scan (chunk_scan_resident.hip) and the shapes it takes.
+bool chunk_scan_resident_fits(const Problem& p);
+hipError_t launch_chunk_scan_resident(const Problem& p, hipStream_t stream);
 
 // Compile-time instantiation tables (host queries, no GPU needed).
 bool chunk_state_has(int io, int64_t P, int64_t N, int64_t Q);

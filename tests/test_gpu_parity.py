@@ -233,3 +233,35 @@ def test_outputs_follow_the_stream():
         z = y.float() * 1.0
     s.synchronize()
     assert torch.equal(z, ref_y.float())
+
+
+# ---------------------------------------------- C.B^T-resident scan (bf16, P=64, Q=256, N in {64, 128})
+# That kernel walks consecutive heads of a chunk per workgroup and keeps the
+# chunk's C.B^T in registers; these cases drive its walk (ragged last
+# chunks, chunk and group changes inside a workgroup's range, grids with and
+# without the XCD grouping, fewer tiles than workgroups).
+RESIDENT = {
+    "T1": dict(batch=2, seqlen=1, nheads=3),
+    "T200": dict(batch=2, seqlen=200, nheads=3),
+    "T256": dict(batch=1, seqlen=256, nheads=5),
+    "T257": dict(batch=2, seqlen=257, nheads=3),
+    "T1000-N64": dict(batch=1, seqlen=1000, nheads=4, dstate=64),
+    "groups-xcd": dict(batch=4, seqlen=2048, nheads=8, ngroups=2),
+    "walk-crosses-chunks": dict(batch=1, seqlen=4096, nheads=24),
+    "walk-ragged-xcd": dict(batch=8, seqlen=700, nheads=6, ngroups=3),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RESIDENT))
+def test_resident_scan_walks(name):
+    cfg = LayerConfig(f"resident-{name}", **{**dict(headdim=64, dstate=128, ngroups=1, chunk=256, io="bf16",
+                                                  seed=500 + len(name), init_sigma=0.2), **RESIDENT[name]})
+    log(f"[resident] {name}: {cfg}")
+    inp = generate(cfg)
+    yr, fr = oracle_all(inp, cfg)
+    dev = to_device(inp, cfg.io)
+    y, fin = run(dev, cfg.chunk)
+    log("  " + check_close(host(y), yr, cfg.io, "y"))
+    log("  " + check_close(host(fin), fr, cfg.io, "final_state"))
+    y2, _ = run(dev, cfg.chunk)
+    assert torch.equal(y, y2), "two identical calls must give identical y"
