@@ -22,9 +22,12 @@
 // one per 32-token block.
 //
 // Waves. 4 waves; wave w owns the 32-row t-blocks w and 7 - w, i.e. the
-// causal (t-block, j-block) pairs k = 0..8: (w, k) for k <= w, then
-// (7 - w, k - w - 1); pair w and pair 8 are diagonal blocks. Every wave has
-// 9 pairs.
+// causal (t-block, j-block) pairs (w, 0..w) and (7 - w, 0..7 - w): 9 pairs
+// for every wave. Pair blocks sit in 9 register slots: slot k holds (w, k)
+// for k <= w and (7 - w, 8 - k) for k > w. Slots 0 and 4..8 therefore
+// belong to one t-block whatever the wave; slots 1..3 are emitted once per
+// t-block behind a wave-uniform branch, so the accumulator each product
+// feeds is always known at compile time.
 //
 // LDS layouts (all reads conflict-free):
 //  - x tile: 256 rows of 128 bytes, unpadded; global row j sits at row slot
@@ -39,6 +42,8 @@
 //    16-byte piece.
 #include "ssd_device.h"
 #include "ssd_launch.h"
+
+#include <type_traits>
 
 namespace ssd {
 
@@ -163,7 +168,7 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
   __builtin_assume(wave >= 0 && wave < 4);
-  const int lane = tid % 64, m = lane % 32, g = lane / 32;
+  const int lane = tid % 64;
   const int tb0 = wave, tb1 = 7 - wave;
 
   // this workgroup's contiguous range of tiles, heads fastest; with xcd set,
@@ -217,12 +222,12 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
       roff[i] = (uint32_t)(lane * 16);
     }
   }
-  // LDS read bases of the x tile (see the row swizzle above): even and odd
-  // fragment rows differ by +-1 slot in the upper half-wave
-  const int xbe = 512 * g + 4 * m + 128 * g, xbo = 512 * g + 4 * m - 128 * g;
+  // (LDS read bases of the x tile, per tile below: with the row swizzle
+  // above, even and odd fragment rows differ by +-1 slot in the upper
+  // half-wave.)
 
-  float cbc[9][16];   // resident C.B^T blocks, in AGPRs
-  Frag cf[2][KS];
+  float cbc[9][16];   // resident C.B^T blocks (slots, see above), in AGPRs
+  Frag cf[2][KS];     // C fragments of the wave's t-blocks, in AGPRs
   int64_t ckey_cached = -1;
   int ys = 0;     // y stores issued after the current tile's loads (0 or 32)
   int buf = 0;
@@ -258,6 +263,12 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
   };
 
   for (int64_t pos = lo; pos < hi; ++pos) {
+    // lane-derived values are re-derived per tile from a laundered lane id:
+    // hoisted out of the walk, they would outgrow the register file
+    int lt = lane;
+    asm volatile("" : "+v"(lt));
+    const int m = lt & 31, g = lt >> 5;
+    const int xbe = 512 * g + 4 * m + 128 * g, xbo = 512 * g + 4 * m - 128 * g;
     const RTile t = make_rtile<N>(b, k, bk, h, x, Bm, Cm, gcum, dtt, Dp, hprev, y, Tlen, H, G, nc, Tp);
     unsigned char* cur = lds[buf];
     unsigned char* oth = lds[buf ^ 1];
@@ -272,15 +283,21 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
         const int tr = (u ? tb1 : tb0) * 32 + m;
         const bool valid = tr < t.nvalid;
 #pragma unroll
-        for (int s = 0; s < KS; ++s) cf[u][s] = I::load_row(t.ct + (int64_t)tr * G * N + s * 16 + 8 * g, valid);
+        for (int s = 0; s < KS; ++s) {
+          u32x4 c4 = __builtin_bit_cast(u32x4, I::load_row(t.ct + (int64_t)tr * G * N + s * 16 + 8 * g, valid));
+          asm("" : "=a"(c4) : "0"(c4));     // held in AGPRs; the MFMA reads them there
+          cf[u][s] = __builtin_bit_cast(Frag, c4);
+        }
       }
       // the chunk's B rows into the other buffer (padded rows), rows past
       // the sequence clamped to its last row
+      int lanel = lane;   // laundered: these offsets are recomputed per phase, not kept across the walk
+      asm volatile("" : "+v"(lanel));
 #pragma unroll
       for (int i = 0; i < LB; ++i) {
         int kk = wave + 4 * i;
         if (kk >= Cf::IB) kk %= Cf::IB;
-        const int s = kk * 64 + lane;
+        const int s = kk * 64 + lanel;
         int r = s / Cf::BROWP, c = s % Cf::BROWP;
         if (r >= Q) r = Q - 1;
         if (c >= Cf::RB) c = 0;
@@ -292,20 +309,20 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
       wait_vm_barrier<Cf::LT>();
       const unsigned char* bb = oth + m * Cf::BRB + g * 16;
 #pragma unroll
-      for (int kp = 0; kp < 9; ++kp) {
-        const bool first = kp <= wave;
-        const int jb = first ? kp : kp - wave - 1;
+      for (int e = 0; e < 12; ++e) {
+        // emitted (slot, t-block) combinations: slot 0 (u = 0), slots 1..3
+        // for u = 0 and for u = 1, slots 4..8 (u = 1)
+        const int sl = e < 4 ? e : (e < 7 ? e - 3 : e - 3);
+        const int u = e < 4 ? 0 : 1;
+        if (e >= 4 && e < 7 && sl <= wave) continue;   // slot belongs to t-block w
+        if (e >= 1 && e < 4 && sl > wave) continue;    // slot belongs to t-block 7 - w
+        const int jb = u ? 8 - sl : sl;
         const unsigned char* bj = bb + jb * 32 * Cf::BRB;
         f32x16 acc = f32x16{};
-        if (first) {
 #pragma unroll
-          for (int s = 0; s < KS; ++s) I::mma(acc, *reinterpret_cast<const Frag*>(bj + s * 32), cf[0][s]);
-        } else {
+        for (int s = 0; s < KS; ++s) I::mma(acc, *reinterpret_cast<const Frag*>(bj + s * 32), cf[u][s]);
 #pragma unroll
-          for (int s = 0; s < KS; ++s) I::mma(acc, *reinterpret_cast<const Frag*>(bj + s * 32), cf[1][s]);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) cbc[kp][r] = to_agpr(acc[r]);
+        for (int r = 0; r < 16; ++r) cbc[sl][r] = to_agpr(acc[r]);
       }
       lds_barrier();      // the B tile is read; its buffer may be refilled
       ckey_cached = t.ckey;
@@ -356,6 +373,7 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
       const unsigned char* hp = cur + Cf::HOFF + (pe * 32 + m) * Cf::HRB;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
+        if (s % 4 == 0) __builtin_amdgcn_sched_barrier(0);   // bounds the Hprev fragments in flight
         const Frag hhi = *reinterpret_cast<const Frag*>(hp + (2 * s + g) * 32);
         const Frag hlo = *reinterpret_cast<const Frag*>(hp + (2 * s + g) * 32 + 16);
 #pragma unroll
@@ -374,15 +392,20 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
         acc[u][1][r] *= sc;
       }
 
-    // intra-chunk pairs
+    // intra-chunk pairs, slot by slot, specialised per wave (straight-line code)
     const unsigned char* xt = cur;
+    auto pairs = [&](auto wtag) {
+      constexpr int W = decltype(wtag)::value;
 #pragma unroll
-    for (int kp = 0; kp < 9; ++kp) {
-      __builtin_amdgcn_sched_barrier(0);   // one pair at a time: bounds the live registers
-      const bool first = kp <= wave;
-      const int jb = first ? kp : kp - wave - 1;
-      const bool diag = first ? (kp == wave) : (kp == 8);
-      const float gtu = first ? gt0 : gt1;
+    for (int e = 0; e < 12; ++e) {
+      const int sl = e < 4 ? e : e - 3;       // the same emission order as the C.B^T phase
+      const int u = e < 4 ? 0 : 1;
+      if (e >= 4 && e < 7 && sl <= W) continue;
+      if (e >= 1 && e < 4 && sl > W) continue;
+      const int jb = u ? 8 - sl : sl;
+      const int tb = u ? 7 - W : W;
+      const bool diag = jb == tb;
+      const float gtu = u ? gt1 : gt0;
       const int j0 = jb * 32;
       // x dwords of rows drow(q, g) of the block (columns 2m, 2m+1)
       uint32_t d[16];
@@ -397,38 +420,35 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
         u32x4 e0, e1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint32_t a = d[js * 8 + 2 * i], c = d[js * 8 + 2 * i + 1];
-          e0[i] = __builtin_amdgcn_perm(c, a, 0x05040100u);   // low halves: column 2m
-          e1[i] = __builtin_amdgcn_perm(c, a, 0x07060302u);   // high halves: column 2m + 1
+          const uint32_t lo2 = d[js * 8 + 2 * i], hi2 = d[js * 8 + 2 * i + 1];
+          e0[i] = __builtin_amdgcn_perm(hi2, lo2, 0x05040100u);   // low halves: column 2m
+          e1[i] = __builtin_amdgcn_perm(hi2, lo2, 0x07060302u);   // high halves: column 2m + 1
         }
         xf[0][js] = __builtin_bit_cast(Frag, e0);
         xf[1][js] = __builtin_bit_cast(Frag, e1);
       }
-      float v[16], cb[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) cb[r] = from_agpr(cbc[kp][r]);
+      float v[16];
       if (!diag) {
         // every t is past the whole j-block: 2^(G'_t - G'_j) = 2^(G'_t - G'_end) 2^(G'_end - G'_j)
         const float a = exp2_hw(gtu - sG[j0 + 31]);
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
           const float4 wv = *reinterpret_cast<const float4*>(&sW[j0 + 8 * c4 + 4 * g]);
-          v[4 * c4 + 0] = cb[4 * c4 + 0] * (wv.x * a);
-          v[4 * c4 + 1] = cb[4 * c4 + 1] * (wv.y * a);
-          v[4 * c4 + 2] = cb[4 * c4 + 2] * (wv.z * a);
-          v[4 * c4 + 3] = cb[4 * c4 + 3] * (wv.w * a);
+          v[4 * c4 + 0] = from_agpr(cbc[sl][4 * c4 + 0]) * (wv.x * a);
+          v[4 * c4 + 1] = from_agpr(cbc[sl][4 * c4 + 1]) * (wv.y * a);
+          v[4 * c4 + 2] = from_agpr(cbc[sl][4 * c4 + 2]) * (wv.z * a);
+          v[4 * c4 + 3] = from_agpr(cbc[sl][4 * c4 + 3]) * (wv.w * a);
         }
       } else {
         // diagonal block: direct decay; the causal mask is a select
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int jr = drow(q, g);
-          const float val = cb[q] * exp2_hw(gtu - sG[j0 + jr]) * sDt[j0 + jr];
+          const float val = from_agpr(cbc[sl][q]) * exp2_hw(gtu - sG[j0 + jr]) * sDt[j0 + jr];
           v[q] = (m >= jr) ? val : 0.f;
         }
       }
       // (hi, lo) bf16 split of the decayed block, two MFMAs per x fragment
-      Frag ahi[2], alo[2];
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
         u32x4 uh, ul;
@@ -440,61 +460,60 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
           ul[i] = pack_bf16x2(v[js * 8 + 2 * i] - __uint_as_float(hh << 16),
                               v[js * 8 + 2 * i + 1] - __uint_as_float(hh & 0xffff0000u));
         }
-        ahi[js] = __builtin_bit_cast(Frag, uh);
-        alo[js] = __builtin_bit_cast(Frag, ul);
-      }
-      if (first) {
+        const Frag ahi = __builtin_bit_cast(Frag, uh), alo = __builtin_bit_cast(Frag, ul);
 #pragma unroll
-        for (int js = 0; js < 2; ++js)
-#pragma unroll
-          for (int pe = 0; pe < 2; ++pe) {
-            I::mma(acc[0][pe], ahi[js], xf[pe][js]);
-            I::mma(acc[0][pe], alo[js], xf[pe][js]);
-          }
-      } else {
-#pragma unroll
-        for (int js = 0; js < 2; ++js)
-#pragma unroll
-          for (int pe = 0; pe < 2; ++pe) {
-            I::mma(acc[1][pe], ahi[js], xf[pe][js]);
-            I::mma(acc[1][pe], alo[js], xf[pe][js]);
-          }
-      }
-      if (diag) {
-        // D x for the block's own rows: the same x dwords
-        if (first) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            acc[0][0][r] += t.Dh * bf16lo(d[r]);
-            acc[0][1][r] += t.Dh * bf16hi(d[r]);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            acc[1][0][r] += t.Dh * bf16lo(d[r]);
-            acc[1][1][r] += t.Dh * bf16hi(d[r]);
-          }
+        for (int pe = 0; pe < 2; ++pe) {
+          I::mma(acc[u][pe], ahi, xf[pe][js]);
+          I::mma(acc[u][pe], alo, xf[pe][js]);
         }
       }
     }
-
-    // y: one dword (columns 2m, 2m+1) per lane per row. The row offset is
-    // wave-uniform; the lane offset is re-derived per tile (laundered), so
-    // the compiler does not keep 32 loop-invariant row addresses alive
-    // across the whole walk.
-    const bool full = t.nvalid == Q;
-    uint32_t ylane = (uint32_t)(4 * g) * xrb + 4 * m;
-    uint32_t xrbs = xrb;
-    asm volatile("" : "+v"(ylane), "+s"(xrbs));
+    };
+    switch (wave) {
+      case 0: pairs(std::integral_constant<int, 0>{}); break;
+      case 1: pairs(std::integral_constant<int, 1>{}); break;
+      case 2: pairs(std::integral_constant<int, 2>{}); break;
+      default: pairs(std::integral_constant<int, 3>{}); break;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // D x on the rows of the wave's own t-blocks
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u) {
+      const int j0 = (u ? tb1 : tb0) * 32;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int trow = (u ? tb1 : tb0) * 32 + 8 * (r / 4) + r % 4;   // + 4g in ylane
-        if (full || trow + 4 * g < t.nvalid)
-          *reinterpret_cast<uint32_t*>(t.y + (uint32_t)trow * xrbs + ylane) =
-              pack_bf16x2(acc[u][0][r], acc[u][1][r]);
+        const uint32_t xd = *reinterpret_cast<const uint32_t*>(
+            xt + j0 * 128 + 128 * (8 * (r / 4) + r % 4) + ((r & 1) ? xbo : xbe));
+        acc[u][0][r] += t.Dh * bf16lo(xd);
+        acc[u][1][r] += t.Dh * bf16hi(xd);
       }
+    }
+
+    // y: one dword (columns 2m, 2m+1) per lane per row, through a buffer
+    // resource over the tile's valid rows. Full tiles put the row in the
+    // scalar offset (no per-store address arithmetic); a ragged tile keeps
+    // the whole offset in the range-checked vector operand, so rows past
+    // the sequence are dropped. The lane offset is re-derived per tile
+    // (laundered) so the compiler does not keep row addresses alive across
+    // the walk.
+    const bool full = t.nvalid == Q;
+    {
+      uint32_t ylane = (uint32_t)(4 * g) * xrb + 4 * m;
+      uint32_t xrbs = xrb;
+      asm volatile("" : "+v"(ylane), "+s"(xrbs));
+      const __amdgpu_buffer_rsrc_t yr = make_rsrc(t.y, (uint32_t)t.nvalid * xrbs);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t trow = (uint32_t)((u ? tb1 : tb0) * 32 + 8 * (r / 4) + r % 4);   // + 4g in ylane
+          const uint32_t val = pack_bf16x2(acc[u][0][r], acc[u][1][r]);
+          if (full)
+            __builtin_amdgcn_raw_buffer_store_b32(val, yr, ylane, trow * xrbs, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(val, yr, ylane + trow * xrbs, 0, 0);
+        }
+    }
     ys = (prefetch && full) ? 1 : 0;
     buf ^= 1;
   }
