@@ -38,21 +38,22 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 F32_PEAK_TFLOPS = 157.3        # MI355X dense fp32 MFMA, published
 KERNELS = ["ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_pass", "ssd_chunk_scan"]
-KERNEL_SOURCES = {"ssd_chunk_cumsum": "chunk_cumsum.hip", "ssd_chunk_state": "chunk_state.hip",
-                  "ssd_state_pass": "state_pass.hip", "ssd_chunk_scan": "chunk_scan.hip",
-                  "ssd_step": "ssd_step.hip"}
+KERNEL_SOURCES = {"ssd_chunk_cumsum": ["chunk_cumsum.hip"], "ssd_chunk_state": ["chunk_state.hip"],
+                  "ssd_state_pass": ["state_pass.hip"],
+                  "ssd_chunk_scan": ["chunk_scan.hip", "chunk_scan_resident.hip"],
+                  "ssd_step": ["ssd_step.hip"]}
 TRAFFIC_SUMMARY = {"mamba2-2.7b": "hbm_traffic_mamba2-2.7b.md",
                    "mamba2-2.7b-decode": "hbm_traffic_mamba2-2.7b-decode.md"}
 
 
 def source_hash(kernel):
-    """sha256 (first 16 hex digits) of a kernel's .hip file followed by the
+    """sha256 (first 16 hex digits) of a kernel's .hip files followed by the
     shared device header: the key under which measured traffic is recorded.
     (ssd_launch.h holds only host-side declarations.)"""
     import hashlib
     csrc = os.path.join(ROOT, "state_space_sequence_ssd_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[kernel], "ssd_device.h"):
+    for f in KERNEL_SOURCES[kernel] + ["ssd_device.h"]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
