@@ -23,6 +23,10 @@
  *                     product of the "Kernel 2: fwd_pass_state" section)
  *   ssd_state_pass    the sequential pass over chunk checkpoints
  *                     (the chunk loop of the same section)
+ *   (for bf16 io with headdim 64 the chunk states can instead be computed
+ *   inside the state pass: one kernel, ssd_chunk_state_pass, with the
+ *   structure of the blog's "Kernel 2", the per-chunk states never reaching
+ *   memory; mamba2_ssd_fused_state_pass tells which path a call takes)
  *   ssd_chunk_scan    the per-chunk outputs: decayed carried-state term,
  *                     masked decayed C.B^T product with dt*x, and D*x
  *                     (blog section "Kernel 3: compute_out")
@@ -99,6 +103,9 @@ typedef struct {
  *                                      of token t in its chunk's state
  *   states  float [batch][nheads][nchunks][headdim][dstate]
  *                                      each chunk's own contribution S_k
+ *                                      (not written when the states are
+ *                                      computed inside the pass, see
+ *                                      mamba2_ssd_fused_state_pass)
  *   hprev   [batch][nheads][nchunks][headdim][dstate] states h entering
  *           each chunk; io = F32: float; io = BF16: bf16 pairs, 4 bytes per
  *           element: for each row and each aligned group of 8 dstate
@@ -167,10 +174,22 @@ int mamba2_ssd_fwd(const mamba2_ssd_dims* dims, int io_dtype,
                    const float* init_state, void* y, float* final_state,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* 1 if mamba2_ssd_fwd with these sizes computes the chunk states inside
+ * the state pass (one kernel, ssd_chunk_state_pass; the workspace's states
+ * region is then left untouched), 0 if it runs ssd_chunk_state and
+ * ssd_state_pass, or if the sizes are invalid. The environment variable
+ * MAMBA2_SSD_STATE_PATH (read on every call) overrides the choice: "unfused"
+ * forces the two kernels, "fused" the one kernel wherever it supports the
+ * shape (bf16, headdim 64, dstate 64/128/256, chunk 128/256). Both paths
+ * give bit-identical results. Host only. */
+int mamba2_ssd_fused_state_pass(const mamba2_ssd_dims* dims, int io_dtype);
+
 /* mamba2_ssd_fwd that also records caller-created events on `stream`, so
  * each kernel can be timed where it runs: events[0] before ssd_chunk_cumsum,
  * events[1] before ssd_chunk_state, events[2] before ssd_state_pass,
- * events[3] before ssd_chunk_scan and events[4] after it. `events` points to
+ * events[3] before ssd_chunk_scan and events[4] after it. On the fused path
+ * events[1]..events[2] enclose ssd_chunk_state_pass and events[2]..events[3]
+ * nothing. `events` points to
  * 5 hipEvent_t handles (passed as void*) owned by the caller; NULL makes the
  * call identical to mamba2_ssd_fwd. The kernels and their order are the
  * same; a failed event record returns MAMBA2_SSD_ERR_HIP. */

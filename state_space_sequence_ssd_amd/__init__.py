@@ -20,7 +20,8 @@ __all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_
            "mamba2_ssd_fwd_workspace_bytes", "mamba2_ssd_workspace_layout_query",
            "mamba2_ssd_status_string", "mamba2_ssd_last_hip_error",
            "ssd_step", "ssd_step_ptr", "step_supported", "step_check_args", "StepDims",
-           "mamba2_ssd_step", "mamba2_ssd_step_check_args", "mamba2_ssd_step_supported"]
+           "mamba2_ssd_step", "mamba2_ssd_step_check_args", "mamba2_ssd_step_supported",
+           "mamba2_ssd_fused_state_pass", "fused_state_pass"]
 
 # The C entry points under their own names (ctypes functions with prototypes).
 mamba2_ssd_fwd = lib.mamba2_ssd_fwd
@@ -31,6 +32,7 @@ mamba2_ssd_fwd_workspace_bytes = lib.mamba2_ssd_fwd_workspace_bytes
 mamba2_ssd_workspace_layout_query = lib.mamba2_ssd_workspace_layout_query
 mamba2_ssd_status_string = lib.mamba2_ssd_status_string
 mamba2_ssd_last_hip_error = lib.mamba2_ssd_last_hip_error
+mamba2_ssd_fused_state_pass = lib.mamba2_ssd_fused_state_pass
 mamba2_ssd_step = lib.mamba2_ssd_step
 mamba2_ssd_step_check_args = lib.mamba2_ssd_step_check_args
 mamba2_ssd_step_supported = lib.mamba2_ssd_step_supported
@@ -54,6 +56,12 @@ def workspace_layout(dims, io: int) -> WorkspaceLayout:
     if st != 0:
         raise SsdError(st)
     return out
+
+
+def fused_state_pass(dims, io: int) -> bool:
+    """Whether a forward call with these sizes computes the chunk states inside
+    the state pass (then the workspace's states region is not written)."""
+    return bool(lib.mamba2_ssd_fused_state_pass(ctypes.byref(_dims(dims)), io))
 
 
 def workspace_bytes(dims, io: int) -> int:

@@ -83,6 +83,8 @@ def _load():
     L.mamba2_ssd_fwd_timed.argtypes = [dims_p, ctypes.c_int, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, sz, vp,
                                        ctypes.POINTER(ctypes.c_void_p)]
     L.mamba2_ssd_fwd_timed.restype = ctypes.c_int
+    L.mamba2_ssd_fused_state_pass.argtypes = [dims_p, ctypes.c_int]
+    L.mamba2_ssd_fused_state_pass.restype = ctypes.c_int
     step_p = ctypes.POINTER(StepDims)
     L.mamba2_ssd_step_supported.argtypes = [i64, ctypes.c_int]
     L.mamba2_ssd_step_supported.restype = ctypes.c_int

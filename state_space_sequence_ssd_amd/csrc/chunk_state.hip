@@ -197,6 +197,190 @@ __global__ __launch_bounds__((StateCfg<T, P, N>::THREADS)) void ssd_chunk_state(
     state_tile<T, P, N, Q, false>(x, Bm, wst, states, Tlen, H, G, nc, Tp, h, k, b, pg, ng0, m, g);
 }
 
+// ---------------------------------------------------------------------------
+// ssd_chunk_state_pass: the chunk states and the pass over them in one kernel
+// (the structure of the blog's "Kernel 2: fwd_pass_state": one program walks
+// a head's chunks in order, computes each chunk's contribution with an MMA
+// and jumps the carried state over the chunk), for bf16 io with headdim 64.
+// One wave owns one (batch, head, 64-column dstate group): it holds the state
+// h for 64 x 64 entries in the MFMA accumulator layout, and for each chunk k
+//   hprev[k] = h (as bf16 (hi, lo) pairs, the state pass's format),
+//   S_k      = X_k^T (w o B_k)  (the tile product above, same operands),
+//   h        = 2^(G'_last,k) h + S_k   (fmaf, as the state pass does),
+// then writes final = h. The per-chunk states never reach memory: this
+// saves writing and re-reading them (4 P N bytes each way per chunk). The
+// loads of x, B and w run a ring of RING k-steps (16 tokens each) that
+// continues across chunk boundaries; the ring size divides the k-steps of a
+// chunk so every slot index stays static. The chunks of one head are
+// sequential here, so this form needs many (batch, head) pairs to fill the
+// GPU; the host takes it only then.
+template <int N, int Q>
+struct FusedCfg {
+  static constexpr int P = 64, KSTEPS = Q / 16;
+  static constexpr int RING = 8;   // k-steps of loads in flight; divides KSTEPS for Q = 128, 256
+  static constexpr int NNG = N / 64;          // dstate groups (waves) per (batch, head)
+  static_assert(KSTEPS % RING == 0, "ring slots must repeat every chunk");
+};
+
+template <int N, int Q>
+__global__ __launch_bounds__(64) void ssd_chunk_state_pass(
+    const bf16* __restrict__ x, const bf16* __restrict__ Bm, const float* __restrict__ wst,
+    const float* __restrict__ gcum, const float* init, void* __restrict__ hprev, float* final_state,
+    int64_t Tlen, int H, int G, int64_t nc, int64_t Tp) {
+  using I = Io<bf16>;
+  using Fc = FusedCfg<N, Q>;
+  constexpr int P = 64, KPL = 8, KSTEPS = Fc::KSTEPS, RING = Fc::RING, NNG = Fc::NNG;
+  const int lane = threadIdx.x, m = lane % 32, g = lane / 32;
+  const int64_t wid = blockIdx.x;
+  const int ng = (int)(wid % NNG);
+  const int64_t bh = wid / NNG;
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  const int grp = h / (H / G);
+  const uint32_t xsb = (uint32_t)H * P * 2, bsb = (uint32_t)G * N * 2;
+  const int64_t nfull = Tlen / Q;   // chunks entirely inside the sequence
+  const uint32_t xlane = m * 4 + KPL * g * xsb, blane = m * 4 + KPL * g * bsb;
+
+  // resources of chunk k: x (this head, all 64 headdim columns), B (this
+  // group, the wave's 64 dstate columns), both over the chunk's valid rows
+  auto rsrc_x = [&](int64_t k) {
+    const int64_t t0 = k * Q;
+    const int nv = (int)(Tlen - t0 < Q ? Tlen - t0 : Q);
+    return make_rsrc(x + ((b * Tlen + t0) * H + h) * P, (uint32_t)(nv - 1) * xsb + 128);
+  };
+  auto rsrc_b = [&](int64_t k) {
+    const int64_t t0 = k * Q;
+    const int nv = (int)(Tlen - t0 < Q ? Tlen - t0 : Q);
+    return make_rsrc(Bm + ((b * Tlen + t0) * G + grp) * N + ng * 64, (uint32_t)(nv - 1) * bsb + 128);
+  };
+  const float* wrow = wst + bh * Tp;   // chunk k's weights at wrow + k*Q (the workspace covers padding)
+  auto load = [&](Step<bf16, 1>& st, int64_t k, int s, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rb) {
+    if (k < nfull)
+      load_step<bf16, 1, true>(st, s, rx, rb, wrow + k * Q, xlane, blane, xsb, bsb, g);
+    else
+      load_step<bf16, 1, false>(st, s, rx, rb, wrow + k * Q, xlane, blane, xsb, bsb, g);
+  };
+
+  // h[pe][ne][r]: p = 2 drow(r, g) + pe, n = 64 ng + 2m + ne
+  f32x16 hs[2][2];
+  if (init) {
+    const float* ip = init + bh * (int64_t)(P * N) + ng * 64 + 2 * m;
+#pragma unroll
+    for (int pe = 0; pe < 2; ++pe)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float2 v = *reinterpret_cast<const float2*>(ip + (2 * drow(r, g) + pe) * N);
+        hs[pe][0][r] = v.x;
+        hs[pe][1][r] = v.y;
+      }
+  } else {
+#pragma unroll
+    for (int pe = 0; pe < 2; ++pe)
+#pragma unroll
+      for (int ne = 0; ne < 2; ++ne) hs[pe][ne] = f32x16{};
+  }
+
+  // hprev pair stores: row p of chunk k at (b,h,k) block + p * 4N bytes; the
+  // lane's two columns n, n+1 sit in group n/8 at position n%8: its hi
+  // dword at (n/8)*32 + (n%8)*2 bytes, its lo dword 16 bytes further
+  const uint32_t hlane = (uint32_t)(8 * g) * (4 * N) + (uint32_t)((ng * 8 + m / 4) * 32 + (m % 4) * 4);
+  unsigned char* hbase = static_cast<unsigned char*>(hprev) + bh * nc * (int64_t)(P * N) * 4;
+
+  Step<bf16, 1> ring[RING];
+  __amdgpu_buffer_rsrc_t rx = rsrc_x(0), rb = rsrc_b(0);
+  __amdgpu_buffer_rsrc_t rxn = rx, rbn = rb;
+  if (nc > 1) {
+    rxn = rsrc_x(1);
+    rbn = rsrc_b(1);
+  }
+#pragma unroll
+  for (int s = 0; s < RING - 1; ++s) load(ring[s], 0, s, rx, rb);
+
+  for (int64_t k = 0; k < nc; ++k) {
+    // hprev[k] = h
+    {
+      const __amdgpu_buffer_rsrc_t rh = make_rsrc(hbase + k * (int64_t)(P * N) * 4, (uint32_t)(P * N * 4));
+#pragma unroll
+      for (int pe = 0; pe < 2; ++pe)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t d = pack_bf16x2(hs[pe][0][r], hs[pe][1][r]);
+          const uint32_t lo = pack_bf16x2(hs[pe][0][r] - bf16lo(d), hs[pe][1][r] - bf16hi(d));
+          const uint32_t row = (uint32_t)(16 * (r / 4) + 2 * (r % 4) + pe) * (4 * N);   // + 8g rows in hlane
+          __builtin_amdgcn_raw_buffer_store_b32(d, rh, hlane, row, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(lo, rh, hlane + 16, row, 0);
+        }
+    }
+    // S_k over the chunk's k-steps; the loads run RING-1 steps ahead, into
+    // the next chunk near the end
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int pe = 0; pe < 2; ++pe)
+#pragma unroll
+      for (int ne = 0; ne < 2; ++ne) acc[pe][ne] = f32x16{};
+    // (a runtime loop over groups of RING steps, unrolled within: the ring
+    // slot of every step stays static without unrolling the whole chunk)
+    for (int s0 = 0; s0 < KSTEPS; s0 += RING) {
+#pragma unroll
+    for (int si = 0; si < RING; ++si) {
+      const int s = s0 + si;
+      const int sa = s + RING - 1;
+      if (sa < KSTEPS) load(ring[(si + RING - 1) % RING], k, sa, rx, rb);
+      else if (k + 1 < nc) load(ring[(si + RING - 1) % RING], k + 1, sa - KSTEPS, rxn, rbn);
+      const Step<bf16, 1>& cur = ring[si];
+      typename I::Frag ahi[2], alo[2];
+#pragma unroll
+      for (int pe = 0; pe < 2; ++pe) {
+        float v[KPL];
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) v[i] = cur.w[i] * I::elem(cur.xd[i], pe);
+        I::split(v, ahi[pe], alo[pe]);
+      }
+#pragma unroll
+      for (int ne = 0; ne < 2; ++ne) {
+        const typename I::Frag bf = I::from_dwords(cur.bd[0], ne);
+#pragma unroll
+        for (int pe = 0; pe < 2; ++pe) {
+          I::mma(acc[pe][ne], ahi[pe], bf);
+          I::mma(acc[pe][ne], alo[pe], bf);
+        }
+      }
+    }
+    }
+    // h = 2^(G'_last,k) h + S_k
+    const float sc = exp2_hw(gcum[bh * Tp + k * Q + (Q - 1)]);
+#pragma unroll
+    for (int pe = 0; pe < 2; ++pe)
+#pragma unroll
+      for (int ne = 0; ne < 2; ++ne)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) hs[pe][ne][r] = fmaf(sc, hs[pe][ne][r], acc[pe][ne][r]);
+    rx = rxn;
+    rb = rbn;
+    if (k + 2 < nc) {
+      rxn = rsrc_x(k + 2);
+      rbn = rsrc_b(k + 2);
+    }
+  }
+  if (final_state) {
+    float* fp = final_state + bh * (int64_t)(P * N) + ng * 64 + 2 * m;
+#pragma unroll
+    for (int pe = 0; pe < 2; ++pe)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        *reinterpret_cast<float2*>(fp + (2 * drow(r, g) + pe) * N) = make_float2(hs[pe][0][r], hs[pe][1][r]);
+  }
+}
+
+template <int N, int Q>
+hipError_t launch_fused(const Problem& p, hipStream_t stream) {
+  const int64_t waves = p.bt * p.H * FusedCfg<N, Q>::NNG;
+  hipLaunchKernelGGL((ssd_chunk_state_pass<N, Q>), dim3((unsigned)waves), dim3(64), 0, stream, (const bf16*)p.x,
+                     (const bf16*)p.B, p.wst, p.gcum, p.init, p.hprev, p.final_state, p.T, (int)p.H, (int)p.G,
+                     p.nc, p.Tp);
+  return hipGetLastError();
+}
+
 template <typename T, int P, int N, int Q>
 hipError_t launch_one(const Problem& p, hipStream_t stream) {
   using Cfg = StateCfg<T, P, N>;
@@ -226,6 +410,29 @@ bool chunk_state_has(int io, int64_t P, int64_t N, int64_t Q) {
 
 hipError_t launch_chunk_state(const Problem& p, hipStream_t stream) {
   return p.io == 1 ? dispatch<bf16>(p, stream) : dispatch<float>(p, stream);
+}
+
+bool chunk_state_pass_fits(const Problem& p) {
+  // bf16, headdim 64, dstate 64/128/256, chunk 128/256, at least one chunk
+  return p.io == 1 && p.P == 64 && (p.Q == 128 || p.Q == 256) && (p.N == 64 || p.N == 128 || p.N == 256) &&
+         p.nc > 0;
+}
+
+bool chunk_state_pass_pays(const Problem&) {
+  // Measured on MI355X, this form loses on every configuration tried: each
+  // wave walks its head's chunks in sequence and its dword loads keep only
+  // about 16 KB in flight, so a chunk costs ~10-12 us (2.7B-like layer:
+  // 392 us against 310 us for ssd_chunk_state + ssd_state_pass). It runs
+  // only when MAMBA2_SSD_STATE_PATH=fused asks for it.
+  return false;
+}
+
+hipError_t launch_chunk_state_pass(const Problem& p, hipStream_t stream) {
+#define SSD_CASE(NN, QQ) \
+  if (p.N == NN && p.Q == QQ) return launch_fused<NN, QQ>(p, stream);
+  SSD_CASE(64, 128) SSD_CASE(64, 256) SSD_CASE(128, 128) SSD_CASE(128, 256) SSD_CASE(256, 128) SSD_CASE(256, 256)
+#undef SSD_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ssd

@@ -8,6 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
 #include <cstring>
 #include <string>
 
@@ -94,6 +95,25 @@ void layout_of(const mamba2_ssd_dims* d, const Sizes& s, mamba2_ssd_workspace_la
   off = align_up(off + (size_t)s.n_chunkstates * 4);
   L->total_bytes = off;
   L->nchunks = s.nc;
+}
+
+// Whether a forward call computes the chunk states inside the state pass
+// (one kernel, see chunk_state.hip). MAMBA2_SSD_STATE_PATH in the environment
+// (read per call) overrides the size rule: "unfused" forces the two-kernel
+// path, "fused" takes the one-kernel path for every shape it supports. A
+// diagnostic switch; both paths give bit-identical results.
+bool use_fused_state(const ssd::Problem& p) {
+  const char* e = std::getenv("MAMBA2_SSD_STATE_PATH");
+  if (e && std::strcmp(e, "unfused") == 0) return false;
+  if (e && std::strcmp(e, "fused") == 0) return ssd::chunk_state_pass_fits(p);
+  return ssd::chunk_state_pass_fits(p) && ssd::chunk_state_pass_pays(p);
+}
+
+ssd::Problem problem_of(const mamba2_ssd_dims* d, int io, const Sizes& s) {
+  ssd::Problem p{};
+  p.bt = d->batch; p.T = d->seqlen; p.H = d->nheads; p.P = d->headdim; p.N = d->dstate;
+  p.G = d->ngroups; p.Q = d->chunk; p.nc = s.nc; p.Tp = s.Tp; p.io = io;
+  return p;
 }
 
 struct Range {
@@ -187,9 +207,7 @@ int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* d, int io, const void* x, const 
   layout_of(d, s, &L);
   char* ws = static_cast<char*>(workspace);
 
-  ssd::Problem p;
-  p.bt = d->batch; p.T = d->seqlen; p.H = d->nheads; p.P = d->headdim; p.N = d->dstate;
-  p.G = d->ngroups; p.Q = d->chunk; p.nc = s.nc; p.Tp = s.Tp; p.io = io;
+  ssd::Problem p = problem_of(d, io, s);
   p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D;
   p.init = init_state; p.y = y; p.final_state = final_state;
   p.gcum = reinterpret_cast<float*>(ws + L.gcum_offset);
@@ -206,10 +224,17 @@ int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* d, int io, const void* x, const 
   mark(0);
   if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_cumsum(p, hs);
   mark(1);
-  if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_state(p, hs);
-  mark(2);
-  // with seqlen == 0 the pass runs zero chunks: final_state = init_state (or 0)
-  if (err == hipSuccess && (s.nc > 0 || final_state)) err = ssd::launch_state_pass(p, hs);
+  if (use_fused_state(p)) {
+    // chunk states and the pass in one kernel; the events around the pass
+    // then enclose nothing
+    if (err == hipSuccess) err = ssd::launch_chunk_state_pass(p, hs);
+    mark(2);
+  } else {
+    if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_state(p, hs);
+    mark(2);
+    // with seqlen == 0 the pass runs zero chunks: final_state = init_state (or 0)
+    if (err == hipSuccess && (s.nc > 0 || final_state)) err = ssd::launch_state_pass(p, hs);
+  }
   mark(3);
   if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_scan(p, hs);
   mark(4);
@@ -218,6 +243,12 @@ int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* d, int io, const void* x, const 
     return MAMBA2_SSD_ERR_HIP;
   }
   return MAMBA2_SSD_OK;
+}
+
+int mamba2_ssd_fused_state_pass(const mamba2_ssd_dims* dims, int io_dtype) {
+  Sizes s;
+  if (check_dims(dims, io_dtype, &s) != MAMBA2_SSD_OK) return 0;
+  return use_fused_state(problem_of(dims, io_dtype, s)) ? 1 : 0;
 }
 
 int mamba2_ssd_step_supported(int64_t dstate, int io_dtype) {

@@ -47,6 +47,11 @@ hipError_t launch_chunk_state(const Problem& p, hipStream_t stream);
 hipError_t launch_state_pass(const Problem& p, hipStream_t stream);
 hipError_t launch_chunk_scan(const Problem& p, hipStream_t stream);
 hipError_t launch_ssd_step(const StepProblem& p, hipStream_t stream);
+// The chunk states and the state pass in one kernel (chunk_state.hip): the
+// shapes it supports, and the sizes for which the forward call prefers it.
+bool chunk_state_pass_fits(const Problem& p);
+bool chunk_state_pass_pays(const Problem& p);
+hipError_t launch_chunk_state_pass(const Problem& p, hipStream_t stream);
 // The C.B^T-resident scan (chunk_scan_resident.hip) and the shapes it takes.
 bool chunk_scan_resident_fits(const Problem& p);
 hipError_t launch_chunk_scan_resident(const Problem& p, hipStream_t stream);

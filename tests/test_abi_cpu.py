@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
         "mamba2_ssd_check_args", "mamba2_ssd_fwd", "mamba2_ssd_fwd_timed", "mamba2_ssd_fwd_workspace_bytes",
         "mamba2_ssd_last_hip_error", "mamba2_ssd_status_string", "mamba2_ssd_supported",
         "mamba2_ssd_workspace_layout_query", "mamba2_ssd_step", "mamba2_ssd_step_check_args",
-        "mamba2_ssd_step_supported"])
+        "mamba2_ssd_step_supported", "mamba2_ssd_fused_state_pass"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -275,3 +275,20 @@ def test_step_empty_and_errors_without_launching():
         ssd.ssd_step_ptr(ssd.StepDims(1, 3, 64, 128, 2), BF16, 1, 1, 1, 1, 1, 1, 1, 1)
     assert e.value.status == GROUPS
     assert ssd._lib.lib.mamba2_ssd_step_check_args(None, BF16, 1, 1, 1, 1, 1, 1, 1, 1) == NULLP
+
+
+def test_fused_state_pass_query(monkeypatch):
+    # by default the two-kernel path runs (the one-kernel form does not pay)
+    assert not ssd.fused_state_pass(HEADLINE, BF16)
+    assert not ssd.fused_state_pass(HEADLINE, F32)                      # fp32 io: two kernels
+    assert not ssd.fused_state_pass(Dims(1, 65536, 80, 64, 128, 1, 256), BF16)   # too few (b, h) pairs
+    assert not ssd.fused_state_pass(Dims(4, 8192, 80, 128, 128, 1, 256), BF16)   # headdim 128
+    assert not ssd.fused_state_pass(Dims(4, 0, 80, 64, 128, 1, 256), BF16)       # no chunks
+    assert not ssd.fused_state_pass(Dims(4, 8192, 80, 64, 128, 3, 256), BF16)    # invalid (groups)
+    monkeypatch.setenv("MAMBA2_SSD_STATE_PATH", "unfused")
+    assert not ssd.fused_state_pass(HEADLINE, BF16)
+    monkeypatch.setenv("MAMBA2_SSD_STATE_PATH", "fused")
+    assert ssd.fused_state_pass(Dims(1, 65536, 80, 64, 128, 1, 256), BF16)
+    assert ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 128), BF16)
+    assert not ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 64), BF16)        # chunk 64: not supported
+    assert not ssd.fused_state_pass(HEADLINE, F32)

@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 import torch
 
+import state_space_sequence_ssd_amd as ssd
 from oracle import ssd_chunked, ssd_sequential
 from tests.gpu_helpers import check_close, host, log, run, to_device, workspace_views
 from workloads import CONFIGS, HELD_OUT, LayerConfig, config_by_name, generate
@@ -265,3 +266,66 @@ def test_resident_scan_walks(name):
     log("  " + check_close(host(fin), fr, cfg.io, "final_state"))
     y2, _ = run(dev, cfg.chunk)
     assert torch.equal(y, y2), "two identical calls must give identical y"
+
+
+# ------------------------------------ chunk states computed inside the state pass
+# (bf16, headdim 64: the one-kernel path). MAMBA2_SSD_STATE_PATH forces either
+# path regardless of size; both must match the oracle, and each other bit for
+# bit (the same products in the same order, the same fp32 update).
+FUSED = {
+    "2.7b-ragged": dict(batch=2, seqlen=3 * 256 + 13, nheads=5),
+    "one-chunk": dict(batch=3, seqlen=100, nheads=2),
+    "N64-Q128": dict(batch=1, seqlen=5 * 128 + 1, nheads=4, dstate=64, chunk=128),
+    "N256-groups": dict(batch=1, seqlen=600, nheads=8, dstate=256, ngroups=2),
+    "Q128-exact": dict(batch=2, seqlen=4 * 128, nheads=3, chunk=128),
+}
+
+
+def _hprev_bytes(ws, L, dims):
+    n = dims.batch * dims.nheads * L.nchunks * dims.headdim * dims.dstate * 4
+    return ws[L.hprev_offset:L.hprev_offset + n].clone()
+
+
+@pytest.mark.parametrize("name", sorted(FUSED))
+def test_fused_state_pass(name, monkeypatch):
+    cfg = LayerConfig(f"fused-{name}", **{**dict(headdim=64, dstate=128, ngroups=1, chunk=256, io="bf16",
+                                               seed=700 + len(name), init_sigma=0.3), **FUSED[name]})
+    log(f"[fused] {name}: {cfg}")
+    inp = generate(cfg)
+    yr, fr, inter = oracle_all(inp, cfg, intermediates=True)
+    dev = to_device(inp, cfg.io)
+    monkeypatch.setenv("MAMBA2_SSD_STATE_PATH", "fused")
+    y1, f1, ws1, L, dims = run(dev, cfg.chunk, keep_workspace=True)
+    assert ssd.fused_state_pass(dims, 1)
+    v = workspace_views(ws1, L, dims, 1)
+    log("  " + check_close(host(v["hprev"]), inter["hprev"], cfg.io, "hprev (fused)"))
+    log("  " + check_close(host(y1), yr, cfg.io, "y (fused)"))
+    log("  " + check_close(host(f1), fr, cfg.io, "final_state (fused)"))
+    monkeypatch.setenv("MAMBA2_SSD_STATE_PATH", "unfused")
+    y2, f2, ws2, _, _ = run(dev, cfg.chunk, keep_workspace=True)
+    assert not ssd.fused_state_pass(dims, 1)
+    assert torch.equal(_hprev_bytes(ws1, L, dims), _hprev_bytes(ws2, L, dims)), "hprev differs between paths"
+    assert torch.equal(f1, f2), "final_state differs between paths"
+    assert torch.equal(y1, y2), "y differs between paths"
+
+
+def test_fused_state_pass_in_place_and_no_final(monkeypatch):
+    """init_state may be final_state (in-place update); final_state may be absent."""
+    cfg = LayerConfig("fused-inplace", batch=2, seqlen=2 * 256 + 40, nheads=3, headdim=64, dstate=128,
+                      ngroups=1, chunk=256, io="bf16", seed=731, init_sigma=0.3)
+    inp = generate(cfg)
+    yr, fr = oracle_all(inp, cfg)
+    dev = to_device(inp, cfg.io)
+    monkeypatch.setenv("MAMBA2_SSD_STATE_PATH", "fused")
+    st = dev["init_state"].clone()
+    y, fin = ssd.ssd_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], cfg.chunk, st,
+                         final_state=st)
+    torch.cuda.synchronize()
+    assert fin.data_ptr() == st.data_ptr()
+    check_close(host(st), fr, cfg.io, "final_state in place (fused)")
+    check_close(host(y), yr, cfg.io, "y (fused, in place)")
+    y2, none = ssd.ssd_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], cfg.chunk,
+                           dev["init_state"], return_final_state=False)
+    torch.cuda.synchronize()
+    assert none is None
+    check_close(host(y2), yr, cfg.io, "y (fused, no final)")
