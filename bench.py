@@ -41,6 +41,7 @@ KERNELS = ["ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_pass", "ssd_chunk_s
 KERNEL_SOURCES = {"ssd_chunk_cumsum": ["chunk_cumsum.hip"], "ssd_chunk_state": ["chunk_state.hip"],
                   "ssd_state_pass": ["state_pass.hip"],
                   "ssd_chunk_scan": ["chunk_scan.hip", "chunk_scan_resident.hip"],
+                  "ssd_chunk_state_pass": ["chunk_state.hip"],
                   "ssd_step": ["ssd_step.hip"]}
 TRAFFIC_SUMMARY = {"mamba2-2.7b": "hbm_traffic_mamba2-2.7b.md",
                    "mamba2-2.7b-decode": "hbm_traffic_mamba2-2.7b-decode.md"}
@@ -97,6 +98,10 @@ def algorithmic_cost(cfg):
         "ssd_chunk_cumsum": (dt + 2 * gq, 0.0),
         "ssd_chunk_state": (x + bc + 2 * gq + st, 2.0 * Bt * H * Tp * P * N),
         "ssd_state_pass": (2 * st + fin + init + Bt * H * nc * 4, 2.0 * Bt * H * nc * P * N),
+        # chunk states inside the pass: x, B, the weights and the chunk-end
+        # cumsums in, Hprev (and final, init) out; no per-chunk states
+        "ssd_chunk_state_pass": (x + bc + gq + Bt * H * nc * 4 + st + fin + init,
+                                 2.0 * Bt * H * Tp * P * N + 2.0 * Bt * H * nc * P * N),
         "ssd_chunk_scan": (2 * x + 2 * bc + 2 * gq + st + H * 4,
                            2.0 * Bt * H * Tp * P * N                       # C . Hprev^T
                            + Bt * H * nc * Q * (Q + 1) * P                 # causal (CB) . X
@@ -326,20 +331,25 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    per_kernel_ms = {k: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in events]))
-                     for i, k in enumerate(KERNELS)}
+    # the kernels this call ran, and the events around each
+    if ssd.fused_state_pass(dims, io):
+        spans = [("ssd_chunk_cumsum", 0, 1), ("ssd_chunk_state_pass", 1, 3), ("ssd_chunk_scan", 3, 4)]
+    else:
+        spans = [(k, i, i + 1) for i, k in enumerate(KERNELS)]
+    ran = [k for k, _, _ in spans]
+    per_kernel_ms = {k: float(np.mean([ev[a].elapsed_time(ev[b]) for ev in events])) for k, a, b in spans}
     gpu_ms = float(np.mean([ev[0].elapsed_time(ev[4]) for ev in events]))
     tokens = cfg.batch * cfg.seqlen
     cost = algorithmic_cost(cfg)
     kern = {}
-    for k in KERNELS:
+    for k in ran:
         nbytes, flops = cost[k]
         sec = per_kernel_ms[k] * 1e-3
         peak_tf = BF16_PEAK_TFLOPS if cfg.io == "bf16" else F32_PEAK_TFLOPS
         kern[k] = {"us": round(per_kernel_ms[k] * 1e3, 2), "alg_bytes": int(nbytes),
                    "GB/s": round(nbytes / sec / 1e9, 1), "frac_hbm": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
                    "alg_TFLOP/s": round(flops / sec / 1e12, 2), "frac_mfma": round(flops / sec / 1e12 / peak_tf, 4)}
-    dom = max(KERNELS, key=lambda k: per_kernel_ms[k])
+    dom = max(ran, key=lambda k: per_kernel_ms[k])
     achieved = kern[dom]["GB/s"]
     traffic = measured_traffic(cfg.name, dom)
 
@@ -365,7 +375,7 @@ def main():
                      "traffic_GB/s": None if traffic is None else round(traffic / (per_kernel_ms[dom] * 1e6), 1)},
         "gpu_event_ms_per_step": round(gpu_ms, 4),
         "kernels": kern,
-        "path_bytes_per_step": int(sum(c[0] for c in cost.values())),
+        "path_bytes_per_step": int(sum(cost[k][0] for k in ran)),
     }
     if not args.no_cpu:
         base, parity = cpu_baseline(cfg, inp, y.float().cpu().numpy())

@@ -23,10 +23,11 @@
  *                     product of the "Kernel 2: fwd_pass_state" section)
  *   ssd_state_pass    the sequential pass over chunk checkpoints
  *                     (the chunk loop of the same section)
- *   (for bf16 io with headdim 64 the chunk states can instead be computed
- *   inside the state pass: one kernel, ssd_chunk_state_pass, with the
- *   structure of the blog's "Kernel 2", the per-chunk states never reaching
- *   memory; mamba2_ssd_fused_state_pass tells which path a call takes)
+ *   (for bf16 io, headdim 64, chunk 256 and many (batch, head) pairs the
+ *   chunk states are computed inside the state pass instead: one kernel,
+ *   ssd_chunk_state_pass, with the structure of the blog's "Kernel 2", the
+ *   per-chunk states never reaching memory; mamba2_ssd_fused_state_pass
+ *   tells which path a call takes)
  *   ssd_chunk_scan    the per-chunk outputs: decayed carried-state term,
  *                     masked decayed C.B^T product with dt*x, and D*x
  *                     (blog section "Kernel 3: compute_out")
@@ -180,8 +181,9 @@ int mamba2_ssd_fwd(const mamba2_ssd_dims* dims, int io_dtype,
  * ssd_state_pass, or if the sizes are invalid. The environment variable
  * MAMBA2_SSD_STATE_PATH (read on every call) overrides the choice: "unfused"
  * forces the two kernels, "fused" the one kernel wherever it supports the
- * shape (bf16, headdim 64, dstate 64/128/256, chunk 128/256). Both paths
- * give bit-identical results. Host only. */
+ * shape (bf16, headdim 64, dstate 64/128/256, chunk 256). The paths agree
+ * to fp32 rounding (the one kernel sums each chunk's two halves separately).
+ * Host only. */
 int mamba2_ssd_fused_state_pass(const mamba2_ssd_dims* dims, int io_dtype);
 
 /* mamba2_ssd_fwd that also records caller-created events on `stream`, so

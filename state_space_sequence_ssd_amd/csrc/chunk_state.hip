@@ -217,128 +217,176 @@ __global__ __launch_bounds__((StateCfg<T, P, N>::THREADS)) void ssd_chunk_state(
 template <int N, int Q>
 struct FusedCfg {
   static constexpr int P = 64, KSTEPS = Q / 16;
-  static constexpr int RING = 8;   // k-steps of loads in flight; divides KSTEPS for Q = 128, 256
-  static constexpr int NNG = N / 64;          // dstate groups (waves) per (batch, head)
-  static_assert(KSTEPS % RING == 0, "ring slots must repeat every chunk");
+  static constexpr int HALF = KSTEPS / 2;     // k-steps per wave per chunk
+  static constexpr int RING = 4;              // k-steps staged in LDS per wave
+  static constexpr int NNG = N / 64;          // dstate groups per (batch, head)
+  static_assert(KSTEPS == 16, "a wave stores its 16 hprev state rows over its 8 k-steps of a chunk");
 };
 
+// Direct global->LDS load of 16 bytes per lane from a wave-uniform base plus a
+// per-lane offset; lane i's bytes land at lds + 16 i (lds wave-uniform, in M0).
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
+// A workgroup of two waves per (batch, head, 64-column dstate group). Wave kh
+// takes k-steps 8 kh .. 8 kh + 7 of every chunk (16 tokens each), so the
+// chunk's product S_k is the sum of the two waves' partial sums. After a
+// chunk, wave kh hands the other wave its partial sum of the state rows of
+// parity 1 - kh through LDS and adds the other's partial of parity kh: each
+// wave then holds S_k, and owns the state h, for the rows of its own parity
+// (p = 2 drow(r, g) + kh), which it updates and stores to hprev. Each
+// wave's 16-row steps of x (all 64 headdim columns) and B (the group's 64
+// columns) go to its own RING LDS slots by four 1-KB direct loads, RING-1
+// steps ahead, and each chunk's 256 weights w by one more. Within a slot, row
+// r sits at row slot r ^ ((r >> 3) & 1), so the two half-waves of a dword
+// read (rows 8g + i) hit different halves of the bank space. A wave stores
+// its hprev pairs 4 dwords per k-step; so before step t is read, the
+// operations issued after its loads number at least 4 + 8 (RING - 1) = 28.
 template <int N, int Q>
-__global__ __launch_bounds__(64) void ssd_chunk_state_pass(
+__global__ __launch_bounds__(128) void ssd_chunk_state_pass(
     const bf16* __restrict__ x, const bf16* __restrict__ Bm, const float* __restrict__ wst,
     const float* __restrict__ gcum, const float* init, void* __restrict__ hprev, float* final_state,
-    int64_t Tlen, int H, int G, int64_t nc, int64_t Tp) {
+    int64_t Tlen, int H, int G, int64_t nc, int64_t Tp, int xcd) {
   using I = Io<bf16>;
   using Fc = FusedCfg<N, Q>;
-  constexpr int P = 64, KPL = 8, KSTEPS = Fc::KSTEPS, RING = Fc::RING, NNG = Fc::NNG;
-  const int lane = threadIdx.x, m = lane % 32, g = lane / 32;
+  constexpr int P = 64, KPL = 8, HALF = Fc::HALF, RING = Fc::RING, NNG = Fc::NNG;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[2][RING][4096];   // per wave: x rows, then B rows
+  __shared__ __attribute__((aligned(1024))) float wbuf[2][2][Q];                 // per wave, by chunk parity
+  __shared__ __attribute__((aligned(1024))) float4 xch[2][8][64];                // partial sums handed over
+
+  const int kh = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int lane = threadIdx.x % 64, m = lane % 32, g = lane / 32;
+  // workgroup -> (batch*head, dstate group). With xcd set (batch*heads a
+  // multiple of 8), the groups of one head are 8 workgroups apart: the
+  // dispatcher deals workgroups to the 8 XCDs in turn, so they run on the
+  // same XCD at about the same time and the second read of the head's x
+  // rows hits that XCD's L2.
   const int64_t wid = blockIdx.x;
-  const int ng = (int)(wid % NNG);
-  const int64_t bh = wid / NNG;
+  int ng;
+  int64_t bh;
+  if (xcd) {
+    ng = (int)((wid / 8) % NNG);
+    bh = (wid / (8 * NNG)) * 8 + wid % 8;
+  } else {
+    ng = (int)(wid % NNG);
+    bh = wid / NNG;
+  }
   const int h = (int)(bh % H);
   const int64_t b = bh / H;
   const int grp = h / (H / G);
   const uint32_t xsb = (uint32_t)H * P * 2, bsb = (uint32_t)G * N * 2;
-  const int64_t nfull = Tlen / Q;   // chunks entirely inside the sequence
-  const uint32_t xlane = m * 4 + KPL * g * xsb, blane = m * 4 + KPL * g * bsb;
+  const int64_t nsteps = nc * HALF;   // this wave's k-steps over the walk
+  // per-lane load offsets within a step: instruction q (rows 8q..8q+7 of the
+  // step) puts lane l at row slot 8q + l/8, which holds row 8q + ((l/8) ^ q)
+  const int rq0 = (lane >> 3), rq1 = 8 + ((lane >> 3) ^ 1);
+  const uint32_t piece = (uint32_t)(lane & 7) * 16;
+  // LDS read offsets: row 8g + i of a step sits at slot 8g + (i ^ g), i.e.
+  // +1 slot for even i and -1 for odd i in the upper half-wave
+  const int rde = (8 * g + g) * 128 + 4 * m, rdo = (8 * g - g) * 128 + 4 * m;
 
-  // resources of chunk k: x (this head, all 64 headdim columns), B (this
-  // group, the wave's 64 dstate columns), both over the chunk's valid rows
-  auto rsrc_x = [&](int64_t k) {
+  // issue the loads of this wave's k-step t (chunk t / HALF, chunk step
+  // 8 kh + t % HALF) into its slot, and at its first step of a chunk the
+  // chunk's weights
+  auto issue = [&](int64_t t) {
+    const int64_t k = t / HALF;
+    const int s = (int)(t - k * HALF) + HALF * kh;
     const int64_t t0 = k * Q;
     const int nv = (int)(Tlen - t0 < Q ? Tlen - t0 : Q);
-    return make_rsrc(x + ((b * Tlen + t0) * H + h) * P, (uint32_t)(nv - 1) * xsb + 128);
-  };
-  auto rsrc_b = [&](int64_t k) {
-    const int64_t t0 = k * Q;
-    const int nv = (int)(Tlen - t0 < Q ? Tlen - t0 : Q);
-    return make_rsrc(Bm + ((b * Tlen + t0) * G + grp) * N + ng * 64, (uint32_t)(nv - 1) * bsb + 128);
-  };
-  const float* wrow = wst + bh * Tp;   // chunk k's weights at wrow + k*Q (the workspace covers padding)
-  auto load = [&](Step<bf16, 1>& st, int64_t k, int s, __amdgpu_buffer_rsrc_t rx, __amdgpu_buffer_rsrc_t rb) {
-    if (k < nfull)
-      load_step<bf16, 1, true>(st, s, rx, rb, wrow + k * Q, xlane, blane, xsb, bsb, g);
-    else
-      load_step<bf16, 1, false>(st, s, rx, rb, wrow + k * Q, xlane, blane, xsb, bsb, g);
+    const unsigned char* xs = reinterpret_cast<const unsigned char*>(x + ((b * Tlen + t0) * H + h) * P);
+    const unsigned char* bs = reinterpret_cast<const unsigned char*>(Bm + ((b * Tlen + t0) * G + grp) * N + ng * 64);
+    unsigned char* slot = ring[kh][t % RING];
+    if (s == HALF * kh) dma16(wst + bh * Tp + t0, (uint32_t)lane * 16, wbuf[kh][k & 1]);
+    const int r0 = s * 16;
+    if (r0 + 16 <= nv) {
+      dma16(xs + (uint32_t)r0 * xsb, (uint32_t)rq0 * xsb + piece, slot);
+      dma16(xs + (uint32_t)r0 * xsb, (uint32_t)rq1 * xsb + piece, slot + 1024);
+      dma16(bs + (uint32_t)r0 * bsb, (uint32_t)rq0 * bsb + piece, slot + 2048);
+      dma16(bs + (uint32_t)r0 * bsb, (uint32_t)rq1 * bsb + piece, slot + 3072);
+    } else {
+      // rows past the sequence: the last row again (finite; its weight is 0)
+      const uint32_t a0 = (uint32_t)min(r0 + rq0, nv - 1), a1 = (uint32_t)min(r0 + rq1, nv - 1);
+      dma16(xs, a0 * xsb + piece, slot);
+      dma16(xs, a1 * xsb + piece, slot + 1024);
+      dma16(bs, a0 * bsb + piece, slot + 2048);
+      dma16(bs, a1 * bsb + piece, slot + 3072);
+    }
   };
 
-  // h[pe][ne][r]: p = 2 drow(r, g) + pe, n = 64 ng + 2m + ne
-  f32x16 hs[2][2];
+  // this wave's state rows: hs[ne][r], p = 2 drow(r, g) + kh, n = 64 ng + 2m + ne
+  f32x16 hs[2];
   if (init) {
     const float* ip = init + bh * (int64_t)(P * N) + ng * 64 + 2 * m;
 #pragma unroll
-    for (int pe = 0; pe < 2; ++pe)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float2 v = *reinterpret_cast<const float2*>(ip + (2 * drow(r, g) + pe) * N);
-        hs[pe][0][r] = v.x;
-        hs[pe][1][r] = v.y;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float2 v = *reinterpret_cast<const float2*>(ip + (2 * drow(r, g) + kh) * N);
+      hs[0][r] = v.x;
+      hs[1][r] = v.y;
+    }
   } else {
-#pragma unroll
-    for (int pe = 0; pe < 2; ++pe)
-#pragma unroll
-      for (int ne = 0; ne < 2; ++ne) hs[pe][ne] = f32x16{};
+    hs[0] = f32x16{};
+    hs[1] = f32x16{};
   }
-
   // hprev pair stores: row p of chunk k at (b,h,k) block + p * 4N bytes; the
   // lane's two columns n, n+1 sit in group n/8 at position n%8: its hi
   // dword at (n/8)*32 + (n%8)*2 bytes, its lo dword 16 bytes further
-  const uint32_t hlane = (uint32_t)(8 * g) * (4 * N) + (uint32_t)((ng * 8 + m / 4) * 32 + (m % 4) * 4);
+  const uint32_t hlane = (uint32_t)(8 * g + kh) * (4 * N) + (uint32_t)((ng * 8 + m / 4) * 32 + (m % 4) * 4);
   unsigned char* hbase = static_cast<unsigned char*>(hprev) + bh * nc * (int64_t)(P * N) * 4;
 
-  Step<bf16, 1> ring[RING];
-  __amdgpu_buffer_rsrc_t rx = rsrc_x(0), rb = rsrc_b(0);
-  __amdgpu_buffer_rsrc_t rxn = rx, rbn = rb;
-  if (nc > 1) {
-    rxn = rsrc_x(1);
-    rbn = rsrc_b(1);
-  }
-#pragma unroll
-  for (int s = 0; s < RING - 1; ++s) load(ring[s], 0, s, rx, rb);
+  for (int64_t t = 0; t < RING - 1 && t < nsteps; ++t) issue(t);
+  if (init) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // h is complete before the first split
 
   for (int64_t k = 0; k < nc; ++k) {
-    // hprev[k] = h
-    {
-      const __amdgpu_buffer_rsrc_t rh = make_rsrc(hbase + k * (int64_t)(P * N) * 4, (uint32_t)(P * N * 4));
-#pragma unroll
-      for (int pe = 0; pe < 2; ++pe)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t d = pack_bf16x2(hs[pe][0][r], hs[pe][1][r]);
-          const uint32_t lo = pack_bf16x2(hs[pe][0][r] - bf16lo(d), hs[pe][1][r] - bf16hi(d));
-          const uint32_t row = (uint32_t)(16 * (r / 4) + 2 * (r % 4) + pe) * (4 * N);   // + 8g rows in hlane
-          __builtin_amdgcn_raw_buffer_store_b32(d, rh, hlane, row, 0);
-          __builtin_amdgcn_raw_buffer_store_b32(lo, rh, hlane + 16, row, 0);
-        }
-    }
-    // S_k over the chunk's k-steps; the loads run RING-1 steps ahead, into
-    // the next chunk near the end
     f32x16 acc[2][2];
 #pragma unroll
     for (int pe = 0; pe < 2; ++pe)
 #pragma unroll
       for (int ne = 0; ne < 2; ++ne) acc[pe][ne] = f32x16{};
-    // (a runtime loop over groups of RING steps, unrolled within: the ring
-    // slot of every step stays static without unrolling the whole chunk)
-    for (int s0 = 0; s0 < KSTEPS; s0 += RING) {
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(hbase + k * (int64_t)(P * N) * 4, (uint32_t)(P * N * 4));
+    const float* wk = wbuf[kh][k & 1] + HALF * kh * 16;
 #pragma unroll
-    for (int si = 0; si < RING; ++si) {
-      const int s = s0 + si;
-      const int sa = s + RING - 1;
-      if (sa < KSTEPS) load(ring[(si + RING - 1) % RING], k, sa, rx, rb);
-      else if (k + 1 < nc) load(ring[(si + RING - 1) % RING], k + 1, sa - KSTEPS, rxn, rbn);
-      const Step<bf16, 1>& cur = ring[si];
+    for (int si = 0; si < HALF; ++si) {
+      const int64_t t = k * HALF + si;
+      // the slot refilled below was read one step ago
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (t + RING - 1 < nsteps) issue(t + RING - 1);
+      // hprev[k] = h: this wave's state rows r = 2 si, 2 si + 1
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        const int r = 2 * si + e2;
+        const uint32_t d = pack_bf16x2(hs[0][r], hs[1][r]);
+        const uint32_t lo = pack_bf16x2(hs[0][r] - bf16lo(d), hs[1][r] - bf16hi(d));
+        const uint32_t row = (uint32_t)(16 * (r / 4) + 2 * (r % 4)) * (4 * N);   // + (8g + kh) rows in hlane
+        __builtin_amdgcn_raw_buffer_store_b32(d, rh, hlane, row, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(lo, rh, hlane + 16, row, 0);
+      }
+      // step t has landed once the operations issued after it are outstanding at most
+      if (t + RING - 1 >= nsteps) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      else if (t < RING - 1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(28)" ::: "memory");
+      const unsigned char* sb = ring[kh][t % RING];
+      uint32_t xd[KPL], bd[KPL];
+#pragma unroll
+      for (int i = 0; i < KPL; ++i) {
+        xd[i] = *reinterpret_cast<const uint32_t*>(sb + i * 128 + ((i & 1) ? rdo : rde));
+        bd[i] = *reinterpret_cast<const uint32_t*>(sb + 2048 + i * 128 + ((i & 1) ? rdo : rde));
+      }
+      const float4 w0 = *reinterpret_cast<const float4*>(wk + si * 16 + 8 * g);
+      const float4 w1 = *reinterpret_cast<const float4*>(wk + si * 16 + 8 * g + 4);
+      const float wv[KPL] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
       typename I::Frag ahi[2], alo[2];
 #pragma unroll
       for (int pe = 0; pe < 2; ++pe) {
         float v[KPL];
 #pragma unroll
-        for (int i = 0; i < KPL; ++i) v[i] = cur.w[i] * I::elem(cur.xd[i], pe);
+        for (int i = 0; i < KPL; ++i) v[i] = wv[i] * I::elem(xd[i], pe);
         I::split(v, ahi[pe], alo[pe]);
       }
 #pragma unroll
       for (int ne = 0; ne < 2; ++ne) {
-        const typename I::Frag bf = I::from_dwords(cur.bd[0], ne);
+        const typename I::Frag bf = I::from_dwords(bd, ne);
 #pragma unroll
         for (int pe = 0; pe < 2; ++pe) {
           I::mma(acc[pe][ne], ahi[pe], bf);
@@ -346,38 +394,61 @@ __global__ __launch_bounds__(64) void ssd_chunk_state_pass(
         }
       }
     }
+    // hand over the partial sum of the other wave's rows, take ours
+    // (fixed-index branches: a selected register index would go to scratch)
+    float4* mine = xch[kh][0] + lane;
+    const float4* theirs = xch[kh ^ 1][0] + lane;
+    f32x16 part[2];
+    if (kh == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ne = i / 4, r0 = (i % 4) * 4;
+        mine[i * 64] = make_float4(acc[1][ne][r0], acc[1][ne][r0 + 1], acc[1][ne][r0 + 2], acc[1][ne][r0 + 3]);
+      }
+      part[0] = acc[0][0];
+      part[1] = acc[0][1];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ne = i / 4, r0 = (i % 4) * 4;
+        mine[i * 64] = make_float4(acc[0][ne][r0], acc[0][ne][r0 + 1], acc[0][ne][r0 + 2], acc[0][ne][r0 + 3]);
+      }
+      part[0] = acc[1][0];
+      part[1] = acc[1][1];
     }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ne = i / 4, r0 = (i % 4) * 4;
+      const float4 o = theirs[i * 64];
+      part[ne][r0] += o.x;
+      part[ne][r0 + 1] += o.y;
+      part[ne][r0 + 2] += o.z;
+      part[ne][r0 + 3] += o.w;
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // read before the next hand-over
     // h = 2^(G'_last,k) h + S_k
     const float sc = exp2_hw(gcum[bh * Tp + k * Q + (Q - 1)]);
 #pragma unroll
-    for (int pe = 0; pe < 2; ++pe)
+    for (int ne = 0; ne < 2; ++ne)
 #pragma unroll
-      for (int ne = 0; ne < 2; ++ne)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) hs[pe][ne][r] = fmaf(sc, hs[pe][ne][r], acc[pe][ne][r]);
-    rx = rxn;
-    rb = rbn;
-    if (k + 2 < nc) {
-      rxn = rsrc_x(k + 2);
-      rbn = rsrc_b(k + 2);
-    }
+      for (int r = 0; r < 16; ++r) hs[ne][r] = fmaf(sc, hs[ne][r], part[ne][r]);
   }
   if (final_state) {
     float* fp = final_state + bh * (int64_t)(P * N) + ng * 64 + 2 * m;
 #pragma unroll
-    for (int pe = 0; pe < 2; ++pe)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        *reinterpret_cast<float2*>(fp + (2 * drow(r, g) + pe) * N) = make_float2(hs[pe][0][r], hs[pe][1][r]);
+    for (int r = 0; r < 16; ++r)
+      *reinterpret_cast<float2*>(fp + (2 * drow(r, g) + kh) * N) = make_float2(hs[0][r], hs[1][r]);
   }
 }
 
 template <int N, int Q>
 hipError_t launch_fused(const Problem& p, hipStream_t stream) {
-  const int64_t waves = p.bt * p.H * FusedCfg<N, Q>::NNG;
-  hipLaunchKernelGGL((ssd_chunk_state_pass<N, Q>), dim3((unsigned)waves), dim3(64), 0, stream, (const bf16*)p.x,
+  const int64_t groups = p.bt * p.H * FusedCfg<N, Q>::NNG;
+  const int xcd = (p.bt * p.H) % 8 == 0 ? 1 : 0;
+  hipLaunchKernelGGL((ssd_chunk_state_pass<N, Q>), dim3((unsigned)groups), dim3(128), 0, stream, (const bf16*)p.x,
                      (const bf16*)p.B, p.wst, p.gcum, p.init, p.hprev, p.final_state, p.T, (int)p.H, (int)p.G,
-                     p.nc, p.Tp);
+                     p.nc, p.Tp, xcd);
   return hipGetLastError();
 }
 
@@ -413,24 +484,23 @@ hipError_t launch_chunk_state(const Problem& p, hipStream_t stream) {
 }
 
 bool chunk_state_pass_fits(const Problem& p) {
-  // bf16, headdim 64, dstate 64/128/256, chunk 128/256, at least one chunk
-  return p.io == 1 && p.P == 64 && (p.Q == 128 || p.Q == 256) && (p.N == 64 || p.N == 128 || p.N == 256) &&
-         p.nc > 0;
+  // bf16, headdim 64, dstate 64/128/256, chunk 256, at least one chunk
+  return p.io == 1 && p.P == 64 && p.Q == 256 && (p.N == 64 || p.N == 128 || p.N == 256) && p.nc > 0;
 }
 
-bool chunk_state_pass_pays(const Problem&) {
-  // Measured on MI355X, this form loses on every configuration tried: each
-  // wave walks its head's chunks in sequence and its dword loads keep only
-  // about 16 KB in flight, so a chunk costs ~10-12 us (2.7B-like layer:
-  // 392 us against 310 us for ssd_chunk_state + ssd_state_pass). It runs
-  // only when MAMBA2_SSD_STATE_PATH=fused asks for it.
-  return false;
+bool chunk_state_pass_pays(const Problem& p) {
+  // Each (batch, head, dstate group) walks its head's chunks in sequence, so
+  // the one-kernel form wins only when those pairs alone fill the GPU.
+  // Measured on MI355X: 2.7B-like layer (640 pairs) 288 us against 310 us
+  // for ssd_chunk_state + ssd_state_pass; 130M-like (384 pairs) 59 against
+  // 50 us; a 80-pair long prefill is several times slower.
+  return p.bt * p.H * (p.N / 64) >= 512;
 }
 
 hipError_t launch_chunk_state_pass(const Problem& p, hipStream_t stream) {
 #define SSD_CASE(NN, QQ) \
   if (p.N == NN && p.Q == QQ) return launch_fused<NN, QQ>(p, stream);
-  SSD_CASE(64, 128) SSD_CASE(64, 256) SSD_CASE(128, 128) SSD_CASE(128, 256) SSD_CASE(256, 128) SSD_CASE(256, 256)
+  SSD_CASE(64, 256) SSD_CASE(128, 256) SSD_CASE(256, 256)
 #undef SSD_CASE
   return hipErrorInvalidValue;
 }

@@ -101,7 +101,7 @@ void layout_of(const mamba2_ssd_dims* d, const Sizes& s, mamba2_ssd_workspace_la
 // (one kernel, see chunk_state.hip). MAMBA2_SSD_STATE_PATH in the environment
 // (read per call) overrides the size rule: "unfused" forces the two-kernel
 // path, "fused" takes the one-kernel path for every shape it supports. A
-// diagnostic switch; both paths give bit-identical results.
+// diagnostic switch; the paths agree to fp32 rounding.
 bool use_fused_state(const ssd::Problem& p) {
   const char* e = std::getenv("MAMBA2_SSD_STATE_PATH");
   if (e && std::strcmp(e, "unfused") == 0) return false;

@@ -278,8 +278,9 @@ def test_step_empty_and_errors_without_launching():
 
 
 def test_fused_state_pass_query(monkeypatch):
-    # by default the two-kernel path runs (the one-kernel form does not pay)
-    assert not ssd.fused_state_pass(HEADLINE, BF16)
+    # the 2.7B-like layer: bf16, headdim 64, 4 x 80 heads x 2 dstate groups
+    assert ssd.fused_state_pass(HEADLINE, BF16)
+    assert not ssd.fused_state_pass(Dims(8, 2048, 24, 64, 128, 1, 256), BF16)    # 384 pairs: two kernels
     assert not ssd.fused_state_pass(HEADLINE, F32)                      # fp32 io: two kernels
     assert not ssd.fused_state_pass(Dims(1, 65536, 80, 64, 128, 1, 256), BF16)   # too few (b, h) pairs
     assert not ssd.fused_state_pass(Dims(4, 8192, 80, 128, 128, 1, 256), BF16)   # headdim 128
@@ -289,6 +290,6 @@ def test_fused_state_pass_query(monkeypatch):
     assert not ssd.fused_state_pass(HEADLINE, BF16)
     monkeypatch.setenv("MAMBA2_SSD_STATE_PATH", "fused")
     assert ssd.fused_state_pass(Dims(1, 65536, 80, 64, 128, 1, 256), BF16)
-    assert ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 128), BF16)
-    assert not ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 64), BF16)        # chunk 64: not supported
+    assert ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 256), BF16)
+    assert not ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 128), BF16)       # chunk 128: not supported
     assert not ssd.fused_state_pass(HEADLINE, F32)

@@ -269,21 +269,18 @@ def test_resident_scan_walks(name):
 
 
 # ------------------------------------ chunk states computed inside the state pass
-# (bf16, headdim 64: the one-kernel path). MAMBA2_SSD_STATE_PATH forces either
-# path regardless of size; both must match the oracle, and each other bit for
-# bit (the same products in the same order, the same fp32 update).
+# (bf16, headdim 64, chunk 256: the one-kernel path). MAMBA2_SSD_STATE_PATH
+# forces either path regardless of size; both must match the oracle, and each
+# other up to fp32 rounding (the one-kernel form sums a chunk's two halves
+# separately, then adds them).
 FUSED = {
     "2.7b-ragged": dict(batch=2, seqlen=3 * 256 + 13, nheads=5),
     "one-chunk": dict(batch=3, seqlen=100, nheads=2),
-    "N64-Q128": dict(batch=1, seqlen=5 * 128 + 1, nheads=4, dstate=64, chunk=128),
+    "N64": dict(batch=1, seqlen=5 * 256 + 1, nheads=4, dstate=64),
     "N256-groups": dict(batch=1, seqlen=600, nheads=8, dstate=256, ngroups=2),
-    "Q128-exact": dict(batch=2, seqlen=4 * 128, nheads=3, chunk=128),
+    "exact-chunks": dict(batch=2, seqlen=4 * 256, nheads=3),
+    "long-walk": dict(batch=1, seqlen=20 * 256 + 77, nheads=2),
 }
-
-
-def _hprev_bytes(ws, L, dims):
-    n = dims.batch * dims.nheads * L.nchunks * dims.headdim * dims.dstate * 4
-    return ws[L.hprev_offset:L.hprev_offset + n].clone()
 
 
 @pytest.mark.parametrize("name", sorted(FUSED))
@@ -304,9 +301,13 @@ def test_fused_state_pass(name, monkeypatch):
     monkeypatch.setenv("MAMBA2_SSD_STATE_PATH", "unfused")
     y2, f2, ws2, _, _ = run(dev, cfg.chunk, keep_workspace=True)
     assert not ssd.fused_state_pass(dims, 1)
-    assert torch.equal(_hprev_bytes(ws1, L, dims), _hprev_bytes(ws2, L, dims)), "hprev differs between paths"
-    assert torch.equal(f1, f2), "final_state differs between paths"
-    assert torch.equal(y1, y2), "y differs between paths"
+    v2 = workspace_views(ws2, L, dims, 1)
+    for what, a1, a2 in (("hprev", v["hprev"], v2["hprev"]), ("final_state", f1, f2)):
+        a1, a2 = host(a1), host(a2)
+        rel = float(np.max(np.abs(a1 - a2))) / max(float(np.max(np.abs(a2))), 1e-30)
+        assert rel <= 1e-5, f"{what}: paths differ by {rel:.2e} (normwise)"
+    yy1, yy2 = host(y1), host(y2)
+    assert np.all(np.abs(yy1 - yy2) <= 2.0 ** -7 * np.abs(yy2) + 1e-6), "y: paths differ by more than 1 bf16 ulp"
 
 
 def test_fused_state_pass_in_place_and_no_final(monkeypatch):
