@@ -150,6 +150,21 @@ __device__ __forceinline__ RTile make_rtile(int64_t b, int64_t k, int64_t bk, in
   return t;
 }
 
+// The intra-chunk pairs of wave W, in emission order e = 0..11 (slot sl,
+// t-block choice u): which emissions the wave keeps, the j-block of an
+// emission, and the wave's next kept emission after e (-1: none).
+__host__ __device__ constexpr bool pair_kept(int e, int W) {
+  return !((e >= 4 && e < 7 && e - 3 <= W) || (e >= 1 && e < 4 && e > W));
+}
+__host__ __device__ constexpr int pair_jb(int e) { return e < 4 ? e : 8 - (e - 3); }
+__host__ __device__ constexpr bool pair_diag(int e, int W) { return pair_jb(e) == (e < 4 ? W : 7 - W); }
+__host__ __device__ constexpr int next_pair(int e, int W) {
+  for (int f = e + 1; f < 12; ++f)
+    if (pair_kept(f, W)) return f;
+  return -1;
+}
+static_assert(pair_kept(0, 0) && pair_kept(0, 3) && pair_jb(0) == 0, "every wave starts at j-block 0");
+
 template <int N>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict__ Bm, const bf16* __restrict__ Cm,
@@ -164,6 +179,7 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
 
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2][Cf::BUF];
   __shared__ __attribute__((aligned(16))) float sW[Q];   // dt_j * 2^(G'_end(block of j) - G'_j) <= dt_j
+  __shared__ __attribute__((aligned(16))) float sE[Q];   // 2^(G'_t) <= 1
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -337,6 +353,7 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
     {
       const float gi = sG[tid];
       sW[tid] = sDt[tid] * exp2_hw(sG[tid | 31] - gi);   // exponent <= 0
+      sE[tid] = exp2_hw(gi);
     }
     const float gt0 = sG[tb0 * 32 + m], gt1 = sG[tb1 * 32 + m];
     lds_barrier();
@@ -368,26 +385,39 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int pe = 0; pe < 2; ++pe) acc[u][pe] = f32x16{};
-#pragma unroll
-    for (int pe = 0; pe < 2; ++pe) {
+    // Hprev fragments in blocks of 4 k-steps, each block read while the
+    // previous one's MFMAs run
+    constexpr int HB = KS / 4;   // blocks per column half
+    Frag hf[2][2][4];            // [buffer][hi, lo][k-step in block]
+    auto load_h = [&](int blk, Frag (*dst)[4]) {
+      const int pe = blk / HB, s0 = (blk % HB) * 4;
       const unsigned char* hp = cur + Cf::HOFF + (pe * 32 + m) * Cf::HRB;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        if (s % 4 == 0) __builtin_amdgcn_sched_barrier(0);   // bounds the Hprev fragments in flight
-        const Frag hhi = *reinterpret_cast<const Frag*>(hp + (2 * s + g) * 32);
-        const Frag hlo = *reinterpret_cast<const Frag*>(hp + (2 * s + g) * 32 + 16);
+      for (int i = 0; i < 4; ++i) {
+        dst[0][i] = *reinterpret_cast<const Frag*>(hp + (2 * (s0 + i) + g) * 32);
+        dst[1][i] = *reinterpret_cast<const Frag*>(hp + (2 * (s0 + i) + g) * 32 + 16);
+      }
+    };
+    load_h(0, hf[0]);
+#pragma unroll
+    for (int blk = 0; blk < 2 * HB; ++blk) {
+      if (blk + 1 < 2 * HB) load_h(blk + 1, hf[(blk + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int pe = blk / HB, s0 = (blk % HB) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          I::mma(acc[u][pe], cf[u][s], hhi);
-          I::mma(acc[u][pe], cf[u][s], hlo);
+          I::mma(acc[u][pe], cf[u][s0 + i], hf[blk & 1][0][i]);
+          I::mma(acc[u][pe], cf[u][s0 + i], hf[blk & 1][1][i]);
         }
-      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float sc = exp2_hw(sG[(u ? tb1 : tb0) * 32 + drow(r, g)]);
+        const float sc = sE[(u ? tb1 : tb0) * 32 + drow(r, g)];
         acc[u][0][r] *= sc;
         acc[u][1][r] *= sc;
       }
@@ -396,24 +426,44 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
     const unsigned char* xt = cur;
     auto pairs = [&](auto wtag) {
       constexpr int W = decltype(wtag)::value;
+      // x dwords of rows drow(q, g) of j-block jb (columns 2m, 2m+1)
+      auto load_x = [&](int jb, uint32_t* d) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int off = jb * 32 * 128 + 128 * (8 * (q / 4) + q % 4);
+          d[q] = *reinterpret_cast<const uint32_t*>(xt + off + ((q & 1) ? xbo : xbe));
+        }
+      };
+      // each pair's x rows are read one pair ahead, so their LDS latency
+      // hides behind the previous pair's work
+      // an off-diagonal pair's weights w_j and G'_end of its j-block, also
+      // read one pair ahead
+      auto load_w = [&](int jb, float4* wv, float& ge) {
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) wv[c4] = *reinterpret_cast<const float4*>(&sW[jb * 32 + 8 * c4 + 4 * g]);
+        ge = sG[jb * 32 + 31];
+      };
+      uint32_t d[16];
+      float4 wv[4];
+      float ge = 0.f;
+      load_x(0, d);   // the first pair of every wave is (t-block W, j-block 0)
+      if (!pair_diag(0, W)) load_w(0, wv, ge);
 #pragma unroll
     for (int e = 0; e < 12; ++e) {
       const int sl = e < 4 ? e : e - 3;       // the same emission order as the C.B^T phase
       const int u = e < 4 ? 0 : 1;
-      if (e >= 4 && e < 7 && sl <= W) continue;
-      if (e >= 1 && e < 4 && sl > W) continue;
+      if (!pair_kept(e, W)) continue;
       const int jb = u ? 8 - sl : sl;
       const int tb = u ? 7 - W : W;
       const bool diag = jb == tb;
       const float gtu = u ? gt1 : gt0;
       const int j0 = jb * 32;
-      // x dwords of rows drow(q, g) of the block (columns 2m, 2m+1)
-      uint32_t d[16];
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int off = j0 * 128 + 128 * (8 * (q / 4) + q % 4);
-        d[q] = *reinterpret_cast<const uint32_t*>(xt + off + ((q & 1) ? xbo : xbe));
-      }
+      uint32_t dn[16];
+      float4 wvn[4];
+      float gen = 0.f;
+      const int en = next_pair(e, W);
+      if (en >= 0) load_x(pair_jb(en), dn);
+      if (en >= 0 && !pair_diag(en, W)) load_w(pair_jb(en), wvn, gen);
       Frag xf[2][2];   // [pe][js]
 #pragma unroll
       for (int js = 0; js < 2; ++js) {
@@ -430,22 +480,31 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
       float v[16];
       if (!diag) {
         // every t is past the whole j-block: 2^(G'_t - G'_j) = 2^(G'_t - G'_end) 2^(G'_end - G'_j)
-        const float a = exp2_hw(gtu - sG[j0 + 31]);
+        const float a = exp2_hw(gtu - ge);
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) {
-          const float4 wv = *reinterpret_cast<const float4*>(&sW[j0 + 8 * c4 + 4 * g]);
-          v[4 * c4 + 0] = from_agpr(cbc[sl][4 * c4 + 0]) * (wv.x * a);
-          v[4 * c4 + 1] = from_agpr(cbc[sl][4 * c4 + 1]) * (wv.y * a);
-          v[4 * c4 + 2] = from_agpr(cbc[sl][4 * c4 + 2]) * (wv.z * a);
-          v[4 * c4 + 3] = from_agpr(cbc[sl][4 * c4 + 3]) * (wv.w * a);
+          v[4 * c4 + 0] = from_agpr(cbc[sl][4 * c4 + 0]) * (wv[c4].x * a);
+          v[4 * c4 + 1] = from_agpr(cbc[sl][4 * c4 + 1]) * (wv[c4].y * a);
+          v[4 * c4 + 2] = from_agpr(cbc[sl][4 * c4 + 2]) * (wv[c4].z * a);
+          v[4 * c4 + 3] = from_agpr(cbc[sl][4 * c4 + 3]) * (wv[c4].w * a);
         }
       } else {
-        // diagonal block: direct decay; the causal mask is a select
+        // diagonal block: direct decay; the causal mask is a select. The
+        // skip term D x_t is the product of this block's diagonal with x,
+        // so D joins the diagonal entries here and rides in the same MFMAs
+        // (instead of a read-modify-write of the accumulators).
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int jr = drow(q, g);
-          const float val = from_agpr(cbc[sl][q]) * exp2_hw(gtu - sG[j0 + jr]) * sDt[j0 + jr];
-          v[q] = (m >= jr) ? val : 0.f;
+        for (int c4 = 0; c4 < 4; ++c4) {
+          // rows drow(4 c4 + i, g) = 8 c4 + 4 g + i: four consecutive G', dt
+          const float4 g4 = *reinterpret_cast<const float4*>(&sG[j0 + 8 * c4 + 4 * g]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&sDt[j0 + 8 * c4 + 4 * g]);
+          const float gq[4] = {g4.x, g4.y, g4.z, g4.w}, dq[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int q = 4 * c4 + i, jr = drow(q, g);
+            const float val = from_agpr(cbc[sl][q]) * exp2_hw(gtu - gq[i]) * dq[i];
+            v[q] = (m > jr) ? val : ((m == jr) ? val + t.Dh : 0.f);
+          }
         }
       }
       // (hi, lo) bf16 split of the decayed block, two MFMAs per x fragment
@@ -467,6 +526,13 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
           I::mma(acc[u][pe], alo, xf[pe][js]);
         }
       }
+#pragma unroll
+      for (int q = 0; q < 16; ++q) d[q] = dn[q];
+      if (en >= 0 && !pair_diag(en, W)) {
+#pragma unroll
+        for (int c4 = 0; c4 < 4; ++c4) wv[c4] = wvn[c4];
+        ge = gen;
+      }
     }
     };
     switch (wave) {
@@ -476,18 +542,6 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
       default: pairs(std::integral_constant<int, 3>{}); break;
     }
     __builtin_amdgcn_sched_barrier(0);
-    // D x on the rows of the wave's own t-blocks
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j0 = (u ? tb1 : tb0) * 32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t xd = *reinterpret_cast<const uint32_t*>(
-            xt + j0 * 128 + 128 * (8 * (r / 4) + r % 4) + ((r & 1) ? xbo : xbe));
-        acc[u][0][r] += t.Dh * bf16lo(xd);
-        acc[u][1][r] += t.Dh * bf16hi(xd);
-      }
-    }
 
     // y: one dword (columns 2m, 2m+1) per lane per row, through a buffer
     // resource over the tile's valid rows. Full tiles put the row in the
