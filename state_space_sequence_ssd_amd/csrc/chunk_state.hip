@@ -243,8 +243,9 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, const vo
 // steps ahead, and each chunk's 256 weights w by one more. Within a slot, row
 // r sits at row slot r ^ ((r >> 3) & 1), so the two half-waves of a dword
 // read (rows 8g + i) hit different halves of the bank space. A wave stores
-// its hprev pairs 4 dwords per k-step; so before step t is read, the
-// operations issued after its loads number at least 4 + 8 (RING - 1) = 28.
+// hprev with one 16-byte store per lane per k-step, issued after that step's
+// loads; so before step t is read, the operations issued after its loads
+// number at least 1 + 5 (RING - 1) = 16 (12 for the first RING - 1 steps).
 template <int N, int Q>
 __global__ __launch_bounds__(128) void ssd_chunk_state_pass(
     const bf16* __restrict__ x, const bf16* __restrict__ Bm, const float* __restrict__ wst,
@@ -329,11 +330,28 @@ __global__ __launch_bounds__(128) void ssd_chunk_state_pass(
     hs[0] = f32x16{};
     hs[1] = f32x16{};
   }
-  // hprev pair stores: row p of chunk k at (b,h,k) block + p * 4N bytes; the
-  // lane's two columns n, n+1 sit in group n/8 at position n%8: its hi
-  // dword at (n/8)*32 + (n%8)*2 bytes, its lo dword 16 bytes further
-  const uint32_t hlane = (uint32_t)(8 * g + kh) * (4 * N) + (uint32_t)((ng * 8 + m / 4) * 32 + (m % 4) * 4);
+  // hprev[k] goes out through LDS: after each state update the wave writes
+  // its 32 state rows (p = 2 j + kh, j = 0..31) as (hi, lo) pairs in the
+  // stored format into its half of xch (one 256-byte row per j: column n of
+  // the group at (n/8)*32 + (n%8)*2 bytes, lo 16 bytes after hi), and during
+  // the next chunk each k-step stores 4 of these rows with one 16-byte store
+  // per lane. In memory, row p of chunk k holds this group's columns in the
+  // 256 bytes at p * 4N + 256 ng.
+  unsigned char* stg = reinterpret_cast<unsigned char*>(xch[kh][0]);
+  const uint32_t sw_off = (uint32_t)(m / 4) * 32 + (uint32_t)(m % 4) * 4;
+  auto stage = [&]() {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t d = pack_bf16x2(hs[0][r], hs[1][r]);
+      const uint32_t lo = pack_bf16x2(hs[0][r] - bf16lo(d), hs[1][r] - bf16hi(d));
+      unsigned char* row = stg + drow(r, g) * 256 + sw_off;
+      *reinterpret_cast<uint32_t*>(row) = d;
+      *reinterpret_cast<uint32_t*>(row + 16) = lo;
+    }
+  };
+  const uint32_t st_row = (uint32_t)(lane >> 4), st_piece = (uint32_t)(lane & 15) * 16;
   unsigned char* hbase = static_cast<unsigned char*>(hprev) + bh * nc * (int64_t)(P * N) * 4;
+  stage();
 
   for (int64_t t = 0; t < RING - 1 && t < nsteps; ++t) issue(t);
   if (init) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // h is complete before the first split
@@ -352,20 +370,17 @@ __global__ __launch_bounds__(128) void ssd_chunk_state_pass(
       // the slot refilled below was read one step ago
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (t + RING - 1 < nsteps) issue(t + RING - 1);
-      // hprev[k] = h: this wave's state rows r = 2 si, 2 si + 1
-#pragma unroll
-      for (int e2 = 0; e2 < 2; ++e2) {
-        const int r = 2 * si + e2;
-        const uint32_t d = pack_bf16x2(hs[0][r], hs[1][r]);
-        const uint32_t lo = pack_bf16x2(hs[0][r] - bf16lo(d), hs[1][r] - bf16hi(d));
-        const uint32_t row = (uint32_t)(16 * (r / 4) + 2 * (r % 4)) * (4 * N);   // + (8g + kh) rows in hlane
-        __builtin_amdgcn_raw_buffer_store_b32(d, rh, hlane, row, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(lo, rh, hlane + 16, row, 0);
+      // hprev[k] = h: staged rows j = 4 si .. 4 si + 3, 16 bytes per lane,
+      // streamed (the next kernel reads them, long after they leave the caches)
+      {
+        const uint32_t j = (uint32_t)(4 * si) + st_row;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(stg + j * 256 + st_piece);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rh, (2 * j + kh) * (4 * N) + ng * 256 + st_piece, 0, 2);
       }
       // step t has landed once the operations issued after it are outstanding at most
       if (t + RING - 1 >= nsteps) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      else if (t < RING - 1) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(28)" ::: "memory");
+      else if (t < RING - 1) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
       const unsigned char* sb = ring[kh][t % RING];
       uint32_t xd[KPL], bd[KPL];
 #pragma unroll
@@ -433,6 +448,7 @@ __global__ __launch_bounds__(128) void ssd_chunk_state_pass(
     for (int ne = 0; ne < 2; ++ne)
 #pragma unroll
       for (int r = 0; r < 16; ++r) hs[ne][r] = fmaf(sc, hs[ne][r], part[ne][r]);
+    if (k + 1 < nc) stage();   // hprev[k + 1]; xch is free again after the second barrier
   }
   if (final_state) {
     float* fp = final_state + bh * (int64_t)(P * N) + ng * 64 + 2 * m;
