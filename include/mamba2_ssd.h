@@ -77,6 +77,17 @@ extern "C" {
 #define MAMBA2_SSD_F32  0   /* IEEE binary32                                    */
 #define MAMBA2_SSD_BF16 1   /* bfloat16 (upper half of a binary32)              */
 
+/* Layout flag, OR-ed into the io_dtype argument of the forward entry points
+ * (mamba2_ssd_supported, _workspace_layout_query, _fwd_workspace_bytes,
+ * _check_args, _fwd, _fwd_timed, _fused_state_pass): dt is given head-major,
+ * float [batch][nheads][seqlen], instead of token-major [batch][seqlen][nheads].
+ * This is the [batch, head, token] global-memory layout the blog's
+ * "Mamba-2 performance optimizations" section recommends for dt and the
+ * decay cumsum (contiguous per-head reads); results are identical in both
+ * layouts. Any other bit above the low byte gives MAMBA2_SSD_ERR_UNSUPPORTED.
+ * The decode step (mamba2_ssd_step) takes no flags: its dt is [batch][nheads]. */
+#define MAMBA2_SSD_DT_HEAD_MAJOR 0x100
+
 /* Problem sizes. batch and seqlen may be 0 (nothing to compute: with
  * seqlen == 0 final_state receives init_state, or zeros). seqlen need not be
  * a multiple of chunk: the last chunk is then ragged and behaves as if

@@ -11,10 +11,11 @@ from __future__ import annotations
 import ctypes
 from typing import Optional, Tuple
 
-from ._lib import (BF16, F32, STATUS, Dims, SsdError, StepDims, WorkspaceLayout, lib, status_string)
+from ._lib import (BF16, DT_HEAD_MAJOR, F32, STATUS, Dims, SsdError, StepDims, WorkspaceLayout, lib,
+                   status_string)
 
 __all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_layout", "check_args",
-           "Dims", "WorkspaceLayout", "SsdError", "F32", "BF16", "STATUS", "status_string",
+           "Dims", "WorkspaceLayout", "SsdError", "F32", "BF16", "DT_HEAD_MAJOR", "STATUS", "status_string",
            "ssd_fwd_timed_ptr", "mamba2_ssd_fwd", "mamba2_ssd_fwd_timed", "mamba2_ssd_check_args",
            "mamba2_ssd_supported",
            "mamba2_ssd_fwd_workspace_bytes", "mamba2_ssd_workspace_layout_query",
@@ -94,12 +95,14 @@ def ssd_fwd_timed_ptr(dims, io, x, dt, A, B, C, D, init_state, y, final_state, w
 
 
 def ssd_fwd(x, dt, A, B, C, D, chunk: int, init_state=None, *, return_final_state: bool = True,
-            y=None, final_state=None, workspace=None) -> Tuple[object, Optional[object]]:
+            y=None, final_state=None, workspace=None,
+            dt_head_major: bool = False) -> Tuple[object, Optional[object]]:
     """Forward pass on torch CUDA tensors (all contiguous, same device).
 
     x [batch, seqlen, nheads, headdim] and B, C [batch, seqlen, ngroups,
     dstate] share the io dtype (torch.bfloat16 or torch.float32); dt
-    [batch, seqlen, nheads], A and D [nheads] and init_state [batch, nheads,
+    [batch, seqlen, nheads] (or [batch, nheads, seqlen] with
+    ``dt_head_major``), A and D [nheads] and init_state [batch, nheads,
     headdim, dstate] are float32. Returns ``(y, final_state)``; final_state is
     None when ``return_final_state`` is False. ``y``, ``final_state`` and
     ``workspace`` (a uint8 tensor) may be passed to reuse memory; otherwise
@@ -127,12 +130,15 @@ def ssd_fwd(x, dt, A, B, C, D, chunk: int, init_state=None, *, return_final_stat
             raise ValueError("all tensors must be contiguous")
     bt, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    if tuple(dt.shape) != (bt, T, H) or tuple(B.shape) != (bt, T, G, N) or tuple(C.shape) != (bt, T, G, N) \
+    dt_shape = (bt, H, T) if dt_head_major else (bt, T, H)
+    if tuple(dt.shape) != dt_shape or tuple(B.shape) != (bt, T, G, N) or tuple(C.shape) != (bt, T, G, N) \
             or tuple(A.shape) != (H,) or tuple(D.shape) != (H,):
         raise ValueError("inconsistent shapes")
     if init_state is not None and tuple(init_state.shape) != (bt, H, P, N):
         raise ValueError("init_state must be [batch, nheads, headdim, dstate]")
     dims = Dims(bt, T, H, P, N, G, chunk)
+    if dt_head_major:
+        io |= DT_HEAD_MAJOR
     if y is None:
         y = torch.empty_like(x)
     if return_final_state and final_state is None:

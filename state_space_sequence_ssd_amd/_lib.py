@@ -8,6 +8,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmamba2_s
 
 F32 = 0
 BF16 = 1
+DT_HEAD_MAJOR = 0x100   # OR-ed into io: dt given as [batch, nheads, seqlen]
 
 STATUS = {
     0: "OK",

@@ -4,8 +4,9 @@
 // the sum restarts at every chunk and is stored pre-multiplied by log2 e).
 //
 // One workgroup per (block of 16 heads, chunk, batch row). The dt tile
-// [chunk tokens][16 heads] is read as whole 64-byte rows, scanned per head
-// through LDS, and written transposed, [batch][head][token], so the
+// [chunk tokens][16 heads] is read as whole 64-byte rows (or, for dt given
+// head-major, as each head's contiguous run of the chunk's tokens), scanned
+// per head through LDS, and written transposed, [batch][head][token], so the
 // consumers read each head's decays contiguously (the blog's "GMEM layout"
 // point, done here once for both consumers). Three arrays come out, all
 // head-major: dt itself, G' (the scaled cumsum) and the chunk-state weight
@@ -36,7 +37,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_cumsum(const float* __restrict_
                                                         float* __restrict__ gcum,
                                                         float* __restrict__ dtt,
                                                         float* __restrict__ wst,
-                                                        int64_t T, int H, int64_t Tp) {
+                                                        int64_t T, int H, int64_t Tp, int dt_hm) {
   constexpr int SL = Q / kSeg;
   __shared__ float s_t[Q][kHB + 1];   // dt tile, then the scaled cumsum in place
   __shared__ float s_w[Q][kHB + 1];   // state weights
@@ -50,24 +51,44 @@ __global__ __launch_bounds__(256) void ssd_chunk_cumsum(const float* __restrict_
   const int64_t t0 = (int64_t)k * Q;
   const int nh = H - h0 < kHB ? H - h0 : kHB;          // heads of this block
   const int nt = T - t0 < Q ? (int)(T - t0) : Q;       // tokens of this chunk
-  const float* src = dt + (b * T + t0) * H + h0;
-
-  // token-major tile, kHB heads per row (64 bytes); whole rows as 16-byte
-  // pieces when every row of the block is full and 16-byte aligned
-  if (nh == kHB && H % 4 == 0 && (reinterpret_cast<uintptr_t>(dt) & 15) == 0) {
-    for (int idx = tid; idx < Q * (kHB / 4); idx += 256) {
-      const int t = idx / (kHB / 4), c = idx % (kHB / 4);
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < nt) v = *reinterpret_cast<const float4*>(src + (int64_t)t * H + 4 * c);
-      s_t[t][4 * c] = v.x; s_t[t][4 * c + 1] = v.y; s_t[t][4 * c + 2] = v.z; s_t[t][4 * c + 3] = v.w;
+  if (dt_hm) {
+    // head-major dt: each head's tokens of the chunk are contiguous; 16-byte
+    // pieces when every head row is 16-byte aligned and the chunk is full
+    const float* srch = dt + (b * H + h0) * T + t0;
+    if (nt == Q && T % 4 == 0 && (reinterpret_cast<uintptr_t>(dt) & 15) == 0) {
+      for (int idx = tid; idx < kHB * (Q / 4); idx += 256) {
+        const int hh = idx / (Q / 4), t = 4 * (idx % (Q / 4));
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (hh < nh) v = *reinterpret_cast<const float4*>(srch + (int64_t)hh * T + t);
+        s_t[t][hh] = v.x; s_t[t + 1][hh] = v.y; s_t[t + 2][hh] = v.z; s_t[t + 3][hh] = v.w;
+      }
+    } else {
+      for (int idx = tid; idx < kHB * Q; idx += 256) {
+        const int hh = idx / Q, t = idx % Q;
+        s_t[t][hh] = (t < nt && hh < nh) ? srch[(int64_t)hh * T + t] : 0.f;
+      }
     }
+    __syncthreads();
   } else {
-    for (int idx = tid; idx < Q * kHB; idx += 256) {
-      const int t = idx / kHB, hh = idx % kHB;
-      s_t[t][hh] = (t < nt && hh < nh) ? src[(int64_t)t * H + hh] : 0.f;
+    const float* src = dt + (b * T + t0) * H + h0;
+
+    // token-major tile, kHB heads per row (64 bytes); whole rows as 16-byte
+    // pieces when every row of the block is full and 16-byte aligned
+    if (nh == kHB && H % 4 == 0 && (reinterpret_cast<uintptr_t>(dt) & 15) == 0) {
+      for (int idx = tid; idx < Q * (kHB / 4); idx += 256) {
+        const int t = idx / (kHB / 4), c = idx % (kHB / 4);
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (t < nt) v = *reinterpret_cast<const float4*>(src + (int64_t)t * H + 4 * c);
+        s_t[t][4 * c] = v.x; s_t[t][4 * c + 1] = v.y; s_t[t][4 * c + 2] = v.z; s_t[t][4 * c + 3] = v.w;
+      }
+    } else {
+      for (int idx = tid; idx < Q * kHB; idx += 256) {
+        const int t = idx / kHB, hh = idx % kHB;
+        s_t[t][hh] = (t < nt && hh < nh) ? src[(int64_t)t * H + hh] : 0.f;
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   // dt, head-major: each thread writes 4 consecutive tokens of one head
   for (int idx = tid; idx < (Q / 4) * kHB; idx += 256) {
@@ -129,13 +150,13 @@ hipError_t launch_chunk_cumsum(const Problem& p, hipStream_t stream) {
   const dim3 block(256);
   switch (p.Q) {
     case 64:
-      hipLaunchKernelGGL(ssd_chunk_cumsum<64>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp);
+      hipLaunchKernelGGL(ssd_chunk_cumsum<64>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp, p.dt_head_major);
       break;
     case 128:
-      hipLaunchKernelGGL(ssd_chunk_cumsum<128>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp);
+      hipLaunchKernelGGL(ssd_chunk_cumsum<128>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp, p.dt_head_major);
       break;
     case 256:
-      hipLaunchKernelGGL(ssd_chunk_cumsum<256>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp);
+      hipLaunchKernelGGL(ssd_chunk_cumsum<256>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp, p.dt_head_major);
       break;
     default:
       return hipErrorInvalidValue;

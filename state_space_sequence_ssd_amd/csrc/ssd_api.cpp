@@ -31,7 +31,13 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
 }
 
 bool valid_io(int io) { return io == MAMBA2_SSD_F32 || io == MAMBA2_SSD_BF16; }
-size_t io_size(int io) { return io == MAMBA2_SSD_BF16 ? 2 : 4; }
+// The io argument of the forward entry points: the dtype in the low byte,
+// layout flags above it.
+int io_type(int io_arg) { return io_arg & 0xff; }
+bool valid_io_arg(int io_arg) {
+  return valid_io(io_type(io_arg)) && (io_arg & ~(0xff | MAMBA2_SSD_DT_HEAD_MAJOR)) == 0;
+}
+size_t io_size(int io_arg) { return io_type(io_arg) == MAMBA2_SSD_BF16 ? 2 : 4; }
 
 struct Sizes {
   int64_t nc = 0, Tp = 0;
@@ -39,9 +45,10 @@ struct Sizes {
 };
 
 // Dimension checks shared by every entry point.
-int check_dims(const mamba2_ssd_dims* d, int io, Sizes* s) {
+int check_dims(const mamba2_ssd_dims* d, int io_arg, Sizes* s) {
   if (!d) return MAMBA2_SSD_ERR_NULL_POINTER;
-  if (!valid_io(io)) return MAMBA2_SSD_ERR_UNSUPPORTED;
+  if (!valid_io_arg(io_arg)) return MAMBA2_SSD_ERR_UNSUPPORTED;
+  const int io = io_type(io_arg);
   if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 ||
       d->ngroups <= 0 || d->chunk <= 0)
     return MAMBA2_SSD_ERR_BAD_DIM;
@@ -109,10 +116,11 @@ bool use_fused_state(const ssd::Problem& p) {
   return ssd::chunk_state_pass_fits(p) && ssd::chunk_state_pass_pays(p);
 }
 
-ssd::Problem problem_of(const mamba2_ssd_dims* d, int io, const Sizes& s) {
+ssd::Problem problem_of(const mamba2_ssd_dims* d, int io_arg, const Sizes& s) {
   ssd::Problem p{};
   p.bt = d->batch; p.T = d->seqlen; p.H = d->nheads; p.P = d->headdim; p.N = d->dstate;
-  p.G = d->ngroups; p.Q = d->chunk; p.nc = s.nc; p.Tp = s.Tp; p.io = io;
+  p.G = d->ngroups; p.Q = d->chunk; p.nc = s.nc; p.Tp = s.Tp; p.io = io_type(io_arg);
+  p.dt_head_major = (io_arg & MAMBA2_SSD_DT_HEAD_MAJOR) ? 1 : 0;
   return p;
 }
 
@@ -130,8 +138,9 @@ bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.h
 extern "C" {
 
 int mamba2_ssd_supported(int64_t headdim, int64_t dstate, int64_t chunk, int io_dtype) {
-  return valid_io(io_dtype) && ssd::chunk_state_has(io_dtype, headdim, dstate, chunk) &&
-         ssd::chunk_scan_has(io_dtype, headdim, dstate, chunk);
+  const int io = io_type(io_dtype);
+  return valid_io_arg(io_dtype) && ssd::chunk_state_has(io, headdim, dstate, chunk) &&
+         ssd::chunk_scan_has(io, headdim, dstate, chunk);
 }
 
 int mamba2_ssd_workspace_layout_query(const mamba2_ssd_dims* dims, int io_dtype,

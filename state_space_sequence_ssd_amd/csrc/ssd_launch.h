@@ -11,6 +11,7 @@ struct Problem {
   int64_t bt, T, H, P, N, G, Q;  // batch, seqlen, nheads, headdim, dstate, ngroups, chunk
   int64_t nc, Tp;                // nchunks, nchunks * chunk
   int io;                        // 0 = fp32, 1 = bf16 (x, B, C, y)
+  int dt_head_major;             // dt is [bt][H][T] instead of [bt][T][H]
   const void* x;
   const float* dt;
   const float* A;

@@ -143,6 +143,24 @@ def test_bad_dtype():
     assert _check(SMALL, 3) == UNSUP
 
 
+def test_dt_head_major_flag():
+    """The dt-layout flag rides in the io argument of every forward entry
+    point; it changes nothing that the host checks, and unknown flag bits
+    are rejected."""
+    hm = ssd.DT_HEAD_MAJOR
+    assert hm == 0x100
+    for io in (BF16, F32):
+        assert _check(SMALL, io | hm) == OK
+        assert ssd.workspace_bytes(SMALL, io | hm) == ssd.workspace_bytes(SMALL, io)
+        assert ssd.supported(64, 128, 256, io | hm)
+    for bad in (BF16 | 0x200, BF16 | 0x10000, F32 | hm | 0x400, 2 | hm):
+        assert _check(SMALL, bad) == UNSUP
+        assert ssd.workspace_bytes(SMALL, bad) == 0
+        assert not ssd.supported(64, 128, 256, bad)
+    # the decode step takes no flags
+    assert not ssd.step_supported(128, BF16 | hm)
+
+
 @pytest.mark.parametrize("name", ["x", "dt", "A", "B", "C", "D", "y"])
 def test_null_pointers(name):
     assert _check(SMALL, BF16, **{name: 0}) == NULLP

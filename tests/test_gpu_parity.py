@@ -330,3 +330,38 @@ def test_fused_state_pass_in_place_and_no_final(monkeypatch):
     torch.cuda.synchronize()
     assert none is None
     check_close(host(y2), yr, cfg.io, "y (fused, no final)")
+
+
+# ------------------------------------------------------------ dt layouts
+
+DT_LAYOUT = {
+    "tiny": SMALL["tiny"],                     # f32, full chunks, T % 4 == 0 (16-byte dt reads)
+    "tiny-ragged": SMALL["tiny-ragged"],       # f32, ragged last chunk
+    "2.7b-small": SMALL["2.7b-small"],         # bf16, resident scan, T % 4 != 0
+    "2.7b-even": config_by_name("mamba2-2.7b").with_shape(batch=2, seqlen=3 * 256 + 64, nheads=20),
+}
+
+
+@pytest.mark.parametrize("path", ["default", "fused"])
+@pytest.mark.parametrize("name", sorted(DT_LAYOUT))
+def test_dt_head_major_layout(name, path, monkeypatch):
+    """dt given [batch, nheads, seqlen] (MAMBA2_SSD_DT_HEAD_MAJOR) gives
+    bit-identical results to the token-major call, and matches the oracle."""
+    cfg = DT_LAYOUT[name]
+    if path == "fused":
+        if not (cfg.io == "bf16" and cfg.headdim == 64 and cfg.chunk == 256):
+            pytest.skip("the one-kernel state path takes bf16, headdim 64, chunk 256 only")
+        monkeypatch.setenv("MAMBA2_SSD_STATE_PATH", "fused")
+    log(f"[dt layout] {name} path={path} {cfg}")
+    inp = generate(cfg)
+    dev = to_device(inp, cfg.io)
+    y0, f0 = run(dev, cfg.chunk)
+    dt_hm = dev["dt"].transpose(1, 2).contiguous()
+    y1, f1 = ssd.ssd_fwd(dev["x"], dt_hm, dev["A"], dev["B"], dev["C"], dev["D"], cfg.chunk,
+                         dev["init_state"], dt_head_major=True)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1), "y differs between the dt layouts"
+    assert torch.equal(f0, f1), "final_state differs between the dt layouts"
+    yr, fr = oracle_all(inp, cfg)
+    check_close(host(y1), yr, cfg.io, "y")
+    check_close(host(f1), fr, cfg.io, "final_state")
