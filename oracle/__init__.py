@@ -13,6 +13,10 @@ kernels:
   cumulative decays, in natural ``exp`` (no base-2 rescaling).
 * ``ssd_step``       -- one token of the recurrence for every sequence and
   head (the decode step), updating a given state.
+* ``ssd_bwd_sequential`` / ``ssd_bwd_chunked`` -- every input's gradient
+  (the backward pass), by reverse mode through the token recurrence and from
+  the chunked form, independently of each other (``ssd_bwd.py``; pinned in
+  ``tests/test_oracle_bwd.py``).
 
 Both upcast every input to float64 and never round to a narrower type.
 
@@ -26,5 +30,7 @@ tie both functions to facts fixed outside this package live in
 from .ssd_seq import ssd_sequential, heads_to_groups
 from .ssd_chunked import ssd_chunked
 from .ssd_step import ssd_step
+from .ssd_bwd import ssd_bwd_chunked, ssd_bwd_sequential
 
-__all__ = ["ssd_sequential", "ssd_chunked", "ssd_step", "heads_to_groups"]
+__all__ = ["ssd_sequential", "ssd_chunked", "ssd_step", "heads_to_groups", "ssd_bwd_sequential",
+           "ssd_bwd_chunked"]
