@@ -265,11 +265,64 @@ int mamba2_ssd_step(const mamba2_ssd_step_dims* dims, int io_dtype,
                     const void* B, const void* C, const float* D,
                     float* state, void* y, void* stream);
 
+/* ---- backward pass -------------------------------------------------------
+ *
+ * Every input's gradient for a loss whose gradients with respect to the
+ * forward outputs are dy (with respect to y) and dfinal (with respect to
+ * final_state; NULL means zero). The forward pass is the recurrence at the
+ * top of this header; its gradient follows the chunked form differentiated
+ * block by block, with the state's adjoint running the chunk pass backwards
+ * in time (the "Part 3" derivation of Sasha Rush's "Mamba: The Hard Way"
+ * shows this reversal for the scalar scan: the derivative is the same scan
+ * run in the other direction, and the coefficient gradients need the forward
+ * and backward states together). The forward intermediates are recomputed
+ * inside the call; nothing from a forward call is needed.
+ *
+ * Inputs: dims, io (MAMBA2_SSD_F32 or MAMBA2_SSD_BF16, no layout flags), x,
+ * dt, A, B, C, D, init_state (nullable) exactly as for mamba2_ssd_fwd; dy
+ * [batch][seqlen][nheads][headdim] in the io dtype; dfinal (nullable) float
+ * [batch][nheads][headdim][dstate].
+ * Outputs, all float32, dense, caller-owned, written whole:
+ *   dx  [batch][seqlen][nheads][headdim]   ddt [batch][seqlen][nheads]
+ *   dB  [batch][seqlen][ngroups][dstate]   dC  like dB (sums over the
+ *                                          heads of each group)
+ *   dA  [nheads]   dD [nheads]             (sums over batch rows and tokens)
+ *   dinit [batch][nheads][headdim][dstate] (nullable: not written)
+ * Arithmetic: fp32 throughout (bf16 inputs are exact in fp32).
+ * Workspace: mamba2_ssd_bwd_workspace_bytes(dims, io) bytes, device memory,
+ * 256-byte aligned; it holds padded fp32 copies of the inputs, the chunk
+ * states, the per-chunk C.B^T and dy.x^T blocks and the per-head parts of
+ * dB and dC (about 12.6 GB for batch 4, seqlen 8192, 80 heads, headdim 64,
+ * dstate 128, chunk 256). Sizes are those of mamba2_ssd_fwd, plus
+ * batch * nchunks * nheads <= 65535.
+ * Errors: as mamba2_ssd_check_args (NULL_POINTER for a missing required
+ * pointer: A, D, dA, dD always; x, dt, B, C, dy, dx, ddt, dB, dC when
+ * batch * seqlen > 0), ALIAS when an output overlaps an input, another
+ * output or the workspace, UNSUPPORTED for flag bits in io. Validation runs
+ * on the host before any launch; the call is asynchronous on `stream`. */
+size_t mamba2_ssd_bwd_workspace_bytes(const mamba2_ssd_dims* dims, int io_dtype);
+
+int mamba2_ssd_bwd_check_args(const mamba2_ssd_dims* dims, int io_dtype,
+                              const void* x, const float* dt, const float* A,
+                              const void* B, const void* C, const float* D,
+                              const float* init_state, const void* dy, const float* dfinal,
+                              const float* dx, const float* ddt, const float* dA,
+                              const float* dB, const float* dC, const float* dD,
+                              const float* dinit, const void* workspace,
+                              size_t workspace_bytes);
+
+int mamba2_ssd_bwd(const mamba2_ssd_dims* dims, int io_dtype,
+                   const void* x, const float* dt, const float* A,
+                   const void* B, const void* C, const float* D,
+                   const float* init_state, const void* dy, const float* dfinal,
+                   float* dx, float* ddt, float* dA, float* dB, float* dC, float* dD,
+                   float* dinit, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static string naming a status code. Never NULL. */
 const char* mamba2_ssd_status_string(int status);
 
-/* Text of the last HIP error this thread saw inside mamba2_ssd_fwd
- * (MAMBA2_SSD_ERR_HIP), or "" if none. Valid until the thread's next call. */
+/* Text of the last HIP error this thread saw inside mamba2_ssd_fwd,
+ * mamba2_ssd_bwd or mamba2_ssd_step (MAMBA2_SSD_ERR_HIP), or "" if none. Valid until the thread's next call. */
 const char* mamba2_ssd_last_hip_error(void);
 
 #ifdef __cplusplus

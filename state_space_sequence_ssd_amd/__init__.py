@@ -22,7 +22,9 @@ __all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_
            "mamba2_ssd_status_string", "mamba2_ssd_last_hip_error",
            "ssd_step", "ssd_step_ptr", "step_supported", "step_check_args", "StepDims",
            "mamba2_ssd_step", "mamba2_ssd_step_check_args", "mamba2_ssd_step_supported",
-           "mamba2_ssd_fused_state_pass", "fused_state_pass"]
+           "mamba2_ssd_fused_state_pass", "fused_state_pass",
+           "ssd_bwd", "ssd_bwd_ptr", "bwd_workspace_bytes", "bwd_check_args",
+           "mamba2_ssd_bwd", "mamba2_ssd_bwd_check_args", "mamba2_ssd_bwd_workspace_bytes"]
 
 # The C entry points under their own names (ctypes functions with prototypes).
 mamba2_ssd_fwd = lib.mamba2_ssd_fwd
@@ -37,6 +39,9 @@ mamba2_ssd_fused_state_pass = lib.mamba2_ssd_fused_state_pass
 mamba2_ssd_step = lib.mamba2_ssd_step
 mamba2_ssd_step_check_args = lib.mamba2_ssd_step_check_args
 mamba2_ssd_step_supported = lib.mamba2_ssd_step_supported
+mamba2_ssd_bwd = lib.mamba2_ssd_bwd
+mamba2_ssd_bwd_check_args = lib.mamba2_ssd_bwd_check_args
+mamba2_ssd_bwd_workspace_bytes = lib.mamba2_ssd_bwd_workspace_bytes
 
 
 def _dims(d) -> Dims:
@@ -216,3 +221,68 @@ def ssd_step(x, dt, A, B, C, D, state, *, y=None):
         ssd_step_ptr(StepDims(bt, H, P, N, G), io, x.data_ptr(), dt.data_ptr(), A.data_ptr(), B.data_ptr(),
                      C.data_ptr(), D.data_ptr(), state.data_ptr(), y.data_ptr(), stream)
     return y
+
+
+# ------------------------------------------------------------- backward pass
+
+GRAD_NAMES = ("dx", "ddt", "dA", "dB", "dC", "dD", "dinit")
+
+
+def bwd_workspace_bytes(dims, io: int) -> int:
+    return int(lib.mamba2_ssd_bwd_workspace_bytes(ctypes.byref(_dims(dims)), io))
+
+
+def bwd_check_args(dims, io, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA, dB, dC, dD, dinit,
+                   workspace, ws_bytes) -> int:
+    """Host-only validation of a backward call on raw integer addresses (0 for NULL)."""
+    return int(lib.mamba2_ssd_bwd_check_args(ctypes.byref(_dims(dims)), io, x, dt, A, B, C, D, init_state, dy,
+                                             dfinal, dx, ddt, dA, dB, dC, dD, dinit, workspace, ws_bytes))
+
+
+def ssd_bwd_ptr(dims, io, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA, dB, dC, dD, dinit,
+                workspace, ws_bytes, stream: int = 0) -> None:
+    """mamba2_ssd_bwd on raw device addresses; raises SsdError on a nonzero status."""
+    st = lib.mamba2_ssd_bwd(ctypes.byref(_dims(dims)), io, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt,
+                            dA, dB, dC, dD, dinit, workspace, ws_bytes, stream)
+    if st != 0:
+        raise SsdError(st, lib.mamba2_ssd_last_hip_error().decode())
+
+
+def ssd_bwd(x, dt, A, B, C, D, dy, chunk: int, init_state=None, dfinal=None, *, workspace=None) -> dict:
+    """Gradients of the forward pass on torch CUDA tensors (contiguous, one
+    device): ``dy`` like y (the io dtype), ``dfinal`` float32 like the final
+    state or None. Returns a dict of float32 tensors named dx, ddt, dA, dB,
+    dC, dD and dinit (the initial state's gradient, also when init_state is
+    None). Runs on torch's current stream.
+    """
+    import torch
+
+    io = BF16 if x.dtype == torch.bfloat16 else F32
+    if x.dtype not in (torch.bfloat16, torch.float32) or dy.dtype != x.dtype or B.dtype != x.dtype \
+            or C.dtype != x.dtype:
+        raise TypeError("x, B, C and dy must share the io dtype (bfloat16 or float32)")
+    for name, t in (("dt", dt), ("A", A), ("D", D), ("init_state", init_state), ("dfinal", dfinal)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    for t in (x, dt, A, B, C, D, dy, init_state, dfinal):
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("all tensors must be contiguous GPU tensors")
+    bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dy.shape) != tuple(x.shape) or tuple(dt.shape) != (bt, T, H):
+        raise ValueError("inconsistent shapes")
+    dims = Dims(bt, T, H, P, N, G, chunk)
+    f32 = dict(dtype=torch.float32, device=x.device)
+    g = {"dx": torch.empty((bt, T, H, P), **f32), "ddt": torch.empty((bt, T, H), **f32),
+         "dA": torch.empty((H,), **f32), "dB": torch.empty((bt, T, G, N), **f32),
+         "dC": torch.empty((bt, T, G, N), **f32), "dD": torch.empty((H,), **f32),
+         "dinit": torch.empty((bt, H, P, N), **f32)}
+    nbytes = bwd_workspace_bytes(dims, io)   # 0 for invalid sizes too: the call then reports the status
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    ptr = lambda t: 0 if t is None else t.data_ptr()
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        ssd_bwd_ptr(dims, io, ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), ptr(init_state), ptr(dy),
+                    ptr(dfinal), *[ptr(g[k]) for k in GRAD_NAMES], ptr(workspace), workspace.numel(), stream)
+    return g

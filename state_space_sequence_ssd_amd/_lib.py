@@ -86,6 +86,14 @@ def _load():
     L.mamba2_ssd_fwd_timed.restype = ctypes.c_int
     L.mamba2_ssd_fused_state_pass.argtypes = [dims_p, ctypes.c_int]
     L.mamba2_ssd_fused_state_pass.restype = ctypes.c_int
+    L.mamba2_ssd_bwd_workspace_bytes.argtypes = [dims_p, ctypes.c_int]
+    L.mamba2_ssd_bwd_workspace_bytes.restype = sz
+    L.mamba2_ssd_bwd_check_args.argtypes = [dims_p, ctypes.c_int, vp, fp, fp, vp, vp, fp, fp, vp, fp,
+                                            fp, fp, fp, fp, fp, fp, fp, vp, sz]
+    L.mamba2_ssd_bwd_check_args.restype = ctypes.c_int
+    L.mamba2_ssd_bwd.argtypes = [dims_p, ctypes.c_int, vp, fp, fp, vp, vp, fp, fp, vp, fp,
+                                 fp, fp, fp, fp, fp, fp, fp, vp, sz, vp]
+    L.mamba2_ssd_bwd.restype = ctypes.c_int
     step_p = ctypes.POINTER(StepDims)
     L.mamba2_ssd_step_supported.argtypes = [i64, ctypes.c_int]
     L.mamba2_ssd_step_supported.restype = ctypes.c_int

@@ -13,6 +13,7 @@
 #include <string>
 
 #include "ssd_launch.h"
+#include "ssd_bwd.h"
 
 namespace {
 
@@ -335,5 +336,101 @@ const char* mamba2_ssd_status_string(int status) {
 }
 
 const char* mamba2_ssd_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+
+// ---- backward pass ---------------------------------------------------------
+
+static int bwd_sizes(const mamba2_ssd_dims* d, int io_dtype, Sizes* s, ssd::BwdLayout* L) {
+  if (io_dtype & ~0xff) return MAMBA2_SSD_ERR_UNSUPPORTED;   // no layout flags here
+  const int st = check_dims(d, io_dtype, s);
+  if (st != MAMBA2_SSD_OK) return st;
+  // the GEMM batches (batch, chunk, head) go in grid dimension y
+  int64_t z;
+  if (!mul_ok(d->batch, s->nc, &z) || !mul_ok(z, d->nheads, &z) || z > ssd::kMaxGridYZ) return MAMBA2_SSD_ERR_BAD_DIM;
+  *L = ssd::bwd_layout(d->batch, d->nheads, d->headdim, d->dstate, d->ngroups, d->chunk, s->nc);
+  return MAMBA2_SSD_OK;
+}
+
+size_t mamba2_ssd_bwd_workspace_bytes(const mamba2_ssd_dims* dims, int io_dtype) {
+  Sizes s;
+  ssd::BwdLayout L;
+  if (bwd_sizes(dims, io_dtype, &s, &L) != MAMBA2_SSD_OK) return 0;
+  return L.total;
+}
+
+int mamba2_ssd_bwd_check_args(const mamba2_ssd_dims* d, int io, const void* x, const float* dt, const float* A,
+                              const void* B, const void* C, const float* D, const float* init_state, const void* dy,
+                              const float* dfinal, const float* dx, const float* ddt, const float* dA,
+                              const float* dB, const float* dC, const float* dD, const float* dinit,
+                              const void* workspace, size_t workspace_bytes) {
+  Sizes s;
+  ssd::BwdLayout L;
+  const int st = bwd_sizes(d, io, &s, &L);
+  if (st != MAMBA2_SSD_OK) return st;
+  const bool tokens = s.n_x > 0;
+  if (!A || !D || !dA || !dD) return MAMBA2_SSD_ERR_NULL_POINTER;
+  if (tokens && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC)) return MAMBA2_SSD_ERR_NULL_POINTER;
+  if (d->batch > 0 && (!workspace || workspace_bytes < L.total)) return MAMBA2_SSD_ERR_WORKSPACE;
+  const size_t e = io_size(io);
+  const Range ins[] = {range_of(x, (size_t)s.n_x * e), range_of(dt, (size_t)s.n_dt * 4),
+                       range_of(A, (size_t)d->nheads * 4), range_of(B, (size_t)s.n_bc * e),
+                       range_of(C, (size_t)s.n_bc * e), range_of(D, (size_t)d->nheads * 4),
+                       range_of(init_state, (size_t)s.n_state * 4), range_of(dy, (size_t)s.n_x * e),
+                       range_of(dfinal, (size_t)s.n_state * 4)};
+  const Range outs[] = {range_of(dx, (size_t)s.n_x * 4), range_of(ddt, (size_t)s.n_dt * 4),
+                        range_of(dA, (size_t)d->nheads * 4), range_of(dB, (size_t)s.n_bc * 4),
+                        range_of(dC, (size_t)s.n_bc * 4), range_of(dD, (size_t)d->nheads * 4),
+                        range_of(dinit, (size_t)s.n_state * 4),
+                        range_of(workspace, d->batch > 0 ? L.total : 0)};
+  const int no = sizeof(outs) / sizeof(outs[0]);
+  for (int i = 0; i < no; ++i) {
+    for (const Range& r : ins)
+      if (overlap(outs[i], r)) return MAMBA2_SSD_ERR_ALIAS;
+    for (int j = i + 1; j < no; ++j)
+      if (overlap(outs[i], outs[j])) return MAMBA2_SSD_ERR_ALIAS;
+  }
+  return MAMBA2_SSD_OK;
+}
+
+int mamba2_ssd_bwd(const mamba2_ssd_dims* d, int io, const void* x, const float* dt, const float* A, const void* B,
+                   const void* C, const float* D, const float* init_state, const void* dy, const float* dfinal,
+                   float* dx, float* ddt, float* dA, float* dB, float* dC, float* dD, float* dinit, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  g_last_hip_error.clear();
+  const int st = mamba2_ssd_bwd_check_args(d, io, x, dt, A, B, C, D, init_state, dy, dfinal, dx, ddt, dA, dB, dC, dD,
+                                           dinit, workspace, workspace_bytes);
+  if (st != MAMBA2_SSD_OK) return st;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  {
+    // (with batch 0 the workspace may be null: no kernel then touches it, and
+    // dA, dD receive zeros)
+    Sizes s;
+    ssd::BwdLayout L;
+    bwd_sizes(d, io, &s, &L);
+    char* ws = static_cast<char*>(workspace);
+    auto f = [&](size_t off) { return ws ? reinterpret_cast<float*>(ws + off) : nullptr; };
+    ssd::BwdProblem p{};
+    p.bt = d->batch; p.T = d->seqlen; p.H = d->nheads; p.P = d->headdim; p.N = d->dstate; p.G = d->ngroups;
+    p.Q = d->chunk; p.nc = s.nc; p.Tp = s.Tp; p.io = io;
+    p.x = x; p.dt = dt; p.A = A; p.B = B; p.C = C; p.D = D; p.init = init_state; p.dy = dy; p.dfinal = dfinal;
+    p.dx = dx; p.ddt = ddt; p.dA = dA; p.dB = dB; p.dC = dC; p.dD = dD; p.dinit = dinit;
+    p.gcum = f(L.gcum); p.dtt = f(L.dtt); p.wst = f(L.wst); p.E = f(L.E); p.Xp = f(L.Xp); p.dYp = f(L.dYp);
+    p.Bp = f(L.Bp); p.Cp = f(L.Cp); p.S = f(L.S); p.hprev = f(L.hprev); p.dhn = f(L.dhn); p.CB = f(L.CB);
+    p.DX = f(L.DX); p.W1 = f(L.W1); p.U = f(L.U); p.V = f(L.V); p.dXp = f(L.dXp); p.dBh = f(L.dBh);
+    p.dCh = f(L.dCh); p.rowZ = f(L.rowZ); p.colZ = f(L.colZ); p.colW = f(L.colW); p.dA_part = f(L.dA_part);
+    p.dD_part = f(L.dD_part);
+    // the chunk-local cumsum, dt and the state weights, as the forward pass computes them
+    ssd::Problem fp = problem_of(d, io, s);
+    fp.dt = dt; fp.A = A; fp.gcum = p.gcum; fp.dtt = p.dtt; fp.wst = p.wst;
+    if (s.nc > 0 && d->batch > 0) err = ssd::launch_chunk_cumsum(fp, hs);
+    if (err == hipSuccess) err = ssd::launch_ssd_bwd(p, hs);
+  }
+  if (err != hipSuccess) {
+    g_last_hip_error = hipGetErrorString(err);
+    return MAMBA2_SSD_ERR_HIP;
+  }
+  return MAMBA2_SSD_OK;
+}
 
 }  // extern "C"

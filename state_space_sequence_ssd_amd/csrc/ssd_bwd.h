@@ -1,0 +1,49 @@
+// Host-side description of one backward call (ssd_bwd.hip): sizes, the
+// caller's device pointers and the workspace carve-up. Validated by the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ssd_launch.h"
+
+namespace ssd {
+
+// Byte offsets of the backward workspace's arrays (all fp32, 256-byte aligned).
+struct BwdLayout {
+  size_t gcum, dtt, wst, E;             // [bt][H][Tp]
+  size_t Xp, dYp;                       // [bt][Tp][H][P], zero padded
+  size_t Bp, Cp;                        // [bt][Tp][G][N], zero padded
+  size_t S, hprev, dhn;                 // [bt][H][nc][P][N]
+  size_t CB;                            // [bt][nc][G][Q][Q]
+  size_t DX, W1;                        // [bt][nc][H][Q][Q]
+  size_t U, V;                          // [bt][nc][H][Q][P]
+  size_t dXp;                           // [bt][Tp][H][P]
+  size_t dBh, dCh;                      // [bt][Tp][H][N]
+  size_t rowZ, colZ, colW;              // [bt][H][Tp]
+  size_t dA_part, dD_part;              // [bt][H][nc]
+  size_t total;
+};
+
+BwdLayout bwd_layout(int64_t bt, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q, int64_t nc);
+
+struct BwdProblem {
+  int64_t bt, T, H, P, N, G, Q, nc, Tp;
+  int io;                               // 0 = fp32, 1 = bf16 (x, B, C, dy)
+  const void* x; const float* dt; const float* A; const void* B; const void* C; const float* D;
+  const float* init;                    // may be null
+  const void* dy;
+  const float* dfinal;                  // may be null
+  float* dx; float* ddt; float* dA; float* dB; float* dC; float* dD;
+  float* dinit;                         // may be null
+  // workspace arrays (see BwdLayout)
+  float *gcum, *dtt, *wst, *E, *Xp, *dYp, *Bp, *Cp, *S, *hprev, *dhn, *CB, *DX, *W1, *U, *V, *dXp, *dBh,
+      *dCh, *rowZ, *colZ, *colW, *dA_part, *dD_part;
+};
+
+// Enqueues the backward kernels after the cumsum (which the caller runs into
+// gcum, dtt and wst first).
+hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t stream);
+
+}  // namespace ssd

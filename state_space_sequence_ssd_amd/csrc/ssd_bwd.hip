@@ -1,0 +1,497 @@
+// The backward pass of the SSD layer: every input's gradient from the
+// upstream gradients dy (like y) and dfinal (like the final state).
+//
+// Source of the method: the chunked "jump" form of the forward pass (NVIDIA
+// developer blog "Accelerating Mamba-2 with high-performance forward-pass
+// kernels in NVIDIA CUDA Tile", section "Mamba-2 architecture") differentiated
+// block by block, and the observation of "Part 3" of Sasha Rush's "Mamba: The
+// Hard Way" that the state's adjoint runs the same scan backwards in time.
+// Per chunk of Q tokens, with G' the chunk-local cumsum of A dt times log2 e,
+// E_i = 2^(G'_i), L_ij = 2^(G'_i - G'_j) (i >= j, else 0), w_j = dt_j
+// 2^(G'_last - G'_j), Hprev the state entering the chunk and dHn the adjoint
+// of the state leaving it:
+//
+//   dHprev = 2^(G'_last) dHn + dY^T diag(E) C            (reverse chunk pass)
+//   dx     = (L o CB o dt_j)^T dY + diag(w) B dHn^T + D dY
+//   dB_h   = (L o DX o dt_j)^T C  + diag(w) X dHn         (summed over a group)
+//   dC_h   = (L o DX o dt_j) B    + diag(E) dY Hprev      (summed over a group)
+//
+// with CB = C B^T and DX = dY X^T, and the gradient with respect to the
+// natural-log cumsum G (rows minus columns of Z = L o CB o DX o dt_j, the
+// carried-state and chunk-end terms) passed to dt and A through
+// G_i = A sum_{s <= i} dt_s.
+//
+// This first form favours clarity over speed: fp32 throughout (bf16 inputs
+// are exact in fp32), the contractions as one batched fp32 GEMM kernel with
+// LDS tiles, and small elementwise kernels between them, all through a
+// caller-provided workspace.
+#include "ssd_bwd.h"
+#include "ssd_device.h"
+
+namespace ssd {
+
+namespace {
+
+// ---------------------------------------------------------------- GEMM
+// C[z] = beta C[z] + diag(rs[z]) (A[z] diag(ks[z]) B[z]), fp32. Every operand
+// is addressed by a base pointer, element strides (row, col) and a batch
+// offset z0 s0 + z1 s1 + (z2 / d2) s2 for z = (z0 Z1 + z1) Z2 + z2; the
+// divisor d2 maps a head index to its group for operands shared by a group.
+// Scale vectors may be null (ones).
+constexpr int GT = 64, GK = 16;   // output tile GT x GT, k-step GK; 256 threads, 4 x 4 each
+
+struct Operand {
+  const float* p;
+  int64_t rs, cs;        // element strides of rows and columns
+  int64_t s0, s1, s2;    // batch strides
+  int d2;                // z2 divisor
+  __device__ int64_t base(int z0, int z1, int z2) const { return z0 * s0 + z1 * s1 + (int64_t)(z2 / d2) * s2; }
+};
+
+struct GemmArgs {
+  Operand a, b, c, rsc, ksc;   // rsc / ksc: only p, s0..s2, d2 used (unit stride vectors)
+  int M, N, K, Z1, Z2;
+  float beta;
+};
+
+__global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
+  __shared__ float sa[GK][GT + 4];
+  __shared__ float sb[GK][GT + 4];
+  const int tiles_n = (g.N + GT - 1) / GT;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
+  const int z = blockIdx.y;
+  const int z2 = z % g.Z2, z1 = (z / g.Z2) % g.Z1, z0 = z / (g.Z2 * g.Z1);
+  const float* A = g.a.p + g.a.base(z0, z1, z2);
+  const float* B = g.b.p + g.b.base(z0, z1, z2);
+  const float* ks = g.ksc.p ? g.ksc.p + g.ksc.base(z0, z1, z2) : nullptr;
+  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  const int m0 = tm * GT, n0 = tn * GT;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < g.K; k0 += GK) {
+    // stage A (GT x GK, as [k][m]) and B (GK x GT, as [k][n]): 4 elements each per thread
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int idx = tid + 256 * e;          // 0 .. 1023
+      const int kk = idx % GK, mm = idx / GK;  // A: consecutive threads walk k
+      const int m = m0 + mm, k = k0 + kk;
+      float v = 0.f;
+      if (m < g.M && k < g.K) {
+        v = A[m * g.a.rs + k * g.a.cs];
+        if (ks) v *= ks[k];
+      }
+      sa[kk][mm] = v;
+      const int nn = idx % GT, kb = idx / GT;  // B: consecutive threads walk n
+      const int n = n0 + nn, kq = k0 + kb;
+      sb[kb][nn] = (n < g.N && kq < g.K) ? B[kq * g.b.rs + n * g.b.cs] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < GK; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = sa[kk][ty + 16 * i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = sb[kk][tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  float* Cp = const_cast<float*>(g.c.p) + g.c.base(z0, z1, z2);
+  const float* rs = g.rsc.p ? g.rsc.p + g.rsc.base(z0, z1, z2) : nullptr;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty + 16 * i;
+    if (m >= g.M) continue;
+    const float r = rs ? rs[m] : 1.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + tx + 16 * j;
+      if (n >= g.N) continue;
+      float* cp = Cp + m * g.c.rs + n * g.c.cs;
+      const float v = r * acc[i][j];
+      *cp = g.beta == 0.f ? v : fmaf(g.beta, *cp, v);
+    }
+  }
+}
+
+Operand op(const float* p, int64_t rs, int64_t cs, int64_t s0, int64_t s1, int64_t s2, int d2 = 1) {
+  return Operand{p, rs, cs, s0, s1, s2, d2};
+}
+Operand none() { return Operand{nullptr, 0, 0, 0, 0, 0, 1}; }
+
+hipError_t gemm(const Operand& a, const Operand& b, const Operand& c, const Operand& rsc, const Operand& ksc,
+                int M, int N, int K, int Z0, int Z1, int Z2, float beta, hipStream_t s) {
+  GemmArgs g{a, b, c, rsc, ksc, M, N, K, Z1, Z2, beta};
+  const int64_t tiles = (int64_t)((M + GT - 1) / GT) * ((N + GT - 1) / GT);
+  const int64_t Z = (int64_t)Z0 * Z1 * Z2;
+  if (Z == 0 || tiles == 0) return hipSuccess;
+  if (Z > kMaxGridYZ) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(bwd_gemm, dim3((unsigned)tiles, (unsigned)Z), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------- elementwise
+template <typename T> __device__ __forceinline__ float ld(const T* p, int64_t i);
+template <> __device__ __forceinline__ float ld<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float ld<bf16>(const bf16* p, int64_t i) {
+  return __uint_as_float((uint32_t)(reinterpret_cast<const uint16_t*>(p)[i]) << 16);
+}
+
+// rows [bt][T][W] of the io type -> fp32 [bt][Tp][W], zero rows past T
+template <typename T>
+__global__ void pad_rows(const T* __restrict__ src, float* __restrict__ dst, int64_t T_, int64_t Tp, int64_t W,
+                         int64_t total) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t w = i % W, t = (i / W) % Tp, b = i / (W * Tp);
+    dst[i] = t < T_ ? ld(src, (b * T_ + t) * W + w) : 0.f;
+  }
+}
+
+__global__ void exp2_all(const float* __restrict__ g, float* __restrict__ e, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    e[i] = exp2_hw(g[i]);
+}
+
+// The chunk recursion over one (b, h) state, one thread per state element:
+// forward (rev = 0): out[k] = h; h = 2^(G'_last,k) h + S[k], from init (or 0);
+// reverse (rev = 1): out[k] = h; h = 2^(G'_last,k) h + S[k] for k from the
+// last chunk down, from dfinal (or 0), and the end value goes to `last`.
+__global__ void chunk_recursion(const float* __restrict__ S, const float* __restrict__ gcum,
+                                const float* __restrict__ h0, float* __restrict__ out, float* __restrict__ last,
+                                int64_t nc, int64_t Tp, int64_t Q, int64_t PN, int64_t total, int rev) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t bh = i / PN, e = i % PN;
+    float h = h0 ? h0[i] : 0.f;
+    for (int64_t s = 0; s < nc; ++s) {
+      const int64_t k = rev ? nc - 1 - s : s;
+      const int64_t o = (bh * nc + k) * PN + e;
+      out[o] = h;
+      h = fmaf(exp2_hw(gcum[bh * Tp + k * Q + Q - 1]), h, S[o]);
+    }
+    if (last) last[i] = h;
+  }
+}
+
+// Per (b, k, h): the masked, decayed blocks W1s = L o CB o dt_j (in its own
+// array) and W2s = L o DX o dt_j (over DX, in place), zero above the
+// diagonal, and the sums the time gradient needs: rows and columns of
+// Z = L o CB o DX o dt_j, and the columns of L o CB o DX. The row sums are
+// taken first, one thread per row, while DX is still intact; then one thread
+// per column writes the blocks. Fixed summation orders: the result does not
+// depend on scheduling.
+__global__ __launch_bounds__(256) void mask_decay(const float* __restrict__ CB, float* __restrict__ DXW2,
+                                                  float* __restrict__ W1, const float* __restrict__ gcum,
+                                                  const float* __restrict__ dtt, float* __restrict__ rowZ,
+                                                  float* __restrict__ colZ, float* __restrict__ colW,
+                                                  int Q, int H, int hpg, int64_t nc, int64_t Tp) {
+  __shared__ float sg[256], sd[256];
+  const int h = blockIdx.x % H;
+  const int64_t k = (blockIdx.x / H) % nc, b = blockIdx.x / (H * nc);
+  const int64_t QQ = (int64_t)Q * Q;
+  const float* cb = CB + ((b * nc + k) * (H / hpg) + h / hpg) * QQ;
+  float* dx = DXW2 + ((b * nc + k) * H + h) * QQ;
+  float* w1 = W1 + ((b * nc + k) * H + h) * QQ;
+  const int64_t tb = (b * H + h) * Tp + k * Q;
+  for (int i = threadIdx.x; i < Q; i += blockDim.x) {
+    sg[i] = gcum[tb + i];
+    sd[i] = dtt[tb + i];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < Q; i += blockDim.x) {
+    float rz = 0.f;
+    for (int j = 0; j <= i; ++j) {
+      const int64_t o = (int64_t)i * Q + j;
+      rz += exp2_hw(sg[i] - sg[j]) * cb[o] * dx[o] * sd[j];
+    }
+    rowZ[tb + i] = rz;
+  }
+  __syncthreads();   // every row has read DX before it is overwritten
+  for (int j = threadIdx.x; j < Q; j += blockDim.x) {
+    const float gj = sg[j], dj = sd[j];
+    float cz = 0.f, cw = 0.f;
+    for (int i = 0; i < Q; ++i) {
+      const int64_t o = (int64_t)i * Q + j;
+      if (i < j) {
+        w1[o] = 0.f;
+        dx[o] = 0.f;
+        continue;
+      }
+      const float L = exp2_hw(sg[i] - gj);
+      const float lcb = L * cb[o], d = dx[o];
+      w1[o] = lcb * dj;
+      dx[o] = L * d * dj;
+      cz += lcb * d * dj;
+      cw += lcb * d;
+    }
+    colZ[tb + j] = cz;
+    colW[tb + j] = cw;
+  }
+}
+
+// Per (b, h, k), Q threads: dx (output), ddt (output), and this chunk's
+// parts of dA and dD. U = B dHn^T and V = C Hprev^T rows, dXp = W1s^T dY.
+__global__ __launch_bounds__(256) void finish_chunk(const BwdProblem p) {
+  __shared__ float s_dg[256], s_dt[256], s_red[256];
+  __shared__ float s_scal[2];
+  const int Q = (int)p.Q, P = (int)p.P, H = (int)p.H;
+  const int h = blockIdx.x % H;
+  const int64_t k = (blockIdx.x / H) % p.nc, b = blockIdx.x / (H * p.nc);
+  const int i = threadIdx.x;
+  const int64_t tb = (b * H + h) * p.Tp + k * Q;
+  const int64_t t = k * Q + i;   // token index
+  const int64_t PN = p.P * p.N;
+  const float* Hp = p.hprev + ((b * H + h) * p.nc + k) * PN;
+  const float* dHn = p.dhn + ((b * H + h) * p.nc + k) * PN;
+  // <dHn, Hprev> over the block
+  float part = 0.f;
+  for (int64_t e = i; e < PN; e += blockDim.x) part += dHn[e] * Hp[e];
+  s_red[i] = part;
+  __syncthreads();
+  for (int s = blockDim.x / 2; s > 0; s /= 2) {
+    if (i < s) s_red[i] += s_red[i + s];
+    __syncthreads();
+  }
+  if (i == 0) s_scal[0] = s_red[0];
+  __syncthreads();
+
+  float bvec = 0.f, dterm = 0.f, gi = 0.f, wi = 0.f;
+  if (i < Q) {
+    const int64_t row = ((b * p.Tp + t) * H + h) * P;           // [bt][Tp][H][P] rows
+    const int64_t urow = (((b * p.nc + k) * H + h) * Q + i) * P;  // [bt][nc][H][Q][P] rows
+    const float D = p.D[h], E = p.E[tb + i];
+    wi = p.wst[tb + i];
+    gi = p.gcum[tb + i];
+    float avec = 0.f, dd = 0.f;
+    for (int q = 0; q < P; ++q) {
+      const float xv = p.Xp[row + q], dyv = p.dYp[row + q], u = p.U[urow + q];
+      avec += dyv * p.V[urow + q];
+      bvec += xv * u;
+      dd += dyv * xv;
+      if (t < p.T) p.dx[((b * p.T + t) * H + h) * P + q] = p.dXp[row + q] + wi * u + D * dyv;
+    }
+    dterm = dd;
+    s_dg[i] = E * avec + p.rowZ[tb + i] - p.colZ[tb + i] - wi * bvec;
+    s_dt[i] = p.dtt[tb + i];
+  }
+  __syncthreads();
+  // the chunk-end term: 2^(G'_last) <dHn, Hprev> + sum_j w_j bvec_j
+  s_red[i] = (i < Q) ? wi * bvec : 0.f;
+  __syncthreads();
+  for (int s = blockDim.x / 2; s > 0; s /= 2) {
+    if (i < s) s_red[i] += s_red[i + s];
+    __syncthreads();
+  }
+  if (i == 0) {
+    const float glast = p.gcum[tb + Q - 1];
+    s_dg[Q - 1] += exp2_hw(glast) * s_scal[0] + s_red[0];
+  }
+  __syncthreads();
+  if (i == 0) {
+    // sequential scans over the chunk (Q <= 256): reverse cumsum of dG into
+    // s_red, and the chunk's dA part sum_i dG_i * cumdt_i
+    float acc = 0.f;
+    for (int j = Q - 1; j >= 0; --j) {
+      acc += s_dg[j];
+      s_red[j] = acc;
+    }
+    float cum = 0.f, da = 0.f;
+    for (int j = 0; j < Q; ++j) {
+      cum += s_dt[j];
+      da += s_dg[j] * cum;
+    }
+    p.dA_part[(b * H + h) * p.nc + k] = da;
+  }
+  __syncthreads();
+  if (i < Q && t < p.T) {
+    const float glast = p.gcum[tb + Q - 1];
+    p.ddt[(b * p.T + t) * H + h] = p.colW[tb + i] + exp2_hw(glast - gi) * bvec + p.A[h] * s_red[i];
+  }
+  // dD part: sum over the chunk of dy . x
+  __syncthreads();
+  s_red[i] = (i < Q) ? dterm : 0.f;
+  __syncthreads();
+  for (int s = blockDim.x / 2; s > 0; s /= 2) {
+    if (i < s) s_red[i] += s_red[i + s];
+    __syncthreads();
+  }
+  if (i == 0) p.dD_part[(b * H + h) * p.nc + k] = s_red[0];
+}
+
+// dB, dC: the sum over a group's heads of the per-head parts [bt][Tp][H][N]
+__global__ void group_sum(const float* __restrict__ part, float* __restrict__ out, int64_t T_, int64_t Tp, int H,
+                          int G, int64_t N, int64_t total) {
+  const int hpg = H / G;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = i % N, g = (i / N) % G, t = (i / (N * G)) % T_, b = i / (N * G * T_);
+    const float* src = part + ((b * Tp + t) * H + g * hpg) * N + n;
+    float s = 0.f;
+    for (int j = 0; j < hpg; ++j) s += src[j * N];
+    out[i] = s;
+  }
+}
+
+// dA, dD: sums over batch rows and chunks of the per-(b, h, k) parts
+__global__ void head_sums(const float* __restrict__ dA_part, const float* __restrict__ dD_part, float* __restrict__ dA,
+                          float* __restrict__ dD, int64_t bt, int H, int64_t nc) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
+  float sa = 0.f, sd = 0.f;
+  for (int64_t b = 0; b < bt; ++b)
+    for (int64_t k = 0; k < nc; ++k) {
+      sa += dA_part[(b * H + h) * nc + k];
+      sd += dD_part[(b * H + h) * nc + k];
+    }
+  dA[h] = sa;
+  dD[h] = sd;
+}
+
+unsigned grid_for(int64_t total) {
+  const int64_t g = (total + 255) / 256;
+  return (unsigned)(g < 65536 ? (g > 0 ? g : 1) : 65536);
+}
+
+}  // namespace
+
+BwdLayout bwd_layout(int64_t bt, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q, int64_t nc) {
+  BwdLayout L{};
+  const int64_t Tp = nc * Q;
+  size_t off = 0;
+  auto take = [&](size_t floats) {
+    const size_t o = off;
+    off = (off + floats * 4 + 255) / 256 * 256;
+    return o;
+  };
+  L.gcum = take(bt * H * Tp);
+  L.dtt = take(bt * H * Tp);
+  L.wst = take(bt * H * Tp);
+  L.E = take(bt * H * Tp);
+  L.Xp = take(bt * Tp * H * P);
+  L.dYp = take(bt * Tp * H * P);
+  L.Bp = take(bt * Tp * G * N);
+  L.Cp = take(bt * Tp * G * N);
+  L.S = take(bt * H * nc * P * N);
+  L.hprev = take(bt * H * nc * P * N);
+  L.dhn = take(bt * H * nc * P * N);
+  L.CB = take(bt * nc * G * Q * Q);
+  L.DX = take(bt * nc * H * Q * Q);
+  L.W1 = take(bt * nc * H * Q * Q);
+  L.U = take(bt * nc * H * Q * P);
+  L.V = take(bt * nc * H * Q * P);
+  L.dXp = take(bt * Tp * H * P);
+  L.dBh = take(bt * Tp * H * N);
+  L.dCh = take(bt * Tp * H * N);
+  L.rowZ = take(bt * H * Tp);
+  L.colZ = take(bt * H * Tp);
+  L.colW = take(bt * H * Tp);
+  L.dA_part = take(bt * H * nc);
+  L.dD_part = take(bt * H * nc);
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
+  const int64_t bt = p.bt, T = p.T, H = p.H, P = p.P, N = p.N, G = p.G, Q = p.Q, nc = p.nc, Tp = p.Tp;
+  const int hpg = (int)(H / G);
+  const int64_t PN = P * N, QQ = Q * Q;
+  hipError_t e = hipSuccess;
+  auto ok = [&](hipError_t r) {
+    if (e == hipSuccess) e = r;
+    return e == hipSuccess;
+  };
+  // 1. inputs to padded fp32, and 2^(G')
+  const int64_t nx = bt * Tp * H * P, nb = bt * Tp * G * N;
+  if (p.io == 1) {
+    hipLaunchKernelGGL(pad_rows<bf16>, dim3(grid_for(nx)), dim3(256), 0, s, (const bf16*)p.x, p.Xp, T, Tp, H * P, nx);
+    hipLaunchKernelGGL(pad_rows<bf16>, dim3(grid_for(nx)), dim3(256), 0, s, (const bf16*)p.dy, p.dYp, T, Tp, H * P, nx);
+    hipLaunchKernelGGL(pad_rows<bf16>, dim3(grid_for(nb)), dim3(256), 0, s, (const bf16*)p.B, p.Bp, T, Tp, G * N, nb);
+    hipLaunchKernelGGL(pad_rows<bf16>, dim3(grid_for(nb)), dim3(256), 0, s, (const bf16*)p.C, p.Cp, T, Tp, G * N, nb);
+  } else {
+    hipLaunchKernelGGL(pad_rows<float>, dim3(grid_for(nx)), dim3(256), 0, s, (const float*)p.x, p.Xp, T, Tp, H * P, nx);
+    hipLaunchKernelGGL(pad_rows<float>, dim3(grid_for(nx)), dim3(256), 0, s, (const float*)p.dy, p.dYp, T, Tp, H * P,
+                       nx);
+    hipLaunchKernelGGL(pad_rows<float>, dim3(grid_for(nb)), dim3(256), 0, s, (const float*)p.B, p.Bp, T, Tp, G * N, nb);
+    hipLaunchKernelGGL(pad_rows<float>, dim3(grid_for(nb)), dim3(256), 0, s, (const float*)p.C, p.Cp, T, Tp, G * N, nb);
+  }
+  const int64_t ng = bt * H * Tp;
+  hipLaunchKernelGGL(exp2_all, dim3(grid_for(ng)), dim3(256), 0, s, p.gcum, p.E, ng);
+  if (!ok(hipGetLastError())) return e;
+
+  // batch order of the chunk GEMMs: z = (b, k, h); tile bases
+  const int Bi = (int)bt, Ki = (int)nc, Hi = (int)H, Qi = (int)Q, Pi = (int)P, Ni = (int)N;
+  // x / dy tile (b, k, h): rows i at stride H P
+  const Operand X = op(p.Xp, H * P, 1, Tp * H * P, Q * H * P, P);
+  const Operand dY = op(p.dYp, H * P, 1, Tp * H * P, Q * H * P, P);
+  const Operand Bt = op(p.Bp, G * N, 1, Tp * G * N, Q * G * N, N, hpg);
+  const Operand Ct = op(p.Cp, G * N, 1, Tp * G * N, Q * G * N, N, hpg);
+  // per-(b, h, k) vectors over the chunk's tokens, [bt][H][Tp]
+  auto vec = [&](const float* v) { return op(v, 0, 0, H * Tp, Q, Tp); };
+  // per-(b, h, k) P x N blocks, [bt][H][nc][P][N], for the (b, k, h) batch order
+  auto blk = [&](const float* v, bool transposed) {
+    return transposed ? op(v, 1, N, H * nc * PN, PN, nc * PN) : op(v, N, 1, H * nc * PN, PN, nc * PN);
+  };
+
+  // 2. forward chunk states S = X^T diag(wst) B, then Hprev
+  ok(gemm(op(p.Xp, 1, H * P, Tp * H * P, Q * H * P, P), Bt, blk(p.S, false), none(), vec(p.wst), Pi, Ni, Qi, Bi, Ki,
+          Hi, 0.f, s));
+  const int64_t nst = bt * H * PN;
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(chunk_recursion, dim3(grid_for(nst)), dim3(256), 0, s, p.S, p.gcum, p.init, p.hprev,
+                       (float*)nullptr, nc, Tp, Q, PN, nst, 0);
+    ok(hipGetLastError());
+  }
+  // 3. dS = dY^T diag(E) C, then the reverse pass: dHn per chunk, dinit
+  ok(gemm(op(p.dYp, 1, H * P, Tp * H * P, Q * H * P, P), Ct, blk(p.S, false), none(), vec(p.E), Pi, Ni, Qi, Bi, Ki, Hi,
+          0.f, s));
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(chunk_recursion, dim3(grid_for(nst)), dim3(256), 0, s, p.S, p.gcum, p.dfinal, p.dhn, p.dinit,
+                       nc, Tp, Q, PN, nst, 1);
+    ok(hipGetLastError());
+  }
+  // 4. CB = C B^T per (b, k, g) and DX = dY X^T per (b, k, h)
+  ok(gemm(op(p.Cp, G * N, 1, Tp * G * N, Q * G * N, N), op(p.Bp, 1, G * N, Tp * G * N, Q * G * N, N),
+          op(p.CB, Q, 1, nc * G * QQ, G * QQ, QQ), none(), none(), Qi, Qi, Ni, Bi, Ki, (int)G, 0.f, s));
+  ok(gemm(dY, op(p.Xp, 1, H * P, Tp * H * P, Q * H * P, P), op(p.DX, Q, 1, nc * H * QQ, H * QQ, QQ), none(), none(), Qi,
+          Qi, Pi, Bi, Ki, Hi, 0.f, s));
+  // 5. masks, decays, and the sums for the time gradient
+  if (e == hipSuccess && bt * nc * H > 0) {
+    hipLaunchKernelGGL(mask_decay, dim3((unsigned)(bt * nc * H)), dim3(256), 0, s, p.CB, p.DX, p.W1, p.gcum, p.dtt,
+                       p.rowZ, p.colZ, p.colW, Qi, Hi, hpg, nc, Tp);
+    ok(hipGetLastError());
+  }
+  const Operand Wqq2 = op(p.DX, Q, 1, nc * H * QQ, H * QQ, QQ);
+  const Operand Wqq1T = op(p.W1, 1, Q, nc * H * QQ, H * QQ, QQ), Wqq2T = op(p.DX, 1, Q, nc * H * QQ, H * QQ, QQ);
+  const Operand Uo = op(p.U, P, 1, nc * H * Q * P, H * Q * P, Q * P), Vo = op(p.V, P, 1, nc * H * Q * P, H * Q * P, Q * P);
+  // 6. U = B dHn^T, V = C Hprev^T (rows j: dHn B_j, Hprev C_j)
+  ok(gemm(Bt, blk(p.dhn, true), Uo, none(), none(), Qi, Pi, Ni, Bi, Ki, Hi, 0.f, s));
+  ok(gemm(Ct, blk(p.hprev, true), Vo, none(), none(), Qi, Pi, Ni, Bi, Ki, Hi, 0.f, s));
+  // 7. dXp = W1s^T dY
+  ok(gemm(Wqq1T, dY, op(p.dXp, H * P, 1, Tp * H * P, Q * H * P, P), none(), none(), Qi, Pi, Qi, Bi, Ki, Hi, 0.f, s));
+  // 8. dB_h = W2s^T C + diag(w) X dHn;  dC_h = W2s B + diag(E) dY Hprev
+  const Operand dBo = op(p.dBh, H * N, 1, Tp * H * N, Q * H * N, N), dCo = op(p.dCh, H * N, 1, Tp * H * N, Q * H * N, N);
+  ok(gemm(Wqq2T, Ct, dBo, none(), none(), Qi, Ni, Qi, Bi, Ki, Hi, 0.f, s));
+  ok(gemm(X, blk(p.dhn, false), dBo, vec(p.wst), none(), Qi, Ni, Pi, Bi, Ki, Hi, 1.f, s));
+  ok(gemm(Wqq2, Bt, dCo, none(), none(), Qi, Ni, Qi, Bi, Ki, Hi, 0.f, s));
+  ok(gemm(dY, blk(p.hprev, false), dCo, vec(p.E), none(), Qi, Ni, Pi, Bi, Ki, Hi, 1.f, s));
+  // 9. dx, ddt and the dA / dD parts; then the group and head sums
+  if (e == hipSuccess && bt * nc * H > 0) {
+    hipLaunchKernelGGL(finish_chunk, dim3((unsigned)(bt * nc * H)), dim3(256), 0, s, p);
+    ok(hipGetLastError());
+  }
+  const int64_t nbo = bt * T * G * N;
+  if (e == hipSuccess && nbo > 0) {
+    hipLaunchKernelGGL(group_sum, dim3(grid_for(nbo)), dim3(256), 0, s, p.dBh, p.dB, T, Tp, Hi, (int)G, N, nbo);
+    hipLaunchKernelGGL(group_sum, dim3(grid_for(nbo)), dim3(256), 0, s, p.dCh, p.dC, T, Tp, Hi, (int)G, N, nbo);
+    ok(hipGetLastError());
+  }
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(head_sums, dim3((unsigned)((H + 255) / 256)), dim3(256), 0, s, p.dA_part, p.dD_part, p.dA,
+                       p.dD, bt, Hi, nc);
+    ok(hipGetLastError());
+  }
+  return e;
+}
+
+}  // namespace ssd

@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
         "mamba2_ssd_check_args", "mamba2_ssd_fwd", "mamba2_ssd_fwd_timed", "mamba2_ssd_fwd_workspace_bytes",
         "mamba2_ssd_last_hip_error", "mamba2_ssd_status_string", "mamba2_ssd_supported",
         "mamba2_ssd_workspace_layout_query", "mamba2_ssd_step", "mamba2_ssd_step_check_args",
-        "mamba2_ssd_step_supported", "mamba2_ssd_fused_state_pass"])
+        "mamba2_ssd_step_supported", "mamba2_ssd_fused_state_pass", "mamba2_ssd_bwd",
+        "mamba2_ssd_bwd_check_args", "mamba2_ssd_bwd_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -311,3 +312,71 @@ def test_fused_state_pass_query(monkeypatch):
     assert ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 256), BF16)
     assert not ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 128), BF16)       # chunk 128: not supported
     assert not ssd.fused_state_pass(HEADLINE, F32)
+
+
+# ------------------------------------------------------------- backward pass
+
+BWD_SMALL = Dims(2, 300, 8, 64, 128, 2, 128)
+
+
+def _bwd_ptrs(d, io):
+    """Disjoint fake addresses for every argument of mamba2_ssd_bwd."""
+    e = 2 if io == BF16 else 4
+    nx = d.batch * d.seqlen * d.nheads * d.headdim
+    nbc = d.batch * d.seqlen * d.ngroups * d.dstate
+    nst = d.batch * d.nheads * d.headdim * d.dstate
+    sizes = [("x", nx * e), ("dt", d.batch * d.seqlen * d.nheads * 4), ("A", d.nheads * 4), ("B", nbc * e),
+             ("C", nbc * e), ("D", d.nheads * 4), ("init", nst * 4), ("dy", nx * e), ("dfinal", nst * 4),
+             ("dx", nx * 4), ("ddt", d.batch * d.seqlen * d.nheads * 4), ("dA", d.nheads * 4), ("dB", nbc * 4),
+             ("dC", nbc * 4), ("dD", d.nheads * 4), ("dinit", nst * 4),
+             ("ws", max(ssd.bwd_workspace_bytes(d, io), 1))]
+    p, addr = {}, 1 << 40
+    for name, n in sizes:
+        p[name] = addr
+        addr += (n + 4095) // 4096 * 4096 + 4096
+    return p
+
+
+def _bwd_check(d, io, **over):
+    p = _bwd_ptrs(d, io)
+    p.update(over)
+    ws_bytes = over.get("ws_bytes", ssd.bwd_workspace_bytes(d, io))
+    return ssd.bwd_check_args(d, io, p["x"], p["dt"], p["A"], p["B"], p["C"], p["D"], p["init"], p["dy"],
+                              p["dfinal"], p["dx"], p["ddt"], p["dA"], p["dB"], p["dC"], p["dD"], p["dinit"],
+                              p["ws"], ws_bytes)
+
+
+def test_bwd_workspace_and_valid_call():
+    for io in (BF16, F32):
+        assert ssd.bwd_workspace_bytes(BWD_SMALL, io) > 0
+        assert _bwd_check(BWD_SMALL, io) == OK
+        assert _bwd_check(BWD_SMALL, io, init=0, dfinal=0, dinit=0) == OK
+    # the headline layer: about 12.6 GB of workspace
+    assert 12e9 < ssd.bwd_workspace_bytes(HEADLINE, BF16) < 13e9
+
+
+def test_bwd_rejects_bad_calls():
+    assert _bwd_check(BWD_SMALL, BF16 | ssd.DT_HEAD_MAJOR) == UNSUP
+    assert ssd.bwd_workspace_bytes(BWD_SMALL, BF16 | ssd.DT_HEAD_MAJOR) == 0
+    for name in ("x", "dt", "A", "B", "C", "D", "dy", "dx", "ddt", "dA", "dB", "dC", "dD"):
+        assert _bwd_check(BWD_SMALL, BF16, **{name: 0}) == NULLP, name
+    assert _bwd_check(BWD_SMALL, BF16, ws=0) == WS
+    assert _bwd_check(BWD_SMALL, BF16, ws_bytes=ssd.bwd_workspace_bytes(BWD_SMALL, BF16) - 1) == WS
+    p = _bwd_ptrs(BWD_SMALL, BF16)
+    # an output on an input, on another output, or on the workspace
+    assert _bwd_check(BWD_SMALL, BF16, dx=p["x"]) == ALIAS
+    assert _bwd_check(BWD_SMALL, BF16, dB=p["dC"]) == ALIAS
+    assert _bwd_check(BWD_SMALL, BF16, dinit=p["ws"]) == ALIAS
+    assert _bwd_check(BWD_SMALL, BF16, dinit=p["init"]) == ALIAS
+    # batch * nchunks * nheads beyond one grid dimension
+    big = Dims(64, 65536, 80, 64, 128, 1, 256)
+    assert ssd.bwd_workspace_bytes(big, BF16) == 0
+
+
+def test_bwd_fails_without_launching():
+    p = _bwd_ptrs(BWD_SMALL, BF16)
+    args = [p[k] for k in ("x", "dt", "A", "B", "C", "D", "init", "dy", "dfinal", "dx", "ddt", "dA", "dB", "dC",
+                           "dD", "dinit", "ws")]
+    args[0] = 0
+    with pytest.raises(ssd.SsdError):
+        ssd.ssd_bwd_ptr(BWD_SMALL, BF16, *args, ssd.bwd_workspace_bytes(BWD_SMALL, BF16))
