@@ -15,7 +15,8 @@ host's cores), whose outputs also check the benchmarked GPU output.
 
 With --config mamba2-2.7b-decode it times the one-token decode step instead
 (256 sequences of the same layer advanced by one token per step, the state
-updated in place), with the same JSON fields.
+updated in place), with the same JSON fields. With --bwd it times the
+backward pass (every input's gradient) on the layer instead.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
 """
@@ -225,6 +226,103 @@ def run_decode(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector, published
+
+
+def bwd_flops(cfg):
+    """Algorithmic flops of one backward call: the chunk-state-shaped
+    contractions (S, dS, B dHn^T, C Hprev^T, X dHn, dY Hprev: 2QPN each per
+    chunk and head), the causal Q x Q products (dY X^T, W1^T dY, W2^T C, W2 B:
+    Q(Q+1) times P or N each, the lower triangle only) and C B^T per chunk
+    and group."""
+    Bt, T, H, P, N, G, Q = cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk
+    nc = math.ceil(T / Q)
+    per_tile = 12 * Q * P * N + 2 * Q * (Q + 1) * (P + N)
+    return Bt * nc * H * per_tile + Bt * nc * G * Q * (Q + 1) * N
+
+
+def run_bwd(args, cfg):
+    """Times mamba2_ssd_bwd (every input's gradient) on the layer; prints one
+    JSON line of its own."""
+    import torch
+
+    import state_space_sequence_ssd_amd as ssd
+    from workloads import generate, round_to_bf16
+
+    dev = torch.device("cuda:0")
+    inp = generate(cfg)
+    rng = np.random.default_rng(cfg.seed + 1000)
+    dy = rng.standard_normal((cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim)).astype(np.float32)
+    dfin = rng.standard_normal((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate)).astype(np.float32)
+
+    def to_dev(k, a):
+        if cfg.io == "bf16" and k in ("x", "B", "C", "dy"):
+            bits = inp[k + "_bits"] if k != "dy" else round_to_bf16(a)[1]
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    t = {k: to_dev(k, inp[k]) for k in ("x", "B", "C", "dt", "A", "D")}
+    t["dy"] = to_dev("dy", dy)
+    t["dfinal"] = to_dev("dfinal", dfin)
+    init = None if inp["init_state"] is None else to_dev("init", inp["init_state"])
+    io = ssd.BF16 if cfg.io == "bf16" else ssd.F32
+    dims = ssd.Dims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk)
+    nbytes = ssd.bwd_workspace_bytes(dims, io)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = {"dx": torch.empty(tuple(t["x"].shape), **f32), "ddt": torch.empty(tuple(t["dt"].shape), **f32),
+         "dA": torch.empty((cfg.nheads,), **f32), "dB": torch.empty(tuple(t["B"].shape), **f32),
+         "dC": torch.empty(tuple(t["C"].shape), **f32), "dD": torch.empty((cfg.nheads,), **f32),
+         "dinit": torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), **f32)}
+    stream = torch.cuda.current_stream(dev)
+    ptr = lambda a: 0 if a is None else a.data_ptr()
+    args_ptrs = [ptr(t["x"]), ptr(t["dt"]), ptr(t["A"]), ptr(t["B"]), ptr(t["C"]), ptr(t["D"]), ptr(init),
+                 ptr(t["dy"]), ptr(t["dfinal"])] + [ptr(g[k]) for k in ssd.GRAD_NAMES] + [ptr(ws), nbytes]
+
+    def call():
+        ssd.ssd_bwd_ptr(dims, io, *args_ptrs, stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        call()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        call()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]))
+    flops = bwd_flops(cfg)
+    achieved = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": "SSD bwd tokens/sec at 2.7B-layer shape (1 GPU); % fp32 vector peak",
+        "value": round(cfg.tokens * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name + "-bwd", "batch": cfg.batch, "seqlen": cfg.seqlen, "nheads": cfg.nheads,
+                   "headdim": cfg.headdim, "dstate": cfg.dstate, "ngroups": cfg.ngroups, "chunk": cfg.chunk,
+                   "io": cfg.io, "seed": cfg.seed, "tokens_per_step": cfg.tokens},
+        "roofline": {"bound": "alu", "kernel": "whole backward call", "achieved": round(achieved, 2),
+                     "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP32_VALU_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "gpu_event_ms_per_step": round(ms, 4),
+        "alg_flops_per_step": int(flops),
+        "workspace_bytes": int(nbytes),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(cfg, inp, y_gpu, budget_s=10.0):
     """The chunked fp64 oracle, as it stands, on whole batch rows of the same
     layer until `budget_s` has elapsed; its outputs are checked against the
@@ -268,6 +366,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="mamba2-2.7b")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time the backward pass (mamba2_ssd_bwd) on the layer instead, one JSON line of its own")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy, a dispatch of known size that "
                          "HBM byte counters (FETCH_SIZE, WRITE_SIZE) can be scaled against")
@@ -288,6 +388,8 @@ def main():
     cfg = config_by_name(args.config)
     if cfg.seqlen == 1 and cfg.name.endswith("-decode"):
         return run_decode(args, cfg)
+    if args.bwd:
+        return run_bwd(args, cfg)
     dev = torch.device("cuda:0")
     inp = generate(cfg)
     io = ssd.BF16 if cfg.io == "bf16" else ssd.F32

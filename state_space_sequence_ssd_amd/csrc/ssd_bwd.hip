@@ -48,15 +48,22 @@ struct Operand {
   __device__ int64_t base(int z0, int z1, int z2) const { return z0 * s0 + z1 * s1 + (int64_t)(z2 / d2) * s2; }
 };
 
+// Causal shapes. The Q x Q blocks are used on and below the diagonal only:
+// kLowerOut computes only output tiles that reach it (the others are never
+// read), kKFromRow / kKToRow limit the contraction to k >= m (A upper
+// triangular, a transposed lower block) or k <= m (A lower triangular).
+enum : int { kFull = 0, kLowerOut = 1, kKFromRow = 2, kKToRow = 3 };
+
 struct GemmArgs {
   Operand a, b, c, rsc, ksc;   // rsc / ksc: only p, s0..s2, d2 used (unit stride vectors)
   int M, N, K, Z1, Z2;
   float beta;
+  int shape;
 };
 
 __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
-  __shared__ float sa[GK][GT + 4];
-  __shared__ float sb[GK][GT + 4];
+  __shared__ __attribute__((aligned(16))) float sa[GK][GT + 4];
+  __shared__ __attribute__((aligned(16))) float sb[GK][GT + 4];
   const int tiles_n = (g.N + GT - 1) / GT;
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
   const int z = blockIdx.y;
@@ -66,32 +73,36 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
   const float* ks = g.ksc.p ? g.ksc.p + g.ksc.base(z0, z1, z2) : nullptr;
   const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
   const int m0 = tm * GT, n0 = tn * GT;
+  if (g.shape == kLowerOut && n0 > m0 + GT - 1) return;   // wholly above the diagonal
+  const int kbeg = g.shape == kKFromRow ? m0 : 0;
+  const int kend = g.shape == kKToRow ? min(g.K, m0 + GT) : g.K;
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < g.K; k0 += GK) {
+  for (int k0 = kbeg; k0 < kend; k0 += GK) {
     // stage A (GT x GK, as [k][m]) and B (GK x GT, as [k][n]): 4 elements each per thread
+    // consecutive threads walk whichever index is contiguous in memory
+    const bool a_k_unit = g.a.cs == 1, b_n_unit = g.b.cs == 1;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int idx = tid + 256 * e;          // 0 .. 1023
-      const int kk = idx % GK, mm = idx / GK;  // A: consecutive threads walk k
+      const int kk = a_k_unit ? idx % GK : idx / GT, mm = a_k_unit ? idx / GK : idx % GT;
       const int m = m0 + mm, k = k0 + kk;
       float v = 0.f;
-      if (m < g.M && k < g.K) {
+      if (m < g.M && k < kend) {
         v = A[m * g.a.rs + k * g.a.cs];
         if (ks) v *= ks[k];
       }
       sa[kk][mm] = v;
-      const int nn = idx % GT, kb = idx / GT;  // B: consecutive threads walk n
+      const int nn = b_n_unit ? idx % GT : idx / GK, kb = b_n_unit ? idx / GT : idx % GK;
       const int n = n0 + nn, kq = k0 + kb;
-      sb[kb][nn] = (n < g.N && kq < g.K) ? B[kq * g.b.rs + n * g.b.cs] : 0.f;
+      sb[kb][nn] = (n < g.N && kq < kend) ? B[kq * g.b.rs + n * g.b.cs] : 0.f;
     }
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < GK; ++kk) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) av[i] = sa[kk][ty + 16 * i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) bv[j] = sb[kk][tx + 16 * j];
+      // this thread's 4 rows and 4 columns are consecutive: one 16-byte read each
+      const float4 a4 = *reinterpret_cast<const float4*>(&sa[kk][4 * ty]);
+      const float4 b4 = *reinterpret_cast<const float4*>(&sb[kk][4 * tx]);
+      const float av[4] = {a4.x, a4.y, a4.z, a4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -103,12 +114,12 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
   const float* rs = g.rsc.p ? g.rsc.p + g.rsc.base(z0, z1, z2) : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int m = m0 + ty + 16 * i;
+    const int m = m0 + 4 * ty + i;
     if (m >= g.M) continue;
     const float r = rs ? rs[m] : 1.f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int n = n0 + tx + 16 * j;
+      const int n = n0 + 4 * tx + j;
       if (n >= g.N) continue;
       float* cp = Cp + m * g.c.rs + n * g.c.cs;
       const float v = r * acc[i][j];
@@ -123,8 +134,8 @@ Operand op(const float* p, int64_t rs, int64_t cs, int64_t s0, int64_t s1, int64
 Operand none() { return Operand{nullptr, 0, 0, 0, 0, 0, 1}; }
 
 hipError_t gemm(const Operand& a, const Operand& b, const Operand& c, const Operand& rsc, const Operand& ksc,
-                int M, int N, int K, int Z0, int Z1, int Z2, float beta, hipStream_t s) {
-  GemmArgs g{a, b, c, rsc, ksc, M, N, K, Z1, Z2, beta};
+                int M, int N, int K, int Z0, int Z1, int Z2, float beta, hipStream_t s, int shape = kFull) {
+  GemmArgs g{a, b, c, rsc, ksc, M, N, K, Z1, Z2, beta, shape};
   const int64_t tiles = (int64_t)((M + GT - 1) / GT) * ((N + GT - 1) / GT);
   const int64_t Z = (int64_t)Z0 * Z1 * Z2;
   if (Z == 0 || tiles == 0) return hipSuccess;
@@ -179,7 +190,7 @@ __global__ void chunk_recursion(const float* __restrict__ S, const float* __rest
 // array) and W2s = L o DX o dt_j (over DX, in place), zero above the
 // diagonal, and the sums the time gradient needs: rows and columns of
 // Z = L o CB o DX o dt_j, and the columns of L o CB o DX. The row sums are
-// taken first, one thread per row, while DX is still intact; then one thread
+// taken first, one wave per row, while DX is still intact; then one thread
 // per column writes the blocks. Fixed summation orders: the result does not
 // depend on scheduling.
 __global__ __launch_bounds__(256) void mask_decay(const float* __restrict__ CB, float* __restrict__ DXW2,
@@ -200,13 +211,19 @@ __global__ __launch_bounds__(256) void mask_decay(const float* __restrict__ CB, 
     sd[i] = dtt[tb + i];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < Q; i += blockDim.x) {
-    float rz = 0.f;
-    for (int j = 0; j <= i; ++j) {
-      const int64_t o = (int64_t)i * Q + j;
-      rz += exp2_hw(sg[i] - sg[j]) * cb[o] * dx[o] * sd[j];
+  {
+    // row sums: one wave per row at a time, lanes across the row
+    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    for (int i = wave; i < Q; i += blockDim.x / 64) {
+      float rz = 0.f;
+      for (int j = lane; j <= i; j += 64) {
+        const int64_t o = (int64_t)i * Q + j;
+        rz += exp2_hw(sg[i] - sg[j]) * cb[o] * dx[o] * sd[j];
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off /= 2) rz += __shfl_xor(rz, off, 64);
+      if (lane == 0) rowZ[tb + i] = rz;
     }
-    rowZ[tb + i] = rz;
   }
   __syncthreads();   // every row has read DX before it is overwritten
   for (int j = threadIdx.x; j < Q; j += blockDim.x) {
@@ -234,14 +251,14 @@ __global__ __launch_bounds__(256) void mask_decay(const float* __restrict__ CB, 
 // Per (b, h, k), Q threads: dx (output), ddt (output), and this chunk's
 // parts of dA and dD. U = B dHn^T and V = C Hprev^T rows, dXp = W1s^T dY.
 __global__ __launch_bounds__(256) void finish_chunk(const BwdProblem p) {
-  __shared__ float s_dg[256], s_dt[256], s_red[256];
+  __shared__ float s_dg[256], s_dt[256], s_red[256], s_avec[256], s_bvec[256], s_ddx[256];
   __shared__ float s_scal[2];
   const int Q = (int)p.Q, P = (int)p.P, H = (int)p.H;
   const int h = blockIdx.x % H;
   const int64_t k = (blockIdx.x / H) % p.nc, b = blockIdx.x / (H * p.nc);
   const int i = threadIdx.x;
   const int64_t tb = (b * H + h) * p.Tp + k * Q;
-  const int64_t t = k * Q + i;   // token index
+  const int64_t t = k * Q + i;   // this thread's token in the per-token steps
   const int64_t PN = p.P * p.N;
   const float* Hp = p.hprev + ((b * H + h) * p.nc + k) * PN;
   const float* dHn = p.dhn + ((b * H + h) * p.nc + k) * PN;
@@ -257,22 +274,46 @@ __global__ __launch_bounds__(256) void finish_chunk(const BwdProblem p) {
   if (i == 0) s_scal[0] = s_red[0];
   __syncthreads();
 
+  // per-row dot products over headdim, one wave per row at a time with its
+  // lanes across the row (whole-row reads), and dx written on the way
+  {
+    const int wave = i / 64, lane = i % 64;
+    const float D = p.D[h];
+    for (int r = wave; r < Q; r += blockDim.x / 64) {
+      const int64_t tr = k * Q + r;
+      const int64_t row = ((b * p.Tp + tr) * H + h) * P;           // [bt][Tp][H][P] rows
+      const int64_t urow = (((b * p.nc + k) * H + h) * Q + r) * P;  // [bt][nc][H][Q][P] rows
+      const float wr = p.wst[tb + r];
+      float a = 0.f, bb = 0.f, dd = 0.f;
+      for (int q = lane; q < P; q += 64) {
+        const float xv = p.Xp[row + q], dyv = p.dYp[row + q], u = p.U[urow + q];
+        a += dyv * p.V[urow + q];
+        bb += xv * u;
+        dd += dyv * xv;
+        if (tr < p.T) p.dx[((b * p.T + tr) * H + h) * P + q] = p.dXp[row + q] + wr * u + D * dyv;
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off /= 2) {
+        a += __shfl_xor(a, off, 64);
+        bb += __shfl_xor(bb, off, 64);
+        dd += __shfl_xor(dd, off, 64);
+      }
+      if (lane == 0) {
+        s_avec[r] = a;
+        s_bvec[r] = bb;
+        s_ddx[r] = dd;
+      }
+    }
+  }
+  __syncthreads();
   float bvec = 0.f, dterm = 0.f, gi = 0.f, wi = 0.f;
   if (i < Q) {
-    const int64_t row = ((b * p.Tp + t) * H + h) * P;           // [bt][Tp][H][P] rows
-    const int64_t urow = (((b * p.nc + k) * H + h) * Q + i) * P;  // [bt][nc][H][Q][P] rows
-    const float D = p.D[h], E = p.E[tb + i];
+    const float E = p.E[tb + i];
     wi = p.wst[tb + i];
     gi = p.gcum[tb + i];
-    float avec = 0.f, dd = 0.f;
-    for (int q = 0; q < P; ++q) {
-      const float xv = p.Xp[row + q], dyv = p.dYp[row + q], u = p.U[urow + q];
-      avec += dyv * p.V[urow + q];
-      bvec += xv * u;
-      dd += dyv * xv;
-      if (t < p.T) p.dx[((b * p.T + t) * H + h) * P + q] = p.dXp[row + q] + wi * u + D * dyv;
-    }
-    dterm = dd;
+    const float avec = s_avec[i];
+    bvec = s_bvec[i];
+    dterm = s_ddx[i];
     s_dg[i] = E * avec + p.rowZ[tb + i] - p.colZ[tb + i] - wi * bvec;
     s_dt[i] = p.dtt[tb + i];
   }
@@ -452,9 +493,9 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
   }
   // 4. CB = C B^T per (b, k, g) and DX = dY X^T per (b, k, h)
   ok(gemm(op(p.Cp, G * N, 1, Tp * G * N, Q * G * N, N), op(p.Bp, 1, G * N, Tp * G * N, Q * G * N, N),
-          op(p.CB, Q, 1, nc * G * QQ, G * QQ, QQ), none(), none(), Qi, Qi, Ni, Bi, Ki, (int)G, 0.f, s));
+          op(p.CB, Q, 1, nc * G * QQ, G * QQ, QQ), none(), none(), Qi, Qi, Ni, Bi, Ki, (int)G, 0.f, s, kLowerOut));
   ok(gemm(dY, op(p.Xp, 1, H * P, Tp * H * P, Q * H * P, P), op(p.DX, Q, 1, nc * H * QQ, H * QQ, QQ), none(), none(), Qi,
-          Qi, Pi, Bi, Ki, Hi, 0.f, s));
+          Qi, Pi, Bi, Ki, Hi, 0.f, s, kLowerOut));
   // 5. masks, decays, and the sums for the time gradient
   if (e == hipSuccess && bt * nc * H > 0) {
     hipLaunchKernelGGL(mask_decay, dim3((unsigned)(bt * nc * H)), dim3(256), 0, s, p.CB, p.DX, p.W1, p.gcum, p.dtt,
@@ -468,12 +509,13 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
   ok(gemm(Bt, blk(p.dhn, true), Uo, none(), none(), Qi, Pi, Ni, Bi, Ki, Hi, 0.f, s));
   ok(gemm(Ct, blk(p.hprev, true), Vo, none(), none(), Qi, Pi, Ni, Bi, Ki, Hi, 0.f, s));
   // 7. dXp = W1s^T dY
-  ok(gemm(Wqq1T, dY, op(p.dXp, H * P, 1, Tp * H * P, Q * H * P, P), none(), none(), Qi, Pi, Qi, Bi, Ki, Hi, 0.f, s));
+  ok(gemm(Wqq1T, dY, op(p.dXp, H * P, 1, Tp * H * P, Q * H * P, P), none(), none(), Qi, Pi, Qi, Bi, Ki, Hi, 0.f, s,
+          kKFromRow));
   // 8. dB_h = W2s^T C + diag(w) X dHn;  dC_h = W2s B + diag(E) dY Hprev
   const Operand dBo = op(p.dBh, H * N, 1, Tp * H * N, Q * H * N, N), dCo = op(p.dCh, H * N, 1, Tp * H * N, Q * H * N, N);
-  ok(gemm(Wqq2T, Ct, dBo, none(), none(), Qi, Ni, Qi, Bi, Ki, Hi, 0.f, s));
+  ok(gemm(Wqq2T, Ct, dBo, none(), none(), Qi, Ni, Qi, Bi, Ki, Hi, 0.f, s, kKFromRow));
   ok(gemm(X, blk(p.dhn, false), dBo, vec(p.wst), none(), Qi, Ni, Pi, Bi, Ki, Hi, 1.f, s));
-  ok(gemm(Wqq2, Bt, dCo, none(), none(), Qi, Ni, Qi, Bi, Ki, Hi, 0.f, s));
+  ok(gemm(Wqq2, Bt, dCo, none(), none(), Qi, Ni, Qi, Bi, Ki, Hi, 0.f, s, kKToRow));
   ok(gemm(dY, blk(p.hprev, false), dCo, vec(p.E), none(), Qi, Ni, Pi, Bi, Ki, Hi, 1.f, s));
   // 9. dx, ddt and the dA / dD parts; then the group and head sums
   if (e == hipSuccess && bt * nc * H > 0) {

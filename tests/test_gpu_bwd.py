@@ -5,7 +5,10 @@ Tolerance: every gradient is computed in fp32 (bf16 inputs are exact in
 fp32), so each is compared normwise, max|g - g_ref| / max|g_ref| <= 1e-4 per
 tensor. The longest fp32 sums are over a chunk's tokens times headdim or
 dstate (up to 256 * 256 terms): sqrt(65536) * 2^-24 is about 1.5e-5; the
-time gradient also subtracts row and column sums of the same blocks.
+time gradient also subtracts row and column sums of the same blocks. dA is
+one number per head summed over every token of every batch row from those
+time gradients (32768 tokens at the 2.7B-like size), and partly cancels: it
+gets 5e-4.
 """
 import numpy as np
 import pytest
@@ -19,6 +22,7 @@ from workloads import LayerConfig, config_by_name, generate
 pytestmark = pytest.mark.gpu
 
 BWD_TOL = 1e-4
+TOL = {"dA": 5e-4}
 
 CASES = {
     "tiny-f32": config_by_name("tiny"),
@@ -63,7 +67,8 @@ def _check(g, ref, what=""):
         den = max(float(np.max(np.abs(want))), 1e-30) if want.size else 1.0
         rel = float(np.max(np.abs(got - want))) / den if want.size else 0.0
         out.append(f"{k} {rel:.1e}")
-        assert rel <= BWD_TOL, f"{what} {k}: normwise relative error {rel:.3e} > {BWD_TOL}"
+        tol = TOL.get(k, BWD_TOL)
+        assert rel <= tol, f"{what} {k}: normwise relative error {rel:.3e} > {tol}"
     return ", ".join(out)
 
 
@@ -112,3 +117,28 @@ def test_bwd_is_deterministic():
     g2 = _run(cfg, inp, dy, dfin)
     for k in ssd.GRAD_NAMES:
         assert torch.equal(g1[k], g2[k]), f"{k} differs between two identical calls"
+
+
+def test_bwd_headline_sampled_heads():
+    """The 2.7B-like layer at full size, as bench.py --bwd runs it: the
+    per-head gradients (dx, ddt, dinit, dA, dD) of two sampled heads against
+    the oracle run on those heads alone (with one group, dB and dC sum over
+    all 80 heads; they are covered by the smaller cases)."""
+    cfg = config_by_name("mamba2-2.7b").with_shape(init_sigma=0.2)
+    log(f"[bwd] headline {cfg}")
+    inp = generate(cfg)
+    dy, dfin = _upstream(cfg, seed=11)
+    g = _run(cfg, inp, dy, dfin)
+    for h in (7, 61):
+        sl = [h]
+        ref = ssd_bwd_chunked(inp["x"][:, :, sl], inp["dt"][:, :, sl], inp["A"][sl], inp["B"], inp["C"],
+                              inp["D"][sl], dy[:, :, sl], cfg.chunk, inp["init_state"][:, sl], dfin[:, sl])
+        sub = {"dx": g["dx"][:, :, sl], "ddt": g["ddt"][:, :, sl], "dinit": g["dinit"][:, sl],
+               "dA": g["dA"][sl], "dD": g["dD"][sl]}
+        msg = []
+        for k, v in sub.items():
+            got, want = host(v), np.asarray(ref[k], dtype=np.float64)
+            rel = float(np.max(np.abs(got - want))) / max(float(np.max(np.abs(want))), 1e-30)
+            msg.append(f"{k} {rel:.1e}")
+            assert rel <= TOL.get(k, BWD_TOL), f"head {h} {k}: normwise relative error {rel:.3e}"
+        log(f"  head {h}: " + ", ".join(msg))
