@@ -16,7 +16,9 @@ host's cores), whose outputs also check the benchmarked GPU output.
 With --config mamba2-2.7b-decode it times the one-token decode step instead
 (256 sequences of the same layer advanced by one token per step, the state
 updated in place), with the same JSON fields. With --bwd it times the
-backward pass (every input's gradient) on the layer instead.
+backward pass (every input's gradient) on the layer instead. With
+--config s6-page (or another s6-* shape) it times the Mamba-1 selective
+scan on that shape.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
 """
@@ -323,6 +325,90 @@ def run_bwd(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def run_s6(args, cfg):
+    """Times the Mamba-1 selective scan (mamba1_s6_fwd) on one of the S6
+    shapes; one JSON line of its own."""
+    import torch
+
+    import state_space_sequence_ssd_amd as ssd
+    from workloads import generate_s6
+
+    dev = torch.device("cuda:0")
+    inp = generate_s6(cfg)
+    if args.copy_calibration:
+        copy_calibration(dev)
+    t = {k: None if v is None else torch.from_numpy(np.ascontiguousarray(v)).to(dev) for k, v in inp.items()}
+    y = torch.empty_like(t["x"])
+    hT = torch.empty((cfg.batch, cfg.channels, cfg.dstate), dtype=torch.float32, device=dev)
+    dims = ssd.S6Dims(cfg.batch, cfg.seqlen, cfg.channels, cfg.dstate)
+    nbytes_ws = ssd.s6_workspace_bytes(dims)
+    ws = torch.empty(max(nbytes_ws, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ptr = lambda a: 0 if a is None else a.data_ptr()
+    ptrs = [ptr(t[k]) for k in ("x", "delta", "A", "B", "C", "h0")] + [y.data_ptr(), hT.data_ptr(), ws.data_ptr(),
+                                                                      ws.numel()]
+
+    def call():
+        ssd.s6_fwd_ptr(dims, *ptrs, stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        call()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        call()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])) * 1e3
+    Bt, L, D, N = cfg.batch, cfg.seqlen, cfg.channels, cfg.dstate
+    alg = 3 * Bt * D * L * 4 + 2 * Bt * N * L * 4 + D * N * 4 + (Bt * D * N * 4) * (2 if cfg.h0_sigma else 1)
+    achieved = alg / (us * 1e-6) / 1e9
+    out = {
+        "metric": "Mamba-1 selective scan (S6) tokens/sec (1 GPU); % HBM BW",
+        "value": round(cfg.tokens * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "batch": Bt, "seqlen": L, "channels": D, "dstate": N,
+                   "recipe": cfg.recipe, "seed": cfg.seed, "tokens_per_step": cfg.tokens},
+        "roofline": {"bound": "hbm", "kernel": "mamba1_s6_fwd (chunk scan, carry, chunk scan)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "gpu_event_us_per_step": round(us, 2),
+        "alg_bytes_per_step": int(alg),
+    }
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import s6_sequential
+
+        cores = len(os.sched_getaffinity(0))
+        threads = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+        yg = y.cpu().numpy()
+        with threadpool_limits(limits=threads, user_api="blas"):
+            t0 = time.perf_counter()
+            yr, _ = s6_sequential(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["h0"])
+            elapsed = time.perf_counter() - t0
+        rel = float(np.max(np.abs(yg - yr))) / max(float(np.max(np.abs(yr))), 1e-30)
+        out["cpu_baseline"] = {"value": cfg.tokens / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"fp64 S6 oracle on the whole call ({Bt} batch rows, {D} channels), "
+                                         f"{elapsed:.1f} s", "seconds": elapsed}
+        out["parity_vs_oracle"] = {"rows_checked": Bt, "normwise_rel_err": rel, "ok": rel <= 1e-5}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(cfg, inp, y_gpu, budget_s=10.0):
     """The chunked fp64 oracle, as it stands, on whole batch rows of the same
     layer until `budget_s` has elapsed; its outputs are checked against the
@@ -385,6 +471,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.config.startswith("s6-"):
+        from workloads import s6_config_by_name
+        return run_s6(args, s6_config_by_name(args.config))
     cfg = config_by_name(args.config)
     if cfg.seqlen == 1 and cfg.name.endswith("-decode"):
         return run_decode(args, cfg)

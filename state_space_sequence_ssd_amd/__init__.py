@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 from typing import Optional, Tuple
 
-from ._lib import (BF16, DT_HEAD_MAJOR, F32, STATUS, Dims, SsdError, StepDims, WorkspaceLayout, lib,
+from ._lib import (BF16, DT_HEAD_MAJOR, F32, STATUS, Dims, S6Dims, SsdError, StepDims, WorkspaceLayout, lib,
                    status_string)
 
 __all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_layout", "check_args",
@@ -24,7 +24,9 @@ __all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_
            "mamba2_ssd_step", "mamba2_ssd_step_check_args", "mamba2_ssd_step_supported",
            "mamba2_ssd_fused_state_pass", "fused_state_pass",
            "ssd_bwd", "ssd_bwd_ptr", "bwd_workspace_bytes", "bwd_check_args",
-           "mamba2_ssd_bwd", "mamba2_ssd_bwd_check_args", "mamba2_ssd_bwd_workspace_bytes"]
+           "mamba2_ssd_bwd", "mamba2_ssd_bwd_check_args", "mamba2_ssd_bwd_workspace_bytes",
+           "S6Dims", "s6_fwd", "s6_fwd_ptr", "s6_supported", "s6_workspace_bytes", "s6_check_args",
+           "mamba1_s6_fwd", "mamba1_s6_check_args", "mamba1_s6_supported", "mamba1_s6_workspace_bytes"]
 
 # The C entry points under their own names (ctypes functions with prototypes).
 mamba2_ssd_fwd = lib.mamba2_ssd_fwd
@@ -40,6 +42,10 @@ mamba2_ssd_step = lib.mamba2_ssd_step
 mamba2_ssd_step_check_args = lib.mamba2_ssd_step_check_args
 mamba2_ssd_step_supported = lib.mamba2_ssd_step_supported
 mamba2_ssd_bwd = lib.mamba2_ssd_bwd
+mamba1_s6_fwd = lib.mamba1_s6_fwd
+mamba1_s6_check_args = lib.mamba1_s6_check_args
+mamba1_s6_supported = lib.mamba1_s6_supported
+mamba1_s6_workspace_bytes = lib.mamba1_s6_workspace_bytes
 mamba2_ssd_bwd_check_args = lib.mamba2_ssd_bwd_check_args
 mamba2_ssd_bwd_workspace_bytes = lib.mamba2_ssd_bwd_workspace_bytes
 
@@ -286,3 +292,62 @@ def ssd_bwd(x, dt, A, B, C, D, dy, chunk: int, init_state=None, dfinal=None, *, 
         ssd_bwd_ptr(dims, io, ptr(x), ptr(dt), ptr(A), ptr(B), ptr(C), ptr(D), ptr(init_state), ptr(dy),
                     ptr(dfinal), *[ptr(g[k]) for k in GRAD_NAMES], ptr(workspace), workspace.numel(), stream)
     return g
+
+
+# ----------------------------------------------------- Mamba-1 selective scan
+
+def _s6_dims(d) -> S6Dims:
+    if isinstance(d, S6Dims):
+        return d
+    if isinstance(d, dict):
+        return S6Dims(**d)
+    return S6Dims(*d)
+
+
+def s6_supported(dstate: int) -> bool:
+    return bool(lib.mamba1_s6_supported(dstate))
+
+
+def s6_workspace_bytes(dims) -> int:
+    return int(lib.mamba1_s6_workspace_bytes(ctypes.byref(_s6_dims(dims))))
+
+
+def s6_check_args(dims, x, delta, A, B, C, h0, y, hT, workspace, ws_bytes) -> int:
+    """Host-only validation of a selective-scan call on raw addresses (0 for NULL)."""
+    return int(lib.mamba1_s6_check_args(ctypes.byref(_s6_dims(dims)), x, delta, A, B, C, h0, y, hT, workspace,
+                                        ws_bytes))
+
+
+def s6_fwd_ptr(dims, x, delta, A, B, C, h0, y, hT, workspace, ws_bytes, stream: int = 0) -> None:
+    """mamba1_s6_fwd on raw device addresses; raises SsdError on a nonzero status."""
+    st = lib.mamba1_s6_fwd(ctypes.byref(_s6_dims(dims)), x, delta, A, B, C, h0, y, hT, workspace, ws_bytes, stream)
+    if st != 0:
+        raise SsdError(st)
+
+
+def s6_fwd(x, delta, A, B, C, h0=None, *, return_final_state: bool = True, workspace=None):
+    """The Mamba-1 selective scan on float32 CUDA tensors: x, delta
+    [batch, channels, seqlen], A [channels, dstate], B, C [batch, dstate,
+    seqlen], h0 [batch, channels, dstate] or None. Returns ``(y, hT)``."""
+    import torch
+
+    for t in (x, delta, A, B, C, h0):
+        if t is not None and (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("all tensors must be contiguous float32 GPU tensors")
+    bt, D, L = x.shape
+    N = A.shape[1]
+    if tuple(delta.shape) != (bt, D, L) or tuple(A.shape) != (D, N) or tuple(B.shape) != (bt, N, L) \
+            or tuple(C.shape) != (bt, N, L) or (h0 is not None and tuple(h0.shape) != (bt, D, N)):
+        raise ValueError("inconsistent shapes")
+    dims = S6Dims(bt, L, D, N)
+    y = torch.empty_like(x)
+    hT = torch.empty((bt, D, N), dtype=torch.float32, device=x.device) if return_final_state else None
+    nbytes = s6_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    ptr = lambda t: 0 if t is None else t.data_ptr()
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        s6_fwd_ptr(dims, ptr(x), ptr(delta), ptr(A), ptr(B), ptr(C), ptr(h0), ptr(y), ptr(hT), ptr(workspace),
+                   workspace.numel(), stream)
+    return y, hT

@@ -35,6 +35,11 @@ class StepDims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("batch", "nheads", "headdim", "dstate", "ngroups")]
 
 
+class S6Dims(ctypes.Structure):
+    """mamba1_s6_dims"""
+    _fields_ = [(n, ctypes.c_int64) for n in ("batch", "seqlen", "channels", "dstate")]
+
+
 class WorkspaceLayout(ctypes.Structure):
     """mamba2_ssd_workspace_layout"""
     _fields_ = [("total_bytes", ctypes.c_size_t), ("gcum_offset", ctypes.c_size_t),
@@ -94,6 +99,15 @@ def _load():
     L.mamba2_ssd_bwd.argtypes = [dims_p, ctypes.c_int, vp, fp, fp, vp, vp, fp, fp, vp, fp,
                                  fp, fp, fp, fp, fp, fp, fp, vp, sz, vp]
     L.mamba2_ssd_bwd.restype = ctypes.c_int
+    s6_p = ctypes.POINTER(S6Dims)
+    L.mamba1_s6_supported.argtypes = [i64]
+    L.mamba1_s6_supported.restype = ctypes.c_int
+    L.mamba1_s6_workspace_bytes.argtypes = [s6_p]
+    L.mamba1_s6_workspace_bytes.restype = sz
+    L.mamba1_s6_check_args.argtypes = [s6_p, fp, fp, fp, fp, fp, fp, fp, fp, vp, sz]
+    L.mamba1_s6_check_args.restype = ctypes.c_int
+    L.mamba1_s6_fwd.argtypes = [s6_p, fp, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp]
+    L.mamba1_s6_fwd.restype = ctypes.c_int
     step_p = ctypes.POINTER(StepDims)
     L.mamba2_ssd_step_supported.argtypes = [i64, ctypes.c_int]
     L.mamba2_ssd_step_supported.restype = ctypes.c_int

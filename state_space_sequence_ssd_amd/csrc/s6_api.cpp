@@ -1,0 +1,115 @@
+// C ABI of the selective scan (include/mamba1_s6.h): host-side validation,
+// workspace carve-up and launch.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "mamba1_s6.h"
+#include "mamba2_ssd.h"
+#include "s6_launch.h"
+
+namespace {
+
+constexpr int64_t kMaxDimS6 = (int64_t)1 << 40;
+
+struct S6Sizes {
+  int64_t nc = 0, n_x = 0, n_bc = 0, n_state = 0;
+  size_t off_sumd = 0, off_hin = 0, total = 0;
+};
+
+size_t align_up(size_t v) { return (v + 255) / 256 * 256; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+int s6_sizes(const mamba1_s6_dims* d, S6Sizes* s) {
+  if (!d) return MAMBA2_SSD_ERR_NULL_POINTER;
+  if (d->batch < 0 || d->seqlen < 0 || d->channels <= 0 || d->dstate <= 0) return MAMBA2_SSD_ERR_BAD_DIM;
+  if (d->batch > kMaxDimS6 || d->seqlen > kMaxDimS6 || d->channels > kMaxDimS6) return MAMBA2_SSD_ERR_BAD_DIM;
+  if (!ssd::s6_has(d->dstate)) return MAMBA2_SSD_ERR_UNSUPPORTED;
+  S6Sizes r;
+  const int64_t q = ssd::s6_chunk_tokens();
+  r.nc = (d->seqlen + q - 1) / q;
+  if (d->batch > 65535 || r.nc > 65535 || d->channels > INT32_MAX - 256) return MAMBA2_SSD_ERR_BAD_DIM;
+  int64_t bd, t;
+  if (!mul_ok(d->batch, d->channels, &bd) || !mul_ok(bd, d->seqlen, &r.n_x)) return MAMBA2_SSD_ERR_BAD_DIM;
+  if (!mul_ok(d->batch, d->dstate, &t) || !mul_ok(t, d->seqlen, &r.n_bc)) return MAMBA2_SSD_ERR_BAD_DIM;
+  if (!mul_ok(bd, d->dstate, &r.n_state)) return MAMBA2_SSD_ERR_BAD_DIM;
+  int64_t ns, nsum;
+  if (!mul_ok(r.n_state, r.nc, &ns) || !mul_ok(bd, r.nc, &nsum) || !mul_ok(ns, 8, &t)) return MAMBA2_SSD_ERR_BAD_DIM;
+  r.off_sumd = align_up((size_t)ns * 4);
+  r.off_hin = r.off_sumd + align_up((size_t)nsum * 4);
+  r.total = r.off_hin + align_up((size_t)ns * 4);
+  *s = r;
+  return MAMBA2_SSD_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+};
+Range range_of(const void* p, size_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, p ? a + bytes : a};
+}
+bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+}  // namespace
+
+extern "C" {
+
+int mamba1_s6_supported(int64_t dstate) { return ssd::s6_has(dstate) ? 1 : 0; }
+
+size_t mamba1_s6_workspace_bytes(const mamba1_s6_dims* dims) {
+  S6Sizes s;
+  return s6_sizes(dims, &s) == MAMBA2_SSD_OK ? s.total : 0;
+}
+
+int mamba1_s6_check_args(const mamba1_s6_dims* d, const float* x, const float* delta, const float* A,
+                         const float* B, const float* C, const float* h0, const float* y, const float* hT,
+                         const void* workspace, size_t workspace_bytes) {
+  S6Sizes s;
+  const int st = s6_sizes(d, &s);
+  if (st != MAMBA2_SSD_OK) return st;
+  if (!A) return MAMBA2_SSD_ERR_NULL_POINTER;
+  if (s.n_x > 0 && (!x || !delta || !B || !C || !y)) return MAMBA2_SSD_ERR_NULL_POINTER;
+  const bool work = d->batch > 0;
+  if (work && s.total > 0 && (!workspace || workspace_bytes < s.total)) return MAMBA2_SSD_ERR_WORKSPACE;
+  const Range rx = range_of(x, (size_t)s.n_x * 4), rd = range_of(delta, (size_t)s.n_x * 4);
+  const Range rA = range_of(A, (size_t)(d->channels * d->dstate) * 4);
+  const Range rB = range_of(B, (size_t)s.n_bc * 4), rC = range_of(C, (size_t)s.n_bc * 4);
+  const Range rh0 = range_of(h0, (size_t)s.n_state * 4), ry = range_of(y, (size_t)s.n_x * 4);
+  const Range rhT = range_of(hT, (size_t)s.n_state * 4), rws = range_of(workspace, work ? s.total : 0);
+  for (const Range& r : {rx, rd, rA, rB, rC}) {
+    if (overlap(ry, r) || overlap(rhT, r) || overlap(rws, r)) return MAMBA2_SSD_ERR_ALIAS;
+  }
+  if (overlap(ry, rh0) || overlap(rws, rh0) || overlap(ry, rhT) || overlap(ry, rws) || overlap(rhT, rws))
+    return MAMBA2_SSD_ERR_ALIAS;
+  // hT may be exactly h0 (an in-place state update), never a partial overlap
+  if (overlap(rhT, rh0) && !(rhT.lo == rh0.lo && rhT.hi == rh0.hi)) return MAMBA2_SSD_ERR_ALIAS;
+  return MAMBA2_SSD_OK;
+}
+
+int mamba1_s6_fwd(const mamba1_s6_dims* d, const float* x, const float* delta, const float* A, const float* B,
+                  const float* C, const float* h0, float* y, float* hT, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+  const int st = mamba1_s6_check_args(d, x, delta, A, B, C, h0, y, hT, workspace, workspace_bytes);
+  if (st != MAMBA2_SSD_OK) return st;
+  if (d->batch == 0) return MAMBA2_SSD_OK;
+  S6Sizes s;
+  s6_sizes(d, &s);
+  char* ws = static_cast<char*>(workspace);
+  ssd::S6Problem p{};
+  p.bt = d->batch; p.L = d->seqlen; p.D = d->channels; p.N = d->dstate;
+  p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.h0 = h0; p.y = y; p.hT = hT;
+  p.S = ws ? reinterpret_cast<float*>(ws) : nullptr;
+  p.sumd = ws ? reinterpret_cast<float*>(ws + s.off_sumd) : nullptr;
+  p.hin = ws ? reinterpret_cast<float*>(ws + s.off_hin) : nullptr;
+  const hipError_t err = ssd::launch_s6(p, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MAMBA2_SSD_OK : MAMBA2_SSD_ERR_HIP;
+}
+
+}  // extern "C"

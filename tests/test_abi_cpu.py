@@ -20,10 +20,15 @@ OK, NULLP, BAD_DIM, GROUPS, CHUNK, UNSUP, WS, ALIAS = 0, -1, -2, -3, -4, -5, -6,
 ALIGN = -9
 
 
+HEADERS = [HEADER, os.path.join(ROOT, "include", "mamba1_s6.h")]
+
+
 def declared_functions():
-    txt = open(HEADER).read()
-    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(mamba2_ssd_\w+)\s*\(", txt)))
+    names = set()
+    for path in HEADERS:
+        txt = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"\b(mamba[12]_(?:ssd|s6)_\w+)\s*\(", txt))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
@@ -32,7 +37,8 @@ def test_header_declares_the_entry_points():
         "mamba2_ssd_last_hip_error", "mamba2_ssd_status_string", "mamba2_ssd_supported",
         "mamba2_ssd_workspace_layout_query", "mamba2_ssd_step", "mamba2_ssd_step_check_args",
         "mamba2_ssd_step_supported", "mamba2_ssd_fused_state_pass", "mamba2_ssd_bwd",
-        "mamba2_ssd_bwd_check_args", "mamba2_ssd_bwd_workspace_bytes"])
+        "mamba2_ssd_bwd_check_args", "mamba2_ssd_bwd_workspace_bytes", "mamba1_s6_fwd", "mamba1_s6_check_args",
+        "mamba1_s6_supported", "mamba1_s6_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -380,3 +386,53 @@ def test_bwd_fails_without_launching():
     args[0] = 0
     with pytest.raises(ssd.SsdError):
         ssd.ssd_bwd_ptr(BWD_SMALL, BF16, *args, ssd.bwd_workspace_bytes(BWD_SMALL, BF16))
+
+
+# ----------------------------------------------------- selective scan (S6)
+
+S6_SMALL = ssd.S6Dims(2, 300, 96, 16)
+
+
+def _s6_ptrs(d):
+    sizes = [("x", d.batch * d.channels * d.seqlen * 4), ("delta", d.batch * d.channels * d.seqlen * 4),
+             ("A", d.channels * d.dstate * 4), ("B", d.batch * d.dstate * d.seqlen * 4),
+             ("C", d.batch * d.dstate * d.seqlen * 4), ("h0", d.batch * d.channels * d.dstate * 4),
+             ("y", d.batch * d.channels * d.seqlen * 4), ("hT", d.batch * d.channels * d.dstate * 4),
+             ("ws", max(ssd.s6_workspace_bytes(d), 1))]
+    p, addr = {}, 1 << 40
+    for name, n in sizes:
+        p[name] = addr
+        addr += (n + 4095) // 4096 * 4096 + 4096
+    return p
+
+
+def _s6_check(d, **over):
+    p = _s6_ptrs(d)
+    p.update(over)
+    wsb = over.get("ws_bytes", ssd.s6_workspace_bytes(d))
+    return ssd.s6_check_args(d, p["x"], p["delta"], p["A"], p["B"], p["C"], p["h0"], p["y"], p["hT"], p["ws"], wsb)
+
+
+def test_s6_supported_and_workspace():
+    assert [n for n in range(1, 33) if ssd.s6_supported(n)] == [1, 2, 4, 8, 16]
+    # per (b, d, chunk): the chunk's end state and entering state (N floats each) and its delta sum
+    nc = (300 + 63) // 64
+    want = sum((n * 4 + 255) // 256 * 256 for n in (2 * 96 * nc * 16, 2 * 96 * nc, 2 * 96 * nc * 16))
+    assert ssd.s6_workspace_bytes(S6_SMALL) == want
+
+
+def test_s6_validation():
+    assert _s6_check(S6_SMALL) == OK
+    assert _s6_check(S6_SMALL, h0=0, hT=0) == OK
+    for name in ("x", "delta", "A", "B", "C", "y"):
+        assert _s6_check(S6_SMALL, **{name: 0}) == NULLP, name
+    p = _s6_ptrs(S6_SMALL)
+    assert _s6_check(S6_SMALL, y=p["x"]) == ALIAS
+    assert _s6_check(S6_SMALL, hT=p["h0"]) == OK          # in place
+    assert _s6_check(S6_SMALL, hT=p["h0"] + 4) == ALIAS   # partial overlap
+    assert _s6_check(S6_SMALL, ws=0) == WS
+    bad = ssd.S6Dims(2, 300, 96, 12)
+    assert ssd.s6_workspace_bytes(bad) == 0 and _s6_check(bad) == UNSUP
+    assert ssd.s6_workspace_bytes(ssd.S6Dims(70000, 10, 4, 4)) == 0
+    assert ssd.s6_workspace_bytes(ssd.S6Dims(1, 64 * 65536, 4, 4)) == 0
+    assert _s6_check(ssd.S6Dims(0, 300, 96, 16), x=0, delta=0, B=0, C=0, y=0, ws=0) == OK

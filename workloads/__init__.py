@@ -27,7 +27,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["LayerConfig", "CONFIGS", "HELD_OUT", "DECODE_CONFIGS", "config_by_name", "generate",
-           "round_to_bf16", "bf16_bits_to_f32"]
+           "round_to_bf16", "bf16_bits_to_f32", "S6Config", "S6_CONFIGS", "s6_config_by_name", "generate_s6"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -173,3 +173,76 @@ def generate(cfg: LayerConfig, seed: Optional[int] = None) -> dict:
     else:
         out["init_state"] = None
     return out
+
+
+# --------------------------------------------------------------------------
+# The Mamba-1 selective scan (S6): shapes and value recipes of Sasha Rush's
+# "Mamba: The Hard Way", Part 5 ("Mamba / S6"). Layouts as the page's tensors
+# without singleton dimensions: x, delta [batch, channels, seqlen]; A
+# [channels, dstate]; B, C [batch, dstate, seqlen]; h0 [batch, channels,
+# dstate]. All float32.
+
+@dataclasses.dataclass(frozen=True)
+class S6Config:
+    name: str
+    batch: int
+    seqlen: int
+    channels: int
+    dstate: int
+    recipe: str          # "page": the page's create(); "random": signed, varied values
+    seed: int
+    h0_sigma: Optional[float] = None
+    description: str = ""
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seqlen
+
+    def with_shape(self, **kw) -> "S6Config":
+        return dataclasses.replace(self, **kw)
+
+
+S6_CONFIGS = [
+    S6Config("s6-page", batch=8, seqlen=2048, channels=1024, dstate=4, recipe="page", seed=20,
+             description="the page's benchmark call: mamba(*create(S=2048, Ba=8, D=1024, N=4))"),
+    S6Config("s6-mamba1-130m", batch=8, seqlen=2048, channels=1536, dstate=16, recipe="random", seed=21,
+             description="a Mamba-1 130M-like layer: d_inner 1536, d_state 16"),
+    S6Config("s6-small", batch=2, seqlen=300, channels=100, dstate=4, recipe="random", seed=22, h0_sigma=0.5,
+             description="small, ragged in both channels and tokens, with an initial state"),
+]
+
+
+def s6_config_by_name(name: str) -> S6Config:
+    for c in S6_CONFIGS:
+        if c.name == name:
+            return c
+    raise KeyError(name)
+
+
+def generate_s6(cfg: S6Config, seed: Optional[int] = None) -> dict:
+    """Draw one selective-scan input set (float32 numpy arrays).
+
+    recipe "page" follows the page's create(): x ~ U[0, 1), A = -1, B = 0.1,
+    C ~ 0.1 U[0, 1), delta ~ 0.1 U[0, 1). recipe "random": x, B, C ~ N(0, 1),
+    A = -exp(U(-1, 1)), delta = softplus(N(0, 1) - 1). Draw order: x, delta,
+    A, B, C, then h0 (only when h0_sigma is set).
+    """
+    rng = np.random.Generator(np.random.PCG64(cfg.seed if seed is None else seed))
+    bt, L, D, N = cfg.batch, cfg.seqlen, cfg.channels, cfg.dstate
+    f = np.float32
+    if cfg.recipe == "page":
+        x = rng.random((bt, D, L), dtype=f)
+        delta = (0.1 * rng.random((bt, D, L))).astype(f)
+        A = -np.ones((D, N), dtype=f)
+        B = np.full((bt, N, L), 0.1, dtype=f)
+        C = (0.1 * rng.random((bt, N, L))).astype(f)
+    elif cfg.recipe == "random":
+        x = rng.standard_normal((bt, D, L), dtype=f)
+        delta = _softplus(rng.standard_normal((bt, D, L)) - 1.0).astype(f)
+        A = (-np.exp(rng.uniform(-1.0, 1.0, (D, N)))).astype(f)
+        B = rng.standard_normal((bt, N, L), dtype=f)
+        C = rng.standard_normal((bt, N, L), dtype=f)
+    else:
+        raise ValueError(cfg.recipe)
+    h0 = None if cfg.h0_sigma is None else (cfg.h0_sigma * rng.standard_normal((bt, D, N))).astype(f)
+    return {"x": x, "delta": delta, "A": A, "B": B, "C": C, "h0": h0}
