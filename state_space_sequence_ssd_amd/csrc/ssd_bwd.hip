@@ -38,7 +38,7 @@ namespace {
 // offset z0 s0 + z1 s1 + (z2 / d2) s2 for z = (z0 Z1 + z1) Z2 + z2; the
 // divisor d2 maps a head index to its group for operands shared by a group.
 // Scale vectors may be null (ones).
-constexpr int GT = 64, GK = 16;   // output tile GT x GT, k-step GK; 256 threads, 4 x 4 each
+constexpr int GT = 64, GK = 16;   // output tile GT x GT, k-step GK; 256 threads, a 32 x 32 quarter per wave
 
 struct Operand {
   const float* p;
@@ -59,7 +59,75 @@ struct GemmArgs {
   int M, N, K, Z1, Z2;
   float beta;
   int shape;
+  int vec;                     // operands staged as 16-byte pieces (see gemm())
+  // optional second product added to the first: + diag(rs2) (A2 B2), with
+  // contraction length K2 over the full range (no causal shape)
+  Operand a2, b2, rsc2;
+  int K2;
 };
+
+// Stage one GK-deep slice of A (GT rows from m0) and B (GT columns from n0)
+// into LDS as [k][m] and [k][n]; rows, columns and k past the operands are
+// zero.
+__device__ __forceinline__ void stage_k(float (*sa)[GT + 4], float (*sb)[GT + 4], const Operand& ao,
+                                        const Operand& bo, const float* A, const float* B, const float* ks, int m0,
+                                        int n0, int k0, int M, int N, int kend, int vec, int tid) {
+  // consecutive threads walk whichever index is contiguous in memory
+  const bool a_k_unit = ao.cs == 1, b_n_unit = bo.cs == 1;
+  if (vec) {
+    // one 16-byte piece per thread and operand, along the contiguous index
+    if (a_k_unit) {
+      const int mm = tid / 4, kq = (tid % 4) * 4, m = m0 + mm;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (m < M) {
+        v = *reinterpret_cast<const float4*>(A + m * ao.rs + k0 + kq);
+        if (ks) {
+          const float4 s4 = *reinterpret_cast<const float4*>(ks + k0 + kq);
+          v.x *= s4.x; v.y *= s4.y; v.z *= s4.z; v.w *= s4.w;
+        }
+      }
+      sa[kq][mm] = v.x; sa[kq + 1][mm] = v.y; sa[kq + 2][mm] = v.z; sa[kq + 3][mm] = v.w;
+    } else {
+      const int kk = tid / 16, mq = (tid % 16) * 4, k = k0 + kk;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (m0 + mq < M) {
+        v = *reinterpret_cast<const float4*>(A + (m0 + mq) + k * ao.cs);
+        if (ks) {
+          const float sk = ks[k];
+          v.x *= sk; v.y *= sk; v.z *= sk; v.w *= sk;
+        }
+      }
+      *reinterpret_cast<float4*>(&sa[kk][mq]) = v;
+    }
+    if (b_n_unit) {
+      const int kb = tid / 16, nq = (tid % 16) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (n0 + nq < N) v = *reinterpret_cast<const float4*>(B + (k0 + kb) * bo.rs + n0 + nq);
+      *reinterpret_cast<float4*>(&sb[kb][nq]) = v;
+    } else {
+      const int nn = tid / 4, kq = (tid % 4) * 4, n = n0 + nn;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (n < N) v = *reinterpret_cast<const float4*>(B + (k0 + kq) + n * bo.cs);
+      sb[kq][nn] = v.x; sb[kq + 1][nn] = v.y; sb[kq + 2][nn] = v.z; sb[kq + 3][nn] = v.w;
+    }
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int idx = tid + 256 * e;          // 0 .. 1023
+    const int kk = a_k_unit ? idx % GK : idx / GT, mm = a_k_unit ? idx / GK : idx % GT;
+    const int m = m0 + mm, k = k0 + kk;
+    float v = 0.f;
+    if (m < M && k < kend) {
+      v = A[m * ao.rs + k * ao.cs];
+      if (ks) v *= ks[k];
+    }
+    sa[kk][mm] = v;
+    const int nn = b_n_unit ? idx % GT : idx / GK, kb = b_n_unit ? idx / GT : idx % GK;
+    const int n = n0 + nn, kq = k0 + kb;
+    sb[kb][nn] = (n < N && kq < kend) ? B[kq * bo.rs + n * bo.cs] : 0.f;
+  }
+}
 
 __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float sa[GK][GT + 4];
@@ -68,63 +136,54 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
   const int z = blockIdx.y;
   const int z2 = z % g.Z2, z1 = (z / g.Z2) % g.Z1, z0 = z / (g.Z2 * g.Z1);
-  const float* A = g.a.p + g.a.base(z0, z1, z2);
-  const float* B = g.b.p + g.b.base(z0, z1, z2);
-  const float* ks = g.ksc.p ? g.ksc.p + g.ksc.base(z0, z1, z2) : nullptr;
-  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  const int tid = threadIdx.x;
   const int m0 = tm * GT, n0 = tn * GT;
   if (g.shape == kLowerOut && n0 > m0 + GT - 1) return;   // wholly above the diagonal
   const int kbeg = g.shape == kKFromRow ? m0 : 0;
   const int kend = g.shape == kKToRow ? min(g.K, m0 + GT) : g.K;
-  float acc[4][4] = {};
-  for (int k0 = kbeg; k0 < kend; k0 += GK) {
-    // stage A (GT x GK, as [k][m]) and B (GK x GT, as [k][n]): 4 elements each per thread
-    // consecutive threads walk whichever index is contiguous in memory
-    const bool a_k_unit = g.a.cs == 1, b_n_unit = g.b.cs == 1;
+  // each wave computes one 32 x 32 quarter of the tile with the fp32 MFMA
+  // (32x32x2): lane l supplies A[row l%32][k l/32] and B[k l/32][col l%32]
+  const int wave = tid / 64, lane = tid % 64, lm = lane % 32, lg = lane / 32;
+  const int wm = 32 * (wave / 2), wn = 32 * (wave % 2);
+  f32x16 acc = f32x16{}, acc2 = f32x16{};
+  {
+    const float* A = g.a.p + g.a.base(z0, z1, z2);
+    const float* B = g.b.p + g.b.base(z0, z1, z2);
+    const float* ks = g.ksc.p ? g.ksc.p + g.ksc.base(z0, z1, z2) : nullptr;
+    for (int k0 = kbeg; k0 < kend; k0 += GK) {
+      stage_k(sa, sb, g.a, g.b, A, B, ks, m0, n0, k0, g.M, g.N, kend, g.vec, tid);
+      __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int idx = tid + 256 * e;          // 0 .. 1023
-      const int kk = a_k_unit ? idx % GK : idx / GT, mm = a_k_unit ? idx / GK : idx % GT;
-      const int m = m0 + mm, k = k0 + kk;
-      float v = 0.f;
-      if (m < g.M && k < kend) {
-        v = A[m * g.a.rs + k * g.a.cs];
-        if (ks) v *= ks[k];
-      }
-      sa[kk][mm] = v;
-      const int nn = b_n_unit ? idx % GT : idx / GK, kb = b_n_unit ? idx / GT : idx % GK;
-      const int n = n0 + nn, kq = k0 + kb;
-      sb[kb][nn] = (n < g.N && kq < kend) ? B[kq * g.b.rs + n * g.b.cs] : 0.f;
+      for (int kk = 0; kk < GK; kk += 2)
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[kk + lg][wm + lm], sb[kk + lg][wn + lm], acc, 0, 0, 0);
+      __syncthreads();
     }
-    __syncthreads();
+  }
+  if (g.a2.p) {
+    const float* A = g.a2.p + g.a2.base(z0, z1, z2);
+    const float* B = g.b2.p + g.b2.base(z0, z1, z2);
+    for (int k0 = 0; k0 < g.K2; k0 += GK) {
+      stage_k(sa, sb, g.a2, g.b2, A, B, nullptr, m0, n0, k0, g.M, g.N, g.K2, g.vec, tid);
+      __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < GK; ++kk) {
-      // this thread's 4 rows and 4 columns are consecutive: one 16-byte read each
-      const float4 a4 = *reinterpret_cast<const float4*>(&sa[kk][4 * ty]);
-      const float4 b4 = *reinterpret_cast<const float4*>(&sb[kk][4 * tx]);
-      const float av[4] = {a4.x, a4.y, a4.z, a4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+      for (int kk = 0; kk < GK; kk += 2)
+        acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[kk + lg][wm + lm], sb[kk + lg][wn + lm], acc2, 0, 0, 0);
+      __syncthreads();
     }
-    __syncthreads();
   }
   float* Cp = const_cast<float*>(g.c.p) + g.c.base(z0, z1, z2);
   const float* rs = g.rsc.p ? g.rsc.p + g.rsc.base(z0, z1, z2) : nullptr;
+  const float* rs2 = g.rsc2.p ? g.rsc2.p + g.rsc2.base(z0, z1, z2) : nullptr;
+  const int n = n0 + wn + lm;
+  if (n >= g.N) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + 4 * ty + i;
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + wm + drow(r, lg);   // the accumulator's row for this lane and register
     if (m >= g.M) continue;
-    const float r = rs ? rs[m] : 1.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = n0 + 4 * tx + j;
-      if (n >= g.N) continue;
-      float* cp = Cp + m * g.c.rs + n * g.c.cs;
-      const float v = r * acc[i][j];
-      *cp = g.beta == 0.f ? v : fmaf(g.beta, *cp, v);
-    }
+    float* cp = Cp + m * g.c.rs + n * g.c.cs;
+    float v = (rs ? rs[m] : 1.f) * acc[r];
+    if (g.a2.p) v = fmaf(rs2 ? rs2[m] : 1.f, acc2[r], v);
+    *cp = g.beta == 0.f ? v : fmaf(g.beta, *cp, v);
   }
 }
 
@@ -134,8 +193,21 @@ Operand op(const float* p, int64_t rs, int64_t cs, int64_t s0, int64_t s1, int64
 Operand none() { return Operand{nullptr, 0, 0, 0, 0, 0, 1}; }
 
 hipError_t gemm(const Operand& a, const Operand& b, const Operand& c, const Operand& rsc, const Operand& ksc,
-                int M, int N, int K, int Z0, int Z1, int Z2, float beta, hipStream_t s, int shape = kFull) {
-  GemmArgs g{a, b, c, rsc, ksc, M, N, K, Z1, Z2, beta, shape};
+                int M, int N, int K, int Z0, int Z1, int Z2, float beta, hipStream_t s, int shape = kFull,
+                const Operand* a2 = nullptr, const Operand* b2 = nullptr, const Operand* rsc2 = nullptr,
+                int K2 = 0) {
+  // 16-byte staging needs every 4-element piece along the contiguous index
+  // aligned and wholly inside or outside the operand: bases 16-byte aligned,
+  // all other strides multiples of 4, and K, M, N multiples of 4
+  auto al4 = [](const Operand& o) {
+    return (reinterpret_cast<uintptr_t>(o.p) & 15) == 0 && o.s0 % 4 == 0 && o.s1 % 4 == 0 && o.s2 % 4 == 0 &&
+           (o.rs == 1 || o.rs % 4 == 0) && (o.cs == 1 || o.cs % 4 == 0) && (o.rs == 1 || o.cs == 1);
+  };
+  const Operand no{nullptr, 0, 0, 0, 0, 0, 1};
+  const int vec = al4(a) && al4(b) && (!ksc.p || al4(Operand{ksc.p, 1, 1, ksc.s0, ksc.s1, ksc.s2, ksc.d2})) &&
+                  K % 16 == 0 && M % 4 == 0 && N % 4 == 0 && (!a2 || (al4(*a2) && al4(*b2) && K2 % 16 == 0));
+  GemmArgs g{a, b, c, rsc, ksc, M, N, K, Z1, Z2, beta, shape, vec, a2 ? *a2 : no, b2 ? *b2 : no,
+             rsc2 ? *rsc2 : no, K2};
   const int64_t tiles = (int64_t)((M + GT - 1) / GT) * ((N + GT - 1) / GT);
   const int64_t Z = (int64_t)Z0 * Z1 * Z2;
   if (Z == 0 || tiles == 0) return hipSuccess;
@@ -513,10 +585,12 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
           kKFromRow));
   // 8. dB_h = W2s^T C + diag(w) X dHn;  dC_h = W2s B + diag(E) dY Hprev
   const Operand dBo = op(p.dBh, H * N, 1, Tp * H * N, Q * H * N, N), dCo = op(p.dCh, H * N, 1, Tp * H * N, Q * H * N, N);
-  ok(gemm(Wqq2T, Ct, dBo, none(), none(), Qi, Ni, Qi, Bi, Ki, Hi, 0.f, s, kKFromRow));
-  ok(gemm(X, blk(p.dhn, false), dBo, vec(p.wst), none(), Qi, Ni, Pi, Bi, Ki, Hi, 1.f, s));
-  ok(gemm(Wqq2, Bt, dCo, none(), none(), Qi, Ni, Qi, Bi, Ki, Hi, 0.f, s, kKToRow));
-  ok(gemm(dY, blk(p.hprev, false), dCo, vec(p.E), none(), Qi, Ni, Pi, Bi, Ki, Hi, 1.f, s));
+  // (each as one kernel: the causal product and the state product share the output tile)
+  {
+    const Operand dhn = blk(p.dhn, false), hpv = blk(p.hprev, false), w = vec(p.wst), ev = vec(p.E);
+    ok(gemm(Wqq2T, Ct, dBo, none(), none(), Qi, Ni, Qi, Bi, Ki, Hi, 0.f, s, kKFromRow, &X, &dhn, &w, Pi));
+    ok(gemm(Wqq2, Bt, dCo, none(), none(), Qi, Ni, Qi, Bi, Ki, Hi, 0.f, s, kKToRow, &dY, &hpv, &ev, Pi));
+  }
   // 9. dx, ddt and the dA / dD parts; then the group and head sums
   if (e == hipSuccess && bt * nc * H > 0) {
     hipLaunchKernelGGL(finish_chunk, dim3((unsigned)(bt * nc * H)), dim3(256), 0, s, p);
