@@ -16,11 +16,11 @@ struct BwdLayout {
   size_t Xp, dYp;                       // [bt][Tp][H][P], zero padded
   size_t Bp, Cp;                        // [bt][Tp][G][N], zero padded
   size_t S, hprev, dhn;                 // [bt][H][nc][P][N]
-  size_t CB;                            // [bt][nc][G][Q][Q]
+  size_t CB;                            // [bt][nc][G][Q][Q] (C B^T, then the group's sum of W2s)
   size_t DX, W1;                        // [bt][nc][H][Q][Q]
   size_t U, V;                          // [bt][nc][H][Q][P]
   size_t dXp;                           // [bt][Tp][H][P]
-  size_t dBh, dCh;                      // [bt][Tp][H][N]
+  size_t dBh, dCh;                      // [bt][Tp][G][N]
   size_t rowZ, colZ, colW;              // [bt][H][Tp]
   size_t dA_part, dD_part;              // [bt][H][nc]
   size_t total;

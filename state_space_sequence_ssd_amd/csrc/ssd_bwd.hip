@@ -64,14 +64,16 @@ struct GemmArgs {
   // contraction length K2 over the full range (no causal shape)
   Operand a2, b2, rsc2;
   int K2;
+  int hsum;                    // > 0: the second product sums this many heads (see bwd_gemm)
 };
 
 // Stage one GK-deep slice of A (GT rows from m0) and B (GT columns from n0)
 // into LDS as [k][m] and [k][n]; rows, columns and k past the operands are
 // zero.
 __device__ __forceinline__ void stage_k(float (*sa)[GT + 4], float (*sb)[GT + 4], const Operand& ao,
-                                        const Operand& bo, const float* A, const float* B, const float* ks, int m0,
-                                        int n0, int k0, int M, int N, int kend, int vec, int tid) {
+                                        const Operand& bo, const float* A, const float* B, const float* ks,
+                                        const float* ra, int m0, int n0, int k0, int M, int N, int kend, int vec,
+                                        int tid) {
   // consecutive threads walk whichever index is contiguous in memory
   const bool a_k_unit = ao.cs == 1, b_n_unit = bo.cs == 1;
   if (vec) {
@@ -85,6 +87,10 @@ __device__ __forceinline__ void stage_k(float (*sa)[GT + 4], float (*sb)[GT + 4]
           const float4 s4 = *reinterpret_cast<const float4*>(ks + k0 + kq);
           v.x *= s4.x; v.y *= s4.y; v.z *= s4.z; v.w *= s4.w;
         }
+        if (ra) {
+          const float r = ra[m];
+          v.x *= r; v.y *= r; v.z *= r; v.w *= r;
+        }
       }
       sa[kq][mm] = v.x; sa[kq + 1][mm] = v.y; sa[kq + 2][mm] = v.z; sa[kq + 3][mm] = v.w;
     } else {
@@ -95,6 +101,9 @@ __device__ __forceinline__ void stage_k(float (*sa)[GT + 4], float (*sb)[GT + 4]
         if (ks) {
           const float sk = ks[k];
           v.x *= sk; v.y *= sk; v.z *= sk; v.w *= sk;
+        }
+        if (ra) {
+          v.x *= ra[m0 + mq]; v.y *= ra[m0 + mq + 1]; v.z *= ra[m0 + mq + 2]; v.w *= ra[m0 + mq + 3];
         }
       }
       *reinterpret_cast<float4*>(&sa[kk][mq]) = v;
@@ -121,6 +130,7 @@ __device__ __forceinline__ void stage_k(float (*sa)[GT + 4], float (*sb)[GT + 4]
     if (m < M && k < kend) {
       v = A[m * ao.rs + k * ao.cs];
       if (ks) v *= ks[k];
+      if (ra) v *= ra[m];
     }
     sa[kk][mm] = v;
     const int nn = b_n_unit ? idx % GT : idx / GK, kb = b_n_unit ? idx / GT : idx % GK;
@@ -151,7 +161,7 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
     const float* B = g.b.p + g.b.base(z0, z1, z2);
     const float* ks = g.ksc.p ? g.ksc.p + g.ksc.base(z0, z1, z2) : nullptr;
     for (int k0 = kbeg; k0 < kend; k0 += GK) {
-      stage_k(sa, sb, g.a, g.b, A, B, ks, m0, n0, k0, g.M, g.N, kend, g.vec, tid);
+      stage_k(sa, sb, g.a, g.b, A, B, ks, nullptr, m0, n0, k0, g.M, g.N, kend, g.vec, tid);
       __syncthreads();
 #pragma unroll
       for (int kk = 0; kk < GK; kk += 2)
@@ -160,20 +170,29 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
     }
   }
   if (g.a2.p) {
-    const float* A = g.a2.p + g.a2.base(z0, z1, z2);
-    const float* B = g.b2.p + g.b2.base(z0, z1, z2);
-    for (int k0 = 0; k0 < g.K2; k0 += GK) {
-      stage_k(sa, sb, g.a2, g.b2, A, B, nullptr, m0, n0, k0, g.M, g.N, g.K2, g.vec, tid);
-      __syncthreads();
+    // the second product, summed over hsum consecutive heads of the batch
+    // index (head z2 * hsum + hl), each A2 row scaled by its head's rsc2 row
+    // before the sum; with hsum = 0 it is the batch's own product and rsc2
+    // scales its output rows
+    const int nh = g.hsum > 0 ? g.hsum : 1;
+    for (int hl = 0; hl < nh; ++hl) {
+      const int zh = g.hsum > 0 ? z2 * g.hsum + hl : z2;
+      const float* A = g.a2.p + g.a2.base(z0, z1, zh);
+      const float* B = g.b2.p + g.b2.base(z0, z1, zh);
+      const float* ra = (g.hsum > 0 && g.rsc2.p) ? g.rsc2.p + g.rsc2.base(z0, z1, zh) : nullptr;
+      for (int k0 = 0; k0 < g.K2; k0 += GK) {
+        stage_k(sa, sb, g.a2, g.b2, A, B, nullptr, ra, m0, n0, k0, g.M, g.N, g.K2, g.vec, tid);
+        __syncthreads();
 #pragma unroll
-      for (int kk = 0; kk < GK; kk += 2)
-        acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[kk + lg][wm + lm], sb[kk + lg][wn + lm], acc2, 0, 0, 0);
-      __syncthreads();
+        for (int kk = 0; kk < GK; kk += 2)
+          acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[kk + lg][wm + lm], sb[kk + lg][wn + lm], acc2, 0, 0, 0);
+        __syncthreads();
+      }
     }
   }
   float* Cp = const_cast<float*>(g.c.p) + g.c.base(z0, z1, z2);
   const float* rs = g.rsc.p ? g.rsc.p + g.rsc.base(z0, z1, z2) : nullptr;
-  const float* rs2 = g.rsc2.p ? g.rsc2.p + g.rsc2.base(z0, z1, z2) : nullptr;
+  const float* rs2 = (g.hsum == 0 && g.rsc2.p) ? g.rsc2.p + g.rsc2.base(z0, z1, z2) : nullptr;
   const int n = n0 + wn + lm;
   if (n >= g.N) return;
 #pragma unroll
@@ -195,7 +214,7 @@ Operand none() { return Operand{nullptr, 0, 0, 0, 0, 0, 1}; }
 hipError_t gemm(const Operand& a, const Operand& b, const Operand& c, const Operand& rsc, const Operand& ksc,
                 int M, int N, int K, int Z0, int Z1, int Z2, float beta, hipStream_t s, int shape = kFull,
                 const Operand* a2 = nullptr, const Operand* b2 = nullptr, const Operand* rsc2 = nullptr,
-                int K2 = 0) {
+                int K2 = 0, int hsum = 0) {
   // 16-byte staging needs every 4-element piece along the contiguous index
   // aligned and wholly inside or outside the operand: bases 16-byte aligned,
   // all other strides multiples of 4, and K, M, N multiples of 4
@@ -207,7 +226,7 @@ hipError_t gemm(const Operand& a, const Operand& b, const Operand& c, const Oper
   const int vec = al4(a) && al4(b) && (!ksc.p || al4(Operand{ksc.p, 1, 1, ksc.s0, ksc.s1, ksc.s2, ksc.d2})) &&
                   K % 16 == 0 && M % 4 == 0 && N % 4 == 0 && (!a2 || (al4(*a2) && al4(*b2) && K2 % 16 == 0));
   GemmArgs g{a, b, c, rsc, ksc, M, N, K, Z1, Z2, beta, shape, vec, a2 ? *a2 : no, b2 ? *b2 : no,
-             rsc2 ? *rsc2 : no, K2};
+             rsc2 ? *rsc2 : no, K2, hsum};
   const int64_t tiles = (int64_t)((M + GT - 1) / GT) * ((N + GT - 1) / GT);
   const int64_t Z = (int64_t)Z0 * Z1 * Z2;
   if (Z == 0 || tiles == 0) return hipSuccess;
@@ -433,7 +452,20 @@ __global__ __launch_bounds__(256) void finish_chunk(const BwdProblem p) {
   if (i == 0) p.dD_part[(b * H + h) * p.nc + k] = s_red[0];
 }
 
-// dB, dC: the sum over a group's heads of the per-head parts [bt][Tp][H][N]
+// sum over the heads of each group of the Q x Q blocks [bt][nc][H][Q][Q]
+// -> [bt][nc][G][Q][Q]
+__global__ void sum_heads(const float* __restrict__ in, float* __restrict__ out, int hpg, int64_t QQ, int64_t total) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t o = i % QQ, bkg = i / QQ;   // (b * nc + k) * G + g
+    const float* src = in + bkg * hpg * QQ + o;
+    float acc = 0.f;
+    for (int j = 0; j < hpg; ++j) acc += src[j * QQ];
+    out[i] = acc;
+  }
+}
+
+// [bt][Tp][H][N] -> [bt][T][G][N]: the sum over each group's heads of the
+// padded rows (with H = G: the unpadding copy)
 __global__ void group_sum(const float* __restrict__ part, float* __restrict__ out, int64_t T_, int64_t Tp, int H,
                           int G, int64_t N, int64_t total) {
   const int hpg = H / G;
@@ -494,8 +526,8 @@ BwdLayout bwd_layout(int64_t bt, int64_t H, int64_t P, int64_t N, int64_t G, int
   L.U = take(bt * nc * H * Q * P);
   L.V = take(bt * nc * H * Q * P);
   L.dXp = take(bt * Tp * H * P);
-  L.dBh = take(bt * Tp * H * N);
-  L.dCh = take(bt * Tp * H * N);
+  L.dBh = take(bt * Tp * G * N);
+  L.dCh = take(bt * Tp * G * N);
   L.rowZ = take(bt * H * Tp);
   L.colZ = take(bt * H * Tp);
   L.colW = take(bt * H * Tp);
@@ -574,8 +606,7 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
                        p.rowZ, p.colZ, p.colW, Qi, Hi, hpg, nc, Tp);
     ok(hipGetLastError());
   }
-  const Operand Wqq2 = op(p.DX, Q, 1, nc * H * QQ, H * QQ, QQ);
-  const Operand Wqq1T = op(p.W1, 1, Q, nc * H * QQ, H * QQ, QQ), Wqq2T = op(p.DX, 1, Q, nc * H * QQ, H * QQ, QQ);
+  const Operand Wqq1T = op(p.W1, 1, Q, nc * H * QQ, H * QQ, QQ);
   const Operand Uo = op(p.U, P, 1, nc * H * Q * P, H * Q * P, Q * P), Vo = op(p.V, P, 1, nc * H * Q * P, H * Q * P, Q * P);
   // 6. U = B dHn^T, V = C Hprev^T (rows j: dHn B_j, Hprev C_j)
   ok(gemm(Bt, blk(p.dhn, true), Uo, none(), none(), Qi, Pi, Ni, Bi, Ki, Hi, 0.f, s));
@@ -584,12 +615,21 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
   ok(gemm(Wqq1T, dY, op(p.dXp, H * P, 1, Tp * H * P, Q * H * P, P), none(), none(), Qi, Pi, Qi, Bi, Ki, Hi, 0.f, s,
           kKFromRow));
   // 8. dB_h = W2s^T C + diag(w) X dHn;  dC_h = W2s B + diag(E) dY Hprev
-  const Operand dBo = op(p.dBh, H * N, 1, Tp * H * N, Q * H * N, N), dCo = op(p.dCh, H * N, 1, Tp * H * N, Q * H * N, N);
-  // (each as one kernel: the causal product and the state product share the output tile)
+  // per (b, k, group): B and C are shared by the group's heads, so the
+  // causal products take the sum of the heads' W2s blocks (over CB, no longer
+  // needed), and the state products sum the heads' parts inside the kernel
+  const int64_t nsum = bt * nc * G * QQ;
+  if (e == hipSuccess && nsum > 0) {
+    hipLaunchKernelGGL(sum_heads, dim3(grid_for(nsum)), dim3(256), 0, s, p.DX, p.CB, hpg, QQ, nsum);
+    ok(hipGetLastError());
+  }
   {
+    const Operand W2g = op(p.CB, Q, 1, nc * G * QQ, G * QQ, QQ), W2gT = op(p.CB, 1, Q, nc * G * QQ, G * QQ, QQ);
+    const Operand Bg = op(p.Bp, G * N, 1, Tp * G * N, Q * G * N, N), Cg = op(p.Cp, G * N, 1, Tp * G * N, Q * G * N, N);
+    const Operand dBg = op(p.dBh, G * N, 1, Tp * G * N, Q * G * N, N), dCg = op(p.dCh, G * N, 1, Tp * G * N, Q * G * N, N);
     const Operand dhn = blk(p.dhn, false), hpv = blk(p.hprev, false), w = vec(p.wst), ev = vec(p.E);
-    ok(gemm(Wqq2T, Ct, dBo, none(), none(), Qi, Ni, Qi, Bi, Ki, Hi, 0.f, s, kKFromRow, &X, &dhn, &w, Pi));
-    ok(gemm(Wqq2, Bt, dCo, none(), none(), Qi, Ni, Qi, Bi, Ki, Hi, 0.f, s, kKToRow, &dY, &hpv, &ev, Pi));
+    ok(gemm(W2gT, Cg, dBg, none(), none(), Qi, Ni, Qi, Bi, Ki, (int)G, 0.f, s, kKFromRow, &X, &dhn, &w, Pi, hpg));
+    ok(gemm(W2g, Bg, dCg, none(), none(), Qi, Ni, Qi, Bi, Ki, (int)G, 0.f, s, kKToRow, &dY, &hpv, &ev, Pi, hpg));
   }
   // 9. dx, ddt and the dA / dD parts; then the group and head sums
   if (e == hipSuccess && bt * nc * H > 0) {
@@ -598,8 +638,8 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
   }
   const int64_t nbo = bt * T * G * N;
   if (e == hipSuccess && nbo > 0) {
-    hipLaunchKernelGGL(group_sum, dim3(grid_for(nbo)), dim3(256), 0, s, p.dBh, p.dB, T, Tp, Hi, (int)G, N, nbo);
-    hipLaunchKernelGGL(group_sum, dim3(grid_for(nbo)), dim3(256), 0, s, p.dCh, p.dC, T, Tp, Hi, (int)G, N, nbo);
+    hipLaunchKernelGGL(group_sum, dim3(grid_for(nbo)), dim3(256), 0, s, p.dBh, p.dB, T, Tp, (int)G, (int)G, N, nbo);
+    hipLaunchKernelGGL(group_sum, dim3(grid_for(nbo)), dim3(256), 0, s, p.dCh, p.dC, T, Tp, (int)G, (int)G, N, nbo);
     ok(hipGetLastError());
   }
   if (e == hipSuccess) {
