@@ -291,8 +291,8 @@ int mamba2_ssd_step(const mamba2_ssd_step_dims* dims, int io_dtype,
  * Arithmetic: fp32 throughout (bf16 inputs are exact in fp32).
  * Workspace: mamba2_ssd_bwd_workspace_bytes(dims, io) bytes, device memory,
  * 256-byte aligned; it holds padded fp32 copies of the inputs, the chunk
- * states, the per-chunk C.B^T and dy.x^T blocks and the per-head parts of
- * dB and dC (about 12.6 GB for batch 4, seqlen 8192, 80 heads, headdim 64,
+ * states, the per-chunk C.B^T and dy.x^T blocks and the per-group parts of
+ * dB and dC (about 9.9 GB for batch 4, seqlen 8192, 80 heads, headdim 64,
  * dstate 128, chunk 256). Sizes are those of mamba2_ssd_fwd, plus
  * batch * nchunks * nheads <= 65535.
  * Errors: as mamba2_ssd_check_args (NULL_POINTER for a missing required
