@@ -76,7 +76,7 @@ struct RCfg {
   // one tile buffer; the C.B^T phase puts the B tile in one as well
   static constexpr int BUF = GOFF + GBYTES > BBYTES ? GOFF + GBYTES : BBYTES;
   static_assert(IX % WAVES == 0, "x loads split evenly");
-  static_assert(2 * BUF + Q * 4 <= 160 * 1024, "LDS");
+  static_assert(2 * BUF + 2 * Q * 4 + 4 * 4096 <= 160 * 1024, "LDS");
   static_assert(LT <= 40 && LB + LT + 2 * KS <= 63, "vmcnt accounting");
 };
 
@@ -180,6 +180,7 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2][Cf::BUF];
   __shared__ __attribute__((aligned(16))) float sW[Q];   // dt_j * 2^(G'_end(block of j) - G'_j) <= dt_j
   __shared__ __attribute__((aligned(16))) float sE[Q];   // 2^(G'_t) <= 1
+  __shared__ __attribute__((aligned(16))) unsigned char ystage[4 * 4096];   // per wave: one 32 x 64 bf16 y block
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -245,7 +246,7 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
   float cbc[9][16];   // resident C.B^T blocks (slots, see above), in AGPRs
   Frag cf[2][KS];     // C fragments of the wave's t-blocks, in AGPRs
   int64_t ckey_cached = -1;
-  int ys = 0;     // y stores issued after the current tile's loads (0 or 32)
+  int ys = 0;     // y stores issued after the current tile's loads: none, or 8
   int buf = 0;
 
   // Issue the loads of one tile into LDS buffer `dst`.
@@ -346,7 +347,7 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
     }
 
     // this tile's loads have landed once only the previous tile's y stores remain
-    if (ys) wait_vm_barrier<32>();
+    if (ys) wait_vm_barrier<8>();
     else wait_vm_barrier<0>();
     const float* sG = reinterpret_cast<const float*>(cur + Cf::GOFF);
     const float* sDt = sG + Q;
@@ -543,31 +544,36 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // y: one dword (columns 2m, 2m+1) per lane per row, through a buffer
-    // resource over the tile's valid rows. Full tiles put the row in the
-    // scalar offset (no per-store address arithmetic); a ragged tile keeps
-    // the whole offset in the range-checked vector operand, so rows past
-    // the sequence are dropped. The lane offset is re-derived per tile
-    // (laundered) so the compiler does not keep row addresses alive across
-    // the walk.
-    const bool full = t.nvalid == Q;
+    // y goes out through LDS in 16-byte row pieces: per t-block, the wave
+    // writes its 32 x 64 block (bf16, 128-byte rows) into its own staging
+    // area, one dword (columns 2m, 2m+1) per lane per row, reads it back as
+    // 16-byte pieces and stores 4 of them per lane, through a buffer resource
+    // over the tile's valid rows (rows past a ragged sequence are dropped by
+    // its range check). One wave's LDS operations run in order, so the
+    // staging area needs no barrier.
     {
-      uint32_t ylane = (uint32_t)(4 * g) * xrb + 4 * m;
+      unsigned char* ys_lds = ystage + wave * 4096;
+      const uint32_t wlane = (uint32_t)(4 * g) * 128 + 4 * m;
+      const int pr = lane / 8, pc = lane % 8;   // piece i * 64 + lane: row 8 i + pr, 16-byte piece pc
+      uint32_t plane = (uint32_t)pr * xrb + (uint32_t)pc * 16;
       uint32_t xrbs = xrb;
-      asm volatile("" : "+v"(ylane), "+s"(xrbs));
+      asm volatile("" : "+v"(plane), "+s"(xrbs));
       const __amdgpu_buffer_rsrc_t yr = make_rsrc(t.y, (uint32_t)t.nvalid * xrbs);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t trow = (uint32_t)((u ? tb1 : tb0) * 32 + 8 * (r / 4) + r % 4);   // + 4g in ylane
-          const uint32_t val = pack_bf16x2(acc[u][0][r], acc[u][1][r]);
-          if (full)
-            __builtin_amdgcn_raw_buffer_store_b32(val, yr, ylane, trow * xrbs, 0);
-          else
-            __builtin_amdgcn_raw_buffer_store_b32(val, yr, ylane + trow * xrbs, 0, 0);
+        for (int r = 0; r < 16; ++r)
+          *reinterpret_cast<uint32_t*>(ys_lds + wlane + (8 * (r / 4) + r % 4) * 128) =
+              pack_bf16x2(acc[u][0][r], acc[u][1][r]);
+        const uint32_t row0 = (uint32_t)((u ? tb1 : tb0) * 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(ys_lds + (8 * i + pr) * 128 + pc * 16);
+          __builtin_amdgcn_raw_buffer_store_b128(v, yr, plane + (row0 + 8 * i) * xrbs, 0, 0);
         }
+      }
     }
+    const bool full = t.nvalid == Q;
     ys = (prefetch && full) ? 1 : 0;
     buf ^= 1;
   }
