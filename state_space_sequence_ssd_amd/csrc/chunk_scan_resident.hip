@@ -29,15 +29,25 @@
 // t-block behind a wave-uniform branch, so the accumulator each product
 // feeds is always known at compile time.
 //
+// Products are formed transposed, y^T = x^T M^T and y_state^T = Hprev C^T:
+// the accumulators hold headdim rows p and token columns t, so x enters as
+// the MFMA's first operand (rows p, contraction over j). gfx950's transposing
+// LDS read (ds_read_b64_tr_b16) gathers such a fragment straight from the
+// row-major x tile: within 16 lanes, lane i supplies the address of row
+// i / 4 at columns 4 (i % 4) .. + 3, and lane 4a + b receives column b of
+// the rows supplied by lanes a, a + 4, a + 8, a + 12. No byte shuffles are
+// needed to split column pairs.
+//
 // LDS layouts (all reads conflict-free):
-//  - x tile: 256 rows of 128 bytes, unpadded; global row j sits at row slot
-//    j ^ ((j >> 2) & 1), so the two half-waves of a dword read (rows j and
-//    j + 4) land on opposite 128-byte halves of the 256-byte bank space. A
-//    wave-instruction of the direct load fills 8 whole slots, so its
-//    per-lane source offset is one constant and the row block is a scalar.
-//  - Hprev: slot rows of N*4 bytes plus one 16-byte pad piece, slot
-//    q*64 + pe*32 + m holding headdim row 2m + pe (fragment reads of 16
-//    consecutive lanes hit 16 distinct bank groups).
+//  - x tile: 256 rows of 128 bytes, unpadded; in rows whose index has bit 1
+//    set the two 64-byte halves are swapped, so the four rows of a
+//    half-wave's transposing read (64 bytes each) fill the four 64-byte
+//    quarters of the 256-byte bank space. A wave-instruction of the direct
+//    load fills 8 whole rows, so its per-lane source offset is one constant
+//    and the row block is a scalar.
+//  - Hprev: slot rows of N*4 bytes plus one 16-byte pad piece, slot p
+//    holding headdim row p (fragment reads of 16 consecutive lanes hit 16
+//    distinct bank groups).
 //  - B tile (C.B^T phase only, in the other buffer): rows padded by one
 //    16-byte piece.
 #include "ssd_device.h"
@@ -221,8 +231,9 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
 
   // per-lane load offsets, fixed for the whole walk
   const uint32_t xrb = (uint32_t)H * P * 2;                  // x / y row stride in bytes
-  const int jl = (lane >> 3) ^ ((lane >> 5) & 1);            // x row (within 8) this lane loads
-  const uint32_t xlane = (uint32_t)jl * xrb + (lane & 7) * 16;
+  const int jl = lane >> 3;                                   // x row (within 8) this lane loads
+  const uint32_t xpiece = (uint32_t)((lane & 7) ^ ((jl & 2) << 1)) * 16;   // its 16 bytes, halves swapped
+  const uint32_t xlane = (uint32_t)jl * xrb + xpiece;
   uint32_t roff[LR];    // Hprev (or G', dt) load offsets of the rest list
 #pragma unroll
   for (int i = 0; i < LR; ++i) {
@@ -233,15 +244,11 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
       int r = s / Cf::HROWP, c = s % Cf::HROWP;
       if (r >= P) r = P - 1;                // tail of the last instruction
       if (c >= Cf::HROWP - 1) c = 0;        // pad piece
-      const int p = 2 * (r % 32) + (r / 32) % 2 + (r / 64) * 64;
-      roff[i] = (uint32_t)(p * N * 4 + c * 16);
+      roff[i] = (uint32_t)(r * N * 4 + c * 16);
     } else {
       roff[i] = (uint32_t)(lane * 16);
     }
   }
-  // (LDS read bases of the x tile, per tile below: with the row swizzle
-  // above, even and odd fragment rows differ by +-1 slot in the upper
-  // half-wave.)
 
   float cbc[9][16];   // resident C.B^T blocks (slots, see above), in AGPRs
   Frag cf[2][KS];     // C fragments of the wave's t-blocks, in AGPRs
@@ -255,9 +262,9 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
   // alive in registers across it.)
   auto issue_tile = [&](const RTile& t, unsigned char* dst) {
     const bool full = t.nvalid == Q;
-    uint32_t xl = xlane, xr = xrb;
+    uint32_t xl = xlane, xr = xrb, xpc = xpiece;
     int jll = jl;
-    asm volatile("" : "+v"(xl), "+v"(jll), "+s"(xr));
+    asm volatile("" : "+v"(xl), "+v"(jll), "+v"(xpc), "+s"(xr));
 #pragma unroll
     for (int i = 0; i < LX; ++i) {
       const int kk = wave + 4 * i;           // 8 x rows per instruction
@@ -265,7 +272,7 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
         lds_dma16_s(t.x + (uint32_t)(kk * 8) * xr, xl, dst + kk * 1024);
       } else {
         const int row = min(kk * 8 + jll, t.nvalid - 1);
-        lds_dma16_s(t.x, (uint32_t)row * xr + (lane & 7) * 16, dst + kk * 1024);
+        lds_dma16_s(t.x, (uint32_t)row * xr + xpc, dst + kk * 1024);
       }
     }
 #pragma unroll
@@ -285,7 +292,11 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
     int lt = lane;
     asm volatile("" : "+v"(lt));
     const int m = lt & 31, g = lt >> 5;
-    const int xbe = 512 * g + 4 * m + 128 * g, xbo = 512 * g + 4 * m - 128 * g;
+    // transposing x reads: lane s supplies row 4 (s / 32) + (s % 16) / 4 of a
+    // 16-row step, headdim columns 16 ((s / 16) % 2) + 4 (s % 4) + 32 pe (the
+    // 64-byte half flipped in rows with bit 1 set); xtr ^ 64 is the pe = 1 read
+    const uint32_t xtr = (uint32_t)(4 * g + ((lt & 15) >> 2)) * 128 +
+                         (((uint32_t)(32 * ((lt >> 4) & 1) + 8 * (lt & 3))) ^ (uint32_t)(64 * ((lt & 15) >> 3)));
     const RTile t = make_rtile<N>(b, k, bk, h, x, Bm, Cm, gcum, dtt, Dp, hprev, y, Tlen, H, G, nc, Tp);
     unsigned char* cur = lds[buf];
     unsigned char* oth = lds[buf ^ 1];
@@ -379,8 +390,8 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
       if (prefetch) issue_tile(nt, oth);
     }
 
-    // carried state: acc[u][pe] = C . Hprev^T, column p = 2m + pe, then rows
-    // scaled by 2^(G'_t)
+    // carried state: acc[u][pe] = Hprev . C^T, row p = 32 pe + drow(r, g),
+    // column t = 32 tb + m, then columns scaled by 2^(G'_t)
     f32x16 acc[2][2];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -409,31 +420,44 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          I::mma(acc[u][pe], cf[u][s0 + i], hf[blk & 1][0][i]);
-          I::mma(acc[u][pe], cf[u][s0 + i], hf[blk & 1][1][i]);
+          I::mma(acc[u][pe], hf[blk & 1][0][i], cf[u][s0 + i]);
+          I::mma(acc[u][pe], hf[blk & 1][1][i], cf[u][s0 + i]);
         }
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u) {
+      const float sc = sE[(u ? tb1 : tb0) * 32 + m];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float sc = sE[(u ? tb1 : tb0) * 32 + drow(r, g)];
         acc[u][0][r] *= sc;
         acc[u][1][r] *= sc;
       }
+    }
 
     // intra-chunk pairs, slot by slot, specialised per wave (straight-line code)
     const unsigned char* xt = cur;
     auto pairs = [&](auto wtag) {
       constexpr int W = decltype(wtag)::value;
-      // x dwords of rows drow(q, g) of j-block jb (columns 2m, 2m+1)
-      auto load_x = [&](int jb, uint32_t* d) {
+      // x^T fragments of j-block jb: d[pe][js] holds headdim row 32 pe + m and,
+      // in k-slot e, token j = 32 jb + 16 js + 4 g + 8 (e / 4) + e % 4 (the
+      // order of the decayed block's k-slots below); two transposing reads each
+      auto load_x = [&](int jb, Frag (*d)[2]) {
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int off = jb * 32 * 128 + 128 * (8 * (q / 4) + q % 4);
-          d[q] = *reinterpret_cast<const uint32_t*>(xt + off + ((q & 1) ? xbo : xbe));
-        }
+        for (int pe = 0; pe < 2; ++pe)
+#pragma unroll
+          for (int js = 0; js < 2; ++js) {
+            uint64_t h2[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const unsigned char* a = xt + (pe ? (xtr ^ 64u) : xtr) + (jb * 32 + 16 * js + 8 * hh) * 128;
+              h2[hh] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                        (__attribute__((address_space(3))) s16x4*)(a)));
+            }
+            const u32x4 w4 = {(uint32_t)h2[0], (uint32_t)(h2[0] >> 32), (uint32_t)h2[1], (uint32_t)(h2[1] >> 32)};
+            d[pe][js] = __builtin_bit_cast(Frag, w4);
+          }
       };
       // each pair's x rows are read one pair ahead, so their LDS latency
       // hides behind the previous pair's work
@@ -444,7 +468,7 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
         for (int c4 = 0; c4 < 4; ++c4) wv[c4] = *reinterpret_cast<const float4*>(&sW[jb * 32 + 8 * c4 + 4 * g]);
         ge = sG[jb * 32 + 31];
       };
-      uint32_t d[16];
+      Frag d[2][2];
       float4 wv[4];
       float ge = 0.f;
       load_x(0, d);   // the first pair of every wave is (t-block W, j-block 0)
@@ -459,25 +483,12 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
       const bool diag = jb == tb;
       const float gtu = u ? gt1 : gt0;
       const int j0 = jb * 32;
-      uint32_t dn[16];
+      Frag dn[2][2];
       float4 wvn[4];
       float gen = 0.f;
       const int en = next_pair(e, W);
       if (en >= 0) load_x(pair_jb(en), dn);
       if (en >= 0 && !pair_diag(en, W)) load_w(pair_jb(en), wvn, gen);
-      Frag xf[2][2];   // [pe][js]
-#pragma unroll
-      for (int js = 0; js < 2; ++js) {
-        u32x4 e0, e1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t lo2 = d[js * 8 + 2 * i], hi2 = d[js * 8 + 2 * i + 1];
-          e0[i] = __builtin_amdgcn_perm(hi2, lo2, 0x05040100u);   // low halves: column 2m
-          e1[i] = __builtin_amdgcn_perm(hi2, lo2, 0x07060302u);   // high halves: column 2m + 1
-        }
-        xf[0][js] = __builtin_bit_cast(Frag, e0);
-        xf[1][js] = __builtin_bit_cast(Frag, e1);
-      }
       float v[16];
       if (!diag) {
         // every t is past the whole j-block: 2^(G'_t - G'_j) = 2^(G'_t - G'_end) 2^(G'_end - G'_j)
@@ -523,12 +534,14 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
         const Frag ahi = __builtin_bit_cast(Frag, uh), alo = __builtin_bit_cast(Frag, ul);
 #pragma unroll
         for (int pe = 0; pe < 2; ++pe) {
-          I::mma(acc[u][pe], ahi, xf[pe][js]);
-          I::mma(acc[u][pe], alo, xf[pe][js]);
+          I::mma(acc[u][pe], d[pe][js], ahi);
+          I::mma(acc[u][pe], d[pe][js], alo);
         }
       }
 #pragma unroll
-      for (int q = 0; q < 16; ++q) d[q] = dn[q];
+      for (int pe = 0; pe < 2; ++pe)
+#pragma unroll
+        for (int js = 0; js < 2; ++js) d[pe][js] = dn[pe][js];
       if (en >= 0 && !pair_diag(en, W)) {
 #pragma unroll
         for (int c4 = 0; c4 < 4; ++c4) wv[c4] = wvn[c4];
@@ -546,14 +559,16 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
 
     // y goes out through LDS in 16-byte row pieces: per t-block, the wave
     // writes its 32 x 64 block (bf16, 128-byte rows) into its own staging
-    // area, one dword (columns 2m, 2m+1) per lane per row, reads it back as
-    // 16-byte pieces and stores 4 of them per lane, through a buffer resource
-    // over the tile's valid rows (rows past a ragged sequence are dropped by
-    // its range check). One wave's LDS operations run in order, so the
-    // staging area needs no barrier.
+    // area, 8 bytes (headdim columns 32 pe + 8 c + 4 g .. + 3 of its token
+    // row m) at a time, reads it back as 16-byte pieces and stores 4 of them
+    // per lane, through a buffer resource over the tile's valid rows (rows
+    // past a ragged sequence are dropped by its range check). In staging row
+    // t, 16-byte piece c sits at c ^ ((t / 2) % 8), which spreads the 32
+    // rows a half-wave writes over the banks. One wave's LDS operations run
+    // in order, so the staging area needs no barrier.
     {
       unsigned char* ys_lds = ystage + wave * 4096;
-      const uint32_t wlane = (uint32_t)(4 * g) * 128 + 4 * m;
+      const uint32_t wrow = (uint32_t)m * 128 + 8 * (uint32_t)g, wsw = (uint32_t)(m >> 1) & 7;
       const int pr = lane / 8, pc = lane % 8;   // piece i * 64 + lane: row 8 i + pr, 16-byte piece pc
       uint32_t plane = (uint32_t)pr * xrb + (uint32_t)pc * 16;
       uint32_t xrbs = xrb;
@@ -562,13 +577,18 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          *reinterpret_cast<uint32_t*>(ys_lds + wlane + (8 * (r / 4) + r % 4) * 128) =
-              pack_bf16x2(acc[u][0][r], acc[u][1][r]);
+        for (int pe = 0; pe < 2; ++pe)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint2 v2 = make_uint2(pack_bf16x2(acc[u][pe][4 * c], acc[u][pe][4 * c + 1]),
+                                        pack_bf16x2(acc[u][pe][4 * c + 2], acc[u][pe][4 * c + 3]));
+            *reinterpret_cast<uint2*>(ys_lds + wrow + (((uint32_t)(4 * pe + c)) ^ wsw) * 16) = v2;
+          }
         const uint32_t row0 = (uint32_t)((u ? tb1 : tb0) * 32);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(ys_lds + (8 * i + pr) * 128 + pc * 16);
+          const uint32_t rsw = (uint32_t)(4 * (i & 1) + (pr >> 1));   // ((8 i + pr) / 2) % 8
+          const u32x4 v = *reinterpret_cast<const u32x4*>(ys_lds + (8 * i + pr) * 128 + ((uint32_t)pc ^ rsw) * 16);
           __builtin_amdgcn_raw_buffer_store_b128(v, yr, plane + (row0 + 8 * i) * xrbs, 0, 0);
         }
       }
