@@ -20,7 +20,12 @@
 // chunk, its N states in registers; a workgroup takes 256 channels of one
 // chunk, so the chunk's B and C rows are staged once in LDS, and each wave
 // stages its 64 channels' x and delta in 16-token column blocks (64-byte row
-// pieces, then each lane walks its own row) and y the same way back.
+// pieces, then each lane walks its own row) and y the same way back, in
+// the x tile (a lane overwrites the x values of its own row it has read).
+// Two column blocks are loaded ahead: the scan itself is short, and one
+// memory round trip per block would set the time; at about 100 registers
+// per lane four waves fit per SIMD, so a 1024-channel, 2048-token, 8-row
+// call runs all its waves at once.
 #include "ssd_device.h"
 #include "s6_launch.h"
 
@@ -32,27 +37,39 @@ constexpr int kChunk = 64;    // tokens per chunk
 constexpr int kSub = 16;      // tokens per staged column block
 constexpr int kWaves = 4;     // waves per workgroup, 64 channels each
 
-// one wave's 64 rows x kSub tokens of a [rows][L] array into LDS
-__device__ __forceinline__ void stage_rows(float (*dst)[kSub + 1], const float* src, int64_t row0, int rows_valid,
-                                           int64_t L, int64_t t, int lane, bool vec) {
+// A lane's share of one wave's 64 rows x kSub tokens of a [rows][L] array:
+// rows 16 i + lane / 4, tokens t + 4 (lane % 4) .. + 3 (zeros past the
+// sequence or the channels).
+__device__ __forceinline__ void load_rows(float4 (&v)[4], const float* src, int64_t row0, int rows_valid,
+                                          int64_t L, int64_t t, int lane, bool vec) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = i * 16 + lane / 4, piece = lane % 4;
     const int64_t tk = t + piece * 4;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    float e[4] = {0.f, 0.f, 0.f, 0.f};
     if (r < rows_valid) {
       const float* p = src + (row0 + r) * L + tk;
       if (vec && tk + 3 < L) {
         const float4 q = *reinterpret_cast<const float4*>(p);
-        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+        e[0] = q.x; e[1] = q.y; e[2] = q.z; e[3] = q.w;
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          if (tk + j < L) v[j] = p[j];
+          if (tk + j < L) e[j] = p[j];
       }
     }
+    v[i] = make_float4(e[0], e[1], e[2], e[3]);
+  }
+}
+// ... and those values into the wave's LDS tile [64 rows][kSub + 1]
+__device__ __forceinline__ void store_rows(float (*dst)[kSub + 1], const float4 (&v)[4], int lane) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dst[r][piece * 4 + j] = v[j];
+  for (int i = 0; i < 4; ++i) {
+    const int r = i * 16 + lane / 4, piece = lane % 4;
+    dst[r][piece * 4 + 0] = v[i].x;
+    dst[r][piece * 4 + 1] = v[i].y;
+    dst[r][piece * 4 + 2] = v[i].z;
+    dst[r][piece * 4 + 3] = v[i].w;
   }
 }
 
@@ -66,7 +83,6 @@ __global__ __launch_bounds__(256) void s6_chunk(const float* __restrict__ x, con
   __shared__ __attribute__((aligned(16))) float sC[FINAL ? N : 1][kChunk];
   __shared__ float sx[kWaves][64][kSub + 1];
   __shared__ float sd[kWaves][64][kSub + 1];
-  __shared__ float sy[FINAL ? kWaves : 1][64][kSub + 1];
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int64_t b = blockIdx.z, c = blockIdx.y;
   const int dw = blockIdx.x * 256 + wave * 64;          // the wave's first channel
@@ -75,6 +91,16 @@ __global__ __launch_bounds__(256) void s6_chunk(const float* __restrict__ x, con
   const int rows_valid = D - dw;                         // channels of this wave (may be <= 0)
   const int64_t t0 = c * kChunk;
   const int nt = L - t0 < kChunk ? (int)(L - t0) : kChunk;
+  const int64_t row0 = b * D + dw;
+  constexpr int NB = kChunk / kSub;
+  // two column blocks in flight: blocks 0 and 1 now, block kb + 2 into the
+  // registers block kb has just left
+  float4 xr[2][4], dr[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    load_rows(xr[kb], x, row0, rows_valid, L, t0 + kb * kSub, lane, vec);
+    load_rows(dr[kb], dl, row0, rows_valid, L, t0 + kb * kSub, lane, vec);
+  }
 
   for (int idx = tid; idx < N * kChunk; idx += 256) {
     const int n = idx / kChunk, k = idx % kChunk;
@@ -89,13 +115,19 @@ __global__ __launch_bounds__(256) void s6_chunk(const float* __restrict__ x, con
     h[n] = (FINAL && valid) ? hin[(((int64_t)b * D + d) * nc + c) * N + n] : 0.f;
   }
   float dsum = 0.f;
-  const int64_t row0 = b * D + dw;
   __syncthreads();   // B and C staged
   // From here each wave touches only its own tiles, and one wave's LDS
   // operations complete in program order: no workgroup barrier is needed.
-  for (int ks = 0; ks < nt; ks += kSub) {
-    stage_rows(sx[wave], x, row0, rows_valid, L, t0 + ks, lane, vec);
-    stage_rows(sd[wave], dl, row0, rows_valid, L, t0 + ks, lane, vec);
+#pragma unroll
+  for (int kb = 0; kb < NB; ++kb) {
+    const int ks = kb * kSub;
+    if (ks >= nt) break;
+    store_rows(sx[wave], xr[kb & 1], lane);
+    store_rows(sd[wave], dr[kb & 1], lane);
+    if (kb + 2 < NB) {
+      load_rows(xr[kb & 1], x, row0, rows_valid, L, t0 + (kb + 2) * kSub, lane, vec);
+      load_rows(dr[kb & 1], dl, row0, rows_valid, L, t0 + (kb + 2) * kSub, lane, vec);
+    }
     const int kn = nt - ks < kSub ? nt - ks : kSub;
     // four tokens at a time: B and C of a state for 4 tokens in one 16-byte
     // read. Past the sequence x, delta, B and C are zero, so the padded
@@ -124,8 +156,9 @@ __global__ __launch_bounds__(256) void s6_chunk(const float* __restrict__ x, con
         }
       }
       if (FINAL) {
+        // y replaces x in the lane's own row: those x values are read above
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sy[wave][lane][k4 + j] = yv[j];
+        for (int j = 0; j < 4; ++j) sx[wave][lane][k4 + j] = yv[j];
       }
     }
     if (FINAL) {
@@ -135,12 +168,12 @@ __global__ __launch_bounds__(256) void s6_chunk(const float* __restrict__ x, con
         if (r >= rows_valid) continue;
         float* p = y + (row0 + r) * L + t0 + ks + piece * 4;
         if (vec && piece * 4 + 3 < kn) {
-          *reinterpret_cast<float4*>(p) = make_float4(sy[wave][r][piece * 4], sy[wave][r][piece * 4 + 1],
-                                                      sy[wave][r][piece * 4 + 2], sy[wave][r][piece * 4 + 3]);
+          *reinterpret_cast<float4*>(p) = make_float4(sx[wave][r][piece * 4], sx[wave][r][piece * 4 + 1],
+                                                      sx[wave][r][piece * 4 + 2], sx[wave][r][piece * 4 + 3]);
         } else {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            if (piece * 4 + j < kn) p[j] = sy[wave][r][piece * 4 + j];
+            if (piece * 4 + j < kn) p[j] = sx[wave][r][piece * 4 + j];
         }
       }
     }
