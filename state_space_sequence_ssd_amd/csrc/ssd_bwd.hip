@@ -317,10 +317,13 @@ __global__ __launch_bounds__(256) void mask_decay(const float* __restrict__ CB, 
     }
   }
   __syncthreads();   // every row has read DX before it is overwritten
+  // Entries above the diagonal are read only inside the GT x GT blocks on
+  // it (the causal products run their contraction from the first row of an
+  // output tile, or to its last): only those are cleared.
   for (int j = threadIdx.x; j < Q; j += blockDim.x) {
     const float gj = sg[j], dj = sd[j];
     float cz = 0.f, cw = 0.f;
-    for (int i = 0; i < Q; ++i) {
+    for (int i = (j / GT) * GT; i < Q; ++i) {
       const int64_t o = (int64_t)i * Q + j;
       if (i < j) {
         w1[o] = 0.f;
@@ -454,9 +457,11 @@ __global__ __launch_bounds__(256) void finish_chunk(const BwdProblem p) {
 
 // sum over the heads of each group of the Q x Q blocks [bt][nc][H][Q][Q]
 // -> [bt][nc][G][Q][Q]
-__global__ void sum_heads(const float* __restrict__ in, float* __restrict__ out, int hpg, int64_t QQ, int64_t total) {
+__global__ void sum_heads(const float* __restrict__ in, float* __restrict__ out, int hpg, int Q, int64_t QQ,
+                          int64_t total) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t o = i % QQ, bkg = i / QQ;   // (b * nc + k) * G + g
+    if ((o % Q) / GT > (o / Q) / GT) continue;   // a GT x GT block above the diagonal: never read
     const float* src = in + bkg * hpg * QQ + o;
     float acc = 0.f;
     for (int j = 0; j < hpg; ++j) acc += src[j * QQ];
@@ -620,7 +625,7 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
   // needed), and the state products sum the heads' parts inside the kernel
   const int64_t nsum = bt * nc * G * QQ;
   if (e == hipSuccess && nsum > 0) {
-    hipLaunchKernelGGL(sum_heads, dim3(grid_for(nsum)), dim3(256), 0, s, p.DX, p.CB, hpg, QQ, nsum);
+    hipLaunchKernelGGL(sum_heads, dim3(grid_for(nsum)), dim3(256), 0, s, p.DX, p.CB, hpg, Qi, QQ, nsum);
     ok(hipGetLastError());
   }
   {
