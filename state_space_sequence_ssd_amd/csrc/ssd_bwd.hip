@@ -279,17 +279,21 @@ __global__ void chunk_recursion(const float* __restrict__ S, const float* __rest
 
 // Per (b, k, h): the masked, decayed blocks W1s = L o CB o dt_j (in its own
 // array) and W2s = L o DX o dt_j (over DX, in place), zero above the
-// diagonal, and the sums the time gradient needs: rows and columns of
-// Z = L o CB o DX o dt_j, and the columns of L o CB o DX. The row sums are
-// taken first, one wave per row, while DX is still intact; then one thread
-// per column writes the blocks. Fixed summation orders: the result does not
+// diagonal where they are read, and the sums the time gradient needs: rows
+// and columns of Z = L o CB o DX o dt_j, and the columns of L o CB o DX.
+// One thread per column walks the rows once: it writes the blocks, keeps
+// its column sums, and leaves its Z entries of MD_ROWS rows in LDS, where
+// one wave per row adds them up (lane l takes columns l, l + 64, ...; then
+// a butterfly over the lanes). Fixed summation orders: the result does not
 // depend on scheduling.
+constexpr int MD_ROWS = 16;
 __global__ __launch_bounds__(256) void mask_decay(const float* __restrict__ CB, float* __restrict__ DXW2,
                                                   float* __restrict__ W1, const float* __restrict__ gcum,
                                                   const float* __restrict__ dtt, float* __restrict__ rowZ,
                                                   float* __restrict__ colZ, float* __restrict__ colW,
                                                   int Q, int H, int hpg, int64_t nc, int64_t Tp) {
   __shared__ float sg[256], sd[256];
+  __shared__ float sz[MD_ROWS][256 + 4];
   const int h = blockIdx.x % H;
   const int64_t k = (blockIdx.x / H) % nc, b = blockIdx.x / (H * nc);
   const int64_t QQ = (int64_t)Q * Q;
@@ -302,41 +306,48 @@ __global__ __launch_bounds__(256) void mask_decay(const float* __restrict__ CB, 
     sd[i] = dtt[tb + i];
   }
   __syncthreads();
-  {
-    // row sums: one wave per row at a time, lanes across the row
-    const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    for (int i = wave; i < Q; i += blockDim.x / 64) {
-      float rz = 0.f;
-      for (int j = lane; j <= i; j += 64) {
+  // Q <= 256 = blockDim.x: thread j owns column j. Entries above the
+  // diagonal are read only inside the GT x GT blocks on it (the causal
+  // products run their contraction from the first row of an output tile, or
+  // to its last): only those are cleared.
+  const int j = threadIdx.x, wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const bool col = j < Q;
+  const float gj = col ? sg[j] : 0.f, dj = col ? sd[j] : 0.f;
+  const int ifirst = (j / GT) * GT;
+  float cz = 0.f, cw = 0.f;
+  for (int i0 = 0; i0 < Q; i0 += MD_ROWS) {
+    for (int r = 0; r < MD_ROWS; ++r) {
+      const int i = i0 + r;
+      float z = 0.f;
+      if (col && i >= ifirst) {
         const int64_t o = (int64_t)i * Q + j;
-        rz += exp2_hw(sg[i] - sg[j]) * cb[o] * dx[o] * sd[j];
+        if (i < j) {
+          w1[o] = 0.f;
+          dx[o] = 0.f;
+        } else {
+          const float L = exp2_hw(sg[i] - gj);
+          const float lcb = L * cb[o], d = dx[o];
+          w1[o] = lcb * dj;
+          dx[o] = L * d * dj;
+          z = lcb * d * dj;
+          cz += z;
+          cw += lcb * d;
+        }
       }
+      sz[r][j] = z;
+    }
+    __syncthreads();
+    for (int rr = 0; rr < MD_ROWS / 4; ++rr) {
+      const int r = wave * (MD_ROWS / 4) + rr;
+      float v = 0.f;
+      for (int jj = lane; jj < Q; jj += 64) v += sz[r][jj];
 #pragma unroll
-      for (int off = 32; off >= 1; off /= 2) rz += __shfl_xor(rz, off, 64);
-      if (lane == 0) rowZ[tb + i] = rz;
+      for (int off = 32; off >= 1; off /= 2) v += __shfl_xor(v, off, 64);
+      if (lane == 0) rowZ[tb + i0 + r] = v;
     }
+    __syncthreads();   // the rows are summed before the next block overwrites them
   }
-  __syncthreads();   // every row has read DX before it is overwritten
-  // Entries above the diagonal are read only inside the GT x GT blocks on
-  // it (the causal products run their contraction from the first row of an
-  // output tile, or to its last): only those are cleared.
-  for (int j = threadIdx.x; j < Q; j += blockDim.x) {
-    const float gj = sg[j], dj = sd[j];
-    float cz = 0.f, cw = 0.f;
-    for (int i = (j / GT) * GT; i < Q; ++i) {
-      const int64_t o = (int64_t)i * Q + j;
-      if (i < j) {
-        w1[o] = 0.f;
-        dx[o] = 0.f;
-        continue;
-      }
-      const float L = exp2_hw(sg[i] - gj);
-      const float lcb = L * cb[o], d = dx[o];
-      w1[o] = lcb * dj;
-      dx[o] = L * d * dj;
-      cz += lcb * d * dj;
-      cw += lcb * d;
-    }
+  if (col) {
     colZ[tb + j] = cz;
     colW[tb + j] = cw;
   }
