@@ -260,13 +260,15 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
   // (The per-lane and per-instruction offsets below are derived from values
   // laundered per call, so they are not hoisted out of the walk and kept
   // alive in registers across it.)
-  auto issue_tile = [&](const RTile& t, unsigned char* dst) {
+  // Loads q0 .. q1 - 1 of the tile's LT: x first, then Hprev, G' and dt.
+  auto issue_part = [&](const RTile& t, unsigned char* dst, int q0, int q1) {
     const bool full = t.nvalid == Q;
     uint32_t xl = xlane, xr = xrb, xpc = xpiece;
     int jll = jl;
     asm volatile("" : "+v"(xl), "+v"(jll), "+v"(xpc), "+s"(xr));
 #pragma unroll
     for (int i = 0; i < LX; ++i) {
+      if (i < q0 || i >= q1) continue;
       const int kk = wave + 4 * i;           // 8 x rows per instruction
       if (full) {
         lds_dma16_s(t.x + (uint32_t)(kk * 8) * xr, xl, dst + kk * 1024);
@@ -277,6 +279,7 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
     }
 #pragma unroll
     for (int i = 0; i < LR; ++i) {
+      if (LX + i < q0 || LX + i >= q1) continue;
       int rho = wave + i * 4;
       if (rho >= IH + IG) rho %= IH + IG;
       if (rho < IH)
@@ -285,6 +288,7 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
         lds_dma16_s(rho == IH ? t.gc : t.dtc, roff[i], dst + Cf::GOFF + (rho - IH) * 1024);
     }
   };
+  auto issue_tile = [&](const RTile& t, unsigned char* dst) { issue_part(t, dst, 0, Cf::LT); };
 
   for (int64_t pos = lo; pos < hi; ++pos) {
     // lane-derived values are re-derived per tile from a laundered lane id:
@@ -384,11 +388,13 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
       }
     }
     bool prefetch = false;
+    RTile nt = t;
     if (has_next) {
-      const RTile nt = make_rtile<N>(b, k, bk, h, x, Bm, Cm, gcum, dtt, Dp, hprev, y, Tlen, H, G, nc, Tp);
+      nt = make_rtile<N>(b, k, bk, h, x, Bm, Cm, gcum, dtt, Dp, hprev, y, Tlen, H, G, nc, Tp);
       prefetch = nt.ckey == ckey_cached;
-      if (prefetch) issue_tile(nt, oth);
     }
+    // (its loads are issued among the carried-state MFMAs below: a wave that
+    // waits to issue a direct load leaves the MFMAs it has issued running)
 
     // carried state: acc[u][pe] = Hprev . C^T, row p = 32 pe + drow(r, g),
     // column t = 32 tb + m, then columns scaled by 2^(G'_t)
@@ -423,6 +429,7 @@ void ssd_chunk_scan_resident(const bf16* __restrict__ x, const bf16* __restrict_
           I::mma(acc[u][pe], hf[blk & 1][0][i], cf[u][s0 + i]);
           I::mma(acc[u][pe], hf[blk & 1][1][i], cf[u][s0 + i]);
         }
+      if (prefetch) issue_part(nt, oth, blk * Cf::LT / (2 * HB), (blk + 1) * Cf::LT / (2 * HB));
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
