@@ -139,6 +139,69 @@ __device__ __forceinline__ void stage_k(float (*sa)[GT + 4], float (*sb)[GT + 4]
   }
 }
 
+// The 16-byte path of stage_k in two halves, so the loads of the next slice
+// can be in flight while this slice's MFMAs run: kload reads a thread's
+// pieces of A and B (and the scale factors) into registers, kstore applies
+// the scales and writes them into LDS.
+struct KSlice {
+  float4 a, b, sa4;   // A piece, B piece, A scales (k scales or row scales)
+  float sa1;          // the other A scale (a row scale or a k scale)
+};
+__device__ __forceinline__ void kload(KSlice& v, const Operand& ao, const Operand& bo, const float* A,
+                                      const float* B, const float* ks, const float* ra, int m0, int n0, int k0,
+                                      int M, int N, int tid) {
+  const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f), o4 = make_float4(1.f, 1.f, 1.f, 1.f);
+  v.a = z4;
+  v.sa4 = o4;
+  v.sa1 = 1.f;
+  if (ao.cs == 1) {
+    const int mm = tid / 4, kq = (tid % 4) * 4, m = m0 + mm;
+    if (m < M) {
+      v.a = *reinterpret_cast<const float4*>(A + m * ao.rs + k0 + kq);
+      if (ks) v.sa4 = *reinterpret_cast<const float4*>(ks + k0 + kq);
+      if (ra) v.sa1 = ra[m];
+    }
+  } else {
+    const int kk = tid / 16, mq = (tid % 16) * 4, k = k0 + kk;
+    if (m0 + mq < M) {
+      v.a = *reinterpret_cast<const float4*>(A + (m0 + mq) + k * ao.cs);
+      if (ks) v.sa1 = ks[k];
+      if (ra) v.sa4 = make_float4(ra[m0 + mq], ra[m0 + mq + 1], ra[m0 + mq + 2], ra[m0 + mq + 3]);
+    }
+  }
+  v.b = z4;
+  if (bo.cs == 1) {
+    const int kb = tid / 16, nq = (tid % 16) * 4;
+    if (n0 + nq < N) v.b = *reinterpret_cast<const float4*>(B + (k0 + kb) * bo.rs + n0 + nq);
+  } else {
+    const int nn = tid / 4, kq = (tid % 4) * 4, n = n0 + nn;
+    if (n < N) v.b = *reinterpret_cast<const float4*>(B + (k0 + kq) + n * bo.cs);
+  }
+}
+__device__ __forceinline__ void kstore(float (*sa)[GT + 4], float (*sb)[GT + 4], const KSlice& v, const Operand& ao,
+                                       const Operand& bo, int tid) {
+  // (x k scale) then (x row scale), as stage_k multiplies
+  const bool kfirst = ao.cs == 1;   // sa4 holds the k scales
+  const float4 a = kfirst ? make_float4(v.a.x * v.sa4.x * v.sa1, v.a.y * v.sa4.y * v.sa1, v.a.z * v.sa4.z * v.sa1,
+                                        v.a.w * v.sa4.w * v.sa1)
+                          : make_float4(v.a.x * v.sa1 * v.sa4.x, v.a.y * v.sa1 * v.sa4.y, v.a.z * v.sa1 * v.sa4.z,
+                                        v.a.w * v.sa1 * v.sa4.w);
+  if (ao.cs == 1) {
+    const int mm = tid / 4, kq = (tid % 4) * 4;
+    sa[kq][mm] = a.x; sa[kq + 1][mm] = a.y; sa[kq + 2][mm] = a.z; sa[kq + 3][mm] = a.w;
+  } else {
+    const int kk = tid / 16, mq = (tid % 16) * 4;
+    *reinterpret_cast<float4*>(&sa[kk][mq]) = a;
+  }
+  if (bo.cs == 1) {
+    const int kb = tid / 16, nq = (tid % 16) * 4;
+    *reinterpret_cast<float4*>(&sb[kb][nq]) = v.b;
+  } else {
+    const int nn = tid / 4, kq = (tid % 4) * 4;
+    sb[kq][nn] = v.b.x; sb[kq + 1][nn] = v.b.y; sb[kq + 2][nn] = v.b.z; sb[kq + 3][nn] = v.b.w;
+  }
+}
+
 __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float sa[GK][GT + 4];
   __shared__ __attribute__((aligned(16))) float sb[GK][GT + 4];
@@ -160,13 +223,28 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
     const float* A = g.a.p + g.a.base(z0, z1, z2);
     const float* B = g.b.p + g.b.base(z0, z1, z2);
     const float* ks = g.ksc.p ? g.ksc.p + g.ksc.base(z0, z1, z2) : nullptr;
-    for (int k0 = kbeg; k0 < kend; k0 += GK) {
-      stage_k(sa, sb, g.a, g.b, A, B, ks, nullptr, m0, n0, k0, g.M, g.N, kend, g.vec, tid);
-      __syncthreads();
+    if (g.vec) {
+      // the next slice's loads are issued before this slice's MFMAs
+      KSlice v;
+      if (kbeg < kend) kload(v, g.a, g.b, A, B, ks, nullptr, m0, n0, kbeg, g.M, g.N, tid);
+      for (int k0 = kbeg; k0 < kend; k0 += GK) {
+        kstore(sa, sb, v, g.a, g.b, tid);
+        __syncthreads();
+        if (k0 + GK < kend) kload(v, g.a, g.b, A, B, ks, nullptr, m0, n0, k0 + GK, g.M, g.N, tid);
 #pragma unroll
-      for (int kk = 0; kk < GK; kk += 2)
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[kk + lg][wm + lm], sb[kk + lg][wn + lm], acc, 0, 0, 0);
-      __syncthreads();
+        for (int kk = 0; kk < GK; kk += 2)
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[kk + lg][wm + lm], sb[kk + lg][wn + lm], acc, 0, 0, 0);
+        __syncthreads();
+      }
+    } else {
+      for (int k0 = kbeg; k0 < kend; k0 += GK) {
+        stage_k(sa, sb, g.a, g.b, A, B, ks, nullptr, m0, n0, k0, g.M, g.N, kend, g.vec, tid);
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < GK; kk += 2)
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[kk + lg][wm + lm], sb[kk + lg][wn + lm], acc, 0, 0, 0);
+        __syncthreads();
+      }
     }
   }
   if (g.a2.p) {
@@ -180,13 +258,27 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
       const float* A = g.a2.p + g.a2.base(z0, z1, zh);
       const float* B = g.b2.p + g.b2.base(z0, z1, zh);
       const float* ra = (g.hsum > 0 && g.rsc2.p) ? g.rsc2.p + g.rsc2.base(z0, z1, zh) : nullptr;
-      for (int k0 = 0; k0 < g.K2; k0 += GK) {
-        stage_k(sa, sb, g.a2, g.b2, A, B, nullptr, ra, m0, n0, k0, g.M, g.N, g.K2, g.vec, tid);
-        __syncthreads();
+      if (g.vec) {
+        KSlice v;
+        if (g.K2 > 0) kload(v, g.a2, g.b2, A, B, nullptr, ra, m0, n0, 0, g.M, g.N, tid);
+        for (int k0 = 0; k0 < g.K2; k0 += GK) {
+          kstore(sa, sb, v, g.a2, g.b2, tid);
+          __syncthreads();
+          if (k0 + GK < g.K2) kload(v, g.a2, g.b2, A, B, nullptr, ra, m0, n0, k0 + GK, g.M, g.N, tid);
 #pragma unroll
-        for (int kk = 0; kk < GK; kk += 2)
-          acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[kk + lg][wm + lm], sb[kk + lg][wn + lm], acc2, 0, 0, 0);
-        __syncthreads();
+          for (int kk = 0; kk < GK; kk += 2)
+            acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[kk + lg][wm + lm], sb[kk + lg][wn + lm], acc2, 0, 0, 0);
+          __syncthreads();
+        }
+      } else {
+        for (int k0 = 0; k0 < g.K2; k0 += GK) {
+          stage_k(sa, sb, g.a2, g.b2, A, B, nullptr, ra, m0, n0, k0, g.M, g.N, g.K2, g.vec, tid);
+          __syncthreads();
+#pragma unroll
+          for (int kk = 0; kk < GK; kk += 2)
+            acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[kk + lg][wm + lm], sb[kk + lg][wn + lm], acc2, 0, 0, 0);
+          __syncthreads();
+        }
       }
     }
   }
