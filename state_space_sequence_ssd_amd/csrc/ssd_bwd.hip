@@ -65,6 +65,7 @@ struct GemmArgs {
   Operand a2, b2, rsc2;
   int K2;
   int hsum;                    // > 0: the second product sums this many heads (see bwd_gemm)
+  int cvec;                    // output rows contiguous and 16-byte aligned (see gemm())
 };
 
 // Stage one GK-deep slice of A (GT rows from m0) and B (GT columns from n0)
@@ -202,7 +203,7 @@ __device__ __forceinline__ void kstore(float (*sa)[GT + 4], float (*sb)[GT + 4],
   }
 }
 
-__global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bwd_gemm(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float sa[GK][GT + 4];
   __shared__ __attribute__((aligned(16))) float sb[GK][GT + 4];
   const int tiles_n = (g.N + GT - 1) / GT;
@@ -285,6 +286,29 @@ __global__ __launch_bounds__(256) void bwd_gemm(GemmArgs g) {
   float* Cp = const_cast<float*>(g.c.p) + g.c.base(z0, z1, z2);
   const float* rs = g.rsc.p ? g.rsc.p + g.rsc.base(z0, z1, z2) : nullptr;
   const float* rs2 = (g.hsum == 0 && g.rsc2.p) ? g.rsc2.p + g.rsc2.base(z0, z1, z2) : nullptr;
+  if (g.cvec && g.beta == 0.f && m0 + GT <= g.M && n0 + GT <= g.N) {
+    // whole tile, row-major output: each wave's 32 x 32 quarter goes out
+    // through LDS as 16-byte row pieces, 4 stores per lane instead of 16
+    // (rows of 32 values plus 8 of padding: the two half-waves write rows 4
+    // apart, 32 banks apart)
+    __shared__ __attribute__((aligned(16))) float so[4][32][40];
+    float (*q)[40] = so[wave];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int mr = drow(r, lg);
+      float v = (rs ? rs[m0 + wm + mr] : 1.f) * acc[r];
+      if (g.a2.p) v = fmaf(rs2 ? rs2[m0 + wm + mr] : 1.f, acc2[r], v);
+      q[mr][lm] = v;
+    }
+    // a wave's own LDS operations complete in order: no barrier
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * i + lane / 8, c4 = (lane % 8) * 4;
+      const float4 v = *reinterpret_cast<const float4*>(&q[row][c4]);
+      *reinterpret_cast<float4*>(Cp + (int64_t)(m0 + wm + row) * g.c.rs + n0 + wn + c4) = v;
+    }
+    return;
+  }
   const int n = n0 + wn + lm;
   if (n >= g.N) return;
 #pragma unroll
@@ -317,8 +341,12 @@ hipError_t gemm(const Operand& a, const Operand& b, const Operand& c, const Oper
   const Operand no{nullptr, 0, 0, 0, 0, 0, 1};
   const int vec = al4(a) && al4(b) && (!ksc.p || al4(Operand{ksc.p, 1, 1, ksc.s0, ksc.s1, ksc.s2, ksc.d2})) &&
                   K % 16 == 0 && M % 4 == 0 && N % 4 == 0 && (!a2 || (al4(*a2) && al4(*b2) && K2 % 16 == 0));
+  // 16-byte output pieces: unit column stride, row and batch strides
+  // multiples of 4, base 16-byte aligned
+  const int cvec = c.cs == 1 && (reinterpret_cast<uintptr_t>(c.p) & 15) == 0 && c.rs % 4 == 0 && c.s0 % 4 == 0 &&
+                   c.s1 % 4 == 0 && c.s2 % 4 == 0;
   GemmArgs g{a, b, c, rsc, ksc, M, N, K, Z1, Z2, beta, shape, vec, a2 ? *a2 : no, b2 ? *b2 : no,
-             rsc2 ? *rsc2 : no, K2, hsum};
+             rsc2 ? *rsc2 : no, K2, hsum, cvec};
   const int64_t tiles = (int64_t)((M + GT - 1) / GT) * ((N + GT - 1) / GT);
   const int64_t Z = (int64_t)Z0 * Z1 * Z2;
   if (Z == 0 || tiles == 0) return hipSuccess;
