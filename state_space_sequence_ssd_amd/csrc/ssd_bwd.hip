@@ -436,6 +436,18 @@ __global__ __launch_bounds__(256) void mask_decay(const float* __restrict__ CB, 
   const int ifirst = (j / GT) * GT;
   float cz = 0.f, cw = 0.f;
   for (int i0 = 0; i0 < Q; i0 += MD_ROWS) {
+    // the block's loads first, so they are in flight together (issued after
+    // the previous block's stores, a load would wait for them)
+    float cbv[MD_ROWS], dxv[MD_ROWS];
+#pragma unroll
+    for (int r = 0; r < MD_ROWS; ++r) {
+      const int i = i0 + r;
+      const int64_t o = (int64_t)i * Q + j;
+      const bool lower = col && i >= j;
+      cbv[r] = lower ? cb[o] : 0.f;
+      dxv[r] = lower ? dx[o] : 0.f;
+    }
+#pragma unroll
     for (int r = 0; r < MD_ROWS; ++r) {
       const int i = i0 + r;
       float z = 0.f;
@@ -446,7 +458,7 @@ __global__ __launch_bounds__(256) void mask_decay(const float* __restrict__ CB, 
           dx[o] = 0.f;
         } else {
           const float L = exp2_hw(sg[i] - gj);
-          const float lcb = L * cb[o], d = dx[o];
+          const float lcb = L * cbv[r], d = dxv[r];
           w1[o] = lcb * dj;
           dx[o] = L * d * dj;
           z = lcb * d * dj;
