@@ -372,6 +372,37 @@ __global__ void pad_rows(const T* __restrict__ src, float* __restrict__ dst, int
   }
 }
 
+// The same, 8 values per thread (W a multiple of 8, both arrays 16-byte
+// aligned): one 16-byte (bf16) or two (fp32) loads and two 16-byte stores,
+// so a thread's loads are not each issued behind its previous store.
+template <typename T> __device__ __forceinline__ void ld8(const T* p, float* v);
+template <> __device__ __forceinline__ void ld8<float>(const float* p, float* v) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <> __device__ __forceinline__ void ld8<bf16>(const bf16* p, float* v) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <typename T>
+__global__ void pad_rows8(const T* __restrict__ src, float* __restrict__ dst, int64_t T_, int64_t Tp, int64_t W,
+                          int64_t total8) {
+  const int64_t W8 = W / 8;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total8; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t w8 = i % W8, t = (i / W8) % Tp, b = i / (W8 * Tp);
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (t < T_) ld8(src + (b * T_ + t) * W + 8 * w8, v);
+    float4* d = reinterpret_cast<float4*>(dst + 8 * i);
+    d[0] = make_float4(v[0], v[1], v[2], v[3]);
+    d[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
 __global__ void exp2_all(const float* __restrict__ g, float* __restrict__ e, int64_t n) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
     e[i] = exp2_hw(g[i]);
@@ -696,18 +727,27 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
   };
   // 1. inputs to padded fp32, and 2^(G')
   const int64_t nx = bt * Tp * H * P, nb = bt * Tp * G * N;
-  if (p.io == 1) {
-    hipLaunchKernelGGL(pad_rows<bf16>, dim3(grid_for(nx)), dim3(256), 0, s, (const bf16*)p.x, p.Xp, T, Tp, H * P, nx);
-    hipLaunchKernelGGL(pad_rows<bf16>, dim3(grid_for(nx)), dim3(256), 0, s, (const bf16*)p.dy, p.dYp, T, Tp, H * P, nx);
-    hipLaunchKernelGGL(pad_rows<bf16>, dim3(grid_for(nb)), dim3(256), 0, s, (const bf16*)p.B, p.Bp, T, Tp, G * N, nb);
-    hipLaunchKernelGGL(pad_rows<bf16>, dim3(grid_for(nb)), dim3(256), 0, s, (const bf16*)p.C, p.Cp, T, Tp, G * N, nb);
-  } else {
-    hipLaunchKernelGGL(pad_rows<float>, dim3(grid_for(nx)), dim3(256), 0, s, (const float*)p.x, p.Xp, T, Tp, H * P, nx);
-    hipLaunchKernelGGL(pad_rows<float>, dim3(grid_for(nx)), dim3(256), 0, s, (const float*)p.dy, p.dYp, T, Tp, H * P,
-                       nx);
-    hipLaunchKernelGGL(pad_rows<float>, dim3(grid_for(nb)), dim3(256), 0, s, (const float*)p.B, p.Bp, T, Tp, G * N, nb);
-    hipLaunchKernelGGL(pad_rows<float>, dim3(grid_for(nb)), dim3(256), 0, s, (const float*)p.C, p.Cp, T, Tp, G * N, nb);
-  }
+  // inputs to padded fp32 rows, 8 values per thread where the rows allow
+  auto pad = [&](const void* src, float* dst, int64_t W, int64_t n) {
+    const bool v8 = W % 8 == 0 && (reinterpret_cast<uintptr_t>(src) & 15) == 0 &&
+                    (reinterpret_cast<uintptr_t>(dst) & 15) == 0;
+    if (p.io == 1) {
+      if (v8)
+        hipLaunchKernelGGL(pad_rows8<bf16>, dim3(grid_for(n / 8)), dim3(256), 0, s, (const bf16*)src, dst, T, Tp, W, n / 8);
+      else
+        hipLaunchKernelGGL(pad_rows<bf16>, dim3(grid_for(n)), dim3(256), 0, s, (const bf16*)src, dst, T, Tp, W, n);
+    } else {
+      if (v8)
+        hipLaunchKernelGGL(pad_rows8<float>, dim3(grid_for(n / 8)), dim3(256), 0, s, (const float*)src, dst, T, Tp, W,
+                           n / 8);
+      else
+        hipLaunchKernelGGL(pad_rows<float>, dim3(grid_for(n)), dim3(256), 0, s, (const float*)src, dst, T, Tp, W, n);
+    }
+  };
+  pad(p.x, p.Xp, H * P, nx);
+  pad(p.dy, p.dYp, H * P, nx);
+  pad(p.B, p.Bp, G * N, nb);
+  pad(p.C, p.Cp, G * N, nb);
   const int64_t ng = bt * H * Tp;
   hipLaunchKernelGGL(exp2_all, dim3(grid_for(ng)), dim3(256), 0, s, p.gcum, p.E, ng);
   if (!ok(hipGetLastError())) return e;
