@@ -415,14 +415,29 @@ __global__ void exp2_all(const float* __restrict__ g, float* __restrict__ e, int
 __global__ void chunk_recursion(const float* __restrict__ S, const float* __restrict__ gcum,
                                 const float* __restrict__ h0, float* __restrict__ out, float* __restrict__ last,
                                 int64_t nc, int64_t Tp, int64_t Q, int64_t PN, int64_t total, int rev) {
+  // chunks are taken CR at a time with their loads issued first: a load
+  // issued after the previous chunk's store would wait for it
+  constexpr int CR = 16;
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t bh = i / PN, e = i % PN;
     float h = h0 ? h0[i] : 0.f;
-    for (int64_t s = 0; s < nc; ++s) {
-      const int64_t k = rev ? nc - 1 - s : s;
-      const int64_t o = (bh * nc + k) * PN + e;
-      out[o] = h;
-      h = fmaf(exp2_hw(gcum[bh * Tp + k * Q + Q - 1]), h, S[o]);
+    for (int64_t s0 = 0; s0 < nc; s0 += CR) {
+      float sv[CR], gv[CR];
+#pragma unroll
+      for (int c = 0; c < CR; ++c) {
+        const int64_t s = s0 + c;
+        const int64_t k = rev ? nc - 1 - s : s;
+        sv[c] = s < nc ? S[(bh * nc + k) * PN + e] : 0.f;
+        gv[c] = s < nc ? gcum[bh * Tp + k * Q + Q - 1] : 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < CR; ++c) {
+        const int64_t s = s0 + c;
+        if (s >= nc) break;
+        const int64_t k = rev ? nc - 1 - s : s;
+        out[(bh * nc + k) * PN + e] = h;
+        h = fmaf(exp2_hw(gv[c]), h, sv[c]);
+      }
     }
     if (last) last[i] = h;
   }
