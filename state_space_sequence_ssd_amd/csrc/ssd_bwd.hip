@@ -647,14 +647,24 @@ __global__ __launch_bounds__(256) void finish_chunk(const BwdProblem p) {
 // sum over the heads of each group of the Q x Q blocks [bt][nc][H][Q][Q]
 // -> [bt][nc][G][Q][Q]
 __global__ void sum_heads(const float* __restrict__ in, float* __restrict__ out, int hpg, int Q, int64_t QQ,
-                          int64_t total) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+                          int64_t total4) {
+  // four adjacent values of a row per thread (Q a multiple of 4): 16-byte
+  // loads, one per head, and one 16-byte store
+  for (int64_t i4 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i4 < total4;
+       i4 += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = 4 * i4;
     const int64_t o = i % QQ, bkg = i / QQ;   // (b * nc + k) * G + g
     if ((o % Q) / GT > (o / Q) / GT) continue;   // a GT x GT block above the diagonal: never read
     const float* src = in + bkg * hpg * QQ + o;
-    float acc = 0.f;
-    for (int j = 0; j < hpg; ++j) acc += src[j * QQ];
-    out[i] = acc;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < hpg; ++j) {
+      const float4 v = *reinterpret_cast<const float4*>(src + j * QQ);
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    *reinterpret_cast<float4*>(out + i) = acc;
   }
 }
 
@@ -823,7 +833,7 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
   // needed), and the state products sum the heads' parts inside the kernel
   const int64_t nsum = bt * nc * G * QQ;
   if (e == hipSuccess && nsum > 0) {
-    hipLaunchKernelGGL(sum_heads, dim3(grid_for(nsum)), dim3(256), 0, s, p.DX, p.CB, hpg, Qi, QQ, nsum);
+    hipLaunchKernelGGL(sum_heads, dim3(grid_for(nsum / 4)), dim3(256), 0, s, p.DX, p.CB, hpg, Qi, QQ, nsum / 4);
     ok(hipGetLastError());
   }
   {
