@@ -298,7 +298,8 @@ int mamba2_ssd_step(const mamba2_ssd_step_dims* dims, int io_dtype,
  * Errors: as mamba2_ssd_check_args (NULL_POINTER for a missing required
  * pointer: A, D, dA, dD always; x, dt, B, C, dy, dx, ddt, dB, dC when
  * batch * seqlen > 0), ALIAS when an output overlaps an input, another
- * output or the workspace, UNSUPPORTED for flag bits in io. Validation runs
+ * output or the workspace, ALIGN for a workspace that is not 256-byte
+ * aligned, UNSUPPORTED for flag bits in io. Validation runs
  * on the host before any launch; the call is asynchronous on `stream`. */
 size_t mamba2_ssd_bwd_workspace_bytes(const mamba2_ssd_dims* dims, int io_dtype);
 

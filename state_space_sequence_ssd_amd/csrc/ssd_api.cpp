@@ -371,6 +371,8 @@ int mamba2_ssd_bwd_check_args(const mamba2_ssd_dims* d, int io, const void* x, c
   if (!A || !D || !dA || !dD) return MAMBA2_SSD_ERR_NULL_POINTER;
   if (tokens && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC)) return MAMBA2_SSD_ERR_NULL_POINTER;
   if (d->batch > 0 && (!workspace || workspace_bytes < L.total)) return MAMBA2_SSD_ERR_WORKSPACE;
+  // its regions start at 256-byte offsets and are read in 16-byte pieces
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return MAMBA2_SSD_ERR_ALIGN;
   const size_t e = io_size(io);
   const Range ins[] = {range_of(x, (size_t)s.n_x * e), range_of(dt, (size_t)s.n_dt * 4),
                        range_of(A, (size_t)d->nheads * 4), range_of(B, (size_t)s.n_bc * e),

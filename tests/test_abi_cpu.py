@@ -367,6 +367,8 @@ def test_bwd_rejects_bad_calls():
     for name in ("x", "dt", "A", "B", "C", "D", "dy", "dx", "ddt", "dA", "dB", "dC", "dD"):
         assert _bwd_check(BWD_SMALL, BF16, **{name: 0}) == NULLP, name
     assert _bwd_check(BWD_SMALL, BF16, ws=0) == WS
+    # the workspace's regions are read in 16-byte pieces from 256-byte offsets
+    assert _bwd_check(BWD_SMALL, BF16, ws=_bwd_ptrs(BWD_SMALL, BF16)["ws"] + 16) == ALIGN
     assert _bwd_check(BWD_SMALL, BF16, ws_bytes=ssd.bwd_workspace_bytes(BWD_SMALL, BF16) - 1) == WS
     p = _bwd_ptrs(BWD_SMALL, BF16)
     # an output on an input, on another output, or on the workspace
