@@ -203,7 +203,10 @@ __device__ __forceinline__ void kstore(float (*sa)[GT + 4], float (*sb)[GT + 4],
   }
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void bwd_gemm(GemmArgs g) {
+// HAS2: the optional second product (only the dB and dC products have it);
+// without it the kernel needs fewer registers
+template <bool HAS2>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HAS2 ? 3 : 4))) void bwd_gemm(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) float sa[GK][GT + 4];
   __shared__ __attribute__((aligned(16))) float sb[GK][GT + 4];
   const int tiles_n = (g.N + GT - 1) / GT;
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
       }
     }
   }
-  if (g.a2.p) {
+  if (HAS2 && g.a2.p) {
     // the second product, summed over hsum consecutive heads of the batch
     // index (head z2 * hsum + hl), each A2 row scaled by its head's rsc2 row
     // before the sum; with hsum = 0 it is the batch's own product and rsc2
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     for (int r = 0; r < 16; ++r) {
       const int mr = drow(r, lg);
       float v = (rs ? rs[m0 + wm + mr] : 1.f) * acc[r];
-      if (g.a2.p) v = fmaf(rs2 ? rs2[m0 + wm + mr] : 1.f, acc2[r], v);
+      if (HAS2 && g.a2.p) v = fmaf(rs2 ? rs2[m0 + wm + mr] : 1.f, acc2[r], v);
       q[mr][lm] = v;
     }
     // a wave's own LDS operations complete in order: no barrier
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void b
     if (m >= g.M) continue;
     float* cp = Cp + m * g.c.rs + n * g.c.cs;
     float v = (rs ? rs[m] : 1.f) * acc[r];
-    if (g.a2.p) v = fmaf(rs2 ? rs2[m] : 1.f, acc2[r], v);
+    if (HAS2 && g.a2.p) v = fmaf(rs2 ? rs2[m] : 1.f, acc2[r], v);
     *cp = g.beta == 0.f ? v : fmaf(g.beta, *cp, v);
   }
 }
@@ -351,7 +354,10 @@ hipError_t gemm(const Operand& a, const Operand& b, const Operand& c, const Oper
   const int64_t Z = (int64_t)Z0 * Z1 * Z2;
   if (Z == 0 || tiles == 0) return hipSuccess;
   if (Z > kMaxGridYZ) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_gemm, dim3((unsigned)tiles, (unsigned)Z), dim3(256), 0, s, g);
+  if (a2)
+    hipLaunchKernelGGL(bwd_gemm<true>, dim3((unsigned)tiles, (unsigned)Z), dim3(256), 0, s, g);
+  else
+    hipLaunchKernelGGL(bwd_gemm<false>, dim3((unsigned)tiles, (unsigned)Z), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
