@@ -207,8 +207,12 @@ __device__ __forceinline__ void kstore(float (*sa)[GT + 4], float (*sb)[GT + 4],
 // without it the kernel needs fewer registers
 template <bool HAS2>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HAS2 ? 3 : 4))) void bwd_gemm(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) float sa[GK][GT + 4];
-  __shared__ __attribute__((aligned(16))) float sb[GK][GT + 4];
+  // one LDS block: the A and B slices while the products run, then the
+  // output staging (every wave has passed the last slice's barrier by then)
+  constexpr int kSlice = GK * (GT + 4), kStage = 4 * 32 * 40;
+  __shared__ __attribute__((aligned(16))) float lds[2 * kSlice > kStage ? 2 * kSlice : kStage];
+  float (*sa)[GT + 4] = reinterpret_cast<float (*)[GT + 4]>(lds);
+  float (*sb)[GT + 4] = reinterpret_cast<float (*)[GT + 4]>(lds + kSlice);
   const int tiles_n = (g.N + GT - 1) / GT;
   const int tm = blockIdx.x / tiles_n, tn = blockIdx.x % tiles_n;
   const int z = blockIdx.y;
@@ -294,8 +298,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HAS2 ? 3 : 
     // through LDS as 16-byte row pieces, 4 stores per lane instead of 16
     // (rows of 32 values plus 8 of padding: the two half-waves write rows 4
     // apart, 32 banks apart)
-    __shared__ __attribute__((aligned(16))) float so[4][32][40];
-    float (*q)[40] = so[wave];
+    float (*q)[40] = reinterpret_cast<float (*)[40]>(lds + wave * 32 * 40);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int mr = drow(r, lg);
