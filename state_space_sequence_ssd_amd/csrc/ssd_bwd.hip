@@ -60,11 +60,12 @@ struct GemmArgs {
   float beta;
   int shape;
   int vec;                     // operands staged as 16-byte pieces (see gemm())
-  // optional second product added to the first: + diag(rs2) (A2 B2), with
-  // contraction length K2 over the full range (no causal shape)
+  // optional second product added to the first: the sum over hsum heads of
+  // (diag(rsc2_head) A2_head) B2_head, contraction length K2 over the full
+  // range (no causal shape); only without an output row scale
   Operand a2, b2, rsc2;
   int K2;
-  int hsum;                    // > 0: the second product sums this many heads (see bwd_gemm)
+  int hsum;                    // heads the second product sums (>= 1 when a2 is set)
   int cvec;                    // output rows contiguous and 16-byte aligned (see gemm())
 };
 
@@ -226,7 +227,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HAS2 ? 3 : 
   // (32x32x2): lane l supplies A[row l%32][k l/32] and B[k l/32][col l%32]
   const int wave = tid / 64, lane = tid % 64, lm = lane % 32, lg = lane / 32;
   const int wm = 32 * (wave / 2), wn = 32 * (wave % 2);
-  f32x16 acc = f32x16{}, acc2 = f32x16{};
+  f32x16 acc = f32x16{};
   {
     const float* A = g.a.p + g.a.base(z0, z1, z2);
     const float* B = g.b.p + g.b.base(z0, z1, z2);
@@ -258,14 +259,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HAS2 ? 3 : 
   if (HAS2 && g.a2.p) {
     // the second product, summed over hsum consecutive heads of the batch
     // index (head z2 * hsum + hl), each A2 row scaled by its head's rsc2 row
-    // before the sum; with hsum = 0 it is the batch's own product and rsc2
-    // scales its output rows
-    const int nh = g.hsum > 0 ? g.hsum : 1;
-    for (int hl = 0; hl < nh; ++hl) {
-      const int zh = g.hsum > 0 ? z2 * g.hsum + hl : z2;
+    // before the sum, into the same accumulators (the host allows a second
+    // product only with hsum > 0 and no output row scale)
+    for (int hl = 0; hl < g.hsum; ++hl) {
+      const int zh = z2 * g.hsum + hl;
       const float* A = g.a2.p + g.a2.base(z0, z1, zh);
       const float* B = g.b2.p + g.b2.base(z0, z1, zh);
-      const float* ra = (g.hsum > 0 && g.rsc2.p) ? g.rsc2.p + g.rsc2.base(z0, z1, zh) : nullptr;
+      const float* ra = g.rsc2.p ? g.rsc2.p + g.rsc2.base(z0, z1, zh) : nullptr;
       if (g.vec) {
         KSlice v;
         if (g.K2 > 0) kload(v, g.a2, g.b2, A, B, nullptr, ra, m0, n0, 0, g.M, g.N, tid);
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HAS2 ? 3 : 
           if (k0 + GK < g.K2) kload(v, g.a2, g.b2, A, B, nullptr, ra, m0, n0, k0 + GK, g.M, g.N, tid);
 #pragma unroll
           for (int kk = 0; kk < GK; kk += 2)
-            acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[kk + lg][wm + lm], sb[kk + lg][wn + lm], acc2, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[kk + lg][wm + lm], sb[kk + lg][wn + lm], acc, 0, 0, 0);
           __syncthreads();
         }
       } else {
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HAS2 ? 3 : 
           __syncthreads();
 #pragma unroll
           for (int kk = 0; kk < GK; kk += 2)
-            acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[kk + lg][wm + lm], sb[kk + lg][wn + lm], acc2, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[kk + lg][wm + lm], sb[kk + lg][wn + lm], acc, 0, 0, 0);
           __syncthreads();
         }
       }
@@ -292,7 +292,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HAS2 ? 3 : 
   }
   float* Cp = const_cast<float*>(g.c.p) + g.c.base(z0, z1, z2);
   const float* rs = g.rsc.p ? g.rsc.p + g.rsc.base(z0, z1, z2) : nullptr;
-  const float* rs2 = (g.hsum == 0 && g.rsc2.p) ? g.rsc2.p + g.rsc2.base(z0, z1, z2) : nullptr;
   if (g.cvec && g.beta == 0.f && m0 + GT <= g.M && n0 + GT <= g.N) {
     // whole tile, row-major output: each wave's 32 x 32 quarter goes out
     // through LDS as 16-byte row pieces, 4 stores per lane instead of 16
@@ -303,7 +302,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HAS2 ? 3 : 
     for (int r = 0; r < 16; ++r) {
       const int mr = drow(r, lg);
       float v = (rs ? rs[m0 + wm + mr] : 1.f) * acc[r];
-      if (HAS2 && g.a2.p) v = fmaf(rs2 ? rs2[m0 + wm + mr] : 1.f, acc2[r], v);
       q[mr][lm] = v;
     }
     // a wave's own LDS operations complete in order: no barrier
@@ -323,7 +321,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HAS2 ? 3 : 
     if (m >= g.M) continue;
     float* cp = Cp + m * g.c.rs + n * g.c.cs;
     float v = (rs ? rs[m] : 1.f) * acc[r];
-    if (HAS2 && g.a2.p) v = fmaf(rs2 ? rs2[m] : 1.f, acc2[r], v);
     *cp = g.beta == 0.f ? v : fmaf(g.beta, *cp, v);
   }
 }
@@ -357,6 +354,7 @@ hipError_t gemm(const Operand& a, const Operand& b, const Operand& c, const Oper
   const int64_t Z = (int64_t)Z0 * Z1 * Z2;
   if (Z == 0 || tiles == 0) return hipSuccess;
   if (Z > kMaxGridYZ) return hipErrorInvalidValue;
+  if (a2 && (hsum <= 0 || rsc.p)) return hipErrorInvalidValue;   // see bwd_gemm
   if (a2)
     hipLaunchKernelGGL(bwd_gemm<true>, dim3((unsigned)tiles, (unsigned)Z), dim3(256), 0, s, g);
   else
