@@ -45,7 +45,10 @@ KERNEL_SOURCES = {"ssd_chunk_cumsum": ["chunk_cumsum.hip"], "ssd_chunk_state": [
                   "ssd_state_pass": ["state_pass.hip"],
                   "ssd_chunk_scan": ["chunk_scan.hip", "chunk_scan_resident.hip"],
                   "ssd_chunk_state_pass": ["chunk_state.hip"],
+                  "ssd_chunk_chained": ["chunk_chained.hip"],
                   "ssd_step": ["ssd_step.hip"]}
+PATHS = {"auto": 0x0000, "four": 0x1000, "three": 0x2000, "chained": 0x3000}   # MAMBA2_SSD_PATH_*
+FLUSH_BYTES = 1 << 30          # scratch written before each cold step (> the 256 MB last-level cache)
 TRAFFIC_SUMMARY = {"mamba2-2.7b": "hbm_traffic_mamba2-2.7b.md",
                    "mamba2-2.7b-decode": "hbm_traffic_mamba2-2.7b-decode.md"}
 
@@ -97,6 +100,11 @@ def algorithmic_cost(cfg):
     st = Bt * H * nc * P * N * 4      # all chunk states (fp32)
     fin = Bt * H * P * N * 4
     init = fin if cfg.init_sigma is not None else 0
+    scan_flops = (2.0 * Bt * H * Tp * P * N                       # C . Hprev^T
+                  + Bt * H * nc * Q * (Q + 1) * P                 # causal (CB) . X
+                  + Bt * G * nc * Q * (Q + 1) * N)                # causal C . B^T once per group
+    state_flops = 2.0 * Bt * H * Tp * P * N
+    pass_flops = 2.0 * Bt * H * nc * P * N
     cost = {
         "ssd_chunk_cumsum": (dt + 2 * gq, 0.0),
         "ssd_chunk_state": (x + bc + 2 * gq + st, 2.0 * Bt * H * Tp * P * N),
@@ -105,12 +113,25 @@ def algorithmic_cost(cfg):
         # cumsums in, Hprev (and final, init) out; no per-chunk states
         "ssd_chunk_state_pass": (x + bc + gq + Bt * H * nc * 4 + st + fin + init,
                                  2.0 * Bt * H * Tp * P * N + 2.0 * Bt * H * nc * P * N),
-        "ssd_chunk_scan": (2 * x + 2 * bc + 2 * gq + st + H * 4,
-                           2.0 * Bt * H * Tp * P * N                       # C . Hprev^T
-                           + Bt * H * nc * Q * (Q + 1) * P                 # causal (CB) . X
-                           + Bt * G * nc * Q * (Q + 1) * N),               # causal C . B^T once per group
+        # Hprev counted at 4 bytes per element (fp32, or the bf16 (hi, lo) pair)
+        "ssd_chunk_scan": (2 * x + 2 * bc + 2 * gq + st + H * 4, scan_flops),
+        # the three in one: x, B, C, G', dt in, y and final out; the carried
+        # state handed between chunks is not an input or an output
+        "ssd_chunk_chained": (2 * x + 2 * bc + 2 * gq + fin + init + 2 * H * 4,
+                              state_flops + pass_flops + scan_flops),
     }
     return cost
+
+
+def path_spans(path):
+    """(kernel, first event, last event) of each kernel a forward call runs on
+    the given sequence (events as mamba2_ssd_fwd_timed records them)."""
+    import state_space_sequence_ssd_amd as ssd
+    if path == ssd.PATH_CHAINED:
+        return [("ssd_chunk_cumsum", 0, 1), ("ssd_chunk_chained", 1, 4)]
+    if path == ssd.PATH_THREE:
+        return [("ssd_chunk_cumsum", 0, 1), ("ssd_chunk_state_pass", 1, 3), ("ssd_chunk_scan", 3, 4)]
+    return [(k, i, i + 1) for i, k in enumerate(KERNELS)]
 
 
 def copy_calibration(dev):
@@ -450,7 +471,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="mamba2-2.7b")
+    ap.add_argument("--config", default="mamba2-2.7b",
+                    help="workload name, or 'all' for every forward configuration plus the held-out shape "
+                         "(one JSON line each)")
+    ap.add_argument("--path", default="auto", choices=sorted(PATHS),
+                    help="force a kernel sequence of the forward call (default: the library's choice)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of CPU oracle work for the cpu_baseline sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--bwd", action="store_true",
                     help="time the backward pass (mamba2_ssd_bwd) on the layer instead, one JSON line of its own")
@@ -471,17 +498,44 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    if args.config.startswith("s6-"):
+    if args.config == "all":
+        cfg = None
+    elif args.config.startswith("s6-"):
         from workloads import s6_config_by_name
         return run_s6(args, s6_config_by_name(args.config))
-    cfg = config_by_name(args.config)
-    if cfg.seqlen == 1 and cfg.name.endswith("-decode"):
+    else:
+        cfg = config_by_name(args.config)
+    if cfg is not None and cfg.seqlen == 1 and cfg.name.endswith("-decode"):
         return run_decode(args, cfg)
     if args.bwd:
         return run_bwd(args, cfg)
+    if args.config == "all":
+        for c in ALL_CONFIGS():
+            print(json.dumps(run_forward(args, c)), flush=True)
+        return
+    print(json.dumps(run_forward(args, cfg)), flush=True)
+
+
+def ALL_CONFIGS():
+    from workloads import CONFIGS, HELD_OUT
+    return list(CONFIGS) + [HELD_OUT]
+
+
+def run_forward(args, cfg):
+    """Times mamba2_ssd_fwd on one layer: K steps back to back (warm), then K
+    steps each preceded by a write of FLUSH_BYTES of scratch outside the timed
+    events (cold: the inputs come from HBM, not the last-level cache). The
+    cold figures are the primary ones. Returns the JSON record."""
+    import torch
+
+    import state_space_sequence_ssd_amd as ssd
+    from workloads import generate
+
+    # small layers (tiny, 130M-like) take at least 200 timed calls in the all-configs sweep
+    steps = args.steps if (args.config != "all" or cfg.tokens > 16384) else max(args.steps, 200)
     dev = torch.device("cuda:0")
     inp = generate(cfg)
-    io = ssd.BF16 if cfg.io == "bf16" else ssd.F32
+    io = (ssd.BF16 if cfg.io == "bf16" else ssd.F32) | PATHS[args.path]
 
     def to_dev(k):
         if cfg.io == "bf16" and k in ("x", "B", "C"):
@@ -492,9 +546,10 @@ def main():
     init = None if inp["init_state"] is None else to_dev("init_state")
     dims = ssd.Dims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk)
     L = ssd.workspace_layout(dims, io)
-    ws = torch.empty(L.total_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(L.total_bytes, 1), dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
     fin = torch.empty((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate), dtype=torch.float32, device=dev)
+    scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     ptrs = (x.data_ptr(), dt.data_ptr(), A.data_ptr(), B.data_ptr(), C.data_ptr(), D.data_ptr(),
             0 if init is None else init.data_ptr(), y.data_ptr(), fin.data_ptr(), ws.data_ptr(), ws.numel())
@@ -514,44 +569,57 @@ def main():
     warm = new_events()
     for _ in range(args.warmup):
         step(warm)
-    events = [new_events() for _ in range(args.steps)]
+    # warm: K steps back to back
+    events_w = [new_events() for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    for i in range(steps):
+        step(events_w[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_w = time.perf_counter() - t0
+    # cold: K steps, each after a scratch write that evicts the inputs from the caches
+    events_c = [new_events() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        scratch.fill_(float(i))
+        step(events_c[i])
+    torch.cuda.synchronize()
+    wall_c = time.perf_counter() - t0
 
-    # the kernels this call ran, and the events around each
-    if ssd.fused_state_pass(dims, io):
-        spans = [("ssd_chunk_cumsum", 0, 1), ("ssd_chunk_state_pass", 1, 3), ("ssd_chunk_scan", 3, 4)]
-    else:
-        spans = [(k, i, i + 1) for i, k in enumerate(KERNELS)]
+    spans = path_spans(L.path)
     ran = [k for k, _, _ in spans]
-    per_kernel_ms = {k: float(np.mean([ev[a].elapsed_time(ev[b]) for ev in events])) for k, a, b in spans}
-    gpu_ms = float(np.mean([ev[0].elapsed_time(ev[4]) for ev in events]))
     tokens = cfg.batch * cfg.seqlen
     cost = algorithmic_cost(cfg)
-    kern = {}
-    for k in ran:
-        nbytes, flops = cost[k]
-        sec = per_kernel_ms[k] * 1e-3
-        peak_tf = BF16_PEAK_TFLOPS if cfg.io == "bf16" else F32_PEAK_TFLOPS
-        kern[k] = {"us": round(per_kernel_ms[k] * 1e3, 2), "alg_bytes": int(nbytes),
-                   "GB/s": round(nbytes / sec / 1e9, 1), "frac_hbm": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
-                   "alg_TFLOP/s": round(flops / sec / 1e12, 2), "frac_mfma": round(flops / sec / 1e12 / peak_tf, 4)}
-    dom = max(ran, key=lambda k: per_kernel_ms[k])
-    achieved = kern[dom]["GB/s"]
+    peak_tf = BF16_PEAK_TFLOPS if cfg.io == "bf16" else F32_PEAK_TFLOPS
+
+    def figures(events):
+        per_ms = {k: float(np.mean([ev[a].elapsed_time(ev[b]) for ev in events])) for k, a, b in spans}
+        kern = {}
+        for k in ran:
+            nbytes, flops = cost[k]
+            sec = per_ms[k] * 1e-3
+            kern[k] = {"us": round(per_ms[k] * 1e3, 2), "alg_bytes": int(nbytes),
+                       "GB/s": round(nbytes / sec / 1e9, 1), "frac_hbm": round(nbytes / sec / 1e9 / HBM_PEAK_GBS, 4),
+                       "alg_TFLOP/s": round(flops / sec / 1e12, 2),
+                       "frac_mfma": round(flops / sec / 1e12 / peak_tf, 4)}
+        step_ms = float(np.mean([ev[0].elapsed_time(ev[4]) for ev in events]))
+        return per_ms, kern, step_ms
+
+    per_c, kern_c, step_c = figures(events_c)
+    per_w, kern_w, step_w = figures(events_w)
+    dom = max(ran, key=lambda k: per_c[k])
+    achieved = kern_c[dom]["GB/s"]
     traffic = measured_traffic(cfg.name, dom)
 
     out = {
         "metric": "SSD fwd tokens/sec at 2.7B-layer shape (1 GPU); % MFMA peak / % HBM BW",
-        "value": round(tokens * args.steps / wall, 1),
+        "value": round(tokens / (step_c * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_step": round(step_c, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -563,18 +631,27 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "traffic_unit": "bytes/launch",
-                     "traffic_GB/s": None if traffic is None else round(traffic / (per_kernel_ms[dom] * 1e6), 1)},
-        "gpu_event_ms_per_step": round(gpu_ms, 4),
-        "kernels": kern,
+                     "traffic_GB/s": None if traffic is None else round(traffic / (per_c[dom] * 1e6), 1),
+                     "cache": "cold"},
+        "timing": ("value and ms_per_step: mean HIP-event time of one forward call over the K cold steps "
+                   f"(each after a {FLUSH_BYTES >> 20} MiB scratch write outside the events); "
+                   "warm: the same K calls back to back"),
+        "path": ssd.PATH_NAMES[L.path],
+        "kernels": kern_c,
+        "warm": {"value": round(tokens * steps / wall_w, 1), "ms_per_step_wall": round(wall_w / steps * 1e3, 4),
+                 "ms_per_step_events": round(step_w, 4), "kernels": kern_w},
+        "cold_wall_s_incl_flush": round(wall_c, 4),
         "path_bytes_per_step": int(sum(cost[k][0] for k in ran)),
     }
+    if dom == "ssd_chunk_scan":
+        out["roofline"]["hprev_bytes_per_element"] = 4
     if not args.no_cpu:
-        base, parity = cpu_baseline(cfg, inp, y.float().cpu().numpy())
+        base, parity = cpu_baseline(cfg, inp, y.float().cpu().numpy(), budget_s=args.cpu_budget)
         out["cpu_baseline"] = base
         out["parity_vs_oracle"] = parity
     else:
         out["cpu_baseline"] = None
-    print(json.dumps(out), flush=True)
+    return out
 
 
 if __name__ == "__main__":

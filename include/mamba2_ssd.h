@@ -26,8 +26,8 @@
  *   (for bf16 io, headdim 64, chunk 256 and many (batch, head) pairs the
  *   chunk states are computed inside the state pass instead: one kernel,
  *   ssd_chunk_state_pass, with the structure of the blog's "Kernel 2", the
- *   per-chunk states never reaching memory; mamba2_ssd_fused_state_pass
- *   tells which path a call takes)
+ *   per-chunk states never reaching memory; mamba2_ssd_fwd_path tells which
+ *   kernel sequence a call takes, and a field of io_dtype can force one)
  *   ssd_chunk_scan    the per-chunk outputs: decayed carried-state term,
  *                     masked decayed C.B^T product with dt*x, and D*x
  *                     (blog section "Kernel 3: compute_out")
@@ -79,7 +79,7 @@ extern "C" {
 
 /* Layout flag, OR-ed into the io_dtype argument of the forward entry points
  * (mamba2_ssd_supported, _workspace_layout_query, _fwd_workspace_bytes,
- * _check_args, _fwd, _fwd_timed, _fused_state_pass): dt is given head-major,
+ * _check_args, _fwd, _fwd_timed, _fwd_path, _fused_state_pass): dt is given head-major,
  * float [batch][nheads][seqlen], instead of token-major [batch][seqlen][nheads].
  * This is the [batch, head, token] global-memory layout the blog's
  * "Mamba-2 performance optimizations" section recommends for dt and the
@@ -87,6 +87,28 @@ extern "C" {
  * layouts. Any other bit above the low byte gives MAMBA2_SSD_ERR_UNSUPPORTED.
  * The decode step (mamba2_ssd_step) takes no flags: its dt is [batch][nheads]. */
 #define MAMBA2_SSD_DT_HEAD_MAJOR 0x100
+
+/* Kernel sequence, a field OR-ed into the io_dtype argument of the forward
+ * entry points (bits 12-13). Every sequence computes the same function (the
+ * results agree to fp32 rounding); they differ in how the chunk states reach
+ * the outputs. AUTO (0) lets the library choose by shape; the others force
+ * one sequence, and a shape the forced sequence does not support gives
+ * MAMBA2_SSD_ERR_UNSUPPORTED from every forward entry point.
+ *   FOUR     ssd_chunk_cumsum, ssd_chunk_state, ssd_state_pass,
+ *            ssd_chunk_scan (every supported shape)
+ *   THREE    ssd_chunk_cumsum, ssd_chunk_state_pass, ssd_chunk_scan (bf16,
+ *            headdim 64, chunk 256)
+ *   CHAINED  ssd_chunk_cumsum, then one kernel that computes each chunk's
+ *            state contribution, the pass and the outputs, handing the
+ *            carried state from each chunk to the next through the
+ *            workspace (bf16, headdim 64, dstate 64 or 128, chunk 256)
+ * The workspace size depends on the sequence: query it with the same
+ * io_dtype value that is passed to the call. */
+#define MAMBA2_SSD_PATH_AUTO    0x0000
+#define MAMBA2_SSD_PATH_FOUR    0x1000
+#define MAMBA2_SSD_PATH_THREE   0x2000
+#define MAMBA2_SSD_PATH_CHAINED 0x3000
+#define MAMBA2_SSD_PATH_MASK    0x3000
 
 /* Problem sizes. batch and seqlen may be 0 (nothing to compute: with
  * seqlen == 0 final_state receives init_state, or zeros). seqlen need not be
@@ -115,14 +137,20 @@ typedef struct {
  *                                      of token t in its chunk's state
  *   states  float [batch][nheads][nchunks][headdim][dstate]
  *                                      each chunk's own contribution S_k
- *                                      (not written when the states are
- *                                      computed inside the pass, see
- *                                      mamba2_ssd_fused_state_pass)
+ *                                      (FOUR only; no bytes on the other
+ *                                      sequences)
  *   hprev   [batch][nheads][nchunks][headdim][dstate] states h entering
  *           each chunk; io = F32: float; io = BF16: bf16 pairs, 4 bytes per
  *           element: for each row and each aligned group of 8 dstate
  *           columns, the 8 values bf16(h) followed by the 8 values
- *           bf16(h - bf16(h)), so hi + lo carries h to about 16 bits        */
+ *           bf16(h - bf16(h)), so hi + lo carries h to about 16 bits
+ *           (FOUR and THREE; no bytes on CHAINED)
+ *   chain   float [batch][nheads][headdim][dstate] (CHAINED only): the
+ *           carried state handed from each chunk to the next
+ *   sync    int32 (CHAINED only): a work counter and one progress flag per
+ *           (batch, head), cleared by ssd_chunk_cumsum
+ * A region a sequence does not use has no bytes: its offset equals the next
+ * region's. */
 typedef struct {
   size_t total_bytes;
   size_t gcum_offset;
@@ -130,7 +158,10 @@ typedef struct {
   size_t wst_offset;
   size_t states_offset;
   size_t hprev_offset;
+  size_t chain_offset;
+  size_t sync_offset;
   int64_t nchunks;
+  int32_t path;       /* the MAMBA2_SSD_PATH_* sequence the layout is for */
 } mamba2_ssd_workspace_layout;
 
 /* 1 if (headdim, dstate, chunk, io_dtype) has compiled kernels, else 0.
@@ -147,8 +178,13 @@ int mamba2_ssd_workspace_layout_query(const mamba2_ssd_dims* dims, int io_dtype,
 size_t mamba2_ssd_fwd_workspace_bytes(const mamba2_ssd_dims* dims, int io_dtype);
 
 /* Every host-side check of mamba2_ssd_fwd, without touching the GPU: sizes,
- * support, required pointers, workspace size and aliasing. Pointers are only
- * compared, never dereferenced, so any values may be passed.
+ * support, required pointers, alignment, workspace size and aliasing.
+ * Pointers are only compared, never dereferenced, so any values may be
+ * passed.
+ * Alignment (MAMBA2_SSD_ERR_ALIGN): x, B, C, y, init_state and final_state
+ * on 16 bytes, dt, A and D on 4, the workspace on 256 (the kernels move
+ * these arrays in 16-byte pieces; hipMalloc and torch allocations satisfy
+ * this; a view at an odd element offset may not).
  * Aliasing rules: init_state may be the same pointer as final_state (an
  * in-place state update); apart from that, y, final_state and the
  * workspace must not overlap any other array. Inputs may overlap each
@@ -186,23 +222,27 @@ int mamba2_ssd_fwd(const mamba2_ssd_dims* dims, int io_dtype,
                    const float* init_state, void* y, float* final_state,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* The kernel sequence mamba2_ssd_fwd takes for these sizes and io_dtype
+ * (including its path field): MAMBA2_SSD_PATH_FOUR, _THREE or _CHAINED, or a
+ * negative status when the arguments are invalid or the forced sequence
+ * does not support the shape. AUTO chooses CHAINED where it supports the
+ * shape, else THREE when its (batch, head, dstate group) walks alone fill
+ * the GPU, else FOUR. Host only. */
+int mamba2_ssd_fwd_path(const mamba2_ssd_dims* dims, int io_dtype);
+
 /* 1 if mamba2_ssd_fwd with these sizes computes the chunk states inside
- * the state pass (one kernel, ssd_chunk_state_pass; the workspace's states
- * region is then left untouched), 0 if it runs ssd_chunk_state and
- * ssd_state_pass, or if the sizes are invalid. The environment variable
- * MAMBA2_SSD_STATE_PATH (read on every call) overrides the choice: "unfused"
- * forces the two kernels, "fused" the one kernel wherever it supports the
- * shape (bf16, headdim 64, dstate 64/128/256, chunk 256). The paths agree
- * to fp32 rounding (the one kernel sums each chunk's two halves separately).
- * Host only. */
+ * another kernel (sequences THREE and CHAINED: the workspace holds no states
+ * region), 0 if it runs ssd_chunk_state and ssd_state_pass (FOUR), or if
+ * the arguments are invalid. Host only. */
 int mamba2_ssd_fused_state_pass(const mamba2_ssd_dims* dims, int io_dtype);
 
 /* mamba2_ssd_fwd that also records caller-created events on `stream`, so
  * each kernel can be timed where it runs: events[0] before ssd_chunk_cumsum,
  * events[1] before ssd_chunk_state, events[2] before ssd_state_pass,
- * events[3] before ssd_chunk_scan and events[4] after it. On the fused path
+ * events[3] before ssd_chunk_scan and events[4] after it. On THREE,
  * events[1]..events[2] enclose ssd_chunk_state_pass and events[2]..events[3]
- * nothing. `events` points to
+ * nothing; on CHAINED, events[1]..events[2] enclose the chained kernel and
+ * the later spans nothing. `events` points to
  * 5 hipEvent_t handles (passed as void*) owned by the caller; NULL makes the
  * call identical to mamba2_ssd_fwd. The kernels and their order are the
  * same; a failed event record returns MAMBA2_SSD_ERR_HIP. */

@@ -11,8 +11,8 @@ from __future__ import annotations
 import ctypes
 from typing import Optional, Tuple
 
-from ._lib import (BF16, DT_HEAD_MAJOR, F32, STATUS, Dims, S6Dims, SsdError, StepDims, WorkspaceLayout, lib,
-                   status_string)
+from ._lib import (BF16, DT_HEAD_MAJOR, F32, PATH_AUTO, PATH_CHAINED, PATH_FOUR, PATH_NAMES, PATH_THREE, STATUS,
+                   Dims, S6Dims, SsdError, StepDims, WorkspaceLayout, lib, status_string)
 
 __all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_layout", "check_args",
            "Dims", "WorkspaceLayout", "SsdError", "F32", "BF16", "DT_HEAD_MAJOR", "STATUS", "status_string",
@@ -22,7 +22,8 @@ __all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_
            "mamba2_ssd_status_string", "mamba2_ssd_last_hip_error",
            "ssd_step", "ssd_step_ptr", "step_supported", "step_check_args", "StepDims",
            "mamba2_ssd_step", "mamba2_ssd_step_check_args", "mamba2_ssd_step_supported",
-           "mamba2_ssd_fused_state_pass", "fused_state_pass",
+           "mamba2_ssd_fused_state_pass", "fused_state_pass", "mamba2_ssd_fwd_path", "fwd_path",
+           "PATH_AUTO", "PATH_FOUR", "PATH_THREE", "PATH_CHAINED", "PATH_NAMES",
            "ssd_bwd", "ssd_bwd_ptr", "bwd_workspace_bytes", "bwd_check_args",
            "mamba2_ssd_bwd", "mamba2_ssd_bwd_check_args", "mamba2_ssd_bwd_workspace_bytes",
            "S6Dims", "s6_fwd", "s6_fwd_ptr", "s6_supported", "s6_workspace_bytes", "s6_check_args",
@@ -38,6 +39,7 @@ mamba2_ssd_workspace_layout_query = lib.mamba2_ssd_workspace_layout_query
 mamba2_ssd_status_string = lib.mamba2_ssd_status_string
 mamba2_ssd_last_hip_error = lib.mamba2_ssd_last_hip_error
 mamba2_ssd_fused_state_pass = lib.mamba2_ssd_fused_state_pass
+mamba2_ssd_fwd_path = lib.mamba2_ssd_fwd_path
 mamba2_ssd_step = lib.mamba2_ssd_step
 mamba2_ssd_step_check_args = lib.mamba2_ssd_step_check_args
 mamba2_ssd_step_supported = lib.mamba2_ssd_step_supported
@@ -76,6 +78,17 @@ def fused_state_pass(dims, io: int) -> bool:
     return bool(lib.mamba2_ssd_fused_state_pass(ctypes.byref(_dims(dims)), io))
 
 
+def fwd_path(dims, io: int) -> int:
+    """The kernel sequence (PATH_FOUR, PATH_THREE or PATH_CHAINED) a forward
+    call with these sizes and io value (including its path field) takes;
+    raises SsdError when the arguments are invalid or the forced sequence does
+    not support the shape."""
+    st = int(lib.mamba2_ssd_fwd_path(ctypes.byref(_dims(dims)), io))
+    if st < 0:
+        raise SsdError(st)
+    return st
+
+
 def workspace_bytes(dims, io: int) -> int:
     return int(lib.mamba2_ssd_fwd_workspace_bytes(ctypes.byref(_dims(dims)), io))
 
@@ -107,7 +120,7 @@ def ssd_fwd_timed_ptr(dims, io, x, dt, A, B, C, D, init_state, y, final_state, w
 
 def ssd_fwd(x, dt, A, B, C, D, chunk: int, init_state=None, *, return_final_state: bool = True,
             y=None, final_state=None, workspace=None,
-            dt_head_major: bool = False) -> Tuple[object, Optional[object]]:
+            dt_head_major: bool = False, path: int = PATH_AUTO) -> Tuple[object, Optional[object]]:
     """Forward pass on torch CUDA tensors (all contiguous, same device).
 
     x [batch, seqlen, nheads, headdim] and B, C [batch, seqlen, ngroups,
@@ -117,7 +130,9 @@ def ssd_fwd(x, dt, A, B, C, D, chunk: int, init_state=None, *, return_final_stat
     headdim, dstate] are float32. Returns ``(y, final_state)``; final_state is
     None when ``return_final_state`` is False. ``y``, ``final_state`` and
     ``workspace`` (a uint8 tensor) may be passed to reuse memory; otherwise
-    they are allocated with torch. Runs on torch's current stream.
+    they are allocated with torch. ``path`` forces a kernel sequence
+    (PATH_FOUR, PATH_THREE, PATH_CHAINED; PATH_AUTO lets the library choose).
+    Runs on torch's current stream.
     """
     import torch
 
@@ -150,6 +165,7 @@ def ssd_fwd(x, dt, A, B, C, D, chunk: int, init_state=None, *, return_final_stat
     dims = Dims(bt, T, H, P, N, G, chunk)
     if dt_head_major:
         io |= DT_HEAD_MAJOR
+    io |= path
     if y is None:
         y = torch.empty_like(x)
     if return_final_state and final_state is None:

@@ -9,6 +9,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmamba2_s
 F32 = 0
 BF16 = 1
 DT_HEAD_MAJOR = 0x100   # OR-ed into io: dt given as [batch, nheads, seqlen]
+# kernel sequence, a field OR-ed into io (see include/mamba2_ssd.h)
+PATH_AUTO, PATH_FOUR, PATH_THREE, PATH_CHAINED = 0x0000, 0x1000, 0x2000, 0x3000
+PATH_NAMES = {PATH_FOUR: "four", PATH_THREE: "three", PATH_CHAINED: "chained"}
 
 STATUS = {
     0: "OK",
@@ -44,8 +47,9 @@ class WorkspaceLayout(ctypes.Structure):
     """mamba2_ssd_workspace_layout"""
     _fields_ = [("total_bytes", ctypes.c_size_t), ("gcum_offset", ctypes.c_size_t),
                 ("dtt_offset", ctypes.c_size_t), ("wst_offset", ctypes.c_size_t),
-                ("states_offset", ctypes.c_size_t),
-                ("hprev_offset", ctypes.c_size_t), ("nchunks", ctypes.c_int64)]
+                ("states_offset", ctypes.c_size_t), ("hprev_offset", ctypes.c_size_t),
+                ("chain_offset", ctypes.c_size_t), ("sync_offset", ctypes.c_size_t),
+                ("nchunks", ctypes.c_int64), ("path", ctypes.c_int32)]
 
 
 def _hip_runtimes_mapped():
@@ -89,6 +93,8 @@ def _load():
     L.mamba2_ssd_fwd_timed.argtypes = [dims_p, ctypes.c_int, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, sz, vp,
                                        ctypes.POINTER(ctypes.c_void_p)]
     L.mamba2_ssd_fwd_timed.restype = ctypes.c_int
+    L.mamba2_ssd_fwd_path.argtypes = [dims_p, ctypes.c_int]
+    L.mamba2_ssd_fwd_path.restype = ctypes.c_int
     L.mamba2_ssd_fused_state_pass.argtypes = [dims_p, ctypes.c_int]
     L.mamba2_ssd_fused_state_pass.restype = ctypes.c_int
     L.mamba2_ssd_bwd_workspace_bytes.argtypes = [dims_p, ctypes.c_int]

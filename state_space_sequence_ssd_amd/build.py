@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["ssd_api.cpp", "chunk_cumsum.hip", "chunk_state.hip", "state_pass.hip", "chunk_scan.hip",
-           "chunk_scan_resident.hip", "ssd_step.hip", "ssd_bwd.hip", "s6_scan.hip",
+           "chunk_scan_resident.hip", "chunk_chained.hip", "ssd_step.hip", "ssd_bwd.hip", "s6_scan.hip",
            "s6_api.cpp"]
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 are generated.
@@ -64,7 +64,8 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(lambda s: _compile(s, hipcc, verbose), SOURCES))
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    # -z defs: a symbol no source defines fails the link instead of the load
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,-z,defs", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"linking {LIB_NAME} failed:\n{' '.join(cmd)}\n{r.stderr}")

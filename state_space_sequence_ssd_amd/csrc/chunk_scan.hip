@@ -579,7 +579,7 @@ void ssd_chunk_scan_persistent(const T* __restrict__ x, const T* __restrict__ Bm
   using Frag = typename I::Frag;
   using Cfg = ScanCfg<T, P, N, Q>;
   constexpr int E = I::E, KPL = I::KPL, CG = Cfg::CG, NTB = Cfg::NTB, TBW = Cfg::TBW;
-  constexpr int PGW = Cfg::PGW, NPS = Cfg::NPS, WAVES = Cfg::WAVES;
+  constexpr int PGW = Cfg::PGW, NPS = Cfg::NPS;
   constexpr int LOADS = Cfg::LOADS, HLOADS = Cfg::HLOADS;
   constexpr int BRB = Cfg::BROWP * 16, XRB = Cfg::XROWP * 16;
   constexpr int KS = N / (2 * KPL);

@@ -36,14 +36,34 @@ bool valid_io(int io) { return io == MAMBA2_SSD_F32 || io == MAMBA2_SSD_BF16; }
 // layout flags above it.
 int io_type(int io_arg) { return io_arg & 0xff; }
 bool valid_io_arg(int io_arg) {
-  return valid_io(io_type(io_arg)) && (io_arg & ~(0xff | MAMBA2_SSD_DT_HEAD_MAJOR)) == 0;
+  return valid_io(io_type(io_arg)) && (io_arg & ~(0xff | MAMBA2_SSD_DT_HEAD_MAJOR | MAMBA2_SSD_PATH_MASK)) == 0;
 }
+int path_field(int io_arg) { return io_arg & MAMBA2_SSD_PATH_MASK; }
 size_t io_size(int io_arg) { return io_type(io_arg) == MAMBA2_SSD_BF16 ? 2 : 4; }
 
 struct Sizes {
+  int path = 0;                  // MAMBA2_SSD_PATH_FOUR, _THREE or _CHAINED
   int64_t nc = 0, Tp = 0;
   int64_t n_x = 0, n_dt = 0, n_bc = 0, n_state = 0, n_chunkstates = 0;
 };
+
+// The kernel sequence a forward call takes (MAMBA2_SSD_PATH_FOUR, _THREE or
+// _CHAINED), or 0 when the path field of io_arg asks for one that does not
+// support the shape. Automatic choice: the chained kernel wherever it
+// supports the shape; otherwise the chunk states inside the state pass when
+// the (batch, head, dstate group) walks alone fill the GPU
+// (chunk_state_pass_pays); otherwise the four kernels.
+int choose_path(const ssd::Problem& p, int io_arg) {
+  switch (path_field(io_arg)) {
+    case MAMBA2_SSD_PATH_FOUR: return MAMBA2_SSD_PATH_FOUR;
+    case MAMBA2_SSD_PATH_THREE: return ssd::chunk_state_pass_fits(p) ? MAMBA2_SSD_PATH_THREE : 0;
+    case MAMBA2_SSD_PATH_CHAINED: return ssd::chunk_chained_fits(p) ? MAMBA2_SSD_PATH_CHAINED : 0;
+    default: break;
+  }
+  if (ssd::chunk_chained_fits(p)) return MAMBA2_SSD_PATH_CHAINED;
+  if (ssd::chunk_state_pass_fits(p) && ssd::chunk_state_pass_pays(p)) return MAMBA2_SSD_PATH_THREE;
+  return MAMBA2_SSD_PATH_FOUR;
+}
 
 // Dimension checks shared by every entry point.
 int check_dims(const mamba2_ssd_dims* d, int io_arg, Sizes* s) {
@@ -84,12 +104,20 @@ int check_dims(const mamba2_ssd_dims* d, int io_arg, Sizes* s) {
   if (d->chunk * d->nheads * d->headdim * esz >= (int64_t)1 << 31 ||
       d->chunk * d->ngroups * d->dstate * esz >= (int64_t)1 << 31)
     return MAMBA2_SSD_ERR_BAD_DIM;
+  ssd::Problem p{};
+  p.bt = d->batch; p.T = d->seqlen; p.H = d->nheads; p.P = d->headdim; p.N = d->dstate;
+  p.G = d->ngroups; p.Q = d->chunk; p.nc = r.nc; p.Tp = r.Tp; p.io = io;
+  r.path = choose_path(p, io_arg);
+  if (!r.path) return MAMBA2_SSD_ERR_UNSUPPORTED;
   *s = r;
   return MAMBA2_SSD_OK;
 }
 
+// Regions a path does not use take no bytes (their offset is that of the
+// next region).
 void layout_of(const mamba2_ssd_dims* d, const Sizes& s, mamba2_ssd_workspace_layout* L) {
   const size_t bh = (size_t)d->batch * (size_t)d->nheads;
+  const bool four = s.path == MAMBA2_SSD_PATH_FOUR, chained = s.path == MAMBA2_SSD_PATH_CHAINED;
   size_t off = 0;
   L->gcum_offset = off;
   off = align_up(off + bh * (size_t)s.Tp * 4);
@@ -98,23 +126,16 @@ void layout_of(const mamba2_ssd_dims* d, const Sizes& s, mamba2_ssd_workspace_la
   L->wst_offset = off;
   off = align_up(off + bh * (size_t)s.Tp * 4);
   L->states_offset = off;
-  off = align_up(off + (size_t)s.n_chunkstates * 4);
+  if (four) off = align_up(off + (size_t)s.n_chunkstates * 4);
   L->hprev_offset = off;
-  off = align_up(off + (size_t)s.n_chunkstates * 4);
+  if (!chained) off = align_up(off + (size_t)s.n_chunkstates * 4);
+  L->chain_offset = off;
+  if (chained) off = align_up(off + (size_t)s.n_state * 4);
+  L->sync_offset = off;
+  if (chained) off = align_up(off + (bh + 64) * 4);
   L->total_bytes = off;
   L->nchunks = s.nc;
-}
-
-// Whether a forward call computes the chunk states inside the state pass
-// (one kernel, see chunk_state.hip). MAMBA2_SSD_STATE_PATH in the environment
-// (read per call) overrides the size rule: "unfused" forces the two-kernel
-// path, "fused" takes the one-kernel path for every shape it supports. A
-// diagnostic switch; the paths agree to fp32 rounding.
-bool use_fused_state(const ssd::Problem& p) {
-  const char* e = std::getenv("MAMBA2_SSD_STATE_PATH");
-  if (e && std::strcmp(e, "unfused") == 0) return false;
-  if (e && std::strcmp(e, "fused") == 0) return ssd::chunk_state_pass_fits(p);
-  return ssd::chunk_state_pass_fits(p) && ssd::chunk_state_pass_pays(p);
+  L->path = s.path;
 }
 
 ssd::Problem problem_of(const mamba2_ssd_dims* d, int io_arg, const Sizes& s) {
@@ -170,6 +191,12 @@ int mamba2_ssd_check_args(const mamba2_ssd_dims* d, int io, const void* x, const
   const bool tokens = s.n_x > 0;
   if (!A || !D) return MAMBA2_SSD_ERR_NULL_POINTER;
   if (tokens && (!x || !dt || !B || !C || !y)) return MAMBA2_SSD_ERR_NULL_POINTER;
+  // the kernels move x, B, C, y and the states in 16-byte pieces and address
+  // the workspace regions at 256-byte offsets
+  auto mis = [](const void* q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) & (a - 1)) != 0; };
+  if (mis(x, 16) || mis(B, 16) || mis(C, 16) || mis(y, 16) || mis(init_state, 16) || mis(final_state, 16) ||
+      mis(dt, 4) || mis(A, 4) || mis(D, 4) || mis(workspace, kAlign))
+    return MAMBA2_SSD_ERR_ALIGN;
   mamba2_ssd_workspace_layout L;
   layout_of(d, s, &L);
   if (d->batch > 0 && L.total_bytes > 0 && (!workspace || workspace_bytes < L.total_bytes))
@@ -225,6 +252,8 @@ int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* d, int io, const void* x, const 
   p.wst = reinterpret_cast<float*>(ws + L.wst_offset);
   p.states = reinterpret_cast<float*>(ws + L.states_offset);
   p.hprev = ws + L.hprev_offset;
+  p.chain = reinterpret_cast<float*>(ws + L.chain_offset);
+  p.sync = reinterpret_cast<int*>(ws + L.sync_offset);
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
   hipError_t err = hipSuccess;
@@ -234,19 +263,29 @@ int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* d, int io, const void* x, const 
   mark(0);
   if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_cumsum(p, hs);
   mark(1);
-  if (use_fused_state(p)) {
-    // chunk states and the pass in one kernel; the events around the pass
-    // then enclose nothing
-    if (err == hipSuccess) err = ssd::launch_chunk_state_pass(p, hs);
-    mark(2);
-  } else {
-    if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_state(p, hs);
-    mark(2);
-    // with seqlen == 0 the pass runs zero chunks: final_state = init_state (or 0)
-    if (err == hipSuccess && (s.nc > 0 || final_state)) err = ssd::launch_state_pass(p, hs);
+  switch (s.path) {
+    case MAMBA2_SSD_PATH_CHAINED:
+      // states, pass and outputs in one kernel: events 1..2 enclose it
+      if (err == hipSuccess) err = ssd::launch_chunk_chained(p, hs);
+      mark(2);
+      mark(3);
+      break;
+    case MAMBA2_SSD_PATH_THREE:
+      // chunk states and the pass in one kernel: events 1..2 enclose it
+      if (err == hipSuccess) err = ssd::launch_chunk_state_pass(p, hs);
+      mark(2);
+      mark(3);
+      if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_scan(p, hs);
+      break;
+    default:
+      if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_state(p, hs);
+      mark(2);
+      // with seqlen == 0 the pass runs zero chunks: final_state = init_state (or 0)
+      if (err == hipSuccess && (s.nc > 0 || final_state)) err = ssd::launch_state_pass(p, hs);
+      mark(3);
+      if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_scan(p, hs);
+      break;
   }
-  mark(3);
-  if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_scan(p, hs);
   mark(4);
   if (err != hipSuccess) {
     g_last_hip_error = hipGetErrorString(err);
@@ -255,10 +294,16 @@ int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* d, int io, const void* x, const 
   return MAMBA2_SSD_OK;
 }
 
+int mamba2_ssd_fwd_path(const mamba2_ssd_dims* dims, int io_dtype) {
+  Sizes s;
+  const int st = check_dims(dims, io_dtype, &s);
+  return st != MAMBA2_SSD_OK ? st : s.path;
+}
+
 int mamba2_ssd_fused_state_pass(const mamba2_ssd_dims* dims, int io_dtype) {
   Sizes s;
   if (check_dims(dims, io_dtype, &s) != MAMBA2_SSD_OK) return 0;
-  return use_fused_state(problem_of(dims, io_dtype, s)) ? 1 : 0;
+  return s.path != MAMBA2_SSD_PATH_FOUR ? 1 : 0;
 }
 
 int mamba2_ssd_step_supported(int64_t dstate, int io_dtype) {

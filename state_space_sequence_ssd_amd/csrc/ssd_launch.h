@@ -26,6 +26,8 @@ struct Problem {
   float* wst;                    // workspace: [bt][H][Tp]
   float* states;                 // workspace: [bt][H][nc][P][N]
   void* hprev;                   // workspace: [bt][H][nc][P][N] fp32, or bf16 (hi, lo) pairs
+  float* chain;                  // workspace (chained path): [bt][H][P][N] carried state slots
+  int* sync;                     // workspace (chained path): ticket counter, then one flag per (bt, H)
 };
 
 // One decode step (see ssd_step.hip). Device pointers, validated by the ABI.
@@ -53,6 +55,11 @@ hipError_t launch_ssd_step(const StepProblem& p, hipStream_t stream);
 bool chunk_state_pass_fits(const Problem& p);
 bool chunk_state_pass_pays(const Problem& p);
 hipError_t launch_chunk_state_pass(const Problem& p, hipStream_t stream);
+// States, pass and outputs in one kernel, the carried state handed from
+// chunk to chunk through memory (chunk_chained.hip); the cumsum kernel clears
+// its counters.
+bool chunk_chained_fits(const Problem& p);
+hipError_t launch_chunk_chained(const Problem& p, hipStream_t stream);
 // The C.B^T-resident scan (chunk_scan_resident.hip) and the shapes it takes.
 bool chunk_scan_resident_fits(const Problem& p);
 hipError_t launch_chunk_scan_resident(const Problem& p, hipStream_t stream);

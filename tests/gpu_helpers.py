@@ -44,18 +44,19 @@ def to_device(inp: dict, io: str, dev="cuda:0") -> dict:
     return out
 
 
-def run(dev_inp: dict, chunk: int, keep_workspace=False, init_state="default", final=True):
-    """Call the library; optionally return the workspace for per-kernel checks."""
+def run(dev_inp: dict, chunk: int, keep_workspace=False, init_state="default", final=True, path=0):
+    """Call the library (``path``: a PATH_* kernel sequence, 0 = the library's
+    choice); optionally return the workspace for per-kernel checks."""
     init = dev_inp["init_state"] if init_state == "default" else init_state
     x = dev_inp["x"]
     io = BF16 if x.dtype == torch.bfloat16 else F32
     bt, T, H, P = x.shape
     G, N = dev_inp["B"].shape[2:]
     dims = Dims(bt, T, H, P, N, G, chunk)
-    L = ssd.workspace_layout(dims, io)
+    L = ssd.workspace_layout(dims, io | path)
     ws = torch.empty(max(L.total_bytes, 1), dtype=torch.uint8, device=x.device)
     y, fin = ssd.ssd_fwd(x, dev_inp["dt"], dev_inp["A"], dev_inp["B"], dev_inp["C"], dev_inp["D"], chunk,
-                         init, return_final_state=final, workspace=ws)
+                         init, return_final_state=final, workspace=ws, path=path)
     torch.cuda.synchronize()
     if keep_workspace:
         return y, fin, ws, L, dims

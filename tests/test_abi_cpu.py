@@ -36,7 +36,8 @@ def test_header_declares_the_entry_points():
         "mamba2_ssd_check_args", "mamba2_ssd_fwd", "mamba2_ssd_fwd_timed", "mamba2_ssd_fwd_workspace_bytes",
         "mamba2_ssd_last_hip_error", "mamba2_ssd_status_string", "mamba2_ssd_supported",
         "mamba2_ssd_workspace_layout_query", "mamba2_ssd_step", "mamba2_ssd_step_check_args",
-        "mamba2_ssd_step_supported", "mamba2_ssd_fused_state_pass", "mamba2_ssd_bwd",
+        "mamba2_ssd_step_supported", "mamba2_ssd_fused_state_pass", "mamba2_ssd_fwd_path",
+        "mamba2_ssd_bwd",
         "mamba2_ssd_bwd_check_args", "mamba2_ssd_bwd_workspace_bytes", "mamba1_s6_fwd", "mamba1_s6_check_args",
         "mamba1_s6_supported", "mamba1_s6_workspace_bytes"])
 
@@ -60,20 +61,62 @@ HEADLINE = Dims(4, 8192, 80, 64, 128, 1, 256)
 
 
 def test_workspace_layout_headline():
-    L = ssd.workspace_layout(HEADLINE, BF16)
+    """Regions per kernel sequence: FOUR holds the chunk states and hprev,
+    THREE only hprev, CHAINED neither but the carried-state slots and the
+    sync words; unused regions take no bytes."""
     nc = 32
-    assert L.nchunks == nc
-    assert L.gcum_offset == 0
-    assert L.dtt_offset == 4 * 80 * 8192 * 4
-    assert L.wst_offset == 2 * 4 * 80 * 8192 * 4
-    assert L.states_offset == 3 * 4 * 80 * 8192 * 4
+    gq = 4 * 80 * 8192 * 4                      # one [batch][nheads][Tp] fp32 array
     states = 4 * 80 * nc * 64 * 128 * 4
-    assert L.hprev_offset == L.states_offset + states
-    assert L.total_bytes == L.hprev_offset + states          # hprev is fp32 for every io dtype
-    for off in (L.gcum_offset, L.dtt_offset, L.wst_offset, L.states_offset, L.hprev_offset, L.total_bytes):
-        assert off % 256 == 0
-    assert ssd.workspace_bytes(HEADLINE, BF16) == L.total_bytes
-    assert ssd.workspace_bytes(HEADLINE, F32) == L.total_bytes
+    four = ssd.workspace_layout(HEADLINE, BF16 | ssd.PATH_FOUR)
+    assert four.path == ssd.PATH_FOUR and four.nchunks == nc
+    assert (four.gcum_offset, four.dtt_offset, four.wst_offset, four.states_offset) == (0, gq, 2 * gq, 3 * gq)
+    assert four.hprev_offset == four.states_offset + states
+    assert four.chain_offset == four.sync_offset == four.total_bytes == four.hprev_offset + states
+    three = ssd.workspace_layout(HEADLINE, BF16 | ssd.PATH_THREE)
+    assert three.path == ssd.PATH_THREE
+    assert three.states_offset == three.hprev_offset == 3 * gq
+    assert three.total_bytes == three.hprev_offset + states
+    for L in (four, three):
+        for off in (L.gcum_offset, L.dtt_offset, L.wst_offset, L.states_offset, L.hprev_offset, L.total_bytes):
+            assert off % 256 == 0
+    auto = ssd.workspace_layout(HEADLINE, BF16)
+    assert auto.path == ssd.fwd_path(HEADLINE, BF16)
+    assert ssd.workspace_bytes(HEADLINE, BF16) == auto.total_bytes
+    assert ssd.workspace_bytes(HEADLINE, F32) == four.total_bytes   # fp32 io: four kernels
+    if ssd.fwd_path(HEADLINE, BF16) == ssd.PATH_CHAINED:
+        ch = ssd.workspace_layout(HEADLINE, BF16 | ssd.PATH_CHAINED)
+        assert ch.states_offset == ch.hprev_offset == ch.chain_offset == 3 * gq
+        assert ch.sync_offset == ch.chain_offset + 4 * 80 * 64 * 128 * 4
+        assert ch.total_bytes == ch.sync_offset + ((4 * 80 + 64) * 4 + 255) // 256 * 256
+
+
+def test_path_field():
+    """The kernel-sequence field of io: forcing a sequence that does not take
+    the shape is UNSUPPORTED everywhere; FOUR takes every supported shape."""
+    for io in (BF16, F32):
+        assert ssd.fwd_path(SMALL, io | ssd.PATH_FOUR) == ssd.PATH_FOUR
+        assert _check(SMALL, io | ssd.PATH_FOUR) == OK
+    assert ssd.fwd_path(HEADLINE, BF16 | ssd.PATH_THREE) == ssd.PATH_THREE
+    assert ssd.fwd_path(HEADLINE, F32) == ssd.PATH_FOUR
+    for d, io in ((HEADLINE, F32 | ssd.PATH_THREE), (SMALL, BF16 | ssd.PATH_THREE),   # fp32; chunk 128
+                  (Dims(4, 8192, 80, 128, 128, 1, 256), BF16 | ssd.PATH_THREE)):     # headdim 128
+        assert _check(d, io) == UNSUP
+        with pytest.raises(ssd.SsdError):
+            ssd.fwd_path(d, io)
+        assert ssd.workspace_bytes(d, io) == 0
+    if not ssd.fwd_path(HEADLINE, BF16) == ssd.PATH_CHAINED:
+        assert _check(HEADLINE, BF16 | ssd.PATH_CHAINED) == UNSUP
+    assert ssd.fwd_path(Dims(8, 2048, 24, 64, 128, 1, 256), BF16 | ssd.PATH_FOUR) == ssd.PATH_FOUR
+
+
+def test_alignment():
+    """x, B, C, y, init, final on 16 bytes; dt, A, D on 4; workspace on 256."""
+    p, _ = _ptrs(SMALL, BF16)
+    for name, off in (("x", 2), ("x", 8), ("B", 8), ("C", 4), ("y", 2), ("init", 8), ("fin", 4), ("dt", 2),
+                      ("A", 1), ("D", 2), ("ws", 16)):
+        assert _check(SMALL, BF16, **{name: p[name] + off}) == ALIGN, name
+    assert _check(SMALL, BF16, ws=p["ws"] + 256) == OK
+    assert _check(SMALL, BF16, dt=p["dt"] + 4) == OK
 
 
 def test_workspace_layout_ragged_pads_to_chunks():
@@ -192,20 +235,20 @@ def test_alias_rules():
     assert _check(SMALL, BF16, fin=p["init"]) == OK              # in-place state update
     assert _check(SMALL, BF16, fin=p["init"] + 64) == ALIAS       # partial overlap
     assert _check(SMALL, BF16, fin=p["dt"]) == ALIAS
-    assert _check(SMALL, BF16, ws=p["y"] + 8) == ALIAS
+    assert _check(SMALL, BF16, ws=p["y"] + 256) == ALIAS
     assert _check(SMALL, BF16, ws=p["C"]) == ALIAS
     assert _check(SMALL, BF16, C=p["B"]) == OK                     # inputs may overlap each other
 
 
 def test_empty_problems():
     d0 = Dims(0, 100, 8, 64, 128, 1, 64)
-    assert ssd.check_args(d0, BF16, 0, 0, 1, 0, 0, 1, 0, 0, 0, 0, 0) == OK
+    assert ssd.check_args(d0, BF16, 0, 0, 256, 0, 0, 512, 0, 0, 0, 0, 0) == OK
     dt0 = Dims(2, 0, 8, 64, 128, 1, 64)
     assert ssd.workspace_bytes(dt0, BF16) == 0
     assert ssd.workspace_layout(dt0, BF16).nchunks == 0
-    assert ssd.check_args(dt0, BF16, 0, 0, 1, 0, 0, 1, 1 << 30, 0, 1 << 31, 0, 0) == OK
+    assert ssd.check_args(dt0, BF16, 0, 0, 256, 0, 0, 512, 1 << 30, 0, 1 << 31, 0, 0) == OK
     # fwd with batch 0 returns OK without touching the GPU
-    ssd.ssd_fwd_ptr(d0, BF16, 0, 0, 1, 0, 0, 1, 0, 0, 0, 0, 0, 0)
+    ssd.ssd_fwd_ptr(d0, BF16, 0, 0, 256, 0, 0, 512, 0, 0, 0, 0, 0, 0)
 
 
 def test_fwd_reports_validation_errors_without_launching():
@@ -302,22 +345,21 @@ def test_step_empty_and_errors_without_launching():
     assert ssd._lib.lib.mamba2_ssd_step_check_args(None, BF16, 1, 1, 1, 1, 1, 1, 1, 1) == NULLP
 
 
-def test_fused_state_pass_query(monkeypatch):
+def test_fused_state_pass_query():
     # the 2.7B-like layer: bf16, headdim 64, 4 x 80 heads x 2 dstate groups
     assert ssd.fused_state_pass(HEADLINE, BF16)
-    assert not ssd.fused_state_pass(Dims(8, 2048, 24, 64, 128, 1, 256), BF16)    # 384 pairs: two kernels
-    assert not ssd.fused_state_pass(HEADLINE, F32)                      # fp32 io: two kernels
-    assert not ssd.fused_state_pass(Dims(1, 65536, 80, 64, 128, 1, 256), BF16)   # too few (b, h) pairs
+    assert not ssd.fused_state_pass(HEADLINE, F32)                      # fp32 io: four kernels
     assert not ssd.fused_state_pass(Dims(4, 8192, 80, 128, 128, 1, 256), BF16)   # headdim 128
-    assert not ssd.fused_state_pass(Dims(4, 0, 80, 64, 128, 1, 256), BF16)       # no chunks
     assert not ssd.fused_state_pass(Dims(4, 8192, 80, 64, 128, 3, 256), BF16)    # invalid (groups)
-    monkeypatch.setenv("MAMBA2_SSD_STATE_PATH", "unfused")
-    assert not ssd.fused_state_pass(HEADLINE, BF16)
-    monkeypatch.setenv("MAMBA2_SSD_STATE_PATH", "fused")
-    assert ssd.fused_state_pass(Dims(1, 65536, 80, 64, 128, 1, 256), BF16)
-    assert ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 256), BF16)
-    assert not ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 128), BF16)       # chunk 128: not supported
-    assert not ssd.fused_state_pass(HEADLINE, F32)
+    assert not ssd.fused_state_pass(HEADLINE, BF16 | ssd.PATH_FOUR)
+    assert ssd.fused_state_pass(Dims(1, 65536, 80, 64, 128, 1, 256), BF16 | ssd.PATH_THREE)
+    assert ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 256), BF16 | ssd.PATH_THREE)
+    assert not ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 128), BF16 | ssd.PATH_THREE)   # chunk 128
+    if ssd.fwd_path(HEADLINE, BF16) != ssd.PATH_CHAINED:
+        # without the chained kernel the size rule decides
+        assert not ssd.fused_state_pass(Dims(8, 2048, 24, 64, 128, 1, 256), BF16)   # 384 walks: four kernels
+        assert not ssd.fused_state_pass(Dims(1, 65536, 80, 64, 128, 1, 256), BF16)  # 160 walks
+        assert not ssd.fused_state_pass(Dims(4, 0, 80, 64, 128, 1, 256), BF16)      # no chunks
 
 
 # ------------------------------------------------------------- backward pass

@@ -35,12 +35,14 @@ def oracle_all(inp, cfg, intermediates=False):
 
 @pytest.mark.parametrize("name", sorted(SMALL))
 def test_small_variant_parity(name):
+    """Every kernel's output on the FOUR sequence (the only one that writes
+    each intermediate to the workspace) against the oracle's intermediates."""
     cfg = SMALL[name]
     log(f"[parity] {name}: {cfg}")
     inp = generate(cfg)
     yr, fr, inter = oracle_all(inp, cfg, intermediates=True)
     dev = to_device(inp, cfg.io)
-    y, fin, ws, L, dims = run(dev, cfg.chunk, keep_workspace=True)
+    y, fin, ws, L, dims = run(dev, cfg.chunk, keep_workspace=True, path=ssd.PATH_FOUR)
     io = 1 if cfg.io == "bf16" else 0
     v = workspace_views(ws, L, dims, io)
     Tp = L.nchunks * cfg.chunk
@@ -139,9 +141,11 @@ def test_dt_zero_holds_state_exactly():
     check_close(host(y), yr, cfg.io, "y with dt == 0")
 
 
-def test_zero_decay_is_linear_attention():
-    """A = 0 (the limit of the decay going away): causal linear attention."""
-    cfg = _cfg(seqlen=2 * 128 + 3, io="f32", init_sigma=None)
+@pytest.mark.parametrize("io,chunk", [("f32", 128), ("bf16", 128), ("bf16", 256)])
+def test_zero_decay_is_linear_attention(io, chunk):
+    """A = 0 (the limit of the decay going away): causal linear attention,
+    as one dense T x T masked product."""
+    cfg = _cfg(seqlen=2 * chunk + 3, io=io, init_sigma=None, chunk=chunk, headdim=64)
     inp = generate(cfg)
     inp["A"][:] = 0.0
     y, fin = run(to_device(inp, cfg.io), cfg.chunk)
@@ -154,7 +158,7 @@ def test_zero_decay_is_linear_attention():
             Cg, Bg = C[b, :, 0].astype(np.float64), B[b, :, 0].astype(np.float64)
             X = x[b, :, h].astype(np.float64)
             ref[b, :, h] = ((Cg @ Bg.T) * mask) @ (dt[b, :, h, None] * X) + D[h] * X
-    check_close(host(y), ref, "f32", "linear attention")
+    log("  " + check_close(host(y), ref, io, "linear attention"))
 
 
 def test_in_place_state_update():
@@ -269,10 +273,10 @@ def test_resident_scan_walks(name):
 
 
 # ------------------------------------ chunk states computed inside the state pass
-# (bf16, headdim 64, chunk 256: the one-kernel path). MAMBA2_SSD_STATE_PATH
-# forces either path regardless of size; both must match the oracle, and each
-# other up to fp32 rounding (the one-kernel form sums a chunk's two halves
-# separately, then adds them).
+# (bf16, headdim 64, chunk 256: the THREE sequence). The path field of io
+# forces either sequence regardless of size; both must match the oracle, and
+# each other up to fp32 rounding (the one-kernel form sums a chunk's two
+# halves separately, then adds them).
 FUSED = {
     "2.7b-ragged": dict(batch=2, seqlen=3 * 256 + 13, nheads=5),
     "one-chunk": dict(batch=3, seqlen=100, nheads=2),
@@ -284,24 +288,22 @@ FUSED = {
 
 
 @pytest.mark.parametrize("name", sorted(FUSED))
-def test_fused_state_pass(name, monkeypatch):
+def test_fused_state_pass(name):
     cfg = LayerConfig(f"fused-{name}", **{**dict(headdim=64, dstate=128, ngroups=1, chunk=256, io="bf16",
                                                seed=700 + len(name), init_sigma=0.3), **FUSED[name]})
     log(f"[fused] {name}: {cfg}")
     inp = generate(cfg)
     yr, fr, inter = oracle_all(inp, cfg, intermediates=True)
     dev = to_device(inp, cfg.io)
-    monkeypatch.setenv("MAMBA2_SSD_STATE_PATH", "fused")
-    y1, f1, ws1, L, dims = run(dev, cfg.chunk, keep_workspace=True)
-    assert ssd.fused_state_pass(dims, 1)
+    y1, f1, ws1, L, dims = run(dev, cfg.chunk, keep_workspace=True, path=ssd.PATH_THREE)
+    assert ssd.fused_state_pass(dims, 1 | ssd.PATH_THREE) and L.path == ssd.PATH_THREE
     v = workspace_views(ws1, L, dims, 1)
     log("  " + check_close(host(v["hprev"]), inter["hprev"], cfg.io, "hprev (fused)"))
     log("  " + check_close(host(y1), yr, cfg.io, "y (fused)"))
     log("  " + check_close(host(f1), fr, cfg.io, "final_state (fused)"))
-    monkeypatch.setenv("MAMBA2_SSD_STATE_PATH", "unfused")
-    y2, f2, ws2, _, _ = run(dev, cfg.chunk, keep_workspace=True)
-    assert not ssd.fused_state_pass(dims, 1)
-    v2 = workspace_views(ws2, L, dims, 1)
+    y2, f2, ws2, L2, _ = run(dev, cfg.chunk, keep_workspace=True, path=ssd.PATH_FOUR)
+    assert not ssd.fused_state_pass(dims, 1 | ssd.PATH_FOUR) and L2.path == ssd.PATH_FOUR
+    v2 = workspace_views(ws2, L2, dims, 1)
     for what, a1, a2 in (("hprev", v["hprev"], v2["hprev"]), ("final_state", f1, f2)):
         a1, a2 = host(a1), host(a2)
         rel = float(np.max(np.abs(a1 - a2))) / max(float(np.max(np.abs(a2))), 1e-30)
@@ -310,23 +312,22 @@ def test_fused_state_pass(name, monkeypatch):
     assert np.all(np.abs(yy1 - yy2) <= 2.0 ** -7 * np.abs(yy2) + 1e-6), "y: paths differ by more than 1 bf16 ulp"
 
 
-def test_fused_state_pass_in_place_and_no_final(monkeypatch):
+def test_fused_state_pass_in_place_and_no_final():
     """init_state may be final_state (in-place update); final_state may be absent."""
     cfg = LayerConfig("fused-inplace", batch=2, seqlen=2 * 256 + 40, nheads=3, headdim=64, dstate=128,
                       ngroups=1, chunk=256, io="bf16", seed=731, init_sigma=0.3)
     inp = generate(cfg)
     yr, fr = oracle_all(inp, cfg)
     dev = to_device(inp, cfg.io)
-    monkeypatch.setenv("MAMBA2_SSD_STATE_PATH", "fused")
     st = dev["init_state"].clone()
     y, fin = ssd.ssd_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], cfg.chunk, st,
-                         final_state=st)
+                         final_state=st, path=ssd.PATH_THREE)
     torch.cuda.synchronize()
     assert fin.data_ptr() == st.data_ptr()
     check_close(host(st), fr, cfg.io, "final_state in place (fused)")
     check_close(host(y), yr, cfg.io, "y (fused, in place)")
     y2, none = ssd.ssd_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], cfg.chunk,
-                           dev["init_state"], return_final_state=False)
+                           dev["init_state"], return_final_state=False, path=ssd.PATH_THREE)
     torch.cuda.synchronize()
     assert none is None
     check_close(host(y2), yr, cfg.io, "y (fused, no final)")
@@ -342,23 +343,24 @@ DT_LAYOUT = {
 }
 
 
-@pytest.mark.parametrize("path", ["default", "fused"])
+@pytest.mark.parametrize("path", ["default", "three"])
 @pytest.mark.parametrize("name", sorted(DT_LAYOUT))
-def test_dt_head_major_layout(name, path, monkeypatch):
+def test_dt_head_major_layout(name, path):
     """dt given [batch, nheads, seqlen] (MAMBA2_SSD_DT_HEAD_MAJOR) gives
     bit-identical results to the token-major call, and matches the oracle."""
     cfg = DT_LAYOUT[name]
-    if path == "fused":
+    pf = 0
+    if path == "three":
         if not (cfg.io == "bf16" and cfg.headdim == 64 and cfg.chunk == 256):
-            pytest.skip("the one-kernel state path takes bf16, headdim 64, chunk 256 only")
-        monkeypatch.setenv("MAMBA2_SSD_STATE_PATH", "fused")
+            pytest.skip("the THREE sequence takes bf16, headdim 64, chunk 256 only")
+        pf = ssd.PATH_THREE
     log(f"[dt layout] {name} path={path} {cfg}")
     inp = generate(cfg)
     dev = to_device(inp, cfg.io)
-    y0, f0 = run(dev, cfg.chunk)
+    y0, f0 = run(dev, cfg.chunk, path=pf)
     dt_hm = dev["dt"].transpose(1, 2).contiguous()
     y1, f1 = ssd.ssd_fwd(dev["x"], dt_hm, dev["A"], dev["B"], dev["C"], dev["D"], cfg.chunk,
-                         dev["init_state"], dt_head_major=True)
+                         dev["init_state"], dt_head_major=True, path=pf)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1), "y differs between the dt layouts"
     assert torch.equal(f0, f1), "final_state differs between the dt layouts"
