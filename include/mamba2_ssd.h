@@ -253,6 +253,32 @@ int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* dims, int io_dtype,
                          void* workspace, size_t workspace_bytes, void* stream,
                          void* const* events);
 
+/* ---- forward pass without caller memory -----------------------------------
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Identical
+ * to mamba2_ssd_fwd (same arguments apart from the workspace, same kernels,
+ * same results bit for bit) except that the workspace is a device array
+ * inside the library, MAMBA2_SSD_NOALLOC_MAX_WORKSPACE bytes per GPU, held
+ * from the library's load until the process ends. Calls whose workspace
+ * (mamba2_ssd_fwd_workspace_bytes with the same io_dtype) exceeds it return
+ * MAMBA2_SSD_ERR_WORKSPACE before anything is launched. The call allocates
+ * nothing (no hipMalloc, no library allocator); on its first use on a GPU it
+ * looks up the array's address there (hipGetSymbolAddress).
+ * The array is shared by every call on the same GPU and keeps the last
+ * call's contents (every region a call reads is written by that call first,
+ * so nothing has to start at zero). Calls that overlap in time on one GPU
+ * (on different streams, or from different threads) race on it and give
+ * undefined results; serialise them. The stream's device (the current
+ * device for a NULL stream) selects the array. */
+#define MAMBA2_SSD_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+
+int mamba2_ssd_fwd_noalloc(const mamba2_ssd_dims* dims, int io_dtype,
+                           const void* x, const float* dt, const float* A,
+                           const void* B, const void* C, const float* D,
+                           const float* init_state, void* y, float* final_state,
+                           void* stream);
+
 /* ---- one decode step ----------------------------------------------------
  *
  * The recurrent form of the same layer (blog section "Mamba-2 architecture":

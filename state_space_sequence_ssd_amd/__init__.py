@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 from typing import Optional, Tuple
 
-from ._lib import (BF16, DT_HEAD_MAJOR, F32, PATH_AUTO, PATH_CHAINED, PATH_FOUR, PATH_NAMES, PATH_THREE, STATUS,
+from ._lib import (BF16, DT_HEAD_MAJOR, F32, NOALLOC_MAX_WORKSPACE, PATH_AUTO, PATH_CHAINED, PATH_FOUR, PATH_NAMES, PATH_THREE, STATUS,
                    Dims, S6Dims, SsdError, StepDims, WorkspaceLayout, lib, status_string)
 
 __all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_layout", "check_args",
@@ -24,6 +24,7 @@ __all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_
            "mamba2_ssd_step", "mamba2_ssd_step_check_args", "mamba2_ssd_step_supported",
            "mamba2_ssd_fused_state_pass", "fused_state_pass", "mamba2_ssd_fwd_path", "fwd_path",
            "PATH_AUTO", "PATH_FOUR", "PATH_THREE", "PATH_CHAINED", "PATH_NAMES",
+           "mamba2_ssd_fwd_noalloc", "ssd_fwd_noalloc_ptr", "NOALLOC_MAX_WORKSPACE",
            "ssd_bwd", "ssd_bwd_ptr", "bwd_workspace_bytes", "bwd_check_args",
            "mamba2_ssd_bwd", "mamba2_ssd_bwd_check_args", "mamba2_ssd_bwd_workspace_bytes",
            "S6Dims", "s6_fwd", "s6_fwd_ptr", "s6_supported", "s6_workspace_bytes", "s6_check_args",
@@ -40,6 +41,7 @@ mamba2_ssd_status_string = lib.mamba2_ssd_status_string
 mamba2_ssd_last_hip_error = lib.mamba2_ssd_last_hip_error
 mamba2_ssd_fused_state_pass = lib.mamba2_ssd_fused_state_pass
 mamba2_ssd_fwd_path = lib.mamba2_ssd_fwd_path
+mamba2_ssd_fwd_noalloc = lib.mamba2_ssd_fwd_noalloc
 mamba2_ssd_step = lib.mamba2_ssd_step
 mamba2_ssd_step_check_args = lib.mamba2_ssd_step_check_args
 mamba2_ssd_step_supported = lib.mamba2_ssd_step_supported
@@ -104,6 +106,15 @@ def ssd_fwd_ptr(dims, io, x, dt, A, B, C, D, init_state, y, final_state, workspa
     """mamba2_ssd_fwd on raw device addresses; raises SsdError on a nonzero status."""
     st = lib.mamba2_ssd_fwd(ctypes.byref(_dims(dims)), io, x, dt, A, B, C, D, init_state, y,
                             final_state, workspace, ws_bytes, stream)
+    if st != 0:
+        raise SsdError(st, lib.mamba2_ssd_last_hip_error().decode())
+
+
+def ssd_fwd_noalloc_ptr(dims, io, x, dt, A, B, C, D, init_state, y, final_state, stream: int = 0) -> None:
+    """mamba2_ssd_fwd_noalloc on raw device addresses (the workspace is the
+    library's own device array); raises SsdError on a nonzero status."""
+    st = lib.mamba2_ssd_fwd_noalloc(ctypes.byref(_dims(dims)), io, x, dt, A, B, C, D, init_state, y,
+                                    final_state, stream)
     if st != 0:
         raise SsdError(st, lib.mamba2_ssd_last_hip_error().decode())
 

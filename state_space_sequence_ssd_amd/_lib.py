@@ -12,6 +12,7 @@ DT_HEAD_MAJOR = 0x100   # OR-ed into io: dt given as [batch, nheads, seqlen]
 # kernel sequence, a field OR-ed into io (see include/mamba2_ssd.h)
 PATH_AUTO, PATH_FOUR, PATH_THREE, PATH_CHAINED = 0x0000, 0x1000, 0x2000, 0x3000
 PATH_NAMES = {PATH_FOUR: "four", PATH_THREE: "three", PATH_CHAINED: "chained"}
+NOALLOC_MAX_WORKSPACE = 64 << 20   # MAMBA2_SSD_NOALLOC_MAX_WORKSPACE
 
 STATUS = {
     0: "OK",
@@ -93,6 +94,8 @@ def _load():
     L.mamba2_ssd_fwd_timed.argtypes = [dims_p, ctypes.c_int, vp, fp, fp, vp, vp, fp, fp, vp, fp, vp, sz, vp,
                                        ctypes.POINTER(ctypes.c_void_p)]
     L.mamba2_ssd_fwd_timed.restype = ctypes.c_int
+    L.mamba2_ssd_fwd_noalloc.argtypes = [dims_p, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.mamba2_ssd_fwd_noalloc.restype = ctypes.c_int
     L.mamba2_ssd_fwd_path.argtypes = [dims_p, ctypes.c_int]
     L.mamba2_ssd_fwd_path.restype = ctypes.c_int
     L.mamba2_ssd_fused_state_pass.argtypes = [dims_p, ctypes.c_int]

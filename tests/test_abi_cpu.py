@@ -37,7 +37,7 @@ def test_header_declares_the_entry_points():
         "mamba2_ssd_last_hip_error", "mamba2_ssd_status_string", "mamba2_ssd_supported",
         "mamba2_ssd_workspace_layout_query", "mamba2_ssd_step", "mamba2_ssd_step_check_args",
         "mamba2_ssd_step_supported", "mamba2_ssd_fused_state_pass", "mamba2_ssd_fwd_path",
-        "mamba2_ssd_bwd",
+        "mamba2_ssd_fwd_noalloc", "mamba2_ssd_bwd",
         "mamba2_ssd_bwd_check_args", "mamba2_ssd_bwd_workspace_bytes", "mamba1_s6_fwd", "mamba1_s6_check_args",
         "mamba1_s6_supported", "mamba1_s6_workspace_bytes"])
 
@@ -256,6 +256,19 @@ def test_fwd_reports_validation_errors_without_launching():
         ssd.ssd_fwd_ptr(Dims(1, 64, 3, 64, 64, 2, 64), BF16, 1, 1, 1, 1, 1, 1, 0, 1, 0, 1, 1 << 30, 0)
     assert e.value.status == GROUPS
     assert "multiple" in str(e.value)
+
+
+def test_noalloc_rejects_oversize_without_a_gpu():
+    """The no-allocation entry point checks sizes against its array before
+    anything touches the GPU."""
+    d = Dims(4, 8192, 80, 64, 128, 1, 256)
+    assert ssd.workspace_bytes(d, BF16 | ssd.PATH_FOUR) > ssd.NOALLOC_MAX_WORKSPACE
+    lib = ssd._lib.lib
+    assert lib.mamba2_ssd_fwd_noalloc(ctypes.byref(d), BF16 | ssd.PATH_FOUR, 256, 256, 256, 256, 256, 256,
+                                      0, 1 << 40, 0, 0) == WS
+    assert lib.mamba2_ssd_fwd_noalloc(ctypes.byref(Dims(1, 64, 3, 64, 64, 2, 64)), BF16, 1, 1, 1, 1, 1, 1,
+                                      0, 1, 0, 0) == GROUPS
+    assert lib.mamba2_ssd_fwd_noalloc(None, BF16, 1, 1, 1, 1, 1, 1, 0, 1, 0, 0) == NULLP
 
 
 def test_status_strings():
