@@ -1,11 +1,702 @@
-// Placeholder: the chained one-kernel path is not built yet.
+// ssd_chunk_chained: the chunk states, the pass over them and the outputs in
+// one kernel (bf16 io, headdim 64, chunk 256, dstate 64 or 128). For every
+// (batch, chunk k, head) tile, with G' the chunk-local cumsum of A*dt times
+// log2 e (from ssd_chunk_cumsum) and h_k the state entering chunk k:
+//
+//   S_k     = sum_t w_t x_t (x) B_t,   w_t = dt_t 2^(G'_last - G'_t)   (the chunk's own state)
+//   h_{k+1} = 2^(G'_last) h_k + S_k                                    (the jump over the chunk)
+//   y_t     = 2^(G'_t) C_t . h_k + sum_{j<=t} (C_t . B_j) 2^(G'_t - G'_j) dt_j x_j + D x_t
+//
+// (CUDA Tile Mamba-2 blog, section "Mamba-2 architecture": the jump formula
+// and the decayed block output; "Kernel 2: fwd_pass_state" and "Kernel 3:
+// compute_out" are the two halves fused here.)
+//
+// Why one kernel. Split into a state pass and an output kernel, the path
+// writes every chunk's entering state to memory and reads it back, and reads
+// x twice: about 1 GB of traffic per call at the 2.7B-like layer on top of
+// the 0.7 GB that x, y, B, C and dt themselves need. Here every tile reads
+// x once and writes y once; the only state that moves is h_k itself, handed
+// from the tile of chunk k-1 to the tile of chunk k of the same head.
+//
+// The hand-off. Work items ("tickets") are (chunk k, batch b, block of HB
+// heads of one group), numbered chunk-major and claimed in order from a
+// counter by persistent workgroups. A tile needs h_k, which the tile of
+// chunk k-1 of the same head publishes: it stores h_{k+1} to that head's slot
+// in the workspace (device-coherent stores, so the value is visible to any
+// XCD), waits for the stores to complete, and then raises the head's progress
+// flag to k+1. The consumer polls the flag with device-coherent loads and
+// then reads the slot the same way. The ticket a tile waits on has a lower
+// number, so it was claimed by a workgroup that is already running and that
+// only waits on lower tickets itself: every wait ends. (The polls are bounded
+// all the same: a poll that outlives its bound records an error word in the
+// workspace and goes on.) The counter and flags are cleared by
+// ssd_chunk_cumsum, which runs first on the same stream.
+//
+// A ticket's heads share B and C (one group), so the workgroup computes the
+// causal C.B^T blocks once per ticket and keeps them in AGPRs, as the
+// resident scan does. Per head:
+//   phase A   S_k^T = B^T (w o X): wave w takes headdim half w & 1 and the
+//             dstate blocks NBW (w >> 1) + i, i < NBW = N / 64. B^T and X^T fragments
+//             come from LDS by gfx950's transposing reads; w o X enters as a
+//             bf16 (hi, lo) pair, two MFMAs against the exact bf16 B.
+//   chain     h_k lands in LDS (fp32, padded rows) by direct global->LDS
+//             loads; each wave reads its part in the accumulator layout of
+//             S_k^T, forms h_{k+1} with fmaf and stores it, then rewrites
+//             its part of h_k in place as bf16 (hi, lo) pairs, the operand
+//             format of the carried-state product.
+//   outputs   the resident scan's per-head work: carried-state term h_k.C^T
+//             scaled by 2^(G'_t), then the intra-chunk block pairs (decay,
+//             mask, dt and the hi/lo split applied to the resident C.B^T),
+//             products formed transposed (y^T = x^T M^T), D x on the
+//             diagonal, y out through LDS as 16-byte row pieces.
+// The next head's x tile is loaded while this head's outputs are stored.
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
+#include <type_traits>
+
 namespace ssd {
 
-bool chunk_chained_fits(const Problem&) { return false; }
+namespace {
 
-hipError_t launch_chunk_chained(const Problem&, hipStream_t) { return hipErrorInvalidValue; }
+template <int N>
+struct CCfg {
+  static constexpr int P = 64, Q = 256, NTB = 8, WAVES = 4, THREADS = 256;
+  static constexpr int KS = N / 16;             // bf16 MFMA k-steps over dstate
+  static constexpr int NBW = N / 64;            // dstate blocks per wave in phase A
+  static constexpr int XBYTES = Q * P * 2;      // x tile, 128-byte rows
+  static constexpr int GBYTES = 2 * Q * 4;      // G' row, then dt row
+  static constexpr int HRB = N * 4 + 16;        // state row: N fp32 (or N bf16 pairs) + one pad piece
+  static constexpr int HROWP = HRB / 16;
+  static constexpr int HBYTES = P * HRB;
+  static constexpr int BRB = N * 2;             // B row, unpadded, pieces swizzled
+  static constexpr int NPC = BRB / 16;          // 16-byte pieces per B row
+  static constexpr int BBYTES = Q * BRB;
+  static constexpr int IX = XBYTES / 1024, IG = GBYTES / 1024, IH = HBYTES / 1024, IB = BBYTES / 1024;
+  static constexpr int LX = IX / WAVES, LB = IB / WAVES;
+  static constexpr int LH = (IH + WAVES - 1) / WAVES;
+  static_assert(HBYTES % 1024 == 0 && IX % WAVES == 0 && IB % WAVES == 0, "whole direct-load instructions");
+  static_assert(BBYTES + XBYTES + GBYTES + HBYTES + 4 * 4096 + 3 * Q * 4 + 64 <= 160 * 1024, "LDS");
+};
+
+// 16-byte piece c of B row t sits at piece c ^ bswz(t): the transposing
+// reads of phase A (4 rows x 2 adjacent pieces per 16 lanes) and the row
+// fragment reads of C.B^T (16 rows x 1 piece per 16 lanes) then both hit 16
+// distinct 16-byte bank groups.
+template <int N>
+__device__ __forceinline__ constexpr uint32_t bswz(uint32_t t) {
+  constexpr uint32_t H = CCfg<N>::NPC / 2;
+  return 2 * (t % H) + (t / H) % 2;
+}
+
+// Direct global->LDS load of 16 bytes per lane from a wave-uniform base plus
+// a per-lane offset; lane i's bytes land at lds + 16 i (lds wave-uniform, in
+// M0). SC1: device-coherent (the load misses any cache that could hold a
+// stale copy written by another XCD).
+template <bool SC1>
+__device__ __forceinline__ void dma16(const void* sbase_in, uint32_t voff, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  // the base is wave-uniform by construction; say so, so it goes in SGPRs
+  const uint64_t a = reinterpret_cast<uint64_t>(sbase_in);
+  const void* sbase = reinterpret_cast<const void*>(
+      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)a));
+  if constexpr (SC1)
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 sc1" ::"s"(m0), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ float to_agpr(float v) {
+  float a;
+  asm("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
+  return a;
+}
+__device__ __forceinline__ float from_agpr(float a) {
+  float v;
+  asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+__device__ __forceinline__ void vm_wait0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+__device__ __forceinline__ void vm_lds_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// The sync region (int32 words, cleared by ssd_chunk_cumsum): words 0-1 the
+// 64-bit ticket counter, word 2 the error word (1: a wait hit its bound),
+// from word 64 one progress flag per (batch, head): the number of chunks
+// whose outgoing state has been published. Flags are read and written with
+// relaxed device-scope atomics (device-coherent on every XCD); ordering
+// against the state itself comes from the state's stores completing
+// (vmcnt) before the flag is raised.
+constexpr int kSyncErr = 2;
+constexpr int kSyncFlags = 64;
+constexpr int kMaxPolls = 1 << 18;      // bound of one wait (each poll sleeps, then reloads)
+
+__device__ __forceinline__ int load_flag(const int* f) {
+  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Wait (the whole wave) until *f >= want; on the bound, record the error word.
+__device__ __forceinline__ void wait_flag(const int* f, int want, int* sync) {
+  int v = load_flag(f);
+  int polls = 0;
+  while (v < want) {
+    __builtin_amdgcn_s_sleep(2);
+    if (++polls > kMaxPolls) {
+      __hip_atomic_store(sync + kSyncErr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    v = load_flag(f);
+  }
+}
+
+// The intra-chunk pairs of wave W, in emission order e = 0..11 (as the
+// resident scan: slot 0 and slots 1..3 of t-block W, then slots 1..8 of
+// t-block 7 - W).
+__host__ __device__ constexpr bool pair_kept(int e, int W) {
+  return !((e >= 4 && e < 7 && e - 3 <= W) || (e >= 1 && e < 4 && e > W));
+}
+__host__ __device__ constexpr int pair_jb(int e) { return e < 4 ? e : 8 - (e - 3); }
+__host__ __device__ constexpr bool pair_diag(int e, int W) { return pair_jb(e) == (e < 4 ? W : 7 - W); }
+__host__ __device__ constexpr int next_pair(int e, int W) {
+  for (int f = e + 1; f < 12; ++f)
+    if (pair_kept(f, W)) return f;
+  return -1;
+}
+
+template <int N>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ssd_chunk_chained(const bf16* __restrict__ x, const bf16* __restrict__ Bm, const bf16* __restrict__ Cm,
+                       const float* __restrict__ gcum, const float* __restrict__ dtt, const float* __restrict__ Dp,
+                       const float* init, bf16* __restrict__ y, float* final_state, float* chain, int* sync,
+                       int64_t Tlen, int H, int G, int64_t nc, int64_t Tp, int HB, int64_t ntickets) {
+  using Cf = CCfg<N>;
+  using I = Io<bf16>;
+  using Frag = bf16x8;
+  constexpr int P = 64, Q = 256, KS = Cf::KS, HRB = Cf::HRB, BRB = Cf::BRB, NBW = Cf::NBW;
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+  __shared__ __attribute__((aligned(1024))) unsigned char sB[Cf::BBYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char sX[Cf::XBYTES + Cf::GBYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char sH[Cf::HBYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char sY[4 * 4096];
+  __shared__ __attribute__((aligned(16))) float sW[Q];    // dt_j 2^(G'_end(block of j) - G'_j) <= dt_j
+  __shared__ __attribute__((aligned(16))) float sE[Q];    // 2^(G'_t) <= 1
+  __shared__ __attribute__((aligned(16))) float sWs[Q];   // dt_t 2^(G'_last - G'_t) <= dt_t
+  __shared__ int64_t sTicket;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  __builtin_assume(wave >= 0 && wave < 4);
+  const int lane = tid % 64;
+  const int tb0 = wave, tb1 = 7 - wave;
+  const int NHB = H / HB;
+  const uint32_t xrb = (uint32_t)H * P * 2;       // x / y row stride in bytes
+  const float* sG = reinterpret_cast<const float*>(sX + Cf::XBYTES);
+  const float* sDt = sG + Q;
+
+  // x tile direct loads: instruction kk (8 rows) puts lane l at row
+  // 8 kk + l / 8, 16-byte piece (l % 8) with the 64-byte halves swapped in
+  // rows with bit 1 set
+  const int jl = lane >> 3;
+  const uint32_t xpiece = (uint32_t)((lane & 7) ^ ((jl & 2) << 1)) * 16;
+
+  // issue the x rows, G' and dt rows of head h of (b, k) into sX
+  auto issue_x = [&](int64_t b, int64_t k, int h, int nvalid) {
+    const unsigned char* xs = reinterpret_cast<const unsigned char*>(x + ((b * Tlen + k * Q) * H + h) * P);
+    uint32_t xr = xrb, xpc = xpiece;
+    int jll = jl;
+    asm volatile("" : "+v"(jll), "+v"(xpc), "+s"(xr));
+#pragma unroll
+    for (int i = 0; i < Cf::LX; ++i) {
+      const int kk = wave + 4 * i;
+      const int row = min(kk * 8 + jll, nvalid - 1);
+      dma16<false>(xs, (uint32_t)row * xr + xpc, sX + kk * 1024);
+    }
+    if (wave < Cf::IG) {
+      const float* src = (wave == 0 ? gcum : dtt) + (b * H + h) * Tp + k * Q;
+      dma16<false>(src, (uint32_t)lane * 16, sX + Cf::XBYTES + wave * 1024);
+    }
+  };
+
+  // issue the B rows of (b, k, group) into sB (swizzled pieces)
+  auto issue_B = [&](const bf16* bt, int nvalid) {
+    int ll = lane;
+    asm volatile("" : "+v"(ll));
+#pragma unroll
+    for (int i = 0; i < Cf::LB; ++i) {
+      const int kk = wave + 4 * i;
+      const uint32_t o = (uint32_t)kk * 1024 + (uint32_t)ll * 16;
+      const uint32_t t = o / BRB, cs = (o % BRB) / 16;
+      const uint32_t c = cs ^ bswz<N>(t);
+      const uint32_t row = min((int)t, nvalid - 1);
+      dma16<false>(bt, row * (uint32_t)(G * N * 2) + c * 16, sB + kk * 1024);
+    }
+  };
+
+  // h_k into sH (fp32 rows of N values at stride HRB) from a [P][N] fp32 array
+  auto issue_h = [&](const float* src, bool coherent) {
+    int ll = lane;
+    asm volatile("" : "+v"(ll));
+#pragma unroll
+    for (int i = 0; i < Cf::LH; ++i) {
+      const int kk = wave + 4 * i;
+      if (kk < Cf::IH) {
+        const uint32_t o = (uint32_t)kk * 1024 + (uint32_t)ll * 16;
+        uint32_t r = o / HRB, c = (o % HRB) / 16;
+        if (c >= (uint32_t)(N / 4)) c = 0;            // the pad piece: any valid bytes
+        if (coherent) dma16<true>(src, r * (N * 4) + c * 16, sH + kk * 1024);
+        else dma16<false>(src, r * (N * 4) + c * 16, sH + kk * 1024);
+      }
+    }
+  };
+
+  float cbc[9][16];   // resident C.B^T blocks of the ticket's (b, k, group), in AGPRs
+  Frag cf[2][KS];     // C fragments of the wave's t-blocks, in AGPRs
+
+  for (;;) {
+    if (tid == 0) sTicket = __hip_atomic_fetch_add(reinterpret_cast<long long*>(sync), 1LL, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+    lds_barrier();
+    // wave-uniform: the addresses derived from it are scalar operands
+    const int64_t tv = sTicket;
+    const int64_t ticket = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(tv >> 32)) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readfirstlane((int)tv));
+    if (ticket >= ntickets) break;
+    const int64_t per = ntickets / nc;                          // tickets per chunk = batch * NHB
+    const int64_t k = ticket / per;
+    const int64_t u = ticket % per;
+    const int64_t b = u / NHB;
+    const int hb = (int)(u % NHB);
+    const int h0 = hb * HB;
+    const int grp = h0 / (H / G);
+    const int64_t t0 = k * Q;
+    const int nvalid = (int)(Tlen - t0 < Q ? Tlen - t0 : Q);
+    const bf16* bt = Bm + ((b * Tlen + t0) * G + grp) * N;
+    const bf16* ct = Cm + ((b * Tlen + t0) * G + grp) * N;
+
+    // ---- ticket set-up: B tile, the first head's x, C fragments, C.B^T
+    issue_B(bt, nvalid);
+    issue_x(b, k, h0, nvalid);
+    {
+      int lt = lane;
+      asm volatile("" : "+v"(lt));
+      const int m = lt & 31, g = lt >> 5;
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const int tr = (uu ? tb1 : tb0) * 32 + m;
+        const bool valid = tr < nvalid;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          u32x4 c4 = __builtin_bit_cast(u32x4, I::load_row(ct + (int64_t)tr * G * N + s * 16 + 8 * g, valid));
+          asm("" : "=a"(c4) : "0"(c4));
+          cf[uu][s] = __builtin_bit_cast(Frag, c4);
+        }
+      }
+    }
+    vm_lds_barrier();
+    {
+      int lt = lane;
+      asm volatile("" : "+v"(lt));
+      const int m = lt & 31, g = lt >> 5;
+      const uint32_t sw = bswz<N>((uint32_t)m);   // the row swizzle of rows 32 jb + m
+#pragma unroll
+      for (int e = 0; e < 12; ++e) {
+        const int sl = e < 4 ? e : e - 3;
+        const int uu = e < 4 ? 0 : 1;
+        if (e >= 4 && e < 7 && sl <= wave) continue;
+        if (e >= 1 && e < 4 && sl > wave) continue;
+        const int jb = uu ? 8 - sl : sl;
+        const unsigned char* brow = sB + (jb * 32 + m) * BRB;
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+          I::mma(acc, *reinterpret_cast<const Frag*>(brow + (((uint32_t)(2 * s + g)) ^ sw) * 16), cf[uu][s]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cbc[sl][r] = to_agpr(acc[r]);
+      }
+    }
+
+    for (int j = 0; j < HB; ++j) {
+      const int h = h0 + j;
+      const int64_t bh = b * H + h;
+      int lt = lane;
+      asm volatile("" : "+v"(lt));
+      const int m = lt & 31, g = lt >> 5;
+      // x of this head has landed (issued at ticket start or during the previous head)
+      vm_lds_barrier();
+      {
+        const float gi = sG[tid];
+        sW[tid] = sDt[tid] * exp2_hw(sG[tid | 31] - gi);
+        sWs[tid] = sDt[tid] * exp2_hw(sG[Q - 1] - gi);
+        sE[tid] = exp2_hw(gi);
+      }
+      const float gt0 = sG[tb0 * 32 + m], gt1 = sG[tb1 * 32 + m];
+      const float glast = sG[Q - 1];
+      const float Dh = Dp[h];
+      lds_barrier();
+
+      // transposing x reads: lane s supplies row 4 (s / 32) + (s % 16) / 4 of
+      // a 16-row step, headdim columns 16 ((s / 16) % 2) + 4 (s % 4) + 32 pe
+      // (the 64-byte half flipped in rows with bit 1 set); xtr ^ 64 is pe = 1
+      const uint32_t xtr = (uint32_t)(4 * g + ((lt & 15) >> 2)) * 128 +
+                           (((uint32_t)(32 * ((lt >> 4) & 1) + 8 * (lt & 3))) ^ (uint32_t)(64 * ((lt & 15) >> 3)));
+      // x^T fragment of headdim block pe over tokens 16 s + drow(e, g)
+      auto load_xs = [&](int pe, int s) -> Frag {
+        uint64_t h2[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const unsigned char* a = sX + (pe ? (xtr ^ 64u) : xtr) + (16 * s + 8 * hh) * 128;
+          h2[hh] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                    (__attribute__((address_space(3))) s16x4*)(a)));
+        }
+        const u32x4 w4 = {(uint32_t)h2[0], (uint32_t)(h2[0] >> 32), (uint32_t)h2[1], (uint32_t)(h2[1] >> 32)};
+        return __builtin_bit_cast(Frag, w4);
+      };
+
+      // ---- phase A: S_k^T[n][p] = sum_t B[t][n] (w_t x[t][p]); rows n of
+      // dstate blocks NBW (w >> 1) + i, columns p of headdim block w & 1
+      const int pe_a = wave & 1, nb0 = NBW * (wave >> 1);
+      f32x16 sacc[NBW];
+#pragma unroll
+      for (int i = 0; i < NBW; ++i) sacc[i] = f32x16{};
+      {
+        // B^T fragment reads: lane supplies row 16 s + 8 hh + 4 g + (l % 16) / 4,
+        // the 8 bytes of dstate columns 32 nb + 16 ((l / 16) % 2) + 4 (l % 4) ..
+        const uint32_t a_ = (uint32_t)((lt & 15) >> 2);
+        const uint32_t piece0 = (uint32_t)(2 * ((lt >> 4) & 1) + ((lt & 3) >> 1));
+        const uint32_t half = (uint32_t)(lt & 1) * 8;
+        auto load_bt = [&](int nb, int s) -> Frag {
+          uint64_t h2[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const uint32_t t = (uint32_t)(16 * s + 8 * hh + 4 * g) + a_;
+            const uint32_t c = (uint32_t)(4 * nb) + piece0;
+            const unsigned char* adr = sB + t * BRB + ((c ^ bswz<N>(t)) * 16) + half;
+            h2[hh] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                      (__attribute__((address_space(3))) s16x4*)(adr)));
+          }
+          const u32x4 w4 = {(uint32_t)h2[0], (uint32_t)(h2[0] >> 32), (uint32_t)h2[1], (uint32_t)(h2[1] >> 32)};
+          return __builtin_bit_cast(Frag, w4);
+        };
+#pragma unroll 4
+        for (int s = 0; s < 16; ++s) {
+          const Frag xf = load_xs(pe_a, s);
+          Frag bfr[NBW];
+#pragma unroll
+          for (int i = 0; i < NBW; ++i) bfr[i] = load_bt(nb0 + i, s);
+          const float4 w0 = *reinterpret_cast<const float4*>(&sWs[16 * s + 4 * g]);
+          const float4 w1 = *reinterpret_cast<const float4*>(&sWs[16 * s + 8 + 4 * g]);
+          const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+          const u32x4 xd = __builtin_bit_cast(u32x4, xf);
+          float v[8];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[2 * i] = wv[2 * i] * bf16lo(xd[i]);
+            v[2 * i + 1] = wv[2 * i + 1] * bf16hi(xd[i]);
+          }
+          Frag hi, lo;
+          I::split(v, hi, lo);
+#pragma unroll
+          for (int i = 0; i < NBW; ++i) {
+            I::mma(sacc[i], bfr[i], hi);
+            I::mma(sacc[i], bfr[i], lo);
+          }
+        }
+      }
+
+      // ---- chain: h_k into sH, h_{k+1} out, h_k rewritten as (hi, lo) pairs
+      if (k == 0) {
+        if (init) {
+          issue_h(init + bh * (int64_t)(P * N), false);
+        } else {
+          for (int o = tid * 16; o < Cf::HBYTES; o += 256 * 16) *reinterpret_cast<u32x4*>(sH + o) = u32x4{0u, 0u, 0u, 0u};
+        }
+      } else {
+        wait_flag(sync + kSyncFlags + bh, (int)k, sync);
+        issue_h(chain + bh * (int64_t)(P * N), true);
+      }
+      vm_lds_barrier();
+      {
+        const float alpha = exp2_hw(glast);
+        const int p = 32 * pe_a + m;
+        const bool last = k + 1 == nc;
+        float* dst = last ? final_state : chain;
+        float4 hk[NBW][4];
+#pragma unroll
+        for (int i = 0; i < NBW; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            hk[i][q] = *reinterpret_cast<const float4*>(sH + p * HRB + 4 * (32 * (nb0 + i) + 8 * q + 4 * g));
+        if (dst) {
+          const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst + bh * (int64_t)(P * N), (uint32_t)(P * N * 4));
+#pragma unroll
+          for (int i = 0; i < NBW; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 a = hk[i][q];
+              const u32x4 v = {__float_as_uint(fmaf(alpha, a.x, sacc[i][4 * q])),
+                               __float_as_uint(fmaf(alpha, a.y, sacc[i][4 * q + 1])),
+                               __float_as_uint(fmaf(alpha, a.z, sacc[i][4 * q + 2])),
+                               __float_as_uint(fmaf(alpha, a.w, sacc[i][4 * q + 3]))};
+              const uint32_t off = (uint32_t)(p * N + 32 * (nb0 + i) + 8 * q + 4 * g) * 4;
+              if (last) __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
+              else __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 16);   // sc1
+            }
+        }
+        // h_k as (hi, lo) bf16 pairs, in place: group n / 8 of row p holds 8
+        // hi values then 8 lo values (the same 32 bytes its fp32 values took)
+#pragma unroll
+        for (int i = 0; i < NBW; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 a = hk[i][q];
+            const uint32_t h01 = pack_bf16x2(a.x, a.y), h23 = pack_bf16x2(a.z, a.w);
+            const uint32_t l01 = pack_bf16x2(a.x - bf16lo(h01), a.y - bf16hi(h01));
+            const uint32_t l23 = pack_bf16x2(a.z - bf16lo(h23), a.w - bf16hi(h23));
+            unsigned char* grp8 = sH + p * HRB + (4 * (nb0 + i) + q) * 32 + 8 * g;
+            *reinterpret_cast<uint2*>(grp8) = make_uint2(h01, h23);
+            *reinterpret_cast<uint2*>(grp8 + 16) = make_uint2(l01, l23);
+          }
+      }
+      lds_barrier();
+
+      // ---- carried state: acc[u][pe] = h_k . C^T (rows p, columns t), then
+      // columns scaled by 2^(G'_t)
+      f32x16 acc[2][2];
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+        for (int pe = 0; pe < 2; ++pe) acc[uu][pe] = f32x16{};
+      {
+        constexpr int HBK = KS / 4;
+        Frag hf[2][2][4];
+        auto load_h = [&](int blk, Frag (*dst)[4]) {
+          const int pe = blk / HBK, s0 = (blk % HBK) * 4;
+          const unsigned char* hp = sH + (pe * 32 + m) * HRB;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dst[0][i] = *reinterpret_cast<const Frag*>(hp + (2 * (s0 + i) + g) * 32);
+            dst[1][i] = *reinterpret_cast<const Frag*>(hp + (2 * (s0 + i) + g) * 32 + 16);
+          }
+        };
+        load_h(0, hf[0]);
+#pragma unroll
+        for (int blk = 0; blk < 2 * HBK; ++blk) {
+          if (blk + 1 < 2 * HBK) load_h(blk + 1, hf[(blk + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          const int pe = blk / HBK, s0 = (blk % HBK) * 4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu) {
+              I::mma(acc[uu][pe], hf[blk & 1][0][i], cf[uu][s0 + i]);
+              I::mma(acc[uu][pe], hf[blk & 1][1][i], cf[uu][s0 + i]);
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+#pragma unroll
+      for (int uu = 0; uu < 2; ++uu) {
+        const float sc = sE[(uu ? tb1 : tb0) * 32 + m];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          acc[uu][0][r] *= sc;
+          acc[uu][1][r] *= sc;
+        }
+      }
+      // h_{k+1} is stored (every wave waited for its stores): raise the flag
+      vm_lds_barrier();
+      if (tid == 0) __hip_atomic_store(sync + kSyncFlags + bh, (int)(k + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+      // ---- intra-chunk pairs, slot by slot, specialised per wave
+      auto pairs = [&](auto wtag) {
+        constexpr int W = decltype(wtag)::value;
+        auto load_x = [&](int jb, Frag (*d)[2]) {
+#pragma unroll
+          for (int pe = 0; pe < 2; ++pe)
+#pragma unroll
+            for (int js = 0; js < 2; ++js) d[pe][js] = load_xs(pe, 2 * jb + js);
+        };
+        auto load_w = [&](int jb, float4* wv, float& ge) {
+#pragma unroll
+          for (int c4 = 0; c4 < 4; ++c4) wv[c4] = *reinterpret_cast<const float4*>(&sW[jb * 32 + 8 * c4 + 4 * g]);
+          ge = sG[jb * 32 + 31];
+        };
+        Frag d[2][2];
+        float4 wv[4];
+        float ge = 0.f;
+        load_x(0, d);
+        if (!pair_diag(0, W)) load_w(0, wv, ge);
+#pragma unroll
+        for (int e = 0; e < 12; ++e) {
+          const int sl = e < 4 ? e : e - 3;
+          const int uu = e < 4 ? 0 : 1;
+          if (!pair_kept(e, W)) continue;
+          const int jb = uu ? 8 - sl : sl;
+          const int tbk = uu ? 7 - W : W;
+          const bool diag = jb == tbk;
+          const float gtu = uu ? gt1 : gt0;
+          const int j0 = jb * 32;
+          Frag dn[2][2];
+          float4 wvn[4];
+          float gen = 0.f;
+          const int en = next_pair(e, W);
+          if (en >= 0) load_x(pair_jb(en), dn);
+          if (en >= 0 && !pair_diag(en, W)) load_w(pair_jb(en), wvn, gen);
+          float v[16];
+          if (!diag) {
+            const float a = exp2_hw(gtu - ge);
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+              v[4 * c4 + 0] = from_agpr(cbc[sl][4 * c4 + 0]) * (wv[c4].x * a);
+              v[4 * c4 + 1] = from_agpr(cbc[sl][4 * c4 + 1]) * (wv[c4].y * a);
+              v[4 * c4 + 2] = from_agpr(cbc[sl][4 * c4 + 2]) * (wv[c4].z * a);
+              v[4 * c4 + 3] = from_agpr(cbc[sl][4 * c4 + 3]) * (wv[c4].w * a);
+            }
+          } else {
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) {
+              const float4 g4 = *reinterpret_cast<const float4*>(&sG[j0 + 8 * c4 + 4 * g]);
+              const float4 d4 = *reinterpret_cast<const float4*>(&sDt[j0 + 8 * c4 + 4 * g]);
+              const float gq[4] = {g4.x, g4.y, g4.z, g4.w}, dq[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int q = 4 * c4 + i, jr = drow(q, g);
+                const float val = from_agpr(cbc[sl][q]) * exp2_hw(gtu - gq[i]) * dq[i];
+                v[q] = (m > jr) ? val : ((m == jr) ? val + Dh : 0.f);
+              }
+            }
+          }
+#pragma unroll
+          for (int js = 0; js < 2; ++js) {
+            u32x4 uh, ul;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              uint32_t hh = pack_bf16x2(v[js * 8 + 2 * i], v[js * 8 + 2 * i + 1]);
+              asm volatile("" : "+v"(hh));
+              uh[i] = hh;
+              ul[i] = pack_bf16x2(v[js * 8 + 2 * i] - __uint_as_float(hh << 16),
+                                  v[js * 8 + 2 * i + 1] - __uint_as_float(hh & 0xffff0000u));
+            }
+            const Frag ahi = __builtin_bit_cast(Frag, uh), alo = __builtin_bit_cast(Frag, ul);
+#pragma unroll
+            for (int pe = 0; pe < 2; ++pe) {
+              I::mma(acc[uu][pe], d[pe][js], ahi);
+              I::mma(acc[uu][pe], d[pe][js], alo);
+            }
+          }
+#pragma unroll
+          for (int pe = 0; pe < 2; ++pe)
+#pragma unroll
+            for (int js = 0; js < 2; ++js) d[pe][js] = dn[pe][js];
+          if (en >= 0 && !pair_diag(en, W)) {
+#pragma unroll
+            for (int c4 = 0; c4 < 4; ++c4) wv[c4] = wvn[c4];
+            ge = gen;
+          }
+        }
+      };
+      switch (wave) {
+        case 0: pairs(std::integral_constant<int, 0>{}); break;
+        case 1: pairs(std::integral_constant<int, 1>{}); break;
+        case 2: pairs(std::integral_constant<int, 2>{}); break;
+        default: pairs(std::integral_constant<int, 3>{}); break;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // every wave is done with x and h_k: the next head's x may load
+      lds_barrier();
+      if (j + 1 < HB) issue_x(b, k, h + 1, nvalid);
+
+      // ---- y through LDS in 16-byte row pieces (as the resident scan)
+      {
+        unsigned char* ys_lds = sY + wave * 4096;
+        const uint32_t wrow = (uint32_t)m * 128 + 8 * (uint32_t)g, wsw = (uint32_t)(m >> 1) & 7;
+        const int pr = lane / 8, pc = lane % 8;
+        uint32_t plane = (uint32_t)pr * xrb + (uint32_t)pc * 16;
+        uint32_t xrbs = xrb;
+        asm volatile("" : "+v"(plane), "+s"(xrbs));
+        unsigned char* yt = reinterpret_cast<unsigned char*>(y + ((b * Tlen + t0) * H + h) * P);
+        const __amdgpu_buffer_rsrc_t yr = make_rsrc(yt, (uint32_t)nvalid * xrbs);
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+#pragma unroll
+          for (int pe = 0; pe < 2; ++pe)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const uint2 v2 = make_uint2(pack_bf16x2(acc[uu][pe][4 * c], acc[uu][pe][4 * c + 1]),
+                                          pack_bf16x2(acc[uu][pe][4 * c + 2], acc[uu][pe][4 * c + 3]));
+              *reinterpret_cast<uint2*>(ys_lds + wrow + (((uint32_t)(4 * pe + c)) ^ wsw) * 16) = v2;
+            }
+          const uint32_t row0 = (uint32_t)((uu ? tb1 : tb0) * 32);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t rsw = (uint32_t)(4 * (i & 1) + (pr >> 1));
+            const u32x4 v = *reinterpret_cast<const u32x4*>(ys_lds + (8 * i + pr) * 128 + ((uint32_t)pc ^ rsw) * 16);
+            __builtin_amdgcn_raw_buffer_store_b128(v, yr, plane + (row0 + 8 * i) * xrbs, 0, 0);
+          }
+        }
+      }
+    }
+  }
+}
+
+int chained_heads_per_ticket(const Problem& p, int cus) {
+  const int64_t hpg = p.H / p.G;
+  for (int hb : {4, 2, 1})
+    if (hpg % hb == 0 && (hb == 1 || p.bt * p.nc * (p.H / hb) >= 3 * (int64_t)cus)) return hb;
+  return 1;
+}
+
+template <int N>
+int chained_grid() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    dev = 0;
+  }
+  if (!cached[dev]) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ssd_chunk_chained<N>, 256, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0) {
+      (void)hipGetLastError();
+      cus = 256;
+      per_cu = 1;
+    }
+    cached[dev] = cus * per_cu;
+  }
+  return cached[dev];
+}
+
+template <int N>
+hipError_t launch_chained(const Problem& p, hipStream_t stream) {
+  const int slots = chained_grid<N>();
+  const int HB = chained_heads_per_ticket(p, slots);
+  const int64_t ntickets = p.bt * p.nc * (p.H / HB);
+  const int64_t grid = ntickets < slots ? ntickets : slots;
+  hipLaunchKernelGGL((ssd_chunk_chained<N>), dim3((unsigned)grid), dim3(256), 0, stream, (const bf16*)p.x,
+                     (const bf16*)p.B, (const bf16*)p.C, p.gcum, p.dtt, p.D, p.init, (bf16*)p.y, p.final_state,
+                     p.chain, p.sync, p.T, (int)p.H, (int)p.G, p.nc, p.Tp, HB, ntickets);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool chunk_chained_fits(const Problem& p) {
+  return p.io == 1 && p.P == 64 && p.Q == 256 && (p.N == 64 || p.N == 128) && p.nc > 0;
+}
+
+hipError_t launch_chunk_chained(const Problem& p, hipStream_t stream) {
+  if (p.bt == 0 || p.nc == 0) return hipSuccess;
+  return p.N == 64 ? launch_chained<64>(p, stream) : launch_chained<128>(p, stream);
+}
 
 }  // namespace ssd

@@ -37,7 +37,8 @@ __global__ __launch_bounds__(256) void ssd_chunk_cumsum(const float* __restrict_
                                                         float* __restrict__ gcum,
                                                         float* __restrict__ dtt,
                                                         float* __restrict__ wst,
-                                                        int64_t T, int H, int64_t Tp, int dt_hm) {
+                                                        int64_t T, int H, int64_t Tp, int dt_hm,
+                                                        int* __restrict__ sync, int nsync) {
   constexpr int SL = Q / kSeg;
   __shared__ float s_t[Q][kHB + 1];   // dt tile, then the scaled cumsum in place
   __shared__ float s_w[Q][kHB + 1];   // state weights
@@ -49,6 +50,12 @@ __global__ __launch_bounds__(256) void ssd_chunk_cumsum(const float* __restrict_
   const int64_t b = blockIdx.z;
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)k * Q;
+  // the chained path's counters start at zero (its kernel runs next on the stream)
+  if (sync) {
+    const int64_t gid = ((int64_t)(blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * 256 + tid;
+    const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * gridDim.z * 256;
+    for (int64_t i = gid; i < nsync; i += nthreads) sync[i] = 0;
+  }
   const int nh = H - h0 < kHB ? H - h0 : kHB;          // heads of this block
   const int nt = T - t0 < Q ? (int)(T - t0) : Q;       // tokens of this chunk
   if (dt_hm) {
@@ -137,7 +144,8 @@ __global__ __launch_bounds__(256) void ssd_chunk_cumsum(const float* __restrict_
     if (hl < nh) {
       const int64_t o = (b * H + h0 + hl) * Tp + t0 + t;
       *reinterpret_cast<float4*>(gcum + o) = make_float4(s_t[t][hl], s_t[t + 1][hl], s_t[t + 2][hl], s_t[t + 3][hl]);
-      *reinterpret_cast<float4*>(wst + o) = make_float4(s_w[t][hl], s_w[t + 1][hl], s_w[t + 2][hl], s_w[t + 3][hl]);
+      if (wst)
+        *reinterpret_cast<float4*>(wst + o) = make_float4(s_w[t][hl], s_w[t + 1][hl], s_w[t + 2][hl], s_w[t + 3][hl]);
     }
   }
 }
@@ -150,13 +158,13 @@ hipError_t launch_chunk_cumsum(const Problem& p, hipStream_t stream) {
   const dim3 block(256);
   switch (p.Q) {
     case 64:
-      hipLaunchKernelGGL(ssd_chunk_cumsum<64>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp, p.dt_head_major);
+      hipLaunchKernelGGL(ssd_chunk_cumsum<64>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp, p.dt_head_major, p.sync, p.nsync);
       break;
     case 128:
-      hipLaunchKernelGGL(ssd_chunk_cumsum<128>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp, p.dt_head_major);
+      hipLaunchKernelGGL(ssd_chunk_cumsum<128>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp, p.dt_head_major, p.sync, p.nsync);
       break;
     case 256:
-      hipLaunchKernelGGL(ssd_chunk_cumsum<256>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp, p.dt_head_major);
+      hipLaunchKernelGGL(ssd_chunk_cumsum<256>, grid, block, 0, stream, p.dt, p.A, p.gcum, p.dtt, p.wst, p.T, (int)p.H, p.Tp, p.dt_head_major, p.sync, p.nsync);
       break;
     default:
       return hipErrorInvalidValue;

@@ -53,6 +53,7 @@ struct Sizes {
 // supports the shape; otherwise the chunk states inside the state pass when
 // the (batch, head, dstate group) walks alone fill the GPU
 // (chunk_state_pass_pays); otherwise the four kernels.
+constexpr bool kAutoChained = false;
 int choose_path(const ssd::Problem& p, int io_arg) {
   switch (path_field(io_arg)) {
     case MAMBA2_SSD_PATH_FOUR: return MAMBA2_SSD_PATH_FOUR;
@@ -60,7 +61,7 @@ int choose_path(const ssd::Problem& p, int io_arg) {
     case MAMBA2_SSD_PATH_CHAINED: return ssd::chunk_chained_fits(p) ? MAMBA2_SSD_PATH_CHAINED : 0;
     default: break;
   }
-  if (ssd::chunk_chained_fits(p)) return MAMBA2_SSD_PATH_CHAINED;
+  if (kAutoChained && ssd::chunk_chained_fits(p)) return MAMBA2_SSD_PATH_CHAINED;
   if (ssd::chunk_state_pass_fits(p) && ssd::chunk_state_pass_pays(p)) return MAMBA2_SSD_PATH_THREE;
   return MAMBA2_SSD_PATH_FOUR;
 }
@@ -124,7 +125,7 @@ void layout_of(const mamba2_ssd_dims* d, const Sizes& s, mamba2_ssd_workspace_la
   L->dtt_offset = off;
   off = align_up(off + bh * (size_t)s.Tp * 4);
   L->wst_offset = off;
-  off = align_up(off + bh * (size_t)s.Tp * 4);
+  if (!chained) off = align_up(off + bh * (size_t)s.Tp * 4);   // the chained kernel forms w itself
   L->states_offset = off;
   if (four) off = align_up(off + (size_t)s.n_chunkstates * 4);
   L->hprev_offset = off;
@@ -252,8 +253,11 @@ int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* d, int io, const void* x, const 
   p.wst = reinterpret_cast<float*>(ws + L.wst_offset);
   p.states = reinterpret_cast<float*>(ws + L.states_offset);
   p.hprev = ws + L.hprev_offset;
-  p.chain = reinterpret_cast<float*>(ws + L.chain_offset);
-  p.sync = reinterpret_cast<int*>(ws + L.sync_offset);
+  const bool chained = s.path == MAMBA2_SSD_PATH_CHAINED;
+  if (chained) p.wst = nullptr;
+  p.chain = chained ? reinterpret_cast<float*>(ws + L.chain_offset) : nullptr;
+  p.sync = chained ? reinterpret_cast<int*>(ws + L.sync_offset) : nullptr;
+  p.nsync = chained ? (int)(d->batch * d->nheads + 64) : 0;
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
   hipError_t err = hipSuccess;

@@ -27,7 +27,8 @@ struct Problem {
   float* states;                 // workspace: [bt][H][nc][P][N]
   void* hprev;                   // workspace: [bt][H][nc][P][N] fp32, or bf16 (hi, lo) pairs
   float* chain;                  // workspace (chained path): [bt][H][P][N] carried state slots
-  int* sync;                     // workspace (chained path): ticket counter, then one flag per (bt, H)
+  int* sync;                     // workspace (chained path): ticket counter, error word, flags per (bt, H)
+  int nsync;                     // int32 words of sync (0 = none); ssd_chunk_cumsum clears them
 };
 
 // One decode step (see ssd_step.hip). Device pointers, validated by the ABI.

@@ -83,11 +83,12 @@ def test_workspace_layout_headline():
     assert auto.path == ssd.fwd_path(HEADLINE, BF16)
     assert ssd.workspace_bytes(HEADLINE, BF16) == auto.total_bytes
     assert ssd.workspace_bytes(HEADLINE, F32) == four.total_bytes   # fp32 io: four kernels
-    if ssd.fwd_path(HEADLINE, BF16) == ssd.PATH_CHAINED:
-        ch = ssd.workspace_layout(HEADLINE, BF16 | ssd.PATH_CHAINED)
-        assert ch.states_offset == ch.hprev_offset == ch.chain_offset == 3 * gq
-        assert ch.sync_offset == ch.chain_offset + 4 * 80 * 64 * 128 * 4
-        assert ch.total_bytes == ch.sync_offset + ((4 * 80 + 64) * 4 + 255) // 256 * 256
+    ch = ssd.workspace_layout(HEADLINE, BF16 | ssd.PATH_CHAINED)
+    assert ch.path == ssd.PATH_CHAINED
+    assert ch.wst_offset == ch.states_offset == ch.hprev_offset == ch.chain_offset == 2 * gq   # no w, S, hprev
+    assert ch.sync_offset == ch.chain_offset + 4 * 80 * 64 * 128 * 4
+    assert ch.total_bytes == ch.sync_offset + ((4 * 80 + 64) * 4 + 255) // 256 * 256
+    assert ch.total_bytes <= ssd.NOALLOC_MAX_WORKSPACE     # the headline fits the no-allocation entry point
 
 
 def test_path_field():
@@ -104,8 +105,11 @@ def test_path_field():
         with pytest.raises(ssd.SsdError):
             ssd.fwd_path(d, io)
         assert ssd.workspace_bytes(d, io) == 0
-    if not ssd.fwd_path(HEADLINE, BF16) == ssd.PATH_CHAINED:
-        assert _check(HEADLINE, BF16 | ssd.PATH_CHAINED) == UNSUP
+    assert ssd.fwd_path(HEADLINE, BF16 | ssd.PATH_CHAINED) == ssd.PATH_CHAINED
+    assert ssd.fwd_path(Dims(1, 65536, 80, 64, 64, 1, 256), BF16 | ssd.PATH_CHAINED) == ssd.PATH_CHAINED
+    for d, io in ((HEADLINE, F32), (Dims(4, 8192, 80, 128, 128, 1, 256), BF16),
+                  (Dims(4, 8192, 80, 64, 256, 1, 256), BF16), (Dims(4, 8192, 80, 64, 128, 1, 128), BF16)):
+        assert _check(d, io | ssd.PATH_CHAINED) == UNSUP    # fp32; headdim 128; dstate 256; chunk 128
     assert ssd.fwd_path(Dims(8, 2048, 24, 64, 128, 1, 256), BF16 | ssd.PATH_FOUR) == ssd.PATH_FOUR
 
 

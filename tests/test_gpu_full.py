@@ -12,11 +12,16 @@ import numpy as np
 import pytest
 import torch
 
+import state_space_sequence_ssd_amd as ssd
 from oracle import ssd_chunked
 from tests.gpu_helpers import check_close, host, log, run, to_device
 from workloads import CONFIGS, generate
 
 pytestmark = pytest.mark.gpu
+
+
+def _dims(cfg):
+    return ssd.Dims(cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim, cfg.dstate, cfg.ngroups, cfg.chunk)
 
 
 @functools.lru_cache(maxsize=1)
@@ -25,13 +30,17 @@ def _inputs(name):
     return cfg, generate(cfg)
 
 
-@pytest.mark.parametrize("cfg", CONFIGS, ids=[c.name for c in CONFIGS])
-def test_full_config_every_head(cfg):
+CHAINED_OK = [c for c in CONFIGS if c.io == "bf16" and c.headdim == 64 and c.chunk == 256 and c.dstate <= 128]
+
+
+@pytest.mark.parametrize("cfg,path", [(c, 0) for c in CONFIGS] + [(c, ssd.PATH_CHAINED) for c in CHAINED_OK],
+                         ids=[c.name for c in CONFIGS] + [c.name + "-chained" for c in CHAINED_OK])
+def test_full_config_every_head(cfg, path):
     log(f"[full] {cfg.name}: generating inputs")
     cfg, inp = _inputs(cfg.name)
     dev = to_device(inp, cfg.io)
-    log(f"[full] {cfg.name}: GPU call")
-    y, fin = run(dev, cfg.chunk)
+    log(f"[full] {cfg.name}: GPU call (path {ssd.fwd_path(_dims(cfg), (1 if cfg.io == 'bf16' else 0) | path):#x})")
+    y, fin = run(dev, cfg.chunk, path=path)
     yg, fg = host(y), host(fin)
     del y, dev
     torch.cuda.empty_cache()

@@ -333,6 +333,74 @@ def test_fused_state_pass_in_place_and_no_final():
     check_close(host(y2), yr, cfg.io, "y (fused, no final)")
 
 
+# --------------------------------- states, pass and outputs in one kernel
+# (bf16, headdim 64, chunk 256, dstate 64/128: the CHAINED sequence). Each
+# case is checked against the oracle and against the FOUR sequence, and the
+# workspace's error word (set when a wait for the previous chunk's state hits
+# its bound) must stay 0.
+CHAINED = {
+    "ragged-init": dict(batch=2, seqlen=3 * 256 + 13, nheads=5, init_sigma=0.3),
+    "one-chunk": dict(batch=3, seqlen=100, nheads=2),
+    "N64-groups": dict(batch=1, seqlen=5 * 256 + 1, nheads=8, dstate=64, ngroups=2, init_sigma=0.2),
+    "exact-chunks": dict(batch=2, seqlen=4 * 256, nheads=6),
+    "long-walk": dict(batch=1, seqlen=40 * 256 + 77, nheads=3, init_sigma=0.1),
+    "many-heads": dict(batch=2, seqlen=6 * 256, nheads=48, init_sigma=0.1),
+}
+
+
+def _sync_error_word(ws, L):
+    return int(ws[L.sync_offset + 8:L.sync_offset + 12].view(torch.int32).item())
+
+
+@pytest.mark.parametrize("name", sorted(CHAINED))
+def test_chained_sequence(name):
+    cfg = LayerConfig(f"chained-{name}", **{**dict(headdim=64, dstate=128, ngroups=1, chunk=256, io="bf16",
+                                                 seed=900 + len(name)), **CHAINED[name]})
+    log(f"[chained] {name}: {cfg}")
+    inp = generate(cfg)
+    yr, fr = oracle_all(inp, cfg)
+    dev = to_device(inp, cfg.io)
+    y, fin, ws, L, dims = run(dev, cfg.chunk, keep_workspace=True, path=ssd.PATH_CHAINED)
+    assert L.path == ssd.PATH_CHAINED
+    assert L.states_offset == L.hprev_offset == L.chain_offset == L.wst_offset
+    assert _sync_error_word(ws, L) == 0, "a wait for the previous chunk's state hit its bound"
+    log("  " + check_close(host(y), yr, cfg.io, "y (chained)"))
+    log("  " + check_close(host(fin), fr, cfg.io, "final_state (chained)"))
+    y4, f4 = run(dev, cfg.chunk, path=ssd.PATH_FOUR)
+    rel = float(torch.max(torch.abs(fin - f4))) / max(float(torch.max(torch.abs(f4))), 1e-30)
+    assert rel <= 1e-5, f"final_state: CHAINED and FOUR differ by {rel:.2e} (normwise)"
+    # the sequences sum in different orders (fp32), then round to bf16: at most
+    # one bf16 ulp apart, plus an absolute floor for values near zero
+    yy, y4h = host(y), host(y4)
+    diff = np.abs(yy - y4h)
+    bound = 2.0 ** -7 * np.abs(y4h) + 1e-5 * float(np.max(np.abs(y4h)))
+    i = np.unravel_index(int(np.argmax(diff / bound)), diff.shape)
+    assert np.all(diff <= bound), (f"y: CHAINED and FOUR differ beyond one bf16 ulp: worst at {i}: "
+                                   f"{yy[i]:.6g} vs {y4h[i]:.6g} (max|y| {float(np.max(np.abs(y4h))):.3g})")
+    y2, f2 = run(dev, cfg.chunk, path=ssd.PATH_CHAINED)
+    assert torch.equal(y, y2) and torch.equal(fin, f2), "two identical calls must give identical results"
+
+
+def test_chained_in_place_and_no_final():
+    cfg = LayerConfig("chained-inplace", batch=2, seqlen=2 * 256 + 40, nheads=3, headdim=64, dstate=128,
+                      ngroups=1, chunk=256, io="bf16", seed=931, init_sigma=0.3)
+    inp = generate(cfg)
+    yr, fr = oracle_all(inp, cfg)
+    dev = to_device(inp, cfg.io)
+    st = dev["init_state"].clone()
+    y, fin = ssd.ssd_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], cfg.chunk, st,
+                         final_state=st, path=ssd.PATH_CHAINED)
+    torch.cuda.synchronize()
+    assert fin.data_ptr() == st.data_ptr()
+    check_close(host(st), fr, cfg.io, "final_state in place (chained)")
+    check_close(host(y), yr, cfg.io, "y (chained, in place)")
+    y2, none = ssd.ssd_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], cfg.chunk,
+                           dev["init_state"], return_final_state=False, path=ssd.PATH_CHAINED)
+    torch.cuda.synchronize()
+    assert none is None
+    check_close(host(y2), yr, cfg.io, "y (chained, no final)")
+
+
 # ------------------------------------------------------------ dt layouts
 
 DT_LAYOUT = {
