@@ -109,6 +109,30 @@ __device__ __forceinline__ void dma16(const void* sbase_in, uint32_t voff, const
                  : "memory", "m0");
 }
 
+// The same through a buffer resource: lane i's 16 bytes at byte voff + soff
+// of the resource land at lds + 16 i; offsets at or past the resource's
+// size load zeros (the zero padding of a ragged chunk, with no branches).
+template <bool SC1>
+__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, const void* lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
+  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
+  if constexpr (SC1)
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen sc1 lds" ::"s"(m0), "v"(voff), "s"(r), "s"(so)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(r), "s"(so)
+                 : "memory", "m0");
+}
+
+// A buffer resource built from wave-uniform values read back as such (so it
+// sits in SGPRs even where the compiler has kept its inputs in VGPRs).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t urs(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const void* b = reinterpret_cast<const void*>(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                                                (uint32_t)__builtin_amdgcn_readfirstlane((int)a));
+  return make_rsrc(b, (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes));
+}
+
 __device__ __forceinline__ float to_agpr(float v) {
   float a;
   asm("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
@@ -163,6 +187,12 @@ __host__ __device__ constexpr bool pair_kept(int e, int W) {
 }
 __host__ __device__ constexpr int pair_jb(int e) { return e < 4 ? e : 8 - (e - 3); }
 __host__ __device__ constexpr bool pair_diag(int e, int W) { return pair_jb(e) == (e < 4 ? W : 7 - W); }
+__host__ __device__ constexpr int kept_index(int e, int W) {
+  int n = 0;
+  for (int f = 0; f < e; ++f)
+    if (pair_kept(f, W)) ++n;
+  return n;
+}
 __host__ __device__ constexpr int next_pair(int e, int W) {
   for (int f = e + 1; f < 12; ++f)
     if (pair_kept(f, W)) return f;
@@ -202,87 +232,130 @@ void ssd_chunk_chained(const bf16* __restrict__ x, const bf16* __restrict__ Bm, 
 
   // x tile direct loads: instruction kk (8 rows) puts lane l at row
   // 8 kk + l / 8, 16-byte piece (l % 8) with the 64-byte halves swapped in
-  // rows with bit 1 set
-  const int jl = lane >> 3;
-  const uint32_t xpiece = (uint32_t)((lane & 7) ^ ((jl & 2) << 1)) * 16;
+  // rows with bit 1 set. B tile direct loads: instruction kk puts lane l at
+  // row RPI kk + t_l, stored piece c_s = l % PPR, which holds logical piece
+  // c_s ^ bswz(row); the swizzle of row RPI (wave + 4 i) + t_l equals that of
+  // RPI wave + t_l (bswz has period 16 rows for N = 128 and 8 for N = 64), so
+  // a lane's source offset is one constant for all of its B loads. The
+  // per-lane offsets are derived where a group of loads is issued, from a
+  // laundered lane id, so they do not stay live across the head.
+  constexpr int PPR = BRB / 16, RPI = 1024 / BRB;
+  const uint32_t bstride = (uint32_t)G * N * 2;
+  struct LoadLane {
+    uint32_t jl, xpiece, x_lane, b_tl, b_cs, b_lane;
+  };
+  auto load_lane = [&]() {
+    int ll = lane;
+    asm volatile("" : "+v"(ll));
+    LoadLane L;
+    L.jl = (uint32_t)ll >> 3;
+    L.xpiece = (((uint32_t)ll & 7) ^ ((L.jl & 2) << 1)) * 16;
+    L.x_lane = L.jl * xrb + L.xpiece;
+    L.b_tl = (uint32_t)ll / PPR;
+    L.b_cs = (uint32_t)ll % PPR;
+    L.b_lane = L.b_tl * bstride + ((L.b_cs ^ bswz<N>((uint32_t)(RPI * wave) + L.b_tl)) * 16);
+    return L;
+  };
 
-  // issue the x rows, G' and dt rows of head h of (b, k) into sX
-  auto issue_x = [&](int64_t b, int64_t k, int h, int nvalid) {
-    const unsigned char* xs = reinterpret_cast<const unsigned char*>(x + ((b * Tlen + k * Q) * H + h) * P);
-    uint32_t xr = xrb, xpc = xpiece;
-    int jll = jl;
-    asm volatile("" : "+v"(jll), "+v"(xpc), "+s"(xr));
-#pragma unroll
-    for (int i = 0; i < Cf::LX; ++i) {
-      const int kk = wave + 4 * i;
-      const int row = min(kk * 8 + jll, nvalid - 1);
-      dma16<false>(xs, (uint32_t)row * xr + xpc, sX + kk * 1024);
-    }
+  // resources over one head's chunk of x (rows past the sequence read as
+  // zeros), over the chunk's B rows of one group, and over one state
+  auto x_rsrc = [&](int b, int k, int h, int nvalid) {
+    const bf16* xs = x + (((int64_t)b * Tlen + (int64_t)k * Q) * H + h) * P;
+    return urs(xs, (uint32_t)(nvalid - 1) * xrb + P * 2);
+  };
+  auto b_rsrc = [&](const bf16* bt, int nvalid) { return urs(bt, (uint32_t)(nvalid - 1) * bstride + N * 2); };
+  // one of the LX x-row loads (instruction i of this wave)
+  auto issue_x_one = [&](const LoadLane& L, __amdgpu_buffer_rsrc_t rx, int i) {
+    int w = wave;
+    asm volatile("" : "+s"(w));
+    const int kk = w + 4 * i;
+    bdma16<false>(rx, L.x_lane, (uint32_t)(kk * 8) * xrb, sX + kk * 1024);
+  };
+  // the G' row (wave 0) or dt row (wave 1) of head h of (b, k)
+  auto issue_gd = [&](int b, int k, int h) {
     if (wave < Cf::IG) {
-      const float* src = (wave == 0 ? gcum : dtt) + (b * H + h) * Tp + k * Q;
-      dma16<false>(src, (uint32_t)lane * 16, sX + Cf::XBYTES + wave * 1024);
+      const float* src = (wave == 0 ? gcum : dtt) + ((int64_t)b * H + h) * Tp + (int64_t)k * Q;
+      bdma16<false>(urs(src, Q * 4), (uint32_t)lane * 16, 0, sX + Cf::XBYTES + wave * 1024);
     }
   };
-
-  // issue the B rows of (b, k, group) into sB (swizzled pieces)
-  auto issue_B = [&](const bf16* bt, int nvalid) {
-    int ll = lane;
-    asm volatile("" : "+v"(ll));
-#pragma unroll
-    for (int i = 0; i < Cf::LB; ++i) {
-      const int kk = wave + 4 * i;
+  // one of the LB B-row loads (instruction i of this wave), swizzled pieces
+  auto issue_B_one = [&](const LoadLane& L, __amdgpu_buffer_rsrc_t rb, int i) {
+    int w = wave;
+    asm volatile("" : "+s"(w));
+    const int kk = w + 4 * i;
+    bdma16<false>(rb, L.b_lane, (uint32_t)(RPI * kk) * bstride, sB + kk * 1024);
+  };
+  // one of the LH state-row loads (instruction i of this wave) of h_k into sH;
+  // the pad piece of each row reads past the resource (zeros)
+  auto issue_h_one = [&](__amdgpu_buffer_rsrc_t rh, bool coherent, int i) {
+    int w = wave;
+    asm volatile("" : "+s"(w));
+    const int kk = w + 4 * i;
+    if (kk < Cf::IH) {
+      int ll = lane;
+      asm volatile("" : "+v"(ll));
       const uint32_t o = (uint32_t)kk * 1024 + (uint32_t)ll * 16;
-      const uint32_t t = o / BRB, cs = (o % BRB) / 16;
-      const uint32_t c = cs ^ bswz<N>(t);
-      const uint32_t row = min((int)t, nvalid - 1);
-      dma16<false>(bt, row * (uint32_t)(G * N * 2) + c * 16, sB + kk * 1024);
+      const uint32_t r = o / HRB, c = (o % HRB) / 16;
+      const uint32_t voff = c < (uint32_t)(N / 4) ? r * (N * 4) + c * 16 : 0x7ffffff0u;
+      if (coherent) bdma16<true>(rh, voff, 0, sH + kk * 1024);
+      else bdma16<false>(rh, voff, 0, sH + kk * 1024);
     }
   };
-
-  // h_k into sH (fp32 rows of N values at stride HRB) from a [P][N] fp32 array
-  auto issue_h = [&](const float* src, bool coherent) {
-    int ll = lane;
-    asm volatile("" : "+v"(ll));
+  auto h_rsrc = [&](const float* src) { return urs(src, (uint32_t)(P * N * 4)); };
+  auto issue_x = [&](int b, int k, int h, int nvalid) {
+    const LoadLane L = load_lane();
+    const __amdgpu_buffer_rsrc_t rx = x_rsrc(b, k, h, nvalid);
 #pragma unroll
-    for (int i = 0; i < Cf::LH; ++i) {
-      const int kk = wave + 4 * i;
-      if (kk < Cf::IH) {
-        const uint32_t o = (uint32_t)kk * 1024 + (uint32_t)ll * 16;
-        uint32_t r = o / HRB, c = (o % HRB) / 16;
-        if (c >= (uint32_t)(N / 4)) c = 0;            // the pad piece: any valid bytes
-        if (coherent) dma16<true>(src, r * (N * 4) + c * 16, sH + kk * 1024);
-        else dma16<false>(src, r * (N * 4) + c * 16, sH + kk * 1024);
-      }
-    }
+    for (int i = 0; i < Cf::LX; ++i) issue_x_one(L, rx, i);
+    issue_gd(b, k, h);
+  };
+  auto issue_B = [&](const bf16* bt, int nvalid) {
+    const LoadLane L = load_lane();
+    const __amdgpu_buffer_rsrc_t rb = b_rsrc(bt, nvalid);
+#pragma unroll
+    for (int i = 0; i < Cf::LB; ++i) issue_B_one(L, rb, i);
+  };
+  auto issue_h = [&](const float* src, bool coherent) {
+    const __amdgpu_buffer_rsrc_t rh = h_rsrc(src);
+#pragma unroll
+    for (int i = 0; i < Cf::LH; ++i) issue_h_one(rh, coherent, i);
   };
 
   float cbc[9][16];   // resident C.B^T blocks of the ticket's (b, k, group), in AGPRs
   Frag cf[2][KS];     // C fragments of the wave's t-blocks, in AGPRs
 
+  auto uniform64 = [](int64_t v) {
+    return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)v));
+  };
+  const int64_t per = ntickets / nc;                          // tickets per chunk = batch * NHB
+  if (tid == 0) sTicket = __hip_atomic_fetch_add(reinterpret_cast<long long*>(sync), 1LL, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+  lds_barrier();
+  // wave-uniform: the addresses derived from it are scalar operands
+  int64_t ticket = uniform64(sTicket);
+  bool prefetched = false;   // the ticket's B tile and first x tile were issued during the previous ticket
+  int flag_raw = 0;          // the next head's progress flag, polled during the previous head
+
   for (;;) {
-    if (tid == 0) sTicket = __hip_atomic_fetch_add(reinterpret_cast<long long*>(sync), 1LL, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-    lds_barrier();
-    // wave-uniform: the addresses derived from it are scalar operands
-    const int64_t tv = sTicket;
-    const int64_t ticket = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(tv >> 32)) << 32) |
-                                     (uint32_t)__builtin_amdgcn_readfirstlane((int)tv));
     if (ticket >= ntickets) break;
-    const int64_t per = ntickets / nc;                          // tickets per chunk = batch * NHB
-    const int64_t k = ticket / per;
-    const int64_t u = ticket % per;
-    const int64_t b = u / NHB;
-    const int hb = (int)(u % NHB);
+    const int k = (int)(ticket / per);
+    const int u = (int)(ticket % per);
+    const int b = u / NHB;
+    const int hb = u % NHB;
     const int h0 = hb * HB;
     const int grp = h0 / (H / G);
-    const int64_t t0 = k * Q;
+    const int64_t t0 = (int64_t)k * Q;
     const int nvalid = (int)(Tlen - t0 < Q ? Tlen - t0 : Q);
-    const bf16* bt = Bm + ((b * Tlen + t0) * G + grp) * N;
-    const bf16* ct = Cm + ((b * Tlen + t0) * G + grp) * N;
+    const bf16* bt = Bm + (((int64_t)b * Tlen + t0) * G + grp) * N;
+    const bf16* ct = Cm + (((int64_t)b * Tlen + t0) * G + grp) * N;
+    int64_t next_ticket = ntickets;
 
     // ---- ticket set-up: B tile, the first head's x, C fragments, C.B^T
-    issue_B(bt, nvalid);
-    issue_x(b, k, h0, nvalid);
+    if (!prefetched) {
+      issue_B(bt, nvalid);
+      issue_x(b, k, h0, nvalid);
+    }
     {
       int lt = lane;
       asm volatile("" : "+v"(lt));
@@ -324,12 +397,16 @@ void ssd_chunk_chained(const bf16* __restrict__ x, const bf16* __restrict__ Bm, 
 
     for (int j = 0; j < HB; ++j) {
       const int h = h0 + j;
-      const int64_t bh = b * H + h;
+      const int64_t bh = (int64_t)b * H + h;
       int lt = lane;
       asm volatile("" : "+v"(lt));
       const int m = lt & 31, g = lt >> 5;
-      // x of this head has landed (issued at ticket start or during the previous head)
-      vm_lds_barrier();
+      // this head's x has landed (and the previous head's flag poll); the 8 y
+      // stores of the previous head may still be in flight
+      asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (j == HB - 1 && tid == 0)
+        sTicket = __hip_atomic_fetch_add(reinterpret_cast<long long*>(sync), 1LL, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
       {
         const float gi = sG[tid];
         sW[tid] = sDt[tid] * exp2_hw(sG[tid | 31] - gi);
@@ -339,7 +416,16 @@ void ssd_chunk_chained(const bf16* __restrict__ x, const bf16* __restrict__ Bm, 
       const float gt0 = sG[tb0 * 32 + m], gt1 = sG[tb1 * 32 + m];
       const float glast = sG[Q - 1];
       const float Dh = Dp[h];
+      // h_k: from the initial state (or zeros) at chunk 0, else from the
+      // previous chunk's tile once its flag is up (polled during the
+      // previous head; a poll that missed is repeated at the chain step)
+      bool h_issue = k == 0 ? init != nullptr : __builtin_amdgcn_readfirstlane(flag_raw) >= (int)k;
+      if (k == 0 && !init)
+        for (int o = tid * 16; o < Cf::HBYTES; o += 256 * 16) *reinterpret_cast<u32x4*>(sH + o) = u32x4{0u, 0u, 0u, 0u};
+      const float* hsrc = k == 0 ? init + bh * (int64_t)(P * N) : chain + bh * (int64_t)(P * N);
+      const __amdgpu_buffer_rsrc_t rh = h_rsrc(hsrc);
       lds_barrier();
+      if (j == HB - 1) next_ticket = uniform64(sTicket);   // claimed above, visible after the barrier
 
       // transposing x reads: lane s supplies row 4 (s / 32) + (s % 16) / 4 of
       // a 16-row step, headdim columns 16 ((s / 16) % 2) + 4 (s % 4) + 32 pe
@@ -360,7 +446,9 @@ void ssd_chunk_chained(const bf16* __restrict__ x, const bf16* __restrict__ Bm, 
       };
 
       // ---- phase A: S_k^T[n][p] = sum_t B[t][n] (w_t x[t][p]); rows n of
-      // dstate blocks NBW (w >> 1) + i, columns p of headdim block w & 1
+      // dstate blocks NBW (w >> 1) + i, columns p of headdim block w & 1.
+      // Each step's fragments are read while the previous step computes;
+      // h_k's direct loads (when issued here) go one per step among the MFMAs.
       const int pe_a = wave & 1, nb0 = NBW * (wave >> 1);
       f32x16 sacc[NBW];
 #pragma unroll
@@ -368,87 +456,108 @@ void ssd_chunk_chained(const bf16* __restrict__ x, const bf16* __restrict__ Bm, 
       {
         // B^T fragment reads: lane supplies row 16 s + 8 hh + 4 g + (l % 16) / 4,
         // the 8 bytes of dstate columns 32 nb + 16 ((l / 16) % 2) + 4 (l % 4) ..
+        // (row 16 s + t_r has the swizzle of row t_r: bswz has period 16 or 8)
         const uint32_t a_ = (uint32_t)((lt & 15) >> 2);
         const uint32_t piece0 = (uint32_t)(2 * ((lt >> 4) & 1) + ((lt & 3) >> 1));
         const uint32_t half = (uint32_t)(lt & 1) * 8;
-        auto load_bt = [&](int nb, int s) -> Frag {
+        uint32_t btoff[2][NBW];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < NBW; ++i) {
+            const uint32_t tr = (uint32_t)(8 * hh + 4 * g) + a_;
+            btoff[hh][i] = tr * BRB + (((uint32_t)(4 * (nb0 + i)) + piece0) ^ bswz<N>(tr)) * 16 + half;
+          }
+        auto load_bt = [&](int i, int s) -> Frag {
           uint64_t h2[2];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const uint32_t t = (uint32_t)(16 * s + 8 * hh + 4 * g) + a_;
-            const uint32_t c = (uint32_t)(4 * nb) + piece0;
-            const unsigned char* adr = sB + t * BRB + ((c ^ bswz<N>(t)) * 16) + half;
+            const unsigned char* adr = sB + btoff[hh][i] + 16 * s * BRB;
             h2[hh] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                                                       (__attribute__((address_space(3))) s16x4*)(adr)));
           }
           const u32x4 w4 = {(uint32_t)h2[0], (uint32_t)(h2[0] >> 32), (uint32_t)h2[1], (uint32_t)(h2[1] >> 32)};
           return __builtin_bit_cast(Frag, w4);
         };
-#pragma unroll 4
-        for (int s = 0; s < 16; ++s) {
-          const Frag xf = load_xs(pe_a, s);
-          Frag bfr[NBW];
+        // software pipeline over the 16 steps: at step s the fragments of step
+        // s + 2 are read, the (hi, lo) split of step s + 1 is formed, and the
+        // MFMAs of step s run (their split was formed one step earlier)
+        Frag xf[3], bfr[3][NBW];
+        float4 wq[3][2];
+        Frag shi[2], slo[2];
+        auto ldA = [&](int s, int sl) {
+          xf[sl] = load_xs(pe_a, s);
 #pragma unroll
-          for (int i = 0; i < NBW; ++i) bfr[i] = load_bt(nb0 + i, s);
-          const float4 w0 = *reinterpret_cast<const float4*>(&sWs[16 * s + 4 * g]);
-          const float4 w1 = *reinterpret_cast<const float4*>(&sWs[16 * s + 8 + 4 * g]);
-          const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-          const u32x4 xd = __builtin_bit_cast(u32x4, xf);
-          float v[8];
+          for (int i = 0; i < NBW; ++i) bfr[sl][i] = load_bt(i, s);
+          wq[sl][0] = *reinterpret_cast<const float4*>(&sWs[16 * s + 4 * g]);
+          wq[sl][1] = *reinterpret_cast<const float4*>(&sWs[16 * s + 8 + 4 * g]);
+        };
+        // w o x of one step as a bf16 (hi, lo) pair; each hi value is taken as
+        // a bit slice of the packed pair
+        auto splitA = [&](int sl, Frag& hi, Frag& lo) {
+          const float wv[8] = {wq[sl][0].x, wq[sl][0].y, wq[sl][0].z, wq[sl][0].w,
+                               wq[sl][1].x, wq[sl][1].y, wq[sl][1].z, wq[sl][1].w};
+          const u32x4 xd = __builtin_bit_cast(u32x4, xf[sl]);
+          u32x4 uh, ul;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            v[2 * i] = wv[2 * i] * bf16lo(xd[i]);
-            v[2 * i + 1] = wv[2 * i + 1] * bf16hi(xd[i]);
+            const float v0 = wv[2 * i] * bf16lo(xd[i]), v1 = wv[2 * i + 1] * bf16hi(xd[i]);
+            uint32_t hh = pack_bf16x2(v0, v1);
+            asm volatile("" : "+v"(hh));
+            uh[i] = hh;
+            ul[i] = pack_bf16x2(v0 - __uint_as_float(hh << 16), v1 - __uint_as_float(hh & 0xffff0000u));
           }
-          Frag hi, lo;
-          I::split(v, hi, lo);
+          hi = __builtin_bit_cast(Frag, uh);
+          lo = __builtin_bit_cast(Frag, ul);
+        };
+        ldA(0, 0);
+        ldA(1, 1);
+        splitA(0, shi[0], slo[0]);
 #pragma unroll
-          for (int i = 0; i < NBW; ++i) {
-            I::mma(sacc[i], bfr[i], hi);
-            I::mma(sacc[i], bfr[i], lo);
+        for (int s = 0; s < 16; ++s) {
+          if (s + 2 < 16) ldA(s + 2, (s + 2) % 3);
+          if (h_issue && s < Cf::LH) issue_h_one(rh, k > 0, s);
+#pragma unroll
+          for (int i = 0; i < NBW; ++i) I::mma(sacc[i], bfr[s % 3][i], shi[s & 1]);
+#pragma unroll
+          for (int i = 0; i < NBW; ++i) I::mma(sacc[i], bfr[s % 3][i], slo[s & 1]);
+          if (s + 1 < 16) splitA((s + 1) % 3, shi[(s + 1) & 1], slo[(s + 1) & 1]);
+          // interleave this step's MFMAs with the next step's split
+#pragma unroll
+          for (int q = 0; q < 2 * NBW; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 40 / (2 * NBW), 0);   // then VALU
           }
         }
       }
 
-      // ---- chain: h_k into sH, h_{k+1} out, h_k rewritten as (hi, lo) pairs
-      if (k == 0) {
-        if (init) {
-          issue_h(init + bh * (int64_t)(P * N), false);
-        } else {
-          for (int o = tid * 16; o < Cf::HBYTES; o += 256 * 16) *reinterpret_cast<u32x4*>(sH + o) = u32x4{0u, 0u, 0u, 0u};
-        }
-      } else {
+      // ---- chain: h_k in sH, h_{k+1} out, h_k rewritten as (hi, lo) pairs
+      if (!h_issue && k > 0) {
         wait_flag(sync + kSyncFlags + bh, (int)k, sync);
-        issue_h(chain + bh * (int64_t)(P * N), true);
+        issue_h(hsrc, true);
       }
       vm_lds_barrier();
+      // h_{k+1} (this wave's part), stored among the pairs below
+      u32x4 hn[NBW][4];
       {
         const float alpha = exp2_hw(glast);
         const int p = 32 * pe_a + m;
-        const bool last = k + 1 == nc;
-        float* dst = last ? final_state : chain;
         float4 hk[NBW][4];
 #pragma unroll
         for (int i = 0; i < NBW; ++i)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             hk[i][q] = *reinterpret_cast<const float4*>(sH + p * HRB + 4 * (32 * (nb0 + i) + 8 * q + 4 * g));
-        if (dst) {
-          const __amdgpu_buffer_rsrc_t rs = make_rsrc(dst + bh * (int64_t)(P * N), (uint32_t)(P * N * 4));
 #pragma unroll
-          for (int i = 0; i < NBW; ++i)
+        for (int i = 0; i < NBW; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float4 a = hk[i][q];
-              const u32x4 v = {__float_as_uint(fmaf(alpha, a.x, sacc[i][4 * q])),
-                               __float_as_uint(fmaf(alpha, a.y, sacc[i][4 * q + 1])),
-                               __float_as_uint(fmaf(alpha, a.z, sacc[i][4 * q + 2])),
-                               __float_as_uint(fmaf(alpha, a.w, sacc[i][4 * q + 3]))};
-              const uint32_t off = (uint32_t)(p * N + 32 * (nb0 + i) + 8 * q + 4 * g) * 4;
-              if (last) __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 0);
-              else __builtin_amdgcn_raw_buffer_store_b128(v, rs, off, 0, 16);   // sc1
-            }
-        }
+          for (int q = 0; q < 4; ++q) {
+            const float4 a = hk[i][q];
+            hn[i][q] = u32x4{__float_as_uint(fmaf(alpha, a.x, sacc[i][4 * q])),
+                             __float_as_uint(fmaf(alpha, a.y, sacc[i][4 * q + 1])),
+                             __float_as_uint(fmaf(alpha, a.z, sacc[i][4 * q + 2])),
+                             __float_as_uint(fmaf(alpha, a.w, sacc[i][4 * q + 3]))};
+          }
         // h_k as (hi, lo) bf16 pairs, in place: group n / 8 of row p holds 8
         // hi values then 8 lo values (the same 32 bytes its fp32 values took)
 #pragma unroll
@@ -466,53 +575,61 @@ void ssd_chunk_chained(const bf16* __restrict__ x, const bf16* __restrict__ Bm, 
       }
       lds_barrier();
 
-      // ---- carried state: acc[u][pe] = h_k . C^T (rows p, columns t), then
-      // columns scaled by 2^(G'_t)
+      // the next head: the next of this ticket, or the first of the next ticket
+      bool has_next = true, new_ticket = false;
+      int nk = k, nb = b;
+      int nh = h + 1, nvn = nvalid;
+      const bf16* nbt = bt;
+      if (j + 1 == HB) {
+        new_ticket = true;
+        has_next = next_ticket < ntickets;
+        if (has_next) {
+          nk = (int)(next_ticket / per);
+          const int nu = (int)(next_ticket % per);
+          nb = nu / NHB;
+          nh = (nu % NHB) * HB;
+          const int64_t nt0 = (int64_t)nk * Q;
+          nvn = (int)(Tlen - nt0 < Q ? Tlen - nt0 : Q);
+          nbt = Bm + (((int64_t)nb * Tlen + nt0) * G + nh / (H / G)) * N;
+        }
+      }
+
+      // after pair number idx (0..8) of the pairs below: this wave's stores of
+      // h_{k+1} (spread over the first five pairs, so the write path drains
+      // between them) and, before a new ticket, its loads of that ticket's B
+      // tile (B of this ticket is no longer read)
+      const bool last_chunk = k + 1 == nc;
+      float* hdst = last_chunk ? final_state : chain;
+      auto pair_hook = [&](int idx) {
+        constexpr int NS = NBW * 4;
+        if (hdst) {
+          const __amdgpu_buffer_rsrc_t rs = urs(hdst + bh * (int64_t)(P * N), (uint32_t)(P * N * 4));
+          int ll = lane;
+          asm volatile("" : "+v"(ll));
+          const int p = 32 * pe_a + (ll & 31), gg = ll >> 5;
+#pragma unroll
+          for (int si = 0; si < NS; ++si) {
+            if (si < idx * NS / 5 || si >= (idx + 1) * NS / 5) continue;
+            const int i = si / 4, q = si % 4;
+            const uint32_t off = (uint32_t)(p * N + 32 * (nb0 + i) + 8 * q + 4 * gg) * 4;
+            if (last_chunk) __builtin_amdgcn_raw_buffer_store_b128(hn[i][q], rs, off, 0, 0);
+            else __builtin_amdgcn_raw_buffer_store_b128(hn[i][q], rs, off, 0, 16);   // sc1
+          }
+        }
+        if (has_next && new_ticket) {
+          const LoadLane LB_ = load_lane();
+          const __amdgpu_buffer_rsrc_t rbn = b_rsrc(nbt, nvn);
+#pragma unroll
+          for (int q = 0; q < Cf::LB; ++q)
+            if (q >= idx * Cf::LB / 9 && q < (idx + 1) * Cf::LB / 9) issue_B_one(LB_, rbn, q);
+        }
+      };
+
       f32x16 acc[2][2];
 #pragma unroll
       for (int uu = 0; uu < 2; ++uu)
 #pragma unroll
         for (int pe = 0; pe < 2; ++pe) acc[uu][pe] = f32x16{};
-      {
-        constexpr int HBK = KS / 4;
-        Frag hf[2][2][4];
-        auto load_h = [&](int blk, Frag (*dst)[4]) {
-          const int pe = blk / HBK, s0 = (blk % HBK) * 4;
-          const unsigned char* hp = sH + (pe * 32 + m) * HRB;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            dst[0][i] = *reinterpret_cast<const Frag*>(hp + (2 * (s0 + i) + g) * 32);
-            dst[1][i] = *reinterpret_cast<const Frag*>(hp + (2 * (s0 + i) + g) * 32 + 16);
-          }
-        };
-        load_h(0, hf[0]);
-#pragma unroll
-        for (int blk = 0; blk < 2 * HBK; ++blk) {
-          if (blk + 1 < 2 * HBK) load_h(blk + 1, hf[(blk + 1) & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-          const int pe = blk / HBK, s0 = (blk % HBK) * 4;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int uu = 0; uu < 2; ++uu) {
-              I::mma(acc[uu][pe], hf[blk & 1][0][i], cf[uu][s0 + i]);
-              I::mma(acc[uu][pe], hf[blk & 1][1][i], cf[uu][s0 + i]);
-            }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-#pragma unroll
-      for (int uu = 0; uu < 2; ++uu) {
-        const float sc = sE[(uu ? tb1 : tb0) * 32 + m];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          acc[uu][0][r] *= sc;
-          acc[uu][1][r] *= sc;
-        }
-      }
-      // h_{k+1} is stored (every wave waited for its stores): raise the flag
-      vm_lds_barrier();
-      if (tid == 0) __hip_atomic_store(sync + kSyncFlags + bh, (int)(k + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
       // ---- intra-chunk pairs, slot by slot, specialised per wave
       auto pairs = [&](auto wtag) {
@@ -591,6 +708,7 @@ void ssd_chunk_chained(const bf16* __restrict__ x, const bf16* __restrict__ Bm, 
               I::mma(acc[uu][pe], d[pe][js], alo);
             }
           }
+          pair_hook(kept_index(e, W));
 #pragma unroll
           for (int pe = 0; pe < 2; ++pe)
 #pragma unroll
@@ -610,9 +728,73 @@ void ssd_chunk_chained(const bf16* __restrict__ x, const bf16* __restrict__ Bm, 
       }
       __builtin_amdgcn_sched_barrier(0);
 
-      // every wave is done with x and h_k: the next head's x may load
-      lds_barrier();
-      if (j + 1 < HB) issue_x(b, k, h + 1, nvalid);
+      // h_{k+1} is stored (each wave waits for its stores, issued among the
+      // first pairs), and every wave is done with x: raise the flag; the next
+      // head's x may load
+      vm_lds_barrier();
+      if (tid == 0) __hip_atomic_store(sync + kSyncFlags + bh, (int)(k + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+      // ---- carried state: tmp[u][pe] = h_k . C^T (rows p, columns t), then
+      // acc += 2^(G'_t) tmp. The next head's x, G' and dt (and for a new
+      // ticket its B tile) are issued among these MFMAs.
+      {
+        constexpr int HBK = KS / 4, NBLK = 2 * HBK;
+        constexpr int NPF = Cf::LX + 1;               // x rows, G'/dt row
+        const LoadLane LL = load_lane();
+        const __amdgpu_buffer_rsrc_t rxn = x_rsrc(nb, nk, nh, nvn);
+        auto prefetch = [&](int q0, int q1) {
+          if (!has_next) return;
+#pragma unroll
+          for (int q = 0; q < NPF; ++q) {
+            if (q < q0 || q >= q1) continue;
+            if (q < Cf::LX) issue_x_one(LL, rxn, q);
+            else issue_gd(nb, nk, nh);
+          }
+        };
+        f32x16 tmp[2][2];
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu)
+#pragma unroll
+          for (int pe = 0; pe < 2; ++pe) tmp[uu][pe] = f32x16{};
+        Frag hf[2][2][4];
+        auto load_h = [&](int blk, Frag (*dst)[4]) {
+          const int pe = blk / HBK, s0 = (blk % HBK) * 4;
+          const unsigned char* hp = sH + (pe * 32 + m) * HRB;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            dst[0][i] = *reinterpret_cast<const Frag*>(hp + (2 * (s0 + i) + g) * 32);
+            dst[1][i] = *reinterpret_cast<const Frag*>(hp + (2 * (s0 + i) + g) * 32 + 16);
+          }
+        };
+        load_h(0, hf[0]);
+#pragma unroll
+        for (int blk = 0; blk < NBLK; ++blk) {
+          if (blk + 1 < NBLK) load_h(blk + 1, hf[(blk + 1) & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+          const int pe = blk / HBK, s0 = (blk % HBK) * 4;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int uu = 0; uu < 2; ++uu) {
+              I::mma(tmp[uu][pe], hf[blk & 1][0][i], cf[uu][s0 + i]);
+              I::mma(tmp[uu][pe], hf[blk & 1][1][i], cf[uu][s0 + i]);
+            }
+          prefetch(blk * NPF / NBLK, (blk + 1) * NPF / NBLK);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int uu = 0; uu < 2; ++uu) {
+          const float sc = sE[(uu ? tb1 : tb0) * 32 + m];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            acc[uu][0][r] = fmaf(sc, tmp[uu][0][r], acc[uu][0][r]);
+            acc[uu][1][r] = fmaf(sc, tmp[uu][1][r], acc[uu][1][r]);
+          }
+        }
+      }
+      // the next head's flag, read at its start (after the y stores below)
+      if (has_next && nk > 0)
+        flag_raw = __hip_atomic_load(sync + kSyncFlags + (int64_t)nb * H + nh, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
       // ---- y through LDS in 16-byte row pieces (as the resident scan)
       {
@@ -622,8 +804,8 @@ void ssd_chunk_chained(const bf16* __restrict__ x, const bf16* __restrict__ Bm, 
         uint32_t plane = (uint32_t)pr * xrb + (uint32_t)pc * 16;
         uint32_t xrbs = xrb;
         asm volatile("" : "+v"(plane), "+s"(xrbs));
-        unsigned char* yt = reinterpret_cast<unsigned char*>(y + ((b * Tlen + t0) * H + h) * P);
-        const __amdgpu_buffer_rsrc_t yr = make_rsrc(yt, (uint32_t)nvalid * xrbs);
+        unsigned char* yt = reinterpret_cast<unsigned char*>(y + (((int64_t)b * Tlen + t0) * H + h) * P);
+        const __amdgpu_buffer_rsrc_t yr = urs(yt, (uint32_t)nvalid * xrbs);
 #pragma unroll
         for (int uu = 0; uu < 2; ++uu) {
 #pragma unroll
@@ -644,6 +826,8 @@ void ssd_chunk_chained(const bf16* __restrict__ x, const bf16* __restrict__ Bm, 
         }
       }
     }
+    ticket = next_ticket;
+    prefetched = true;
   }
 }
 
