@@ -50,6 +50,7 @@
 //             products formed transposed (y^T = x^T M^T), D x on the
 //             diagonal, y out through LDS as 16-byte row pieces.
 // The next head's x tile is loaded while this head's outputs are stored.
+#include "lookback_device.h"
 #include "ssd_device.h"
 #include "ssd_launch.h"
 
@@ -58,6 +59,8 @@
 namespace ssd {
 
 namespace {
+
+using namespace lookback;
 
 template <int N>
 struct CCfg {
@@ -79,60 +82,6 @@ struct CCfg {
   static_assert(BBYTES + XBYTES + GBYTES + HBYTES + 4 * 4096 + 3 * Q * 4 + 64 <= 160 * 1024, "LDS");
 };
 
-// 16-byte piece c of B row t sits at piece c ^ bswz(t): the transposing
-// reads of phase A (4 rows x 2 adjacent pieces per 16 lanes) and the row
-// fragment reads of C.B^T (16 rows x 1 piece per 16 lanes) then both hit 16
-// distinct 16-byte bank groups.
-template <int N>
-__device__ __forceinline__ constexpr uint32_t bswz(uint32_t t) {
-  constexpr uint32_t H = CCfg<N>::NPC / 2;
-  return 2 * (t % H) + (t / H) % 2;
-}
-
-// Direct global->LDS load of 16 bytes per lane from a wave-uniform base plus
-// a per-lane offset; lane i's bytes land at lds + 16 i (lds wave-uniform, in
-// M0). SC1: device-coherent (the load misses any cache that could hold a
-// stale copy written by another XCD).
-template <bool SC1>
-__device__ __forceinline__ void dma16(const void* sbase_in, uint32_t voff, const void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
-  // the base is wave-uniform by construction; say so, so it goes in SGPRs
-  const uint64_t a = reinterpret_cast<uint64_t>(sbase_in);
-  const void* sbase = reinterpret_cast<const void*>(
-      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
-      (uint32_t)__builtin_amdgcn_readfirstlane((int)a));
-  if constexpr (SC1)
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2 sc1" ::"s"(m0), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff), "s"(sbase)
-                 : "memory", "m0");
-}
-
-// The same through a buffer resource: lane i's 16 bytes at byte voff + soff
-// of the resource land at lds + 16 i; offsets at or past the resource's
-// size load zeros (the zero padding of a ragged chunk, with no branches).
-template <bool SC1>
-__device__ __forceinline__ void bdma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, const void* lds) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)reinterpret_cast<uintptr_t>(lds));
-  const uint32_t so = __builtin_amdgcn_readfirstlane(soff);
-  if constexpr (SC1)
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen sc1 lds" ::"s"(m0), "v"(voff), "s"(r), "s"(so)
-                 : "memory", "m0");
-  else
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds" ::"s"(m0), "v"(voff), "s"(r), "s"(so)
-                 : "memory", "m0");
-}
-
-// A buffer resource built from wave-uniform values read back as such (so it
-// sits in SGPRs even where the compiler has kept its inputs in VGPRs).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t urs(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  const void* b = reinterpret_cast<const void*>(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
-                                                (uint32_t)__builtin_amdgcn_readfirstlane((int)a));
-  return make_rsrc(b, (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes));
-}
-
 __device__ __forceinline__ float to_agpr(float v) {
   float a;
   asm("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
@@ -142,41 +91,6 @@ __device__ __forceinline__ float from_agpr(float a) {
   float v;
   asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
   return v;
-}
-
-__device__ __forceinline__ void vm_wait0() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-__device__ __forceinline__ void vm_lds_barrier() {
-  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// The sync region (int32 words, cleared by ssd_chunk_cumsum): words 0-1 the
-// 64-bit ticket counter, word 2 the error word (1: a wait hit its bound),
-// from word 64 one progress flag per (batch, head): the number of chunks
-// whose outgoing state has been published. Flags are read and written with
-// relaxed device-scope atomics (device-coherent on every XCD); ordering
-// against the state itself comes from the state's stores completing
-// (vmcnt) before the flag is raised.
-constexpr int kSyncErr = 2;
-constexpr int kSyncFlags = 64;
-constexpr int kMaxPolls = 1 << 18;      // bound of one wait (each poll sleeps, then reloads)
-
-__device__ __forceinline__ int load_flag(const int* f) {
-  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
-
-// Wait (the whole wave) until *f >= want; on the bound, record the error word.
-__device__ __forceinline__ void wait_flag(const int* f, int want, int* sync) {
-  int v = load_flag(f);
-  int polls = 0;
-  while (v < want) {
-    __builtin_amdgcn_s_sleep(2);
-    if (++polls > kMaxPolls) {
-      __hip_atomic_store(sync + kSyncErr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
-    }
-    v = load_flag(f);
-  }
 }
 
 // The intra-chunk pairs of wave W, in emission order e = 0..11 (as the
@@ -324,10 +238,6 @@ void ssd_chunk_chained(const bf16* __restrict__ x, const bf16* __restrict__ Bm, 
   float cbc[9][16];   // resident C.B^T blocks of the ticket's (b, k, group), in AGPRs
   Frag cf[2][KS];     // C fragments of the wave's t-blocks, in AGPRs
 
-  auto uniform64 = [](int64_t v) {
-    return (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32)) << 32) |
-                     (uint32_t)__builtin_amdgcn_readfirstlane((int)v));
-  };
   const int64_t per = ntickets / nc;                          // tickets per chunk = batch * NHB
   if (tid == 0) sTicket = __hip_atomic_fetch_add(reinterpret_cast<long long*>(sync), 1LL, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
