@@ -46,10 +46,8 @@ KERNEL_SOURCES = {"ssd_chunk_cumsum": ["chunk_cumsum.hip"], "ssd_chunk_state": [
                   "ssd_chunk_scan": ["chunk_scan.hip", "chunk_scan_resident.hip"],
                   "ssd_chunk_state_pass": ["chunk_state.hip"],
                   "ssd_chunk_chained": ["chunk_chained.hip", "lookback_device.h"],
-                  "ssd_state_lookback": ["state_lookback.hip", "lookback_device.h"],
                   "ssd_step": ["ssd_step.hip"]}
-PATHS = {"auto": 0x0000, "four": 0x1000, "three": 0x2000, "chained": 0x3000,
-         "lookback": 0x4000}   # MAMBA2_SSD_PATH_*
+PATHS = {"auto": 0x0000, "four": 0x1000, "three": 0x2000, "chained": 0x3000}   # MAMBA2_SSD_PATH_*
 FLUSH_BYTES = 1 << 30          # scratch written before each cold step (> the 256 MB last-level cache)
 TRAFFIC_SUMMARY = {"mamba2-2.7b": "hbm_traffic_mamba2-2.7b.md",
                    "mamba2-2.7b-decode": "hbm_traffic_mamba2-2.7b-decode.md"}
@@ -115,11 +113,6 @@ def algorithmic_cost(cfg):
         # cumsums in, Hprev (and final, init) out; no per-chunk states
         "ssd_chunk_state_pass": (x + bc + gq + Bt * H * nc * 4 + st + fin + init,
                                  2.0 * Bt * H * Tp * P * N + 2.0 * Bt * H * nc * P * N),
-        # the same by the look-back kernel: x, B, G' and dt rows in, Hprev (and
-        # final, init) out; the state handed between chunks is not an input
-        # or an output
-        "ssd_state_lookback": (x + bc + 2 * gq + st + fin + init,
-                               2.0 * Bt * H * Tp * P * N + 2.0 * Bt * H * nc * P * N),
         # Hprev counted at 4 bytes per element (fp32, or the bf16 (hi, lo) pair)
         "ssd_chunk_scan": (2 * x + 2 * bc + 2 * gq + st + H * 4, scan_flops),
         # the three in one: x, B, C, G', dt in, y and final out; the carried
@@ -138,8 +131,6 @@ def path_spans(path):
         return [("ssd_chunk_cumsum", 0, 1), ("ssd_chunk_chained", 1, 4)]
     if path == ssd.PATH_THREE:
         return [("ssd_chunk_cumsum", 0, 1), ("ssd_chunk_state_pass", 1, 3), ("ssd_chunk_scan", 3, 4)]
-    if path == ssd.PATH_LOOKBACK:
-        return [("ssd_chunk_cumsum", 0, 1), ("ssd_state_lookback", 1, 3), ("ssd_chunk_scan", 3, 4)]
     return [(k, i, i + 1) for i, k in enumerate(KERNELS)]
 
 

@@ -102,20 +102,13 @@ extern "C" {
  *            state contribution, the pass and the outputs, handing the
  *            carried state from each chunk to the next through the
  *            workspace (bf16, headdim 64, dstate 64 or 128, chunk 256)
- *   LOOKBACK ssd_chunk_cumsum, ssd_state_lookback (each chunk's state
- *            contribution and the pass, the carried state handed from each
- *            chunk to the next through the workspace), ssd_chunk_scan (bf16,
- *            headdim 64, dstate 64 or 128, chunk 256, an even number of
- *            heads per group)
- * Other values of the field are invalid (MAMBA2_SSD_ERR_UNSUPPORTED).
  * The workspace size depends on the sequence: query it with the same
  * io_dtype value that is passed to the call. */
-#define MAMBA2_SSD_PATH_AUTO     0x0000
-#define MAMBA2_SSD_PATH_FOUR     0x1000
-#define MAMBA2_SSD_PATH_THREE    0x2000
-#define MAMBA2_SSD_PATH_CHAINED  0x3000
-#define MAMBA2_SSD_PATH_LOOKBACK 0x4000
-#define MAMBA2_SSD_PATH_MASK     0x7000
+#define MAMBA2_SSD_PATH_AUTO    0x0000
+#define MAMBA2_SSD_PATH_FOUR    0x1000
+#define MAMBA2_SSD_PATH_THREE   0x2000
+#define MAMBA2_SSD_PATH_CHAINED 0x3000
+#define MAMBA2_SSD_PATH_MASK    0x3000
 
 /* Problem sizes. batch and seqlen may be 0 (nothing to compute: with
  * seqlen == 0 final_state receives init_state, or zeros). seqlen need not be
@@ -230,15 +223,15 @@ int mamba2_ssd_fwd(const mamba2_ssd_dims* dims, int io_dtype,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* The kernel sequence mamba2_ssd_fwd takes for these sizes and io_dtype
- * (including its path field): MAMBA2_SSD_PATH_FOUR, _THREE, _CHAINED or
- * _LOOKBACK, or a negative status when the arguments are invalid or the
- * forced sequence does not support the shape. AUTO chooses LOOKBACK where it
- * supports the shape, else THREE when its (batch, head, dstate group) walks
- * alone fill the GPU, else FOUR. Host only. */
+ * (including its path field): MAMBA2_SSD_PATH_FOUR, _THREE or _CHAINED, or a
+ * negative status when the arguments are invalid or the forced sequence
+ * does not support the shape. AUTO chooses CHAINED where it supports the
+ * shape, else THREE when its (batch, head, dstate group) walks alone fill
+ * the GPU, else FOUR. Host only. */
 int mamba2_ssd_fwd_path(const mamba2_ssd_dims* dims, int io_dtype);
 
 /* 1 if mamba2_ssd_fwd with these sizes computes the chunk states inside
- * another kernel (sequences THREE, CHAINED and LOOKBACK: the workspace holds no states
+ * another kernel (sequences THREE and CHAINED: the workspace holds no states
  * region), 0 if it runs ssd_chunk_state and ssd_state_pass (FOUR), or if
  * the arguments are invalid. Host only. */
 int mamba2_ssd_fused_state_pass(const mamba2_ssd_dims* dims, int io_dtype);

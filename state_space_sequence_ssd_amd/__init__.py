@@ -11,7 +11,7 @@ from __future__ import annotations
 import ctypes
 from typing import Optional, Tuple
 
-from ._lib import (BF16, DT_HEAD_MAJOR, F32, NOALLOC_MAX_WORKSPACE, PATH_AUTO, PATH_CHAINED, PATH_FOUR, PATH_LOOKBACK, PATH_NAMES, PATH_THREE, STATUS,
+from ._lib import (BF16, DT_HEAD_MAJOR, F32, NOALLOC_MAX_WORKSPACE, PATH_AUTO, PATH_CHAINED, PATH_FOUR, PATH_NAMES, PATH_THREE, STATUS,
                    Dims, S6Dims, SsdError, StepDims, WorkspaceLayout, lib, status_string)
 
 __all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_layout", "check_args",
@@ -23,7 +23,7 @@ __all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_
            "ssd_step", "ssd_step_ptr", "step_supported", "step_check_args", "StepDims",
            "mamba2_ssd_step", "mamba2_ssd_step_check_args", "mamba2_ssd_step_supported",
            "mamba2_ssd_fused_state_pass", "fused_state_pass", "mamba2_ssd_fwd_path", "fwd_path",
-           "PATH_AUTO", "PATH_FOUR", "PATH_THREE", "PATH_CHAINED", "PATH_LOOKBACK", "PATH_NAMES",
+           "PATH_AUTO", "PATH_FOUR", "PATH_THREE", "PATH_CHAINED", "PATH_NAMES",
            "mamba2_ssd_fwd_noalloc", "ssd_fwd_noalloc_ptr", "NOALLOC_MAX_WORKSPACE",
            "ssd_bwd", "ssd_bwd_ptr", "bwd_workspace_bytes", "bwd_check_args",
            "mamba2_ssd_bwd", "mamba2_ssd_bwd_check_args", "mamba2_ssd_bwd_workspace_bytes",
@@ -81,7 +81,7 @@ def fused_state_pass(dims, io: int) -> bool:
 
 
 def fwd_path(dims, io: int) -> int:
-    """The kernel sequence (PATH_FOUR, PATH_THREE, PATH_CHAINED or PATH_LOOKBACK) a forward
+    """The kernel sequence (PATH_FOUR, PATH_THREE or PATH_CHAINED) a forward
     call with these sizes and io value (including its path field) takes;
     raises SsdError when the arguments are invalid or the forced sequence does
     not support the shape."""
@@ -142,7 +142,7 @@ def ssd_fwd(x, dt, A, B, C, D, chunk: int, init_state=None, *, return_final_stat
     None when ``return_final_state`` is False. ``y``, ``final_state`` and
     ``workspace`` (a uint8 tensor) may be passed to reuse memory; otherwise
     they are allocated with torch. ``path`` forces a kernel sequence
-    (PATH_FOUR, PATH_THREE, PATH_CHAINED, PATH_LOOKBACK; PATH_AUTO lets the library choose).
+    (PATH_FOUR, PATH_THREE, PATH_CHAINED; PATH_AUTO lets the library choose).
     Runs on torch's current stream.
     """
     import torch

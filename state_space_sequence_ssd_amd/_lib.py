@@ -10,8 +10,8 @@ F32 = 0
 BF16 = 1
 DT_HEAD_MAJOR = 0x100   # OR-ed into io: dt given as [batch, nheads, seqlen]
 # kernel sequence, a field OR-ed into io (see include/mamba2_ssd.h)
-PATH_AUTO, PATH_FOUR, PATH_THREE, PATH_CHAINED, PATH_LOOKBACK = 0x0000, 0x1000, 0x2000, 0x3000, 0x4000
-PATH_NAMES = {PATH_FOUR: "four", PATH_THREE: "three", PATH_CHAINED: "chained", PATH_LOOKBACK: "lookback"}
+PATH_AUTO, PATH_FOUR, PATH_THREE, PATH_CHAINED = 0x0000, 0x1000, 0x2000, 0x3000
+PATH_NAMES = {PATH_FOUR: "four", PATH_THREE: "three", PATH_CHAINED: "chained"}
 NOALLOC_MAX_WORKSPACE = 64 << 20   # MAMBA2_SSD_NOALLOC_MAX_WORKSPACE
 
 STATUS = {

@@ -1,17 +1,15 @@
-// Device helpers shared by the kernels that hand the carried state from chunk
-// to chunk through memory (ssd_chunk_chained, ssd_state_lookback): direct
-// global->LDS loads, wave-uniform buffer resources, the progress flags of the
-// hand-off, and the piece swizzle of the B tile in LDS.
+// Device helpers of the kernel that hands the carried state from chunk to
+// chunk through memory (ssd_chunk_chained): direct global->LDS loads,
+// wave-uniform buffer resources, the progress flags of the hand-off, and the
+// piece swizzle of the B tile in LDS.
 //
 // The hand-off protocol (the blog's "Kernel 2: fwd_pass_state" walks a head's
 // chunks in order inside one program; here the chunks of a head are spread
 // over workgroups, each waiting for its predecessor). Work items ("tickets")
 // are numbered chunk-major and claimed in order from a counter by persistent
 // workgroups. The tile of chunk k of a head stores h_{k+1} with
-// device-coherent stores, waits for them to complete, and then advances the
-// head's progress flag (ssd_chunk_chained sets it to k+1 once the whole
-// state is stored; ssd_state_lookback adds 1 per quarter of the state, so it
-// reaches 4 (k+1)); the tile of chunk k+1 polls that flag with
+// device-coherent stores, waits for them to complete, and then raises the
+// head's progress flag to k+1; the tile of chunk k+1 polls that flag with
 // device-coherent loads and reads the state the same way. A tile waits only
 // on a lower ticket, claimed by a workgroup that is already running and that
 // only waits on lower tickets itself, so every wait ends; the polls are

@@ -36,34 +36,32 @@ bool valid_io(int io) { return io == MAMBA2_SSD_F32 || io == MAMBA2_SSD_BF16; }
 // layout flags above it.
 int io_type(int io_arg) { return io_arg & 0xff; }
 bool valid_io_arg(int io_arg) {
-  return valid_io(io_type(io_arg)) && (io_arg & ~(0xff | MAMBA2_SSD_DT_HEAD_MAJOR | MAMBA2_SSD_PATH_MASK)) == 0 &&
-         (io_arg & MAMBA2_SSD_PATH_MASK) <= MAMBA2_SSD_PATH_LOOKBACK;
+  return valid_io(io_type(io_arg)) && (io_arg & ~(0xff | MAMBA2_SSD_DT_HEAD_MAJOR | MAMBA2_SSD_PATH_MASK)) == 0;
 }
 int path_field(int io_arg) { return io_arg & MAMBA2_SSD_PATH_MASK; }
 size_t io_size(int io_arg) { return io_type(io_arg) == MAMBA2_SSD_BF16 ? 2 : 4; }
 
 struct Sizes {
-  int path = 0;                  // MAMBA2_SSD_PATH_FOUR, _THREE, _CHAINED or _LOOKBACK
+  int path = 0;                  // MAMBA2_SSD_PATH_FOUR, _THREE or _CHAINED
   int64_t nc = 0, Tp = 0;
   int64_t n_x = 0, n_dt = 0, n_bc = 0, n_state = 0, n_chunkstates = 0;
 };
 
-// The kernel sequence a forward call takes (MAMBA2_SSD_PATH_FOUR, _THREE,
-// _CHAINED or _LOOKBACK), or 0 when the path field of io_arg asks for one
-// that does not support the shape. Automatic choice: the look-back state
-// kernel wherever it supports the shape; otherwise the chunk states inside
-// the state pass when the (batch, head, dstate group) walks alone fill the
-// GPU (chunk_state_pass_pays); otherwise the four kernels.
-constexpr bool kAutoLookback = false;
+// The kernel sequence a forward call takes (MAMBA2_SSD_PATH_FOUR, _THREE or
+// _CHAINED), or 0 when the path field of io_arg asks for one that does not
+// support the shape. Automatic choice: the chained kernel wherever it
+// supports the shape; otherwise the chunk states inside the state pass when
+// the (batch, head, dstate group) walks alone fill the GPU
+// (chunk_state_pass_pays); otherwise the four kernels.
+constexpr bool kAutoChained = false;
 int choose_path(const ssd::Problem& p, int io_arg) {
   switch (path_field(io_arg)) {
     case MAMBA2_SSD_PATH_FOUR: return MAMBA2_SSD_PATH_FOUR;
     case MAMBA2_SSD_PATH_THREE: return ssd::chunk_state_pass_fits(p) ? MAMBA2_SSD_PATH_THREE : 0;
     case MAMBA2_SSD_PATH_CHAINED: return ssd::chunk_chained_fits(p) ? MAMBA2_SSD_PATH_CHAINED : 0;
-    case MAMBA2_SSD_PATH_LOOKBACK: return ssd::state_lookback_fits(p) ? MAMBA2_SSD_PATH_LOOKBACK : 0;
     default: break;
   }
-  if (kAutoLookback && ssd::state_lookback_fits(p)) return MAMBA2_SSD_PATH_LOOKBACK;
+  if (kAutoChained && ssd::chunk_chained_fits(p)) return MAMBA2_SSD_PATH_CHAINED;
   if (ssd::chunk_state_pass_fits(p) && ssd::chunk_state_pass_pays(p)) return MAMBA2_SSD_PATH_THREE;
   return MAMBA2_SSD_PATH_FOUR;
 }
@@ -121,22 +119,21 @@ int check_dims(const mamba2_ssd_dims* d, int io_arg, Sizes* s) {
 void layout_of(const mamba2_ssd_dims* d, const Sizes& s, mamba2_ssd_workspace_layout* L) {
   const size_t bh = (size_t)d->batch * (size_t)d->nheads;
   const bool four = s.path == MAMBA2_SSD_PATH_FOUR, chained = s.path == MAMBA2_SSD_PATH_CHAINED;
-  const bool handoff = chained || s.path == MAMBA2_SSD_PATH_LOOKBACK;   // slots and flags
   size_t off = 0;
   L->gcum_offset = off;
   off = align_up(off + bh * (size_t)s.Tp * 4);
   L->dtt_offset = off;
   off = align_up(off + bh * (size_t)s.Tp * 4);
   L->wst_offset = off;
-  if (!handoff) off = align_up(off + bh * (size_t)s.Tp * 4);   // the hand-off kernels form w themselves
+  if (!chained) off = align_up(off + bh * (size_t)s.Tp * 4);   // the chained kernel forms w itself
   L->states_offset = off;
   if (four) off = align_up(off + (size_t)s.n_chunkstates * 4);
   L->hprev_offset = off;
   if (!chained) off = align_up(off + (size_t)s.n_chunkstates * 4);
   L->chain_offset = off;
-  if (handoff) off = align_up(off + (size_t)s.n_state * 4);
+  if (chained) off = align_up(off + (size_t)s.n_state * 4);
   L->sync_offset = off;
-  if (handoff) off = align_up(off + (bh + 64) * 4);
+  if (chained) off = align_up(off + (bh + 64) * 4);
   L->total_bytes = off;
   L->nchunks = s.nc;
   L->path = s.path;
@@ -256,11 +253,11 @@ int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* d, int io, const void* x, const 
   p.wst = reinterpret_cast<float*>(ws + L.wst_offset);
   p.states = reinterpret_cast<float*>(ws + L.states_offset);
   p.hprev = ws + L.hprev_offset;
-  const bool handoff = s.path == MAMBA2_SSD_PATH_CHAINED || s.path == MAMBA2_SSD_PATH_LOOKBACK;
-  if (handoff) p.wst = nullptr;
-  p.chain = handoff ? reinterpret_cast<float*>(ws + L.chain_offset) : nullptr;
-  p.sync = handoff ? reinterpret_cast<int*>(ws + L.sync_offset) : nullptr;
-  p.nsync = handoff ? (int)(d->batch * d->nheads + 64) : 0;
+  const bool chained = s.path == MAMBA2_SSD_PATH_CHAINED;
+  if (chained) p.wst = nullptr;
+  p.chain = chained ? reinterpret_cast<float*>(ws + L.chain_offset) : nullptr;
+  p.sync = chained ? reinterpret_cast<int*>(ws + L.sync_offset) : nullptr;
+  p.nsync = chained ? (int)(d->batch * d->nheads + 64) : 0;
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
   hipError_t err = hipSuccess;
@@ -276,13 +273,6 @@ int mamba2_ssd_fwd_timed(const mamba2_ssd_dims* d, int io, const void* x, const 
       if (err == hipSuccess) err = ssd::launch_chunk_chained(p, hs);
       mark(2);
       mark(3);
-      break;
-    case MAMBA2_SSD_PATH_LOOKBACK:
-      // chunk states and the pass by the look-back kernel: events 1..2 enclose it
-      if (err == hipSuccess) err = ssd::launch_state_lookback(p, hs);
-      mark(2);
-      mark(3);
-      if (err == hipSuccess && s.nc > 0) err = ssd::launch_chunk_scan(p, hs);
       break;
     case MAMBA2_SSD_PATH_THREE:
       // chunk states and the pass in one kernel: events 1..2 enclose it

@@ -26,8 +26,8 @@ struct Problem {
   float* wst;                    // workspace: [bt][H][Tp]
   float* states;                 // workspace: [bt][H][nc][P][N]
   void* hprev;                   // workspace: [bt][H][nc][P][N] fp32, or bf16 (hi, lo) pairs
-  float* chain;                  // workspace (hand-off paths): [bt][H][P][N] carried state slots
-  int* sync;                     // workspace (hand-off paths): ticket counter, error word, flags per (bt, H)
+  float* chain;                  // workspace (chained path): [bt][H][P][N] carried state slots
+  int* sync;                     // workspace (chained path): ticket counter, error word, flags per (bt, H)
   int nsync;                     // int32 words of sync (0 = none); ssd_chunk_cumsum clears them
 };
 
@@ -61,11 +61,6 @@ hipError_t launch_chunk_state_pass(const Problem& p, hipStream_t stream);
 // its counters.
 bool chunk_chained_fits(const Problem& p);
 hipError_t launch_chunk_chained(const Problem& p, hipStream_t stream);
-// Chunk states and the pass, each chunk's tile on any workgroup, the carried
-// state handed from chunk to chunk through memory (state_lookback.hip); it
-// writes hprev as bf16 (hi, lo) pairs. The cumsum kernel clears its counters.
-bool state_lookback_fits(const Problem& p);
-hipError_t launch_state_lookback(const Problem& p, hipStream_t stream);
 // The C.B^T-resident scan (chunk_scan_resident.hip) and the shapes it takes.
 bool chunk_scan_resident_fits(const Problem& p);
 hipError_t launch_chunk_scan_resident(const Problem& p, hipStream_t stream);

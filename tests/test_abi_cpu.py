@@ -89,12 +89,6 @@ def test_workspace_layout_headline():
     assert ch.sync_offset == ch.chain_offset + 4 * 80 * 64 * 128 * 4
     assert ch.total_bytes == ch.sync_offset + ((4 * 80 + 64) * 4 + 255) // 256 * 256
     assert ch.total_bytes <= ssd.NOALLOC_MAX_WORKSPACE     # the headline fits the no-allocation entry point
-    lb = ssd.workspace_layout(HEADLINE, BF16 | ssd.PATH_LOOKBACK)
-    assert lb.path == ssd.PATH_LOOKBACK
-    assert lb.wst_offset == lb.states_offset == lb.hprev_offset == 2 * gq      # no w, no S
-    assert lb.chain_offset == lb.hprev_offset + states
-    assert lb.sync_offset == lb.chain_offset + 4 * 80 * 64 * 128 * 4
-    assert lb.total_bytes == lb.sync_offset + ((4 * 80 + 64) * 4 + 255) // 256 * 256
 
 
 def test_path_field():
@@ -117,14 +111,6 @@ def test_path_field():
                   (Dims(4, 8192, 80, 64, 256, 1, 256), BF16), (Dims(4, 8192, 80, 64, 128, 1, 128), BF16)):
         assert _check(d, io | ssd.PATH_CHAINED) == UNSUP    # fp32; headdim 128; dstate 256; chunk 128
     assert ssd.fwd_path(Dims(8, 2048, 24, 64, 128, 1, 256), BF16 | ssd.PATH_FOUR) == ssd.PATH_FOUR
-    assert ssd.fwd_path(HEADLINE, BF16 | ssd.PATH_LOOKBACK) == ssd.PATH_LOOKBACK
-    assert ssd.fwd_path(Dims(1, 300, 6, 64, 64, 3, 256), BF16 | ssd.PATH_LOOKBACK) == ssd.PATH_LOOKBACK
-    for d, io in ((HEADLINE, F32), (Dims(4, 8192, 80, 128, 128, 1, 256), BF16),
-                  (Dims(4, 8192, 80, 64, 256, 1, 256), BF16), (Dims(4, 8192, 80, 64, 128, 1, 128), BF16),
-                  (Dims(1, 300, 3, 64, 64, 1, 256), BF16), (Dims(1, 300, 6, 64, 64, 2, 256), BF16)):
-        assert _check(d, io | ssd.PATH_LOOKBACK) == UNSUP   # ...; odd heads per group (3, 3)
-    for bad in (0x5000, 0x6000, 0x7000):                    # path field values with no sequence
-        assert _check(SMALL, BF16 | bad) == UNSUP
 
 
 def test_alignment():

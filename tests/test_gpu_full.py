@@ -31,12 +31,10 @@ def _inputs(name):
 
 
 CHAINED_OK = [c for c in CONFIGS if c.io == "bf16" and c.headdim == 64 and c.chunk == 256 and c.dstate <= 128]
-LOOKBACK_OK = [c for c in CHAINED_OK if (c.nheads // c.ngroups) % 2 == 0]
-CASES = ([(c, 0, c.name) for c in CONFIGS] + [(c, ssd.PATH_CHAINED, c.name + "-chained") for c in CHAINED_OK] +
-         [(c, ssd.PATH_LOOKBACK, c.name + "-lookback") for c in LOOKBACK_OK])
 
 
-@pytest.mark.parametrize("cfg,path", [c[:2] for c in CASES], ids=[c[2] for c in CASES])
+@pytest.mark.parametrize("cfg,path", [(c, 0) for c in CONFIGS] + [(c, ssd.PATH_CHAINED) for c in CHAINED_OK],
+                         ids=[c.name for c in CONFIGS] + [c.name + "-chained" for c in CHAINED_OK])
 def test_full_config_every_head(cfg, path):
     log(f"[full] {cfg.name}: generating inputs")
     cfg, inp = _inputs(cfg.name)

@@ -406,76 +406,6 @@ def test_chained_in_place_and_no_final():
     check_close(host(y2), yr, cfg.io, "y (chained, no final)")
 
 
-# ------------------------------- states and pass by the look-back kernel
-# (bf16, headdim 64, chunk 256, dstate 64/128, an even number of heads per
-# group: the LOOKBACK sequence, whose scan is the resident one). hprev, y and
-# final_state are checked against the oracle and against the FOUR sequence;
-# the error word must stay 0. "four-per-ticket" is large enough for the
-# launcher to give each ticket four heads (two rounds per B tile); the others
-# take two.
-LOOKBACK = {
-    "ragged-init": dict(batch=2, seqlen=3 * 256 + 13, nheads=6, init_sigma=0.3),
-    "one-chunk": dict(batch=3, seqlen=100, nheads=2),
-    "N64-groups": dict(batch=1, seqlen=5 * 256 + 1, nheads=8, dstate=64, ngroups=2, init_sigma=0.2),
-    "exact-chunks": dict(batch=2, seqlen=4 * 256, nheads=6),
-    "long-walk": dict(batch=1, seqlen=40 * 256 + 77, nheads=2, init_sigma=0.1),
-    "many-heads": dict(batch=2, seqlen=6 * 256, nheads=48, init_sigma=0.1),
-    "four-per-ticket": dict(batch=4, seqlen=64 * 256 - 5, nheads=16, init_sigma=0.1),
-}
-
-
-@pytest.mark.parametrize("name", sorted(LOOKBACK))
-def test_lookback_sequence(name):
-    cfg = LayerConfig(f"lookback-{name}", **{**dict(headdim=64, dstate=128, ngroups=1, chunk=256, io="bf16",
-                                                  seed=950 + len(name)), **LOOKBACK[name]})
-    log(f"[lookback] {name}: {cfg}")
-    inp = generate(cfg)
-    yr, fr, inter = oracle_all(inp, cfg, intermediates=True)
-    dev = to_device(inp, cfg.io)
-    y, fin, ws, L, dims = run(dev, cfg.chunk, keep_workspace=True, path=ssd.PATH_LOOKBACK)
-    assert L.path == ssd.PATH_LOOKBACK and ssd.fused_state_pass(dims, 1 | ssd.PATH_LOOKBACK)
-    assert L.wst_offset == L.states_offset == L.hprev_offset   # no w or per-chunk states regions
-    assert _sync_error_word(ws, L) == 0, "a wait for the previous chunk's state hit its bound"
-    v = workspace_views(ws, L, dims, 1)
-    log("  " + check_close(host(v["hprev"]), inter["hprev"], cfg.io, "hprev (lookback)"))
-    log("  " + check_close(host(y), yr, cfg.io, "y (lookback)"))
-    log("  " + check_close(host(fin), fr, cfg.io, "final_state (lookback)"))
-    y4, f4, ws4, L4, _ = run(dev, cfg.chunk, keep_workspace=True, path=ssd.PATH_FOUR)
-    v4 = workspace_views(ws4, L4, dims, 1)
-    for what, a1, a2, tol in (("hprev", v["hprev"], v4["hprev"], HPREV_PAIR_TOL), ("final_state", fin, f4, 1e-5)):
-        a1, a2 = host(a1), host(a2)
-        rel = float(np.max(np.abs(a1 - a2))) / max(float(np.max(np.abs(a2))), 1e-30)
-        assert rel <= tol, f"{what}: LOOKBACK and FOUR differ by {rel:.2e} (normwise)"
-    yy, y4h = host(y), host(y4)
-    diff = np.abs(yy - y4h)
-    bound = 2.0 ** -7 * np.abs(y4h) + 1e-5 * float(np.max(np.abs(y4h)))
-    i = np.unravel_index(int(np.argmax(diff / bound)), diff.shape)
-    assert np.all(diff <= bound), (f"y: LOOKBACK and FOUR differ beyond one bf16 ulp: worst at {i}: "
-                                   f"{yy[i]:.6g} vs {y4h[i]:.6g} (max|y| {float(np.max(np.abs(y4h))):.3g})")
-    y2, f2 = run(dev, cfg.chunk, path=ssd.PATH_LOOKBACK)
-    assert torch.equal(y, y2) and torch.equal(fin, f2), "two identical calls must give identical results"
-
-
-def test_lookback_in_place_and_no_final():
-    cfg = LayerConfig("lookback-inplace", batch=2, seqlen=2 * 256 + 40, nheads=4, headdim=64, dstate=128,
-                      ngroups=1, chunk=256, io="bf16", seed=961, init_sigma=0.3)
-    inp = generate(cfg)
-    yr, fr = oracle_all(inp, cfg)
-    dev = to_device(inp, cfg.io)
-    st = dev["init_state"].clone()
-    y, fin = ssd.ssd_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], cfg.chunk, st,
-                         final_state=st, path=ssd.PATH_LOOKBACK)
-    torch.cuda.synchronize()
-    assert fin.data_ptr() == st.data_ptr()
-    check_close(host(st), fr, cfg.io, "final_state in place (lookback)")
-    check_close(host(y), yr, cfg.io, "y (lookback, in place)")
-    y2, none = ssd.ssd_fwd(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], cfg.chunk,
-                           dev["init_state"], return_final_state=False, path=ssd.PATH_LOOKBACK)
-    torch.cuda.synchronize()
-    assert none is None
-    check_close(host(y2), yr, cfg.io, "y (lookback, no final)")
-
-
 # ------------------------------------------------------------ dt layouts
 
 DT_LAYOUT = {
