@@ -402,7 +402,7 @@ def run_s6(args, cfg):
         "data": "synthetic",
         "config": {"workload": cfg.name, "batch": Bt, "seqlen": L, "channels": D, "dstate": N,
                    "recipe": cfg.recipe, "seed": cfg.seed, "tokens_per_step": cfg.tokens},
-        "roofline": {"bound": "hbm", "kernel": "mamba1_s6_fwd (chunk scan, carry, chunk scan)",
+        "roofline": {"bound": "hbm", "kernel": "mamba1_s6_fwd (s6_clear, s6_onepass)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
         "gpu_event_us_per_step": round(us, 2),

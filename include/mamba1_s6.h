@@ -21,10 +21,13 @@
  *   h0, hT        [batch][channels][dstate]
  * delta >= 0 and A < 0 are documented preconditions, not checked on device.
  *
- * The scan runs chunk-parallel (chunks of 64 tokens: each chunk's own scan,
- * a carry pass over the chunk boundaries, then each chunk again from its
- * entering state), through a caller-provided workspace of
- * mamba1_s6_workspace_bytes(dims) bytes. Status codes are the MAMBA2_SSD_*
+ * The scan runs chunk-parallel in one pass over x and delta (chunks of 64
+ * tokens: each chunk's own scan from a zero state, its entering state from
+ * the summaries the earlier chunks publish, then the chunk again from that
+ * state), through a caller-provided workspace of
+ * mamba1_s6_workspace_bytes(dims) bytes that holds those summaries and the
+ * chunks' progress flags (cleared by the call itself). Two calls that share
+ * a workspace must not overlap in time. Status codes are the MAMBA2_SSD_*
  * values of mamba2_ssd.h; validation runs on the host before any launch and
  * the call is asynchronous on `stream`.
  */

@@ -14,7 +14,7 @@ constexpr int64_t kMaxDimS6 = (int64_t)1 << 40;
 
 struct S6Sizes {
   int64_t nc = 0, n_x = 0, n_bc = 0, n_state = 0;
-  size_t off_sumd = 0, off_hin = 0, total = 0;
+  size_t off_sumd = 0, off_incl = 0, off_sync = 0, total = 0;
 };
 
 size_t align_up(size_t v) { return (v + 255) / 256 * 256; }
@@ -41,9 +41,11 @@ int s6_sizes(const mamba1_s6_dims* d, S6Sizes* s) {
   if (!mul_ok(bd, d->dstate, &r.n_state)) return MAMBA2_SSD_ERR_BAD_DIM;
   int64_t ns, nsum;
   if (!mul_ok(r.n_state, r.nc, &ns) || !mul_ok(bd, r.nc, &nsum) || !mul_ok(ns, 8, &t)) return MAMBA2_SSD_ERR_BAD_DIM;
+  const int64_t nsync = ssd::s6_sync_words(d->batch, d->channels, d->seqlen);
   r.off_sumd = align_up((size_t)ns * 4);
-  r.off_hin = r.off_sumd + align_up((size_t)nsum * 4);
-  r.total = r.off_hin + align_up((size_t)ns * 4);
+  r.off_incl = r.off_sumd + align_up((size_t)nsum * 4);
+  r.off_sync = r.off_incl + align_up((size_t)ns * 4);
+  r.total = r.off_sync + align_up((size_t)nsync * 4);
   *s = r;
   return MAMBA2_SSD_OK;
 }
@@ -105,9 +107,10 @@ int mamba1_s6_fwd(const mamba1_s6_dims* d, const float* x, const float* delta, c
   ssd::S6Problem p{};
   p.bt = d->batch; p.L = d->seqlen; p.D = d->channels; p.N = d->dstate;
   p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.h0 = h0; p.y = y; p.hT = hT;
-  p.S = ws ? reinterpret_cast<float*>(ws) : nullptr;
-  p.sumd = ws ? reinterpret_cast<float*>(ws + s.off_sumd) : nullptr;
-  p.hin = ws ? reinterpret_cast<float*>(ws + s.off_hin) : nullptr;
+  p.aggS = ws ? reinterpret_cast<float*>(ws) : nullptr;
+  p.aggD = ws ? reinterpret_cast<float*>(ws + s.off_sumd) : nullptr;
+  p.incl = ws ? reinterpret_cast<float*>(ws + s.off_incl) : nullptr;
+  p.sync = ws ? reinterpret_cast<int*>(ws + s.off_sync) : nullptr;
   const hipError_t err = ssd::launch_s6(p, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? MAMBA2_SSD_OK : MAMBA2_SSD_ERR_HIP;
 }

@@ -6,26 +6,30 @@
 // Layouts: x, delta, y [batch][channels][seqlen]; B, C [batch][dstate][seqlen];
 // A [channels][dstate]; states [batch][channels][dstate]; all fp32.
 //
-// The sequence is cut into chunks of kChunk tokens, scanned in parallel:
-//   s6_chunk<N, false>  each (b, d, chunk) scans its tokens from a zero state:
-//                       the chunk's end state S and its sum of delta;
-//   s6_carry<N>         per (b, d, n), the chunks in order: the state entering
-//                       each chunk, h <- 2^(log2e A sum(delta)) h + S (the
-//                       chunk's decays multiply to exp(A sum(delta))), and
-//                       the final state;
-//   s6_chunk<N, true>   each (b, d, chunk) scans again from its entering
-//                       state and writes y.
-// The "Part 2/3" view of the page is the same: a scan splits into blocks
-// whose summaries combine associatively. A thread owns one channel of one
-// chunk, its N states in registers; a workgroup takes 256 channels of one
-// chunk, so the chunk's B and C rows are staged once in LDS, and each wave
-// stages its 64 channels' x and delta in 16-token column blocks (64-byte row
-// pieces, then each lane walks its own row) and y the same way back, in
-// the x tile (a lane overwrites the x values of its own row it has read).
-// Two column blocks are loaded ahead: the scan itself is short, and one
-// memory round trip per block would set the time; at about 100 registers
-// per lane four waves fit per SIMD, so a 1024-channel, 2048-token, 8-row
-// call runs all its waves at once.
+// The sequence is cut into chunks of kChunk tokens. One kernel, s6_onepass,
+// takes work items ("tickets") (chunk c, batch row b, block of 256 channels),
+// numbered chunk-major and claimed in order by persistent workgroups; a lane
+// owns one channel and holds its chunk's x and delta in registers, so each is
+// read from memory once:
+//   1. the chunk is scanned from a zero state: its end state S and its sum of
+//      delta, published (device-coherent stores, then flag 1 for the block);
+//   2. the state entering the chunk is found by looking back over the earlier
+//      chunks of the same rows: a chunk whose flag is 2 has published its
+//      inclusive end state P and ends the walk; a chunk with flag 1
+//      contributes its S and its decay exp(A sum(delta)) (the chunk's decays
+//      multiply to that) and the walk goes on. The walk never passes chunk 0:
+//      there it waits for flag 2, which chunk 0 raises without waiting on
+//      anything (it alone reads h0, before any inclusive state exists, so hT
+//      may be h0);
+//   3. the inclusive end state is published (flag 2) and the chunk is
+//      scanned again from the entering state, writing y.
+// A tile waits only for flag 1 of lower tickets, which their workgroups
+// raise before they wait on anything, or for flag 2 of chunk 0: every wait
+// ends (the polls are bounded all the same, recording an error word). The
+// "Part 2/3" view of the page is the same: a scan splits into blocks whose
+// summaries combine associatively. A small kernel clears the counter and
+// flags first.
+#include "lookback_device.h"
 #include "ssd_device.h"
 #include "s6_launch.h"
 
@@ -34,203 +38,369 @@ namespace ssd {
 namespace {
 
 constexpr int kChunk = 64;    // tokens per chunk
-constexpr int kSub = 16;      // tokens per staged column block
-constexpr int kWaves = 4;     // waves per workgroup, 64 channels each
+constexpr int kLanes = 256;   // channels per workgroup (4 waves)
+constexpr int kSyncWords = 64;   // sync region head: ticket counter (0-1), error word (2)
+constexpr int kMaxPolls = 1 << 20;
 
-// A lane's share of one wave's 64 rows x kSub tokens of a [rows][L] array:
-// rows 16 i + lane / 4, tokens t + 4 (lane % 4) .. + 3 (zeros past the
-// sequence or the channels).
-__device__ __forceinline__ void load_rows(float4 (&v)[4], const float* src, int64_t row0, int rows_valid,
-                                          int64_t L, int64_t t, int lane, bool vec) {
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int flag_of(const int* f) {
+  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+// wait (the whole wave) until *f >= want; returns the value seen
+__device__ __forceinline__ int wait_flag(const int* f, int want, int* sync) {
+  int v = flag_of(f);
+  for (int polls = 0; v < want; ++polls) {
+    if (polls > kMaxPolls) {
+      __hip_atomic_store(sync + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+    v = flag_of(f);
+  }
+  return v;
+}
+
+__global__ void s6_clear(int* sync, int64_t words) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < words; i += (int64_t)gridDim.x * blockDim.x)
+    sync[i] = 0;
+}
+
+// seqlen 0: the final state is the initial one (or zeros)
+__global__ void s6_pass_state(const float* h0, float* hT, int64_t n) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) hT[i] = h0 ? h0[i] : 0.f;
+}
+
+// A wave's 64 channel rows of one chunk (64 tokens, 256 bytes each) in LDS:
+// 16-byte piece q (tokens 4 q .. 4 q + 3) of row r sits at piece q ^ (r % 16),
+// so both the coalesced transfers (4 whole rows per instruction) and each
+// lane's walk along its own row hit distinct 16-byte bank groups.
+__device__ __forceinline__ uint32_t tile_off(uint32_t r, uint32_t q) { return r * 256 + ((q ^ (r & 15)) << 4); }
+
+// rows [rows0 .. rows0 + 63] of a [rows][L] array, tokens t0 .. t0 + 63, into
+// the wave's tile by direct global->LDS loads (rows at or past `rows_valid`
+// read as zeros; the caller masks tokens past the sequence)
+__device__ __forceinline__ void tile_load(const float* src, int64_t row0, int rows_valid, int64_t L, int64_t t0,
+                                          unsigned char* tile, int lane) {
+  asm volatile("" : "+v"(lane));   // per-lane offsets formed here, not kept live across the ticket
+  const __amdgpu_buffer_rsrc_t r = lookback::urs(src + row0 * L, (uint32_t)((int64_t)rows_valid * L * 4));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = i * 16 + lane / 4, piece = lane % 4;
-    const int64_t tk = t + piece * 4;
-    float e[4] = {0.f, 0.f, 0.f, 0.f};
-    if (r < rows_valid) {
-      const float* p = src + (row0 + r) * L + tk;
-      if (vec && tk + 3 < L) {
-        const float4 q = *reinterpret_cast<const float4*>(p);
-        e[0] = q.x; e[1] = q.y; e[2] = q.z; e[3] = q.w;
-      } else {
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t row = (uint32_t)(4 * i + (lane >> 4)), q = (uint32_t)(lane & 15) ^ (row & 15);
+    lookback::bdma16<false>(r, (uint32_t)(row * L + t0 + 4 * q) * 4, 0, tile + i * 1024);
+  }
+}
+
+// The same with 4-byte loads, for rows that are not 16-byte aligned: lane l
+// takes token t0 + l of each row (zeros past the sequence or the rows).
+__device__ __forceinline__ void tile_load_scalar(const float* src, int64_t row0, int rows_valid, int64_t L,
+                                                 int64_t t0, int nt, unsigned char* tile, int lane) {
+  asm volatile("" : "+v"(lane));
+#pragma unroll 8
+  for (int r = 0; r < 64; ++r) {
+    const float v = (r < rows_valid && lane < nt) ? src[(row0 + r) * L + t0 + lane] : 0.f;
+    *reinterpret_cast<float*>(tile + tile_off((uint32_t)r, (uint32_t)lane >> 2) + (lane & 3) * 4) = v;
+  }
+}
+
+template <int N, bool VEC>
+__global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 ? 1 : 2))) void s6_onepass(const float* __restrict__ x, const float* __restrict__ dl,
+                                                     const float* __restrict__ A, const float* __restrict__ Bm,
+                                                     const float* __restrict__ Cm, const float* h0, float* y,
+                                                     float* hT, float* aggS, float* aggD, float* incl, int* sync,
+                                                     int64_t L, int D, int64_t nc, int64_t ntickets) {
+  __shared__ __attribute__((aligned(16))) float sB[N][kChunk];
+  __shared__ __attribute__((aligned(16))) float sC[N][kChunk];
+  __shared__ __attribute__((aligned(1024))) unsigned char sT[kLanes / 64][64 * 256];   // per wave: x, delta, then y
+  __shared__ int64_t sTicket;
+  const int tid = threadIdx.x;
+  const int wave = tid / 64, lane = tid % 64;
+  unsigned char* const tile = sT[wave];
+  const int ncb = (D + kLanes - 1) / kLanes;
+  const int64_t per = ntickets / nc;   // tickets per chunk = batch rows * channel blocks
+  int* const flags = sync + kSyncWords;
+
+  if (tid == 0) sTicket = __hip_atomic_fetch_add(reinterpret_cast<long long*>(sync), 1LL, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  int64_t ticket = sTicket;
+  while (ticket < ntickets) {
+    const int64_t c = ticket / per;
+    const int64_t u = ticket % per;
+    const int64_t b = u / ncb;
+    const int cb = (int)(u % ncb);
+    const int d = cb * kLanes + tid;
+    const bool valid = d < D;
+    const int64_t t0 = c * kChunk;
+    const int nt = L - t0 < kChunk ? (int)(L - t0) : kChunk;
+
+    for (int idx = tid; idx < N * kChunk; idx += kLanes) {
+      const int n = idx / kChunk, k = idx % kChunk;
+      const int64_t o = (b * N + n) * L + t0 + k;
+      sB[n][k] = k < nt ? Bm[o] : 0.f;
+      sC[n][k] = k < nt ? Cm[o] : 0.f;
+    }
+    // the lane's x and delta (zeros past the sequence or the channels)
+    float xr[kChunk], dr[kChunk];
+    const int64_t wrow0 = b * D + cb * kLanes + wave * 64;   // the wave's first row
+    const int wrows = D - (cb * kLanes + wave * 64);          // its rows inside the array (may be <= 0)
+    {
+      // whole rows through the wave's tile: x, then delta (the tile is the
+      // wave's own, so no workgroup barrier; a direct load has landed in LDS
+      // once vmcnt says so)
+      float* const dst[2] = {xr, dr};
+      const float* const srcs[2] = {x, dl};
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (tk + j < L) e[j] = p[j];
+      for (int a = 0; a < 2; ++a) {
+        if constexpr (VEC) {
+          if (wrows > 0) tile_load(srcs[a], wrow0, wrows < 64 ? wrows : 64, L, t0, tile, lane);
+        } else {
+          tile_load_scalar(srcs[a], wrow0, wrows, L, t0, nt, tile, lane);
+        }
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+#pragma unroll
+        for (int q = 0; q < kChunk / 4; ++q) {
+          const float4 v = *reinterpret_cast<const float4*>(tile + tile_off((uint32_t)ln, (uint32_t)q));
+          // (past the sequence the direct loads read the next row: masked here;
+          // nt is a multiple of 4 on that path)
+          const bool in = !VEC || 4 * q < nt;
+          dst[a][4 * q] = in ? v.x : 0.f;
+          dst[a][4 * q + 1] = in ? v.y : 0.f;
+          dst[a][4 * q + 2] = in ? v.z : 0.f;
+          dst[a][4 * q + 3] = in ? v.w : 0.f;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read out before the tile is refilled
       }
     }
-    v[i] = make_float4(e[0], e[1], e[2], e[3]);
-  }
-}
-// ... and those values into the wave's LDS tile [64 rows][kSub + 1]
-__device__ __forceinline__ void store_rows(float (*dst)[kSub + 1], const float4 (&v)[4], int lane) {
+    float a2[N];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = i * 16 + lane / 4, piece = lane % 4;
-    dst[r][piece * 4 + 0] = v[i].x;
-    dst[r][piece * 4 + 1] = v[i].y;
-    dst[r][piece * 4 + 2] = v[i].z;
-    dst[r][piece * 4 + 3] = v[i].w;
-  }
-}
+    for (int n = 0; n < N; ++n) a2[n] = valid ? A[(int64_t)d * N + n] * kLog2e : 0.f;
+    __syncthreads();   // B and C staged
 
-template <int N, bool FINAL>
-__global__ __launch_bounds__(256) void s6_chunk(const float* __restrict__ x, const float* __restrict__ dl,
-                                                const float* __restrict__ A, const float* __restrict__ Bm,
-                                                const float* __restrict__ Cm, const float* __restrict__ hin,
-                                                float* __restrict__ y, float* __restrict__ S,
-                                                float* __restrict__ sumd, int64_t L, int D, int64_t nc, int vec) {
-  __shared__ __attribute__((aligned(16))) float sB[N][kChunk];
-  __shared__ __attribute__((aligned(16))) float sC[FINAL ? N : 1][kChunk];
-  __shared__ float sx[kWaves][64][kSub + 1];
-  __shared__ float sd[kWaves][64][kSub + 1];
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-  const int64_t b = blockIdx.z, c = blockIdx.y;
-  const int dw = blockIdx.x * 256 + wave * 64;          // the wave's first channel
-  const int d = dw + lane;
-  const bool valid = d < D;
-  const int rows_valid = D - dw;                         // channels of this wave (may be <= 0)
-  const int64_t t0 = c * kChunk;
-  const int nt = L - t0 < kChunk ? (int)(L - t0) : kChunk;
-  const int64_t row0 = b * D + dw;
-  constexpr int NB = kChunk / kSub;
-  // two column blocks in flight: blocks 0 and 1 now, block kb + 2 into the
-  // registers block kb has just left
-  float4 xr[2][4], dr[2][4];
+    // 1. the chunk from a zero state. Past the sequence x, delta, B and C are
+    // zero, so padded tokens leave h unchanged (exp2(0) = 1, no input).
+    float h[N];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    load_rows(xr[kb], x, row0, rows_valid, L, t0 + kb * kSub, lane, vec);
-    load_rows(dr[kb], dl, row0, rows_valid, L, t0 + kb * kSub, lane, vec);
-  }
-
-  for (int idx = tid; idx < N * kChunk; idx += 256) {
-    const int n = idx / kChunk, k = idx % kChunk;
-    const int64_t o = (b * N + n) * L + t0 + k;
-    sB[n][k] = k < nt ? Bm[o] : 0.f;
-    if (FINAL) sC[n][k] = k < nt ? Cm[o] : 0.f;
-  }
-  float a2[N], h[N];
+    for (int n = 0; n < N; ++n) h[n] = 0.f;
+    float dsum = 0.f;
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
-    a2[n] = valid ? A[(int64_t)d * N + n] * kLog2e : 0.f;
-    h[n] = (FINAL && valid) ? hin[(((int64_t)b * D + d) * nc + c) * N + n] : 0.f;
-  }
-  float dsum = 0.f;
-  __syncthreads();   // B and C staged
-  // From here each wave touches only its own tiles, and one wave's LDS
-  // operations complete in program order: no workgroup barrier is needed.
-#pragma unroll
-  for (int kb = 0; kb < NB; ++kb) {
-    const int ks = kb * kSub;
-    if (ks >= nt) break;
-    store_rows(sx[wave], xr[kb & 1], lane);
-    store_rows(sd[wave], dr[kb & 1], lane);
-    if (kb + 2 < NB) {
-      load_rows(xr[kb & 1], x, row0, rows_valid, L, t0 + (kb + 2) * kSub, lane, vec);
-      load_rows(dr[kb & 1], dl, row0, rows_valid, L, t0 + (kb + 2) * kSub, lane, vec);
-    }
-    const int kn = nt - ks < kSub ? nt - ks : kSub;
-    // four tokens at a time: B and C of a state for 4 tokens in one 16-byte
-    // read. Past the sequence x, delta, B and C are zero, so the padded
-    // tokens of the last group leave h unchanged (exp2(0) = 1, no input).
-    for (int k4 = 0; k4 < kn; k4 += 4) {
-      float dv[4], u[4], yv[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int t4 = 0; t4 < kChunk; t4 += 4) {
+      float u[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        dv[j] = sd[wave][lane][k4 + j];
-        u[j] = dv[j] * sx[wave][lane][k4 + j];
-        dsum += dv[j];
+        u[j] = dr[t4 + j] * xr[t4 + j];
+        dsum += dr[t4 + j];
       }
 #pragma unroll
       for (int n = 0; n < N; ++n) {
-        const float4 b4 = *reinterpret_cast<const float4*>(&sB[n][ks + k4]);
+        const float4 b4 = *reinterpret_cast<const float4*>(&sB[n][t4]);
         const float bj[4] = {b4.x, b4.y, b4.z, b4.w};
-        float cj[4] = {0.f, 0.f, 0.f, 0.f};
-        if (FINAL) {
-          const float4 c4 = *reinterpret_cast<const float4*>(&sC[n][ks + k4]);
-          cj[0] = c4.x; cj[1] = c4.y; cj[2] = c4.z; cj[3] = c4.w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[n] = fmaf(exp2_hw(dr[t4 + j] * a2[n]), h[n], u[j] * bj[j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // one group of tokens at a time: bounded live ranges
+    }
+    const int64_t agg = (b * nc + c) * D + d;   // the lane's (b, c, d) record
+    int* const myflag = flags + (b * nc + c) * ncb + cb;
+
+    // 2. the entering state
+    float hin[N];
+    if (c == 0) {
+#pragma unroll
+      for (int n = 0; n < N; ++n) hin[n] = (h0 && valid) ? h0[(b * D + d) * N + n] : 0.f;
+    } else {
+      if (valid) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) st_coherent(aggS + agg * N + n, h[n]);
+        st_coherent(aggD + agg, dsum);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();   // every lane's aggregate is out
+      if (tid == 0) __hip_atomic_store(myflag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // hin = acc + lam * (inclusive state of the chunk where the walk ends)
+      float acc[N], lam[N];
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        acc[n] = 0.f;
+        lam[n] = 1.f;
+      }
+      // (the flag of chunk j - 1 is read together with chunk j's summary: one
+      // round trip per chunk walked)
+      int fseen = flag_of(flags + (b * nc + c - 1) * ncb + cb);
+      for (int64_t j = c - 1;; --j) {
+        const int* fj = flags + (b * nc + j) * ncb + cb;
+        const int want = j == 0 ? 2 : 1;
+        const int f = fseen >= want ? fseen : wait_flag(fj, want, sync);
+        const int64_t o = (b * nc + j) * D + d;
+        if (f >= 2 || j == 0) {   // (at chunk 0 only after a wait that hit its bound is f < 2)
+#pragma unroll
+          for (int n = 0; n < N; ++n) hin[n] = valid ? fmaf(lam[n], ld_coherent(incl + o * N + n), acc[n]) : 0.f;
+          break;
         }
+        float sj[N];
+        const float sd = valid ? ld_coherent(aggD + o) : 0.f;
+#pragma unroll
+        for (int n = 0; n < N; ++n) sj[n] = valid ? ld_coherent(aggS + o * N + n) : 0.f;
+        fseen = flag_of(fj - ncb);   // chunk j - 1 (j >= 1 here)
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+          acc[n] = fmaf(lam[n], sj[n], acc[n]);
+          lam[n] *= exp2_hw(a2[n] * sd);
+        }
+      }
+    }
+    // 3. the inclusive end state, published; hT after the last chunk
+    {
+      const bool last = c + 1 == nc;
+      if (valid) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+          const float hout = fmaf(exp2_hw(a2[n] * dsum), hin[n], h[n]);
+          if (!last) st_coherent(incl + agg * N + n, hout);
+          else if (hT) hT[(b * D + d) * N + n] = hout;
+        }
+      }
+      if (!last) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(myflag, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    // ... and the chunk again from the entering state: y replaces x. (The
+    // decays are recomputed: kept from the first scan they would take 64 N
+    // registers per lane, so the operands are laundered to stop the compiler
+    // from keeping them.)
+#pragma unroll
+    for (int t = 0; t < kChunk; ++t) asm volatile("" : "+v"(dr[t]));
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      asm volatile("" : "+v"(a2[n]));
+      h[n] = hin[n];
+    }
+#pragma unroll
+    for (int t4 = 0; t4 < kChunk; t4 += 4) {
+      float u[4], yv[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) u[j] = dr[t4 + j] * xr[t4 + j];
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        const float4 b4 = *reinterpret_cast<const float4*>(&sB[n][t4]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&sC[n][t4]);
+        const float bj[4] = {b4.x, b4.y, b4.z, b4.w}, cj[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          h[n] = fmaf(exp2_hw(dv[j] * a2[n]), h[n], u[j] * bj[j]);
-          if (FINAL) yv[j] = fmaf(cj[j], h[n], yv[j]);
+          h[n] = fmaf(exp2_hw(dr[t4 + j] * a2[n]), h[n], u[j] * bj[j]);
+          yv[j] = fmaf(cj[j], h[n], yv[j]);
         }
       }
-      if (FINAL) {
-        // y replaces x in the lane's own row: those x values are read above
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sx[wave][lane][k4 + j] = yv[j];
-      }
+      for (int j = 0; j < 4; ++j) xr[t4 + j] = yv[j];
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (FINAL) {
+    {
+      // through the tile: each lane writes its row, then whole rows go out
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = i * 16 + lane / 4, piece = lane % 4;
-        if (r >= rows_valid) continue;
-        float* p = y + (row0 + r) * L + t0 + ks + piece * 4;
-        if (vec && piece * 4 + 3 < kn) {
-          *reinterpret_cast<float4*>(p) = make_float4(sx[wave][r][piece * 4], sx[wave][r][piece * 4 + 1],
-                                                      sx[wave][r][piece * 4 + 2], sx[wave][r][piece * 4 + 3]);
-        } else {
+      for (int q = 0; q < kChunk / 4; ++q)
+        *reinterpret_cast<float4*>(tile + tile_off((uint32_t)ln, (uint32_t)q)) =
+            make_float4(xr[4 * q], xr[4 * q + 1], xr[4 * q + 2], xr[4 * q + 3]);
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (!VEC) {
+        // lane l stores token t0 + l of each row
+#pragma unroll 8
+        for (int r = 0; r < 64; ++r) {
+          const float v = *reinterpret_cast<const float*>(tile + tile_off((uint32_t)r, (uint32_t)ln >> 2) + (ln & 3) * 4);
+          if (r < wrows && ln < nt) y[(wrow0 + r) * L + t0 + ln] = v;
+        }
+      } else if (wrows > 0) {
+        const __amdgpu_buffer_rsrc_t ry =
+            lookback::urs(y + wrow0 * L, (uint32_t)((int64_t)(wrows < 64 ? wrows : 64) * L * 4));
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (piece * 4 + j < kn) p[j] = sx[wave][r][piece * 4 + j];
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t r = (uint32_t)(4 * i + (ln >> 4)), q = (uint32_t)(ln & 15) ^ (r & 15);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * 256 + ((uint32_t)(ln & 15) << 4));
+          if ((int)(4 * q) < nt) __builtin_amdgcn_raw_buffer_store_b128(v, ry, (r * (uint32_t)L + (uint32_t)t0 + 4 * q) * 4, 0, 0);
         }
       }
     }
-  }
-  if (!FINAL && valid) {
-    const int64_t o = ((int64_t)b * D + d) * nc + c;
-#pragma unroll
-    for (int n = 0; n < N; ++n) S[o * N + n] = h[n];
-    sumd[o] = dsum;
+    // the next ticket (the B, C tiles are free once every lane is past them)
+    __syncthreads();
+    if (tid == 0) sTicket = __hip_atomic_fetch_add(reinterpret_cast<long long*>(sync), 1LL, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    ticket = sTicket;
   }
 }
 
-// per (b, d, n): the state entering every chunk, and the final state
-template <int N>
-__global__ void s6_carry(const float* __restrict__ A, const float* __restrict__ S, const float* __restrict__ sumd,
-                         const float* __restrict__ h0, float* __restrict__ hin, float* __restrict__ hT, int64_t rows,
-                         int D, int64_t nc) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;   // (b * D + d) * N + n
-  if (i >= rows * N) return;
-  const int64_t bd = i / N;
-  const int n = (int)(i % N), d = (int)(bd % D);
-  const float a2 = A[(int64_t)d * N + n] * kLog2e;
-  float h = h0 ? h0[i] : 0.f;
-  for (int64_t c = 0; c < nc; ++c) {
-    const int64_t o = bd * nc + c;
-    hin[o * N + n] = h;
-    h = fmaf(exp2_hw(a2 * sumd[o]), h, S[o * N + n]);
+template <int N, bool VEC>
+int onepass_slots() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    dev = 0;
   }
-  if (hT) hT[i] = h;
+  if (!cached[dev]) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, s6_onepass<N, VEC>, kLanes, 0) != hipSuccess || cus <= 0 ||
+        per_cu <= 0) {
+      (void)hipGetLastError();
+      cus = 256;
+      per_cu = 1;
+    }
+    cached[dev] = cus * per_cu;
+  }
+  return cached[dev];
 }
 
 template <int N>
 hipError_t launch_n(const S6Problem& p, hipStream_t s) {
   const int64_t nc = (p.L + kChunk - 1) / kChunk;
   const int64_t rows = p.bt * p.D;
-  // 16-byte row pieces of x, delta and y when every row starts 16-byte aligned
-  const int vec = (p.L % 4 == 0 && (reinterpret_cast<uintptr_t>(p.x) & 15) == 0 &&
+  if (rows == 0) return hipSuccess;
+  if (nc == 0) {
+    if (p.hT && p.hT != p.h0) {
+      const int64_t n = rows * N;
+      hipLaunchKernelGGL(s6_pass_state, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p.h0, p.hT, n);
+    }
+    return hipGetLastError();
+  }
+  // whole 16-byte pieces of x, delta and y through LDS when every row starts
+  // 16-byte aligned (and 64 rows of one array stay below 2 GB of offsets)
+  const int vec = (p.L % 4 == 0 && p.L <= ((int64_t)1 << 22) && (reinterpret_cast<uintptr_t>(p.x) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(p.delta) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(p.y) & 15) == 0) ? 1 : 0;
-  const dim3 grid((unsigned)((p.D + 255) / 256), (unsigned)nc, (unsigned)p.bt);
-  if (nc > 0 && rows > 0) {
-    hipLaunchKernelGGL((s6_chunk<N, false>), grid, dim3(256), 0, s, p.x, p.delta, p.A, p.B, p.C,
-                       (const float*)nullptr, (float*)nullptr, p.S, p.sumd, p.L, (int)p.D, nc, vec);
-  }
-  if (rows > 0) {
-    const int64_t threads = rows * N;
-    hipLaunchKernelGGL((s6_carry<N>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p.A, p.S, p.sumd,
-                       p.h0, p.hin, p.hT, rows, (int)p.D, nc);
-  }
-  if (nc > 0 && rows > 0) {
-    hipLaunchKernelGGL((s6_chunk<N, true>), grid, dim3(256), 0, s, p.x, p.delta, p.A, p.B, p.C, p.hin, p.y,
-                       (float*)nullptr, (float*)nullptr, p.L, (int)p.D, nc, vec);
-  }
+  const int64_t ncb = (p.D + kLanes - 1) / kLanes;
+  const int64_t ntickets = nc * p.bt * ncb;
+  const int64_t words = kSyncWords + ntickets;
+  const int64_t cblocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
+  hipLaunchKernelGGL(s6_clear, dim3((unsigned)cblocks), dim3(256), 0, s, p.sync, words);
+  const int slots = vec ? onepass_slots<N, true>() : onepass_slots<N, false>();
+  const int64_t grid = ntickets < slots ? ntickets : slots;
+  if (vec)
+    hipLaunchKernelGGL((s6_onepass<N, true>), dim3((unsigned)grid), dim3(kLanes), 0, s, p.x, p.delta, p.A, p.B, p.C,
+                       p.h0, p.y, p.hT, p.aggS, p.aggD, p.incl, p.sync, p.L, (int)p.D, nc, ntickets);
+  else
+    hipLaunchKernelGGL((s6_onepass<N, false>), dim3((unsigned)grid), dim3(kLanes), 0, s, p.x, p.delta, p.A, p.B, p.C,
+                       p.h0, p.y, p.hT, p.aggS, p.aggD, p.incl, p.sync, p.L, (int)p.D, nc, ntickets);
   return hipGetLastError();
 }
 
 }  // namespace
+
+int64_t s6_sync_words(int64_t bt, int64_t D, int64_t L) {
+  const int64_t nc = (L + kChunk - 1) / kChunk;
+  return kSyncWords + nc * bt * ((D + kLanes - 1) / kLanes);
+}
 
 int64_t s6_chunk_tokens() { return kChunk; }
 

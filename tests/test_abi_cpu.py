@@ -476,9 +476,12 @@ def _s6_check(d, **over):
 
 def test_s6_supported_and_workspace():
     assert [n for n in range(1, 33) if ssd.s6_supported(n)] == [1, 2, 4, 8, 16]
-    # per (b, d, chunk): the chunk's end state and entering state (N floats each) and its delta sum
+    # per (b, chunk, d): the chunk's end state from zero and its inclusive end
+    # state (N floats each) and its delta sum; then 64 sync words and one
+    # flag per (b, chunk, block of 256 channels)
     nc = (300 + 63) // 64
-    want = sum((n * 4 + 255) // 256 * 256 for n in (2 * 96 * nc * 16, 2 * 96 * nc, 2 * 96 * nc * 16))
+    want = sum((n * 4 + 255) // 256 * 256
+               for n in (2 * 96 * nc * 16, 2 * 96 * nc, 2 * 96 * nc * 16, 64 + nc * 2 * 1))
     assert ssd.s6_workspace_bytes(S6_SMALL) == want
 
 
