@@ -42,12 +42,42 @@ constexpr int kLanes = 256;   // channels per workgroup (4 waves)
 constexpr int kSyncWords = 64;   // sync region head: ticket counter (0-1), error word (2)
 constexpr int kMaxPolls = 1 << 20;
 
-__device__ __forceinline__ float ld_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// A lane's N-float chunk summary (N consecutive floats at byte `off` of a
+// wave-uniform resource), stored or loaded device-coherent in 16-, 8- or
+// 4-byte pieces, so the writes through to memory are whole lines per wave.
+template <int N>
+__device__ __forceinline__ void st_state(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* v) {
+  if constexpr (N == 1) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, off, 0, 16);
+  } else if constexpr (N == 2) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(v[0]), __float_as_uint(v[1])}, r, off, 0, 16);
+  } else {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q)
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[4 * q]), __float_as_uint(v[4 * q + 1]),
+                                                   __float_as_uint(v[4 * q + 2]), __float_as_uint(v[4 * q + 3])},
+                                             r, off + 16 * q, 0, 16);
+  }
 }
-__device__ __forceinline__ void st_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+template <int N>
+__device__ __forceinline__ void ld_state(__amdgpu_buffer_rsrc_t r, uint32_t off, float* v) {
+  if constexpr (N == 1) {
+    v[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 16));
+  } else if constexpr (N == 2) {
+    const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 16);
+    v[0] = __uint_as_float(w[0]);
+    v[1] = __uint_as_float(w[1]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16 * q, 0, 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * q + e] = __uint_as_float(w[e]);
+    }
+  }
 }
+
 __device__ __forceinline__ int flag_of(const int* f) {
   return __builtin_amdgcn_readfirstlane(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
@@ -207,7 +237,6 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
       }
       __builtin_amdgcn_sched_barrier(0);   // one group of tokens at a time: bounded live ranges
     }
-    const int64_t agg = (b * nc + c) * D + d;   // the lane's (b, c, d) record
     int* const myflag = flags + (b * nc + c) * ncb + cb;
 
     // 2. the entering state
@@ -216,10 +245,12 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
 #pragma unroll
       for (int n = 0; n < N; ++n) hin[n] = (h0 && valid) ? h0[(b * D + d) * N + n] : 0.f;
     } else {
-      if (valid) {
-#pragma unroll
-        for (int n = 0; n < N; ++n) st_coherent(aggS + agg * N + n, h[n]);
-        st_coherent(aggD + agg, dsum);
+      {
+        // the workgroup's 256 records (those of channels past D are dropped)
+        const int64_t rec0 = (b * nc + c) * D + cb * kLanes;
+        const uint32_t nrec = (uint32_t)(D - cb * kLanes < kLanes ? D - cb * kLanes : kLanes);
+        st_state<N>(lookback::urs(aggS + rec0 * N, nrec * N * 4), (uint32_t)tid * N * 4, h);
+        st_state<1>(lookback::urs(aggD + rec0, nrec * 4), (uint32_t)tid * 4, &dsum);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();   // every lane's aggregate is out
@@ -238,16 +269,18 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
         const int* fj = flags + (b * nc + j) * ncb + cb;
         const int want = j == 0 ? 2 : 1;
         const int f = fseen >= want ? fseen : wait_flag(fj, want, sync);
-        const int64_t o = (b * nc + j) * D + d;
+        const int64_t rj = (b * nc + j) * D + cb * kLanes;   // chunk j's records of this block
+        const uint32_t nrec = (uint32_t)(D - cb * kLanes < kLanes ? D - cb * kLanes : kLanes);
         if (f >= 2 || j == 0) {   // (at chunk 0 only after a wait that hit its bound is f < 2)
+          float pj[N];
+          ld_state<N>(lookback::urs(incl + rj * N, nrec * N * 4), (uint32_t)tid * N * 4, pj);
 #pragma unroll
-          for (int n = 0; n < N; ++n) hin[n] = valid ? fmaf(lam[n], ld_coherent(incl + o * N + n), acc[n]) : 0.f;
+          for (int n = 0; n < N; ++n) hin[n] = valid ? fmaf(lam[n], pj[n], acc[n]) : 0.f;
           break;
         }
-        float sj[N];
-        const float sd = valid ? ld_coherent(aggD + o) : 0.f;
-#pragma unroll
-        for (int n = 0; n < N; ++n) sj[n] = valid ? ld_coherent(aggS + o * N + n) : 0.f;
+        float sj[N], sd;
+        ld_state<N>(lookback::urs(aggS + rj * N, nrec * N * 4), (uint32_t)tid * N * 4, sj);
+        ld_state<1>(lookback::urs(aggD + rj, nrec * 4), (uint32_t)tid * 4, &sd);
         fseen = flag_of(fj - ncb);   // chunk j - 1 (j >= 1 here)
 #pragma unroll
         for (int n = 0; n < N; ++n) {
@@ -259,13 +292,16 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
     // 3. the inclusive end state, published; hT after the last chunk
     {
       const bool last = c + 1 == nc;
-      if (valid) {
+      float hout[N];
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-          const float hout = fmaf(exp2_hw(a2[n] * dsum), hin[n], h[n]);
-          if (!last) st_coherent(incl + agg * N + n, hout);
-          else if (hT) hT[(b * D + d) * N + n] = hout;
-        }
+      for (int n = 0; n < N; ++n) hout[n] = fmaf(exp2_hw(a2[n] * dsum), hin[n], h[n]);
+      if (!last) {
+        const int64_t rec0 = (b * nc + c) * D + cb * kLanes;
+        const uint32_t nrec = (uint32_t)(D - cb * kLanes < kLanes ? D - cb * kLanes : kLanes);
+        st_state<N>(lookback::urs(incl + rec0 * N, nrec * N * 4), (uint32_t)tid * N * 4, hout);
+      } else if (hT && valid) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) hT[(b * D + d) * N + n] = hout[n];
       }
       if (!last) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
