@@ -29,10 +29,9 @@ namespace {
 
 // Each thread carries EPT consecutive state elements (EPT = 4 or 8, so one or
 // two 16-byte pieces per chunk) and keeps the S loads of the next DEPTH
-// chunks in flight. The host picks EPT = 8 when that still leaves at least
-// 16 waves per CU, which halves the wave count so every wave of the grid is
-// resident at once (no partial second round of waves, each of which would
-// walk every chunk); smaller problems take EPT = 4 for more parallelism.
+// chunks in flight. The host picks EPT = 8 (half the waves, each walking the
+// chunks with twice the bytes per load) for large problems, EPT = 4 for more
+// parallelism on small ones.
 template <typename T, int EPT>
 __device__ __forceinline__ void store_hprev(void* hp, int64_t chunk_off, int e, const float* h);
 
@@ -95,7 +94,15 @@ __device__ __forceinline__ Piece<EPT> load_piece(const float* p) {
   return r;
 }
 
-template <typename T, int EPT>
+// The jump's decays 2^(G'_last,k) of the (batch, head) go to LDS first (nc
+// floats, one load each by the workgroup's threads), so the walk itself
+// waits only on S. Its steady state is straight-line code with the S loads of
+// chunk k + DEPTH issued unconditionally as chunk k is consumed: with a
+// guarded prefetch the compiler has to assume any load may still be
+// outstanding at the loop head and waits for all of them.
+constexpr int kMaxLdsChunks = 8192;   // chunks per (batch, head) whose decays fit the LDS table
+
+template <typename T, int EPT, bool TABLE>
 __global__ __launch_bounds__(256) void ssd_state_pass(const float* __restrict__ states,
                                                       const float* __restrict__ gcum,
                                                       const float* init,            // may equal final_state
@@ -103,8 +110,13 @@ __global__ __launch_bounds__(256) void ssd_state_pass(const float* __restrict__ 
                                                       float* final_state,
                                                       int nc, int Q, int64_t Tp, int PN) {
   constexpr int DEPTH = 32 / EPT;
+  extern __shared__ float sdec[];   // nc decays
   const int64_t bh = blockIdx.x;
   const int e = (blockIdx.y * 256 + threadIdx.x) * EPT;   // PN is a multiple of 256 * EPT
+
+  const float* glast = gcum + bh * Tp + (Q - 1);
+  if (TABLE)
+    for (int k = threadIdx.x; k < nc; k += 256) sdec[k] = exp2_hw(glast[(int64_t)k * Q]);
 
   Piece<EPT> h;
   if (init) {
@@ -116,24 +128,37 @@ __global__ __launch_bounds__(256) void ssd_state_pass(const float* __restrict__ 
 
   const float* sp = states + bh * (int64_t)nc * PN + e;
   const int64_t hbase = bh * (int64_t)nc * PN;
-  const float* glast = gcum + bh * Tp + (Q - 1);
 
   Piece<EPT> buf[DEPTH];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i)
     if (i < nc) buf[i] = load_piece<EPT>(sp + (int64_t)i * PN);
+  __syncthreads();   // the decay table
 
-  for (int k0 = 0; k0 < nc; k0 += DEPTH) {
+  auto jump = [&](int k, const Piece<EPT>& s) {
+    store_hprev<T, EPT>(hprev, hbase + (int64_t)k * PN, e, h.v);
+    const float sc = TABLE ? sdec[k] : exp2_hw(glast[(int64_t)k * Q]);
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) h.v[j] = fmaf(sc, h.v[j], s.v[j]);
+  };
+  int k0 = 0;
+  for (; k0 + 2 * DEPTH <= nc; k0 += DEPTH) {
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i) {
+      const Piece<EPT> s = buf[i];
+      buf[i] = load_piece<EPT>(sp + (int64_t)(k0 + i + DEPTH) * PN);
+      jump(k0 + i, s);
+    }
+  }
+  // the last DEPTH .. 2 DEPTH - 1 chunks
+  for (; k0 < nc; k0 += DEPTH) {
 #pragma unroll
     for (int i = 0; i < DEPTH; ++i) {
       const int k = k0 + i;
       if (k < nc) {
         const Piece<EPT> s = buf[i];
         if (k + DEPTH < nc) buf[i] = load_piece<EPT>(sp + (int64_t)(k + DEPTH) * PN);
-        store_hprev<T, EPT>(hprev, hbase + (int64_t)k * PN, e, h.v);
-        const float sc = exp2_hw(glast[(int64_t)k * Q]);
-#pragma unroll
-        for (int j = 0; j < EPT; ++j) h.v[j] = fmaf(sc, h.v[j], s.v[j]);
+        jump(k, s);
       }
     }
   }
@@ -149,8 +174,12 @@ template <typename T, int EPT>
 hipError_t launch(const Problem& p, hipStream_t stream) {
   const int PN = (int)(p.P * p.N);
   const dim3 grid((unsigned)(p.bt * p.H), (unsigned)(PN / (256 * EPT)));
-  hipLaunchKernelGGL((ssd_state_pass<T, EPT>), grid, dim3(256), 0, stream, p.states, p.gcum, p.init, p.hprev,
-                     p.final_state, (int)p.nc, (int)p.Q, p.Tp, PN);
+  if (p.nc <= kMaxLdsChunks)
+    hipLaunchKernelGGL((ssd_state_pass<T, EPT, true>), grid, dim3(256), (size_t)p.nc * 4, stream, p.states, p.gcum,
+                       p.init, p.hprev, p.final_state, (int)p.nc, (int)p.Q, p.Tp, PN);
+  else
+    hipLaunchKernelGGL((ssd_state_pass<T, EPT, false>), grid, dim3(256), 0, stream, p.states, p.gcum, p.init,
+                       p.hprev, p.final_state, (int)p.nc, (int)p.Q, p.Tp, PN);
   return hipGetLastError();
 }
 
