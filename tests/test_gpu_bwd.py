@@ -119,26 +119,38 @@ def test_bwd_is_deterministic():
         assert torch.equal(g1[k], g2[k]), f"{k} differs between two identical calls"
 
 
-def test_bwd_headline_sampled_heads():
-    """The 2.7B-like layer at full size, as bench.py --bwd runs it: the
-    per-head gradients (dx, ddt, dinit, dA, dD) of two sampled heads against
-    the oracle run on those heads alone (with one group, dB and dC sum over
-    all 80 heads; they are covered by the smaller cases)."""
+def test_bwd_headline_every_gradient():
+    """The 2.7B-like layer at full size, as bench.py --bwd runs it: every
+    gradient tensor against the oracle, normwise over the whole tensor as in
+    the smaller cases. The oracle runs one batch row at a time (all 80 heads,
+    so dB and dC, which sum over the heads of the group, are complete per
+    row); dA and dD sum over the rows."""
     cfg = config_by_name("mamba2-2.7b").with_shape(init_sigma=0.2)
     log(f"[bwd] headline {cfg}")
     inp = generate(cfg)
     dy, dfin = _upstream(cfg, seed=11)
     g = _run(cfg, inp, dy, dfin)
-    for h in (7, 61):
-        sl = [h]
-        ref = ssd_bwd_chunked(inp["x"][:, :, sl], inp["dt"][:, :, sl], inp["A"][sl], inp["B"], inp["C"],
-                              inp["D"][sl], dy[:, :, sl], cfg.chunk, inp["init_state"][:, sl], dfin[:, sl])
-        sub = {"dx": g["dx"][:, :, sl], "ddt": g["ddt"][:, :, sl], "dinit": g["dinit"][:, sl],
-               "dA": g["dA"][sl], "dD": g["dD"][sl]}
-        msg = []
-        for k, v in sub.items():
-            got, want = host(v), np.asarray(ref[k], dtype=np.float64)
-            rel = float(np.max(np.abs(got - want))) / max(float(np.max(np.abs(want))), 1e-30)
-            msg.append(f"{k} {rel:.1e}")
-            assert rel <= TOL.get(k, BWD_TOL), f"head {h} {k}: normwise relative error {rel:.3e}"
-        log(f"  head {h}: " + ", ".join(msg))
+    got = {k: host(g[k]) for k in ssd.GRAD_NAMES}
+    err = {k: 0.0 for k in ssd.GRAD_NAMES}
+    big = {k: 0.0 for k in ssd.GRAD_NAMES}
+    sums = {"dA": 0.0, "dD": 0.0}
+    for b in range(cfg.batch):
+        r = slice(b, b + 1)
+        log(f"[bwd] headline: oracle, batch row {b} of {cfg.batch}")
+        ref = ssd_bwd_chunked(inp["x"][r], inp["dt"][r], inp["A"], inp["B"][r], inp["C"][r], inp["D"], dy[r],
+                              cfg.chunk, inp["init_state"][r], dfin[r])
+        for k in ("dx", "ddt", "dB", "dC", "dinit"):
+            want = np.asarray(ref[k], dtype=np.float64)
+            err[k] = max(err[k], float(np.max(np.abs(got[k][r] - want))))
+            big[k] = max(big[k], float(np.max(np.abs(want))))
+        for k in sums:
+            sums[k] = sums[k] + np.asarray(ref[k], dtype=np.float64)
+    for k in sums:
+        err[k] = float(np.max(np.abs(got[k] - sums[k])))
+        big[k] = float(np.max(np.abs(sums[k])))
+    msg = []
+    for k in ssd.GRAD_NAMES:
+        rel = err[k] / max(big[k], 1e-30)
+        msg.append(f"{k} {rel:.1e}")
+        assert rel <= TOL.get(k, BWD_TOL), f"{k}: normwise relative error {rel:.3e}"
+    log("  " + ", ".join(msg))
