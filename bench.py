@@ -487,7 +487,7 @@ def main():
                          "HBM byte counters (FETCH_SIZE, WRITE_SIZE) can be scaled against")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}). "
               "Sequence or head sharding across GPUs is a design note only.", file=sys.stderr)
         sys.exit(2)
 

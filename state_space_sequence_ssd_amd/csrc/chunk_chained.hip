@@ -49,7 +49,8 @@
 //             mask, dt and the hi/lo split applied to the resident C.B^T),
 //             products formed transposed (y^T = x^T M^T), D x on the
 //             diagonal, y out through LDS as 16-byte row pieces.
-// The next head's x tile is loaded while this head's outputs are stored.
+// The next head's x tile and G', dt rows (and before a new ticket its B tile)
+// are loaded among this head's carried-state MFMAs and pairs.
 #include "lookback_device.h"
 #include "ssd_device.h"
 #include "ssd_launch.h"
