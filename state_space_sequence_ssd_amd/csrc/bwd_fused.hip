@@ -1,0 +1,471 @@
+// The causal (Q x Q) part of the backward pass, fused: for bf16 io, headdim
+// 64, chunk 256 and dstate 64 or 128, one kernel takes a chunk's heads from
+// the inputs to the per-token results that the rest of the pass consumes,
+//
+//   dXp  = (L o CB o dt_j)^T dY             (the causal part of dx)
+//   colW_j = sum_i L_ij CB_ij DX_ij,  colZ_j = dt_j colW_j
+//   rowZ_i = sum_j L_ij CB_ij DX_ij dt_j     (the time-gradient sums)
+//   W2g  = sum over a group's heads of L o DX o dt_j
+//
+// with CB = C B^T, DX = dY X^T and L_ij = 2^(G'_i - G'_j) (i >= j, else 0):
+// the causal block of the CUDA Tile Mamba-2 blog's decayed block output
+// (section "Mamba-2 architecture") differentiated with respect to x, B, C
+// and the decays; C B^T stays on chip as in its section "Kernel 3:
+// compute_out". No Q x Q block reaches memory except the group's W2g sum.
+//
+// Work split. A workgroup takes one (batch row, chunk, group, segment of the
+// group's heads) and walks the segment's heads. C.B^T depends on the group
+// only: its 36 causal 32x32 blocks are computed once and stay in the
+// accumulation registers (AGPRs). Wave w owns the 32-token column blocks w
+// and 7 - w: the causal blocks (ib, jb) with jb in that pair, 9 for every
+// wave. Owning whole columns keeps dx (a sum over rows i) and colW inside the
+// wave; row sums (rowZ) go through LDS.
+//
+// Per head and block: DX = dY[ib] X[jb]^T on the bf16 MFMA (exact products,
+// fp32 sums), then L, the three weighted blocks and the sums on the VALU,
+// then dx[jb] += W1^T dY[ib] with W1 split into a bf16 (hi, lo) pair against
+// the exact dY. The accumulator layout of a block (lane = column j,
+// registers = rows i) is already the first operand of that product, so W1
+// never moves; dY enters through gfx950's transposing LDS read.
+//
+// Decays. Off the diagonal L_ij = Eloc_i F_j with Eloc_i = 2^(G'_i -
+// G'_(32 ib - 1)) (one per row, computed once per head) and F_j = 2^(G'_(32 ib
+// - 1) - G'_j): both exponents are <= 0, so neither factor overflows and the
+// product underflows only where L itself does. Diagonal blocks take
+// 2^(G'_i - G'_j) directly.
+#include "lookback_device.h"
+#include "ssd_bwd.h"
+#include "ssd_device.h"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kP = 64, kQ = 256;
+constexpr int kTile = kQ * kP * 2;              // one bf16 tile, 32 KB
+constexpr int kBuf = 2 * kTile + 2 * kQ * 4;    // dY, X, G', dt of one head
+constexpr int kZs = 40;                         // scratch row stride, floats
+
+// Piece swizzle of the dY and X tiles (rows of 128 bytes, 8 pieces of 16):
+// logical piece q of row i sits at piece q ^ fsw(i). 16 consecutive rows at
+// one piece (the row fragment reads) and 4 rows at 4 adjacent pieces (the
+// transposing reads) both fall on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ constexpr uint32_t fsw(uint32_t i) { return (((i >> 1) & 1u) << 2) | ((i >> 2) & 3u); }
+__device__ __forceinline__ uint32_t toff(uint32_t i, uint32_t q) { return i * 128u + ((q ^ fsw(i)) << 4); }
+
+__device__ __forceinline__ float to_agpr(float v) {
+  float a;
+  asm("v_accvgpr_write_b32 %0, %1" : "=a"(a) : "v"(v));
+  return a;
+}
+__device__ __forceinline__ float from_agpr(float a) {
+  float v;
+  asm("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
+template <int NVM>
+__device__ __forceinline__ void vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(NVM) : "memory");
+}
+
+template <int V> struct IC { static constexpr int value = V; };
+template <bool V> struct BC { static constexpr bool value = V; };
+
+template <int I, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(IC<I>{});
+    static_for<I + 1, E>(f);
+  }
+}
+
+// Stores each wave issues after a head's prefetch: 2 x (8 dx pieces + colW +
+// colZ) + rowZ. A head waits for its tiles with vmcnt(kStoresAfter), a lower
+// bound, so every load issued before those stores has landed.
+constexpr int kStoresAfter = 16;
+
+// W2 = false: dXp, rowZ, colZ, colW. W2 = true: only the segment's W2 sums
+// (the two do not fit one kernel's registers: C.B^T and the W2 sums are 144
+// values per lane each).
+template <int N, bool W2>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ssd_bwd_qq(const bf16* __restrict__ x, const bf16* __restrict__ dy, const bf16* __restrict__ Bm,
+                const bf16* __restrict__ Cm, const float* __restrict__ gcum, const float* __restrict__ dtt,
+                float* __restrict__ dXp, float* __restrict__ rowZ, float* __restrict__ colZ,
+                float* __restrict__ colW, float* __restrict__ w2part, int64_t Tlen, int H, int G, int64_t nc,
+                int64_t Tp, int nseg) {
+  using Frag = bf16x8;
+  constexpr int KS = N / 16;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2][kBuf];
+  __shared__ __attribute__((aligned(16))) float sEl[kQ];
+  __shared__ __attribute__((aligned(16))) float sRow[4][kQ];
+  __shared__ __attribute__((aligned(16))) float sZ[4][32 * kZs];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __builtin_assume(w >= 0 && w < 4);
+  const int hf = lane >> 5, jl = lane & 31;
+
+  int64_t wi = blockIdx.x;
+  const int seg = (int)(wi % nseg);
+  wi /= nseg;
+  const int grp = (int)(wi % G);
+  const int64_t bkg = wi;              // (b * nc + k) * G + grp
+  wi /= G;
+  const int64_t k = wi % nc, b = wi / nc;
+  const int hpg = H / G, hs = (hpg + nseg - 1) / nseg;
+  const int h0 = grp * hpg + seg * hs;
+  const int h1 = min(h0 + hs, (grp + 1) * hpg);
+  const int64_t t0 = k * kQ;
+  const int nvalid = (int)(Tlen - t0 < kQ ? Tlen - t0 : kQ);
+  const uint32_t xrs = (uint32_t)(H * kP * 2);                       // bytes between token rows of x, dy
+  const uint32_t tbytes = (uint32_t)(nvalid - 1) * xrs + kP * 2;     // a head's rows in the chunk
+
+  // A head's tiles into LDS buffer bi: wave w fills rows 64 w .. 64 w + 63 of
+  // dY and X (8 direct loads each, rows past the sequence as zeros), waves 0
+  // and 1 the G' and dt rows.
+  auto load_tiles = [&](int h, int bi) __attribute__((always_inline)) {
+    unsigned char* base = lds[bi];
+    const int64_t row0 = (b * Tlen + t0) * H + h;
+    const __amdgpu_buffer_rsrc_t rdy = lookback::urs(dy + row0 * kP, tbytes);
+    const __amdgpu_buffer_rsrc_t rx = lookback::urs(x + row0 * kP, tbytes);
+    const uint32_t r = (uint32_t)lane >> 3, qp = (uint32_t)lane & 7;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const uint32_t blk = 8u * w + m, row = 8u * blk + r;
+      const uint32_t voff = row * xrs + ((qp ^ fsw(row)) << 4);
+      lookback::bdma16<false>(rdy, voff, 0, base + 1024 * blk);
+      lookback::bdma16<false>(rx, voff, 0, base + kTile + 1024 * blk);
+    }
+    if (w < 2) {
+      const float* src = (w == 0 ? gcum : dtt) + ((b * H + h) * Tp + t0);
+      lookback::dma16<false>(src, (uint32_t)lane * 16u, base + 2 * kTile + w * 1024);
+    }
+  };
+
+  if (h0 >= h1) return;   // (the host never launches an empty segment)
+  load_tiles(h0, 0);
+
+  // ---- C.B^T blocks of the wave's 9 pairs, into AGPRs
+  // slot s: (ib, jb) = (w + s, w) for s < 8 - w, else (s - 1, 7 - w)
+  float cbr[W2 ? 1 : 9][16];
+  if constexpr (!W2) {
+    const uint32_t brs = (uint32_t)(G * N * 2);
+    const uint32_t bbytes = (uint32_t)(nvalid - 1) * brs + N * 2;
+    const int64_t brow0 = (b * Tlen + t0) * G + grp;
+    const __amdgpu_buffer_rsrc_t rb = lookback::urs(Bm + brow0 * N, bbytes);
+    const __amdgpu_buffer_rsrc_t rc = lookback::urs(Cm + brow0 * N, bbytes);
+    auto ldfr = [&](__amdgpu_buffer_rsrc_t r, int blk, Frag* f) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const uint32_t off = (uint32_t)(32 * blk + jl) * brs + (uint32_t)(16 * kk + 8 * hf) * 2;
+        f[kk] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+      }
+    };
+    Frag b0[KS], b1[KS];
+    ldfr(rb, w, b0);
+    ldfr(rb, 7 - w, b1);
+    static_for<0, 9>([&](auto st) __attribute__((always_inline)) {
+      constexpr int s = decltype(st)::value;
+      const bool c0 = s < 8 - w;
+      const int ib = c0 ? w + s : s - 1;
+      Frag cf[KS];
+      ldfr(rc, ib, cf);
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf[kk], c0 ? b0[kk] : b1[kk], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cbr[s][r] = to_agpr(acc[r]);
+    });
+  }
+
+  float w2s[W2 ? 9 : 1][16];
+  if constexpr (W2) {
+#pragma unroll
+    for (int s = 0; s < 9; ++s)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) w2s[s][r] = 0.f;
+  }
+
+  for (int h = h0, it = 0; h < h1; ++h, ++it) {
+    const int bi = it & 1;
+    if (it == 0 || W2)
+      vm_barrier<0>();
+    else
+      vm_barrier<kStoresAfter>();
+    if (h + 1 < h1) load_tiles(h + 1, bi ^ 1);
+    const unsigned char* cur = lds[bi];
+    const float* gL = reinterpret_cast<const float*>(cur + 2 * kTile);
+    const float* dL = gL + kQ;
+    {
+      const float ga = tid >= 32 ? gL[(tid & ~31) - 1] : 0.f;
+      sEl[tid] = exp2_hw(gL[tid] - ga);
+      *reinterpret_cast<float4*>(&sRow[w][4 * lane]) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    lookback::lds_barrier();
+
+    const int64_t hrow = (b * H + h) * Tp + t0;   // this head's token vectors
+    float* zs = sZ[w];
+
+    // Lane-dependent offsets, derived here from a lane id the compiler
+    // cannot see through, so that it does not precompute every pair's
+    // addresses before the loop and keep them all live.
+    uint32_t lid = (uint32_t)lane;
+    asm volatile("" : "+v"(lid));
+    const uint32_t jlv = lid & 31u, hfv = lid >> 5;
+    // row fragment (row 32 blk + jl, piece 2 kk + hf) of a swizzled tile:
+    // byte 4096 blk + (fb ^ 32 kk)
+    const uint32_t fb = jlv * 128u + ((hfv ^ fsw(jlv)) << 4);
+    // transposing read: lane u = a + 4 m of a 16-lane group supplies row m of
+    // the group's 4 rows (32 ib + 16 ks + 8 hh + 4 hf + m), columns
+    // 32 pb + 16 c + 4 a .. + 3 (c: the group's 16-column half); byte
+    // 4096 ib + 2048 ks + 1024 hh + (tb ^ 64 pb ^ 32 hh)
+    const uint32_t tra = lid & 3u, trm = (lid >> 2) & 3u, trc = (lid >> 4) & 1u;
+    const uint32_t tlp = (2u * trc + (tra >> 1)) ^ (((trm >> 1) << 2) | hfv);
+    const uint32_t tb = (4u * hfv + trm) * 128u + (tlp << 4) + 8u * (tra & 1u);
+    // scratch: lane (hf, jl) writes column jl of rows drow(r, hf), reads row
+    // jl from column 16 hf
+    const uint32_t zwb = 4u * hfv * kZs + jlv, zrb = jlv * kZs + 16u * hfv;
+
+    // column-block state
+    Frag xf[4];
+    float gj = 0.f, dtj = 0.f, colw = 0.f;
+    f32x16 dxa[2];
+    auto load_col = [&](int jb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        xf[kk] = *reinterpret_cast<const Frag*>(cur + kTile + 4096 * jb + (fb ^ (32u * kk)));
+      gj = gL[32 * jb + jlv];
+      dtj = dL[32 * jb + jlv];
+      colw = 0.f;
+      dxa[0] = f32x16{};
+      dxa[1] = f32x16{};
+    };
+    auto flush = [&](int jb) __attribute__((always_inline)) {
+      if constexpr (W2) return;
+      const float cw = colw + __shfl_xor(colw, 32);
+      if (hfv == 0) {
+        colW[hrow + 32 * jb + jlv] = cw;
+        colZ[hrow + 32 * jb + jlv] = cw * dtj;
+      }
+      // dx rows j = 32 jb + row, 32 columns per half, through the scratch as
+      // 16-byte pieces (a wave's LDS operations complete in order)
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) zs[zwb + (8 * (r / 4) + r % 4) * kZs] = dxa[pb][r];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int row = 8 * c + (int)(lid >> 3), c4 = 4 * (int)(lid & 7);
+          const float4 v = *reinterpret_cast<const float4*>(&zs[row * kZs + c4]);
+          *reinterpret_cast<float4*>(dXp + ((b * Tp + t0 + 32 * jb + row) * H + h) * kP + 32 * pb + c4) = v;
+        }
+      }
+    };
+
+    auto pair = [&](auto stag, auto dtag, int ib) __attribute__((always_inline)) {
+      constexpr int s = decltype(stag)::value;
+      constexpr bool DIAG = decltype(dtag)::value;
+      // each pair's work stays between its own scheduling fences: hoisting the
+      // next pairs' LDS reads would only add live registers
+      __builtin_amdgcn_sched_barrier(0);
+      // DX block = dY[ib] X[jb]^T
+      f32x16 dxv = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const Frag a = *reinterpret_cast<const Frag*>(cur + 4096 * ib + (fb ^ (32u * kk)));
+        dxv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, xf[kk], dxv, 0, 0, 0);
+      }
+      // decays of the block's 16 rows in this lane's column
+      float ln[16];
+      if constexpr (DIAG) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 g4 = *reinterpret_cast<const float4*>(&gL[32 * ib + 8 * q + 4 * hfv]);
+          const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * q + e;
+            const float l = exp2_hw(gv[e] - gj);
+            ln[r] = (uint32_t)(8 * q + e) + 4u * hfv >= jlv ? l : 0.f;
+          }
+        }
+      } else {
+        const float F = exp2_hw(gL[32 * ib - 1] - gj);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float4 e4 = *reinterpret_cast<const float4*>(&sEl[32 * ib + 8 * q + 4 * hfv]);
+          ln[4 * q] = e4.x * F;
+          ln[4 * q + 1] = e4.y * F;
+          ln[4 * q + 2] = e4.z * F;
+          ln[4 * q + 3] = e4.w * F;
+        }
+      }
+      if constexpr (W2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) w2s[s][r] += (ln[r] * dtj) * dxv[r];
+        return;
+      }
+      float w1[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float cb = from_agpr(cbr[W2 ? 0 : s][r]);
+        const float d = dxv[r];
+        const float u = ln[r] * (cb * d);
+        colw += u;
+        zs[zwb + (8 * (r / 4) + r % 4) * kZs] = u * dtj;
+        const float ld = ln[r] * dtj;
+        w1[r] = ld * cb;
+      }
+      // row sums of Z over the block's 32 columns: lane (hf, jl) adds row jl,
+      // columns 16 hf .. 16 hf + 15, then the two halves
+      {
+        float rs = 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float4 v = *reinterpret_cast<const float4*>(&zs[zrb + 4 * c]);
+          rs += (v.x + v.y) + (v.z + v.w);
+        }
+        rs += __shfl_xor(rs, 32);
+        if (hfv == 0) sRow[w][32 * ib + jlv] += rs;
+      }
+      // dx[jb] += W1^T dY[ib]: k-slot e of half hf and step ks is row
+      // 16 ks + 8 (e / 4) + 4 hf + e % 4 of the block on both sides
+      typedef short s16x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        Frag hi, lo;
+        Io<bf16>::split(&w1[8 * ks], hi, lo);
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb) {
+          uint64_t h2[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const unsigned char* a = cur + 4096 * ib + 2048 * ks + 1024 * hh + (tb ^ (64u * pb + 32u * hh));
+            h2[hh] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                      (__attribute__((address_space(3))) s16x4*)(a)));
+          }
+          const u32x4 w4 = {(uint32_t)h2[0], (uint32_t)(h2[0] >> 32), (uint32_t)h2[1], (uint32_t)(h2[1] >> 32)};
+          const Frag bfr = __builtin_bit_cast(Frag, w4);
+          dxa[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(hi, bfr, dxa[pb], 0, 0, 0);
+          dxa[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lo, bfr, dxa[pb], 0, 0, 0);
+        }
+      }
+    };
+
+    // the wave's 9 pairs: column block w (slots 0 .. 7 - w), then 7 - w
+    load_col(w);
+    static_for<0, 9>([&](auto st) __attribute__((always_inline)) {
+      constexpr int s = decltype(st)::value;
+      if constexpr (s == 0) {
+        pair(IC<0>{}, BC<true>{}, w);
+      } else if constexpr (s <= 4) {
+        pair(IC<s>{}, BC<false>{}, w + s);
+      } else {
+        if (s < 8 - w) {
+          pair(IC<s>{}, BC<false>{}, w + s);
+        } else if (s == 8 - w) {
+          flush(w);
+          load_col(7 - w);
+          pair(IC<s>{}, BC<true>{}, s - 1);
+        } else {
+          pair(IC<s>{}, BC<false>{}, s - 1);
+        }
+      }
+    });
+    flush(7 - w);
+
+    // rowZ: the four waves' partial row sums
+    if constexpr (!W2) {
+      lookback::lds_barrier();
+      rowZ[hrow + tid] = ((sRow[0][tid] + sRow[1][tid]) + sRow[2][tid]) + sRow[3][tid];
+    }
+  }
+
+  if constexpr (W2) {
+    // this segment's sum of L o DX o dt_j over its heads, causal 32x32 blocks
+    float* o = w2part + ((bkg * nseg + seg) * kQ) * kQ;
+    static_for<0, 9>([&](auto st) __attribute__((always_inline)) {
+      constexpr int s = decltype(st)::value;
+      const bool c0 = s < 8 - w;
+      const int ib = c0 ? w + s : s - 1, jb = c0 ? w : 7 - w;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[(32 * ib + drow(r, hf)) * kQ + 32 * jb + jl] = w2s[s][r];
+    });
+  }
+}
+
+// W2g[bkg] = the sum of the segments' blocks on and below the diagonal; the
+// 32x32 blocks above it inside a 64x64 diagonal tile are cleared (the causal
+// products that read W2g run over whole 64-wide tiles).
+__global__ void w2_segment_sum(const float* __restrict__ part, float* __restrict__ out, int nseg, int64_t total4) {
+  constexpr int64_t QQ = (int64_t)kQ * kQ;
+  for (int64_t i4 = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i4 < total4; i4 += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = 4 * i4, bkg = e / QQ, o = e % QQ;
+    const int i = (int)(o / kQ), j = (int)(o % kQ);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i / 32 >= j / 32) {
+      const float* src = part + bkg * nseg * QQ + o;
+      for (int s = 0; s < nseg; ++s) {
+        const float4 v = *reinterpret_cast<const float4*>(src + s * QQ);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+      }
+    } else if (i / 64 != j / 64) {
+      continue;   // never read
+    }
+    *reinterpret_cast<float4*>(out + e) = acc;
+  }
+}
+
+}  // namespace
+
+bool bwd_fused_supported(int io, int64_t P, int64_t N, int64_t Q) {
+  return io == 1 && P == kP && Q == kQ && (N == 64 || N == 128);
+}
+
+int bwd_fused_segments(int64_t bt, int64_t nc, int64_t H, int64_t G) {
+  const int64_t hpg = H / G, items = bt * nc * G;
+  if (items <= 0 || hpg <= 0) return 1;
+  // about 256 workgroups or more, each walking at least one head
+  int64_t nseg = (256 + items - 1) / items;
+  if (nseg > hpg) nseg = hpg;
+  if (nseg < 1) nseg = 1;
+  const int64_t hs = (hpg + nseg - 1) / nseg;
+  return (int)((hpg + hs - 1) / hs);   // no empty segment
+}
+
+hipError_t launch_bwd_fused_qq(const BwdProblem& p, float* w2part, int nseg, hipStream_t s) {
+  const int64_t items = p.bt * p.nc * p.G * nseg;
+  if (items <= 0) return hipSuccess;
+  if (items > 0x7fffffff) return hipErrorInvalidValue;
+  const bf16* x = static_cast<const bf16*>(p.x);
+  const bf16* dy = static_cast<const bf16*>(p.dy);
+  const bf16* Bm = static_cast<const bf16*>(p.B);
+  const bf16* Cm = static_cast<const bf16*>(p.C);
+  auto launch = [&](auto ntag, auto wtag) {
+    constexpr int NN = decltype(ntag)::value;
+    constexpr bool WW = decltype(wtag)::value;
+    hipLaunchKernelGGL((ssd_bwd_qq<NN, WW>), dim3((unsigned)items), dim3(256), 0, s, x, dy, Bm, Cm, p.gcum, p.dtt,
+                       p.dXp, p.rowZ, p.colZ, p.colW, w2part, p.T, (int)p.H, (int)p.G, p.nc, p.Tp, nseg);
+  };
+  if (p.N == 64) {
+    launch(IC<64>{}, BC<false>{});
+    launch(IC<64>{}, BC<true>{});
+  } else {
+    launch(IC<128>{}, BC<false>{});
+    launch(IC<128>{}, BC<true>{});
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t total4 = p.bt * p.nc * p.G * (int64_t)kQ * kQ / 4;
+  const int64_t g = (total4 + 255) / 256;
+  hipLaunchKernelGGL(w2_segment_sum, dim3((unsigned)(g < 65536 ? g : 65536)), dim3(256), 0, s, w2part, p.CB, nseg,
+                     total4);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -46,4 +46,13 @@ struct BwdProblem {
 // gcum, dtt and wst first).
 hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t stream);
 
+// The fused causal part (bwd_fused.hip): for the shapes it supports it
+// replaces the C B^T and dY X^T products, the masks and decays, the W1^T dY
+// product and the group sums of W2, writing dXp, rowZ, colZ, colW and CB
+// (the group's W2 sum) as those steps do; w2part holds the per-segment sums
+// ([bt][nc][G][nseg][Q][Q]).
+bool bwd_fused_supported(int io, int64_t P, int64_t N, int64_t Q);
+int bwd_fused_segments(int64_t bt, int64_t nc, int64_t H, int64_t G);
+hipError_t launch_bwd_fused_qq(const BwdProblem& p, float* w2part, int nseg, hipStream_t stream);
+
 }  // namespace ssd

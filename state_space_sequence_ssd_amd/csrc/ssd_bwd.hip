@@ -815,34 +815,41 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
                        nc, Tp, Q, PN, nst, 1);
     ok(hipGetLastError());
   }
-  // 4. CB = C B^T per (b, k, g) and DX = dY X^T per (b, k, h)
-  ok(gemm(op(p.Cp, G * N, 1, Tp * G * N, Q * G * N, N), op(p.Bp, 1, G * N, Tp * G * N, Q * G * N, N),
-          op(p.CB, Q, 1, nc * G * QQ, G * QQ, QQ), none(), none(), Qi, Qi, Ni, Bi, Ki, (int)G, 0.f, s, kLowerOut));
-  ok(gemm(dY, op(p.Xp, 1, H * P, Tp * H * P, Q * H * P, P), op(p.DX, Q, 1, nc * H * QQ, H * QQ, QQ), none(), none(), Qi,
-          Qi, Pi, Bi, Ki, Hi, 0.f, s, kLowerOut));
-  // 5. masks, decays, and the sums for the time gradient
-  if (e == hipSuccess && bt * nc * H > 0) {
-    hipLaunchKernelGGL(mask_decay, dim3((unsigned)(bt * nc * H)), dim3(256), 0, s, p.CB, p.DX, p.W1, p.gcum, p.dtt,
-                       p.rowZ, p.colZ, p.colW, Qi, Hi, hpg, nc, Tp);
-    ok(hipGetLastError());
-  }
-  const Operand Wqq1T = op(p.W1, 1, Q, nc * H * QQ, H * QQ, QQ);
-  const Operand Uo = op(p.U, P, 1, nc * H * Q * P, H * Q * P, Q * P), Vo = op(p.V, P, 1, nc * H * Q * P, H * Q * P, Q * P);
   // 6. U = B dHn^T, V = C Hprev^T (rows j: dHn B_j, Hprev C_j)
+  const Operand Uo = op(p.U, P, 1, nc * H * Q * P, H * Q * P, Q * P), Vo = op(p.V, P, 1, nc * H * Q * P, H * Q * P, Q * P);
   ok(gemm(Bt, blk(p.dhn, true), Uo, none(), none(), Qi, Pi, Ni, Bi, Ki, Hi, 0.f, s));
   ok(gemm(Ct, blk(p.hprev, true), Vo, none(), none(), Qi, Pi, Ni, Bi, Ki, Hi, 0.f, s));
-  // 7. dXp = W1s^T dY
-  ok(gemm(Wqq1T, dY, op(p.dXp, H * P, 1, Tp * H * P, Q * H * P, P), none(), none(), Qi, Pi, Qi, Bi, Ki, Hi, 0.f, s,
-          kKFromRow));
+  const bool fused = bwd_fused_supported(p.io, P, N, Q);
+  if (fused) {
+    // 4, 5, 7 and the group sums of W2 in one pass over each chunk's heads
+    ok(launch_bwd_fused_qq(p, p.DX, bwd_fused_segments(bt, nc, H, G), s));
+  } else {
+    // 4. CB = C B^T per (b, k, g) and DX = dY X^T per (b, k, h)
+    ok(gemm(op(p.Cp, G * N, 1, Tp * G * N, Q * G * N, N), op(p.Bp, 1, G * N, Tp * G * N, Q * G * N, N),
+            op(p.CB, Q, 1, nc * G * QQ, G * QQ, QQ), none(), none(), Qi, Qi, Ni, Bi, Ki, (int)G, 0.f, s, kLowerOut));
+    ok(gemm(dY, op(p.Xp, 1, H * P, Tp * H * P, Q * H * P, P), op(p.DX, Q, 1, nc * H * QQ, H * QQ, QQ), none(), none(),
+            Qi, Qi, Pi, Bi, Ki, Hi, 0.f, s, kLowerOut));
+    // 5. masks, decays, and the sums for the time gradient
+    if (e == hipSuccess && bt * nc * H > 0) {
+      hipLaunchKernelGGL(mask_decay, dim3((unsigned)(bt * nc * H)), dim3(256), 0, s, p.CB, p.DX, p.W1, p.gcum, p.dtt,
+                         p.rowZ, p.colZ, p.colW, Qi, Hi, hpg, nc, Tp);
+      ok(hipGetLastError());
+    }
+    // 7. dXp = W1s^T dY
+    const Operand Wqq1T = op(p.W1, 1, Q, nc * H * QQ, H * QQ, QQ);
+    ok(gemm(Wqq1T, dY, op(p.dXp, H * P, 1, Tp * H * P, Q * H * P, P), none(), none(), Qi, Pi, Qi, Bi, Ki, Hi, 0.f, s,
+            kKFromRow));
+    // the group's sum of the heads' W2s blocks (over CB, no longer needed)
+    const int64_t nsum = bt * nc * G * QQ;
+    if (e == hipSuccess && nsum > 0) {
+      hipLaunchKernelGGL(sum_heads, dim3(grid_for(nsum / 4)), dim3(256), 0, s, p.DX, p.CB, hpg, Qi, QQ, nsum / 4);
+      ok(hipGetLastError());
+    }
+  }
   // 8. dB_h = W2s^T C + diag(w) X dHn;  dC_h = W2s B + diag(E) dY Hprev
   // per (b, k, group): B and C are shared by the group's heads, so the
-  // causal products take the sum of the heads' W2s blocks (over CB, no longer
-  // needed), and the state products sum the heads' parts inside the kernel
-  const int64_t nsum = bt * nc * G * QQ;
-  if (e == hipSuccess && nsum > 0) {
-    hipLaunchKernelGGL(sum_heads, dim3(grid_for(nsum / 4)), dim3(256), 0, s, p.DX, p.CB, hpg, Qi, QQ, nsum / 4);
-    ok(hipGetLastError());
-  }
+  // causal products take the sum of the heads' W2s blocks, and the state
+  // products sum the heads' parts inside the kernel
   {
     const Operand W2g = op(p.CB, Q, 1, nc * G * QQ, G * QQ, QQ), W2gT = op(p.CB, 1, Q, nc * G * QQ, G * QQ, QQ);
     const Operand Bg = op(p.Bp, G * N, 1, Tp * G * N, Q * G * N, N), Cg = op(p.Cp, G * N, 1, Tp * G * N, Q * G * N, N);
