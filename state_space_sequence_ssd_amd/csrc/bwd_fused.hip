@@ -421,6 +421,259 @@ __global__ void w2_segment_sum(const float* __restrict__ part, float* __restrict
   }
 }
 
+
+// ---------------------------------------------------------------- finish
+// Per (batch row, chunk, head): the carried-state terms and the per-token
+// results,
+//
+//   U = B dHn^T,  V = C Hprev^T                 (rows: tokens, columns: headdim)
+//   dx_t   = dXp_t + w_t U_t + D dY_t
+//   avec_t = dY_t . V_t,  bvec_t = x_t . U_t,  ddx_t = dY_t . x_t
+//   dG_t   = E_t avec_t + rowZ_t - colZ_t - w_t bvec_t   (+ at the chunk's
+//            last token: 2^(G'_last) <dHn, Hprev> + sum_j w_j bvec_j)
+//   ddt_t  = colW_t + 2^(G'_last - G'_t) bvec_t + A sum_{j >= t} dG_j
+//   dA part = sum_t dG_t cumdt_t,  dD part = sum_t ddx_t
+//
+// with E_t = 2^(G'_t), w_t = dt_t 2^(G'_last - G'_t) and dHn the adjoint of
+// the state leaving the chunk (the chain rule through G_t = A sum_{s <= t}
+// dt_s of the blog's decays, section "Mamba-2 architecture").
+//
+// The two fp32 states are read once per workgroup as whole rows, split into
+// bf16 (hi, lo) planes in LDS (their inner product taken on the way), and
+// every wave takes its MFMA fragments from there. Wave v owns the 32 tokens
+// of block v: U and V on the bf16 MFMA against the exact bf16 B and C rows,
+// lane = headdim column and registers = tokens, so x, dy, dXp and dx are read
+// and written as whole rows. The per-token dot products go through LDS; the
+// chunk's scans are wave scans joined through LDS.
+template <int N>
+struct FinCfg {
+  static constexpr int RP = N / 8;                 // 16-byte pieces per bf16 state row
+  static constexpr int PLANE = kP * N * 2;         // bytes of one bf16 plane
+  static constexpr int LDS = 4 * PLANE;            // dHn hi, lo, Hprev hi, lo
+};
+// piece q of state row p (RP pieces) sits at piece q ^ (p % min(RP, 16)):
+// with RP >= 16 the fragment reads (16 rows, one piece each) hit 16 distinct
+// 16-byte bank groups
+template <int RP>
+__device__ __forceinline__ uint32_t spiece(uint32_t p, uint32_t q) {
+  return q ^ (p & (uint32_t)((RP < 16 ? RP : 16) - 1));
+}
+
+template <int N>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void ssd_bwd_state_finish(
+    const bf16* __restrict__ x, const bf16* __restrict__ dy, const bf16* __restrict__ Bm, const bf16* __restrict__ Cm,
+    const float* __restrict__ Ap, const float* __restrict__ Dp, const float* __restrict__ gcum,
+    const float* __restrict__ dtt, const float* __restrict__ wst, const float* __restrict__ hprev,
+    const float* __restrict__ dhn, const float* __restrict__ dXp, const float* __restrict__ rowZ,
+    const float* __restrict__ colZ, const float* __restrict__ colW, float* __restrict__ dx, float* __restrict__ ddt,
+    float* __restrict__ dA_part, float* __restrict__ dD_part, int64_t Tlen, int H, int G, int64_t nc, int64_t Tp) {
+  using Frag = bf16x8;
+  using Cf = FinCfg<N>;
+  constexpr int KS = N / 16, RP = Cf::RP;
+  __shared__ __attribute__((aligned(16))) unsigned char sS[Cf::LDS];
+  __shared__ __attribute__((aligned(16))) float sZ[8][32 * kZs];
+  __shared__ float sA[kQ], sB[kQ], sD[kQ];
+  __shared__ float sRed[4][8];
+  __shared__ float sTot[2][4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int v = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave 0..7 = token block
+  const int hf = lane >> 5, jl = lane & 31;
+  const int h = (int)(blockIdx.x % H);
+  const int64_t bk = blockIdx.x / H, k = bk % nc, b = bk / nc;
+  const int grp = h / (H / G);
+  const int64_t t0 = k * kQ;
+  const int nvalid = (int)(Tlen - t0 < kQ ? Tlen - t0 : kQ);
+  const int64_t hrow = (b * H + h) * Tp + t0;
+
+  // ---- the states: whole rows in, bf16 (hi, lo) planes out, and <dHn, Hprev>
+  float dot = 0.f;
+  {
+    const float* ds = dhn + ((b * H + h) * nc + k) * (int64_t)(kP * N);
+    const float* hs = hprev + ((b * H + h) * nc + k) * (int64_t)(kP * N);
+    constexpr int NV = kP * N / 4 / 512;   // 16-byte pieces per thread and state
+    float4 dv[NV], hv[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      dv[j] = *reinterpret_cast<const float4*>(ds + 4 * (tid + 512 * j));
+      hv[j] = *reinterpret_cast<const float4*>(hs + 4 * (tid + 512 * j));
+    }
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int e = 4 * (tid + 512 * j), pr = e / N, n0 = e % N;
+      dot = fmaf(dv[j].x, hv[j].x, fmaf(dv[j].y, hv[j].y, fmaf(dv[j].z, hv[j].z, fmaf(dv[j].w, hv[j].w, dot))));
+      const uint32_t off = (uint32_t)pr * (N * 2) + (spiece<RP>(pr, n0 / 8) << 4) + (uint32_t)(n0 % 8) * 2;
+      auto put = [&](const float4& q, int plane) {
+        const uint32_t h01 = pack_bf16x2(q.x, q.y), h23 = pack_bf16x2(q.z, q.w);
+        const uint32_t l01 = pack_bf16x2(q.x - bf16lo(h01), q.y - bf16hi(h01));
+        const uint32_t l23 = pack_bf16x2(q.z - bf16lo(h23), q.w - bf16hi(h23));
+        *reinterpret_cast<uint2*>(sS + plane * Cf::PLANE + off) = make_uint2(h01, h23);
+        *reinterpret_cast<uint2*>(sS + (plane + 1) * Cf::PLANE + off) = make_uint2(l01, l23);
+      };
+      put(dv[j], 0);
+      put(hv[j], 2);
+    }
+  }
+  // B and C rows of the wave's tokens (exact bf16 fragments)
+  Frag bfr[KS], cfr[KS];
+  {
+    const uint32_t brs = (uint32_t)(G * N * 2);
+    const uint32_t bbytes = (uint32_t)(nvalid - 1) * brs + N * 2;
+    const int64_t brow0 = (b * Tlen + t0) * G + grp;
+    const __amdgpu_buffer_rsrc_t rb = lookback::urs(Bm + brow0 * N, bbytes);
+    const __amdgpu_buffer_rsrc_t rc = lookback::urs(Cm + brow0 * N, bbytes);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const uint32_t off = (uint32_t)(32 * v + jl) * brs + (uint32_t)(16 * kk + 8 * hf) * 2;
+      bfr[kk] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+      cfr[kk] = __builtin_bit_cast(Frag, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0));
+    }
+  }
+  __syncthreads();
+
+  // ---- U and V for token block v, both headdim halves
+  f32x16 U[2], V[2];
+  U[0] = U[1] = V[0] = V[1] = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+    for (int pb = 0; pb < 2; ++pb) {
+      const uint32_t pr = (uint32_t)(32 * pb + jl);
+      const uint32_t off = pr * (N * 2) + (spiece<RP>(pr, (uint32_t)(2 * kk + hf)) << 4);
+      const Frag dh = *reinterpret_cast<const Frag*>(sS + off);
+      const Frag dl = *reinterpret_cast<const Frag*>(sS + Cf::PLANE + off);
+      const Frag hh = *reinterpret_cast<const Frag*>(sS + 2 * Cf::PLANE + off);
+      const Frag hl = *reinterpret_cast<const Frag*>(sS + 3 * Cf::PLANE + off);
+      U[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk], dh, U[pb], 0, 0, 0);
+      U[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk], dl, U[pb], 0, 0, 0);
+      V[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cfr[kk], hh, V[pb], 0, 0, 0);
+      V[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cfr[kk], hl, V[pb], 0, 0, 0);
+    }
+  }
+
+  // ---- per token: dx, and the three dot products over headdim
+  {
+    const uint32_t xrs = (uint32_t)(H * kP * 2);
+    const uint32_t xbytes = (uint32_t)(nvalid - 1) * xrs + kP * 2;
+    const int64_t row0 = (b * Tlen + t0) * H + h;
+    const __amdgpu_buffer_rsrc_t rx = lookback::urs(x + row0 * kP, xbytes);
+    const __amdgpu_buffer_rsrc_t ry = lookback::urs(dy + row0 * kP, xbytes);
+    const __amdgpu_buffer_rsrc_t ro = lookback::urs(dx + row0 * kP, (uint32_t)(nvalid - 1) * (xrs * 2) + kP * 4);
+    const float Dh = Dp[h];
+    // every load before any store (a load issued behind a store waits for it)
+    float xv[2][16], yv[2][16], dp[2][16], wv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * v + drow(r, hf);
+      wv[r] = wst[hrow + i];
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
+        const uint32_t eo = (uint32_t)i * xrs + (uint32_t)(32 * pb + jl) * 2;
+        xv[pb][r] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rx, eo, 0, 0) << 16);
+        yv[pb][r] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(ry, eo, 0, 0) << 16);
+        dp[pb][r] = dXp[((b * Tp + t0 + i) * H + h) * kP + 32 * pb + jl];
+      }
+    }
+    float pa[16], pbv[16], pd[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = 32 * v + drow(r, hf);
+      pa[r] = 0.f;
+      pbv[r] = 0.f;
+      pd[r] = 0.f;
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
+        const uint32_t eo = (uint32_t)i * xrs + (uint32_t)(32 * pb + jl) * 2;
+        const float u = U[pb][r], vv = V[pb][r];
+        buf_store_dword(__float_as_uint(dp[pb][r] + wv[r] * u + Dh * yv[pb][r]), ro, 2 * eo);
+        pa[r] = fmaf(yv[pb][r], vv, pa[r]);
+        pbv[r] = fmaf(xv[pb][r], u, pbv[r]);
+        pd[r] = fmaf(yv[pb][r], xv[pb][r], pd[r]);
+      }
+    }
+    // row sums over the 32 lanes of a half through the wave's scratch (a
+    // wave's LDS operations complete in order): lane (hf, jl) adds row jl,
+    // columns 16 hf .. 16 hf + 15, then the two halves
+    float* zs = sZ[v];
+    auto rowsum = [&](const float* val, float* out) __attribute__((always_inline)) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) zs[drow(r, hf) * kZs + jl] = val[r];
+      float rs = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 t4 = *reinterpret_cast<const float4*>(&zs[jl * kZs + 16 * hf + 4 * c]);
+        rs += (t4.x + t4.y) + (t4.z + t4.w);
+      }
+      rs += __shfl_xor(rs, 32);
+      if (hf == 0) out[32 * v + jl] = rs;
+    };
+    rowsum(pa, sA);
+    rowsum(pbv, sB);
+    rowsum(pd, sD);
+  }
+  for (int off = 32; off >= 1; off /= 2) dot += __shfl_xor(dot, off);
+  if (lane == 0) sRed[3][v] = dot;
+  __syncthreads();
+
+  // ---- the chunk's scans, one token per thread of waves 0-3
+  const bool scan = v < 4;
+  const int t = tid & (kQ - 1);
+  float dg = 0.f, bv = 0.f, gt = 0.f, dtv = 0.f, glast = 0.f;
+  auto wave_sum = [&](float val) {
+    for (int off = 32; off >= 1; off /= 2) val += __shfl_xor(val, off);
+    return val;
+  };
+  if (scan) {
+    gt = gcum[hrow + t];
+    dtv = dtt[hrow + t];
+    glast = gcum[hrow + kQ - 1];
+    const float wt = wst[hrow + t];
+    bv = sB[t];
+    dg = exp2_hw(gt) * sA[t] + rowZ[hrow + t] - colZ[hrow + t] - wt * bv;
+    const float s0 = wave_sum(wt * bv), s1 = wave_sum(sD[t]);
+    if (lane == 0) {
+      sRed[0][v] = s0;
+      sRed[1][v] = s1;
+    }
+  }
+  __syncthreads();
+  float suf = 0.f, pre = 0.f;
+  if (scan) {
+    const float swb = ((sRed[0][0] + sRed[0][1]) + sRed[0][2]) + sRed[0][3];
+    float dotv = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dotv += sRed[3][u];
+    if (t == kQ - 1) dg += exp2_hw(glast) * dotv + swb;
+    // suffix sums of dG (within the wave, then the later waves' totals) and
+    // prefix sums of dt
+    suf = dg;
+    pre = dtv;
+    for (int off = 1; off < 64; off *= 2) {
+      const float sd = __shfl_down(suf, off), su = __shfl_up(pre, off);
+      if (lane + off < 64) suf += sd;
+      if (lane >= off) pre += su;
+    }
+    if (lane == 0) sTot[0][v] = suf;
+    if (lane == 63) sTot[1][v] = pre;
+  }
+  __syncthreads();
+  if (scan) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (u > v) suf += sTot[0][u];
+      if (u < v) pre += sTot[1][u];
+    }
+    if (t0 + t < Tlen) ddt[(b * Tlen + t0 + t) * H + h] = colW[hrow + t] + exp2_hw(glast - gt) * bv + Ap[h] * suf;
+    const float s2 = wave_sum(dg * pre);
+    if (lane == 0) sRed[2][v] = s2;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    dA_part[(b * H + h) * nc + k] = ((sRed[2][0] + sRed[2][1]) + sRed[2][2]) + sRed[2][3];
+    dD_part[(b * H + h) * nc + k] = ((sRed[1][0] + sRed[1][1]) + sRed[1][2]) + sRed[1][3];
+  }
+}
+
 }  // namespace
 
 bool bwd_fused_supported(int io, int64_t P, int64_t N, int64_t Q) {
@@ -465,6 +718,25 @@ hipError_t launch_bwd_fused_qq(const BwdProblem& p, float* w2part, int nseg, hip
   const int64_t g = (total4 + 255) / 256;
   hipLaunchKernelGGL(w2_segment_sum, dim3((unsigned)(g < 65536 ? g : 65536)), dim3(256), 0, s, w2part, p.CB, nseg,
                      total4);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_fused_finish(const BwdProblem& p, hipStream_t s) {
+  const int64_t items = p.bt * p.nc * p.H;
+  if (items <= 0) return hipSuccess;
+  if (items > 0x7fffffff) return hipErrorInvalidValue;
+  const bf16* x = static_cast<const bf16*>(p.x);
+  const bf16* dy = static_cast<const bf16*>(p.dy);
+  const bf16* Bm = static_cast<const bf16*>(p.B);
+  const bf16* Cm = static_cast<const bf16*>(p.C);
+  if (p.N == 64)
+    hipLaunchKernelGGL(ssd_bwd_state_finish<64>, dim3((unsigned)items), dim3(512), 0, s, x, dy, Bm, Cm, p.A, p.D,
+                       p.gcum, p.dtt, p.wst, p.hprev, p.dhn, p.dXp, p.rowZ, p.colZ, p.colW, p.dx, p.ddt, p.dA_part,
+                       p.dD_part, p.T, (int)p.H, (int)p.G, p.nc, p.Tp);
+  else
+    hipLaunchKernelGGL(ssd_bwd_state_finish<128>, dim3((unsigned)items), dim3(512), 0, s, x, dy, Bm, Cm, p.A, p.D,
+                       p.gcum, p.dtt, p.wst, p.hprev, p.dhn, p.dXp, p.rowZ, p.colZ, p.colW, p.dx, p.ddt, p.dA_part,
+                       p.dD_part, p.T, (int)p.H, (int)p.G, p.nc, p.Tp);
   return hipGetLastError();
 }
 

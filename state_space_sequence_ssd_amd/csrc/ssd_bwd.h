@@ -54,5 +54,8 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t stream);
 bool bwd_fused_supported(int io, int64_t P, int64_t N, int64_t Q);
 int bwd_fused_segments(int64_t bt, int64_t nc, int64_t H, int64_t G);
 hipError_t launch_bwd_fused_qq(const BwdProblem& p, float* w2part, int nseg, hipStream_t stream);
+// The same shapes: U = B dHn^T and V = C Hprev^T formed on the fly with dx,
+// ddt and the dA / dD parts (in place of the U, V products and finish_chunk).
+hipError_t launch_bwd_fused_finish(const BwdProblem& p, hipStream_t stream);
 
 }  // namespace ssd

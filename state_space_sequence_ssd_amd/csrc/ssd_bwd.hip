@@ -798,9 +798,22 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
     return transposed ? op(v, 1, N, H * nc * PN, PN, nc * PN) : op(v, N, 1, H * nc * PN, PN, nc * PN);
   };
 
+  // chunk-state products on the forward pass's own kernel where it has the
+  // shape (bf16 operands on the bf16 MFMA, read from the unpadded inputs)
+  const bool cs_kernel = chunk_state_has(p.io, P, N, Q);
+  auto chunk_states = [&](const void* xin, const void* bin, float* weights) {
+    if (bt * nc * H == 0) return hipSuccess;   // no chunk: nothing to launch
+    Problem f{};
+    f.bt = bt; f.T = T; f.H = H; f.P = P; f.N = N; f.G = G; f.Q = Q; f.nc = nc; f.Tp = Tp; f.io = p.io;
+    f.x = xin; f.B = bin; f.wst = weights; f.states = p.S;
+    return launch_chunk_state(f, s);
+  };
   // 2. forward chunk states S = X^T diag(wst) B, then Hprev
-  ok(gemm(op(p.Xp, 1, H * P, Tp * H * P, Q * H * P, P), Bt, blk(p.S, false), none(), vec(p.wst), Pi, Ni, Qi, Bi, Ki,
-          Hi, 0.f, s));
+  if (cs_kernel)
+    ok(chunk_states(p.x, p.B, p.wst));
+  else
+    ok(gemm(op(p.Xp, 1, H * P, Tp * H * P, Q * H * P, P), Bt, blk(p.S, false), none(), vec(p.wst), Pi, Ni, Qi, Bi, Ki,
+            Hi, 0.f, s));
   const int64_t nst = bt * H * PN;
   if (e == hipSuccess) {
     hipLaunchKernelGGL(chunk_recursion, dim3(grid_for(nst)), dim3(256), 0, s, p.S, p.gcum, p.init, p.hprev,
@@ -808,18 +821,24 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
     ok(hipGetLastError());
   }
   // 3. dS = dY^T diag(E) C, then the reverse pass: dHn per chunk, dinit
-  ok(gemm(op(p.dYp, 1, H * P, Tp * H * P, Q * H * P, P), Ct, blk(p.S, false), none(), vec(p.E), Pi, Ni, Qi, Bi, Ki, Hi,
-          0.f, s));
+  if (cs_kernel)
+    ok(chunk_states(p.dy, p.C, p.E));
+  else
+    ok(gemm(op(p.dYp, 1, H * P, Tp * H * P, Q * H * P, P), Ct, blk(p.S, false), none(), vec(p.E), Pi, Ni, Qi, Bi, Ki,
+            Hi, 0.f, s));
   if (e == hipSuccess) {
     hipLaunchKernelGGL(chunk_recursion, dim3(grid_for(nst)), dim3(256), 0, s, p.S, p.gcum, p.dfinal, p.dhn, p.dinit,
                        nc, Tp, Q, PN, nst, 1);
     ok(hipGetLastError());
   }
-  // 6. U = B dHn^T, V = C Hprev^T (rows j: dHn B_j, Hprev C_j)
-  const Operand Uo = op(p.U, P, 1, nc * H * Q * P, H * Q * P, Q * P), Vo = op(p.V, P, 1, nc * H * Q * P, H * Q * P, Q * P);
-  ok(gemm(Bt, blk(p.dhn, true), Uo, none(), none(), Qi, Pi, Ni, Bi, Ki, Hi, 0.f, s));
-  ok(gemm(Ct, blk(p.hprev, true), Vo, none(), none(), Qi, Pi, Ni, Bi, Ki, Hi, 0.f, s));
   const bool fused = bwd_fused_supported(p.io, P, N, Q);
+  if (!fused) {
+    // 6. U = B dHn^T, V = C Hprev^T (rows j: dHn B_j, Hprev C_j)
+    const Operand Uo = op(p.U, P, 1, nc * H * Q * P, H * Q * P, Q * P);
+    const Operand Vo = op(p.V, P, 1, nc * H * Q * P, H * Q * P, Q * P);
+    ok(gemm(Bt, blk(p.dhn, true), Uo, none(), none(), Qi, Pi, Ni, Bi, Ki, Hi, 0.f, s));
+    ok(gemm(Ct, blk(p.hprev, true), Vo, none(), none(), Qi, Pi, Ni, Bi, Ki, Hi, 0.f, s));
+  }
   if (fused) {
     // 4, 5, 7 and the group sums of W2 in one pass over each chunk's heads
     ok(launch_bwd_fused_qq(p, p.DX, bwd_fused_segments(bt, nc, H, G), s));
@@ -859,7 +878,10 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
     ok(gemm(W2g, Bg, dCg, none(), none(), Qi, Ni, Qi, Bi, Ki, (int)G, 0.f, s, kKToRow, &dY, &hpv, &ev, Pi, hpg));
   }
   // 9. dx, ddt and the dA / dD parts; then the group and head sums
-  if (e == hipSuccess && bt * nc * H > 0) {
+  if (fused) {
+    // with U and V formed on the fly
+    ok(launch_bwd_fused_finish(p, s));
+  } else if (e == hipSuccess && bt * nc * H > 0) {
     hipLaunchKernelGGL(finish_chunk, dim3((unsigned)(bt * nc * H)), dim3(256), 0, s, p);
     ok(hipGetLastError());
   }
