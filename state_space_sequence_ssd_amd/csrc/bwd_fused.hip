@@ -466,7 +466,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     const float* __restrict__ dtt, const float* __restrict__ wst, const float* __restrict__ hprev,
     const float* __restrict__ dhn, const float* __restrict__ dXp, const float* __restrict__ rowZ,
     const float* __restrict__ colZ, const float* __restrict__ colW, float* __restrict__ dx, float* __restrict__ ddt,
-    float* __restrict__ dA_part, float* __restrict__ dD_part, int64_t Tlen, int H, int G, int64_t nc, int64_t Tp) {
+    float* __restrict__ dA_part, float* __restrict__ dD_part, uint4* __restrict__ dhnT, uint4* __restrict__ hpT,
+    int64_t Tlen, int H, int G, int64_t nc, int64_t Tp) {
   using Frag = bf16x8;
   using Cf = FinCfg<N>;
   constexpr int KS = N / 16, RP = Cf::RP;
@@ -530,6 +531,40 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     }
   }
   __syncthreads();
+
+  // ---- the states transposed into bf16 (hi, lo) MFMA fragments (column n,
+  // 8 consecutive headdim rows per lane), in the order the head-summed dB and
+  // dC products read them: each 16-lane group
+  // gathers 16 columns of 8 rows with the transposing LDS read (lane
+  // u = a + 4 m supplies row m of 4, columns 4 a .. 4 a + 3; lane u receives
+  // column u of the 4 rows)
+  {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const int gi = v * 4 + (lane >> 4), u = lane & 15, ta = u & 3, tm = u >> 2;
+    const int64_t tb = ((b * H + h) * nc + k) * (int64_t)N;   // first (n) row of this tile
+#pragma unroll
+    for (int j = 0; j < N / 64; ++j) {
+      const int it = gi + 32 * j, pg = it % 8, nblk = it / 8;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        uint64_t q[2][2];   // [plane hi/lo][row half]
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint32_t row = (uint32_t)(8 * pg + 4 * hh + tm);
+          const uint32_t off = row * (N * 2) + (spiece<RP>(row, (uint32_t)(2 * nblk + (ta >> 1))) << 4) + 8u * (ta & 1);
+#pragma unroll
+          for (int pl = 0; pl < 2; ++pl)
+            q[pl][hh] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(sS + (2 * st + pl) * Cf::PLANE + off)));
+        }
+        // fragment order: [n block of 32][k-step][plane][lane], lane = 32 (pg % 2) + n % 32
+        const int n = 16 * nblk + u;
+        uint4* dst = (st == 0 ? dhnT : hpT) + (((tb / 32 + n / 32) * 4 + pg / 2) * 2) * 64 + 32 * (pg % 2) + n % 32;
+        dst[0] = make_uint4((uint32_t)q[0][0], (uint32_t)(q[0][0] >> 32), (uint32_t)q[0][1], (uint32_t)(q[0][1] >> 32));
+        dst[64] = make_uint4((uint32_t)q[1][0], (uint32_t)(q[1][0] >> 32), (uint32_t)q[1][1], (uint32_t)(q[1][1] >> 32));
+      }
+    }
+  }
 
   // ---- U and V for token block v, both headdim halves
   f32x16 U[2], V[2];
@@ -674,6 +709,117 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   }
 }
 
+// ---------------------------------------------------------------- head sums
+// The carried-state parts of dB and dC, summed over a group's heads:
+//
+//   dB_t += sum_h w_t^h  x_t^h  dHn^h      dC_t += sum_h E_t^h dY_t^h Hprev^h
+//
+// (per chunk; rows t of the chunk, columns n), i.e. one product per chunk
+// with a contraction over (head, headdim). The row scale times x is split
+// into a bf16 (hi, lo) pair; the states arrive as (hi, lo) MFMA fragments
+// from the finishing kernel; three MFMAs per step (hi.hi, hi.lo, lo.hi).
+// A workgroup computes a 64 x 64 tile (tokens x dstate columns), one 32 x 32
+// block per wave, walking the group's heads; each head's x rows, state
+// fragments and scale row come in by direct global->LDS loads one head
+// ahead. The eight tiles of a (batch row, chunk, group) run on one XCD, so
+// its x rows and states are read from HBM once.
+template <int N>
+struct HsCfg {
+  static constexpr int XB = 64 * 128;              // x rows of the tile, one head
+  static constexpr int SB = 2 * 4 * 2 * 1024;      // state fragments of the tile's 2 column blocks
+  static constexpr int GB = 1024;                  // the head's scale row (the whole chunk)
+  static constexpr int BUF = XB + SB + GB;
+  static constexpr int NI = (XB + SB + GB) / 1024; // direct loads per head
+};
+
+template <int N>
+__global__ __launch_bounds__(256) void ssd_bwd_headsum(const bf16* __restrict__ X, const float* __restrict__ scale,
+                                                       const uint4* __restrict__ ST, float* __restrict__ out,
+                                                       int64_t Tlen, int H, int G, int64_t nc, int64_t Tp,
+                                                       int64_t nbkg) {
+  using Frag = bf16x8;
+  using Cf = HsCfg<N>;
+  constexpr int NT = N / 64;
+  constexpr int ITEMS = (kQ / 64) * NT;   // tiles per (batch row, chunk, group)
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2][Cf::BUF];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hf = lane >> 5, jl = lane & 31;
+  // XCD-aware order: workgroup tau runs on XCD tau % 8; the ITEMS tiles of
+  // one (b, k, g) share an XCD
+  const int64_t tau = blockIdx.x, xcd = tau % 8, slot = tau / 8;
+  const int64_t bkg = (slot / ITEMS) * 8 + xcd;
+  if (bkg >= nbkg) return;
+  const int item = (int)(slot % ITEMS);
+  const int nt = item % NT, itile = item / NT;
+  const int grp = (int)(bkg % G);
+  const int64_t k = (bkg / G) % nc, b = bkg / G / nc;
+  const int64_t t0 = k * kQ;
+  const int nvalid = (int)(Tlen - t0 < kQ ? Tlen - t0 : kQ);
+  const int hpg = H / G;
+  const uint32_t xrs = (uint32_t)(H * kP * 2);
+  // the tile's rows t0 + 64 itile + 0..63 of X (rows past the sequence: zeros)
+  const int rows = nvalid - 64 * itile;   // may be <= 0: then every row is zero
+  const uint32_t xbytes = rows > 0 ? (uint32_t)(rows - 1) * xrs + (uint32_t)(H * kP * 2) : 0u;
+  const bf16* xt = X + (b * Tlen + t0 + (rows > 0 ? 64 * itile : 0)) * H * kP;
+
+  auto load_head = [&](int hl, int bi) __attribute__((always_inline)) {
+    const int h = grp * hpg + hl;
+    unsigned char* base = lds[bi];
+    const __amdgpu_buffer_rsrc_t rx = lookback::urs(xt, xbytes);
+    // instruction m (of NI) covers 1 KB of the buffer; wave w issues m = w, w + 4, ...
+    for (int m = w; m < Cf::NI; m += 4) {
+      if (m < Cf::XB / 1024) {
+        // x rows 8 m .. 8 m + 7; piece q of row r at q ^ ((r >> 1) & 7)
+        const uint32_t r = 8u * m + ((uint32_t)lane >> 3), qp = (uint32_t)lane & 7;
+        const uint32_t q = qp ^ ((r >> 1) & 7u);
+        lookback::bdma16<false>(rx, r * xrs + (uint32_t)h * (kP * 2) + q * 16u, 0, base + 1024 * m);
+      } else if (m < (Cf::XB + Cf::SB) / 1024) {
+        // state fragments: (column block c, k-step kk, plane pl) = 1 KB each
+        const int f = m - Cf::XB / 1024, c = f / 8, kk = (f / 2) % 4, pl = f % 2;
+        const uint4* src = ST + ((((((b * H + h) * nc + k) * (N / 32)) + 2 * nt + c) * 4 + kk) * 2 + pl) * 64;
+        lookback::dma16<false>(src, (uint32_t)lane * 16u, base + 1024 * m);
+      } else {
+        lookback::dma16<false>(scale + (b * H + h) * Tp + t0, (uint32_t)lane * 16u, base + 1024 * m);
+      }
+    }
+  };
+
+  f32x16 acc = f32x16{};
+  const int wi = w >> 1, wn = w & 1;
+  const uint32_t arow = (uint32_t)(32 * wi + jl);    // this lane's A row within the tile
+  load_head(0, 0);
+  for (int hl = 0; hl < hpg; ++hl) {
+    const int bi = hl & 1;
+    lookback::vm_lds_barrier();
+    if (hl + 1 < hpg) load_head(hl + 1, bi ^ 1);
+    const unsigned char* cur = lds[bi];
+    const float sc = reinterpret_cast<const float*>(cur + Cf::XB + Cf::SB)[64 * itile + arow];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint32_t q = (uint32_t)(2 * kk + hf);
+      const u32x4 xr = *reinterpret_cast<const u32x4*>(cur + arow * 128u + ((q ^ ((arow >> 1) & 7u)) << 4));
+      float xv[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xv[2 * e] = sc * bf16lo(xr[e]);
+        xv[2 * e + 1] = sc * bf16hi(xr[e]);
+      }
+      Frag ah, al;
+      Io<bf16>::split(xv, ah, al);
+      const unsigned char* sf = cur + Cf::XB + ((wn * 4 + kk) * 2) * 1024 + 16 * lane;
+      const Frag bh = *reinterpret_cast<const Frag*>(sf), bl = *reinterpret_cast<const Frag*>(sf + 1024);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
+    }
+  }
+  // rows 64 itile + 32 wi + drow(r, hf), column 64 nt + 32 wn + jl
+  float* o = out + ((b * Tp + t0 + 64 * itile + 32 * wi) * G + grp) * (int64_t)N + 64 * nt + 32 * wn + jl;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) o[(int64_t)drow(r, hf) * G * N] = acc[r];
+}
+
 }  // namespace
 
 bool bwd_fused_supported(int io, int64_t P, int64_t N, int64_t Q) {
@@ -721,6 +867,21 @@ hipError_t launch_bwd_fused_qq(const BwdProblem& p, float* w2part, int nseg, hip
   return hipGetLastError();
 }
 
+hipError_t launch_bwd_fused_headsum(const BwdProblem& p, const void* X, const float* scale, const void* ST,
+                                    float* out, hipStream_t s) {
+  const int64_t nbkg = p.bt * p.nc * p.G;
+  const int64_t items = (nbkg + 7) / 8 * 8 * (kQ / 64) * (p.N / 64);
+  if (nbkg <= 0 || p.H <= 0) return hipSuccess;
+  if (items > 0x7fffffff) return hipErrorInvalidValue;
+  if (p.N == 64)
+    hipLaunchKernelGGL(ssd_bwd_headsum<64>, dim3((unsigned)items), dim3(256), 0, s, (const bf16*)X, scale,
+                       (const uint4*)ST, out, p.T, (int)p.H, (int)p.G, p.nc, p.Tp, nbkg);
+  else
+    hipLaunchKernelGGL(ssd_bwd_headsum<128>, dim3((unsigned)items), dim3(256), 0, s, (const bf16*)X, scale,
+                       (const uint4*)ST, out, p.T, (int)p.H, (int)p.G, p.nc, p.Tp, nbkg);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_fused_finish(const BwdProblem& p, hipStream_t s) {
   const int64_t items = p.bt * p.nc * p.H;
   if (items <= 0) return hipSuccess;
@@ -732,11 +893,11 @@ hipError_t launch_bwd_fused_finish(const BwdProblem& p, hipStream_t s) {
   if (p.N == 64)
     hipLaunchKernelGGL(ssd_bwd_state_finish<64>, dim3((unsigned)items), dim3(512), 0, s, x, dy, Bm, Cm, p.A, p.D,
                        p.gcum, p.dtt, p.wst, p.hprev, p.dhn, p.dXp, p.rowZ, p.colZ, p.colW, p.dx, p.ddt, p.dA_part,
-                       p.dD_part, p.T, (int)p.H, (int)p.G, p.nc, p.Tp);
+                       p.dD_part, (uint4*)p.U, (uint4*)p.V, p.T, (int)p.H, (int)p.G, p.nc, p.Tp);
   else
     hipLaunchKernelGGL(ssd_bwd_state_finish<128>, dim3((unsigned)items), dim3(512), 0, s, x, dy, Bm, Cm, p.A, p.D,
                        p.gcum, p.dtt, p.wst, p.hprev, p.dhn, p.dXp, p.rowZ, p.colZ, p.colW, p.dx, p.ddt, p.dA_part,
-                       p.dD_part, p.T, (int)p.H, (int)p.G, p.nc, p.Tp);
+                       p.dD_part, (uint4*)p.U, (uint4*)p.V, p.T, (int)p.H, (int)p.G, p.nc, p.Tp);
   return hipGetLastError();
 }
 

@@ -56,6 +56,12 @@ int bwd_fused_segments(int64_t bt, int64_t nc, int64_t H, int64_t G);
 hipError_t launch_bwd_fused_qq(const BwdProblem& p, float* w2part, int nseg, hipStream_t stream);
 // The same shapes: U = B dHn^T and V = C Hprev^T formed on the fly with dx,
 // ddt and the dA / dD parts (in place of the U, V products and finish_chunk).
+// It also writes dHn and Hprev transposed, [n][p] in bf16 (hi, lo) pairs,
+// into the U and V regions, for:
 hipError_t launch_bwd_fused_finish(const BwdProblem& p, hipStream_t stream);
+// out[t][g][n] = sum over the group's heads of scale_t^h X_t^h S^h (the
+// carried-state parts of dB and dC; ST: the transposed states above).
+hipError_t launch_bwd_fused_headsum(const BwdProblem& p, const void* X, const float* scale, const void* ST,
+                                    float* out, hipStream_t stream);
 
 }  // namespace ssd

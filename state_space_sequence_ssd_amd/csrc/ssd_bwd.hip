@@ -776,8 +776,11 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
         hipLaunchKernelGGL(pad_rows<float>, dim3(grid_for(n)), dim3(256), 0, s, (const float*)src, dst, T, Tp, W, n);
     }
   };
-  pad(p.x, p.Xp, H * P, nx);
-  pad(p.dy, p.dYp, H * P, nx);
+  const bool fused = bwd_fused_supported(p.io, P, N, Q);
+  if (!fused) {   // (the fused kernels read x and dy as they are)
+    pad(p.x, p.Xp, H * P, nx);
+    pad(p.dy, p.dYp, H * P, nx);
+  }
   pad(p.B, p.Bp, G * N, nb);
   pad(p.C, p.Cp, G * N, nb);
   const int64_t ng = bt * H * Tp;
@@ -831,7 +834,6 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
                        nc, Tp, Q, PN, nst, 1);
     ok(hipGetLastError());
   }
-  const bool fused = bwd_fused_supported(p.io, P, N, Q);
   if (!fused) {
     // 6. U = B dHn^T, V = C Hprev^T (rows j: dHn B_j, Hprev C_j)
     const Operand Uo = op(p.U, P, 1, nc * H * Q * P, H * Q * P, Q * P);
@@ -868,22 +870,28 @@ hipError_t launch_ssd_bwd(BwdProblem p, hipStream_t s) {
   // 8. dB_h = W2s^T C + diag(w) X dHn;  dC_h = W2s B + diag(E) dY Hprev
   // per (b, k, group): B and C are shared by the group's heads, so the
   // causal products take the sum of the heads' W2s blocks, and the state
-  // products sum the heads' parts inside the kernel
-  {
-    const Operand W2g = op(p.CB, Q, 1, nc * G * QQ, G * QQ, QQ), W2gT = op(p.CB, 1, Q, nc * G * QQ, G * QQ, QQ);
-    const Operand Bg = op(p.Bp, G * N, 1, Tp * G * N, Q * G * N, N), Cg = op(p.Cp, G * N, 1, Tp * G * N, Q * G * N, N);
-    const Operand dBg = op(p.dBh, G * N, 1, Tp * G * N, Q * G * N, N), dCg = op(p.dCh, G * N, 1, Tp * G * N, Q * G * N, N);
+  // products sum the heads' parts
+  // 9. dx, ddt and the dA / dD parts; then the group and head sums
+  const Operand W2g = op(p.CB, Q, 1, nc * G * QQ, G * QQ, QQ), W2gT = op(p.CB, 1, Q, nc * G * QQ, G * QQ, QQ);
+  const Operand Bg = op(p.Bp, G * N, 1, Tp * G * N, Q * G * N, N), Cg = op(p.Cp, G * N, 1, Tp * G * N, Q * G * N, N);
+  const Operand dBg = op(p.dBh, G * N, 1, Tp * G * N, Q * G * N, N), dCg = op(p.dCh, G * N, 1, Tp * G * N, Q * G * N, N);
+  if (fused) {
+    // the finishing kernel (U and V formed on the fly) also leaves the states
+    // transposed for the head-summed state products; the causal products are
+    // added on top
+    ok(launch_bwd_fused_finish(p, s));
+    ok(launch_bwd_fused_headsum(p, p.x, p.wst, p.U, p.dBh, s));
+    ok(launch_bwd_fused_headsum(p, p.dy, p.E, p.V, p.dCh, s));
+    ok(gemm(W2gT, Cg, dBg, none(), none(), Qi, Ni, Qi, Bi, Ki, (int)G, 1.f, s, kKFromRow));
+    ok(gemm(W2g, Bg, dCg, none(), none(), Qi, Ni, Qi, Bi, Ki, (int)G, 1.f, s, kKToRow));
+  } else {
     const Operand dhn = blk(p.dhn, false), hpv = blk(p.hprev, false), w = vec(p.wst), ev = vec(p.E);
     ok(gemm(W2gT, Cg, dBg, none(), none(), Qi, Ni, Qi, Bi, Ki, (int)G, 0.f, s, kKFromRow, &X, &dhn, &w, Pi, hpg));
     ok(gemm(W2g, Bg, dCg, none(), none(), Qi, Ni, Qi, Bi, Ki, (int)G, 0.f, s, kKToRow, &dY, &hpv, &ev, Pi, hpg));
-  }
-  // 9. dx, ddt and the dA / dD parts; then the group and head sums
-  if (fused) {
-    // with U and V formed on the fly
-    ok(launch_bwd_fused_finish(p, s));
-  } else if (e == hipSuccess && bt * nc * H > 0) {
-    hipLaunchKernelGGL(finish_chunk, dim3((unsigned)(bt * nc * H)), dim3(256), 0, s, p);
-    ok(hipGetLastError());
+    if (e == hipSuccess && bt * nc * H > 0) {
+      hipLaunchKernelGGL(finish_chunk, dim3((unsigned)(bt * nc * H)), dim3(256), 0, s, p);
+      ok(hipGetLastError());
+    }
   }
   const int64_t nbo = bt * T * G * N;
   if (e == hipSuccess && nbo > 0) {
