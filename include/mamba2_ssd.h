@@ -354,12 +354,18 @@ int mamba2_ssd_step(const mamba2_ssd_step_dims* dims, int io_dtype,
  *                                          heads of each group)
  *   dA  [nheads]   dD [nheads]             (sums over batch rows and tokens)
  *   dinit [batch][nheads][headdim][dstate] (nullable: not written)
- * Arithmetic: fp32 throughout (bf16 inputs are exact in fp32).
+ * Arithmetic: fp32 accumulation everywhere. With bf16 io, headdim 64,
+ * chunk 256 and dstate 64 or 128 the products run on the bf16 MFMA: bf16
+ * inputs enter exactly, fp32 intermediates (decayed blocks, states, scaled
+ * rows) as bf16 (hi, lo) pairs, about 2^-17 relative per operand; other
+ * shapes and fp32 io use fp32 operands.
  * Workspace: mamba2_ssd_bwd_workspace_bytes(dims, io) bytes, device memory,
- * 256-byte aligned; it holds padded fp32 copies of the inputs, the chunk
- * states, the per-chunk C.B^T and dy.x^T blocks and the per-group parts of
- * dB and dC (about 9.9 GB for batch 4, seqlen 8192, 80 heads, headdim 64,
- * dstate 128, chunk 256). Sizes are those of mamba2_ssd_fwd, plus
+ * 256-byte aligned; it holds the chunk cumsums, the chunk states and their
+ * adjoints, the per-group C.B^T-weighted sums and the per-token partial
+ * results; for shapes off the bf16 path above also padded fp32 copies of
+ * the inputs and the per-head C.B^T and dy.x^T blocks (batch 4, seqlen
+ * 8192, 80 heads, headdim 64, dstate 128, chunk 256: 2.6 GB with bf16 io,
+ * 9.9 GB with fp32 io). Sizes are those of mamba2_ssd_fwd, plus
  * batch * nchunks * nheads <= 65535.
  * Errors: as mamba2_ssd_check_args (NULL_POINTER for a missing required
  * pointer: A, D, dA, dD always; x, dt, B, C, dy, dx, ddt, dB, dC when

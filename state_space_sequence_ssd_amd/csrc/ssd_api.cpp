@@ -396,7 +396,7 @@ static int bwd_sizes(const mamba2_ssd_dims* d, int io_dtype, Sizes* s, ssd::BwdL
   // the GEMM batches (batch, chunk, head) go in grid dimension y
   int64_t z;
   if (!mul_ok(d->batch, s->nc, &z) || !mul_ok(z, d->nheads, &z) || z > ssd::kMaxGridYZ) return MAMBA2_SSD_ERR_BAD_DIM;
-  *L = ssd::bwd_layout(d->batch, d->nheads, d->headdim, d->dstate, d->ngroups, d->chunk, s->nc);
+  *L = ssd::bwd_layout(d->batch, d->nheads, d->headdim, d->dstate, d->ngroups, d->chunk, s->nc, io_dtype);
   return MAMBA2_SSD_OK;
 }
 

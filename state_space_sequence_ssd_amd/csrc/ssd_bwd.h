@@ -13,12 +13,12 @@ namespace ssd {
 // Byte offsets of the backward workspace's arrays (all fp32, 256-byte aligned).
 struct BwdLayout {
   size_t gcum, dtt, wst, E;             // [bt][H][Tp]
-  size_t Xp, dYp;                       // [bt][Tp][H][P], zero padded
+  size_t Xp, dYp;                       // [bt][Tp][H][P], zero padded (empty on the fused path)
   size_t Bp, Cp;                        // [bt][Tp][G][N], zero padded
   size_t S, hprev, dhn;                 // [bt][H][nc][P][N]
   size_t CB;                            // [bt][nc][G][Q][Q] (C B^T, then the group's sum of W2s)
-  size_t DX, W1;                        // [bt][nc][H][Q][Q]
-  size_t U, V;                          // [bt][nc][H][Q][P]
+  size_t DX, W1;                        // [bt][nc][H][Q][Q] (fused path: DX = per-segment W2 sums, W1 empty)
+  size_t U, V;                          // [bt][nc][H][Q][P] (fused path: transposed dHn, Hprev fragments)
   size_t dXp;                           // [bt][Tp][H][P]
   size_t dBh, dCh;                      // [bt][Tp][G][N]
   size_t rowZ, colZ, colW;              // [bt][H][Tp]
@@ -26,7 +26,8 @@ struct BwdLayout {
   size_t total;
 };
 
-BwdLayout bwd_layout(int64_t bt, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q, int64_t nc);
+// (io selects the layout: the fused path of bwd_fused.hip needs less)
+BwdLayout bwd_layout(int64_t bt, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q, int64_t nc, int io);
 
 struct BwdProblem {
   int64_t bt, T, H, P, N, G, Q, nc, Tp;

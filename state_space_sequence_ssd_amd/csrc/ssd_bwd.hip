@@ -711,8 +711,12 @@ unsigned grid_for(int64_t total) {
 
 }  // namespace
 
-BwdLayout bwd_layout(int64_t bt, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q, int64_t nc) {
+BwdLayout bwd_layout(int64_t bt, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q, int64_t nc, int io) {
   BwdLayout L{};
+  // the fused kernels need no padded x or dy and no per-head Q x Q blocks:
+  // DX holds the per-segment W2 sums, U and V the transposed states
+  const bool fused = bwd_fused_supported(io, P, N, Q);
+  const int64_t nseg = fused ? bwd_fused_segments(bt, nc, H, G) : 0;
   const int64_t Tp = nc * Q;
   size_t off = 0;
   auto take = [&](size_t floats) {
@@ -724,18 +728,18 @@ BwdLayout bwd_layout(int64_t bt, int64_t H, int64_t P, int64_t N, int64_t G, int
   L.dtt = take(bt * H * Tp);
   L.wst = take(bt * H * Tp);
   L.E = take(bt * H * Tp);
-  L.Xp = take(bt * Tp * H * P);
-  L.dYp = take(bt * Tp * H * P);
+  L.Xp = take(fused ? 0 : bt * Tp * H * P);
+  L.dYp = take(fused ? 0 : bt * Tp * H * P);
   L.Bp = take(bt * Tp * G * N);
   L.Cp = take(bt * Tp * G * N);
   L.S = take(bt * H * nc * P * N);
   L.hprev = take(bt * H * nc * P * N);
   L.dhn = take(bt * H * nc * P * N);
   L.CB = take(bt * nc * G * Q * Q);
-  L.DX = take(bt * nc * H * Q * Q);
-  L.W1 = take(bt * nc * H * Q * Q);
-  L.U = take(bt * nc * H * Q * P);
-  L.V = take(bt * nc * H * Q * P);
+  L.DX = take(fused ? bt * nc * G * nseg * Q * Q : bt * nc * H * Q * Q);
+  L.W1 = take(fused ? 0 : bt * nc * H * Q * Q);
+  L.U = take(fused ? bt * H * nc * P * N : bt * nc * H * Q * P);
+  L.V = take(fused ? bt * H * nc * P * N : bt * nc * H * Q * P);
   L.dXp = take(bt * Tp * H * P);
   L.dBh = take(bt * Tp * G * N);
   L.dCh = take(bt * Tp * G * N);
