@@ -416,8 +416,16 @@ def test_bwd_workspace_and_valid_call():
         assert ssd.bwd_workspace_bytes(BWD_SMALL, io) > 0
         assert _bwd_check(BWD_SMALL, io) == OK
         assert _bwd_check(BWD_SMALL, io, init=0, dfinal=0, dinit=0) == OK
-    # the headline layer: about 9.9 GB of workspace
-    assert 9.5e9 < ssd.bwd_workspace_bytes(HEADLINE, BF16) < 10.5e9
+    # the headline layer: fp32 io keeps padded copies and per-head Q x Q
+    # blocks (about 9.9 GB); the bf16 fused path needs only these arrays
+    assert 9.5e9 < ssd.bwd_workspace_bytes(HEADLINE, F32) < 10.5e9
+    bt, T, H, P, N, G, Q = 4, 8192, 80, 64, 128, 1, 256
+    nc, Tp = T // Q, T
+    nseg = 2   # (b, k, g) items = 128: two head segments make 256 workgroups
+    floats = ([bt * H * Tp] * 4 + [bt * Tp * G * N] * 2 + [bt * H * nc * P * N] * 3 + [bt * nc * G * Q * Q]
+              + [bt * nc * G * nseg * Q * Q] + [bt * H * nc * P * N] * 2 + [bt * Tp * H * P]
+              + [bt * Tp * G * N] * 2 + [bt * H * Tp] * 3 + [bt * H * nc] * 2)
+    assert ssd.bwd_workspace_bytes(HEADLINE, BF16) == sum((4 * f + 255) // 256 * 256 for f in floats)
 
 
 def test_bwd_rejects_bad_calls():
