@@ -725,11 +725,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
 // its x rows and states are read from HBM once.
 template <int N>
 struct HsCfg {
-  static constexpr int XB = 64 * 128;              // x rows of the tile, one head
-  static constexpr int SB = 2 * 4 * 2 * 1024;      // state fragments of the tile's 2 column blocks
+  static constexpr int TT = 128;                   // tokens per tile
+  static constexpr int RB = N == 128 ? 2 : 1;      // 32-row blocks per wave
+  static constexpr int NB = N / 32;                // 32-column blocks per tile (2 per wave)
+  static constexpr int XB = TT * 128;              // x rows of the tile, one head
+  static constexpr int SB = NB * 4 * 2 * 1024;     // state fragments of the tile's column blocks
   static constexpr int GB = 1024;                  // the head's scale row (the whole chunk)
   static constexpr int BUF = XB + SB + GB;
-  static constexpr int NI = (XB + SB + GB) / 1024; // direct loads per head
+  static constexpr int NI = BUF / 1024;            // direct loads per head
+  static constexpr int ITEMS = kQ / TT;            // tiles per (batch row, chunk, group)
 };
 
 template <int N>
@@ -739,35 +743,35 @@ __global__ __launch_bounds__(256) void ssd_bwd_headsum(const bf16* __restrict__ 
                                                        int64_t nbkg) {
   using Frag = bf16x8;
   using Cf = HsCfg<N>;
-  constexpr int NT = N / 64;
-  constexpr int ITEMS = (kQ / 64) * NT;   // tiles per (batch row, chunk, group)
+  constexpr int RB = Cf::RB;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2][Cf::BUF];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hf = lane >> 5, jl = lane & 31;
-  // XCD-aware order: workgroup tau runs on XCD tau % 8; the ITEMS tiles of
-  // one (b, k, g) share an XCD
+  // XCD-aware order: workgroup tau runs on XCD tau % 8; the tiles of one
+  // (b, k, g) share an XCD
   const int64_t tau = blockIdx.x, xcd = tau % 8, slot = tau / 8;
-  const int64_t bkg = (slot / ITEMS) * 8 + xcd;
+  const int64_t bkg = (slot / Cf::ITEMS) * 8 + xcd;
   if (bkg >= nbkg) return;
-  const int item = (int)(slot % ITEMS);
-  const int nt = item % NT, itile = item / NT;
+  const int itile = (int)(slot % Cf::ITEMS);
   const int grp = (int)(bkg % G);
   const int64_t k = (bkg / G) % nc, b = bkg / G / nc;
   const int64_t t0 = k * kQ;
   const int nvalid = (int)(Tlen - t0 < kQ ? Tlen - t0 : kQ);
   const int hpg = H / G;
   const uint32_t xrs = (uint32_t)(H * kP * 2);
-  // the tile's rows t0 + 64 itile + 0..63 of X (rows past the sequence: zeros)
-  const int rows = nvalid - 64 * itile;   // may be <= 0: then every row is zero
+  // the tile's rows t0 + TT itile + 0 .. TT - 1 of X (rows past the sequence: zeros)
+  const int rows = nvalid - Cf::TT * itile;
   const uint32_t xbytes = rows > 0 ? (uint32_t)(rows - 1) * xrs + (uint32_t)(H * kP * 2) : 0u;
-  const bf16* xt = X + (b * Tlen + t0 + (rows > 0 ? 64 * itile : 0)) * H * kP;
+  const bf16* xt = X + (b * Tlen + t0 + (rows > 0 ? Cf::TT * itile : 0)) * H * kP;
+  // wave w: rows rb0 .. rb0 + 32 RB - 1, columns of blocks cb0, cb0 + 1
+  const int rb0 = RB == 2 ? 64 * (w >> 1) : 32 * w;
+  const int cb0 = RB == 2 ? 2 * (w & 1) : 0;
 
   auto load_head = [&](int hl, int bi) __attribute__((always_inline)) {
     const int h = grp * hpg + hl;
     unsigned char* base = lds[bi];
     const __amdgpu_buffer_rsrc_t rx = lookback::urs(xt, xbytes);
-    // instruction m (of NI) covers 1 KB of the buffer; wave w issues m = w, w + 4, ...
     for (int m = w; m < Cf::NI; m += 4) {
       if (m < Cf::XB / 1024) {
         // x rows 8 m .. 8 m + 7; piece q of row r at q ^ ((r >> 1) & 7)
@@ -775,9 +779,9 @@ __global__ __launch_bounds__(256) void ssd_bwd_headsum(const bf16* __restrict__ 
         const uint32_t q = qp ^ ((r >> 1) & 7u);
         lookback::bdma16<false>(rx, r * xrs + (uint32_t)h * (kP * 2) + q * 16u, 0, base + 1024 * m);
       } else if (m < (Cf::XB + Cf::SB) / 1024) {
-        // state fragments: (column block c, k-step kk, plane pl) = 1 KB each
-        const int f = m - Cf::XB / 1024, c = f / 8, kk = (f / 2) % 4, pl = f % 2;
-        const uint4* src = ST + ((((((b * H + h) * nc + k) * (N / 32)) + 2 * nt + c) * 4 + kk) * 2 + pl) * 64;
+        // state fragments: (column block c, k-step kk, plane pl), 1 KB each
+        const int f = m - Cf::XB / 1024;
+        const uint4* src = ST + (((b * H + h) * nc + k) * (N / 32) * 8 + f) * 64;
         lookback::dma16<false>(src, (uint32_t)lane * 16u, base + 1024 * m);
       } else {
         lookback::dma16<false>(scale + (b * H + h) * Tp + t0, (uint32_t)lane * 16u, base + 1024 * m);
@@ -785,39 +789,60 @@ __global__ __launch_bounds__(256) void ssd_bwd_headsum(const bf16* __restrict__ 
     }
   };
 
-  f32x16 acc = f32x16{};
-  const int wi = w >> 1, wn = w & 1;
-  const uint32_t arow = (uint32_t)(32 * wi + jl);    // this lane's A row within the tile
+  f32x16 acc[RB][2];
+#pragma unroll
+  for (int a = 0; a < RB; ++a) acc[a][0] = acc[a][1] = f32x16{};
   load_head(0, 0);
   for (int hl = 0; hl < hpg; ++hl) {
     const int bi = hl & 1;
     lookback::vm_lds_barrier();
     if (hl + 1 < hpg) load_head(hl + 1, bi ^ 1);
     const unsigned char* cur = lds[bi];
-    const float sc = reinterpret_cast<const float*>(cur + Cf::XB + Cf::SB)[64 * itile + arow];
+    const float* scl = reinterpret_cast<const float*>(cur + Cf::XB + Cf::SB) + Cf::TT * itile;
+    float sc[RB];
+#pragma unroll
+    for (int a = 0; a < RB; ++a) sc[a] = scl[rb0 + 32 * a + jl];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const uint32_t q = (uint32_t)(2 * kk + hf);
-      const u32x4 xr = *reinterpret_cast<const u32x4*>(cur + arow * 128u + ((q ^ ((arow >> 1) & 7u)) << 4));
-      float xv[8];
+      Frag ah[RB], al[RB], bh[2], bl[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xv[2 * e] = sc * bf16lo(xr[e]);
-        xv[2 * e + 1] = sc * bf16hi(xr[e]);
+      for (int a = 0; a < RB; ++a) {
+        const uint32_t ar = (uint32_t)(rb0 + 32 * a + jl);
+        const u32x4 xr = *reinterpret_cast<const u32x4*>(cur + ar * 128u + ((q ^ ((ar >> 1) & 7u)) << 4));
+        float xv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xv[2 * e] = sc[a] * bf16lo(xr[e]);
+          xv[2 * e + 1] = sc[a] * bf16hi(xr[e]);
+        }
+        Io<bf16>::split(xv, ah[a], al[a]);
       }
-      Frag ah, al;
-      Io<bf16>::split(xv, ah, al);
-      const unsigned char* sf = cur + Cf::XB + ((wn * 4 + kk) * 2) * 1024 + 16 * lane;
-      const Frag bh = *reinterpret_cast<const Frag*>(sf), bl = *reinterpret_cast<const Frag*>(sf + 1024);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const unsigned char* sf = cur + Cf::XB + (((cb0 + c) * 4 + kk) * 2) * 1024 + 16 * lane;
+        bh[c] = *reinterpret_cast<const Frag*>(sf);
+        bl[c] = *reinterpret_cast<const Frag*>(sf + 1024);
+      }
+#pragma unroll
+      for (int a = 0; a < RB; ++a)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a], bh[c], acc[a][c], 0, 0, 0);
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[a], bl[c], acc[a][c], 0, 0, 0);
+          acc[a][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[a], bh[c], acc[a][c], 0, 0, 0);
+        }
     }
   }
-  // rows 64 itile + 32 wi + drow(r, hf), column 64 nt + 32 wn + jl
-  float* o = out + ((b * Tp + t0 + 64 * itile + 32 * wi) * G + grp) * (int64_t)N + 64 * nt + 32 * wn + jl;
+  // rows TT itile + rb0 + 32 a + drow(r, hf), columns 32 (cb0 + c) + jl
 #pragma unroll
-  for (int r = 0; r < 16; ++r) o[(int64_t)drow(r, hf) * G * N] = acc[r];
+  for (int a = 0; a < RB; ++a)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float* o = out + ((b * Tp + t0 + Cf::TT * itile + rb0 + 32 * a) * G + grp) * (int64_t)N + 32 * (cb0 + c) + jl;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[(int64_t)drow(r, hf) * G * N] = acc[a][c][r];
+    }
 }
 
 }  // namespace
@@ -870,7 +895,7 @@ hipError_t launch_bwd_fused_qq(const BwdProblem& p, float* w2part, int nseg, hip
 hipError_t launch_bwd_fused_headsum(const BwdProblem& p, const void* X, const float* scale, const void* ST,
                                     float* out, hipStream_t s) {
   const int64_t nbkg = p.bt * p.nc * p.G;
-  const int64_t items = (nbkg + 7) / 8 * 8 * (kQ / 64) * (p.N / 64);
+  const int64_t items = (nbkg + 7) / 8 * 8 * (kQ / 128);
   if (nbkg <= 0 || p.H <= 0) return hipSuccess;
   if (items > 0x7fffffff) return hipErrorInvalidValue;
   if (p.N == 64)
