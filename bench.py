@@ -320,8 +320,15 @@ def run_bwd(args, cfg):
     ms = float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]))
     flops = bwd_flops(cfg)
     achieved = flops / (ms * 1e-3) / 1e12
+    fused = cfg.io == "bf16" and cfg.headdim == 64 and cfg.chunk == 256 and cfg.dstate in (64, 128)
+    peak = BF16_MFMA_PEAK_TFLOPS if fused else FP32_VALU_PEAK_TFLOPS
+    base = None
+    if not args.no_cpu:
+        host = {k: g[k].cpu().numpy() for k in ssd.GRAD_NAMES}
+        dy_used = round_to_bf16(dy)[0] if cfg.io == "bf16" else dy   # the values the GPU received
+        base = bwd_cpu_baseline(cfg, inp, dy_used, dfin, host, budget_s=args.cpu_budget)
     out = {
-        "metric": "SSD bwd tokens/sec at 2.7B-layer shape (1 GPU); % fp32 vector peak",
+        "metric": "SSD bwd tokens/sec at 2.7B-layer shape (1 GPU)",
         "value": round(cfg.tokens * args.steps / wall, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -331,20 +338,59 @@ def run_bwd(args, cfg):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if fused else "f32",
         "data": "synthetic",
         "config": {"workload": cfg.name + "-bwd", "batch": cfg.batch, "seqlen": cfg.seqlen, "nheads": cfg.nheads,
                    "headdim": cfg.headdim, "dstate": cfg.dstate, "ngroups": cfg.ngroups, "chunk": cfg.chunk,
                    "io": cfg.io, "seed": cfg.seed, "tokens_per_step": cfg.tokens},
-        "roofline": {"bound": "alu", "kernel": "whole backward call", "achieved": round(achieved, 2),
-                     "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / FP32_VALU_PEAK_TFLOPS, 4),
-                     "traffic": None},
+        # algorithmic flops of the whole call against the peak of the unit
+        # its products run on (bf16 MFMA on the fused path, else fp32)
+        "roofline": {"bound": "mfma" if fused else "alu", "kernel": "whole backward call",
+                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None},
         "gpu_event_ms_per_step": round(ms, 4),
         "alg_flops_per_step": int(flops),
         "workspace_bytes": int(nbytes),
-        "cpu_baseline": None,
+        "cpu_baseline": None if base is None else base[0],
     }
+    if base is not None:
+        out["cpu_parity"] = base[1]
     print(json.dumps(out), flush=True)
+
+
+BF16_MFMA_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+
+
+def bwd_cpu_baseline(cfg, inp, dy, dfin, g_gpu, budget_s=10.0):
+    """The chunked fp64 gradient oracle, as it stands, on batch row 0 of the
+    same layer (all heads, every token); its per-row gradients are compared
+    with the GPU's for that row (dA and dD sum over rows: not compared)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import ssd_bwd_chunked
+
+    cores = len(os.sched_getaffinity(0))
+    threads = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+    with threadpool_limits(limits=threads, user_api="blas"):
+        used = max([i["num_threads"] for i in threadpool_info() if i["user_api"] == "blas"] or [1])
+        init = None if inp["init_state"] is None else inp["init_state"][0:1]
+        t0 = time.perf_counter()
+        ref = ssd_bwd_chunked(inp["x"][0:1], inp["dt"][0:1], inp["A"], inp["B"][0:1], inp["C"][0:1], inp["D"],
+                              dy[0:1], cfg.chunk, init, dfin[0:1])
+        elapsed = time.perf_counter() - t0
+    worst = 0.0
+    for k in ("dx", "ddt", "dB", "dC", "dinit"):
+        if ref.get(k) is None:
+            continue
+        want = np.asarray(ref[k], dtype=np.float64)
+        got = np.asarray(g_gpu[k][0:1], dtype=np.float64)
+        worst = max(worst, float(np.max(np.abs(got - want))) / max(float(np.max(np.abs(want))), 1e-30) / 1e-4)
+    return {
+        "value": cfg.seqlen / elapsed, "unit": "tokens/s", "cores": int(used), "kind": "oracle",
+        "sample": (f"chunked fp64 gradient oracle on batch row 0 of {cfg.batch} ({cfg.seqlen} tokens, all "
+                   f"{cfg.nheads} heads), {elapsed:.1f} s"),
+        "seconds": elapsed,
+    }, {"row_checked": 0, "worst_normwise_err_over_1e-4": worst, "ok": worst <= 1.0}
 
 
 def run_s6(args, cfg):
