@@ -18,7 +18,9 @@ kernels:
   the chunked form, independently of each other (``ssd_bwd.py``; pinned in
   ``tests/test_oracle_bwd.py``).
 * ``s6_sequential`` -- the Mamba-1 selective scan (S6) token by token, the
-  family's second member (``s6.py``; pinned in ``tests/test_oracle_s6.py``).
+  family's second member (``s6.py``; pinned in ``tests/test_oracle_s6.py``),
+  and ``s6_bwd_sequential``, its every-input gradient by reverse mode through
+  the same recurrence (pinned in ``tests/test_oracle_s6_bwd.py``).
 
 Both upcast every input to float64 and never round to a narrower type.
 
@@ -33,7 +35,7 @@ from .ssd_seq import ssd_sequential, heads_to_groups
 from .ssd_chunked import ssd_chunked
 from .ssd_step import ssd_step
 from .ssd_bwd import ssd_bwd_chunked, ssd_bwd_sequential
-from .s6 import s6_sequential
+from .s6 import s6_bwd_sequential, s6_sequential
 
 __all__ = ["ssd_sequential", "ssd_chunked", "ssd_step", "heads_to_groups", "ssd_bwd_sequential",
-           "ssd_bwd_chunked", "s6_sequential"]
+           "ssd_bwd_chunked", "s6_sequential", "s6_bwd_sequential"]
