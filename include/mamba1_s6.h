@@ -64,10 +64,55 @@ int mamba1_s6_check_args(const mamba1_s6_dims* dims, const float* x, const float
                          const float* y, const float* hT, const void* workspace,
                          size_t workspace_bytes);
 
-/* The scan; returns a status code after enqueueing its three kernels. */
+/* The scan; returns a status code after enqueueing its kernels (the clearing
+ * of the workspace's counter and flags, then the one-pass scan). */
 int mamba1_s6_fwd(const mamba1_s6_dims* dims, const float* x, const float* delta,
                   const float* A, const float* B, const float* C, const float* h0,
                   float* y, float* hT, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- backward pass -------------------------------------------------------
+ *
+ * Every input's gradient of the scan above for a loss whose gradients with
+ * respect to its outputs are dy (like y) and dhT (like hT; NULL means zero).
+ * The state's adjoint g runs the same scan backwards in time ("Mamba: The
+ * Hard Way", Part 3, applied to each scalar chain of Part 5):
+ *
+ *     g_t = C[b,n,t] dy[b,d,t] + a_{t+1} g_{t+1}      (after the last token: dhT)
+ *     dx[b,d,t]     = sum_n g_t B[b,n,t] delta_t
+ *     ddelta[b,d,t] = sum_n g_t (A[d,n] a_t h_{t-1} + B[b,n,t] x_t)
+ *     dA[d,n]       = sum_{b,t} g_t delta_t a_t h_{t-1}
+ *     dB[b,n,t]     = sum_d g_t delta_t x_t,   dC[b,n,t] = sum_d dy_t h_t
+ *     dh0[b,d,n]    = a_0 g_0
+ *
+ * Inputs: dims, x, delta, A, B, C, h0 (nullable) exactly as for
+ * mamba1_s6_fwd; dy [batch][channels][seqlen]; dhT (nullable)
+ * [batch][channels][dstate]. Outputs, float32, dense, caller-owned, written
+ * whole: dx, ddelta like x; dA like A; dB, dC like B; dh0 like h0 (nullable:
+ * not written). dstate 1, 2, 4 or 8 (UNSUPPORTED for 16).
+ * The call runs the forward scan for the chunks' end states (no y), then the
+ * chunks' backward scans with their entering adjoints, the per-chunk
+ * gradients (each chunk's states recomputed from its entering state) and the
+ * sums over batch rows, chunks and channel blocks, in fixed orders
+ * (deterministic). fp32 arithmetic throughout.
+ * Workspace: mamba1_s6_bwd_workspace_bytes(dims) bytes of device memory
+ * (the forward's, plus per-chunk adjoints and partial sums); two calls that
+ * share it must not overlap in time.
+ * Errors: as mamba1_s6_check_args (NULL_POINTER: A, dA always; x, delta, B,
+ * C, dy, dx, ddelta, dB, dC when batch * seqlen > 0), ALIAS when an output
+ * overlaps an input, another output or the workspace. Validation runs on
+ * the host before any launch; the call is asynchronous on `stream`. */
+size_t mamba1_s6_bwd_workspace_bytes(const mamba1_s6_dims* dims);
+
+int mamba1_s6_bwd_check_args(const mamba1_s6_dims* dims, const float* x, const float* delta,
+                             const float* A, const float* B, const float* C, const float* h0,
+                             const float* dy, const float* dhT, const float* dx, const float* ddelta,
+                             const float* dA, const float* dB, const float* dC, const float* dh0,
+                             const void* workspace, size_t workspace_bytes);
+
+int mamba1_s6_bwd(const mamba1_s6_dims* dims, const float* x, const float* delta, const float* A,
+                  const float* B, const float* C, const float* h0, const float* dy, const float* dhT,
+                  float* dx, float* ddelta, float* dA, float* dB, float* dC, float* dh0,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,7 +28,9 @@ __all__ = ["ssd_fwd", "ssd_fwd_ptr", "supported", "workspace_bytes", "workspace_
            "ssd_bwd", "ssd_bwd_ptr", "bwd_workspace_bytes", "bwd_check_args",
            "mamba2_ssd_bwd", "mamba2_ssd_bwd_check_args", "mamba2_ssd_bwd_workspace_bytes",
            "S6Dims", "s6_fwd", "s6_fwd_ptr", "s6_supported", "s6_workspace_bytes", "s6_check_args",
-           "mamba1_s6_fwd", "mamba1_s6_check_args", "mamba1_s6_supported", "mamba1_s6_workspace_bytes"]
+           "mamba1_s6_fwd", "mamba1_s6_check_args", "mamba1_s6_supported", "mamba1_s6_workspace_bytes",
+           "S6_GRAD_NAMES", "s6_bwd", "s6_bwd_ptr", "s6_bwd_workspace_bytes", "s6_bwd_check_args",
+           "mamba1_s6_bwd", "mamba1_s6_bwd_check_args", "mamba1_s6_bwd_workspace_bytes"]
 
 # The C entry points under their own names (ctypes functions with prototypes).
 mamba2_ssd_fwd = lib.mamba2_ssd_fwd
@@ -50,6 +52,9 @@ mamba1_s6_fwd = lib.mamba1_s6_fwd
 mamba1_s6_check_args = lib.mamba1_s6_check_args
 mamba1_s6_supported = lib.mamba1_s6_supported
 mamba1_s6_workspace_bytes = lib.mamba1_s6_workspace_bytes
+mamba1_s6_bwd = lib.mamba1_s6_bwd
+mamba1_s6_bwd_check_args = lib.mamba1_s6_bwd_check_args
+mamba1_s6_bwd_workspace_bytes = lib.mamba1_s6_bwd_workspace_bytes
 mamba2_ssd_bwd_check_args = lib.mamba2_ssd_bwd_check_args
 mamba2_ssd_bwd_workspace_bytes = lib.mamba2_ssd_bwd_workspace_bytes
 
@@ -378,3 +383,57 @@ def s6_fwd(x, delta, A, B, C, h0=None, *, return_final_state: bool = True, works
         s6_fwd_ptr(dims, ptr(x), ptr(delta), ptr(A), ptr(B), ptr(C), ptr(h0), ptr(y), ptr(hT), ptr(workspace),
                    workspace.numel(), stream)
     return y, hT
+
+
+# the selective scan's gradients, in the order mamba1_s6_bwd takes them
+S6_GRAD_NAMES = ("dx", "ddelta", "dA", "dB", "dC", "dh0")
+
+
+def s6_bwd_workspace_bytes(dims) -> int:
+    return int(lib.mamba1_s6_bwd_workspace_bytes(ctypes.byref(_s6_dims(dims))))
+
+
+def s6_bwd_check_args(dims, x, delta, A, B, C, h0, dy, dhT, dx, ddelta, dA, dB, dC, dh0, workspace,
+                      ws_bytes) -> int:
+    """Host-only validation of a selective-scan backward call on raw addresses (0 for NULL)."""
+    return int(lib.mamba1_s6_bwd_check_args(ctypes.byref(_s6_dims(dims)), x, delta, A, B, C, h0, dy, dhT, dx,
+                                            ddelta, dA, dB, dC, dh0, workspace, ws_bytes))
+
+
+def s6_bwd_ptr(dims, x, delta, A, B, C, h0, dy, dhT, dx, ddelta, dA, dB, dC, dh0, workspace, ws_bytes,
+               stream: int = 0) -> None:
+    """mamba1_s6_bwd on raw device addresses; raises SsdError on a nonzero status."""
+    st = lib.mamba1_s6_bwd(ctypes.byref(_s6_dims(dims)), x, delta, A, B, C, h0, dy, dhT, dx, ddelta, dA, dB, dC,
+                           dh0, workspace, ws_bytes, stream)
+    if st != 0:
+        raise SsdError(st)
+
+
+def s6_bwd(x, delta, A, B, C, dy, h0=None, dhT=None, *, workspace=None):
+    """Gradients of the selective scan on float32 CUDA tensors (shapes as
+    ``s6_fwd``; dy like x, dhT like h0 or None). Returns a dict with dx,
+    ddelta, dA, dB, dC and dh0."""
+    import torch
+
+    for t in (x, delta, A, B, C, dy, h0, dhT):
+        if t is not None and (t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("all tensors must be contiguous float32 GPU tensors")
+    bt, D, L = x.shape
+    N = A.shape[1]
+    for t, shape in ((delta, (bt, D, L)), (A, (D, N)), (B, (bt, N, L)), (C, (bt, N, L)), (dy, (bt, D, L)),
+                     (h0, (bt, D, N)), (dhT, (bt, D, N))):
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError("inconsistent shapes")
+    dims = S6Dims(bt, L, D, N)
+    g = {"dx": torch.empty_like(x), "ddelta": torch.empty_like(x), "dA": torch.empty_like(A),
+         "dB": torch.empty_like(B), "dC": torch.empty_like(B),
+         "dh0": torch.empty((bt, D, N), dtype=torch.float32, device=x.device)}
+    nbytes = s6_bwd_workspace_bytes(dims)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=x.device)
+    ptr = lambda t: 0 if t is None else t.data_ptr()
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        s6_bwd_ptr(dims, ptr(x), ptr(delta), ptr(A), ptr(B), ptr(C), ptr(h0), ptr(dy), ptr(dhT),
+                   *[ptr(g[k]) for k in S6_GRAD_NAMES], ptr(workspace), workspace.numel(), stream)
+    return g

@@ -117,6 +117,12 @@ def _load():
     L.mamba1_s6_check_args.restype = ctypes.c_int
     L.mamba1_s6_fwd.argtypes = [s6_p, fp, fp, fp, fp, fp, fp, fp, fp, vp, sz, vp]
     L.mamba1_s6_fwd.restype = ctypes.c_int
+    L.mamba1_s6_bwd_workspace_bytes.argtypes = [s6_p]
+    L.mamba1_s6_bwd_workspace_bytes.restype = sz
+    L.mamba1_s6_bwd_check_args.argtypes = [s6_p] + [fp] * 14 + [vp, sz]
+    L.mamba1_s6_bwd_check_args.restype = ctypes.c_int
+    L.mamba1_s6_bwd.argtypes = [s6_p] + [fp] * 14 + [vp, sz, vp]
+    L.mamba1_s6_bwd.restype = ctypes.c_int
     step_p = ctypes.POINTER(StepDims)
     L.mamba2_ssd_step_supported.argtypes = [i64, ctypes.c_int]
     L.mamba2_ssd_step_supported.restype = ctypes.c_int

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["ssd_api.cpp", "ssd_noalloc.cpp", "chunk_cumsum.hip", "chunk_state.hip", "state_pass.hip", "chunk_scan.hip",
-           "chunk_scan_resident.hip", "chunk_chained.hip", "ssd_step.hip", "ssd_bwd.hip", "bwd_fused.hip", "s6_scan.hip",
+           "chunk_scan_resident.hip", "chunk_chained.hip", "ssd_step.hip", "ssd_bwd.hip", "bwd_fused.hip", "s6_scan.hip", "s6_bwd.hip",
            "s6_api.cpp"]
 
 # -packed-fp32-ops off: no v_pk_{add,mul,fma}_f32 are generated.

@@ -1,0 +1,425 @@
+// The backward pass of the selective scan (S6): every input's gradient for
+// upstream gradients dy (like y) and dhT (like the final state). Per scalar
+// chain (batch row b, channel d, state n), with a_t = exp(delta_t A[d, n]),
+// u_t = B[n, t] delta_t x_t and h_t = a_t h_{t-1} + u_t, the state's adjoint
+// runs the same scan backwards in time ("Mamba: The Hard Way", Part 3, on
+// the chains of Part 5):
+//
+//   g_t = C[n, t] dy_t + a_{t+1} g_{t+1}         (after the last token: dhT)
+//   dx_t = sum_n g_t B delta_t,   ddelta_t = sum_n g_t (A a_t h_{t-1} + B x_t)
+//   dA  += g_t delta_t a_t h_{t-1},   dh0 = a_0 g_0
+//   dB[n, t] = sum_d g_t delta_t x_t,   dC[n, t] = sum_d dy_t h_t
+//
+// Chunks of 64 tokens, as in the forward pass:
+//   0. the forward scan (s6_onepass) leaves every chunk's end state;
+//   1. s6_bwd_local: each chunk's adjoint scanned backwards from zero; its
+//      value leaving the chunk's first token (times that token's decay) O_c
+//      and the chunk's sum of delta (its decays multiply to exp(A sum));
+//   2. s6_bwd_carry: the adjoint entering each chunk from the right,
+//      R_{c-1} = O_c + exp(A sum_c delta) R_c from R_last = dhT, and dh0;
+//   3. s6_bwd_chunk: per chunk, the states recomputed forward from the
+//      entering state (kept every S tokens), then per S-token piece, last
+//      first, the piece's states again and the backward step for each token,
+//      which gives dx, ddelta and the per-chunk parts of dA, dB and dC (the
+//      dB and dC parts summed over the workgroup's 256 channels through LDS);
+//   4. s6_bwd_reduce: dA over batch rows and chunks, dB and dC over channel
+//      blocks (fixed orders: deterministic).
+// Lanes are channels, as in the forward pass; each lane holds its chunk's x,
+// delta and dy in registers, read as whole rows through a per-wave LDS tile.
+#include "lookback_device.h"
+#include "ssd_device.h"
+#include "s6_device.h"
+#include "s6_launch.h"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kChunk = 64;    // tokens per chunk (the forward pass's)
+constexpr int kLanes = 256;   // channels per workgroup
+
+// piece length of the recomputation: the states of S tokens are held at once
+template <int N> struct BwdPiece { static constexpr int S = N >= 8 ? 4 : 8; };
+
+// 1. per (batch row, chunk, channel block): O_c and the chunk's sum of delta
+template <int N, bool VEC>
+__global__ __launch_bounds__(kLanes) void s6_bwd_local(const float* __restrict__ dl, const float* __restrict__ A,
+                                                       const float* __restrict__ Cm, const float* __restrict__ dy,
+                                                       float* __restrict__ O, float* __restrict__ SD, int64_t L,
+                                                       int D, int64_t nc) {
+  __shared__ __attribute__((aligned(16))) float sC[N][kChunk];
+  __shared__ __attribute__((aligned(1024))) unsigned char sT[kLanes / 64][64 * 256];
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int ncb = (D + kLanes - 1) / kLanes;
+  const int64_t c = blockIdx.y;
+  const int64_t b = blockIdx.x / ncb;
+  const int cb = (int)(blockIdx.x % ncb);
+  const int d = cb * kLanes + tid;
+  const bool valid = d < D;
+  const int64_t t0 = c * kChunk;
+  const int nt = L - t0 < kChunk ? (int)(L - t0) : kChunk;
+  for (int idx = tid; idx < N * kChunk; idx += kLanes) {
+    const int n = idx / kChunk, k = idx % kChunk;
+    sC[n][k] = k < nt ? Cm[(b * N + n) * L + t0 + k] : 0.f;
+  }
+  const int64_t wrow0 = b * D + cb * kLanes + wave * 64;
+  const int wrows = D - (cb * kLanes + wave * 64);
+  float dr[kChunk], gy[kChunk];
+  s6::rows_in<VEC>(dl, wrow0, wrows, L, t0, nt, sT[wave], lane, dr);
+  s6::rows_in<VEC>(dy, wrow0, wrows, L, t0, nt, sT[wave], lane, gy);
+  float a2[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) a2[n] = valid ? A[(int64_t)d * N + n] * kLog2e : 0.f;
+  __syncthreads();   // C staged
+  float carry[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) carry[n] = 0.f;
+  float dsum = 0.f;
+#pragma unroll
+  for (int t = kChunk - 1; t >= 0; --t) {
+    dsum += dr[t];
+#pragma unroll
+    for (int n = 0; n < N; ++n) carry[n] = exp2_hw(dr[t] * a2[n]) * fmaf(sC[n][t], gy[t], carry[n]);
+  }
+  if (valid) {
+    const int64_t rec = (b * nc + c) * D + d;
+#pragma unroll
+    for (int n = 0; n < N; ++n) O[rec * N + n] = carry[n];
+    SD[rec] = dsum;
+  }
+}
+
+// 2. per (batch row, channel): the adjoint entering each chunk from the
+// right, R[c]; dh0 at the end. Chunks are walked from the last, their
+// records read eight chunks ahead.
+template <int N>
+__global__ __launch_bounds__(256) void s6_bwd_carry(const float* __restrict__ A, const float* __restrict__ O,
+                                                    const float* __restrict__ SD, const float* __restrict__ dhT,
+                                                    float* __restrict__ R, float* __restrict__ dh0, int64_t bt, int D,
+                                                    int64_t nc) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;   // b * D + d
+  if (i >= bt * D) return;
+  const int64_t b = i / D;
+  const int d = (int)(i % D);
+  float a2[N], r[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    a2[n] = A[(int64_t)d * N + n] * kLog2e;
+    r[n] = dhT ? dhT[i * N + n] : 0.f;
+  }
+  constexpr int CR = 8;
+  for (int64_t c1 = nc - 1; c1 >= 0; c1 -= CR) {
+    float ov[CR][N], sv[CR];
+#pragma unroll
+    for (int j = 0; j < CR; ++j) {
+      const int64_t c = c1 - j;
+      const int64_t rec = (b * nc + (c >= 0 ? c : 0)) * D + d;
+#pragma unroll
+      for (int n = 0; n < N; ++n) ov[j][n] = c >= 0 ? O[rec * N + n] : 0.f;
+      sv[j] = c >= 0 ? SD[rec] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < CR; ++j) {
+      const int64_t c = c1 - j;
+      if (c < 0) break;
+      const int64_t rec = (b * nc + c) * D + d;
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        R[rec * N + n] = r[n];
+        r[n] = fmaf(exp2_hw(a2[n] * sv[j]), r[n], ov[j][n]);
+      }
+    }
+  }
+  if (dh0) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) dh0[i * N + n] = r[n];
+  }
+}
+
+// 3. per (batch row, chunk, channel block): dx, ddelta and the chunk's parts
+// of dA, dB and dC
+template <int N, bool VEC>
+__global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(1, 1))) void s6_bwd_chunk(
+    const float* __restrict__ x, const float* __restrict__ dl, const float* __restrict__ A,
+    const float* __restrict__ Bm, const float* __restrict__ Cm, const float* __restrict__ dy, const float* h0,
+    const float* __restrict__ incl, const float* __restrict__ R, float* __restrict__ dx, float* __restrict__ ddl,
+    float* __restrict__ dA_part, float* __restrict__ dB_part, float* __restrict__ dC_part, int64_t L, int D,
+    int64_t nc) {
+  constexpr int S = BwdPiece<N>::S, NS = kChunk / S;
+  constexpr int NQ = 2 * S * N;                 // per-lane values of a piece's dB and dC parts
+  constexpr int TPQ = kLanes / NQ;              // threads summing one of them
+  static_assert(NQ <= kLanes && kLanes % NQ == 0, "piece sums split evenly");
+  __shared__ __attribute__((aligned(16))) float sB[N][kChunk];
+  __shared__ __attribute__((aligned(16))) float sC[N][kChunk];
+  __shared__ __attribute__((aligned(1024))) unsigned char sT[kLanes / 64][64 * 256];
+  // piece sums: lane l's value q at sR[q][l + 4 (l / SPAN)] (padded per
+  // thread span, so the span reads of 16 threads fall on distinct banks)
+  constexpr int SPAN = kLanes / TPQ;
+  __shared__ __attribute__((aligned(16))) float sR[NQ][kLanes + 4 * TPQ];
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int ncb = (D + kLanes - 1) / kLanes;
+  const int64_t c = blockIdx.y;
+  const int64_t b = blockIdx.x / ncb;
+  const int cb = (int)(blockIdx.x % ncb);
+  const int d = cb * kLanes + tid;
+  const bool valid = d < D;
+  const int64_t t0 = c * kChunk;
+  const int nt = L - t0 < kChunk ? (int)(L - t0) : kChunk;
+  for (int idx = tid; idx < N * kChunk; idx += kLanes) {
+    const int n = idx / kChunk, k = idx % kChunk;
+    const int64_t o = (b * N + n) * L + t0 + k;
+    sB[n][k] = k < nt ? Bm[o] : 0.f;
+    sC[n][k] = k < nt ? Cm[o] : 0.f;
+  }
+  const int64_t wrow0 = b * D + cb * kLanes + wave * 64;
+  const int wrows = D - (cb * kLanes + wave * 64);
+  // x and delta in registers; dy stays in the wave's tile (read per token)
+  float xr[kChunk], dr[kChunk];
+  s6::rows_in<VEC>(x, wrow0, wrows, L, t0, nt, sT[wave], lane, xr);
+  s6::rows_in<VEC>(dl, wrow0, wrows, L, t0, nt, sT[wave], lane, dr);
+  {
+    float gy[kChunk];
+    s6::rows_in<VEC>(dy, wrow0, wrows, L, t0, nt, sT[wave], lane, gy);
+    // the tile keeps dy, zeroed where rows_in masked it (rows past D, tokens
+    // past the sequence)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int q = 0; q < kChunk / 4; ++q)
+      *reinterpret_cast<float4*>(sT[wave] + s6::tile_off((uint32_t)ln, (uint32_t)q)) =
+          make_float4(gy[4 * q], gy[4 * q + 1], gy[4 * q + 2], gy[4 * q + 3]);
+  }
+  const unsigned char* dyrow = sT[wave];
+  int lnd = lane;
+  asm volatile("" : "+v"(lnd));
+  float an[N], a2[N], h[N], g[N];
+  {
+    const int64_t rec = (b * nc + c) * D + d;
+#pragma unroll
+    for (int n = 0; n < N; ++n) {
+      an[n] = valid ? A[(int64_t)d * N + n] : 0.f;
+      a2[n] = an[n] * kLog2e;
+      g[n] = valid ? R[rec * N + n] : 0.f;
+      if (!valid)
+        h[n] = 0.f;
+      else if (c == 0)
+        h[n] = h0 ? h0[((int64_t)b * D + d) * N + n] : 0.f;
+      else
+        h[n] = incl[(rec - D) * N + n];   // chunk c - 1's end state
+    }
+  }
+  __syncthreads();   // B and C staged
+
+  // the states at the start of every piece
+  float ck[NS][N];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) ck[j][n] = h[n];
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const int t = S * j + i;
+      const float u = dr[t] * xr[t];
+#pragma unroll
+      for (int n = 0; n < N; ++n) h[n] = fmaf(exp2_hw(dr[t] * a2[n]), h[n], u * sB[n][t]);
+    }
+  }
+  float dA[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) dA[n] = 0.f;
+  const int q0 = tid / TPQ, qp = tid % TPQ;   // this thread's piece sum and its share of the lanes
+  // The pieces, last first, as a loop that is not unrolled (unrolled, the
+  // compiler interleaves the pieces and keeps far more live than one piece
+  // needs): the current piece always sits in the last S entries of xr, dr
+  // and in the last checkpoint; after it, its outputs (dx, ddelta) take its
+  // place and the arrays rotate right by one piece, so after NS pieces every
+  // output is back at its token's position.
+#pragma unroll 1
+  for (int m = 0; m < NS; ++m) {
+    const int j = NS - 1 - m;   // the piece's position in the chunk
+    constexpr int P0 = kChunk - S;
+    // the piece's entering states and decays, recomputed
+    float hp[S][N], av[S][N];
+#pragma unroll
+    for (int n = 0; n < N; ++n) h[n] = ck[NS - 1][n];
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      const int t = S * j + i;
+      const float u = dr[P0 + i] * xr[P0 + i];
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        hp[i][n] = h[n];
+        av[i][n] = exp2_hw(dr[P0 + i] * a2[n]);
+        h[n] = fmaf(av[i][n], h[n], u * sB[n][t]);
+      }
+    }
+    // the backward steps, last token first; each step's per-lane parts of
+    // dB (g_t delta_t x_t) and dC (dy_t h_t) go to LDS at once: value
+    // q = (i N + n) of dB, S N + (i N + n) of dC
+    __syncthreads();   // the previous piece's sums are read out
+    const int wl = tid + 4 * (tid / SPAN);
+#pragma unroll
+    for (int i = S - 1; i >= 0; --i) {
+      const int t = S * j + i;
+      const float gyt = *reinterpret_cast<const float*>(dyrow + s6::tile_off((uint32_t)lnd, (uint32_t)(t / 4)) + (t % 4) * 4);
+      const float dxt = dr[P0 + i] * xr[P0 + i];
+      float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+      for (int n = 0; n < N; ++n) {
+        const float gn = fmaf(sC[n][t], gyt, g[n]);     // dL/dh_t
+        const float ah = av[i][n] * hp[i][n];
+        const float bnt = sB[n][t];
+        sR[S * N + i * N + n][wl] = gyt * fmaf(dxt, bnt, ah);   // dy_t h_t
+        s1 = fmaf(gn, bnt, s1);
+        const float ga = gn * ah;
+        s2 = fmaf(ga, an[n], s2);
+        dA[n] = fmaf(dr[P0 + i], ga, dA[n]);
+        sR[i * N + n][wl] = gn * dxt;                    // g_t delta_t x_t
+        g[n] = av[i][n] * gn;                            // dL/dh_{t-1} from step t
+      }
+      const float xt = xr[P0 + i];
+      xr[P0 + i] = dr[P0 + i] * s1;   // dx_t
+      dr[P0 + i] = fmaf(xt, s1, s2);  // ddelta_t
+    }
+    // rotate: the outputs to the front, the next piece to the back
+    {
+      float tx[S], td[S];
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        tx[i] = xr[P0 + i];
+        td[i] = dr[P0 + i];
+      }
+#pragma unroll
+      for (int k = kChunk - 1; k >= S; --k) {
+        xr[k] = xr[k - S];
+        dr[k] = dr[k - S];
+      }
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        xr[i] = tx[i];
+        dr[i] = td[i];
+      }
+#pragma unroll
+      for (int q = NS - 1; q >= 1; --q)
+#pragma unroll
+        for (int n = 0; n < N; ++n) ck[q][n] = ck[q - 1][n];
+    }
+    // the piece's dB and dC parts summed over the workgroup's channels: TPQ
+    // threads sum one value over kLanes / TPQ lanes each, then combine by
+    // shuffles
+    __syncthreads();
+    {
+      float acc = 0.f;
+      const float* src = &sR[q0][qp * (SPAN + 4)];
+#pragma unroll
+      for (int l = 0; l < SPAN; l += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(src + l);
+        acc += (v.x + v.y) + (v.z + v.w);
+      }
+#pragma unroll
+      for (int off = 1; off < TPQ; off *= 2) acc += __shfl_xor(acc, off);
+      if (qp == 0) {
+        const int which = q0 / (S * N), rem = q0 % (S * N), i = rem / N, n = rem % N;
+        const int t = S * j + i;
+        if (t < nt) {
+          float* part = which == 0 ? dB_part : dC_part;
+          part[((b * ncb + cb) * N + n) * L + t0 + t] = acc;
+        }
+      }
+    }
+  }
+  // dx and ddelta out as whole rows; the chunk's dA part
+  s6::rows_out<VEC>(dx, wrow0, wrows, L, t0, nt, sT[wave], lane, xr);
+  s6::rows_out<VEC>(ddl, wrow0, wrows, L, t0, nt, sT[wave], lane, dr);
+  if (valid) {
+#pragma unroll
+    for (int n = 0; n < N; ++n) dA_part[((b * nc + c) * D + d) * N + n] = dA[n];
+  }
+}
+
+// 4. the sums: dA over batch rows and chunks; dB, dC over channel blocks
+__global__ void s6_bwd_reduce_dA(const float* __restrict__ part, float* __restrict__ dA, int64_t rows, int64_t DN) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= DN) return;
+  float s = 0.f;
+  for (int64_t r = 0; r < rows; ++r) s += part[r * DN + i];
+  dA[i] = s;
+}
+__global__ void s6_bwd_reduce_bc(const float* __restrict__ pb, const float* __restrict__ pc, float* __restrict__ dB,
+                                 float* __restrict__ dC, int64_t bt, int ncb, int64_t NL) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < bt * NL; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = i / NL, e = i % NL;
+    float sb = 0.f, sc = 0.f;
+    for (int k = 0; k < ncb; ++k) {
+      sb += pb[(b * ncb + k) * NL + e];
+      sc += pc[(b * ncb + k) * NL + e];
+    }
+    dB[i] = sb;
+    dC[i] = sc;
+  }
+}
+
+unsigned grid_of(int64_t n) {
+  const int64_t g = (n + 255) / 256;
+  return (unsigned)(g < 65536 ? (g > 0 ? g : 1) : 65536);
+}
+
+template <int N>
+hipError_t launch_bwd_n(const S6BwdProblem& p, hipStream_t s) {
+  const int64_t nc = (p.L + kChunk - 1) / kChunk;
+  const int64_t ncb = (p.D + kLanes - 1) / kLanes;
+  const int vec = (p.L % 4 == 0 && p.L <= ((int64_t)1 << 22) && (reinterpret_cast<uintptr_t>(p.x) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(p.delta) & 15) == 0 && (reinterpret_cast<uintptr_t>(p.dy) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(p.dx) & 15) == 0 && (reinterpret_cast<uintptr_t>(p.ddelta) & 15) == 0)
+                      ? 1 : 0;
+  const dim3 grid((unsigned)(p.bt * ncb), (unsigned)nc);
+  if (p.bt == 0 || nc == 0) {
+    // no token: dA is zero, dh0 the upstream dhT (or zero); nothing else
+    hipLaunchKernelGGL(s6_bwd_reduce_dA, dim3(grid_of(p.D * N)), dim3(256), 0, s, p.dA_part, p.dA, (int64_t)0,
+                       p.D * N);
+    if (p.bt > 0)
+      hipLaunchKernelGGL(s6_bwd_carry<N>, dim3(grid_of(p.bt * p.D)), dim3(256), 0, s, p.A, p.O, p.SD, p.dhT, p.R,
+                         p.dh0, p.bt, (int)p.D, (int64_t)0);
+    return hipGetLastError();
+  }
+  if (vec)
+    hipLaunchKernelGGL((s6_bwd_local<N, true>), grid, dim3(kLanes), 0, s, p.delta, p.A, p.C, p.dy, p.O, p.SD, p.L,
+                       (int)p.D, nc);
+  else
+    hipLaunchKernelGGL((s6_bwd_local<N, false>), grid, dim3(kLanes), 0, s, p.delta, p.A, p.C, p.dy, p.O, p.SD, p.L,
+                       (int)p.D, nc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(s6_bwd_carry<N>, dim3(grid_of(p.bt * p.D)), dim3(256), 0, s, p.A, p.O, p.SD, p.dhT, p.R, p.dh0,
+                     p.bt, (int)p.D, nc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (vec)
+    hipLaunchKernelGGL((s6_bwd_chunk<N, true>), grid, dim3(kLanes), 0, s, p.x, p.delta, p.A, p.B, p.C, p.dy, p.h0,
+                       p.incl, p.R, p.dx, p.ddelta, p.dA_part, p.dB_part, p.dC_part, p.L, (int)p.D, nc);
+  else
+    hipLaunchKernelGGL((s6_bwd_chunk<N, false>), grid, dim3(kLanes), 0, s, p.x, p.delta, p.A, p.B, p.C, p.dy, p.h0,
+                       p.incl, p.R, p.dx, p.ddelta, p.dA_part, p.dB_part, p.dC_part, p.L, (int)p.D, nc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(s6_bwd_reduce_dA, dim3(grid_of(p.D * N)), dim3(256), 0, s, p.dA_part, p.dA, p.bt * nc, p.D * N);
+  hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3(grid_of(p.bt * N * p.L)), dim3(256), 0, s, p.dB_part, p.dC_part, p.dB,
+                     p.dC, p.bt, (int)ncb, (int64_t)N * p.L);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool s6_bwd_has(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8; }
+
+hipError_t launch_s6_bwd(const S6BwdProblem& p, hipStream_t s) {
+  switch (p.N) {
+    case 1: return launch_bwd_n<1>(p, s);
+    case 2: return launch_bwd_n<2>(p, s);
+    case 4: return launch_bwd_n<4>(p, s);
+    case 8: return launch_bwd_n<8>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ssd

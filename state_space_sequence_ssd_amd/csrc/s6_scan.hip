@@ -31,6 +31,7 @@
 // flags first.
 #include "lookback_device.h"
 #include "ssd_device.h"
+#include "s6_device.h"
 #include "s6_launch.h"
 
 namespace ssd {
@@ -106,38 +107,6 @@ __global__ void s6_pass_state(const float* h0, float* hT, int64_t n) {
   if (i < n) hT[i] = h0 ? h0[i] : 0.f;
 }
 
-// A wave's 64 channel rows of one chunk (64 tokens, 256 bytes each) in LDS:
-// 16-byte piece q (tokens 4 q .. 4 q + 3) of row r sits at piece q ^ (r % 16),
-// so both the coalesced transfers (4 whole rows per instruction) and each
-// lane's walk along its own row hit distinct 16-byte bank groups.
-__device__ __forceinline__ uint32_t tile_off(uint32_t r, uint32_t q) { return r * 256 + ((q ^ (r & 15)) << 4); }
-
-// rows [rows0 .. rows0 + 63] of a [rows][L] array, tokens t0 .. t0 + 63, into
-// the wave's tile by direct global->LDS loads (rows at or past `rows_valid`
-// read as zeros; the caller masks tokens past the sequence)
-__device__ __forceinline__ void tile_load(const float* src, int64_t row0, int rows_valid, int64_t L, int64_t t0,
-                                          unsigned char* tile, int lane) {
-  asm volatile("" : "+v"(lane));   // per-lane offsets formed here, not kept live across the ticket
-  const __amdgpu_buffer_rsrc_t r = lookback::urs(src + row0 * L, (uint32_t)((int64_t)rows_valid * L * 4));
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t row = (uint32_t)(4 * i + (lane >> 4)), q = (uint32_t)(lane & 15) ^ (row & 15);
-    lookback::bdma16<false>(r, (uint32_t)(row * L + t0 + 4 * q) * 4, 0, tile + i * 1024);
-  }
-}
-
-// The same with 4-byte loads, for rows that are not 16-byte aligned: lane l
-// takes token t0 + l of each row (zeros past the sequence or the rows).
-__device__ __forceinline__ void tile_load_scalar(const float* src, int64_t row0, int rows_valid, int64_t L,
-                                                 int64_t t0, int nt, unsigned char* tile, int lane) {
-  asm volatile("" : "+v"(lane));
-#pragma unroll 8
-  for (int r = 0; r < 64; ++r) {
-    const float v = (r < rows_valid && lane < nt) ? src[(row0 + r) * L + t0 + lane] : 0.f;
-    *reinterpret_cast<float*>(tile + tile_off((uint32_t)r, (uint32_t)lane >> 2) + (lane & 3) * 4) = v;
-  }
-}
-
 template <int N, bool VEC>
 __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 ? 1 : 2))) void s6_onepass(const float* __restrict__ x, const float* __restrict__ dl,
                                                      const float* __restrict__ A, const float* __restrict__ Bm,
@@ -188,16 +157,16 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         if constexpr (VEC) {
-          if (wrows > 0) tile_load(srcs[a], wrow0, wrows < 64 ? wrows : 64, L, t0, tile, lane);
+          if (wrows > 0) s6::tile_load(srcs[a], wrow0, wrows < 64 ? wrows : 64, L, t0, tile, lane);
         } else {
-          tile_load_scalar(srcs[a], wrow0, wrows, L, t0, nt, tile, lane);
+          s6::tile_load_scalar(srcs[a], wrow0, wrows, L, t0, nt, tile, lane);
         }
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         int ln = lane;
         asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int q = 0; q < kChunk / 4; ++q) {
-          const float4 v = *reinterpret_cast<const float4*>(tile + tile_off((uint32_t)ln, (uint32_t)q));
+          const float4 v = *reinterpret_cast<const float4*>(tile + s6::tile_off((uint32_t)ln, (uint32_t)q));
           // (past the sequence the direct loads read the next row: masked here;
           // nt is a multiple of 4 on that path)
           const bool in = !VEC || 4 * q < nt;
@@ -309,10 +278,13 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
         if (tid == 0) __hip_atomic_store(myflag, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    // ... and the chunk again from the entering state: y replaces x. (The
+    // ... and the chunk again from the entering state: y replaces x (unless
+    // no y is asked for: the backward pass runs this kernel for the chunks'
+    // end states alone). (The
     // decays are recomputed: kept from the first scan they would take 64 N
     // registers per lane, so the operands are laundered to stop the compiler
     // from keeping them.)
+    if (y) {
 #pragma unroll
     for (int t = 0; t < kChunk; ++t) asm volatile("" : "+v"(dr[t]));
 #pragma unroll
@@ -346,14 +318,14 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
       asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int q = 0; q < kChunk / 4; ++q)
-        *reinterpret_cast<float4*>(tile + tile_off((uint32_t)ln, (uint32_t)q)) =
+        *reinterpret_cast<float4*>(tile + s6::tile_off((uint32_t)ln, (uint32_t)q)) =
             make_float4(xr[4 * q], xr[4 * q + 1], xr[4 * q + 2], xr[4 * q + 3]);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (!VEC) {
         // lane l stores token t0 + l of each row
 #pragma unroll 8
         for (int r = 0; r < 64; ++r) {
-          const float v = *reinterpret_cast<const float*>(tile + tile_off((uint32_t)r, (uint32_t)ln >> 2) + (ln & 3) * 4);
+          const float v = *reinterpret_cast<const float*>(tile + s6::tile_off((uint32_t)r, (uint32_t)ln >> 2) + (ln & 3) * 4);
           if (r < wrows && ln < nt) y[(wrow0 + r) * L + t0 + ln] = v;
         }
       } else if (wrows > 0) {
@@ -366,6 +338,7 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
           if ((int)(4 * q) < nt) __builtin_amdgcn_raw_buffer_store_b128(v, ry, (r * (uint32_t)L + (uint32_t)t0 + 4 * q) * 4, 0, 0);
         }
       }
+    }
     }
     // the next ticket (the B, C tiles are free once every lane is past them)
     __syncthreads();
@@ -439,6 +412,8 @@ int64_t s6_sync_words(int64_t bt, int64_t D, int64_t L) {
 }
 
 int64_t s6_chunk_tokens() { return kChunk; }
+
+int64_t s6_channel_block() { return kLanes; }
 
 bool s6_has(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8 || N == 16; }
 

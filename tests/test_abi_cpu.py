@@ -39,7 +39,8 @@ def test_header_declares_the_entry_points():
         "mamba2_ssd_step_supported", "mamba2_ssd_fused_state_pass", "mamba2_ssd_fwd_path",
         "mamba2_ssd_fwd_noalloc", "mamba2_ssd_bwd",
         "mamba2_ssd_bwd_check_args", "mamba2_ssd_bwd_workspace_bytes", "mamba1_s6_fwd", "mamba1_s6_check_args",
-        "mamba1_s6_supported", "mamba1_s6_workspace_bytes"])
+        "mamba1_s6_supported", "mamba1_s6_workspace_bytes", "mamba1_s6_bwd", "mamba1_s6_bwd_check_args",
+        "mamba1_s6_bwd_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -508,3 +509,51 @@ def test_s6_validation():
     assert ssd.s6_workspace_bytes(ssd.S6Dims(70000, 10, 4, 4)) == 0
     assert ssd.s6_workspace_bytes(ssd.S6Dims(1, 64 * 65536, 4, 4)) == 0
     assert _s6_check(ssd.S6Dims(0, 300, 96, 16), x=0, delta=0, B=0, C=0, y=0, ws=0) == OK
+
+
+def _s6_bwd_ptrs(d):
+    bt, L, D, N = d.batch, d.seqlen, d.channels, d.dstate
+    sizes = {"x": bt * D * L, "delta": bt * D * L, "A": D * N, "B": bt * N * L, "C": bt * N * L,
+             "h0": bt * D * N, "dy": bt * D * L, "dhT": bt * D * N, "dx": bt * D * L, "ddelta": bt * D * L,
+             "dA": D * N, "dB": bt * N * L, "dC": bt * N * L, "dh0": bt * D * N}
+    p, base = {}, 1 << 40
+    for k, n in sizes.items():
+        p[k] = base
+        base += (4 * n + 4095) // 4096 * 4096 + 4096
+    p["ws"] = base
+    return p
+
+
+def _s6_bwd_check(d, **over):
+    p = _s6_bwd_ptrs(d)
+    p.update(over)
+    ws_bytes = over.get("ws_bytes", ssd.s6_bwd_workspace_bytes(d))
+    return ssd.s6_bwd_check_args(d, p["x"], p["delta"], p["A"], p["B"], p["C"], p["h0"], p["dy"], p["dhT"], p["dx"],
+                                 p["ddelta"], p["dA"], p["dB"], p["dC"], p["dh0"], p["ws"], ws_bytes)
+
+
+def test_s6_bwd_workspace_and_validation():
+    # the forward's workspace, then per (b, chunk, d): the chunk's outgoing
+    # adjoint, its delta sum, its entering adjoint and its dA part; per
+    # (b, block of 256 channels): the dB and dC parts
+    nc, ncb = (300 + 63) // 64, 1
+    fwd = ssd.s6_workspace_bytes(ssd.S6Dims(2, 300, 96, 4))
+    d4 = ssd.S6Dims(2, 300, 96, 4)
+    want = fwd + sum((n * 4 + 255) // 256 * 256 for n in (2 * nc * 96 * 4, 2 * nc * 96, 2 * nc * 96 * 4,
+                                                          2 * nc * 96 * 4, 2 * ncb * 4 * 300, 2 * ncb * 4 * 300))
+    assert ssd.s6_bwd_workspace_bytes(d4) == want
+    assert _s6_bwd_check(d4) == OK
+    assert _s6_bwd_check(d4, h0=0, dhT=0, dh0=0) == OK
+    for name in ("x", "delta", "A", "B", "C", "dy", "dx", "ddelta", "dA", "dB", "dC"):
+        assert _s6_bwd_check(d4, **{name: 0}) == NULLP, name
+    p = _s6_bwd_ptrs(d4)
+    assert _s6_bwd_check(d4, dx=p["x"]) == ALIAS
+    assert _s6_bwd_check(d4, dB=p["dC"]) == ALIAS
+    assert _s6_bwd_check(d4, dh0=p["h0"]) == ALIAS
+    assert _s6_bwd_check(d4, ws=0) == WS
+    # dstate 16 has a forward scan but no backward kernels
+    assert ssd.s6_supported(16) and ssd.s6_bwd_workspace_bytes(ssd.S6Dims(2, 300, 96, 16)) == 0
+    assert _s6_bwd_check(ssd.S6Dims(2, 300, 96, 16)) == UNSUP
+    # empty batch: only A and dA are needed
+    e = ssd.S6Dims(0, 300, 96, 4)
+    assert _s6_bwd_check(e, x=0, delta=0, B=0, C=0, dy=0, dx=0, ddelta=0, dB=0, dC=0, ws=0) == OK
