@@ -18,7 +18,7 @@ With --config mamba2-2.7b-decode it times the one-token decode step instead
 updated in place), with the same JSON fields. With --bwd it times the
 backward pass (every input's gradient) on the layer instead. With
 --config s6-page (or another s6-* shape) it times the Mamba-1 selective
-scan on that shape.
+scan on that shape, and with both its backward pass.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
 """
@@ -477,6 +477,101 @@ def run_s6(args, cfg):
     print(json.dumps(out), flush=True)
 
 
+def run_s6_bwd(args, cfg):
+    """Times the selective scan's backward pass (mamba1_s6_bwd, every input's
+    gradient) on one of the S6 shapes; one JSON line of its own."""
+    import torch
+
+    import state_space_sequence_ssd_amd as ssd
+    from workloads import generate_s6
+
+    dev = torch.device("cuda:0")
+    inp = generate_s6(cfg)
+    if args.copy_calibration:
+        copy_calibration(dev)
+    Bt, L, D, N = cfg.batch, cfg.seqlen, cfg.channels, cfg.dstate
+    rng = np.random.default_rng(cfg.seed + 1000)
+    dy = rng.standard_normal((Bt, D, L)).astype(np.float32)
+    dhT = rng.standard_normal((Bt, D, N)).astype(np.float32)
+    to_dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    t = {k: to_dev(v) for k, v in inp.items()}
+    t["dy"], t["dhT"] = to_dev(dy), to_dev(dhT)
+    g = {"dx": torch.empty_like(t["x"]), "ddelta": torch.empty_like(t["x"]), "dA": torch.empty_like(t["A"]),
+         "dB": torch.empty_like(t["B"]), "dC": torch.empty_like(t["B"]),
+         "dh0": torch.empty((Bt, D, N), dtype=torch.float32, device=dev)}
+    dims = ssd.S6Dims(Bt, L, D, N)
+    nbytes_ws = ssd.s6_bwd_workspace_bytes(dims)
+    ws = torch.empty(max(nbytes_ws, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ptr = lambda a: 0 if a is None else a.data_ptr()
+    ptrs = ([ptr(t[k]) for k in ("x", "delta", "A", "B", "C", "h0", "dy", "dhT")]
+            + [ptr(g[k]) for k in ssd.S6_GRAD_NAMES] + [ws.data_ptr(), ws.numel()])
+
+    def call():
+        ssd.s6_bwd_ptr(dims, *ptrs, stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        call()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        call()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = float(np.mean([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])) * 1e3
+    # each input read once and each gradient written once: x, delta, dy and
+    # dx, ddelta (token x channel); B, C and dB, dC (token x state); A, dA;
+    # h0 (when given), dhT and dh0
+    states = Bt * D * N * 4 * (3 if cfg.h0_sigma else 2)
+    alg = 5 * Bt * D * L * 4 + 4 * Bt * N * L * 4 + 2 * D * N * 4 + states
+    achieved = alg / (us * 1e-6) / 1e9
+    out = {
+        "metric": "Mamba-1 selective scan (S6) backward tokens/sec (1 GPU); % HBM BW",
+        "value": round(cfg.tokens * args.steps / wall, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name + "-bwd", "batch": Bt, "seqlen": L, "channels": D, "dstate": N,
+                   "recipe": cfg.recipe, "seed": cfg.seed, "tokens_per_step": cfg.tokens},
+        "roofline": {"bound": "hbm", "kernel": "whole backward call (mamba1_s6_bwd)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+        "gpu_event_us_per_step": round(us, 2),
+        "alg_bytes_per_step": int(alg),
+        "workspace_bytes": int(nbytes_ws),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        from threadpoolctl import threadpool_limits
+
+        from oracle import s6_bwd_sequential
+
+        cores = len(os.sched_getaffinity(0))
+        threads = min(cores, int(os.environ.get("OMP_NUM_THREADS", cores)))
+        host = {k: g[k].cpu().numpy() for k in ssd.S6_GRAD_NAMES}
+        with threadpool_limits(limits=threads, user_api="blas"):
+            t0 = time.perf_counter()
+            ref = s6_bwd_sequential(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], dy, inp["h0"], dhT)
+            elapsed = time.perf_counter() - t0
+        worst = max(float(np.max(np.abs(host[k] - ref[k]))) / max(float(np.max(np.abs(ref[k]))), 1e-30)
+                    for k in ssd.S6_GRAD_NAMES)
+        out["cpu_baseline"] = {"value": cfg.tokens / elapsed, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"fp64 S6 gradient oracle on the whole call ({Bt} batch rows, {D} "
+                                         f"channels), {elapsed:.1f} s", "seconds": elapsed}
+        out["parity_vs_oracle"] = {"rows_checked": Bt, "worst_normwise_rel_err": worst, "ok": worst <= 1e-5}
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(cfg, inp, y_gpu, budget_s=10.0):
     """The chunked fp64 oracle, as it stands, on whole batch rows of the same
     layer until `budget_s` has elapsed; its outputs are checked against the
@@ -527,7 +622,8 @@ def main():
                     help="seconds of CPU oracle work for the cpu_baseline sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--bwd", action="store_true",
-                    help="time the backward pass (mamba2_ssd_bwd) on the layer instead, one JSON line of its own")
+                    help="time the backward pass (mamba2_ssd_bwd, or mamba1_s6_bwd with an s6-* config) instead, "
+                         "one JSON line of its own")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy, a dispatch of known size that "
                          "HBM byte counters (FETCH_SIZE, WRITE_SIZE) can be scaled against")
@@ -549,7 +645,8 @@ def main():
         cfg = None
     elif args.config.startswith("s6-"):
         from workloads import s6_config_by_name
-        return run_s6(args, s6_config_by_name(args.config))
+        s6cfg = s6_config_by_name(args.config)
+        return run_s6_bwd(args, s6cfg) if args.bwd else run_s6(args, s6cfg)
     else:
         cfg = config_by_name(args.config)
     if cfg is not None and cfg.seqlen == 1 and cfg.name.endswith("-decode"):

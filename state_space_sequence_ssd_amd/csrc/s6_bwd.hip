@@ -97,42 +97,44 @@ __global__ __launch_bounds__(256) void s6_bwd_carry(const float* __restrict__ A,
                                                     const float* __restrict__ SD, const float* __restrict__ dhT,
                                                     float* __restrict__ R, float* __restrict__ dh0, int64_t bt, int D,
                                                     int64_t nc) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;   // b * D + d
-  if (i >= bt * D) return;
-  const int64_t b = i / D;
-  const int d = (int)(i % D);
-  float a2[N], r[N];
+  // i = b * D + d; grid-stride, the grid being capped at 65536 workgroups
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < bt * D;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = i / D;
+    const int d = (int)(i % D);
+    float a2[N], r[N];
 #pragma unroll
-  for (int n = 0; n < N; ++n) {
-    a2[n] = A[(int64_t)d * N + n] * kLog2e;
-    r[n] = dhT ? dhT[i * N + n] : 0.f;
-  }
-  constexpr int CR = 8;
-  for (int64_t c1 = nc - 1; c1 >= 0; c1 -= CR) {
-    float ov[CR][N], sv[CR];
-#pragma unroll
-    for (int j = 0; j < CR; ++j) {
-      const int64_t c = c1 - j;
-      const int64_t rec = (b * nc + (c >= 0 ? c : 0)) * D + d;
-#pragma unroll
-      for (int n = 0; n < N; ++n) ov[j][n] = c >= 0 ? O[rec * N + n] : 0.f;
-      sv[j] = c >= 0 ? SD[rec] : 0.f;
+    for (int n = 0; n < N; ++n) {
+      a2[n] = A[(int64_t)d * N + n] * kLog2e;
+      r[n] = dhT ? dhT[i * N + n] : 0.f;
     }
+    constexpr int CR = 8;
+    for (int64_t c1 = nc - 1; c1 >= 0; c1 -= CR) {
+      float ov[CR][N], sv[CR];
 #pragma unroll
-    for (int j = 0; j < CR; ++j) {
-      const int64_t c = c1 - j;
-      if (c < 0) break;
-      const int64_t rec = (b * nc + c) * D + d;
+      for (int j = 0; j < CR; ++j) {
+        const int64_t c = c1 - j;
+        const int64_t rec = (b * nc + (c >= 0 ? c : 0)) * D + d;
 #pragma unroll
-      for (int n = 0; n < N; ++n) {
-        R[rec * N + n] = r[n];
-        r[n] = fmaf(exp2_hw(a2[n] * sv[j]), r[n], ov[j][n]);
+        for (int n = 0; n < N; ++n) ov[j][n] = c >= 0 ? O[rec * N + n] : 0.f;
+        sv[j] = c >= 0 ? SD[rec] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < CR; ++j) {
+        const int64_t c = c1 - j;
+        if (c < 0) break;
+        const int64_t rec = (b * nc + c) * D + d;
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+          R[rec * N + n] = r[n];
+          r[n] = fmaf(exp2_hw(a2[n] * sv[j]), r[n], ov[j][n]);
+        }
       }
     }
-  }
-  if (dh0) {
+    if (dh0) {
 #pragma unroll
-    for (int n = 0; n < N; ++n) dh0[i * N + n] = r[n];
+      for (int n = 0; n < N; ++n) dh0[i * N + n] = r[n];
+    }
   }
 }
 
@@ -338,13 +340,31 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 }
 
 // 4. the sums: dA over batch rows and chunks; dB, dC over channel blocks
-__global__ void s6_bwd_reduce_dA(const float* __restrict__ part, float* __restrict__ dA, int64_t rows, int64_t DN) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= DN) return;
+// dA: each workgroup takes 64 consecutive (d, n) columns; its 16 waves sum
+// every 16th row (batch row, chunk) each, and wave 0 adds the 16 partial
+// sums in wave order.
+constexpr int kRedWaves = 16;
+__global__ __launch_bounds__(64 * kRedWaves) void s6_bwd_reduce_dA(const float* __restrict__ part,
+                                                                   float* __restrict__ dA, int64_t rows,
+                                                                   int64_t DN) {
+  __shared__ float red[kRedWaves][64];
+  const int lane = threadIdx.x % 64, w = threadIdx.x / 64;
+  const int64_t i = blockIdx.x * (int64_t)64 + lane;
   float s = 0.f;
-  for (int64_t r = 0; r < rows; ++r) s += part[r * DN + i];
-  dA[i] = s;
+  if (i < DN) {
+#pragma unroll 8
+    for (int64_t r = w; r < rows; r += kRedWaves) s += part[r * DN + i];
+  }
+  red[w][lane] = s;
+  __syncthreads();
+  if (w == 0 && i < DN) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < kRedWaves; ++k) t += red[k][lane];
+    dA[i] = t;
+  }
 }
+unsigned dA_grid(int64_t DN) { return (unsigned)(DN > 0 ? (DN + 63) / 64 : 1); }
 __global__ void s6_bwd_reduce_bc(const float* __restrict__ pb, const float* __restrict__ pc, float* __restrict__ dB,
                                  float* __restrict__ dC, int64_t bt, int ncb, int64_t NL) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < bt * NL; i += (int64_t)gridDim.x * blockDim.x) {
@@ -375,7 +395,7 @@ hipError_t launch_bwd_n(const S6BwdProblem& p, hipStream_t s) {
   const dim3 grid((unsigned)(p.bt * ncb), (unsigned)nc);
   if (p.bt == 0 || nc == 0) {
     // no token: dA is zero, dh0 the upstream dhT (or zero); nothing else
-    hipLaunchKernelGGL(s6_bwd_reduce_dA, dim3(grid_of(p.D * N)), dim3(256), 0, s, p.dA_part, p.dA, (int64_t)0,
+    hipLaunchKernelGGL(s6_bwd_reduce_dA, dim3(dA_grid(p.D * N)), dim3(64 * kRedWaves), 0, s, p.dA_part, p.dA, (int64_t)0,
                        p.D * N);
     if (p.bt > 0)
       hipLaunchKernelGGL(s6_bwd_carry<N>, dim3(grid_of(p.bt * p.D)), dim3(256), 0, s, p.A, p.O, p.SD, p.dhT, p.R,
@@ -402,7 +422,7 @@ hipError_t launch_bwd_n(const S6BwdProblem& p, hipStream_t s) {
                        p.incl, p.R, p.dx, p.ddelta, p.dA_part, p.dB_part, p.dC_part, p.L, (int)p.D, nc);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(s6_bwd_reduce_dA, dim3(grid_of(p.D * N)), dim3(256), 0, s, p.dA_part, p.dA, p.bt * nc, p.D * N);
+  hipLaunchKernelGGL(s6_bwd_reduce_dA, dim3(dA_grid(p.D * N)), dim3(64 * kRedWaves), 0, s, p.dA_part, p.dA, p.bt * nc, p.D * N);
   hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3(grid_of(p.bt * N * p.L)), dim3(256), 0, s, p.dB_part, p.dC_part, p.dB,
                      p.dC, p.bt, (int)ncb, (int64_t)N * p.L);
   return hipGetLastError();
