@@ -63,7 +63,7 @@ int s6_bwd_sizes(const mamba1_s6_dims* d, S6BwdSizes* s) {
   const int st = s6_sizes(d, &r.f);
   if (st != MAMBA2_SSD_OK) return st;
   if (!ssd::s6_bwd_has(d->dstate)) return MAMBA2_SSD_ERR_UNSUPPORTED;
-  const int64_t cbk = ssd::s6_channel_block();
+  const int64_t cbk = ssd::s6_bwd_channel_block();
   r.ncb = (d->channels + cbk - 1) / cbk;
   int64_t ns, bd, nsum, bcb, t, nbc;
   if (!mul_ok(r.f.n_state, r.f.nc, &ns) || !mul_ok(d->batch, d->channels, &bd) || !mul_ok(bd, r.f.nc, &nsum))

@@ -413,8 +413,6 @@ int64_t s6_sync_words(int64_t bt, int64_t D, int64_t L) {
 
 int64_t s6_chunk_tokens() { return kChunk; }
 
-int64_t s6_channel_block() { return kLanes; }
-
 bool s6_has(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8 || N == 16; }
 
 hipError_t launch_s6(const S6Problem& p, hipStream_t s) {

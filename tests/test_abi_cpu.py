@@ -535,8 +535,8 @@ def _s6_bwd_check(d, **over):
 def test_s6_bwd_workspace_and_validation():
     # the forward's workspace, then per (b, chunk, d): the chunk's outgoing
     # adjoint, its delta sum, its entering adjoint and its dA part; per
-    # (b, block of 256 channels): the dB and dC parts
-    nc, ncb = (300 + 63) // 64, 1
+    # (b, block of 64 channels): the dB and dC parts
+    nc, ncb = (300 + 63) // 64, 2
     fwd = ssd.s6_workspace_bytes(ssd.S6Dims(2, 300, 96, 4))
     d4 = ssd.S6Dims(2, 300, 96, 4)
     want = fwd + sum((n * 4 + 255) // 256 * 256 for n in (2 * nc * 96 * 4, 2 * nc * 96, 2 * nc * 96 * 4,

@@ -34,6 +34,8 @@ CASES = {
     "one-token": SMALL.with_shape(seqlen=1),
     "vec-path": SMALL.with_shape(seqlen=4 * 97, channels=256),                 # 16-byte rows, ragged chunk
     "two-blocks": SMALL.with_shape(batch=3, seqlen=200, channels=600),
+    "scalar-half": SMALL.with_shape(seqlen=237, channels=130),               # 4-byte rows, 13 tokens in the last half
+    "n2-short-tail": SMALL.with_shape(dstate=2, seqlen=148, channels=70),    # last chunk within its first half
 }
 
 
