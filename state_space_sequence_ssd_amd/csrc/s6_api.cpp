@@ -194,12 +194,14 @@ int mamba1_s6_bwd(const mamba1_s6_dims* d, const float* x, const float* delta, c
   auto f = [&](size_t off) { return ws ? reinterpret_cast<float*>(ws + off) : nullptr; };
   hipError_t err = hipSuccess;
   if (d->batch > 0 && s.f.nc > 0) {
-    // the forward scan for the chunks' end states (no y)
+    // the forward sweep: the chunks' end states (no y) and, from dy, each
+    // chunk's own adjoint record O and delta sum SD
     ssd::S6Problem p{};
     p.bt = d->batch; p.L = d->seqlen; p.D = d->channels; p.N = d->dstate;
     p.x = x; p.delta = delta; p.A = A; p.B = B; p.C = C; p.h0 = h0; p.y = nullptr; p.hT = nullptr;
     p.aggS = f(0); p.aggD = f(s.f.off_sumd); p.incl = f(s.f.off_incl);
     p.sync = ws ? reinterpret_cast<int*>(ws + s.f.off_sync) : nullptr;
+    p.dy = dy; p.O = f(s.off_O); p.SD = f(s.off_SD);
     err = ssd::launch_s6(p, hs);
   }
   if (err == hipSuccess) {

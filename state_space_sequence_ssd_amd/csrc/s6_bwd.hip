@@ -11,10 +11,11 @@
 //   dB[n, t] = sum_d g_t delta_t x_t,   dC[n, t] = sum_d dy_t h_t
 //
 // Chunks of 64 tokens, as in the forward pass:
-//   0. the forward scan (s6_onepass) leaves every chunk's end state;
-//   1. s6_bwd_local: each chunk's adjoint scanned backwards from zero; its
-//      value leaving the chunk's first token (times that token's decay) O_c
-//      and the chunk's sum of delta (its decays multiply to exp(A sum));
+//   1. the forward sweep (s6_onepass in its backward mode) leaves every
+//      chunk's end state and, from dy, the chunk's own adjoint record: O_c,
+//      the adjoint its dy alone leaves at its first token (times that
+//      token's decay), sum_t (a_t0 ... a_t) C_t dy_t, and the chunk's sum of
+//      delta (its decays multiply to exp(A sum));
 //   2. s6_bwd_carry: the adjoint entering each chunk from the right,
 //      R_{c-1} = O_c + exp(A sum_c delta) R_c from R_last = dhT, and dh0;
 //   3. s6_bwd_chunk: per chunk and 64 channels (one wave), the states
@@ -37,60 +38,12 @@ namespace ssd {
 
 namespace {
 
-constexpr int kChunk = 64;    // tokens per chunk (the forward pass's)
-constexpr int kLanes = 256;     // channels per workgroup of the local pass (4 waves)
+constexpr int kChunk = 64;      // tokens per chunk (the forward pass's)
+constexpr int kLanes = 256;     // channels per workgroup of the wide chunk kernel (4 waves)
 constexpr int kBwdLanes = 64;   // channels per workgroup of the chunk kernel (one wave)
 
 // piece length of the recomputation: the states of S tokens are held at once
 template <int N> struct BwdPiece { static constexpr int S = N >= 8 ? 4 : 8; };
-
-// 1. per (batch row, chunk, channel block): O_c and the chunk's sum of delta
-template <int N, bool VEC>
-__global__ __launch_bounds__(kLanes) void s6_bwd_local(const float* __restrict__ dl, const float* __restrict__ A,
-                                                       const float* __restrict__ Cm, const float* __restrict__ dy,
-                                                       float* __restrict__ O, float* __restrict__ SD, int64_t L,
-                                                       int D, int64_t nc) {
-  __shared__ __attribute__((aligned(16))) float sC[N][kChunk];
-  __shared__ __attribute__((aligned(1024))) unsigned char sT[kLanes / 64][64 * 256];
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-  const int ncb = (D + kLanes - 1) / kLanes;
-  const int64_t c = blockIdx.y;
-  const int64_t b = blockIdx.x / ncb;
-  const int cb = (int)(blockIdx.x % ncb);
-  const int d = cb * kLanes + tid;
-  const bool valid = d < D;
-  const int64_t t0 = c * kChunk;
-  const int nt = L - t0 < kChunk ? (int)(L - t0) : kChunk;
-  for (int idx = tid; idx < N * kChunk; idx += kLanes) {
-    const int n = idx / kChunk, k = idx % kChunk;
-    sC[n][k] = k < nt ? Cm[(b * N + n) * L + t0 + k] : 0.f;
-  }
-  const int64_t wrow0 = b * D + cb * kLanes + wave * 64;
-  const int wrows = D - (cb * kLanes + wave * 64);
-  float dr[kChunk], gy[kChunk];
-  s6::rows_in<VEC>(dl, wrow0, wrows, L, t0, nt, sT[wave], lane, dr);
-  s6::rows_in<VEC>(dy, wrow0, wrows, L, t0, nt, sT[wave], lane, gy);
-  float a2[N];
-#pragma unroll
-  for (int n = 0; n < N; ++n) a2[n] = valid ? A[(int64_t)d * N + n] * kLog2e : 0.f;
-  __syncthreads();   // C staged
-  float carry[N];
-#pragma unroll
-  for (int n = 0; n < N; ++n) carry[n] = 0.f;
-  float dsum = 0.f;
-#pragma unroll
-  for (int t = kChunk - 1; t >= 0; --t) {
-    dsum += dr[t];
-#pragma unroll
-    for (int n = 0; n < N; ++n) carry[n] = exp2_hw(dr[t] * a2[n]) * fmaf(sC[n][t], gy[t], carry[n]);
-  }
-  if (valid) {
-    const int64_t rec = (b * nc + c) * D + d;
-#pragma unroll
-    for (int n = 0; n < N; ++n) O[rec * N + n] = carry[n];
-    SD[rec] = dsum;
-  }
-}
 
 // 2. per (batch row, channel): the adjoint entering each chunk from the
 // right, R[c]; dh0 at the end. Chunks are walked from the last, their
@@ -677,17 +630,10 @@ hipError_t launch_bwd_n(const S6BwdProblem& p, hipStream_t s) {
                          p.dh0, p.bt, (int)p.D, (int64_t)0);
     return hipGetLastError();
   }
-  if (vec)
-    hipLaunchKernelGGL((s6_bwd_local<N, true>), grid, dim3(kLanes), 0, s, p.delta, p.A, p.C, p.dy, p.O, p.SD, p.L,
-                       (int)p.D, nc);
-  else
-    hipLaunchKernelGGL((s6_bwd_local<N, false>), grid, dim3(kLanes), 0, s, p.delta, p.A, p.C, p.dy, p.O, p.SD, p.L,
-                       (int)p.D, nc);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  // (O and SD come from the forward sweep, s6_onepass)
   hipLaunchKernelGGL(s6_bwd_carry<N>, dim3(grid_of(p.bt * p.D)), dim3(256), 0, s, p.A, p.O, p.SD, p.dhT, p.R, p.dh0,
                      p.bt, (int)p.D, nc);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (N <= 4) {
     if (vec)

@@ -21,6 +21,11 @@ struct S6Problem {
   float* aggD;                  // workspace: [bt][nchunks][D] each chunk's sum of delta
   float* incl;                  // workspace: [bt][nchunks][D][N] each chunk's end state
   int* sync;                    // workspace: s6_sync_words int32 (ticket counter, error word, flags)
+  // the backward pass's forward sweep (y, hT null): with dy set, each chunk's
+  // adjoint record O [bt][nchunks][D][N] and delta sum SD [bt][nchunks][D]
+  const float* dy = nullptr;    // [bt][D][L]
+  float* O = nullptr;
+  float* SD = nullptr;
 };
 
 // One backward call (s6_bwd.hip): the inputs above, the upstream gradients,

@@ -107,18 +107,27 @@ __global__ void s6_pass_state(const float* h0, float* hT, int64_t n) {
   if (i < n) hT[i] = h0 ? h0[i] : 0.f;
 }
 
-template <int N, bool VEC>
+// BWD: the backward pass's forward sweep. No y and no final state; instead,
+// from dy, each chunk's adjoint record for the backward pass: O, the
+// adjoint that the chunk's own dy leaves at its first token,
+// sum_t (a_t0 ... a_t) C_t dy_t per state, and the chunk's sum of delta SD
+// (so the backward pass needs no reverse sweep of its own per chunk).
+template <int N, bool VEC, bool BWD>
 __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 ? 1 : 2))) void s6_onepass(const float* __restrict__ x, const float* __restrict__ dl,
                                                      const float* __restrict__ A, const float* __restrict__ Bm,
                                                      const float* __restrict__ Cm, const float* h0, float* y,
                                                      float* hT, float* aggS, float* aggD, float* incl, int* sync,
-                                                     int64_t L, int D, int64_t nc, int64_t ntickets) {
+                                                     const float* __restrict__ dy, float* __restrict__ Oc,
+                                                     float* __restrict__ SD, int64_t L, int D, int64_t nc,
+                                                     int64_t ntickets) {
   __shared__ __attribute__((aligned(16))) float sB[N][kChunk];
   __shared__ __attribute__((aligned(16))) float sC[N][kChunk];
   __shared__ __attribute__((aligned(1024))) unsigned char sT[kLanes / 64][64 * 256];   // per wave: x, delta, then y
   __shared__ int64_t sTicket;
   const int tid = threadIdx.x;
-  const int wave = tid / 64, lane = tid % 64;
+  // (the wave index read back as uniform: the tile addresses it forms stay in
+  // scalar registers)
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   unsigned char* const tile = sT[wave];
   const int ncb = (D + kLanes - 1) / kLanes;
   const int64_t per = ntickets / nc;   // tickets per chunk = batch rows * channel blocks
@@ -178,6 +187,16 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // read out before the tile is refilled
       }
     }
+    if constexpr (BWD) {
+      // dy stays in the tile, read 4 tokens at a time by its lane (past the
+      // sequence it holds the next row's tokens, which meet C = 0 there)
+      if constexpr (VEC) {
+        if (wrows > 0) s6::tile_load(dy, wrow0, wrows < 64 ? wrows : 64, L, t0, tile, lane);
+      } else {
+        s6::tile_load_scalar(dy, wrow0, wrows, L, t0, nt, tile, lane);
+      }
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    }
     float a2[N];
 #pragma unroll
     for (int n = 0; n < N; ++n) a2[n] = valid ? A[(int64_t)d * N + n] * kLog2e : 0.f;
@@ -185,10 +204,16 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
 
     // 1. the chunk from a zero state. Past the sequence x, delta, B and C are
     // zero, so padded tokens leave h unchanged (exp2(0) = 1, no input).
-    float h[N];
+    float h[N], pa[N], oa[N];   // (BWD: the running decay product and O)
 #pragma unroll
-    for (int n = 0; n < N; ++n) h[n] = 0.f;
+    for (int n = 0; n < N; ++n) {
+      h[n] = 0.f;
+      pa[n] = 1.f;
+      oa[n] = 0.f;
+    }
     float dsum = 0.f;
+    int lnb = lane;
+    asm volatile("" : "+v"(lnb));
 #pragma unroll
     for (int t4 = 0; t4 < kChunk; t4 += 4) {
       float u[4];
@@ -197,14 +222,42 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
         u[j] = dr[t4 + j] * xr[t4 + j];
         dsum += dr[t4 + j];
       }
+      float gj[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BWD) {
+        const float4 g4 = *reinterpret_cast<const float4*>(tile + s6::tile_off((uint32_t)lnb, (uint32_t)(t4 / 4)));
+        gj[0] = g4.x;
+        gj[1] = g4.y;
+        gj[2] = g4.z;
+        gj[3] = g4.w;
+      }
 #pragma unroll
       for (int n = 0; n < N; ++n) {
         const float4 b4 = *reinterpret_cast<const float4*>(&sB[n][t4]);
         const float bj[4] = {b4.x, b4.y, b4.z, b4.w};
+        if constexpr (BWD) {
+          const float4 c4 = *reinterpret_cast<const float4*>(&sC[n][t4]);
+          const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) h[n] = fmaf(exp2_hw(dr[t4 + j] * a2[n]), h[n], u[j] * bj[j]);
+          for (int j = 0; j < 4; ++j) {
+            const float a = exp2_hw(dr[t4 + j] * a2[n]);
+            h[n] = fmaf(a, h[n], u[j] * bj[j]);
+            pa[n] *= a;
+            oa[n] = fmaf(pa[n], cj[j] * gj[j], oa[n]);
+          }
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) h[n] = fmaf(exp2_hw(dr[t4 + j] * a2[n]), h[n], u[j] * bj[j]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);   // one group of tokens at a time: bounded live ranges
+    }
+    if constexpr (BWD) {
+      // (through resources over the block's valid records: no branch, which
+      // the compiler would otherwise sink the O chain into)
+      const int64_t rec0 = (b * nc + c) * D + cb * kLanes;
+      const uint32_t nrec = (uint32_t)(D - cb * kLanes < kLanes ? D - cb * kLanes : kLanes);
+      st_state<N>(lookback::urs(Oc + rec0 * N, nrec * N * 4), (uint32_t)tid * N * 4, oa);
+      st_state<1>(lookback::urs(SD + rec0, nrec * 4), (uint32_t)tid * 4, &dsum);
     }
     int* const myflag = flags + (b * nc + c) * ncb + cb;
 
@@ -284,7 +337,7 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
     // decays are recomputed: kept from the first scan they would take 64 N
     // registers per lane, so the operands are laundered to stop the compiler
     // from keeping them.)
-    if (y) {
+    if (!BWD && y) {
 #pragma unroll
     for (int t = 0; t < kChunk; ++t) asm volatile("" : "+v"(dr[t]));
 #pragma unroll
@@ -349,7 +402,7 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
   }
 }
 
-template <int N, bool VEC>
+template <int N, bool VEC, bool BWD>
 int onepass_slots() {
   static int cached[64] = {};
   int dev = 0;
@@ -360,7 +413,7 @@ int onepass_slots() {
   if (!cached[dev]) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, s6_onepass<N, VEC>, kLanes, 0) != hipSuccess || cus <= 0 ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, s6_onepass<N, VEC, BWD>, kLanes, 0) != hipSuccess || cus <= 0 ||
         per_cu <= 0) {
       (void)hipGetLastError();
       cus = 256;
@@ -387,20 +440,32 @@ hipError_t launch_n(const S6Problem& p, hipStream_t s) {
   // 16-byte aligned (and 64 rows of one array stay below 2 GB of offsets)
   const int vec = (p.L % 4 == 0 && p.L <= ((int64_t)1 << 22) && (reinterpret_cast<uintptr_t>(p.x) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(p.delta) & 15) == 0 &&
-                   (reinterpret_cast<uintptr_t>(p.y) & 15) == 0) ? 1 : 0;
+                   (reinterpret_cast<uintptr_t>(p.y) & 15) == 0 && (reinterpret_cast<uintptr_t>(p.dy) & 15) == 0)
+                      ? 1 : 0;
   const int64_t ncb = (p.D + kLanes - 1) / kLanes;
   const int64_t ntickets = nc * p.bt * ncb;
   const int64_t words = kSyncWords + ntickets;
   const int64_t cblocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
   hipLaunchKernelGGL(s6_clear, dim3((unsigned)cblocks), dim3(256), 0, s, p.sync, words);
-  const int slots = vec ? onepass_slots<N, true>() : onepass_slots<N, false>();
-  const int64_t grid = ntickets < slots ? ntickets : slots;
-  if (vec)
-    hipLaunchKernelGGL((s6_onepass<N, true>), dim3((unsigned)grid), dim3(kLanes), 0, s, p.x, p.delta, p.A, p.B, p.C,
-                       p.h0, p.y, p.hT, p.aggS, p.aggD, p.incl, p.sync, p.L, (int)p.D, nc, ntickets);
-  else
-    hipLaunchKernelGGL((s6_onepass<N, false>), dim3((unsigned)grid), dim3(kLanes), 0, s, p.x, p.delta, p.A, p.B, p.C,
-                       p.h0, p.y, p.hT, p.aggS, p.aggD, p.incl, p.sync, p.L, (int)p.D, nc, ntickets);
+  const auto go = [&](auto kernel, int slots) {
+    const int64_t grid = ntickets < slots ? ntickets : slots;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kLanes), 0, s, p.x, p.delta, p.A, p.B, p.C, p.h0, p.y,
+                       p.hT, p.aggS, p.aggD, p.incl, p.sync, p.dy, p.O, p.SD, p.L, (int)p.D, nc, ntickets);
+  };
+  if (p.dy) {
+    if constexpr (N <= 8) {
+      if (vec)
+        go(s6_onepass<N, true, true>, onepass_slots<N, true, true>());
+      else
+        go(s6_onepass<N, false, true>, onepass_slots<N, false, true>());
+    } else {
+      return hipErrorInvalidValue;   // no backward pass for this N
+    }
+  } else if (vec) {
+    go(s6_onepass<N, true, false>, onepass_slots<N, true, false>());
+  } else {
+    go(s6_onepass<N, false, false>, onepass_slots<N, false, false>());
+  }
   return hipGetLastError();
 }
 
