@@ -45,34 +45,33 @@ constexpr int kBwdLanes = 64;   // channels per workgroup of the chunk kernel (o
 // piece length of the recomputation: the states of S tokens are held at once
 template <int N> struct BwdPiece { static constexpr int S = N >= 8 ? 4 : 8; };
 
-// 2. per (batch row, channel): the adjoint entering each chunk from the
-// right, R[c]; dh0 at the end. Chunks are walked from the last, their
-// records read eight chunks ahead.
+// 2. per (batch row, channel, state): the adjoint entering each chunk from
+// the right, R[c]; dh0 at the end. Chunks are walked from the last, their
+// records read eight chunks ahead; threads take consecutive (channel, state)
+// pairs, so every record read and written is coalesced.
 template <int N>
 __global__ __launch_bounds__(256) void s6_bwd_carry(const float* __restrict__ A, const float* __restrict__ O,
                                                     const float* __restrict__ SD, const float* __restrict__ dhT,
                                                     float* __restrict__ R, float* __restrict__ dh0, int64_t bt, int D,
                                                     int64_t nc) {
-  // i = b * D + d; grid-stride, the grid being capped at 65536 workgroups
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < bt * D;
+  // i = (b * D + d) * N + n; grid-stride, the grid being capped at 65536
+  // workgroups
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < bt * D * N;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t b = i / D;
-    const int d = (int)(i % D);
-    float a2[N], r[N];
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-      a2[n] = A[(int64_t)d * N + n] * kLog2e;
-      r[n] = dhT ? dhT[i * N + n] : 0.f;
-    }
+    const int64_t bd = i / N;
+    const int n = (int)(i % N);
+    const int64_t b = bd / D;
+    const int d = (int)(bd % D);
+    const float a2 = A[(int64_t)d * N + n] * kLog2e;
+    float r = dhT ? dhT[i] : 0.f;
     constexpr int CR = 8;
     for (int64_t c1 = nc - 1; c1 >= 0; c1 -= CR) {
-      float ov[CR][N], sv[CR];
+      float ov[CR], sv[CR];
 #pragma unroll
       for (int j = 0; j < CR; ++j) {
         const int64_t c = c1 - j;
         const int64_t rec = (b * nc + (c >= 0 ? c : 0)) * D + d;
-#pragma unroll
-        for (int n = 0; n < N; ++n) ov[j][n] = c >= 0 ? O[rec * N + n] : 0.f;
+        ov[j] = c >= 0 ? O[rec * N + n] : 0.f;
         sv[j] = c >= 0 ? SD[rec] : 0.f;
       }
 #pragma unroll
@@ -80,17 +79,11 @@ __global__ __launch_bounds__(256) void s6_bwd_carry(const float* __restrict__ A,
         const int64_t c = c1 - j;
         if (c < 0) break;
         const int64_t rec = (b * nc + c) * D + d;
-#pragma unroll
-        for (int n = 0; n < N; ++n) {
-          R[rec * N + n] = r[n];
-          r[n] = fmaf(exp2_hw(a2[n] * sv[j]), r[n], ov[j][n]);
-        }
+        R[rec * N + n] = r;
+        r = fmaf(exp2_hw(a2 * sv[j]), r, ov[j]);
       }
     }
-    if (dh0) {
-#pragma unroll
-      for (int n = 0; n < N; ++n) dh0[i * N + n] = r[n];
-    }
+    if (dh0) dh0[i] = r;
   }
 }
 
@@ -593,17 +586,53 @@ __global__ __launch_bounds__(64 * kRedWaves) void s6_bwd_reduce_dA(const float* 
   }
 }
 unsigned dA_grid(int64_t DN) { return (unsigned)(DN > 0 ? (DN + 63) / 64 : 1); }
+// dB, dC: the channel blocks' parts summed in block order; V4: four
+// consecutive tokens per thread (N L a multiple of 4, dB and dC 16-byte
+// aligned)
+template <bool V4>
 __global__ void s6_bwd_reduce_bc(const float* __restrict__ pb, const float* __restrict__ pc, float* __restrict__ dB,
                                  float* __restrict__ dC, int64_t bt, int ncb, int64_t NL) {
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < bt * NL; i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t b = i / NL, e = i % NL;
-    float sb = 0.f, sc = 0.f;
-    for (int k = 0; k < ncb; ++k) {
-      sb += pb[(b * ncb + k) * NL + e];
-      sc += pc[(b * ncb + k) * NL + e];
+  constexpr int W = V4 ? 4 : 1;
+  const int64_t nl = NL / W;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < bt * nl; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = i / nl, e = (i % nl) * W;
+    if constexpr (V4) {
+      float4 sb = make_float4(0.f, 0.f, 0.f, 0.f), sc = sb;
+      // eight blocks' loads issued before their sums (left to itself the
+      // compiler waits for each load in turn)
+      int k = 0;
+      for (; k + 8 <= ncb; k += 8) {
+        float4 vb[8], vc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int64_t o = (b * ncb + k + j) * NL + e;
+          vb[j] = *reinterpret_cast<const float4*>(pb + o);
+          vc[j] = *reinterpret_cast<const float4*>(pc + o);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          sb.x += vb[j].x; sb.y += vb[j].y; sb.z += vb[j].z; sb.w += vb[j].w;
+          sc.x += vc[j].x; sc.y += vc[j].y; sc.z += vc[j].z; sc.w += vc[j].w;
+        }
+      }
+      for (; k < ncb; ++k) {
+        const float4 vb = *reinterpret_cast<const float4*>(pb + (b * ncb + k) * NL + e);
+        const float4 vc = *reinterpret_cast<const float4*>(pc + (b * ncb + k) * NL + e);
+        sb.x += vb.x; sb.y += vb.y; sb.z += vb.z; sb.w += vb.w;
+        sc.x += vc.x; sc.y += vc.y; sc.z += vc.z; sc.w += vc.w;
+      }
+      *reinterpret_cast<float4*>(dB + b * NL + e) = sb;
+      *reinterpret_cast<float4*>(dC + b * NL + e) = sc;
+    } else {
+      float sb = 0.f, sc = 0.f;
+#pragma unroll 8
+      for (int k = 0; k < ncb; ++k) {
+        sb += pb[(b * ncb + k) * NL + e];
+        sc += pc[(b * ncb + k) * NL + e];
+      }
+      dB[b * NL + e] = sb;
+      dC[b * NL + e] = sc;
     }
-    dB[i] = sb;
-    dC[i] = sc;
   }
 }
 
@@ -626,13 +655,13 @@ hipError_t launch_bwd_n(const S6BwdProblem& p, hipStream_t s) {
     hipLaunchKernelGGL(s6_bwd_reduce_dA, dim3(dA_grid(p.D * N)), dim3(64 * kRedWaves), 0, s, p.dA_part, p.dA, (int64_t)0,
                        p.D * N);
     if (p.bt > 0)
-      hipLaunchKernelGGL(s6_bwd_carry<N>, dim3(grid_of(p.bt * p.D)), dim3(256), 0, s, p.A, p.O, p.SD, p.dhT, p.R,
-                         p.dh0, p.bt, (int)p.D, (int64_t)0);
+      hipLaunchKernelGGL(s6_bwd_carry<N>, dim3(grid_of(p.bt * p.D * N)), dim3(256), 0, s, p.A, p.O, p.SD, p.dhT,
+                         p.R, p.dh0, p.bt, (int)p.D, (int64_t)0);
     return hipGetLastError();
   }
   // (O and SD come from the forward sweep, s6_onepass)
-  hipLaunchKernelGGL(s6_bwd_carry<N>, dim3(grid_of(p.bt * p.D)), dim3(256), 0, s, p.A, p.O, p.SD, p.dhT, p.R, p.dh0,
-                     p.bt, (int)p.D, nc);
+  hipLaunchKernelGGL(s6_bwd_carry<N>, dim3(grid_of(p.bt * p.D * N)), dim3(256), 0, s, p.A, p.O, p.SD, p.dhT, p.R,
+                     p.dh0, p.bt, (int)p.D, nc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (N <= 4) {
@@ -653,8 +682,13 @@ hipError_t launch_bwd_n(const S6BwdProblem& p, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(s6_bwd_reduce_dA, dim3(dA_grid(p.D * N)), dim3(64 * kRedWaves), 0, s, p.dA_part, p.dA, p.bt * nc, p.D * N);
-  hipLaunchKernelGGL(s6_bwd_reduce_bc, dim3(grid_of(p.bt * N * p.L)), dim3(256), 0, s, p.dB_part, p.dC_part, p.dB,
-                     p.dC, p.bt, (int)(N <= 4 ? ncb1 : ncb), (int64_t)N * p.L);
+  const int ncbp = (int)(N <= 4 ? ncb1 : ncb);
+  if ((N * p.L) % 4 == 0 && (reinterpret_cast<uintptr_t>(p.dB) & 15) == 0 && (reinterpret_cast<uintptr_t>(p.dC) & 15) == 0)
+    hipLaunchKernelGGL(s6_bwd_reduce_bc<true>, dim3(grid_of(p.bt * N * p.L / 4)), dim3(256), 0, s, p.dB_part,
+                       p.dC_part, p.dB, p.dC, p.bt, ncbp, (int64_t)N * p.L);
+  else
+    hipLaunchKernelGGL(s6_bwd_reduce_bc<false>, dim3(grid_of(p.bt * N * p.L)), dim3(256), 0, s, p.dB_part, p.dC_part,
+                       p.dB, p.dC, p.bt, ncbp, (int64_t)N * p.L);
   return hipGetLastError();
 }
 
