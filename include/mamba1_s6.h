@@ -89,11 +89,11 @@ int mamba1_s6_fwd(const mamba1_s6_dims* dims, const float* x, const float* delta
  * [batch][channels][dstate]. Outputs, float32, dense, caller-owned, written
  * whole: dx, ddelta like x; dA like A; dB, dC like B; dh0 like h0 (nullable:
  * not written). dstate 1, 2, 4 or 8 (UNSUPPORTED for 16).
- * The call runs the forward scan for the chunks' end states (no y), then the
- * chunks' backward scans with their entering adjoints, the per-chunk
- * gradients (each chunk's states recomputed from its entering state) and the
- * sums over batch rows, chunks and channel blocks, in fixed orders
- * (deterministic). fp32 arithmetic throughout.
+ * The call runs the forward scan for the chunks' end states (no y), which
+ * also forms each chunk's own adjoint record from dy; then the chunks'
+ * entering adjoints, the per-chunk gradients (each chunk's states recomputed
+ * from its entering state) and the sums over batch rows, chunks and channel
+ * blocks, in fixed orders (deterministic). fp32 arithmetic throughout.
  * Workspace: mamba1_s6_bwd_workspace_bytes(dims) bytes of device memory
  * (the forward's, plus per-chunk adjoints and partial sums); two calls that
  * share it must not overlap in time.
