@@ -275,6 +275,8 @@ def run_bwd(args, cfg):
 
     dev = torch.device("cuda:0")
     inp = generate(cfg)
+    if args.copy_calibration:
+        copy_calibration(dev)
     rng = np.random.default_rng(cfg.seed + 1000)
     dy = rng.standard_normal((cfg.batch, cfg.seqlen, cfg.nheads, cfg.headdim)).astype(np.float32)
     dfin = rng.standard_normal((cfg.batch, cfg.nheads, cfg.headdim, cfg.dstate)).astype(np.float32)
