@@ -467,7 +467,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
     const float* __restrict__ dhn, const float* __restrict__ dXp, const float* __restrict__ rowZ,
     const float* __restrict__ colZ, const float* __restrict__ colW, float* __restrict__ dx, float* __restrict__ ddt,
     float* __restrict__ dA_part, float* __restrict__ dD_part, uint4* __restrict__ dhnT, uint4* __restrict__ hpT,
-    int64_t Tlen, int H, int G, int64_t nc, int64_t Tp) {
+    int64_t Tlen, int H, int G, int64_t nc, int64_t Tp, int64_t nbk) {
   using Frag = bf16x8;
   using Cf = FinCfg<N>;
   constexpr int KS = N / 16, RP = Cf::RP;
@@ -480,8 +480,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void s
   const int tid = threadIdx.x, lane = tid & 63;
   const int v = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave 0..7 = token block
   const int hf = lane >> 5, jl = lane & 31;
-  const int h = (int)(blockIdx.x % H);
-  const int64_t bk = blockIdx.x / H, k = bk % nc, b = bk / nc;
+  // XCD-aware order: workgroup tau runs on XCD tau % 8, and the heads of one
+  // (b, k) share an XCD, so its B, C rows and DX blocks are read into one L2
+  const int64_t tau = blockIdx.x, xcd = tau % 8, slot = tau / 8;
+  const int64_t bk = (slot / H) * 8 + xcd;
+  if (bk >= nbk) return;
+  const int h = (int)(slot % H);
+  const int64_t k = bk % nc, b = bk / nc;
   const int grp = h / (H / G);
   const int64_t t0 = k * kQ;
   const int nvalid = (int)(Tlen - t0 < kQ ? Tlen - t0 : kQ);
@@ -908,8 +913,9 @@ hipError_t launch_bwd_fused_headsum(const BwdProblem& p, const void* X, const fl
 }
 
 hipError_t launch_bwd_fused_finish(const BwdProblem& p, hipStream_t s) {
-  const int64_t items = p.bt * p.nc * p.H;
-  if (items <= 0) return hipSuccess;
+  const int64_t nbk = p.bt * p.nc;
+  const int64_t items = (nbk + 7) / 8 * 8 * p.H;   // (b, k) padded to a multiple of 8
+  if (nbk <= 0 || p.H <= 0) return hipSuccess;
   if (items > 0x7fffffff) return hipErrorInvalidValue;
   const bf16* x = static_cast<const bf16*>(p.x);
   const bf16* dy = static_cast<const bf16*>(p.dy);
@@ -918,11 +924,11 @@ hipError_t launch_bwd_fused_finish(const BwdProblem& p, hipStream_t s) {
   if (p.N == 64)
     hipLaunchKernelGGL(ssd_bwd_state_finish<64>, dim3((unsigned)items), dim3(512), 0, s, x, dy, Bm, Cm, p.A, p.D,
                        p.gcum, p.dtt, p.wst, p.hprev, p.dhn, p.dXp, p.rowZ, p.colZ, p.colW, p.dx, p.ddt, p.dA_part,
-                       p.dD_part, (uint4*)p.U, (uint4*)p.V, p.T, (int)p.H, (int)p.G, p.nc, p.Tp);
+                       p.dD_part, (uint4*)p.U, (uint4*)p.V, p.T, (int)p.H, (int)p.G, p.nc, p.Tp, nbk);
   else
     hipLaunchKernelGGL(ssd_bwd_state_finish<128>, dim3((unsigned)items), dim3(512), 0, s, x, dy, Bm, Cm, p.A, p.D,
                        p.gcum, p.dtt, p.wst, p.hprev, p.dhn, p.dXp, p.rowZ, p.colZ, p.colW, p.dx, p.ddt, p.dA_part,
-                       p.dD_part, (uint4*)p.U, (uint4*)p.V, p.T, (int)p.H, (int)p.G, p.nc, p.Tp);
+                       p.dD_part, (uint4*)p.U, (uint4*)p.V, p.T, (int)p.H, (int)p.G, p.nc, p.Tp, nbk);
   return hipGetLastError();
 }
 
