@@ -57,8 +57,10 @@ size_t mamba1_s6_workspace_bytes(const mamba1_s6_dims* dims);
 /* Host-only validation of a call: NULL_POINTER (a required pointer missing:
  * A always; x, delta, B, C, y when batch * seqlen > 0), BAD_DIM (a size out
  * of range or a grid limit: batch <= 65535, ceil(seqlen / 64) <= 65535),
- * UNSUPPORTED (dstate), WORKSPACE, ALIAS (y or hT overlapping an input,
- * each other or the workspace; hT may equal h0 exactly). */
+ * UNSUPPORTED (dstate), WORKSPACE, ALIGN (a float array not 4-byte
+ * aligned, or the workspace not 256-byte aligned when batch > 0), ALIAS (y
+ * or hT overlapping an input, each other or the workspace; hT may equal h0
+ * exactly). */
 int mamba1_s6_check_args(const mamba1_s6_dims* dims, const float* x, const float* delta,
                          const float* A, const float* B, const float* C, const float* h0,
                          const float* y, const float* hT, const void* workspace,
@@ -98,8 +100,8 @@ int mamba1_s6_fwd(const mamba1_s6_dims* dims, const float* x, const float* delta
  * (the forward's, plus per-chunk adjoints and partial sums); two calls that
  * share it must not overlap in time.
  * Errors: as mamba1_s6_check_args (NULL_POINTER: A, dA always; x, delta, B,
- * C, dy, dx, ddelta, dB, dC when batch * seqlen > 0), ALIAS when an output
- * overlaps an input, another output or the workspace. Validation runs on
+ * C, dy, dx, ddelta, dB, dC when batch * seqlen > 0; ALIGN as there), ALIAS
+ * when an output overlaps an input, another output or the workspace. Validation runs on
  * the host before any launch; the call is asynchronous on `stream`. */
 size_t mamba1_s6_bwd_workspace_bytes(const mamba1_s6_dims* dims);
 

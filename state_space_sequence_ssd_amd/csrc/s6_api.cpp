@@ -3,9 +3,11 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <initializer_list>
 
 #include "mamba1_s6.h"
 #include "mamba2_ssd.h"
+
 #include "s6_launch.h"
 
 namespace {
@@ -91,6 +93,16 @@ Range range_of(const void* p, size_t bytes) {
 }
 bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
 
+// float arrays at their natural 4 bytes; the workspace at 256 bytes (its
+// records are moved in 16-byte pieces and its ticket counter is a 64-bit
+// atomic)
+bool floats_aligned(std::initializer_list<const float*> ps) {
+  for (const float* q : ps)
+    if (reinterpret_cast<uintptr_t>(q) % 4) return false;
+  return true;
+}
+bool workspace_aligned(const void* w) { return reinterpret_cast<uintptr_t>(w) % 256 == 0; }
+
 }  // namespace
 
 extern "C" {
@@ -112,6 +124,8 @@ int mamba1_s6_check_args(const mamba1_s6_dims* d, const float* x, const float* d
   if (s.n_x > 0 && (!x || !delta || !B || !C || !y)) return MAMBA2_SSD_ERR_NULL_POINTER;
   const bool work = d->batch > 0;
   if (work && s.total > 0 && (!workspace || workspace_bytes < s.total)) return MAMBA2_SSD_ERR_WORKSPACE;
+  if (!floats_aligned({x, delta, A, B, C, h0, y, hT}) || (work && !workspace_aligned(workspace)))
+    return MAMBA2_SSD_ERR_ALIGN;
   const Range rx = range_of(x, (size_t)s.n_x * 4), rd = range_of(delta, (size_t)s.n_x * 4);
   const Range rA = range_of(A, (size_t)(d->channels * d->dstate) * 4);
   const Range rB = range_of(B, (size_t)s.n_bc * 4), rC = range_of(C, (size_t)s.n_bc * 4);
@@ -164,6 +178,9 @@ int mamba1_s6_bwd_check_args(const mamba1_s6_dims* d, const float* x, const floa
     return MAMBA2_SSD_ERR_NULL_POINTER;
   const bool work = d->batch > 0;
   if (work && (!workspace || workspace_bytes < s.total)) return MAMBA2_SSD_ERR_WORKSPACE;
+  if (!floats_aligned({x, delta, A, B, C, h0, dy, dhT, dx, ddelta, dA, dB, dC, dh0}) ||
+      (work && !workspace_aligned(workspace)))
+    return MAMBA2_SSD_ERR_ALIGN;
   const size_t nx = (size_t)s.f.n_x * 4, nbc = (size_t)s.f.n_bc * 4, nst = (size_t)s.f.n_state * 4;
   const size_t nA = (size_t)(d->channels * d->dstate) * 4;
   const Range ins[] = {range_of(x, nx), range_of(delta, nx), range_of(A, nA), range_of(B, nbc), range_of(C, nbc),

@@ -504,6 +504,11 @@ def test_s6_validation():
     assert _s6_check(S6_SMALL, hT=p["h0"]) == OK          # in place
     assert _s6_check(S6_SMALL, hT=p["h0"] + 4) == ALIAS   # partial overlap
     assert _s6_check(S6_SMALL, ws=0) == WS
+    # float arrays at 4 bytes, the workspace at 256 bytes
+    for name in ("x", "delta", "A", "B", "C", "h0", "y", "hT"):
+        assert _s6_check(S6_SMALL, **{name: p[name] + 2}) == ALIGN, name
+    assert _s6_check(S6_SMALL, ws=p["ws"] + 16) == ALIGN
+    assert _s6_check(S6_SMALL, x=p["x"] + 4, y=p["y"] + 8) == OK   # 4-byte offsets take the 4-byte loads
     bad = ssd.S6Dims(2, 300, 96, 12)
     assert ssd.s6_workspace_bytes(bad) == 0 and _s6_check(bad) == UNSUP
     assert ssd.s6_workspace_bytes(ssd.S6Dims(70000, 10, 4, 4)) == 0
@@ -551,6 +556,10 @@ def test_s6_bwd_workspace_and_validation():
     assert _s6_bwd_check(d4, dB=p["dC"]) == ALIAS
     assert _s6_bwd_check(d4, dh0=p["h0"]) == ALIAS
     assert _s6_bwd_check(d4, ws=0) == WS
+    for name in ("x", "dy", "dhT", "dx", "dA", "dB", "dh0"):
+        assert _s6_bwd_check(d4, **{name: p[name] + 2}) == ALIGN, name
+    assert _s6_bwd_check(d4, ws=p["ws"] + 64) == ALIGN
+    assert _s6_bwd_check(d4, dB=p["dB"] + 4, dC=p["dC"] + 12) == OK
     # dstate 16 has a forward scan but no backward kernels
     assert ssd.s6_supported(16) and ssd.s6_bwd_workspace_bytes(ssd.S6Dims(2, 300, 96, 16)) == 0
     assert _s6_bwd_check(ssd.S6Dims(2, 300, 96, 16)) == UNSUP
