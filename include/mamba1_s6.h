@@ -90,7 +90,7 @@ int mamba1_s6_fwd(const mamba1_s6_dims* dims, const float* x, const float* delta
  * mamba1_s6_fwd; dy [batch][channels][seqlen]; dhT (nullable)
  * [batch][channels][dstate]. Outputs, float32, dense, caller-owned, written
  * whole: dx, ddelta like x; dA like A; dB, dC like B; dh0 like h0 (nullable:
- * not written). dstate 1, 2, 4 or 8 (UNSUPPORTED for 16).
+ * not written). dstate 1, 2, 4, 8 or 16.
  * The call runs the forward scan for the chunks' end states (no y), which
  * also forms each chunk's own adjoint record from dy; then the chunks'
  * entering adjoints, the per-chunk gradients (each chunk's states recomputed

@@ -18,12 +18,14 @@
 //      delta (its decays multiply to exp(A sum));
 //   2. s6_bwd_carry: the adjoint entering each chunk from the right,
 //      R_{c-1} = O_c + exp(A sum_c delta) R_c from R_last = dhT, and dh0;
-//   3. s6_bwd_chunk: per chunk and 64 channels (one wave), the states
-//      recomputed forward from the entering state (kept every S tokens),
-//      then per S-token piece, last first, the piece's states again and the
-//      backward step for each token, which gives dx, ddelta and the
-//      per-chunk parts of dA, dB and dC (the dB and dC parts summed over the
-//      wave's 64 channels in registers, by lane swaps and DPP);
+//   3. s6_bwd_chunk: per chunk and 64 channels (one wave) and group of up
+//      to 4 states (one pass per group, each adding its terms of dx and
+//      ddelta to the earlier passes'), the states recomputed forward from
+//      the entering state (kept every 8 tokens), then per 8-token piece, last
+//      first, the piece's states again and the backward step for each token,
+//      which gives dx, ddelta and the per-chunk parts of dA, dB and dC (the
+//      dB and dC parts summed over the wave's 64 channels in registers, by
+//      lane swaps and DPP);
 //   4. s6_bwd_reduce: dA over batch rows and chunks, dB and dC over channel
 //      blocks (fixed orders: deterministic).
 // Lanes are channels, as in the forward pass; each lane holds its chunk's x
@@ -39,11 +41,10 @@ namespace ssd {
 namespace {
 
 constexpr int kChunk = 64;      // tokens per chunk (the forward pass's)
-constexpr int kLanes = 256;     // channels per workgroup of the wide chunk kernel (4 waves)
 constexpr int kBwdLanes = 64;   // channels per workgroup of the chunk kernel (one wave)
 
 // piece length of the recomputation: the states of S tokens are held at once
-template <int N> struct BwdPiece { static constexpr int S = N >= 8 ? 4 : 8; };
+template <int N> struct BwdPiece { static constexpr int S = 8; };
 
 // 2. per (batch row, channel, state): the adjoint entering each chunk from
 // the right, R[c]; dh0 at the end. Chunks are walked from the last, their
@@ -264,20 +265,36 @@ __device__ __forceinline__ void half_dy(const float* dy, int64_t row0, int rows_
   for (int t = 0; t < kHalf; ++t) sY[t][lane] = gy[t];
 }
 
+// A half chunk's outputs out as whole rows; with ACC, added to what an
+// earlier state group's pass left there (fixed order: deterministic)
+template <bool VEC, bool ACC>
+__device__ __forceinline__ void half_out(float* dst, int64_t row0, int rows_valid, int64_t L, int64_t t0h, int nth,
+                                         unsigned char* tile, int lane, float* v) {
+  if constexpr (ACC) {
+    float prev[kHalf];
+    s6::rows_in<VEC, kHalf>(dst, row0, rows_valid, L, t0h, nth, tile, lane, prev);
+#pragma unroll
+    for (int t = 0; t < kHalf; ++t) v[t] = prev[t] + v[t];
+  }
+  s6::rows_out<VEC, kHalf>(dst, row0, rows_valid, L, t0h, nth, tile, lane, v);
+}
+
 // 3. per (batch row, chunk, 64 channels; one wave): dx, ddelta and the
-// chunk's parts of dA, dB and dC (N <= 4). The chunk is taken in halves of
-// 32 tokens, the second first: forward over the first half (its piece
+// chunk's parts of dA, dB and dC for the states n0 .. n0 + N - 1 of NT (N <=
+// 4; larger dstates run one pass per group of 4 states, each adding its dx,
+// ddelta terms to the earlier passes': ACC). The chunk is taken in halves
+// of 32 tokens, the second first: forward over the first half (its piece
 // checkpoints kept), forward over the second, backward over the second, then
 // the first half's x and delta read again and its backward steps. At most
 // 256 registers and 18 KB of LDS: two waves per SIMD.
-template <int N, bool VEC>
+template <int N, int NT, bool VEC, bool ACC>
 __global__ __launch_bounds__(kBwdLanes) __attribute__((amdgpu_waves_per_eu(2))) void s6_bwd_chunk(
     const float* __restrict__ x, const float* __restrict__ dl, const float* __restrict__ A,
     const float* __restrict__ Bm, const float* __restrict__ Cm, const float* __restrict__ dy, const float* h0,
-    const float* __restrict__ incl, const float* __restrict__ R, float* __restrict__ dx, float* __restrict__ ddl,
+    const float* __restrict__ incl, const float* __restrict__ R, float* dx, float* ddl,
     float* __restrict__ dA_part, float* __restrict__ dB_part, float* __restrict__ dC_part, int64_t L, int D,
-    int64_t nc) {
-  static_assert(N <= 4, "N = 8 takes s6_bwd_chunk_wide");
+    int64_t nc, int n0) {
+  static_assert(N <= 4 && NT % N == 0, "at most 4 states per pass");
   constexpr int S = BwdPiece<N>::S, NP = kHalf / S;
   constexpr int T1 = ilog2(2 * N), T3 = 6 - T1 - ilog2(S);
   __shared__ __attribute__((aligned(16))) float sB[N][kChunk];
@@ -296,7 +313,7 @@ __global__ __launch_bounds__(kBwdLanes) __attribute__((amdgpu_waves_per_eu(2))) 
   const int nt0 = nt < kHalf ? nt : kHalf, nt1 = nt > kHalf ? nt - kHalf : 0;
   for (int idx = lane; idx < N * kChunk; idx += kBwdLanes) {
     const int n = idx / kChunk, k = idx % kChunk;
-    const int64_t o = (b * N + n) * L + t0 + k;
+    const int64_t o = (b * NT + n0 + n) * L + t0 + k;
     sB[n][k] = k < nt ? Bm[o] : 0.f;
     sC[n][k] = k < nt ? Cm[o] : 0.f;
   }
@@ -310,16 +327,16 @@ __global__ __launch_bounds__(kBwdLanes) __attribute__((amdgpu_waves_per_eu(2))) 
     const int64_t rec = (b * nc + c) * D + d;
 #pragma unroll
     for (int n = 0; n < N; ++n) {
-      an[n] = valid ? A[(int64_t)d * N + n] : 0.f;
+      an[n] = valid ? A[(int64_t)d * NT + n0 + n] : 0.f;
       a2[n] = an[n] * kLog2e;
-      g[n] = valid ? R[rec * N + n] : 0.f;
+      g[n] = valid ? R[rec * NT + n0 + n] : 0.f;
       dA[n] = 0.f;
       if (!valid)
         h[n] = 0.f;
       else if (c == 0)
-        h[n] = h0 ? h0[((int64_t)b * D + d) * N + n] : 0.f;
+        h[n] = h0 ? h0[((int64_t)b * D + d) * NT + n0 + n] : 0.f;
       else
-        h[n] = incl[(rec - D) * N + n];   // chunk c - 1's end state
+        h[n] = incl[(rec - D) * NT + n0 + n];   // chunk c - 1's end state
     }
   }
   __syncthreads();   // B and C staged
@@ -329,7 +346,7 @@ __global__ __launch_bounds__(kBwdLanes) __attribute__((amdgpu_waves_per_eu(2))) 
   const unsigned ul = (unsigned)lane;
   const int vsum = (int)(ul >> (6 - T1)), isum = (int)((ul >> T3) & (S - 1));
   const bool writer = (ul & ((1u << T3) - 1)) == 0;
-  float* const part = (vsum < N ? dB_part : dC_part) + ((b * ncb + cb) * N + vsum % N) * L + t0;
+  float* const part = (vsum < N ? dB_part : dC_part) + ((b * ncb + cb) * NT + n0 + vsum % N) * L + t0;
 
   float ck0[NP][N];
   half_forward<N, S>(xr, dr, a2, sB, 0, h, ck0);   // h: the state after the first half
@@ -340,8 +357,8 @@ __global__ __launch_bounds__(kBwdLanes) __attribute__((amdgpu_waves_per_eu(2))) 
     half_forward<N, S>(xr, dr, a2, sB, kHalf, h, ck1);
     half_dy<VEC>(dy, wrow0, wrows, L, t0 + kHalf, nt1, sT, lane, sY);
     half_backward<N, S>(xr, dr, ck1, an, a2, g, dA, sB, sC, sY, kHalf, lane, part, writer, isum, nt1);
-    s6::rows_out<VEC, kHalf>(dx, wrow0, wrows, L, t0 + kHalf, nt1, sT, lane, xr);
-    s6::rows_out<VEC, kHalf>(ddl, wrow0, wrows, L, t0 + kHalf, nt1, sT, lane, dr);
+    half_out<VEC, ACC>(dx, wrow0, wrows, L, t0 + kHalf, nt1, sT, lane, xr);
+    half_out<VEC, ACC>(ddl, wrow0, wrows, L, t0 + kHalf, nt1, sT, lane, dr);
   }
   if (nt1 > 0) {
     s6::rows_in<VEC, kHalf>(x, wrow0, wrows, L, t0, nt0, sT, lane, xr);
@@ -349,214 +366,11 @@ __global__ __launch_bounds__(kBwdLanes) __attribute__((amdgpu_waves_per_eu(2))) 
   }
   half_dy<VEC>(dy, wrow0, wrows, L, t0, nt0, sT, lane, sY);
   half_backward<N, S>(xr, dr, ck0, an, a2, g, dA, sB, sC, sY, 0, lane, part, writer, isum, nt0);
-  s6::rows_out<VEC, kHalf>(dx, wrow0, wrows, L, t0, nt0, sT, lane, xr);
-  s6::rows_out<VEC, kHalf>(ddl, wrow0, wrows, L, t0, nt0, sT, lane, dr);
+  half_out<VEC, ACC>(dx, wrow0, wrows, L, t0, nt0, sT, lane, xr);
+  half_out<VEC, ACC>(ddl, wrow0, wrows, L, t0, nt0, sT, lane, dr);
   if (valid) {
 #pragma unroll
-    for (int n = 0; n < N; ++n) dA_part[((b * nc + c) * D + d) * N + n] = dA[n];
-  }
-}
-
-// 3'. The same for N = 8, where one half chunk's states and checkpoints do
-// not fit two waves per SIMD: per (batch row, chunk, 256 channels; four
-// waves), the whole chunk's x and delta in registers, dy in the wave's tile,
-// the pieces' dB and dC values summed over the 256 channels through LDS
-template <int N, bool VEC>
-__global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(1, 1))) void s6_bwd_chunk_wide(
-    const float* __restrict__ x, const float* __restrict__ dl, const float* __restrict__ A,
-    const float* __restrict__ Bm, const float* __restrict__ Cm, const float* __restrict__ dy, const float* h0,
-    const float* __restrict__ incl, const float* __restrict__ R, float* __restrict__ dx, float* __restrict__ ddl,
-    float* __restrict__ dA_part, float* __restrict__ dB_part, float* __restrict__ dC_part, int64_t L, int D,
-    int64_t nc) {
-  constexpr int S = BwdPiece<N>::S, NS = kChunk / S;
-  constexpr int NQ = 2 * S * N;                 // per-lane values of a piece's dB and dC parts
-  constexpr int TPQ = kLanes / NQ;              // threads summing one of them
-  static_assert(NQ <= kLanes && kLanes % NQ == 0, "piece sums split evenly");
-  __shared__ __attribute__((aligned(16))) float sB[N][kChunk];
-  __shared__ __attribute__((aligned(16))) float sC[N][kChunk];
-  __shared__ __attribute__((aligned(1024))) unsigned char sT[kLanes / 64][64 * 256];
-  // piece sums: lane l's value q at sR[q][l + 4 (l / SPAN)] (padded per
-  // thread span, so the span reads of 16 threads fall on distinct banks)
-  constexpr int SPAN = kLanes / TPQ;
-  __shared__ __attribute__((aligned(16))) float sR[NQ][kLanes + 4 * TPQ];
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
-  const int ncb = (D + kLanes - 1) / kLanes;
-  const int64_t c = blockIdx.y;
-  const int64_t b = blockIdx.x / ncb;
-  const int cb = (int)(blockIdx.x % ncb);
-  const int d = cb * kLanes + tid;
-  const bool valid = d < D;
-  const int64_t t0 = c * kChunk;
-  const int nt = L - t0 < kChunk ? (int)(L - t0) : kChunk;
-  for (int idx = tid; idx < N * kChunk; idx += kLanes) {
-    const int n = idx / kChunk, k = idx % kChunk;
-    const int64_t o = (b * N + n) * L + t0 + k;
-    sB[n][k] = k < nt ? Bm[o] : 0.f;
-    sC[n][k] = k < nt ? Cm[o] : 0.f;
-  }
-  const int64_t wrow0 = b * D + cb * kLanes + wave * 64;
-  const int wrows = D - (cb * kLanes + wave * 64);
-  // x and delta in registers; dy stays in the wave's tile (read per token)
-  float xr[kChunk], dr[kChunk];
-  s6::rows_in<VEC>(x, wrow0, wrows, L, t0, nt, sT[wave], lane, xr);
-  s6::rows_in<VEC>(dl, wrow0, wrows, L, t0, nt, sT[wave], lane, dr);
-  {
-    float gy[kChunk];
-    s6::rows_in<VEC>(dy, wrow0, wrows, L, t0, nt, sT[wave], lane, gy);
-    // the tile keeps dy, zeroed where rows_in masked it (rows past D, tokens
-    // past the sequence)
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
-#pragma unroll
-    for (int q = 0; q < kChunk / 4; ++q)
-      *reinterpret_cast<float4*>(sT[wave] + s6::tile_off((uint32_t)ln, (uint32_t)q)) =
-          make_float4(gy[4 * q], gy[4 * q + 1], gy[4 * q + 2], gy[4 * q + 3]);
-  }
-  const unsigned char* dyrow = sT[wave];
-  int lnd = lane;
-  asm volatile("" : "+v"(lnd));
-  float an[N], a2[N], h[N], g[N];
-  {
-    const int64_t rec = (b * nc + c) * D + d;
-#pragma unroll
-    for (int n = 0; n < N; ++n) {
-      an[n] = valid ? A[(int64_t)d * N + n] : 0.f;
-      a2[n] = an[n] * kLog2e;
-      g[n] = valid ? R[rec * N + n] : 0.f;
-      if (!valid)
-        h[n] = 0.f;
-      else if (c == 0)
-        h[n] = h0 ? h0[((int64_t)b * D + d) * N + n] : 0.f;
-      else
-        h[n] = incl[(rec - D) * N + n];   // chunk c - 1's end state
-    }
-  }
-  __syncthreads();   // B and C staged
-
-  // the states at the start of every piece
-  float ck[NS][N];
-#pragma unroll
-  for (int j = 0; j < NS; ++j) {
-#pragma unroll
-    for (int n = 0; n < N; ++n) ck[j][n] = h[n];
-#pragma unroll
-    for (int i = 0; i < S; ++i) {
-      const int t = S * j + i;
-      const float u = dr[t] * xr[t];
-#pragma unroll
-      for (int n = 0; n < N; ++n) h[n] = fmaf(exp2_hw(dr[t] * a2[n]), h[n], u * sB[n][t]);
-    }
-  }
-  float dA[N];
-#pragma unroll
-  for (int n = 0; n < N; ++n) dA[n] = 0.f;
-  const int q0 = tid / TPQ, qp = tid % TPQ;   // this thread's piece sum and its share of the lanes
-  // The pieces, last first, as a loop that is not unrolled (unrolled, the
-  // compiler interleaves the pieces and keeps far more live than one piece
-  // needs): the current piece always sits in the last S entries of xr, dr
-  // and in the last checkpoint; after it, its outputs (dx, ddelta) take its
-  // place and the arrays rotate right by one piece, so after NS pieces every
-  // output is back at its token's position.
-#pragma unroll 1
-  for (int m = 0; m < NS; ++m) {
-    const int j = NS - 1 - m;   // the piece's position in the chunk
-    constexpr int P0 = kChunk - S;
-    // the piece's entering states and decays, recomputed
-    float hp[S][N], av[S][N];
-#pragma unroll
-    for (int n = 0; n < N; ++n) h[n] = ck[NS - 1][n];
-#pragma unroll
-    for (int i = 0; i < S; ++i) {
-      const int t = S * j + i;
-      const float u = dr[P0 + i] * xr[P0 + i];
-#pragma unroll
-      for (int n = 0; n < N; ++n) {
-        hp[i][n] = h[n];
-        av[i][n] = exp2_hw(dr[P0 + i] * a2[n]);
-        h[n] = fmaf(av[i][n], h[n], u * sB[n][t]);
-      }
-    }
-    // the backward steps, last token first; each step's per-lane parts of
-    // dB (g_t delta_t x_t) and dC (dy_t h_t) go to LDS at once: value
-    // q = (i N + n) of dB, S N + (i N + n) of dC
-    __syncthreads();   // the previous piece's sums are read out
-    const int wl = tid + 4 * (tid / SPAN);
-#pragma unroll
-    for (int i = S - 1; i >= 0; --i) {
-      const int t = S * j + i;
-      const float gyt = *reinterpret_cast<const float*>(dyrow + s6::tile_off((uint32_t)lnd, (uint32_t)(t / 4)) + (t % 4) * 4);
-      const float dxt = dr[P0 + i] * xr[P0 + i];
-      float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-      for (int n = 0; n < N; ++n) {
-        const float gn = fmaf(sC[n][t], gyt, g[n]);     // dL/dh_t
-        const float ah = av[i][n] * hp[i][n];
-        const float bnt = sB[n][t];
-        sR[S * N + i * N + n][wl] = gyt * fmaf(dxt, bnt, ah);   // dy_t h_t
-        s1 = fmaf(gn, bnt, s1);
-        const float ga = gn * ah;
-        s2 = fmaf(ga, an[n], s2);
-        dA[n] = fmaf(dr[P0 + i], ga, dA[n]);
-        sR[i * N + n][wl] = gn * dxt;                    // g_t delta_t x_t
-        g[n] = av[i][n] * gn;                            // dL/dh_{t-1} from step t
-      }
-      const float xt = xr[P0 + i];
-      xr[P0 + i] = dr[P0 + i] * s1;   // dx_t
-      dr[P0 + i] = fmaf(xt, s1, s2);  // ddelta_t
-    }
-    // rotate: the outputs to the front, the next piece to the back
-    {
-      float tx[S], td[S];
-#pragma unroll
-      for (int i = 0; i < S; ++i) {
-        tx[i] = xr[P0 + i];
-        td[i] = dr[P0 + i];
-      }
-#pragma unroll
-      for (int k = kChunk - 1; k >= S; --k) {
-        xr[k] = xr[k - S];
-        dr[k] = dr[k - S];
-      }
-#pragma unroll
-      for (int i = 0; i < S; ++i) {
-        xr[i] = tx[i];
-        dr[i] = td[i];
-      }
-#pragma unroll
-      for (int q = NS - 1; q >= 1; --q)
-#pragma unroll
-        for (int n = 0; n < N; ++n) ck[q][n] = ck[q - 1][n];
-    }
-    // the piece's dB and dC parts summed over the workgroup's channels: TPQ
-    // threads sum one value over kLanes / TPQ lanes each, then combine by
-    // shuffles
-    __syncthreads();
-    {
-      float acc = 0.f;
-      const float* src = &sR[q0][qp * (SPAN + 4)];
-#pragma unroll
-      for (int l = 0; l < SPAN; l += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(src + l);
-        acc += (v.x + v.y) + (v.z + v.w);
-      }
-#pragma unroll
-      for (int off = 1; off < TPQ; off *= 2) acc += __shfl_xor(acc, off);
-      if (qp == 0) {
-        const int which = q0 / (S * N), rem = q0 % (S * N), i = rem / N, n = rem % N;
-        const int t = S * j + i;
-        if (t < nt) {
-          float* part = which == 0 ? dB_part : dC_part;
-          part[((b * ncb + cb) * N + n) * L + t0 + t] = acc;
-        }
-      }
-    }
-  }
-  // dx and ddelta out as whole rows; the chunk's dA part
-  s6::rows_out<VEC>(dx, wrow0, wrows, L, t0, nt, sT[wave], lane, xr);
-  s6::rows_out<VEC>(ddl, wrow0, wrows, L, t0, nt, sT[wave], lane, dr);
-  if (valid) {
-#pragma unroll
-    for (int n = 0; n < N; ++n) dA_part[((b * nc + c) * D + d) * N + n] = dA[n];
+    for (int n = 0; n < N; ++n) dA_part[((b * nc + c) * D + d) * NT + n0 + n] = dA[n];
   }
 }
 
@@ -644,12 +458,12 @@ unsigned grid_of(int64_t n) {
 template <int N>
 hipError_t launch_bwd_n(const S6BwdProblem& p, hipStream_t s) {
   const int64_t nc = (p.L + kChunk - 1) / kChunk;
-  const int64_t ncb = (p.D + kLanes - 1) / kLanes, ncb1 = (p.D + kBwdLanes - 1) / kBwdLanes;
+  const int64_t ncb = (p.D + kBwdLanes - 1) / kBwdLanes;
   const int vec = (p.L % 4 == 0 && p.L <= ((int64_t)1 << 22) && (reinterpret_cast<uintptr_t>(p.x) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(p.delta) & 15) == 0 && (reinterpret_cast<uintptr_t>(p.dy) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(p.dx) & 15) == 0 && (reinterpret_cast<uintptr_t>(p.ddelta) & 15) == 0)
                       ? 1 : 0;
-  const dim3 grid((unsigned)(p.bt * ncb), (unsigned)nc), grid1((unsigned)(p.bt * ncb1), (unsigned)nc);
+  const dim3 grid((unsigned)(p.bt * ncb), (unsigned)nc);
   if (p.bt == 0 || nc == 0) {
     // no token: dA is zero, dh0 the upstream dhT (or zero); nothing else
     hipLaunchKernelGGL(s6_bwd_reduce_dA, dim3(dA_grid(p.D * N)), dim3(64 * kRedWaves), 0, s, p.dA_part, p.dA, (int64_t)0,
@@ -664,25 +478,29 @@ hipError_t launch_bwd_n(const S6BwdProblem& p, hipStream_t s) {
                      p.dh0, p.bt, (int)p.D, nc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (N <= 4) {
-    if (vec)
-      hipLaunchKernelGGL((s6_bwd_chunk<N, true>), grid1, dim3(kBwdLanes), 0, s, p.x, p.delta, p.A, p.B, p.C, p.dy,
-                         p.h0, p.incl, p.R, p.dx, p.ddelta, p.dA_part, p.dB_part, p.dC_part, p.L, (int)p.D, nc);
-    else
-      hipLaunchKernelGGL((s6_bwd_chunk<N, false>), grid1, dim3(kBwdLanes), 0, s, p.x, p.delta, p.A, p.B, p.C, p.dy,
-                         p.h0, p.incl, p.R, p.dx, p.ddelta, p.dA_part, p.dB_part, p.dC_part, p.L, (int)p.D, nc);
-  } else {
-    if (vec)
-      hipLaunchKernelGGL((s6_bwd_chunk_wide<N, true>), grid, dim3(kLanes), 0, s, p.x, p.delta, p.A, p.B, p.C, p.dy,
-                         p.h0, p.incl, p.R, p.dx, p.ddelta, p.dA_part, p.dB_part, p.dC_part, p.L, (int)p.D, nc);
-    else
-      hipLaunchKernelGGL((s6_bwd_chunk_wide<N, false>), grid, dim3(kLanes), 0, s, p.x, p.delta, p.A, p.B, p.C, p.dy,
-                         p.h0, p.incl, p.R, p.dx, p.ddelta, p.dA_part, p.dB_part, p.dC_part, p.L, (int)p.D, nc);
+  // one pass per group of (up to) 4 states; passes after the first add to dx, ddelta
+  constexpr int NG = N < 4 ? N : 4;
+  for (int n0 = 0; n0 < N; n0 += NG) {
+    const auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, grid, dim3(kBwdLanes), 0, s, p.x, p.delta, p.A, p.B, p.C, p.dy, p.h0, p.incl, p.R,
+                         p.dx, p.ddelta, p.dA_part, p.dB_part, p.dC_part, p.L, (int)p.D, nc, n0);
+    };
+    if (n0 == 0) {
+      if (vec)
+        go(s6_bwd_chunk<NG, N, true, false>);
+      else
+        go(s6_bwd_chunk<NG, N, false, false>);
+    } else if constexpr (N > NG) {
+      if (vec)
+        go(s6_bwd_chunk<NG, N, true, true>);
+      else
+        go(s6_bwd_chunk<NG, N, false, true>);
+    }
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(s6_bwd_reduce_dA, dim3(dA_grid(p.D * N)), dim3(64 * kRedWaves), 0, s, p.dA_part, p.dA, p.bt * nc, p.D * N);
-  const int ncbp = (int)(N <= 4 ? ncb1 : ncb);
+  const int ncbp = (int)ncb;
   if ((N * p.L) % 4 == 0 && (reinterpret_cast<uintptr_t>(p.dB) & 15) == 0 && (reinterpret_cast<uintptr_t>(p.dC) & 15) == 0)
     hipLaunchKernelGGL(s6_bwd_reduce_bc<true>, dim3(grid_of(p.bt * N * p.L / 4)), dim3(256), 0, s, p.dB_part,
                        p.dC_part, p.dB, p.dC, p.bt, ncbp, (int64_t)N * p.L);
@@ -694,7 +512,7 @@ hipError_t launch_bwd_n(const S6BwdProblem& p, hipStream_t s) {
 
 }  // namespace
 
-bool s6_bwd_has(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8; }
+bool s6_bwd_has(int64_t N) { return N == 1 || N == 2 || N == 4 || N == 8 || N == 16; }
 int64_t s6_bwd_channel_block() { return kBwdLanes; }
 
 hipError_t launch_s6_bwd(const S6BwdProblem& p, hipStream_t s) {
@@ -703,6 +521,7 @@ hipError_t launch_s6_bwd(const S6BwdProblem& p, hipStream_t s) {
     case 2: return launch_bwd_n<2>(p, s);
     case 4: return launch_bwd_n<4>(p, s);
     case 8: return launch_bwd_n<8>(p, s);
+    case 16: return launch_bwd_n<16>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

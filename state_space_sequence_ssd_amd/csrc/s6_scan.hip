@@ -453,14 +453,10 @@ hipError_t launch_n(const S6Problem& p, hipStream_t s) {
                        p.hT, p.aggS, p.aggD, p.incl, p.sync, p.dy, p.O, p.SD, p.L, (int)p.D, nc, ntickets);
   };
   if (p.dy) {
-    if constexpr (N <= 8) {
-      if (vec)
-        go(s6_onepass<N, true, true>, onepass_slots<N, true, true>());
-      else
-        go(s6_onepass<N, false, true>, onepass_slots<N, false, true>());
-    } else {
-      return hipErrorInvalidValue;   // no backward pass for this N
-    }
+    if (vec)
+      go(s6_onepass<N, true, true>, onepass_slots<N, true, true>());
+    else
+      go(s6_onepass<N, false, true>, onepass_slots<N, false, true>());
   } else if (vec) {
     go(s6_onepass<N, true, false>, onepass_slots<N, true, false>());
   } else {

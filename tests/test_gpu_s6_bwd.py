@@ -30,7 +30,9 @@ CASES = {
     "page-small": s6_config_by_name("s6-page").with_shape(batch=2, seqlen=256, channels=96),
     "n1": SMALL.with_shape(dstate=1, seqlen=129, channels=64),
     "n2": SMALL.with_shape(dstate=2, seqlen=64, channels=300),
-    "n8": SMALL.with_shape(dstate=8, seqlen=517, channels=257, h0_sigma=None),
+    "n8": SMALL.with_shape(dstate=8, seqlen=517, channels=257, h0_sigma=None),   # two passes of 4 states
+    "n16": SMALL.with_shape(dstate=16, seqlen=300, channels=130),                 # four passes
+    "n16-scalar": SMALL.with_shape(dstate=16, seqlen=171, channels=70),
     "one-token": SMALL.with_shape(seqlen=1),
     "vec-path": SMALL.with_shape(seqlen=4 * 97, channels=256),                 # 16-byte rows, ragged chunk
     "two-blocks": SMALL.with_shape(batch=3, seqlen=200, channels=600),
@@ -114,6 +116,15 @@ def test_s6_bwd_is_deterministic():
     g1, g2 = _run(inp, dy, dhT), _run(inp, dy, dhT)
     for k in ssd.S6_GRAD_NAMES:
         assert np.array_equal(host(g1[k]), host(g2[k])), k
+
+
+def test_s6_bwd_mamba1_130m_every_gradient():
+    # a Mamba-1 130M-like layer (dstate 16, 1536 channels, batch 8, 2048
+    # tokens) against the oracle on every element of every gradient
+    cfg = s6_config_by_name("s6-mamba1-130m")
+    inp = generate_s6(cfg)
+    dy, dhT = _upstream(cfg, 12)
+    log("  " + _check(_run(inp, dy, dhT), _ref(inp, dy, dhT), "130m-like"))
 
 
 def test_s6_bwd_page_size_every_gradient():
