@@ -43,7 +43,7 @@ int s6_sizes(const mamba1_s6_dims* d, S6Sizes* s) {
   if (!mul_ok(bd, d->dstate, &r.n_state)) return MAMBA2_SSD_ERR_BAD_DIM;
   int64_t ns, nsum;
   if (!mul_ok(r.n_state, r.nc, &ns) || !mul_ok(bd, r.nc, &nsum) || !mul_ok(ns, 8, &t)) return MAMBA2_SSD_ERR_BAD_DIM;
-  const int64_t nsync = ssd::s6_sync_words(d->batch, d->channels, d->seqlen);
+  const int64_t nsync = ssd::s6_sync_words(d->batch, d->channels, d->seqlen, d->dstate);
   r.off_sumd = align_up((size_t)ns * 4);
   r.off_incl = r.off_sumd + align_up((size_t)nsum * 4);
   r.off_sync = r.off_incl + align_up((size_t)ns * 4);

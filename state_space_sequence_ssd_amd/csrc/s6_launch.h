@@ -60,7 +60,7 @@ int64_t s6_chunk_tokens();      // tokens per chunk of the parallel scan
 int64_t s6_bwd_channel_block();   // channels per block of the backward's dB, dC partial sums
 bool s6_bwd_has(int64_t N);
 hipError_t launch_s6_bwd(const S6BwdProblem& p, hipStream_t stream);
-int64_t s6_sync_words(int64_t bt, int64_t D, int64_t L);
+int64_t s6_sync_words(int64_t bt, int64_t D, int64_t L, int64_t N);
 bool s6_has(int64_t N);
 hipError_t launch_s6(const S6Problem& p, hipStream_t stream);
 

@@ -39,7 +39,12 @@ namespace ssd {
 namespace {
 
 constexpr int kChunk = 64;    // tokens per chunk
-constexpr int kLanes = 256;   // channels per workgroup (4 waves)
+constexpr int kLanes = 256;   // threads per workgroup (4 waves)
+
+// Lanes per channel: dstate 16 splits each channel's states over a lane
+// pair (8 each), which keeps two waves per SIMD; the pair's partial outputs
+// are added by one DPP step. Channels per workgroup: kLanes / NL.
+template <int N> struct Lanes { static constexpr int NL = N >= 16 ? 2 : 1, NS = N / NL, CB = kLanes / NL; };
 constexpr int kSyncWords = 64;   // sync region head: ticket counter (0-1), error word (2)
 constexpr int kMaxPolls = 1 << 20;
 
@@ -113,7 +118,7 @@ __global__ void s6_pass_state(const float* h0, float* hT, int64_t n) {
 // sum_t (a_t0 ... a_t) C_t dy_t per state, and the chunk's sum of delta SD
 // (so the backward pass needs no reverse sweep of its own per chunk).
 template <int N, bool VEC, bool BWD>
-__global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 ? 1 : 2))) void s6_onepass(const float* __restrict__ x, const float* __restrict__ dl,
+__global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(2))) void s6_onepass(const float* __restrict__ x, const float* __restrict__ dl,
                                                      const float* __restrict__ A, const float* __restrict__ Bm,
                                                      const float* __restrict__ Cm, const float* h0, float* y,
                                                      float* hT, float* aggS, float* aggD, float* incl, int* sync,
@@ -124,12 +129,14 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
   __shared__ __attribute__((aligned(16))) float sC[N][kChunk];
   __shared__ __attribute__((aligned(1024))) unsigned char sT[kLanes / 64][64 * 256];   // per wave: x, delta, then y
   __shared__ int64_t sTicket;
+  constexpr int NL = Lanes<N>::NL, NS = Lanes<N>::NS, CB = Lanes<N>::CB, RW = 64 / NL;   // RW: rows per wave
   const int tid = threadIdx.x;
+  const int sub = tid % NL;   // the lane's states: sub NS .. sub NS + NS - 1
   // (the wave index read back as uniform: the tile addresses it forms stay in
   // scalar registers)
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   unsigned char* const tile = sT[wave];
-  const int ncb = (D + kLanes - 1) / kLanes;
+  const int ncb = (D + CB - 1) / CB;
   const int64_t per = ntickets / nc;   // tickets per chunk = batch rows * channel blocks
   int* const flags = sync + kSyncWords;
 
@@ -142,7 +149,7 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
     const int64_t u = ticket % per;
     const int64_t b = u / ncb;
     const int cb = (int)(u % ncb);
-    const int d = cb * kLanes + tid;
+    const int d = cb * CB + tid / NL;
     const bool valid = d < D;
     const int64_t t0 = c * kChunk;
     const int nt = L - t0 < kChunk ? (int)(L - t0) : kChunk;
@@ -155,8 +162,8 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
     }
     // the lane's x and delta (zeros past the sequence or the channels)
     float xr[kChunk], dr[kChunk];
-    const int64_t wrow0 = b * D + cb * kLanes + wave * 64;   // the wave's first row
-    const int wrows = D - (cb * kLanes + wave * 64);          // its rows inside the array (may be <= 0)
+    const int64_t wrow0 = b * D + cb * CB + wave * RW;   // the wave's first row
+    const int wrows = D - (cb * CB + wave * RW);          // its rows inside the array (may be <= 0)
     {
       // whole rows through the wave's tile: x, then delta (the tile is the
       // wave's own, so no workgroup barrier; a direct load has landed in LDS
@@ -166,12 +173,12 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         if constexpr (VEC) {
-          if (wrows > 0) s6::tile_load(srcs[a], wrow0, wrows < 64 ? wrows : 64, L, t0, tile, lane);
+          if (wrows > 0) s6::tile_load(srcs[a], wrow0, wrows < RW ? wrows : RW, L, t0, tile, lane);
         } else {
-          s6::tile_load_scalar(srcs[a], wrow0, wrows, L, t0, nt, tile, lane);
+          s6::tile_load_scalar(srcs[a], wrow0, wrows < RW ? wrows : RW, L, t0, nt, tile, lane);
         }
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-        int ln = lane;
+        int ln = lane / NL;   // the lane's channel row (a lane pair reads the same row)
         asm volatile("" : "+v"(ln));
 #pragma unroll
         for (int q = 0; q < kChunk / 4; ++q) {
@@ -191,28 +198,28 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
       // dy stays in the tile, read 4 tokens at a time by its lane (past the
       // sequence it holds the next row's tokens, which meet C = 0 there)
       if constexpr (VEC) {
-        if (wrows > 0) s6::tile_load(dy, wrow0, wrows < 64 ? wrows : 64, L, t0, tile, lane);
+        if (wrows > 0) s6::tile_load(dy, wrow0, wrows < RW ? wrows : RW, L, t0, tile, lane);
       } else {
-        s6::tile_load_scalar(dy, wrow0, wrows, L, t0, nt, tile, lane);
+        s6::tile_load_scalar(dy, wrow0, wrows < RW ? wrows : RW, L, t0, nt, tile, lane);
       }
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     }
-    float a2[N];
+    float a2[NS];
 #pragma unroll
-    for (int n = 0; n < N; ++n) a2[n] = valid ? A[(int64_t)d * N + n] * kLog2e : 0.f;
+    for (int n = 0; n < NS; ++n) a2[n] = valid ? A[(int64_t)d * N + sub * NS + n] * kLog2e : 0.f;
     __syncthreads();   // B and C staged
 
     // 1. the chunk from a zero state. Past the sequence x, delta, B and C are
     // zero, so padded tokens leave h unchanged (exp2(0) = 1, no input).
-    float h[N], pa[N], oa[N];   // (BWD: the running decay product and O)
+    float h[NS], pa[NS], oa[NS];   // (BWD: the running decay product and O)
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
+    for (int n = 0; n < NS; ++n) {
       h[n] = 0.f;
       pa[n] = 1.f;
       oa[n] = 0.f;
     }
     float dsum = 0.f;
-    int lnb = lane;
+    int lnb = lane / NL;
     asm volatile("" : "+v"(lnb));
 #pragma unroll
     for (int t4 = 0; t4 < kChunk; t4 += 4) {
@@ -231,11 +238,11 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
         gj[3] = g4.w;
       }
 #pragma unroll
-      for (int n = 0; n < N; ++n) {
-        const float4 b4 = *reinterpret_cast<const float4*>(&sB[n][t4]);
+      for (int n = 0; n < NS; ++n) {
+        const float4 b4 = *reinterpret_cast<const float4*>(&sB[sub * NS + n][t4]);
         const float bj[4] = {b4.x, b4.y, b4.z, b4.w};
         if constexpr (BWD) {
-          const float4 c4 = *reinterpret_cast<const float4*>(&sC[n][t4]);
+          const float4 c4 = *reinterpret_cast<const float4*>(&sC[sub * NS + n][t4]);
           const float cj[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -254,33 +261,34 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
     if constexpr (BWD) {
       // (through resources over the block's valid records: no branch, which
       // the compiler would otherwise sink the O chain into)
-      const int64_t rec0 = (b * nc + c) * D + cb * kLanes;
-      const uint32_t nrec = (uint32_t)(D - cb * kLanes < kLanes ? D - cb * kLanes : kLanes);
-      st_state<N>(lookback::urs(Oc + rec0 * N, nrec * N * 4), (uint32_t)tid * N * 4, oa);
-      st_state<1>(lookback::urs(SD + rec0, nrec * 4), (uint32_t)tid * 4, &dsum);
+      const int64_t rec0 = (b * nc + c) * D + cb * CB;
+      const uint32_t nrec = (uint32_t)(D - cb * CB < CB ? D - cb * CB : CB);
+      st_state<NS>(lookback::urs(Oc + rec0 * N, nrec * N * 4), (uint32_t)tid * NS * 4, oa);
+      st_state<1>(lookback::urs(SD + rec0, nrec * 4), (uint32_t)(tid / NL) * 4, &dsum);
     }
     int* const myflag = flags + (b * nc + c) * ncb + cb;
 
     // 2. the entering state
-    float hin[N];
+    float hin[NS];
     if (c == 0) {
 #pragma unroll
-      for (int n = 0; n < N; ++n) hin[n] = (h0 && valid) ? h0[(b * D + d) * N + n] : 0.f;
+      for (int n = 0; n < NS; ++n) hin[n] = (h0 && valid) ? h0[(b * D + d) * N + sub * NS + n] : 0.f;
     } else {
       {
-        // the workgroup's 256 records (those of channels past D are dropped)
-        const int64_t rec0 = (b * nc + c) * D + cb * kLanes;
-        const uint32_t nrec = (uint32_t)(D - cb * kLanes < kLanes ? D - cb * kLanes : kLanes);
-        st_state<N>(lookback::urs(aggS + rec0 * N, nrec * N * 4), (uint32_t)tid * N * 4, h);
-        st_state<1>(lookback::urs(aggD + rec0, nrec * 4), (uint32_t)tid * 4, &dsum);
+        // the workgroup's CB records (those of channels past D are dropped;
+        // a lane pair's two lanes write the same delta sum)
+        const int64_t rec0 = (b * nc + c) * D + cb * CB;
+        const uint32_t nrec = (uint32_t)(D - cb * CB < CB ? D - cb * CB : CB);
+        st_state<NS>(lookback::urs(aggS + rec0 * N, nrec * N * 4), (uint32_t)tid * NS * 4, h);
+        st_state<1>(lookback::urs(aggD + rec0, nrec * 4), (uint32_t)(tid / NL) * 4, &dsum);
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();   // every lane's aggregate is out
       if (tid == 0) __hip_atomic_store(myflag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // hin = acc + lam * (inclusive state of the chunk where the walk ends)
-      float acc[N], lam[N];
+      float acc[NS], lam[NS];
 #pragma unroll
-      for (int n = 0; n < N; ++n) {
+      for (int n = 0; n < NS; ++n) {
         acc[n] = 0.f;
         lam[n] = 1.f;
       }
@@ -291,21 +299,21 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
         const int* fj = flags + (b * nc + j) * ncb + cb;
         const int want = j == 0 ? 2 : 1;
         const int f = fseen >= want ? fseen : wait_flag(fj, want, sync);
-        const int64_t rj = (b * nc + j) * D + cb * kLanes;   // chunk j's records of this block
-        const uint32_t nrec = (uint32_t)(D - cb * kLanes < kLanes ? D - cb * kLanes : kLanes);
+        const int64_t rj = (b * nc + j) * D + cb * CB;   // chunk j's records of this block
+        const uint32_t nrec = (uint32_t)(D - cb * CB < CB ? D - cb * CB : CB);
         if (f >= 2 || j == 0) {   // (at chunk 0 only after a wait that hit its bound is f < 2)
-          float pj[N];
-          ld_state<N>(lookback::urs(incl + rj * N, nrec * N * 4), (uint32_t)tid * N * 4, pj);
+          float pj[NS];
+          ld_state<NS>(lookback::urs(incl + rj * N, nrec * N * 4), (uint32_t)tid * NS * 4, pj);
 #pragma unroll
-          for (int n = 0; n < N; ++n) hin[n] = valid ? fmaf(lam[n], pj[n], acc[n]) : 0.f;
+          for (int n = 0; n < NS; ++n) hin[n] = valid ? fmaf(lam[n], pj[n], acc[n]) : 0.f;
           break;
         }
-        float sj[N], sd;
-        ld_state<N>(lookback::urs(aggS + rj * N, nrec * N * 4), (uint32_t)tid * N * 4, sj);
-        ld_state<1>(lookback::urs(aggD + rj, nrec * 4), (uint32_t)tid * 4, &sd);
+        float sj[NS], sd;
+        ld_state<NS>(lookback::urs(aggS + rj * N, nrec * N * 4), (uint32_t)tid * NS * 4, sj);
+        ld_state<1>(lookback::urs(aggD + rj, nrec * 4), (uint32_t)(tid / NL) * 4, &sd);
         fseen = flag_of(fj - ncb);   // chunk j - 1 (j >= 1 here)
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
+        for (int n = 0; n < NS; ++n) {
           acc[n] = fmaf(lam[n], sj[n], acc[n]);
           lam[n] *= exp2_hw(a2[n] * sd);
         }
@@ -314,16 +322,16 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
     // 3. the inclusive end state, published; hT after the last chunk
     {
       const bool last = c + 1 == nc;
-      float hout[N];
+      float hout[NS];
 #pragma unroll
-      for (int n = 0; n < N; ++n) hout[n] = fmaf(exp2_hw(a2[n] * dsum), hin[n], h[n]);
+      for (int n = 0; n < NS; ++n) hout[n] = fmaf(exp2_hw(a2[n] * dsum), hin[n], h[n]);
       if (!last) {
-        const int64_t rec0 = (b * nc + c) * D + cb * kLanes;
-        const uint32_t nrec = (uint32_t)(D - cb * kLanes < kLanes ? D - cb * kLanes : kLanes);
-        st_state<N>(lookback::urs(incl + rec0 * N, nrec * N * 4), (uint32_t)tid * N * 4, hout);
+        const int64_t rec0 = (b * nc + c) * D + cb * CB;
+        const uint32_t nrec = (uint32_t)(D - cb * CB < CB ? D - cb * CB : CB);
+        st_state<NS>(lookback::urs(incl + rec0 * N, nrec * N * 4), (uint32_t)tid * NS * 4, hout);
       } else if (hT && valid) {
 #pragma unroll
-        for (int n = 0; n < N; ++n) hT[(b * D + d) * N + n] = hout[n];
+        for (int n = 0; n < NS; ++n) hT[(b * D + d) * N + sub * NS + n] = hout[n];
       }
       if (!last) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -341,7 +349,7 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
 #pragma unroll
     for (int t = 0; t < kChunk; ++t) asm volatile("" : "+v"(dr[t]));
 #pragma unroll
-    for (int n = 0; n < N; ++n) {
+    for (int n = 0; n < NS; ++n) {
       asm volatile("" : "+v"(a2[n]));
       h[n] = hin[n];
     }
@@ -351,9 +359,9 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
 #pragma unroll
       for (int j = 0; j < 4; ++j) u[j] = dr[t4 + j] * xr[t4 + j];
 #pragma unroll
-      for (int n = 0; n < N; ++n) {
-        const float4 b4 = *reinterpret_cast<const float4*>(&sB[n][t4]);
-        const float4 c4 = *reinterpret_cast<const float4*>(&sC[n][t4]);
+      for (int n = 0; n < NS; ++n) {
+        const float4 b4 = *reinterpret_cast<const float4*>(&sB[sub * NS + n][t4]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&sC[sub * NS + n][t4]);
         const float bj[4] = {b4.x, b4.y, b4.z, b4.w}, cj[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -361,31 +369,41 @@ __global__ __launch_bounds__(kLanes) __attribute__((amdgpu_waves_per_eu(N >= 16 
           yv[j] = fmaf(cj[j], h[n], yv[j]);
         }
       }
+      if constexpr (NL == 2) {
+        // the pair's partial sums over their states: each lane adds its
+        // partner's (lanes 2i, 2i + 1; DPP quad permutation 1, 0, 3, 2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          yv[j] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(yv[j]), 0xB1, 0xF, 0xF, false));
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) xr[t4 + j] = yv[j];
       __builtin_amdgcn_sched_barrier(0);
     }
     {
-      // through the tile: each lane writes its row, then whole rows go out
+      // through the tile: each lane writes its row (a lane pair its two
+      // halves), then whole rows go out
       int ln = lane;
       asm volatile("" : "+v"(ln));
+      const uint32_t row = (uint32_t)(ln / NL);
 #pragma unroll
       for (int q = 0; q < kChunk / 4; ++q)
-        *reinterpret_cast<float4*>(tile + s6::tile_off((uint32_t)ln, (uint32_t)q)) =
-            make_float4(xr[4 * q], xr[4 * q + 1], xr[4 * q + 2], xr[4 * q + 3]);
+        if (NL == 1 || q / (kChunk / 4 / NL) == sub)
+          *reinterpret_cast<float4*>(tile + s6::tile_off(row, (uint32_t)q)) =
+              make_float4(xr[4 * q], xr[4 * q + 1], xr[4 * q + 2], xr[4 * q + 3]);
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       if (!VEC) {
         // lane l stores token t0 + l of each row
 #pragma unroll 8
-        for (int r = 0; r < 64; ++r) {
+        for (int r = 0; r < RW; ++r) {
           const float v = *reinterpret_cast<const float*>(tile + s6::tile_off((uint32_t)r, (uint32_t)ln >> 2) + (ln & 3) * 4);
           if (r < wrows && ln < nt) y[(wrow0 + r) * L + t0 + ln] = v;
         }
       } else if (wrows > 0) {
         const __amdgpu_buffer_rsrc_t ry =
-            lookback::urs(y + wrow0 * L, (uint32_t)((int64_t)(wrows < 64 ? wrows : 64) * L * 4));
+            lookback::urs(y + wrow0 * L, (uint32_t)((int64_t)(wrows < RW ? wrows : RW) * L * 4));
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < RW / 4; ++i) {
           const uint32_t r = (uint32_t)(4 * i + (ln >> 4)), q = (uint32_t)(ln & 15) ^ (r & 15);
           const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * 256 + ((uint32_t)(ln & 15) << 4));
           if ((int)(4 * q) < nt) __builtin_amdgcn_raw_buffer_store_b128(v, ry, (r * (uint32_t)L + (uint32_t)t0 + 4 * q) * 4, 0, 0);
@@ -442,7 +460,7 @@ hipError_t launch_n(const S6Problem& p, hipStream_t s) {
                    (reinterpret_cast<uintptr_t>(p.delta) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(p.y) & 15) == 0 && (reinterpret_cast<uintptr_t>(p.dy) & 15) == 0)
                       ? 1 : 0;
-  const int64_t ncb = (p.D + kLanes - 1) / kLanes;
+  const int64_t ncb = (p.D + Lanes<N>::CB - 1) / Lanes<N>::CB;
   const int64_t ntickets = nc * p.bt * ncb;
   const int64_t words = kSyncWords + ntickets;
   const int64_t cblocks = (words + 255) / 256 < 1024 ? (words + 255) / 256 : 1024;
@@ -467,9 +485,10 @@ hipError_t launch_n(const S6Problem& p, hipStream_t s) {
 
 }  // namespace
 
-int64_t s6_sync_words(int64_t bt, int64_t D, int64_t L) {
+int64_t s6_sync_words(int64_t bt, int64_t D, int64_t L, int64_t N) {
   const int64_t nc = (L + kChunk - 1) / kChunk;
-  return kSyncWords + nc * bt * ((D + kLanes - 1) / kLanes);
+  const int64_t cbk = N >= 16 ? Lanes<16>::CB : kLanes;   // channels per workgroup
+  return kSyncWords + nc * bt * ((D + cbk - 1) / cbk);
 }
 
 int64_t s6_chunk_tokens() { return kChunk; }

@@ -30,6 +30,7 @@ CASES = {
     "n16": s6_config_by_name("s6-mamba1-130m").with_shape(batch=1, seqlen=333, channels=130),
     "one-token": SMALL.with_shape(seqlen=1),
     "vec-path": SMALL.with_shape(seqlen=4 * 97, channels=256, dstate=16),
+    "n16-scalar": SMALL.with_shape(dstate=16, batch=3, seqlen=171, channels=70),   # lane pairs, 4-byte rows
 }
 
 
@@ -112,3 +113,13 @@ def test_s6_page_shape_sampled_channels():
     ds = np.array([0, 1, 255, 256, 511, 700, 1023])
     yr, hr = s6_sequential(inp["x"][:, ds], inp["delta"][:, ds], inp["A"][ds], inp["B"], inp["C"], None)
     log(f"  y {_close(y[:, ds], yr, 'y'):.1e}, hT {_close(hT[:, ds], hr, 'hT'):.1e}")
+
+
+def test_s6_mamba1_130m_every_element():
+    # the Mamba-1 130M-like layer (dstate 16: each channel's states on a lane
+    # pair) against the oracle on every element of y and hT
+    cfg = s6_config_by_name("s6-mamba1-130m")
+    inp = generate_s6(cfg)
+    y, hT = _run(_dev(inp))
+    yr, hr = s6_sequential(inp["x"], inp["delta"], inp["A"], inp["B"], inp["C"], inp["h0"])
+    log(f"  y {_close(y, yr, 'y'):.1e}, hT {_close(hT, hr, 'hT'):.1e}")
