@@ -468,6 +468,262 @@ hipError_t launch_fused(const Problem& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// ssd_chunk_state_pass_rows: the same outputs as ssd_chunk_state_pass above,
+// for bf16 io with dstate 128 or 256, any supported headdim and chunk. A
+// workgroup owns one (batch, head, 128-column dstate slice); its
+// P/16 waves each own 16 headdim rows and walk the chunks together, all of
+// them reading the same x and B tiles from one LDS ring. For each chunk k a
+// wave computes
+//   hprev[k] = h   (bf16 (hi, lo) pairs, the state pass's format),
+//   S_k^T    = B_k^T (w o X_k)   (128 dstate rows x 16 headdim columns),
+//   h        = 2^(G'_last,k) h + S_k   (fmaf, as the state pass does),
+// then writes final = h. The per-chunk states never reach memory.
+//
+// Operands. The 16x16x32 bf16 MFMA takes both operands from the ring through
+// gfx950's transposing LDS read (ds_read_b64_tr_b16): the contraction index,
+// the token, is the slow index of x and B in memory. The product is formed
+// transposed, dstate as the MFMA rows and headdim as its columns, so a lane's
+// four accumulator registers hold four consecutive dstate columns of one
+// headdim row; a swap between neighbouring 16-lane rows (v_permlane16_swap)
+// then gives each lane a whole 16-byte piece of the stored (hi, lo) format.
+// The weight w_t is applied to x, each value once per wave, and w o x enters
+// as a bf16 (hi, lo) pair in two MFMAs against the exact bf16 B
+// (Io<bf16>::split). In a k-step of 32 tokens, lane group q = lane / 16 holds
+// tokens 8 q .. 8 q + 7 in its k-slots, the MFMA's own layout.
+//
+// Ring. A k-step's slot holds the step's 32 x rows (2P bytes each), its 32 B
+// rows of the workgroup's dstate slice (256 bytes each) and its 32 weights.
+// The 32-byte segments of every row sit XOR-swizzled by row bits, so the
+// eight rows a half-wave's transposing read touches land in eight different
+// bank groups. Each wave loads its share of every step (one x piece, 8 / W
+// B pieces and part of the weights) D - 1 steps ahead by direct global->LDS
+// loads, waits for them, and a workgroup barrier per step makes every share
+// visible and frees the slot read a step earlier. Past the end of the walk
+// the waves load the last step again, into slots no one reads, so every step
+// issues the same vector memory operations and one constant wait count
+// covers every step (they complete in order).
+template <int P, int Q>
+struct SpCfg {
+  static constexpr int W = P / 16;            // waves per workgroup
+  static constexpr int KS = Q / 32;           // k-steps per chunk
+  static constexpr int PPS = 8 / KS;          // hprev stores per wave per k-step (8 per chunk)
+  static constexpr int XRB = 2 * P;           // x row bytes
+  static constexpr int XOFF = 0, BOFF = 32 * XRB, WOFF = BOFF + 32 * 256, SLOT = WOFF + 128;
+  static constexpr int XL = 32 * XRB / 1024;  // x loads per step (one per wave)
+  static constexpr int BL = 8 / W;            // B loads per wave per step
+  static constexpr int LPS = 1 + BL + 1;      // loads per wave per step (x, B, w)
+  static constexpr int D = P == 64 ? 6 : 4;   // ring slots
+  // vector memory operations issued after a step's loads when it is waited
+  // for, at the top of its iteration: the stores of the iteration that issued
+  // them and D - 2 whole iterations; for the steps loaded before the walk,
+  // at least D - 2 issues
+  static constexpr int VM_STEADY = (D - 1) * PPS + (D - 2) * LPS;
+  static constexpr int VM_FIRST = (D - 2) * LPS;
+  static_assert(XL == W, "one x load per wave per step");
+  static_assert(KS >= 1 && 8 % KS == 0, "8 hprev stores per chunk");
+  static_assert(VM_STEADY <= 63, "vmcnt range");
+  static_assert(D * SLOT <= 80 * 1024, "two workgroups per CU");
+};
+
+// 32-byte segment swizzle of a ring row: segment c of row r sits at c ^ f(r).
+// Eight rows of a half-wave's transposing read (rows 8 q + 4 hh + 0..3 for
+// q = 0, 1, or 2, 3) get eight different bank groups: in 256-byte rows the
+// bank group is the position itself; in 128-byte rows it is the position
+// plus 4 (r % 2).
+__device__ __forceinline__ constexpr uint32_t swz256(uint32_t r) { return (r & 3) | ((r >> 1) & 4); }
+__device__ __forceinline__ constexpr uint32_t swz128(uint32_t r) { return ((r >> 1) & 1) | ((r >> 2) & 2); }
+
+template <int P, int N, int Q>
+__global__ __launch_bounds__(64 * (P / 16)) void ssd_chunk_state_pass_rows(
+    const bf16* __restrict__ x, const bf16* __restrict__ Bm, const float* __restrict__ wst,
+    const float* __restrict__ gcum, const float* init, void* __restrict__ hprev, float* final_state,
+    int64_t Tlen, int H, int G, int64_t nc, int64_t Tp, int xcd) {
+  using Sc = SpCfg<P, Q>;
+  using I = Io<bf16>;
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  constexpr int W = Sc::W, KS = Sc::KS, PPS = Sc::PPS, D = Sc::D, NG = N / 128, XRB = Sc::XRB;
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[D][Sc::SLOT];
+
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const int lane = threadIdx.x % 64, q = lane / 16, li = lane % 16;
+  // workgroup -> (batch*head, dstate slice); with xcd set (batch*heads a
+  // multiple of 8) the slices of one head are 8 workgroups apart, on one XCD
+  const int64_t wid = blockIdx.x;
+  int ng;
+  int64_t bh;
+  if (xcd) {
+    ng = (int)((wid / 8) % NG);
+    bh = (wid / (8 * NG)) * 8 + wid % 8;
+  } else {
+    ng = (int)(wid % NG);
+    bh = wid / NG;
+  }
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  const int grp = h / (H / G);
+  const uint32_t xsb = (uint32_t)H * P * 2, bsb = (uint32_t)G * N * 2;
+  const int64_t nsteps = nc * KS;
+  const bf16* xs0 = x + (b * Tlen * H + h) * P;                 // token 0 of the head
+  const bf16* bs0 = Bm + (b * Tlen * G + grp) * N + ng * 128;
+  const float* ws0 = wst + bh * Tp;
+
+  // this wave's loads of a step: x piece `wave` (rows 1024/XRB * wave ..),
+  // B pieces BL * wave .. (4 rows each), weights 32/W floats
+  constexpr int XRPL = 1024 / XRB;                               // x rows per load
+  const uint32_t xr = (uint32_t)(XRPL * wave + lane / (XRB / 16));
+  const uint32_t xps = (uint32_t)(lane % (XRB / 16));            // 16-byte LDS piece in the row
+  const uint32_t xsw = P == 64 ? swz128(xr) : swz256(xr);
+  const uint32_t xsrc = ((((xps >> 1) ^ xsw)) << 5) + ((xps & 1) << 4);
+  const uint32_t bps = (uint32_t)(lane % 16);
+  constexpr int WLANES = 8 / W;                                  // 16-byte weight pieces per wave
+  auto issue = [&](int64_t u) {
+    unsigned char* sp = ring[u % D];
+    const int64_t tb = 32 * u;
+    if (lane < WLANES) dma16(ws0 + tb + 4 * WLANES * wave, (uint32_t)lane * 16, sp + Sc::WOFF + 16 * WLANES * wave);
+    if (tb + 32 <= Tlen) {
+      dma16(xs0 + tb * H * P, xr * xsb + xsrc, sp + Sc::XOFF + 1024 * wave);
+#pragma unroll
+      for (int j = 0; j < Sc::BL; ++j) {
+        const uint32_t br = (uint32_t)(4 * (Sc::BL * wave + j) + lane / 16);
+        dma16(bs0 + tb * G * N, br * bsb + ((((bps >> 1) ^ swz256(br))) << 5) + ((bps & 1) << 4),
+              sp + Sc::BOFF + 1024 * (Sc::BL * wave + j));
+      }
+    } else {
+      // rows past the sequence: the last row again (finite; its weight is 0)
+      const int64_t base = tb < Tlen - 1 ? tb : Tlen - 1;
+      const int64_t rx = tb + xr < Tlen - 1 ? tb + xr : Tlen - 1;
+      dma16(xs0 + base * H * P, (uint32_t)(rx - base) * xsb + xsrc, sp + Sc::XOFF + 1024 * wave);
+#pragma unroll
+      for (int j = 0; j < Sc::BL; ++j) {
+        const uint32_t br = (uint32_t)(4 * (Sc::BL * wave + j) + lane / 16);
+        const int64_t rb = tb + br < Tlen - 1 ? tb + br : Tlen - 1;
+        dma16(bs0 + base * G * N, (uint32_t)(rb - base) * bsb + ((((bps >> 1) ^ swz256(br))) << 5) + ((bps & 1) << 4),
+              sp + Sc::BOFF + 1024 * (Sc::BL * wave + j));
+      }
+    }
+  };
+
+  // transposing reads: lane supplies row 8 q + 4 hh + li / 4, columns
+  // 16 c + 4 (li % 4) of 32-byte segment c (this wave's headdim segment for x,
+  // dstate block jj for B)
+  const uint32_t rr = (uint32_t)(8 * q + li / 4);                // row for hh = 0; hh = 1 adds 4
+  const uint32_t col8 = (uint32_t)(li % 4) * 8;
+  uint32_t xtr[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const uint32_t r = rr + 4 * hh;
+    xtr[hh] = r * XRB + (((uint32_t)wave ^ (P == 64 ? swz128(r) : swz256(r))) << 5) + col8;
+  }
+  const uint32_t brow0 = rr * 256 + col8, bsw0 = swz256(rr), bsw1 = swz256(rr + 4);
+
+  // the state: lane holds headdim row p = 16 wave + li and, in hs[jj][i],
+  // dstate column 128 ng + 16 jj + 4 q + i
+  const int p = 16 * wave + li;
+  f32x4 hs[8];
+  if (init) {
+    const float* ip = init + bh * (int64_t)(P * N) + p * N + ng * 128 + 4 * q;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const float4 v = *reinterpret_cast<const float4*>(ip + 16 * jj);
+      hs[jj] = f32x4{v.x, v.y, v.z, v.w};
+    }
+  } else {
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) hs[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  unsigned char* hbase = static_cast<unsigned char*>(hprev) + bh * nc * (int64_t)(P * N) * 4;
+  // piece (jj, q / 2) of row p: dstate columns 128 ng + 16 jj + 8 (q / 2) ..
+  // + 7; lane groups q = 0, 2 store its hi halves, q = 1, 3 its lo halves
+  const uint32_t hrow = (uint32_t)p * (4 * N) + (uint32_t)(16 * ng + q / 2) * 32 + (uint32_t)(q % 2) * 16;
+
+  for (int64_t u = 0; u < D - 1; ++u) issue(u < nsteps ? u : nsteps - 1);
+
+  for (int64_t k = 0; k < nc; ++k) {
+    f32x4 acc[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(hbase + k * (int64_t)(P * N) * 4, (uint32_t)(P * N * 4));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int64_t t = k * KS + s;
+      // this wave's loads of step t have landed and its reads of step t - 1
+      // are done; after the barrier, so are every wave's
+      if (t < D - 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(Sc::VM_FIRST) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(Sc::VM_STEADY) : "memory");
+      issue(t + D - 1 < nsteps ? t + D - 1 : nsteps - 1);
+      const unsigned char* sp = ring[t % D];
+      uint64_t x2[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        x2[hh] = __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                  (__attribute__((address_space(3))) s16x4*)(sp + Sc::XOFF + xtr[hh])));
+      const float4 w0 = *reinterpret_cast<const float4*>(sp + Sc::WOFF + 32 * q);
+      const float4 w1 = *reinterpret_cast<const float4*>(sp + Sc::WOFF + 32 * q + 16);
+      bf16x8 bfr[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const uint64_t b0 = __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(sp + Sc::BOFF + brow0 + ((jj ^ bsw0) << 5))));
+        const uint64_t b1 = __builtin_bit_cast(uint64_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(sp + Sc::BOFF + brow0 + 4 * 256 + ((jj ^ bsw1) << 5))));
+        const u32x4 w4 = {(uint32_t)b0, (uint32_t)(b0 >> 32), (uint32_t)b1, (uint32_t)(b1 >> 32)};
+        bfr[jj] = __builtin_bit_cast(bf16x8, w4);
+      }
+      const uint32_t xd[4] = {(uint32_t)x2[0], (uint32_t)(x2[0] >> 32), (uint32_t)x2[1], (uint32_t)(x2[1] >> 32)};
+      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = wv[e] * I::elem(xd[e / 2], e % 2);
+      bf16x8 xhi, xlo;
+      I::split(v, xhi, xlo);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[jj], xhi, acc[jj], 0, 0, 0);
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[jj], xlo, acc[jj], 0, 0, 0);
+      // hprev[k] = h: blocks s*PPS .. s*PPS + PPS - 1
+#pragma unroll
+      for (int i = 0; i < PPS; ++i) {
+        const int jj = s * PPS + i;
+        const uint32_t a0 = pack_bf16x2(hs[jj][0], hs[jj][1]);
+        const uint32_t a1 = pack_bf16x2(hs[jj][2], hs[jj][3]);
+        const uint32_t l0 = pack_bf16x2(hs[jj][0] - bf16lo(a0), hs[jj][1] - bf16hi(a0));
+        const uint32_t l1 = pack_bf16x2(hs[jj][2] - bf16lo(a1), hs[jj][3] - bf16hi(a1));
+        const auto s0 = __builtin_amdgcn_permlane16_swap(a0, l0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane16_swap(a1, l1, false, false);
+        const u32x4 vv = {s0[0], s1[0], s0[1], s1[1]};
+        __builtin_amdgcn_raw_buffer_store_b128(vv, rh, hrow + (uint32_t)jj * 64, 0, 0);
+      }
+    }
+    // h = 2^(G'_last,k) h + S_k
+    const float sc = exp2_hw(gcum[bh * Tp + k * Q + (Q - 1)]);
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hs[jj][i] = fmaf(sc, hs[jj][i], acc[jj][i]);
+  }
+  if (final_state) {
+    float* fp = final_state + bh * (int64_t)(P * N) + p * N + ng * 128 + 4 * q;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj)
+      *reinterpret_cast<float4*>(fp + 16 * jj) = make_float4(hs[jj][0], hs[jj][1], hs[jj][2], hs[jj][3]);
+  }
+  // the ring's last loads land in this workgroup's LDS: they must finish before it exits
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+template <int P, int N, int Q>
+hipError_t launch_rows(const Problem& p, hipStream_t stream) {
+  constexpr int NG = N / 128;
+  const int64_t groups = p.bt * p.H * NG;
+  const int xcd = (p.bt * p.H) % 8 == 0 ? 1 : 0;
+  hipLaunchKernelGGL((ssd_chunk_state_pass_rows<P, N, Q>), dim3((unsigned)groups), dim3(64 * (P / 16)), 0, stream,
+                     (const bf16*)p.x, (const bf16*)p.B, p.wst, p.gcum, p.init, p.hprev, p.final_state, p.T,
+                     (int)p.H, (int)p.G, p.nc, p.Tp, xcd);
+  return hipGetLastError();
+}
+
 template <typename T, int P, int N, int Q>
 hipError_t launch_one(const Problem& p, hipStream_t stream) {
   using Cfg = StateCfg<T, P, N>;
@@ -500,23 +756,45 @@ hipError_t launch_chunk_state(const Problem& p, hipStream_t stream) {
 }
 
 bool chunk_state_pass_fits(const Problem& p) {
-  // bf16, headdim 64, dstate 64/128/256, chunk 256, at least one chunk
-  return p.io == 1 && p.P == 64 && p.Q == 256 && (p.N == 64 || p.N == 128 || p.N == 256) && p.nc > 0;
+  // bf16, at least one chunk; headdim 64 and chunk 256 (ssd_chunk_state_pass,
+  // dstate 64, 128 or 256), or dstate 128 or 256 (ssd_chunk_state_pass_rows)
+  if (p.io != 1 || p.nc <= 0) return false;
+  return (p.P == 64 && p.Q == 256 && (p.N == 64 || p.N == 128 || p.N == 256)) ||
+         ((p.P == 64 || p.P == 128) && (p.N == 128 || p.N == 256));
 }
 
+namespace {
+// The two-wave form walks (batch, head, 64-column dstate group)s; it takes
+// headdim 64, chunk 256 when those walks alone fill the GPU.
+bool two_wave_form(const Problem& p) {
+  return p.P == 64 && p.Q == 256 && (p.N == 64 || !(p.bt * p.H * (p.N / 64) < 512));
+}
+}  // namespace
+
 bool chunk_state_pass_pays(const Problem& p) {
-  // Each (batch, head, dstate group) walks its head's chunks in sequence, so
-  // the one-kernel form wins only when those pairs alone fill the GPU.
-  // Measured on MI355X: 2.7B-like layer (640 pairs) 288 us against 310 us
-  // for ssd_chunk_state + ssd_state_pass; 130M-like (384 pairs) 59 against
-  // 50 us; a 80-pair long prefill is several times slower.
-  return p.bt * p.H * (p.N / 64) >= 512;
+  // Each walk is sequential over the chunks, so the one-kernel forms need
+  // many of them. Measured on MI355X (us, against ssd_chunk_state +
+  // ssd_state_pass): two-wave form at the 2.7B-like layer (640 walks) 291
+  // against 329; the row form with 192 (batch, head) workgroups (130M-like)
+  // 58 against 63, with 256 (grouped wide state, headdim 128, dstate 256,
+  // chunk 128) 821 against 1693, with 80 (long prefill) 1232 against 674.
+  if (two_wave_form(p)) return p.bt * p.H * (p.N / 64) >= 512;
+  return p.bt * p.H * (p.N / 128) >= 128;
 }
 
 hipError_t launch_chunk_state_pass(const Problem& p, hipStream_t stream) {
+  if (two_wave_form(p)) {
 #define SSD_CASE(NN, QQ) \
   if (p.N == NN && p.Q == QQ) return launch_fused<NN, QQ>(p, stream);
-  SSD_CASE(64, 256) SSD_CASE(128, 256) SSD_CASE(256, 256)
+    SSD_CASE(64, 256) SSD_CASE(128, 256) SSD_CASE(256, 256)
+#undef SSD_CASE
+    return hipErrorInvalidValue;
+  }
+#define SSD_CASE(PP, NN, QQ) \
+  if (p.P == PP && p.N == NN && p.Q == QQ) return launch_rows<PP, NN, QQ>(p, stream);
+#define SSD_Q(PP, NN) SSD_CASE(PP, NN, 64) SSD_CASE(PP, NN, 128) SSD_CASE(PP, NN, 256)
+  SSD_Q(64, 128) SSD_Q(64, 256) SSD_Q(128, 128) SSD_Q(128, 256)
+#undef SSD_Q
 #undef SSD_CASE
   return hipErrorInvalidValue;
 }

@@ -100,8 +100,9 @@ def test_path_field():
         assert _check(SMALL, io | ssd.PATH_FOUR) == OK
     assert ssd.fwd_path(HEADLINE, BF16 | ssd.PATH_THREE) == ssd.PATH_THREE
     assert ssd.fwd_path(HEADLINE, F32) == ssd.PATH_FOUR
-    for d, io in ((HEADLINE, F32 | ssd.PATH_THREE), (SMALL, BF16 | ssd.PATH_THREE),   # fp32; chunk 128
-                  (Dims(4, 8192, 80, 128, 128, 1, 256), BF16 | ssd.PATH_THREE)):     # headdim 128
+    for d, io in ((HEADLINE, F32 | ssd.PATH_THREE),                                   # fp32
+                  (Dims(2, 300, 8, 64, 64, 2, 128), BF16 | ssd.PATH_THREE),          # dstate 64, chunk 128
+                  (Dims(4, 8192, 80, 128, 64, 1, 256), BF16 | ssd.PATH_THREE)):      # dstate 64, headdim 128
         assert _check(d, io) == UNSUP
         with pytest.raises(ssd.SsdError):
             ssd.fwd_path(d, io)
@@ -367,16 +368,22 @@ def test_fused_state_pass_query():
     # the 2.7B-like layer: bf16, headdim 64, 4 x 80 heads x 2 dstate groups
     assert ssd.fused_state_pass(HEADLINE, BF16)
     assert not ssd.fused_state_pass(HEADLINE, F32)                      # fp32 io: four kernels
-    assert not ssd.fused_state_pass(Dims(4, 8192, 80, 128, 128, 1, 256), BF16)   # headdim 128
     assert not ssd.fused_state_pass(Dims(4, 8192, 80, 64, 128, 3, 256), BF16)    # invalid (groups)
     assert not ssd.fused_state_pass(HEADLINE, BF16 | ssd.PATH_FOUR)
     assert ssd.fused_state_pass(Dims(1, 65536, 80, 64, 128, 1, 256), BF16 | ssd.PATH_THREE)
     assert ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 256), BF16 | ssd.PATH_THREE)
-    assert not ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 128), BF16 | ssd.PATH_THREE)   # chunk 128
+    assert not ssd.fused_state_pass(Dims(1, 300, 3, 64, 64, 1, 128), BF16 | ssd.PATH_THREE)   # dstate 64, chunk 128
+    # the row form: dstate 128 or 256, headdim 64 or 128, any chunk
+    assert ssd.fused_state_pass(Dims(1, 300, 3, 128, 256, 1, 128), BF16 | ssd.PATH_THREE)
+    assert ssd.fused_state_pass(Dims(1, 300, 3, 64, 128, 1, 64), BF16 | ssd.PATH_THREE)
     if ssd.fwd_path(HEADLINE, BF16) != ssd.PATH_CHAINED:
         # without the chained kernel the size rule decides
-        assert not ssd.fused_state_pass(Dims(8, 2048, 24, 64, 128, 1, 256), BF16)   # 384 walks: four kernels
-        assert not ssd.fused_state_pass(Dims(1, 65536, 80, 64, 128, 1, 256), BF16)  # 160 walks
+        assert ssd.fused_state_pass(Dims(4, 8192, 80, 128, 128, 1, 256), BF16)      # 320 row-form walks
+        assert ssd.fused_state_pass(Dims(8, 2048, 24, 64, 128, 1, 256), BF16)       # 192 row-form walks
+        assert ssd.fused_state_pass(Dims(2, 16384, 64, 128, 256, 8, 128), BF16)     # 256 row-form walks
+        assert not ssd.fused_state_pass(Dims(1, 65536, 80, 64, 128, 1, 256), BF16)  # 80 walks: four kernels
+        assert not ssd.fused_state_pass(Dims(4, 16384, 8, 64, 128, 1, 128), BF16)   # 32 walks
+        assert not ssd.fused_state_pass(Dims(1, 65536, 80, 64, 64, 1, 256), BF16)   # dstate 64: 160 walks
         assert not ssd.fused_state_pass(Dims(4, 0, 80, 64, 128, 1, 256), BF16)      # no chunks
 
 

@@ -273,10 +273,10 @@ def test_resident_scan_walks(name):
 
 
 # ------------------------------------ chunk states computed inside the state pass
-# (bf16, headdim 64, chunk 256: the THREE sequence). The path field of io
+# (bf16, dstate 128 or 256: the THREE sequence). The path field of io
 # forces either sequence regardless of size; both must match the oracle, and
-# each other up to fp32 rounding (the one-kernel form sums a chunk's two
-# halves separately, then adds them).
+# each other up to fp32 rounding (the two forms sum a chunk's tokens in
+# different orders).
 # Two sequences store hprev as bf16 (hi, lo) pairs of fp32 states summed in
 # different orders: each stored pair is within 2^-16 of its fp32 value (hi and
 # lo both round to nearest), so the two may differ by about twice that.
@@ -286,6 +286,9 @@ FUSED = {
     "2.7b-ragged": dict(batch=2, seqlen=3 * 256 + 13, nheads=5),
     "one-chunk": dict(batch=3, seqlen=100, nheads=2),
     "N64": dict(batch=1, seqlen=5 * 256 + 1, nheads=4, dstate=64),
+    "two-wave-form": dict(batch=2, seqlen=2 * 256 + 20, nheads=128),   # 512 walks: the two-wave form
+    "P128-N256-Q128": dict(batch=1, seqlen=700, nheads=8, headdim=128, dstate=256, ngroups=2, chunk=128),
+    "Q64": dict(batch=2, seqlen=5 * 64 + 9, nheads=3, chunk=64),
     "N256-groups": dict(batch=1, seqlen=600, nheads=8, dstate=256, ngroups=2),
     "exact-chunks": dict(batch=2, seqlen=4 * 256, nheads=3),
     "long-walk": dict(batch=1, seqlen=20 * 256 + 77, nheads=2),
@@ -424,8 +427,8 @@ def test_dt_head_major_layout(name, path):
     cfg = DT_LAYOUT[name]
     pf = 0
     if path == "three":
-        if not (cfg.io == "bf16" and cfg.headdim == 64 and cfg.chunk == 256):
-            pytest.skip("the THREE sequence takes bf16, headdim 64, chunk 256 only")
+        if cfg.io != "bf16":
+            pytest.skip("the THREE sequence takes bf16 only")
         pf = ssd.PATH_THREE
     log(f"[dt layout] {name} path={path} {cfg}")
     inp = generate(cfg)
