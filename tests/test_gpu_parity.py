@@ -316,8 +316,13 @@ def test_fused_state_pass(name):
         a1, a2 = host(a1), host(a2)
         rel = float(np.max(np.abs(a1 - a2))) / max(float(np.max(np.abs(a2))), 1e-30)
         assert rel <= tol, f"{what}: paths differ by {rel:.2e} (normwise)"
+    # y: one bf16 ulp of each output, plus what the hprev difference above can
+    # move it by where the carried-state and in-chunk terms cancel (2^-15 of a
+    # term as large as the largest output, with margin)
     yy1, yy2 = host(y1), host(y2)
-    assert np.all(np.abs(yy1 - yy2) <= 2.0 ** -7 * np.abs(yy2) + 1e-6), "y: paths differ by more than 1 bf16 ulp"
+    ymax = float(np.max(np.abs(yy2)))
+    assert np.all(np.abs(yy1 - yy2) <= 2.0 ** -7 * np.abs(yy2) + 2.0 ** -12 * ymax), \
+        "y: paths differ by more than one bf16 ulp plus the hprev difference"
 
 
 def test_fused_state_pass_in_place_and_no_final():
