@@ -95,7 +95,18 @@ struct ScanCfg {
   static constexpr int HLOADS = (IH + WAVES - 1) / WAVES;   // per wave (spares repeat)
   static constexpr int HALLOC = HLDS ? IH * 1024 : 16;
   static constexpr int NBUF = HLDS ? 3 : (BLOCK <= 16384 ? 4 : 3);   // blocks in the LDS ring
+  // Otherwise, with bf16 (hi, lo) Hprev, the carried-state product streams
+  // Hprev through the ring in pieces of two MFMA k-steps (32 dstate columns:
+  // 128 bytes of each row), read once per workgroup: slot rows of 144 bytes
+  // (one 16-byte pad piece) in the row order of the HLDS case, so the 16
+  // lanes of a fragment read hit 16 distinct bank groups.
+  static constexpr bool STAGE = !HLDS && E == 2;
+  static constexpr int SROW = 144;                       // slot row bytes: 8 data pieces + 1 pad
+  static constexpr int NPC = N / 32;                     // pieces (two k-steps each)
+  static constexpr int IHP = P * 9 / 64;                 // wave-instructions per piece
+  static constexpr int HPL = (IHP + WAVES - 1) / WAVES;  // per wave (spares repeat)
   static_assert(NTB % TBW == 0 && NPG % PGW == 0, "tile split");
+  static_assert(!STAGE || (NBUF == 3 && P * SROW <= BLOCK && (P * 9) % 64 == 0 && NTB >= 2), "staged Hprev pieces");
   static_assert(WAVES >= 1 && WAVES <= 8, "tile does not fit a workgroup");
 };
 
@@ -231,6 +242,27 @@ __device__ __forceinline__ void issue_hprev(unsigned char* dst, const unsigned c
   }
 }
 
+// Direct global->LDS loads of Hprev piece c (dstate columns 32 c .. 32 c + 31
+// of every headdim row, bf16 (hi, lo) pairs: bytes 128 c .. 128 c + 127 of
+// each 4N-byte row) into a ring slot: slot row r (144 bytes) holds headdim
+// row (r / 64) * 64 + 2 (r % 32) + (r / 32) % 2, its ninth piece a copy of
+// the first (never read).
+template <typename Cfg>
+__device__ __forceinline__ void issue_hpiece(unsigned char* dst, const unsigned char* hsrc, int c, int wave,
+                                             int lane) {
+  constexpr int P = Cfg::NPG * Cfg::CG, ROWB = (Cfg::HROWP - 1) * 16;
+#pragma unroll
+  for (int i = 0; i < Cfg::HPL; ++i) {
+    const int kk = (wave + i * Cfg::WAVES) % Cfg::IHP;
+    const int s = kk * 64 + lane;
+    const int r = s / 9;
+    int pc = s % 9;
+    if (pc == 8) pc = 0;   // pad piece
+    const int p = (r / 64) * 64 + 2 * (r % 32) + (r / 32) % 2;
+    lds_dma16(hsrc + (int64_t)p * ROWB + c * 128 + pc * 16, dst + kk * 1024);
+  }
+}
+
 template <typename T, int P, int N, int Q>
 __global__ __launch_bounds__((ScanCfg<T, P, N, Q>::THREADS)) __attribute__((amdgpu_waves_per_eu(2)))
 void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
@@ -299,10 +331,25 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
   // Hprev bytes of this chunk: P rows of 4N bytes
   const unsigned char* hsrc = static_cast<const unsigned char*>(hprev) + hoff * 4;
   if constexpr (Cfg::HLDS) issue_hprev<Cfg, T>(sH, hsrc, wave, lane);
-  // the first NBUF-1 j-blocks go in flight behind it
+  // the first NBUF-1 j-blocks go in flight behind it; with staged Hprev its
+  // first two pieces go first, and the j-blocks follow the last pieces
+  constexpr int JOFF = Cfg::STAGE ? Cfg::NPC % NBUF : 0;   // ring slot of j-block 0
+  auto issue_j = [&](int jn) {
+    const int sn = (jn + JOFF) % NBUF;
+    if (full)
+      issue_block_full<Cfg>(ring[sn], reinterpret_cast<const unsigned char*>(bbase) + jn * bblk_bytes,
+                            reinterpret_cast<const unsigned char*>(xbase) + jn * xblk_bytes, boffs, wave);
+    else
+      issue_block<Cfg>(ring[sn], bbase, xbase, brow, xrow, jn, nvalid, wave, lane);
+  };
+  if constexpr (Cfg::STAGE) {
+    issue_hpiece<Cfg>(ring[0], hsrc, 0, wave, lane);
+    if (Cfg::NPC > 1) issue_hpiece<Cfg>(ring[1], hsrc, 1, wave, lane);
+    else issue_j(0);
+  }
 #pragma unroll
   for (int i = 0; i < NBUF - 1; ++i)
-    if (i < NTB) {
+    if (!Cfg::STAGE && i < NTB) {
       if (full)
         issue_block_full<Cfg>(ring[i], reinterpret_cast<const unsigned char*>(bbase) + i * bblk_bytes,
                               reinterpret_cast<const unsigned char*>(xbase) + i * xblk_bytes, boffs, wave);
@@ -318,6 +365,43 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
     for (int q = 0; q < PGW; ++q)
 #pragma unroll
       for (int pe = 0; pe < E; ++pe) acc[u][q][pe] = f32x16{};
+  if constexpr (Cfg::STAGE) {
+    // piece c is in slot c % 3; at its turn the item after it (piece c + 1,
+    // or j-block 0 after the last piece) is still in flight, and the slot
+    // read one turn earlier takes item c + 2 (a piece, then j-blocks 0, 1)
+#pragma unroll
+    for (int c = 0; c < Cfg::NPC; ++c) {
+      if (c + 1 < Cfg::NPC) wait_vm_barrier<Cfg::HPL>();
+      else wait_vm_barrier<LOADS>();
+      if (c + 2 < Cfg::NPC) issue_hpiece<Cfg>(ring[(c + 2) % NBUF], hsrc, c + 2, wave, lane);
+      else if (c + 2 - Cfg::NPC < NBUF - 1) issue_j(c + 2 - Cfg::NPC);
+      const unsigned char* hb = ring[c % NBUF];
+      // one k-step at a time: its fragments are read while the previous
+      // k-step's MFMAs run, and no more of them stay live
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) {
+        Frag hhi[PGW][E], hlo[PGW][E];
+#pragma unroll
+        for (int q = 0; q < PGW; ++q)
+#pragma unroll
+          for (int pe = 0; pe < E; ++pe) {
+            const unsigned char* hp = hb + ((pg0 + q) * 64 + pe * 32 + m) * Cfg::SROW + (2 * sl + g) * 32;
+            hhi[q][pe] = *reinterpret_cast<const Frag*>(hp);
+            hlo[q][pe] = *reinterpret_cast<const Frag*>(hp + 16);
+          }
+#pragma unroll
+        for (int q = 0; q < PGW; ++q)
+#pragma unroll
+          for (int pe = 0; pe < E; ++pe)
+#pragma unroll
+            for (int u = 0; u < TBW; ++u) {
+              I::mma(acc[u][q][pe], cf[u][2 * c + sl], hhi[q][pe]);
+              I::mma(acc[u][q][pe], cf[u][2 * c + sl], hlo[q][pe]);
+            }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
   if constexpr (Cfg::HLDS) {
     // Hprev landed once only the j-block loads issued after it remain
     if constexpr (NBUF - 1 <= NTB) {
@@ -333,7 +417,7 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
     for (int pe = 0; pe < E; ++pe) {
       const int p = (pg0 + q) * CG + E * m + pe;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
+      for (int s = 0; s < (Cfg::STAGE ? 0 : KS); ++s) {
         Frag hhi, hlo;
         if constexpr (Cfg::HLDS) {
           const int slot = E == 2 ? (pg0 + q) * 64 + pe * 32 + m : p;
@@ -390,18 +474,11 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
     if (after <= 0) wait_vm_barrier<0>();
     else if (after == 1) wait_vm_barrier<LOADS>();
     else wait_vm_barrier<2 * LOADS>();
-    if (jb + NBUF - 1 < NTB) {
-      const int jn = jb + NBUF - 1, sn = jn % NBUF;
-      if (full)
-        issue_block_full<Cfg>(ring[sn], reinterpret_cast<const unsigned char*>(bbase) + jn * bblk_bytes,
-                              reinterpret_cast<const unsigned char*>(xbase) + jn * xblk_bytes, boffs, wave);
-      else
-        issue_block<Cfg>(ring[sn], bbase, xbase, brow, xrow, jn, nvalid, wave, lane);
-    }
+    if (jb + NBUF - 1 < NTB) issue_j(jb + NBUF - 1);
     if (jb > tmax) continue;
 
-    const unsigned char* sb = ring[jb % NBUF] + boff;
-    const unsigned char* sx = ring[jb % NBUF] + Cfg::BBYTES + xoff;
+    const unsigned char* sb = ring[(jb + JOFF) % NBUF] + boff;
+    const unsigned char* sx = ring[(jb + JOFF) % NBUF] + Cfg::BBYTES + xoff;
     const int j0 = jb * 32;
     // this lane half's 16 j rows are rows drow(q, g) of the block (D row order)
     float wj[16];
