@@ -51,7 +51,8 @@ KERNEL_SOURCES = {"ssd_chunk_cumsum": ["chunk_cumsum.hip"], "ssd_chunk_state": [
 PATHS = {"auto": 0x0000, "four": 0x1000, "three": 0x2000, "chained": 0x3000}   # MAMBA2_SSD_PATH_*
 FLUSH_BYTES = 1 << 30          # scratch written before each cold step (> the 256 MB last-level cache)
 TRAFFIC_SUMMARY = {"mamba2-2.7b": "hbm_traffic_mamba2-2.7b.md",
-                   "mamba2-2.7b-decode": "hbm_traffic_mamba2-2.7b-decode.md"}
+                   "mamba2-2.7b-decode": "hbm_traffic_mamba2-2.7b-decode.md",
+                   "grouped-wide": "hbm_traffic_grouped-wide.md"}
 
 
 def source_hash(kernel):
