@@ -268,7 +268,7 @@ __global__ __launch_bounds__((ScanCfg<T, P, N, Q>::THREADS)) __attribute__((amdg
 void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
                     const float* __restrict__ gcum, const float* __restrict__ dtt, const float* __restrict__ Dp,
                     const void* __restrict__ hprev, T* __restrict__ y, int64_t Tlen, int H, int G, int64_t nc,
-                    int64_t Tp) {
+                    int64_t Tp, int xcd) {
   using I = Io<T>;
   using Frag = typename I::Frag;
   using Cfg = ScanCfg<T, P, N, Q>;
@@ -292,9 +292,24 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
   int tbs[TBW];
   tbs[0] = tg;
   if constexpr (TBW == 2) tbs[1] = NTB - 1 - tg;
-  const int h = blockIdx.x;
-  const int k = blockIdx.y;
-  const int64_t b = blockIdx.z;
+  // workgroup -> (batch, chunk, head). The heads of one group read the same
+  // B and C rows; with xcd set (batch * chunks * groups a multiple of 8) a
+  // group's heads take consecutive workgroup slots of one XCD (the
+  // dispatcher deals workgroups to the 8 XCDs in turn), so those rows come
+  // from that XCD's L2 after the first head.
+  const int64_t L = blockIdx.x, hpg = H / G;
+  int64_t set, member;
+  if (xcd) {
+    const int64_t j = L / 8;
+    member = j % hpg;
+    set = (j / hpg) * 8 + L % 8;
+  } else {
+    member = L % hpg;
+    set = L / hpg;
+  }
+  const int h = (int)((set % G) * hpg + member);
+  const int k = (int)((set / G) % nc);
+  const int64_t b = set / (G * nc);
   const int grp = h / (H / G);
   const int64_t t0 = (int64_t)k * Q;
   const int nvalid = (int)(Tlen - t0 < Q ? Tlen - t0 : Q);   // >= 1
@@ -981,10 +996,11 @@ hipError_t launch_one(const Problem& p, hipStream_t stream) {
                        stream, (const T*)p.x, (const T*)p.B, (const T*)p.C, p.gcum, p.dtt, p.D,
                        (const void*)p.hprev, (T*)p.y, p.T, (int)p.H, (int)p.G, p.nc, p.Tp, ntiles, xcd);
   } else {
-    const dim3 grid((unsigned)p.H, (unsigned)p.nc, (unsigned)p.bt);
-    hipLaunchKernelGGL((ssd_chunk_scan<T, P, N, Q>), grid, dim3(Cfg::THREADS), 0, stream, (const T*)p.x,
-                       (const T*)p.B, (const T*)p.C, p.gcum, p.dtt, p.D, (const void*)p.hprev, (T*)p.y, p.T,
-                       (int)p.H, (int)p.G, p.nc, p.Tp);
+    const int64_t tiles = p.H * p.nc * p.bt;
+    const int xcd = (p.bt * p.nc * p.G) % 8 == 0 ? 1 : 0;
+    hipLaunchKernelGGL((ssd_chunk_scan<T, P, N, Q>), dim3((unsigned)tiles), dim3(Cfg::THREADS), 0, stream,
+                       (const T*)p.x, (const T*)p.B, (const T*)p.C, p.gcum, p.dtt, p.D, (const void*)p.hprev,
+                       (T*)p.y, p.T, (int)p.H, (int)p.G, p.nc, p.Tp, xcd);
   }
   return hipGetLastError();
 }

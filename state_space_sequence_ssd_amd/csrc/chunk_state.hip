@@ -548,21 +548,27 @@ __global__ __launch_bounds__(64 * (P / 16)) void ssd_chunk_state_pass_rows(
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int lane = threadIdx.x % 64, q = lane / 16, li = lane % 16;
-  // workgroup -> (batch*head, dstate slice); with xcd set (batch*heads a
-  // multiple of 8) the slices of one head are 8 workgroups apart, on one XCD
-  const int64_t wid = blockIdx.x;
-  int ng;
-  int64_t bh;
+  // workgroup -> (batch, group, head of the group, dstate slice). Every head
+  // and slice of a (batch, group) reads the group's B rows; with xcd set
+  // (batch * groups a multiple of 8) they take consecutive workgroup slots
+  // of one XCD (the dispatcher deals workgroups to the 8 XCDs in turn), so
+  // those rows, and each head's x rows for its second slice, come from that
+  // XCD's L2.
+  const int64_t wid = blockIdx.x, hpg = H / G, members = hpg * NG;
+  int64_t set, member;
   if (xcd) {
-    ng = (int)((wid / 8) % NG);
-    bh = (wid / (8 * NG)) * 8 + wid % 8;
+    const int64_t j = wid / 8;
+    member = j % members;
+    set = (j / members) * 8 + wid % 8;
   } else {
-    ng = (int)(wid % NG);
-    bh = wid / NG;
+    member = wid % members;
+    set = wid / members;
   }
-  const int h = (int)(bh % H);
-  const int64_t b = bh / H;
-  const int grp = h / (H / G);
+  const int ng = (int)(member % NG);
+  const int grp = (int)(set % G);
+  const int64_t b = set / G;
+  const int h = (int)(grp * hpg + member / NG);
+  const int64_t bh = b * H + h;
   const uint32_t xsb = (uint32_t)H * P * 2, bsb = (uint32_t)G * N * 2;
   const int64_t nsteps = nc * KS;
   const bf16* xs0 = x + (b * Tlen * H + h) * P;                 // token 0 of the head
@@ -717,7 +723,7 @@ template <int P, int N, int Q>
 hipError_t launch_rows(const Problem& p, hipStream_t stream) {
   constexpr int NG = N / 128;
   const int64_t groups = p.bt * p.H * NG;
-  const int xcd = (p.bt * p.H) % 8 == 0 ? 1 : 0;
+  const int xcd = (p.bt * p.G) % 8 == 0 ? 1 : 0;
   hipLaunchKernelGGL((ssd_chunk_state_pass_rows<P, N, Q>), dim3((unsigned)groups), dim3(64 * (P / 16)), 0, stream,
                      (const bf16*)p.x, (const bf16*)p.B, p.wst, p.gcum, p.init, p.hprev, p.final_state, p.T,
                      (int)p.H, (int)p.G, p.nc, p.Tp, xcd);
