@@ -23,11 +23,13 @@
  *                     product of the "Kernel 2: fwd_pass_state" section)
  *   ssd_state_pass    the sequential pass over chunk checkpoints
  *                     (the chunk loop of the same section)
- *   (for bf16 io, headdim 64, chunk 256 and many (batch, head) pairs the
- *   chunk states are computed inside the state pass instead: one kernel,
- *   ssd_chunk_state_pass, with the structure of the blog's "Kernel 2", the
- *   per-chunk states never reaching memory; mamba2_ssd_fwd_path tells which
- *   kernel sequence a call takes, and a field of io_dtype can force one)
+ *   (for bf16 io and many (batch, head) pairs the chunk states are computed
+ *   inside the state pass instead: one kernel with the structure of the
+ *   blog's "Kernel 2", the per-chunk states never reaching memory --
+ *   ssd_chunk_state_pass for headdim 64, chunk 256, or
+ *   ssd_chunk_state_pass_rows for dstate 128 or 256; mamba2_ssd_fwd_path
+ *   tells which kernel sequence a call takes, and a field of io_dtype can
+ *   force one)
  *   ssd_chunk_scan    the per-chunk outputs: decayed carried-state term,
  *                     masked decayed C.B^T product with dt*x, and D*x
  *                     (blog section "Kernel 3: compute_out")
@@ -96,8 +98,8 @@ extern "C" {
  * MAMBA2_SSD_ERR_UNSUPPORTED from every forward entry point.
  *   FOUR     ssd_chunk_cumsum, ssd_chunk_state, ssd_state_pass,
  *            ssd_chunk_scan (every supported shape)
- *   THREE    ssd_chunk_cumsum, ssd_chunk_state_pass, ssd_chunk_scan (bf16,
- *            headdim 64, chunk 256)
+ *   THREE    ssd_chunk_cumsum, ssd_chunk_state_pass(_rows), ssd_chunk_scan
+ *            (bf16; headdim 64 and chunk 256, or dstate 128 or 256)
  *   CHAINED  ssd_chunk_cumsum, then one kernel that computes each chunk's
  *            state contribution, the pass and the outputs, handing the
  *            carried state from each chunk to the next through the
