@@ -250,7 +250,7 @@ __device__ __forceinline__ void issue_hprev(unsigned char* dst, const unsigned c
 template <typename Cfg>
 __device__ __forceinline__ void issue_hpiece(unsigned char* dst, const unsigned char* hsrc, int c, int wave,
                                              int lane) {
-  constexpr int P = Cfg::NPG * Cfg::CG, ROWB = (Cfg::HROWP - 1) * 16;
+  constexpr int ROWB = (Cfg::HROWP - 1) * 16;
 #pragma unroll
   for (int i = 0; i < Cfg::HPL; ++i) {
     const int kk = (wave + i * Cfg::WAVES) % Cfg::IHP;

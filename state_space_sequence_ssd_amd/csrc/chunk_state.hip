@@ -500,14 +500,21 @@ hipError_t launch_fused(const Problem& p, hipStream_t stream) {
 // B pieces and part of the weights) D - 1 steps ahead by direct global->LDS
 // loads, waits for them, and a workgroup barrier per step makes every share
 // visible and frees the slot read a step earlier. Past the end of the walk
-// the waves load the last step again, into slots no one reads, so every step
-// issues the same vector memory operations and one constant wait count
-// covers every step (they complete in order).
+// the waves load the last step again, into slots no one reads, so the vector
+// memory operations a step issues depend only on its place in the chunk, and
+// each wait count is a compile-time constant of that place (they complete in
+// order).
 template <int P, int Q>
 struct SpCfg {
   static constexpr int W = P / 16;            // waves per workgroup
   static constexpr int KS = Q / 32;           // k-steps per chunk
   static constexpr int PPS = 8 / KS;          // hprev stores per wave per k-step (8 per chunk)
+  // Headdim 128: a chunk's 8 hprev stores per wave go out together at its
+  // first step, so each row's 512 bytes leave at once. Spread over the steps,
+  // each step writing one 128-byte strip of 128 rows, the writes ran at half
+  // the rate there (grouped wide-state layer 805 against 700 us); at headdim 64
+  // (130M-like) the spread stores are faster (57 against 63 us).
+  static constexpr bool BURST = P == 128;
   static constexpr int XRB = 2 * P;           // x row bytes
   static constexpr int XOFF = 0, BOFF = 32 * XRB, WOFF = BOFF + 32 * 256, SLOT = WOFF + 128;
   static constexpr int XL = 32 * XRB / 1024;  // x loads per step (one per wave)
@@ -515,14 +522,21 @@ struct SpCfg {
   static constexpr int LPS = 1 + BL + 1;      // loads per wave per step (x, B, w)
   static constexpr int D = P == 64 ? 6 : 4;   // ring slots
   // vector memory operations issued after a step's loads when it is waited
-  // for, at the top of its iteration: the stores of the iteration that issued
-  // them and D - 2 whole iterations; for the steps loaded before the walk,
-  // at least D - 2 issues
-  static constexpr int VM_STEADY = (D - 1) * PPS + (D - 2) * LPS;
+  // for, at the top of iteration s of a chunk: the loads of the D - 2
+  // iterations after the one that issued them, and the stores of that
+  // iteration and those D - 2 (PPS each, or 8 at each chunk start when the
+  // stores go out together); for the steps loaded before the walk, at least
+  // the loads of D - 2 issues
   static constexpr int VM_FIRST = (D - 2) * LPS;
+  static constexpr int vm_at(int s) {
+    int stores = 0;
+    for (int u = s - (D - 1); u <= s - 1; ++u)
+      stores += BURST ? ((((u % KS) + KS) % KS == 0) ? 8 : 0) : PPS;
+    return (D - 2) * LPS + stores;
+  }
   static_assert(XL == W, "one x load per wave per step");
   static_assert(KS >= 1 && 8 % KS == 0, "8 hprev stores per chunk");
-  static_assert(VM_STEADY <= 63, "vmcnt range");
+  static_assert((D - 2) * LPS + (BURST ? 8 * ((D + KS - 2) / KS) : (D - 1) * PPS) <= 63, "vmcnt range");
   static_assert(D * SLOT <= 80 * 1024, "two workgroups per CU");
 };
 
@@ -643,6 +657,17 @@ __global__ __launch_bounds__(64 * (P / 16)) void ssd_chunk_state_pass_rows(
   // piece (jj, q / 2) of row p: dstate columns 128 ng + 16 jj + 8 (q / 2) ..
   // + 7; lane groups q = 0, 2 store its hi halves, q = 1, 3 its lo halves
   const uint32_t hrow = (uint32_t)p * (4 * N) + (uint32_t)(16 * ng + q / 2) * 32 + (uint32_t)(q % 2) * 16;
+  // one block's piece of hprev[k] = h (the state entering the chunk)
+  auto store_block = [&](__amdgpu_buffer_rsrc_t rh, int jj) {
+    const uint32_t a0 = pack_bf16x2(hs[jj][0], hs[jj][1]);
+    const uint32_t a1 = pack_bf16x2(hs[jj][2], hs[jj][3]);
+    const uint32_t l0 = pack_bf16x2(hs[jj][0] - bf16lo(a0), hs[jj][1] - bf16hi(a0));
+    const uint32_t l1 = pack_bf16x2(hs[jj][2] - bf16lo(a1), hs[jj][3] - bf16hi(a1));
+    const auto s0 = __builtin_amdgcn_permlane16_swap(a0, l0, false, false);
+    const auto s1 = __builtin_amdgcn_permlane16_swap(a1, l1, false, false);
+    const u32x4 vv = {s0[0], s1[0], s0[1], s1[1]};
+    __builtin_amdgcn_raw_buffer_store_b128(vv, rh, hrow + (uint32_t)jj * 64, 0, 0);
+  };
 
   for (int64_t u = 0; u < D - 1; ++u) issue(u < nsteps ? u : nsteps - 1);
 
@@ -657,8 +682,13 @@ __global__ __launch_bounds__(64 * (P / 16)) void ssd_chunk_state_pass_rows(
       // this wave's loads of step t have landed and its reads of step t - 1
       // are done; after the barrier, so are every wave's
       if (t < D - 1) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(Sc::VM_FIRST) : "memory");
-      else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(Sc::VM_STEADY) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(Sc::vm_at(s)) : "memory");
       issue(t + D - 1 < nsteps ? t + D - 1 : nsteps - 1);
+      if constexpr (Sc::BURST)
+        if (s == 0) {
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) store_block(rh, jj);
+        }
       const unsigned char* sp = ring[t % D];
       uint64_t x2[2];
 #pragma unroll
@@ -689,17 +719,9 @@ __global__ __launch_bounds__(64 * (P / 16)) void ssd_chunk_state_pass_rows(
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) acc[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[jj], xlo, acc[jj], 0, 0, 0);
       // hprev[k] = h: blocks s*PPS .. s*PPS + PPS - 1
+      if constexpr (!Sc::BURST) {
 #pragma unroll
-      for (int i = 0; i < PPS; ++i) {
-        const int jj = s * PPS + i;
-        const uint32_t a0 = pack_bf16x2(hs[jj][0], hs[jj][1]);
-        const uint32_t a1 = pack_bf16x2(hs[jj][2], hs[jj][3]);
-        const uint32_t l0 = pack_bf16x2(hs[jj][0] - bf16lo(a0), hs[jj][1] - bf16hi(a0));
-        const uint32_t l1 = pack_bf16x2(hs[jj][2] - bf16lo(a1), hs[jj][3] - bf16hi(a1));
-        const auto s0 = __builtin_amdgcn_permlane16_swap(a0, l0, false, false);
-        const auto s1 = __builtin_amdgcn_permlane16_swap(a1, l1, false, false);
-        const u32x4 vv = {s0[0], s1[0], s0[1], s1[1]};
-        __builtin_amdgcn_raw_buffer_store_b128(vv, rh, hrow + (uint32_t)jj * 64, 0, 0);
+        for (int i = 0; i < PPS; ++i) store_block(rh, s * PPS + i);
       }
     }
     // h = 2^(G'_last,k) h + S_k
