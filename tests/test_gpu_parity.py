@@ -325,6 +325,29 @@ def test_fused_state_pass(name):
         "y: paths differ by more than one bf16 ulp plus the hprev difference"
 
 
+ROW_SWEEP = [(P, N, Q) for P in (64, 128) for N in (128, 256) for Q in (64, 128, 256)]
+
+
+@pytest.mark.parametrize("P,N,Q", ROW_SWEEP)
+def test_row_form_every_instantiation(P, N, Q):
+    """The three-kernel sequence at small sizes runs the row form of the state
+    pass (one workgroup per batch, head and 128-column dstate slice): every
+    headdim, dstate and chunk it is built for, with a ragged last chunk, two
+    groups and a nonzero initial state, against the oracle's hprev, y and
+    final state."""
+    cfg = LayerConfig(f"rows-{P}-{N}-{Q}", batch=1, seqlen=3 * Q + 17, nheads=4, headdim=P, dstate=N,
+                      ngroups=2, chunk=Q, io="bf16", seed=1300 + P + N + Q, init_sigma=0.5)
+    log(f"[rows] P={P} N={N} Q={Q}")
+    inp = generate(cfg)
+    yr, fr, inter = oracle_all(inp, cfg, intermediates=True)
+    y, fin, ws, L, dims = run(to_device(inp, cfg.io), Q, keep_workspace=True, path=ssd.PATH_THREE)
+    assert ssd.fused_state_pass(dims, 1 | ssd.PATH_THREE) and L.path == ssd.PATH_THREE
+    v = workspace_views(ws, L, dims, 1)
+    log("  " + check_close(host(v["hprev"]), inter["hprev"], cfg.io, "hprev (row form)"))
+    log("  " + check_close(host(y), yr, cfg.io, "y"))
+    log("  " + check_close(host(fin), fr, cfg.io, "final_state"))
+
+
 def test_fused_state_pass_in_place_and_no_final():
     """init_state may be final_state (in-place update); final_state may be absent."""
     cfg = LayerConfig("fused-inplace", batch=2, seqlen=2 * 256 + 40, nheads=3, headdim=64, dstate=128,
