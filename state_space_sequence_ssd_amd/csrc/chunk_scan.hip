@@ -272,6 +272,7 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
   using I = Io<T>;
   using Frag = typename I::Frag;
   using Cfg = ScanCfg<T, P, N, Q>;
+  static_assert(!Cfg::HLDS, "Hprev that fits in LDS takes the persistent form below");
   constexpr int E = I::E, KPL = I::KPL, CG = Cfg::CG, NTB = Cfg::NTB, TBW = Cfg::TBW;
   constexpr int PGW = Cfg::PGW, NPS = Cfg::NPS, WAVES = Cfg::WAVES;
   constexpr int NBUF = Cfg::NBUF, LOADS = Cfg::LOADS;
@@ -280,7 +281,6 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
   constexpr int JS = 32 / (2 * KPL);   // MFMA steps over a 32-token j-block
 
   __shared__ __attribute__((aligned(16))) unsigned char ring[NBUF][Cfg::BLOCK];
-  __shared__ __attribute__((aligned(16))) unsigned char sH[Cfg::HALLOC];
   __shared__ __attribute__((aligned(16))) float sG[Q];
   __shared__ __attribute__((aligned(16))) float sDt[Q];
   __shared__ __attribute__((aligned(16))) float sW[Q];   // dt_j * 2^(G'_end(block of j) - G'_j) <= dt_j
@@ -345,9 +345,8 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
 
   // Hprev bytes of this chunk: P rows of 4N bytes
   const unsigned char* hsrc = static_cast<const unsigned char*>(hprev) + hoff * 4;
-  if constexpr (Cfg::HLDS) issue_hprev<Cfg, T>(sH, hsrc, wave, lane);
-  // the first NBUF-1 j-blocks go in flight behind it; with staged Hprev its
-  // first two pieces go first, and the j-blocks follow the last pieces
+  // the first NBUF-1 j-blocks go in flight now; with staged Hprev its first
+  // two pieces go first, and the j-blocks follow the last pieces
   constexpr int JOFF = Cfg::STAGE ? Cfg::NPC % NBUF : 0;   // ring slot of j-block 0
   auto issue_j = [&](int jn) {
     const int sn = (jn + JOFF) % NBUF;
@@ -417,49 +416,26 @@ void ssd_chunk_scan(const T* __restrict__ x, const T* __restrict__ Bm, const T* 
       }
     }
   }
-  if constexpr (Cfg::HLDS) {
-    // Hprev landed once only the j-block loads issued after it remain
-    if constexpr (NBUF - 1 <= NTB) {
-      if constexpr (NBUF == 3) wait_vm_barrier<2 * LOADS>();
-      else wait_vm_barrier<3 * LOADS>();
-    } else {
-      wait_vm_barrier<0>();
-    }
-  }
+  if constexpr (!Cfg::STAGE) {
+    // fp32 Hprev, too large for LDS: each wave loads its fragments from
+    // global memory (the fp32 MFMA takes the state whole, no split)
+    static_assert(!I::SPLIT, "bf16 Hprev is staged");
 #pragma unroll
-  for (int q = 0; q < PGW; ++q)
+    for (int q = 0; q < PGW; ++q)
 #pragma unroll
-    for (int pe = 0; pe < E; ++pe) {
-      const int p = (pg0 + q) * CG + E * m + pe;
+      for (int pe = 0; pe < E; ++pe) {
+        const int p = (pg0 + q) * CG + E * m + pe;
 #pragma unroll
-      for (int s = 0; s < (Cfg::STAGE ? 0 : KS); ++s) {
-        Frag hhi, hlo;
-        if constexpr (Cfg::HLDS) {
-          const int slot = E == 2 ? (pg0 + q) * 64 + pe * 32 + m : p;
-          const unsigned char* hp = sH + slot * (Cfg::HROWP * 16);
-          if constexpr (I::SPLIT) {
-            hhi = *reinterpret_cast<const Frag*>(hp + (2 * s + g) * 32);
-            hlo = *reinterpret_cast<const Frag*>(hp + (2 * s + g) * 32 + 16);
-          } else {
-            hhi = *reinterpret_cast<const Frag*>(hp + (s * 2 * KPL + KPL * g) * 4);
-          }
-        } else if constexpr (I::SPLIT) {
-          // (hi, lo) pairs: 8 hi then 8 lo bf16 per aligned group of 8 columns
-          const bf16* hp = static_cast<const bf16*>(hprev) + 2 * hoff + (int64_t)p * 2 * N + (2 * s + g) * 16;
-          hhi = I::load_row(reinterpret_cast<const T*>(hp), true);
-          hlo = I::load_row(reinterpret_cast<const T*>(hp + 8), true);
-        } else {
-          hhi = I::load_row(static_cast<const T*>(hprev) + hoff + (int64_t)p * N + s * 2 * KPL + KPL * g, true);
-        }
+        for (int s = 0; s < KS; ++s) {
+          const Frag hhi =
+              I::load_row(static_cast<const T*>(hprev) + hoff + (int64_t)p * N + s * 2 * KPL + KPL * g, true);
 #pragma unroll
-        for (int u = 0; u < TBW; ++u) {
-          I::mma(acc[u][q][pe], cf[u][s], hhi);
-          if constexpr (I::SPLIT) I::mma(acc[u][q][pe], cf[u][s], hlo);
+          for (int u = 0; u < TBW; ++u) I::mma(acc[u][q][pe], cf[u][s], hhi);
         }
       }
-    }
+  }
 
-  if constexpr (!Cfg::HLDS) asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // sG, sDt, sW visible
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");   // sG, sDt, sW visible
 #pragma unroll
   for (int u = 0; u < TBW; ++u)
 #pragma unroll
