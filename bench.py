@@ -147,6 +147,28 @@ def copy_calibration(dev):
     del src_buf, dst_buf
 
 
+def copy_rate_gbs(dev, reps=10):
+    """Read plus written bytes per second of plain device-to-device copies of
+    a 256 MiB buffer (the runtime's own copy kernel, source and destination
+    together twice the 256 MB last-level cache), timed with events on the
+    current stream: the streaming rate the chip reaches in practice, reported
+    beside the published peak."""
+    import torch
+    n = 64 * 1024 * 1024
+    src_buf = torch.ones(n, dtype=torch.float32, device=dev)
+    dst_buf = torch.empty_like(src_buf)
+    dst_buf.copy_(src_buf)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst_buf.copy_(src_buf)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    del src_buf, dst_buf
+    return 2.0 * n * 4 / (ms * 1e-3) / 1e9
+
+
 def decode_bytes(cfg):
     """Algorithmic bytes of one decode step: the fp32 state read and written,
     x and y, B and C, dt, A and D, each once."""
@@ -796,6 +818,9 @@ def run_forward(args, cfg):
     }
     if dom == "ssd_chunk_scan":
         out["roofline"]["hprev_bytes_per_element"] = 4
+    copy_gbs = copy_rate_gbs(dev)
+    out["roofline"]["copy_GB/s"] = round(copy_gbs, 1)
+    out["roofline"]["frac_of_copy"] = round(achieved / copy_gbs, 4)
     if not args.no_cpu:
         base, parity = cpu_baseline(cfg, inp, y.float().cpu().numpy(), budget_s=args.cpu_budget)
         out["cpu_baseline"] = base
